@@ -1,0 +1,212 @@
+"""Seeded synthetic inputs for the fused projection path.
+
+This module only *draws* inputs: it holds none of the arithmetic of the method
+(no residual add, no normalisation, no matmul, no activation, no dequantisation).
+Both the HIP path and the CPU oracle take their inputs from here, and from
+nowhere else, so the two sides see bit-identical tensors.
+
+Recipe (stated once, used everywhere):
+
+* generator: numpy PCG64, ``numpy.random.default_rng(seed)``;
+* draw order per workload: x, residual, gamma, beta, W_qkv, b_qkv, W_gu, b_gu
+  (items a workload does not use are skipped, the order of the rest is kept);
+* normal draws are float32 ziggurat samples (``standard_normal(dtype=float32)``)
+  scaled by the standard deviation in float32; uniform draws are float64 and
+  rounded to float32;
+* float32 values are then rounded to the activation dtype by torch's cast,
+  which is round-to-nearest-even;
+* weights are drawn directly in the ``[N, K]`` (output-major, K contiguous)
+  layout that the library consumes;
+* int8 weights: a float32 weight is drawn as above, then quantised per output
+  row with the symmetric max-abs rule ``s = max|w| / 127`` (float32) and
+  ``q = clip(rint(w / s), -127, 127)``.  The stored inputs of the method are
+  ``(q, s)``; how they were produced is not part of the path.
+
+Workload shapes follow the five transformer-block configurations that the
+fused-projection pages are measured on: a tiny fp32 block, a Llama-3-8B decode
+step, a Llama-2-7B prefill batch, a GPT-style fp16 LayerNorm + GELU block, and
+a Llama-2-70B layer with int8 weights at four token counts.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "workload", "generate", "quantize_rows_i8"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    hidden: int
+    act: str                    # "f32" | "f16" | "bf16"
+    wdt: str                    # "f32" | "f16" | "bf16" | "i8"
+    norm: str                   # "rms" | "layer"
+    eps: float
+    x_std: float
+    r_std: float
+    gamma_lo: float
+    gamma_hi: float
+    beta_std: Optional[float]   # LayerNorm only
+    w_std: float
+    # QKV projection (None when the workload has no QKV call)
+    n_heads: Optional[int]
+    n_kv_heads: Optional[int]
+    head_dim: Optional[int]
+    # gate/up or up projection
+    ffn: int
+    act_fn: str                 # "swiglu" | "gelu_tanh" | "none"
+    bias_std: Optional[float]   # bias of the gate/up (or up) projection
+
+    @property
+    def n_qkv(self) -> int:
+        if self.n_heads is None:
+            return 0
+        return (self.n_heads + 2 * self.n_kv_heads) * self.head_dim
+
+    @property
+    def n_gu(self) -> int:
+        return 2 * self.ffn if self.act_fn == "swiglu" else self.ffn
+
+    def with_m(self, M: int) -> "Workload":
+        return dataclasses.replace(self, M=M, name=f"{self.name.split('@')[0]}@M{M}")
+
+
+def _llama70b(M: int) -> Workload:
+    return Workload(
+        name=f"llama2-70b-int8w@M{M}", M=M, hidden=8192, act="bf16", wdt="i8",
+        norm="rms", eps=1e-5, x_std=1.0, r_std=1.0, gamma_lo=0.8, gamma_hi=1.2,
+        beta_std=None, w_std=0.02, n_heads=64, n_kv_heads=8, head_dim=128,
+        ffn=28672, act_fn="swiglu", bias_std=None)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # tiny fp32 block: M=4, hidden=256, 4 Q / 2 KV heads of 64, ffn=512
+    "tiny-f32": Workload(
+        name="tiny-f32", M=4, hidden=256, act="f32", wdt="f32", norm="rms",
+        eps=1e-5, x_std=1.0, r_std=1.0, gamma_lo=0.5, gamma_hi=1.5,
+        beta_std=None, w_std=1.0 / 16.0, n_heads=4, n_kv_heads=2, head_dim=64,
+        ffn=512, act_fn="swiglu", bias_std=None),
+    # Llama-3-8B-shaped decode step, bf16
+    "llama3-8b-decode": Workload(
+        name="llama3-8b-decode", M=32, hidden=4096, act="bf16", wdt="bf16",
+        norm="rms", eps=1e-5, x_std=1.0, r_std=1.0, gamma_lo=0.8, gamma_hi=1.2,
+        beta_std=None, w_std=0.02, n_heads=32, n_kv_heads=8, head_dim=128,
+        ffn=14336, act_fn="swiglu", bias_std=None),
+    # Llama-2-7B-shaped prefill (32 x 512 tokens), bf16, MHA; the tiny block's
+    # distributions with the weight std taken as 1/sqrt(hidden)
+    "llama2-7b-prefill": Workload(
+        name="llama2-7b-prefill", M=16384, hidden=4096, act="bf16", wdt="bf16",
+        norm="rms", eps=1e-5, x_std=1.0, r_std=1.0, gamma_lo=0.5, gamma_hi=1.5,
+        beta_std=None, w_std=1.0 / 64.0, n_heads=32, n_kv_heads=32,
+        head_dim=128, ffn=11008, act_fn="swiglu", bias_std=None),
+    # GPT-style fp16 block: add + LayerNorm -> up GEMM + bias + tanh-GELU
+    "gpt-fp16-gelu": Workload(
+        name="gpt-fp16-gelu", M=2048, hidden=4096, act="f16", wdt="f16",
+        norm="layer", eps=1e-5, x_std=1.0, r_std=1.0, gamma_lo=0.8,
+        gamma_hi=1.2, beta_std=0.02, w_std=0.02, n_heads=None,
+        n_kv_heads=None, head_dim=None, ffn=16384, act_fn="gelu_tanh",
+        bias_std=0.02),
+    "llama2-70b-int8w@M1": _llama70b(1),
+    "llama2-70b-int8w@M16": _llama70b(16),
+    "llama2-70b-int8w@M64": _llama70b(64),
+    "llama2-70b-int8w@M256": _llama70b(256),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+_TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    v = rng.standard_normal(size=shape, dtype=np.float32)
+    v *= np.float32(std)
+    return v
+
+
+def _uniform(rng: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
+    return rng.uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def _to_act(v: np.ndarray, act: str) -> torch.Tensor:
+    return torch.from_numpy(v).to(_TORCH_DT[act])
+
+
+def quantize_rows_i8(w: np.ndarray):
+    """Symmetric per-output-row int8 storage of a float32 ``[N, K]`` weight.
+
+    ``s[j] = max_k |w[j, k]| / 127`` in float32 and
+    ``q[j, k] = clip(rint(w[j, k] / s[j]), -127, 127)``; a zero row gets s = 0
+    and q = 0.  This produces the *stored* weights; the method only ever reads
+    ``(q, s)``.  Rows are processed in blocks to bound host memory.
+    """
+    N, K = w.shape
+    q = np.empty((N, K), dtype=np.int8)
+    s = np.empty((N,), dtype=np.float32)
+    step = max(1, (1 << 24) // max(K, 1))
+    for j0 in range(0, N, step):
+        blk = w[j0:j0 + step]
+        amax = np.abs(blk).max(axis=1).astype(np.float32)
+        sc = (amax / np.float32(127.0)).astype(np.float32)
+        safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+        qq = np.rint(blk / safe[:, None])
+        qq = np.clip(qq, -127, 127)
+        qq[sc == 0] = 0
+        q[j0:j0 + step] = qq.astype(np.int8)
+        s[j0:j0 + step] = sc
+    return torch.from_numpy(q), torch.from_numpy(s)
+
+
+def _weight(rng, wl: Workload, N: int):
+    w = _normal(rng, (N, wl.hidden), wl.w_std)
+    if wl.wdt == "i8":
+        q, s = quantize_rows_i8(w)
+        return q, s
+    return _to_act(w, wl.wdt), None
+
+
+def generate(wl: Workload, seed: int = 0, parts=("qkv", "gu")) -> Dict[str, torch.Tensor]:
+    """All host tensors of one workload (CPU torch tensors, contiguous).
+
+    Keys: x, r, gamma, beta (LayerNorm only), and per projection
+    w_qkv / s_qkv / b_qkv and w_gu / s_gu / b_gu.  ``s_*`` is present only for
+    int8 weights; ``b_*`` only when the workload has that bias.  ``parts``
+    selects which projections to draw, but the draw order (and hence every
+    value) does not depend on it: skipped weights are still drawn.
+    """
+    rng = np.random.default_rng(seed)
+    out: Dict[str, torch.Tensor] = {}
+    M, K = wl.M, wl.hidden
+    out["x"] = _to_act(_normal(rng, (M, K), wl.x_std), wl.act)
+    out["r"] = _to_act(_normal(rng, (M, K), wl.r_std), wl.act)
+    out["gamma"] = _to_act(_uniform(rng, (K,), wl.gamma_lo, wl.gamma_hi), wl.act)
+    if wl.norm == "layer":
+        out["beta"] = _to_act(_normal(rng, (K,), wl.beta_std), wl.act)
+    if wl.n_qkv:
+        w, s = _weight(rng, wl, wl.n_qkv)
+        if "qkv" in parts:
+            out["w_qkv"] = w
+            if s is not None:
+                out["s_qkv"] = s
+        del w, s
+    w, s = _weight(rng, wl, wl.n_gu)
+    if "gu" in parts:
+        out["w_gu"] = w
+        if s is not None:
+            out["s_gu"] = s
+    del w, s
+    if wl.bias_std is not None:
+        out["b_gu"] = _to_act(_normal(rng, (wl.n_gu,), wl.bias_std), wl.act)
+    return out
+
+
+def rows(t: torch.Tensor, idx) -> torch.Tensor:
+    """Gather token rows (rows are independent in every step of the path)."""
+    return t[torch.as_tensor(idx, dtype=torch.long)].contiguous()

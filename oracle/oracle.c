@@ -1,0 +1,320 @@
+/*
+ * CPU oracle for the fused residual-add + norm + projection path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or helper with the HIP
+ * library.
+ *
+ * Everything is computed in IEEE double precision with plain loops, in the
+ * order the method states its steps.  The one deliberate rounding is the GEMM
+ * A-operand: a fused kernel feeds the matrix unit in the activation dtype, so
+ * the normalised row is rounded (round-to-nearest-even) to that dtype before
+ * the product ("reading A"); the unrounded variant is available too
+ * ("reading B", rounded = 0).  Weights are used exactly as stored (int8
+ * weights through their documented dequantisation).
+ *
+ * Sources (web pages on TensorRT-LLM; cited by title and section):
+ *  [D] "TensorRT-LLM 深度工程实践：从模型到生产级推理服务", §2.3 跨算子融合,
+ *      sketch "LayerNorm + QKV Projection 融合" (per-token mean, variance,
+ *      rsqrt(var + eps), gamma * (x - mean) * rsqrt + beta, then the Q, K and V
+ *      products written straight out) and sketch "GEMM + 激活融合（SwiGLU）"
+ *      (y = SiLU(x @ gate) * (x @ up), activation and product in registers).
+ *  [D2] same page, §2.2 图构建与算子映射: QKV projection = one matmul followed
+ *      by reshape and GQA grouping of the heads.
+ *  [I] "2. TensorRT-LLM 简介", 核心原理: the graph-optimisation layer fuses
+ *      QKV, fuses residual + LayerNorm, and matches precision per op.
+ *  [F] "TRT-LLM deep dive" (lib.uml.com.cn), 构建阶段详解 §3 Layer Fusion
+ *      figure: Add -> (Mul/Bias) -> LayerNorm -> GELU collapsed into one
+ *      kernel; 面试视角: LayerNorm + Linear + GELU as a single kernel.
+ *
+ * Readings of points the pages leave open (each repeated where it is used):
+ *  R1 residual add h = x + r, exact; the stored residual stream is
+ *     h_out = RNE_act(h).
+ *  R2 RMSNorm n = h / sqrt(mean(h^2) + eps) * gamma (no mean, no beta).
+ *  R3 LayerNorm uses the biased (1/K) variance; gamma scales after the
+ *     normalisation and beta is added last, as in the sketch [D].
+ *  R4 QKV columns are three contiguous blocks Q | K | V; q, k, v are stored
+ *     token-major [M, heads, head_dim].
+ *  R5 SwiGLU: the weight holds the gate rows [0, F) then the up rows [F, 2F);
+ *     out = SiLU(gate) * up with SiLU(g) = g / (1 + exp(-g)).
+ *  R6 GELU is the tanh approximation
+ *     0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).
+ *  R7 bias (when given) is added to the accumulator before the activation.
+ *  R8 int8 weights: w = RNE_bf16(RNE_f32(q * s)) with s the fp32 scale of the
+ *     output row; both roundings are part of the definition.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3 };
+enum { OR_NORM_NONE = 0, OR_NORM_RMS = 1, OR_NORM_LAYER = 2 };
+enum { OR_ACT_NONE = 0, OR_ACT_SWIGLU = 1, OR_ACT_GELU_TANH = 2 };
+
+/* ---------------------------------------------------------------------------
+ * Number formats.  A binary floating-point format is described by its
+ * significand precision p (bits, implicit bit included), the exponent of its
+ * smallest normal number, and its largest finite value.
+ * ------------------------------------------------------------------------- */
+static void fmt_params(int dtype, int *p, int *emin, double *maxv) {
+    switch (dtype) {
+    case OR_F16:  *p = 11; *emin = -14;  *maxv = 65504.0; break;
+    case OR_BF16: *p = 8;  *emin = -126; *maxv = ldexp(255.0, 120); break; /* (2-2^-7)*2^127 */
+    default:      *p = 24; *emin = -126; *maxv = ldexp(16777215.0, 104); break; /* (2-2^-23)*2^127 */
+    }
+}
+
+/* Round v to the nearest value of the format, ties to even; values beyond the
+ * largest finite number (after rounding) become +-inf.  Works directly from
+ * the double, so there is no double rounding. */
+double or_round(double v, int dtype) {
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    int p, emin; double maxv;
+    fmt_params(dtype, &p, &emin, &maxv);
+    int e2;
+    (void)frexp(v, &e2);          /* v = f * 2^e2, 0.5 <= |f| < 1 */
+    int lead = e2 - 1;            /* exponent of the leading bit */
+    if (lead < emin) lead = emin; /* subnormal range: fixed quantum */
+    int qexp = lead - (p - 1);    /* weight of the last significand bit */
+    double scaled = ldexp(v, -qexp);         /* exact (power-of-two scaling) */
+    double r = nearbyint(scaled);            /* default mode: ties to even */
+    double out = ldexp(r, qexp);
+    if (fabs(out) > maxv) out = copysign(INFINITY, v);
+    return out;
+}
+
+/* Decode one stored element to double. */
+double or_load(const void *ptr, int dtype, int64_t i) {
+    switch (dtype) {
+    case OR_F32: return (double)((const float *)ptr)[i];
+    case OR_I8:  return (double)((const int8_t *)ptr)[i];
+    case OR_BF16: {
+        uint32_t b = ((const uint16_t *)ptr)[i];
+        uint32_t u = b << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return (double)f;
+    }
+    case OR_F16: {
+        uint16_t b = ((const uint16_t *)ptr)[i];
+        int sign = (b >> 15) & 1, ex = (b >> 10) & 31, man = b & 1023;
+        double mag;
+        if (ex == 0)       mag = ldexp((double)man, -24);              /* subnormal */
+        else if (ex == 31) mag = man ? NAN : INFINITY;
+        else               mag = ldexp((double)(1024 + man), ex - 25); /* 1.man * 2^(ex-15) */
+        return sign ? -mag : mag;
+    }
+    }
+    return NAN;
+}
+
+void or_decode_array(const void *in, int dtype, int64_t n, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = or_load(in, dtype, i);
+}
+
+void or_round_array(const double *in, double *out, int64_t n, int dtype) {
+    for (int64_t i = 0; i < n; ++i) out[i] = or_round(in[i], dtype);
+}
+
+/* bf16 bit pattern of a double that is already exactly a bf16 value. */
+static uint16_t bf16_bits_of(double v) {
+    float f = (float)v;   /* exact: v is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* ---------------------------------------------------------------------------
+ * Activations (R5, R6).
+ * ------------------------------------------------------------------------- */
+double or_silu(double g) { return g / (1.0 + exp(-g)); }
+
+double or_gelu_tanh(double y) {
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * y * (1.0 + tanh(c * (y + 0.044715 * y * y * y)));
+}
+
+int or_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------------------
+ * int8 weight dequantisation (R8): w = RNE_bf16(RNE_f32(q * s)).
+ * q * s is exact in double (8-bit times 24-bit significands).
+ * ------------------------------------------------------------------------- */
+int or_dequant_i8(const int8_t *q, const float *s, int64_t N, int64_t K,
+                  double *w_out, uint16_t *bits_out) {
+    for (int64_t j = 0; j < N; ++j) {
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = (double)q[j * K + k] * (double)s[j];
+            double w = or_round(or_round(prod, OR_F32), OR_BF16);
+            if (w_out) w_out[j * K + k] = w;
+            if (bits_out) bits_out[j * K + k] = bf16_bits_of(w);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Residual add and row normalisation, one token row at a time ([D], [I]).
+ *  h = x + r                                        (R1; r may be NULL)
+ *  RMS:   n = h / sqrt(sum(h^2)/K + eps) * gamma    (R2)
+ *  LAYER: mu = sum(h)/K, var = sum((h-mu)^2)/K,
+ *         n = (h - mu) / sqrt(var + eps) * gamma + beta   (R3; beta may be NULL)
+ *  NONE:  n = h
+ * Outputs (each may be NULL): h_out = RNE_act(h), n_out = n, a_out = RNE_act(n).
+ * ------------------------------------------------------------------------- */
+int or_add_norm(const void *x, const void *r, const void *gamma, const void *beta,
+                int act, int norm, double eps, int64_t M, int64_t K,
+                double *h_out, double *n_out, double *a_out) {
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *h = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!h) { bad = 1; continue; }
+        for (int64_t k = 0; k < K; ++k) {
+            double hv = or_load(x, act, m * K + k);
+            if (r) hv += or_load(r, act, m * K + k);
+            h[k] = hv;
+            if (h_out) h_out[m * K + k] = or_round(hv, act);
+        }
+        double mu = 0.0, inv = 1.0;
+        if (norm == OR_NORM_RMS) {
+            double ss = 0.0;
+            for (int64_t k = 0; k < K; ++k) ss += h[k] * h[k];
+            inv = 1.0 / sqrt(ss / (double)K + eps);
+        } else if (norm == OR_NORM_LAYER) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) s += h[k];
+            mu = s / (double)K;
+            double vs = 0.0;
+            for (int64_t k = 0; k < K; ++k) vs += (h[k] - mu) * (h[k] - mu);
+            inv = 1.0 / sqrt(vs / (double)K + eps);
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            double n;
+            if (norm == OR_NORM_RMS) {
+                n = h[k] * inv * or_load(gamma, act, k);
+            } else if (norm == OR_NORM_LAYER) {
+                n = (h[k] - mu) * inv * or_load(gamma, act, k);
+                if (beta) n += or_load(beta, act, k);
+            } else {
+                n = h[k];
+            }
+            if (n_out) n_out[m * K + k] = n;
+            if (a_out) a_out[m * K + k] = or_round(n, act);
+        }
+        free(h);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * The projection product acc[m, j] = sum_k a[m, k] * w[j, k]  ([D]).
+ * w is [N, K] with K contiguous, in its stored dtype; int8 weights go through
+ * the dequantisation above (R8).  Each weight row is decoded once into a
+ * double buffer and then used for every token row.
+ * ------------------------------------------------------------------------- */
+int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scale,
+                 int64_t M, int64_t K, int64_t N, double *acc) {
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j) {
+        double *wr = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!wr) { bad = 1; continue; }
+        if (wdtype == OR_I8)
+            or_dequant_i8((const int8_t *)w + j * K, w_scale + j, 1, K, wr, NULL);
+        else
+            for (int64_t k = 0; k < K; ++k) wr[k] = or_load(w, wdtype, j * K + k);
+        for (int64_t m = 0; m < M; ++m) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) s += a[m * K + k] * wr[k];
+            acc[m * N + j] = s;
+        }
+        free(wr);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Full calls.
+ * ------------------------------------------------------------------------- */
+static double *prologue(const void *x, const void *r, const void *gamma, const void *beta,
+                        int act, int norm, double eps, int64_t M, int64_t K,
+                        double *h_out, int rounded) {
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!a) return NULL;
+    int rc = rounded ? or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, NULL, a)
+                     : or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, a, NULL);
+    if (rc) { free(a); return NULL; }
+    return a;
+}
+
+/* residual add + norm -> QKV product -> (+bias) -> split into q, k, v.
+ * q: [M, H, D], k and v: [M, Hkv, D]; column c of the product is
+ * q[m, c / D, c % D] for c < H*D, then k, then v (R4, [D2]). */
+int or_add_norm_qkv(const void *x, const void *r, const void *gamma, const void *beta,
+                    int act, int norm, double eps,
+                    const void *w, int wdtype, const float *w_scale, const void *bias,
+                    int64_t M, int64_t K, int64_t H, int64_t Hkv, int64_t D,
+                    double *q, double *k, double *v, double *h_out, int rounded) {
+    int64_t N = (H + 2 * Hkv) * D, nq = H * D, nkv = Hkv * D;
+    double *a = prologue(x, r, gamma, beta, act, norm, eps, M, K, h_out, rounded);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)(M * N > 0 ? M * N : 1));
+    if (!a || !acc) { free(a); free(acc); return -1; }
+    if (or_matmul_nt(a, w, wdtype, w_scale, M, K, N, acc)) { free(a); free(acc); return -1; }
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t c = 0; c < N; ++c) {
+            double y = acc[m * N + c];
+            if (bias) y += or_load(bias, act, c);
+            if (c < nq)            q[m * nq + c] = y;
+            else if (c < nq + nkv) k[m * nkv + (c - nq)] = y;
+            else                   v[m * nkv + (c - nq - nkv)] = y;
+        }
+    }
+    free(a);
+    free(acc);
+    return 0;
+}
+
+/* (residual add + norm ->) gate/up or up product -> (+bias) -> activation.
+ * SWIGLU: w is [2F, K] (gate rows then up rows), out[m, j] = SiLU(g) * u (R5).
+ * GELU_TANH / NONE: w is [F, K], out = GELU(acc + b) or acc + b (R6, R7, [F]). */
+int or_gateup_act(const void *x, const void *r, const void *gamma, const void *beta,
+                  int act, int norm, double eps,
+                  const void *w, int wdtype, const float *w_scale, const void *bias,
+                  int64_t M, int64_t K, int64_t F, int actfn,
+                  double *out, double *h_out, int rounded) {
+    int64_t N = actfn == OR_ACT_SWIGLU ? 2 * F : F;
+    double *a = prologue(x, r, gamma, beta, act, norm, eps, M, K, h_out, rounded);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)(M * N > 0 ? M * N : 1));
+    if (!a || !acc) { free(a); free(acc); return -1; }
+    if (or_matmul_nt(a, w, wdtype, w_scale, M, K, N, acc)) { free(a); free(acc); return -1; }
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < F; ++j) {
+            double y;
+            if (actfn == OR_ACT_SWIGLU) {
+                double g = acc[m * N + j], u = acc[m * N + F + j];
+                if (bias) { g += or_load(bias, act, j); u += or_load(bias, act, F + j); }
+                y = or_silu(g) * u;
+            } else {
+                y = acc[m * N + j];
+                if (bias) y += or_load(bias, act, j);
+                if (actfn == OR_ACT_GELU_TANH) y = or_gelu_tanh(y);
+            }
+            out[m * F + j] = y;
+        }
+    }
+    free(a);
+    free(acc);
+    return 0;
+}

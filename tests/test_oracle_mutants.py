@@ -1,0 +1,63 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require
+that the pins catch every one of them.
+
+Each mutant is oracle.c with one textual substitution: a dropped term, a
+wrong sign, a wrong index, a transposed operand, a wrong constant, a missing
+rounding.  The copy is compiled into a temporary directory and the pins are
+run against it through ``oracle.using``.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "residual add dropped": ("if (r) hv += or_load(r, act, m * K + k);", "(void)r;"),
+    "rms uses sum not mean": ("inv = 1.0 / sqrt(ss / (double)K + eps);", "inv = 1.0 / sqrt(ss + eps);"),
+    "eps outside sqrt": ("inv = 1.0 / sqrt(ss / (double)K + eps);", "inv = 1.0 / (sqrt(ss / (double)K) + eps);"),
+    "layernorm mean sign": ("n = (h[k] - mu) * inv * or_load(gamma, act, k);",
+                            "n = (h[k] + mu) * inv * or_load(gamma, act, k);"),
+    "layernorm unbiased variance": ("inv = 1.0 / sqrt(vs / (double)K + eps);",
+                                    "inv = 1.0 / sqrt(vs / (double)(K - 1) + eps);"),
+    "beta dropped": ("if (beta) n += or_load(beta, act, k);", "(void)beta;"),
+    "gamma index shifted": ("n = h[k] * inv * or_load(gamma, act, k);",
+                            "n = h[k] * inv * or_load(gamma, act, (k + 1) % K);"),
+    "A operand not rounded": ("if (a_out) a_out[m * K + k] = or_round(n, act);",
+                              "if (a_out) a_out[m * K + k] = n;"),
+    "weight transposed": ("s += a[m * K + k] * wr[k];", "s += a[m * K + k] * or_load(w, wdtype, k * N + j);"),
+    "qkv k/v swapped": ("else if (c < nq + nkv) k[m * nkv + (c - nq)] = y;",
+                        "else if (c < nq + nkv) v[m * nkv + (c - nq)] = y;"),
+    "swiglu gate/up swapped": ("y = or_silu(g) * u;", "y = or_silu(u) * g;"),
+    "silu sign": ("return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
+    "gelu cubic constant": ("0.044715 * y * y * y", "0.047715 * y * y * y"),
+    "gelu half dropped": ("return 0.5 * y * (1.0 + tanh", "return y * (1.0 + tanh"),
+    "bias after activation": ("if (actfn == OR_ACT_GELU_TANH) y = or_gelu_tanh(y);",
+                              "if (actfn == OR_ACT_GELU_TANH) y = or_gelu_tanh(y - (bias ? or_load(bias, act, j) : 0)) + (bias ? or_load(bias, act, j) : 0);"),
+    "dequant single rounding": ("double w = or_round(or_round(prod, OR_F32), OR_BF16);",
+                                "double w = or_round(prod, OR_BF16);"),
+    "round ties away": ("double r = nearbyint(scaled);", "double r = round(scaled);"),
+    "bf16 precision off by one": ("case OR_BF16: *p = 8;", "case OR_BF16: *p = 9;"),
+    "fp16 subnormal decode": ("mag = ldexp((double)man, -24);", "mag = ldexp((double)man, -25);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = oracle.build(src=str(mut), out=str(tmp_path / "liboracle_mut.so"))
+    failed = []
+    with oracle.using(lib):
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                failed.append(pin.__name__)
+    assert failed, f"no pin caught the mutant '{name}'"
