@@ -1,0 +1,289 @@
+"""Benchmark of the fused projection path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic tokens:
+fused_add_norm_qkv (residual add, row statistics, normalisation into the MFMA
+A-tile, QKV GEMM, GQA split) followed by fused_gateup_act (the same prologue,
+gate/up GEMM, SwiGLU), i.e. the two calls of a transformer block's fused
+projections.  The default workload is the Llama-3-8B-shaped decode step
+(M = 32 tokens, hidden 4096, 32 Q / 8 KV heads of 128, ffn 14336, bf16),
+which is HBM-bound, so the headline value is algorithmic HBM GB/s.
+The prefill workload (Llama-2-7B shape, M = 16384) is timed as a secondary
+line in TFLOP/s.
+
+Inputs are resident in HBM before the timed region.  Several weight sets are
+rotated so that the 256 MB last-level cache cannot serve the weights of one
+step from the previous one.  Per-kernel durations come from the library's
+HIP-event profiler (events on the stream the kernels are launched on).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA
+MALL_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("fusion_residual_add_amd/csrc/fp_kernels.hip", "fusion_residual_add_amd/csrc/fp_api.cpp",
+              "fusion_residual_add_amd/csrc/fp_internal.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algo_bytes(wl, call: str) -> int:
+    """Algorithmic HBM bytes of one call: every input read once, every output
+    written once; the normalised rows and the GEMM intermediates are not
+    counted (the fusion keeps them on chip)."""
+    ea = {"f32": 4, "f16": 2, "bf16": 2}[wl.act]
+    ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}[wl.wdt]
+    M, K = wl.M, wl.hidden
+    b = 2 * M * K * ea + K * ea                      # x, residual, gamma
+    if wl.norm == "layer":
+        b += K * ea                                  # beta
+    if call == "qkv":
+        N = wl.n_qkv
+        b += N * K * ew + M * K * ea + M * N * ea    # weights, h_out, q/k/v
+    else:
+        N = wl.n_gu
+        b += N * K * ew + M * wl.ffn * ea            # weights, out
+        if wl.bias_std is not None:
+            b += N * ea
+    if wl.wdt == "i8":
+        b += 4 * N                                   # per-row scales
+    return b
+
+
+def flops(wl, call: str) -> int:
+    N = wl.n_qkv if call == "qkv" else wl.n_gu
+    return 2 * wl.M * wl.hidden * N
+
+
+class Runner:
+    """Device copies of a workload with R rotating weight sets."""
+
+    def __init__(self, wl, seed=0, min_sets=1):
+        import torch
+        from fusion_residual_add_amd import inputs
+        self.wl = wl
+        dev = torch.device("cuda:0")
+        host = inputs.generate(wl, seed=seed)
+        self.base = {k: v.to(dev) for k, v in host.items()}
+        wbytes = sum(t.numel() * t.element_size() for k, t in self.base.items() if k.startswith("w_"))
+        self.R = max(min_sets, (2 * MALL_BYTES) // max(wbytes, 1) + 1)
+        self.sets = [self.base]
+        for i in range(1, self.R):
+            s = dict(self.base)
+            for k in list(s):
+                if k.startswith("w_"):
+                    s[k] = self.base[k].roll(i, 0).contiguous()   # distinct buffers, same statistics
+            self.sets.append(s)
+        import fusion_residual_add_amd as fra
+        self.fra = fra
+        M = wl.M
+        self.q = torch.empty((M, wl.n_heads or 1, wl.head_dim or 1), dtype=self.base["x"].dtype, device=dev)
+        self.k = torch.empty((M, wl.n_kv_heads or 1, wl.head_dim or 1), dtype=self.base["x"].dtype, device=dev)
+        self.v = torch.empty_like(self.k)
+        self.h = torch.empty_like(self.base["x"])
+        self.out = torch.empty((M, wl.ffn), dtype=self.base["x"].dtype, device=dev)
+        self.ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        need = 0
+        act_t = self.base["x"].dtype
+        for call, N in (("qkv", wl.n_qkv), ("gu", wl.n_gu)):
+            if N:
+                w = self.base["w_qkv" if call == "qkv" else "w_gu"]
+                need = max(need, fra.workspace_bytes(M, wl.hidden, N, act_t, w.dtype))
+        if need > self.ws.numel():
+            self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def qkv(self, i):
+        s, wl = self.sets[i % self.R], self.wl
+        self.fra.fused_add_norm_qkv(s["x"], s["r"], s["gamma"], s["w_qkv"], wl.n_heads, wl.n_kv_heads,
+                                    wl.head_dim, beta=s.get("beta"), norm=wl.norm, eps=wl.eps,
+                                    w_scale=s.get("s_qkv"), bias=s.get("b_qkv"), h_out=self.h,
+                                    q=self.q, k=self.k, v=self.v, workspace=self.ws)
+
+    def gu(self, i):
+        s, wl = self.sets[i % self.R], self.wl
+        self.fra.fused_gateup_act(s["x"], s["r"], s["gamma"], s["w_gu"], wl.ffn, wl.act_fn,
+                                  beta=s.get("beta"), norm=wl.norm, eps=wl.eps, w_scale=s.get("s_gu"),
+                                  bias=s.get("b_gu"), out=self.out, workspace=self.ws)
+
+    def step(self, i):
+        if self.wl.n_qkv:
+            self.qkv(i)
+        self.gu(i)
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def profile_call(runner, call: str, n: int):
+    """Average duration (ms) of each library kernel over n calls of one kind."""
+    import torch
+    fn = runner.qkv if call == "qkv" else runner.gu
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    runner.fra.profile_start()
+    for i in range(n):
+        fn(i)
+    prof = runner.fra.profile_stop()
+    return {k: t / c for k, (c, t) in prof.items()}
+
+
+def load_traffic(kernel_key: str):
+    """HBM traffic per launch measured with rocprofv3 counters (profiles/traffic.json),
+    valid only while the kernel sources are unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    ent = d.get("kernels", {}).get(kernel_key)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    import oracle
+    from fusion_residual_add_amd import inputs
+    inp = inputs.generate(wl, seed=0)
+    oracle.load()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        if wl.n_qkv:
+            oracle.workload_qkv(wl, inp)
+        oracle.workload_gateup(wl, inp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 100:
+            break
+    per_step = el / n
+    step_bytes = (algo_bytes(wl, "qkv") if wl.n_qkv else 0) + algo_bytes(wl, "gu")
+    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the full {wl.name} step (both calls, all {wl.M} tokens) run {n} times "
+                      f"in {el:.1f} s, {per_step * 1e3:.1f} ms per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3-8b-decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the projections shard by heads / by gate-up pairs without communication; "
+              "see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fusion_residual_add_amd import inputs
+    if not os.path.exists(os.path.join(ROOT, "fusion_residual_add_amd", "libfusedproj.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    wl = inputs.workload(args.workload)
+    run = Runner(wl)
+    ms = time_steps(run.step, args.steps, args.warmup)
+    step_bytes = (algo_bytes(wl, "qkv") if wl.n_qkv else 0) + algo_bytes(wl, "gu")
+    step_flops = (flops(wl, "qkv") if wl.n_qkv else 0) + flops(wl, "gu")
+    decode = step_flops / step_bytes < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+    # dominant kernel: the gate/up projection
+    prof_gu = profile_call(run, "gu", 50)
+    gu_kernel = max(prof_gu, key=lambda k: prof_gu[k])
+    gu_ms = prof_gu[gu_kernel]
+    per_call = {"gu": {k: round(v * 1e3, 2) for k, v in prof_gu.items()}}
+    if wl.n_qkv:
+        prof_q = profile_call(run, "qkv", 50)
+        per_call["qkv"] = {k: round(v * 1e3, 2) for k, v in prof_q.items()}
+    if decode:
+        achieved = algo_bytes(wl, "gu") / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        value, unit = step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+    else:
+        achieved = flops(wl, "gu") / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+        value, unit = step_flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+    roof["kernel"] = gu_kernel
+    roof["kernel_avg_us"] = round(gu_ms * 1e3, 2)
+    roof["algo_bytes_per_launch"] = algo_bytes(wl, "gu")
+    roof["traffic"] = load_traffic(f"{wl.name}:{gu_kernel}")
+
+    line = {
+        "metric": "fused-layer TFLOP/s (prefill) and HBM GB/s (decode), % of MI355X roofline",
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.act, "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "hidden": wl.hidden, "n_heads": wl.n_heads,
+                   "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "ffn": wl.ffn,
+                   "act_fn": wl.act_fn, "norm": wl.norm, "weights": wl.wdt,
+                   "calls": (["fused_add_norm_qkv"] if wl.n_qkv else []) + [f"fused_gateup_act({wl.act_fn})"],
+                   "step_algo_bytes": step_bytes, "step_flops": step_flops,
+                   "weight_sets_rotated": run.R},
+        "roofline": roof,
+        "kernel_us": per_call,
+    }
+    del run
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        for name in ("llama2-7b-prefill",):
+            pwl = inputs.workload(name)
+            pr = Runner(pwl)
+            pms = time_steps(pr.step, args.prefill_steps, 3)
+            pfl = flops(pwl, "qkv") + flops(pwl, "gu")
+            pprof = profile_call(pr, "gu", 5)
+            pk = max(pprof, key=lambda k: pprof[k])
+            pq = profile_call(pr, "qkv", 5)
+            sec[name] = {"value": round(pfl / (pms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                         "ms_per_step": round(pms, 4),
+                         "frac_of_bf16_peak": round(pfl / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "kernel_us": {"gu": {k: round(v * 1e3, 1) for k, v in pprof.items()},
+                                       "qkv": {k: round(v * 1e3, 1) for k, v in pq.items()}}}
+            del pr
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+"""fusion_residual_add_amd: fused residual-add + norm + projection kernels for MI355X.
+
+Python binding over the C ABI of ``libfusedproj.so`` (include/fusedproj.h).
+This layer only marshals arguments: it checks that tensors are contiguous
+device tensors of the expected dtype, allocates output / workspace tensors with
+PyTorch when the caller does not pass them, and passes raw pointers and the
+current HIP stream to the library.  Every step of the computation runs in the
+library's HIP kernels; there is no other code path.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import FP_ACT, FP_NORM
+
+__all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_dequant_i8_bf16",
+           "workspace_bytes", "FusedProjError", "profile_start", "profile_stop", "library_path"]
+
+_DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
+       torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8}
+
+
+class FusedProjError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        self.status = status
+        name = _lib.STATUS[status] if 0 <= status < len(_lib.STATUS) else str(status)
+        super().__init__(f"{fn}: {name}: {msg}")
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        lib = _lib.load()
+        raise FusedProjError(fn, status, lib.fp_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, device=None, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.data_ptr()
+
+
+_WS: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def workspace_bytes(M: int, hidden: int, n_cols: int, act_dtype: torch.dtype,
+                    w_dtype: torch.dtype) -> int:
+    return int(_lib.load().fp_workspace_bytes(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype]))
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> Optional[torch.Tensor]:
+    """Per (device, stream) cached workspace: calls on one stream are ordered,
+    so they may share it."""
+    if nbytes == 0:
+        return None
+    key = (device.index, stream)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: Optional[torch.Tensor],
+                       w_qkv: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int, *,
+                       beta: Optional[torch.Tensor] = None, norm: str = "rms", eps: float = 1e-5,
+                       w_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                       write_h: bool = True, out_dtype: Optional[torch.dtype] = None,
+                       h_out: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                       k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """residual add + norm -> QKV projection (+bias) -> q [M,H,D], k/v [M,Hkv,D].
+
+    Returns (q, k, v, h_out) where h_out = rne(x + residual) (None when
+    ``write_h`` is False and no h_out tensor was passed)."""
+    lib = _lib.load()
+    _ptr(x, "x")
+    dev = x.device
+    M, K = x.shape
+    act = x.dtype
+    odt = out_dtype or act
+    wdt = w_qkv.dtype
+    Nw = (n_heads + 2 * n_kv_heads) * head_dim
+    if q is None:
+        q = torch.empty((M, n_heads, head_dim), dtype=odt, device=dev)
+    if k is None:
+        k = torch.empty((M, n_kv_heads, head_dim), dtype=odt, device=dev)
+    if v is None:
+        v = torch.empty((M, n_kv_heads, head_dim), dtype=odt, device=dev)
+    if h_out is None and write_h:
+        h_out = torch.empty_like(x)
+    stream = _stream(dev)
+    need = int(lib.fp_workspace_bytes(M, K, Nw, _DT[act], _DT[wdt]))
+    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    st = lib.fused_add_norm_qkv(
+        _ptr(x, "x", dev, act), _ptr(residual, "residual", dev, act), _ptr(h_out, "h_out", dev, act),
+        _ptr(gamma, "gamma", dev, act), _ptr(beta, "beta", dev, act), FP_NORM[norm], float(eps),
+        _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, torch.float32),
+        _ptr(bias, "bias", dev, act), _ptr(q, "q", dev, odt), _ptr(k, "k", dev, odt),
+        _ptr(v, "v", dev, odt), M, K, n_heads, n_kv_heads, head_dim,
+        _DT[act], _DT[wdt], _DT[odt],
+        None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
+    _check("fused_add_norm_qkv", st)
+    return q, k, v, h_out
+
+
+def fused_gateup_act(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: Optional[torch.Tensor],
+                     w: torch.Tensor, ffn: int, act: str = "swiglu", *,
+                     beta: Optional[torch.Tensor] = None, norm: str = "rms", eps: float = 1e-5,
+                     w_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                     out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                     h_out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """(residual add + norm ->) gate/up or up projection (+bias) -> activation; returns out [M, ffn]."""
+    lib = _lib.load()
+    _ptr(x, "x")
+    dev = x.device
+    M, K = x.shape
+    adt = x.dtype
+    odt = out_dtype or adt
+    wdt = w.dtype
+    Nw = 2 * ffn if act == "swiglu" else ffn
+    if out is None:
+        out = torch.empty((M, ffn), dtype=odt, device=dev)
+    stream = _stream(dev)
+    need = int(lib.fp_workspace_bytes(M, K, Nw, _DT[adt], _DT[wdt]))
+    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    st = lib.fused_gateup_act(
+        _ptr(x, "x", dev, adt), _ptr(residual, "residual", dev, adt), _ptr(h_out, "h_out", dev, adt),
+        _ptr(gamma, "gamma", dev, adt), _ptr(beta, "beta", dev, adt), FP_NORM[norm], float(eps),
+        _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, torch.float32), _ptr(bias, "bias", dev, adt),
+        _ptr(out, "out", dev, odt), M, K, ffn, FP_ACT[act], _DT[adt], _DT[wdt], _DT[odt],
+        None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
+    _check("fused_gateup_act", st)
+    return out
+
+
+def fused_dequant_i8_bf16(q: torch.Tensor, scale: torch.Tensor,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = _lib.load()
+    _ptr(q, "q")
+    dev = q.device
+    N, K = q.shape
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    st = lib.fused_dequant_i8_bf16(_ptr(q, "q", dev, torch.int8), _ptr(scale, "scale", dev, torch.float32),
+                                   _ptr(out, "out", dev, torch.bfloat16), N, K, _stream(dev))
+    _check("fused_dequant_i8_bf16", st)
+    return out
+
+
+def profile_start():
+    _check("fp_profile_start", _lib.load().fp_profile_start())
+
+
+def profile_stop() -> Dict[str, Tuple[int, float]]:
+    """{kernel name: (launches, total ms)} for the kernels enqueued since profile_start()."""
+    import ctypes
+    lib = _lib.load()
+    buf = (_lib.KernelTime * 64)()
+    n = ctypes.c_int(0)
+    _check("fp_profile_stop", lib.fp_profile_stop(buf, 64, ctypes.byref(n)))
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
+            for i in range(min(n.value, 64))}

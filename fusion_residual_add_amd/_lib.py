@@ -1,0 +1,62 @@
+"""ctypes declarations of libfusedproj.so (the C ABI in include/fusedproj.h).
+
+The library is loaded from this package directory only; there is no fallback
+of any kind: if it is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfusedproj.so")
+
+FP_F32, FP_F16, FP_BF16, FP_I8 = 0, 1, 2, 3
+FP_NORM = {"none": 0, "rms": 1, "layer": 2}
+FP_ACT = {"none": 0, "swiglu": 1, "gelu_tanh": 2}
+STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_ALIAS",
+          "FP_E_WORKSPACE", "FP_E_ARG", "FP_E_HIP"]
+
+# every symbol include/fusedproj.h declares
+EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_gateup_act",
+           "fused_dequant_i8_bf16", "fp_status_str", "fp_last_error",
+           "fp_profile_start", "fp_profile_stop"]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    lib.fp_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
+    lib.fp_workspace_bytes.restype = sz
+    lib.fused_add_norm_qkv.argtypes = [vp, vp, vp, vp, vp, ci, f32, vp, vp, vp, vp, vp, vp,
+                                       i64, i64, i64, i64, i64, ci, ci, ci, vp, sz, vp]
+    lib.fused_add_norm_qkv.restype = ci
+    lib.fused_gateup_act.argtypes = [vp, vp, vp, vp, vp, ci, f32, vp, vp, vp, vp,
+                                     i64, i64, i64, ci, ci, ci, ci, vp, sz, vp]
+    lib.fused_gateup_act.restype = ci
+    lib.fused_dequant_i8_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.fused_dequant_i8_bf16.restype = ci
+    lib.fp_status_str.argtypes = [ci]
+    lib.fp_status_str.restype = ctypes.c_char_p
+    lib.fp_last_error.argtypes = []
+    lib.fp_last_error.restype = ctypes.c_char_p
+    lib.fp_profile_start.argtypes = []
+    lib.fp_profile_start.restype = ci
+    lib.fp_profile_stop.argtypes = [ctypes.POINTER(KernelTime), ci, ctypes.POINTER(ci)]
+    lib.fp_profile_stop.restype = ci
+    if path == LIB_PATH:
+        _lib = lib
+    return lib

@@ -1,0 +1,440 @@
+// C-ABI layer of libfusedproj: argument validation (before any HIP call),
+// launch planning (tile family and split-K factor by token count), workspace
+// layout, kernel launches on the caller's stream, error text, and an optional
+// HIP-event profiler for benchmarks.
+#include "fusedproj.h"
+#include "fp_internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_err;
+
+fp_status fail(fp_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+int act_size(int dt) { return dt == FP_F32 ? 4 : dt == FP_I8 ? 1 : 2; }
+
+int act_code(fp_dtype d) {
+    return d == FP_F32 ? fp::ACT_F32 : d == FP_F16 ? fp::ACT_F16 : fp::ACT_BF16;
+}
+
+// ---------------------------------------------------------------------------
+// launch plan
+// ---------------------------------------------------------------------------
+struct Plan {
+    int tile = 0;
+    int tiles_m = 0, tiles_n = 0, splits = 1;
+    size_t stats_off = 0, ctr_off = 0, part_off = 0, total = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+long env_long(const char *name, long dflt) {
+    const char *s = getenv(name);
+    if (!s || !*s) return dflt;
+    return strtol(s, nullptr, 10);
+}
+
+// Decode token counts (M <= 64) use a narrow-M tile that streams 128 weight
+// rows per workgroup; larger M uses the 128x128 tile.  When there are too
+// few tiles to fill 256 CUs twice over, K is split and partial sums are
+// reduced by the last split to arrive (deterministically).
+Plan make_plan(int64_t M, int64_t K, int64_t Nw) {
+    Plan p;
+    if (M <= 16) p.tile = fp::TILE_DEC16;
+    else if (M <= 32) p.tile = fp::TILE_DEC32;
+    else if (M <= 64) p.tile = fp::TILE_DEC64;
+    else p.tile = fp::TILE_PF128;
+    long forced_tile = env_long("FUSEDPROJ_TILE", -1);
+    if (forced_tile >= 0 && forced_tile < fp::TILE_COUNT) {
+        fp::TileShape fs = fp::tile_shape((int)forced_tile);
+        if (forced_tile == fp::TILE_PF128 || M <= fs.bm) p.tile = (int)forced_tile;
+    }
+    const fp::TileShape ts = fp::tile_shape(p.tile);
+    p.tiles_m = (int)((M + ts.bm - 1) / ts.bm);
+    p.tiles_n = (int)((Nw + ts.bn - 1) / ts.bn);
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t KT = K / ts.bk;
+    int64_t s = 1;
+    const int64_t target = 512;
+    if (tiles > 0 && tiles < target) s = (target + tiles - 1) / tiles;
+    int64_t smax = KT / 4;
+    if (smax < 1) smax = 1;
+    if (s > smax) s = smax;
+    if (s > 16) s = 16;
+    long forced = env_long("FUSEDPROJ_SPLITS", 0);
+    if (forced > 0) s = forced < KT ? forced : KT;
+    p.splits = (int)s;
+
+    size_t off = 0;
+    p.stats_off = off;
+    off = align256(off + (size_t)M * 8);
+    p.ctr_off = off;
+    if (p.splits > 1) off = align256(off + (size_t)tiles * 4);
+    p.part_off = off;
+    if (p.splits > 1) off = align256(off + (size_t)tiles * p.splits * ts.bm * ts.bn * 4);
+    p.total = off;
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+bool overlaps(const Range &a, const Range &b) {
+    return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+fp_status check_alias(const std::vector<Range> &ins, const std::vector<Range> &outs) {
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r))
+                return fail(FP_E_ALIAS, "output '%s' overlaps input '%s'", outs[i].name, r.name);
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(FP_E_ALIAS, "output '%s' overlaps output '%s'", outs[i].name, outs[j].name);
+    }
+    return FP_OK;
+}
+
+Range rng(const char *name, const void *p, int64_t bytes) {
+    uintptr_t lo = (uintptr_t)p;
+    return Range{name, lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+fp_status check_dtypes(fp_dtype act, fp_dtype wdt, fp_dtype odt) {
+    if (act != FP_F32 && act != FP_F16 && act != FP_BF16)
+        return fail(FP_E_DTYPE, "act_dtype %d not in {F32, F16, BF16}", (int)act);
+    if (!(wdt == act || (wdt == FP_I8 && act == FP_BF16)))
+        return fail(FP_E_DTYPE, "w_dtype %d must equal act_dtype %d, or be I8 with BF16 activations",
+                    (int)wdt, (int)act);
+    if (!(odt == act || odt == FP_F32))
+        return fail(FP_E_DTYPE, "out_dtype %d must equal act_dtype or be F32", (int)odt);
+    return FP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// event profiler
+// ---------------------------------------------------------------------------
+struct ProfRec {
+    const char *name;
+    hipEvent_t a, b;
+};
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+
+struct ProfScope {
+    ProfRec rec{};
+    hipStream_t s;
+    bool on;
+    ProfScope(const char *name, hipStream_t st) : s(st), on(g_prof) {
+        if (!on) return;
+        rec.name = name;
+        if (hipEventCreate(&rec.a) != hipSuccess || hipEventCreate(&rec.b) != hipSuccess) { on = false; return; }
+        (void)hipEventRecord(rec.a, s);
+    }
+    ~ProfScope() {
+        if (!on) return;
+        (void)hipEventRecord(rec.b, s);
+        g_recs.push_back(rec);
+    }
+};
+
+fp_status hip_fail(hipError_t e, const char *what) {
+    return fail(FP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// the shared body of both projection entry points
+// ---------------------------------------------------------------------------
+struct Common {
+    const void *x, *residual;
+    void *h_out;
+    const void *gamma, *beta;
+    fp_norm norm;
+    float eps;
+    const void *w;
+    const float *w_scale;
+    const void *bias;
+    int64_t M, K, Nw;
+    fp_dtype act, wdt, odt;
+    void *ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+fp_status validate_common(const Common &c, const char *wname) {
+    if (c.M < 0) return fail(FP_E_SHAPE, "M = %lld is negative", (long long)c.M);
+    if (c.K <= 0 || c.K % 64 != 0)
+        return fail(FP_E_SHAPE, "hidden = %lld must be a positive multiple of 64", (long long)c.K);
+    if (c.norm != FP_NORM_NONE && c.norm != FP_NORM_RMS && c.norm != FP_NORM_LAYER)
+        return fail(FP_E_ARG, "norm = %d is not a fp_norm value", (int)c.norm);
+    fp_status st = check_dtypes(c.act, c.wdt, c.odt);
+    if (st != FP_OK) return st;
+    if (!c.x) return fail(FP_E_NULL, "x is NULL");
+    if (!c.w) return fail(FP_E_NULL, "%s is NULL", wname);
+    if (c.norm != FP_NORM_NONE && !c.gamma) return fail(FP_E_NULL, "gamma is NULL but norm is not NONE");
+    if (c.wdt == FP_I8 && !c.w_scale) return fail(FP_E_NULL, "w_scale is NULL for int8 weights");
+    if (!(c.eps >= 0.0f) || c.eps > 1e30f) return fail(FP_E_ARG, "eps must be a finite value >= 0");
+    const void *ptrs[] = {c.x, c.residual, c.h_out, c.gamma, c.beta, c.w, c.w_scale, c.bias, c.ws};
+    const char *names[] = {"x", "residual", "h_out", "gamma", "beta", wname, "w_scale", "bias", "workspace"};
+    for (int i = 0; i < 9; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(FP_E_ALIGN, "%s is not 16-byte aligned", names[i]);
+    return FP_OK;
+}
+
+void add_inputs(const Common &c, std::vector<Range> &ins, const char *wname) {
+    const int ea = act_size(c.act), ew = act_size(c.wdt);
+    ins.push_back(rng("x", c.x, c.M * c.K * ea));
+    if (c.residual) ins.push_back(rng("residual", c.residual, c.M * c.K * ea));
+    if (c.gamma && c.norm != FP_NORM_NONE) ins.push_back(rng("gamma", c.gamma, c.K * ea));
+    if (c.beta && c.norm == FP_NORM_LAYER) ins.push_back(rng("beta", c.beta, c.K * ea));
+    ins.push_back(rng(wname, c.w, c.Nw * c.K * ew));
+    if (c.w_scale && c.wdt == FP_I8) ins.push_back(rng("w_scale", c.w_scale, c.Nw * 4));
+    if (c.bias) ins.push_back(rng("bias", c.bias, c.Nw * ea));
+}
+
+fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
+    if (c.M == 0) return FP_OK;
+    char *ws = (char *)c.ws;
+    const int act = act_code(c.act);
+    float2 *stats = c.norm != FP_NORM_NONE ? (float2 *)(ws + plan.stats_off) : nullptr;
+    unsigned *ctr = plan.splits > 1 ? (unsigned *)(ws + plan.ctr_off) : nullptr;
+    const int n_ctr = plan.splits > 1 ? plan.tiles_m * plan.tiles_n : 0;
+
+    if (stats || c.h_out || n_ctr) {
+        fp::StatsArgs sa;
+        sa.x = c.x;
+        sa.res = c.residual;
+        sa.h_out = c.h_out;
+        sa.stats = stats;
+        sa.norm = (int)c.norm;
+        sa.eps = c.eps;
+        sa.M = c.M;
+        sa.K = c.K;
+        sa.counters = ctr;
+        sa.n_counters = n_ctr;
+        ProfScope ps(fp::stats_kernel_name(act), c.stream);
+        hipError_t e = fp::launch_stats(act, sa, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "stats_kernel launch");
+    }
+    pa.x = c.x;
+    pa.res = c.residual;
+    pa.stats = stats;
+    pa.gamma = c.gamma;
+    pa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
+    pa.norm = (int)c.norm;
+    pa.w = c.w;
+    pa.w_scale = c.w_scale;
+    pa.bias = c.bias;
+    pa.out_f32 = c.odt == FP_F32;
+    pa.M = c.M;
+    pa.K = c.K;
+    pa.Nw = c.Nw;
+    pa.tiles_m = plan.tiles_m;
+    pa.tiles_n = plan.tiles_n;
+    pa.splits = plan.splits;
+    pa.partials = plan.splits > 1 ? (float *)(ws + plan.part_off) : nullptr;
+    pa.counters = ctr;
+    const bool wi8 = c.wdt == FP_I8;
+    ProfScope ps(fp::proj_kernel_name(act, wi8, plan.tile, pa.epi), c.stream);
+    hipError_t e = fp::launch_proj(act, wi8, plan.tile, pa, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "proj_kernel launch");
+    return FP_OK;
+}
+
+fp_status check_workspace(const Common &c, const Plan &plan, std::vector<Range> &outs) {
+    if (c.M == 0) return FP_OK;
+    if (plan.total > 0) {
+        if (!c.ws) return fail(FP_E_WORKSPACE, "workspace is NULL; %zu bytes are needed", plan.total);
+        if (c.ws_bytes < plan.total)
+            return fail(FP_E_WORKSPACE, "workspace has %zu bytes; %zu are needed", c.ws_bytes, plan.total);
+        outs.push_back(rng("workspace", c.ws, (int64_t)plan.total));
+    }
+    return FP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
+                          fp_dtype w_dtype) {
+    if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0) return 0;
+    if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
+    if (M == 0) return 0;
+    return make_plan(M, hidden, n_cols).total;
+}
+
+fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, const void *gamma,
+                             const void *beta, fp_norm norm, float eps, const void *w_qkv,
+                             const float *w_scale, const void *bias, void *q, void *k, void *v,
+                             int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
+                             int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
+                             fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+    if (n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads != 0)
+        return fail(FP_E_SHAPE, "n_heads = %lld, n_kv_heads = %lld: both must be > 0 and n_heads a multiple of n_kv_heads",
+                    (long long)n_heads, (long long)n_kv_heads);
+    if (head_dim <= 0 || head_dim % 16 != 0)
+        return fail(FP_E_SHAPE, "head_dim = %lld must be a positive multiple of 16", (long long)head_dim);
+    Common c{x, residual, h_out, gamma, beta, norm, eps, w_qkv, w_scale, bias,
+             M, hidden, (n_heads + 2 * n_kv_heads) * head_dim, act_dtype, w_dtype, out_dtype,
+             workspace, workspace_bytes, (hipStream_t)hip_stream};
+    fp_status st = validate_common(c, "w_qkv");
+    if (st != FP_OK) return st;
+    if (!q || !k || !v) return fail(FP_E_NULL, "q, k and v must all be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+        return fail(FP_E_ALIGN, "q, k and v must be 16-byte aligned");
+    const int64_t nq = n_heads * head_dim, nkv = n_kv_heads * head_dim;
+    const int eo = act_size(out_dtype), ea = act_size(act_dtype);
+    std::vector<Range> ins, outs;
+    add_inputs(c, ins, "w_qkv");
+    if (h_out) outs.push_back(rng("h_out", h_out, M * hidden * ea));
+    outs.push_back(rng("q", q, M * nq * eo));
+    outs.push_back(rng("k", k, M * nkv * eo));
+    outs.push_back(rng("v", v, M * nkv * eo));
+    const Plan plan = make_plan(M, hidden, c.Nw);
+    st = check_workspace(c, plan, outs);
+    if (st != FP_OK) return st;
+    st = check_alias(ins, outs);
+    if (st != FP_OK) return st;
+
+    fp::ProjArgs pa{};
+    pa.epi = fp::EPI_QKV;
+    pa.out0 = q;
+    pa.out1 = k;
+    pa.out2 = v;
+    pa.nq = nq;
+    pa.nkv = nkv;
+    pa.F = c.Nw;
+    return run(c, plan, pa);
+}
+
+fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, const void *gamma,
+                           const void *beta, fp_norm norm, float eps, const void *w,
+                           const float *w_scale, const void *bias, void *out, int64_t M,
+                           int64_t hidden, int64_t ffn, fp_act act, fp_dtype act_dtype,
+                           fp_dtype w_dtype, fp_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, void *hip_stream) {
+    if (act != FP_ACT_NONE && act != FP_ACT_SWIGLU && act != FP_ACT_GELU_TANH)
+        return fail(FP_E_ARG, "act = %d is not a fp_act value", (int)act);
+    if (ffn <= 0 || ffn % 16 != 0)
+        return fail(FP_E_SHAPE, "ffn = %lld must be a positive multiple of 16", (long long)ffn);
+    const int64_t Nw = act == FP_ACT_SWIGLU ? 2 * ffn : ffn;
+    Common c{x, residual, h_out, gamma, beta, norm, eps, w, w_scale, bias,
+             M, hidden, Nw, act_dtype, w_dtype, out_dtype, workspace, workspace_bytes,
+             (hipStream_t)hip_stream};
+    fp_status st = validate_common(c, "w");
+    if (st != FP_OK) return st;
+    if (!out) return fail(FP_E_NULL, "out is NULL");
+    if (!aligned16(out)) return fail(FP_E_ALIGN, "out is not 16-byte aligned");
+    const int eo = act_size(out_dtype), ea = act_size(act_dtype);
+    std::vector<Range> ins, outs;
+    add_inputs(c, ins, "w");
+    if (h_out) outs.push_back(rng("h_out", h_out, M * hidden * ea));
+    outs.push_back(rng("out", out, M * ffn * eo));
+    const Plan plan = make_plan(M, hidden, Nw);
+    st = check_workspace(c, plan, outs);
+    if (st != FP_OK) return st;
+    st = check_alias(ins, outs);
+    if (st != FP_OK) return st;
+
+    fp::ProjArgs pa{};
+    pa.epi = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
+    pa.out0 = out;
+    pa.F = ffn;
+    return run(c, plan, pa);
+}
+
+fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_bf16, int64_t N,
+                                int64_t K, void *hip_stream) {
+    if (N < 0) return fail(FP_E_SHAPE, "N = %lld is negative", (long long)N);
+    if (K <= 0 || K % 16 != 0) return fail(FP_E_SHAPE, "K = %lld must be a positive multiple of 16", (long long)K);
+    if (!q || !scale || !out_bf16) return fail(FP_E_NULL, "q, scale and out_bf16 must be non-NULL");
+    if (!aligned16(q) || !aligned16(scale) || !aligned16(out_bf16))
+        return fail(FP_E_ALIGN, "q, scale and out_bf16 must be 16-byte aligned");
+    std::vector<Range> ins{rng("q", q, N * K), rng("scale", scale, N * 4)};
+    std::vector<Range> outs{rng("out_bf16", out_bf16, N * K * 2)};
+    fp_status st = check_alias(ins, outs);
+    if (st != FP_OK) return st;
+    if (N == 0) return FP_OK;
+    hipStream_t s = (hipStream_t)hip_stream;
+    ProfScope ps(fp::dequant_kernel_name(), s);
+    hipError_t e = fp::launch_dequant(q, scale, out_bf16, N, K, s);
+    if (e != hipSuccess) return hip_fail(e, "dequant_kernel launch");
+    return FP_OK;
+}
+
+const char *fp_status_str(fp_status s) {
+    switch (s) {
+    case FP_OK: return "ok";
+    case FP_E_NULL: return "null pointer";
+    case FP_E_SHAPE: return "invalid shape";
+    case FP_E_DTYPE: return "unsupported dtype combination";
+    case FP_E_ALIGN: return "misaligned pointer";
+    case FP_E_ALIAS: return "output overlaps another buffer";
+    case FP_E_WORKSPACE: return "workspace missing or too small";
+    case FP_E_ARG: return "invalid enum argument";
+    case FP_E_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *fp_last_error(void) { return g_err.c_str(); }
+
+fp_status fp_profile_start(void) {
+    g_recs.clear();
+    g_prof = true;
+    return FP_OK;
+}
+
+fp_status fp_profile_stop(fp_kernel_time *out, int capacity, int *count) {
+    g_prof = false;
+    std::vector<fp_kernel_time> agg;
+    fp_status st = FP_OK;
+    for (const ProfRec &r : g_recs) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == FP_OK) st = hip_fail(e, "profiler event");
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+        size_t i = 0;
+        for (; i < agg.size(); ++i)
+            if (strcmp(agg[i].name, r.name) == 0) break;
+        if (i == agg.size()) {
+            fp_kernel_time t{};
+            snprintf(t.name, sizeof t.name, "%s", r.name);
+            agg.push_back(t);
+        }
+        agg[i].launches += 1;
+        agg[i].total_ms += ms;
+    }
+    g_recs.clear();
+    if (count) *count = (int)agg.size();
+    for (int i = 0; out && i < capacity && i < (int)agg.size(); ++i) out[i] = agg[i];
+    return st;
+}
+
+}  // extern "C"

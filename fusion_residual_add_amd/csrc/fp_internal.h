@@ -1,0 +1,76 @@
+// Internal interface between the C-ABI layer (fp_api.cpp) and the HIP kernels
+// (fp_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp {
+
+enum ActT { ACT_F32 = 0, ACT_F16 = 1, ACT_BF16 = 2 };
+enum EpiKind { EPI_QKV = 0, EPI_SWIGLU = 1, EPI_GELU = 2, EPI_LINEAR = 3 };
+
+// Tile families the kernels are instantiated for.
+enum TileCfg {
+    TILE_DEC16 = 0,   // BM 16,  BN 128, BK 64, waves 1x4  (decode, M <= 16)
+    TILE_DEC32 = 1,   // BM 32,  BN 128, BK 64, waves 1x4  (decode, M <= 32)
+    TILE_DEC64 = 2,   // BM 64,  BN 128, BK 64, waves 1x4  (decode, M <= 64)
+    TILE_PF128 = 3,   // BM 128, BN 128, BK 64, waves 2x2  (prefill)
+    TILE_COUNT = 4
+};
+
+struct TileShape { int bm, bn, bk; };
+TileShape tile_shape(int cfg);
+
+// Everything one projection launch needs.
+struct ProjArgs {
+    // prologue inputs
+    const void *x;          // [M, K] act
+    const void *res;        // [M, K] act or null
+    const float2 *stats;    // [M] (mean, rstd) or null when norm == 0
+    const void *gamma;      // [K] act
+    const void *beta;       // [K] act or null
+    int norm;               // 0 none, 1 rms, 2 layer
+    // weights
+    const void *w;          // [Nw, K] act or int8
+    const float *w_scale;   // [Nw] (int8 only)
+    const void *bias;       // [Nw] act or null
+    // epilogue
+    int epi;                // EpiKind
+    int out_f32;            // 1: store fp32, 0: store act dtype
+    void *out0;             // q (QKV) or out
+    void *out1;             // k (QKV)
+    void *out2;             // v (QKV)
+    int64_t nq, nkv;        // QKV column split: [0,nq) q, [nq,nq+nkv) k, rest v
+    int64_t F;              // SwiGLU / GELU / linear output width
+    // sizes
+    int64_t M, K, Nw;       // Nw = weight rows
+    // tiling
+    int tiles_m, tiles_n, splits;
+    float *partials;        // split-K partial sums (splits > 1)
+    unsigned *counters;     // per-tile arrival counters (splits > 1)
+};
+
+struct StatsArgs {
+    const void *x, *res;
+    void *h_out;
+    float2 *stats;
+    int norm;
+    float eps;
+    int64_t M, K;
+    unsigned *counters;
+    int n_counters;
+};
+
+hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s);
+hipError_t launch_proj(int act, bool w_i8, int tile, const ProjArgs &a, hipStream_t s);
+hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,
+                          hipStream_t s);
+
+// names used by the event profiler
+const char *stats_kernel_name(int act);
+const char *proj_kernel_name(int act, bool w_i8, int tile, int epi);
+const char *dequant_kernel_name();
+
+}  // namespace fp

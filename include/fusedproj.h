@@ -1,0 +1,165 @@
+/*
+ * fusedproj — fused residual-add + norm + projection kernels for MI355X (gfx950).
+ *
+ * C ABI.  Every tensor is a plain pointer to HIP device memory owned by the
+ * caller, row-major and contiguous; every size is int64_t.  Nothing here
+ * allocates or frees device memory: scratch space is passed in as a
+ * caller-owned workspace whose size fp_workspace_bytes() reports.
+ *
+ * The operations follow the TensorRT-LLM pages this library is built from:
+ *  - "TensorRT-LLM 深度工程实践：从模型到生产级推理服务", §2.3 跨算子融合:
+ *    the LayerNorm + QKV projection fusion sketch (per-token mean and
+ *    variance, rsqrt(var + eps), gamma and beta, then the Q, K and V products
+ *    written straight out without an intermediate tensor) and the SwiGLU
+ *    sketch (SiLU of the gate product times the up product, one write);
+ *    §2.2 图构建与算子映射: the QKV projection is one matmul followed by a
+ *    reshape into GQA head groups;
+ *  - "2. TensorRT-LLM 简介", 核心原理: residual + LayerNorm fusion, QKV
+ *    fusion, per-op precision matching;
+ *  - "TRT-LLM deep dive" (lib.uml.com.cn), 构建阶段详解 §3 Layer Fusion
+ *    figure and 面试视角: Add / Bias / LayerNorm / GELU and LayerNorm +
+ *    Linear + GELU each collapsed into a single kernel.
+ *
+ * Shared conventions
+ *  - Token rows are independent; M (tokens) may be any value >= 0, M == 0 is
+ *    a no-op that returns FP_OK.
+ *  - hidden (K) must be a positive multiple of 64.
+ *  - Weights are [N, K] with K contiguous (the nn.Linear weight layout).
+ *  - Residual add: h = x + residual, formed in fp32 (exact for 16-bit inputs).
+ *    residual may be NULL (h = x).  If h_out is not NULL it receives
+ *    round-to-nearest-even(h) in act_dtype (the residual stream for the next
+ *    block); h_out must not alias x or residual.
+ *  - Norm on h: FP_NORM_RMS   n = h / sqrt(mean(h^2) + eps) * gamma
+ *               FP_NORM_LAYER n = (h - mean) / sqrt(var + eps) * gamma + beta
+ *                             (biased variance; beta may be NULL = 0)
+ *               FP_NORM_NONE  n = h (gamma and beta ignored)
+ *    Row statistics are fp32.  n is rounded to act_dtype (RNE) and fed to the
+ *    matrix cores; it never goes to memory.
+ *  - Product: fp32 accumulation of n * W^T.
+ *  - Int8 weights (w_dtype FP_I8, act_dtype FP_BF16 only): each element is
+ *    dequantised as bf16_rne(f32_rne(q * w_scale[row])), bit-exactly the
+ *    result of fused_dequant_i8_bf16.
+ *  - Dtypes: act_dtype in {F32, F16, BF16}; w_dtype == act_dtype, or FP_I8
+ *    with act_dtype FP_BF16; out_dtype == act_dtype or FP_F32.  gamma, beta
+ *    and bias are act_dtype; w_scale is fp32.
+ *  - Every pointer must be 16-byte aligned.  No output range may overlap an
+ *    input range, another output, or the workspace.
+ *  - Execution is asynchronous on hip_stream (NULL = the default stream);
+ *    the call returns once the kernels are enqueued.  Device faults surface at
+ *    the caller's next synchronisation.
+ *  - Errors: every argument is validated before any HIP call; on any status
+ *    other than FP_OK nothing has been enqueued and no memory was touched,
+ *    except FP_E_HIP (a launch failed; fp_last_error() has the HIP text).
+ *  - The workspace holds per-row statistics, split-K partial sums and
+ *    arrival counters.  Its contents on entry do not matter.  Two calls that
+ *    run concurrently must not share a workspace.
+ *  - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef FUSEDPROJ_H
+#define FUSEDPROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3 } fp_dtype;
+typedef enum { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
+typedef enum { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
+typedef enum {
+    FP_OK = 0,
+    FP_E_NULL = 1,      /* a required pointer is NULL */
+    FP_E_SHAPE = 2,     /* a size is negative, zero where it must not be, or not a required multiple */
+    FP_E_DTYPE = 3,     /* dtype combination not supported */
+    FP_E_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+    FP_E_ALIAS = 5,     /* an output overlaps an input, another output or the workspace */
+    FP_E_WORKSPACE = 6, /* workspace missing or smaller than fp_workspace_bytes() */
+    FP_E_ARG = 7,       /* an enum value is out of range */
+    FP_E_HIP = 8        /* a HIP call failed; see fp_last_error() */
+} fp_status;
+
+/* Bytes of workspace a call with these sizes needs.  n_cols is the number of
+ * weight rows of the projection: (n_heads + 2 n_kv_heads) * head_dim for
+ * fused_add_norm_qkv, 2 * ffn for fused_gateup_act with FP_ACT_SWIGLU, ffn
+ * otherwise.  Returns 0 for invalid sizes or dtypes. */
+size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols,
+                          fp_dtype act_dtype, fp_dtype w_dtype);
+
+/* Residual add + norm -> QKV projection (+ bias) -> GQA split.
+ * ("TensorRT-LLM 深度工程实践…", §2.3 LayerNorm + QKV fusion sketch; §2.2.)
+ *  x, residual : [M, hidden] act_dtype (residual may be NULL)
+ *  h_out       : [M, hidden] act_dtype or NULL
+ *  gamma, beta : [hidden] act_dtype (gamma required unless FP_NORM_NONE)
+ *  w_qkv       : [(H + 2 Hkv) * D, hidden], rows = Q heads, then K, then V
+ *  w_scale     : [(H + 2 Hkv) * D] fp32, required iff w_dtype == FP_I8
+ *  bias        : [(H + 2 Hkv) * D] act_dtype or NULL
+ *  q           : [M, H, D]   out_dtype, token-major
+ *  k, v        : [M, Hkv, D] out_dtype, token-major
+ *  Requires n_heads, n_kv_heads > 0, n_heads % n_kv_heads == 0,
+ *  head_dim a positive multiple of 16. */
+fp_status fused_add_norm_qkv(
+    const void *x, const void *residual, void *h_out,
+    const void *gamma, const void *beta, fp_norm norm, float eps,
+    const void *w_qkv, const float *w_scale, const void *bias,
+    void *q, void *k, void *v,
+    int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+    fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
+    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* (Residual add + norm ->) gate/up or up projection (+ bias) -> activation.
+ * ("TensorRT-LLM 深度工程实践…", §2.3 SwiGLU fusion sketch; "TRT-LLM deep
+ * dive", Layer Fusion figure / LayerNorm + Linear + GELU.)
+ *  act FP_ACT_SWIGLU   : w is [2 ffn, hidden], rows [0, ffn) gate and
+ *                        [ffn, 2 ffn) up; out[m, j] = SiLU(g) * u with
+ *                        g = acc[m, j] + bias[j], u = acc[m, ffn + j] + bias[ffn + j],
+ *                        SiLU(g) = g / (1 + exp(-g))
+ *  act FP_ACT_GELU_TANH: w is [ffn, hidden]; out = GELU_tanh(acc + bias),
+ *                        GELU_tanh(y) = 0.5 y (1 + tanh(sqrt(2/pi)(y + 0.044715 y^3)))
+ *  act FP_ACT_NONE     : w is [ffn, hidden]; out = acc + bias
+ *  out : [M, ffn] out_dtype.  bias (act_dtype, length = rows of w) may be NULL.
+ *  Requires ffn a positive multiple of 16.  Other arguments as above;
+ *  with FP_NORM_NONE and residual NULL the input is x as given. */
+fp_status fused_gateup_act(
+    const void *x, const void *residual, void *h_out,
+    const void *gamma, const void *beta, fp_norm norm, float eps,
+    const void *w, const float *w_scale, const void *bias, void *out,
+    int64_t M, int64_t hidden, int64_t ffn, fp_act act,
+    fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
+    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* int8 per-output-row weight dequantisation to bf16, the same device
+ * function the projection kernels use in their weight loader:
+ * out[j, k] = bf16_rne(f32_rne(q[j, k] * scale[j])).
+ *  q : [N, K] int8, scale : [N] fp32, out_bf16 : [N, K] bf16.
+ *  Requires K a positive multiple of 16, N >= 0. */
+fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_bf16,
+                                int64_t N, int64_t K, void *hip_stream);
+
+/* Static text for a status code. */
+const char *fp_status_str(fp_status s);
+
+/* Message for the last non-FP_OK status returned on this host thread. */
+const char *fp_last_error(void);
+
+/* Per-kernel timing with HIP events, for benchmarks.  Between
+ * fp_profile_start() and fp_profile_stop() every kernel the library enqueues
+ * is bracketed by two events on its stream.  fp_profile_stop() synchronises
+ * those events and fills up to `capacity` records (one per kernel name) with
+ * the number of launches and their summed duration; *count receives the
+ * number of names.  Recording is per process and not thread-safe. */
+typedef struct {
+    char name[64];
+    int64_t launches;
+    double total_ms;
+} fp_kernel_time;
+
+fp_status fp_profile_start(void);
+fp_status fp_profile_stop(fp_kernel_time *out, int capacity, int *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSEDPROJ_H */

@@ -1,0 +1,150 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every symbol
+the header declares, sizes workspaces, and rejects bad arguments before any
+HIP call (so these calls never touch memory; the pointers below are fake)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fusion_residual_add_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fusedproj.h")
+
+FAKE = 0x10000           # 16-byte aligned, never dereferenced
+F32, F16, BF16, I8 = 0, 1, 2, 3
+
+
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = lib()
+    for s in range(len(_lib.STATUS)):
+        assert L.fp_status_str(s)
+    assert L.fp_status_str(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    L = lib()
+    assert L.fp_workspace_bytes(0, 4096, 6144, BF16, BF16) == 0
+    assert L.fp_workspace_bytes(32, 4095, 6144, BF16, BF16) == 0      # hidden not multiple of 64
+    assert L.fp_workspace_bytes(32, 4096, 6144, F16, I8) == 0         # int8 needs bf16 activations
+    dec = L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16)
+    assert dec >= 32 * 8 and dec % 256 == 0
+    big = L.fp_workspace_bytes(16384, 4096, 12288, BF16, BF16)
+    assert big >= 16384 * 8
+
+
+def qkv(**kw):
+    a = dict(x=FAKE, residual=FAKE + 0x1000000, h_out=None, gamma=FAKE + 0x2000000, beta=None,
+             norm=1, eps=1e-5, w=FAKE + 0x3000000, w_scale=None, bias=None,
+             q=FAKE + 0x40000000, k=FAKE + 0x50000000, v=FAKE + 0x60000000, M=0, hidden=4096,
+             H=32, Hkv=8, D=128, act=BF16, wdt=BF16, odt=BF16, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    st = lib().fused_add_norm_qkv(a["x"], a["residual"], a["h_out"], a["gamma"], a["beta"], a["norm"],
+                                  a["eps"], a["w"], a["w_scale"], a["bias"], a["q"], a["k"], a["v"],
+                                  a["M"], a["hidden"], a["H"], a["Hkv"], a["D"], a["act"], a["wdt"],
+                                  a["odt"], a["ws"], a["ws_bytes"], a["stream"])
+    return _lib.STATUS[st], lib().fp_last_error().decode()
+
+
+def gu(**kw):
+    a = dict(x=FAKE, residual=None, h_out=None, gamma=FAKE + 0x2000000, beta=None, norm=1, eps=1e-5,
+             w=FAKE + 0x3000000, w_scale=None, bias=None, out=FAKE + 0x40000000, M=0, hidden=4096,
+             ffn=14336, act=1, adt=BF16, wdt=BF16, odt=BF16, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    st = lib().fused_gateup_act(a["x"], a["residual"], a["h_out"], a["gamma"], a["beta"], a["norm"],
+                                a["eps"], a["w"], a["w_scale"], a["bias"], a["out"], a["M"], a["hidden"],
+                                a["ffn"], a["act"], a["adt"], a["wdt"], a["odt"], a["ws"], a["ws_bytes"],
+                                a["stream"])
+    return _lib.STATUS[st], lib().fp_last_error().decode()
+
+
+def test_m_zero_is_a_noop():
+    assert qkv(M=0)[0] == "FP_OK"
+    assert gu(M=0)[0] == "FP_OK"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), "FP_E_NULL"),
+    (dict(w=None), "FP_E_NULL"),
+    (dict(gamma=None), "FP_E_NULL"),
+    (dict(q=None), "FP_E_NULL"),
+    (dict(wdt=I8), "FP_E_NULL"),                       # int8 without scales
+    (dict(M=-1), "FP_E_SHAPE"),
+    (dict(hidden=4000), "FP_E_SHAPE"),
+    (dict(hidden=0), "FP_E_SHAPE"),
+    (dict(H=30, Hkv=8), "FP_E_SHAPE"),
+    (dict(Hkv=0), "FP_E_SHAPE"),
+    (dict(D=100), "FP_E_SHAPE"),
+    (dict(act=I8), "FP_E_DTYPE"),
+    (dict(act=F16, wdt=BF16), "FP_E_DTYPE"),
+    (dict(act=F16, wdt=I8, w_scale=FAKE + 0x70000000), "FP_E_DTYPE"),
+    (dict(odt=F16), "FP_E_DTYPE"),
+    (dict(norm=7), "FP_E_ARG"),
+    (dict(eps=-1.0), "FP_E_ARG"),
+    (dict(x=FAKE + 8), "FP_E_ALIGN"),
+    (dict(q=FAKE + 0x40000004), "FP_E_ALIGN"),
+    (dict(M=32, ws=None), "FP_E_WORKSPACE"),
+    (dict(M=32, ws=FAKE + 0x7000000, ws_bytes=16), "FP_E_WORKSPACE"),
+    (dict(M=32, ws=FAKE + 0x7000000, ws_bytes=1 << 30, q=FAKE + 0x3000000), "FP_E_ALIAS"),   # q over w
+    (dict(M=32, ws=FAKE + 0x7000000, ws_bytes=1 << 30, k=FAKE + 0x40000000), "FP_E_ALIAS"),  # k over q
+    (dict(M=32, ws=FAKE + 0x7000000, ws_bytes=1 << 30, h_out=FAKE + 0x1000000), "FP_E_ALIAS"),  # in place
+    (dict(M=32, ws=FAKE + 0x40000000, ws_bytes=1 << 30), "FP_E_ALIAS"),  # workspace over q
+])
+def test_qkv_rejects(kw, status):
+    got, msg = qkv(**kw)
+    assert got == status, msg
+    assert msg
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), "FP_E_NULL"),
+    (dict(ffn=1000), "FP_E_SHAPE"),
+    (dict(ffn=0), "FP_E_SHAPE"),
+    (dict(act=9), "FP_E_ARG"),
+    (dict(adt=F32, wdt=F16), "FP_E_DTYPE"),
+    (dict(out=FAKE + 0x40000002), "FP_E_ALIGN"),
+    (dict(M=4, ws=FAKE + 0x7000000, ws_bytes=1 << 30, out=FAKE + 0x2000000 - 64), "FP_E_ALIAS"),  # over gamma
+])
+def test_gateup_rejects(kw, status):
+    got, msg = gu(**kw)
+    assert got == status, msg
+
+
+def test_dequant_rejects():
+    L = lib()
+    assert _lib.STATUS[L.fused_dequant_i8_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 0, 64, None)] == "FP_OK"
+    assert _lib.STATUS[L.fused_dequant_i8_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 60, None)] == "FP_E_SHAPE"
+    assert _lib.STATUS[L.fused_dequant_i8_bf16(None, FAKE + 0x1000000, FAKE + 0x2000000, 4, 64, None)] == "FP_E_NULL"
+    assert _lib.STATUS[L.fused_dequant_i8_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x80, 4, 64, None)] == "FP_E_ALIAS"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import fusion_residual_add_amd as fra
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fra.fused_gateup_act(x, None, torch.ones(64, dtype=torch.bfloat16),
+                             torch.zeros(32, 64, dtype=torch.bfloat16), 16, "swiglu")
