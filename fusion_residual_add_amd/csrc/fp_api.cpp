@@ -191,7 +191,7 @@ fp_status validate_common(const Common &c, const char *wname) {
         return fail(FP_E_ARG, "norm = %d is not a fp_norm value", (int)c.norm);
     fp_status st = check_dtypes(c.act, c.wdt, c.odt);
     if (st != FP_OK) return st;
-    if (!c.x) return fail(FP_E_NULL, "x is NULL");
+    if (!c.x && c.M > 0) return fail(FP_E_NULL, "x is NULL");
     if (!c.w) return fail(FP_E_NULL, "%s is NULL", wname);
     if (c.norm != FP_NORM_NONE && !c.gamma) return fail(FP_E_NULL, "gamma is NULL but norm is not NONE");
     if (c.wdt == FP_I8 && !c.w_scale) return fail(FP_E_NULL, "w_scale is NULL for int8 weights");
@@ -303,7 +303,7 @@ fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, c
              workspace, workspace_bytes, (hipStream_t)hip_stream};
     fp_status st = validate_common(c, "w_qkv");
     if (st != FP_OK) return st;
-    if (!q || !k || !v) return fail(FP_E_NULL, "q, k and v must all be non-NULL");
+    if ((!q || !k || !v) && M > 0) return fail(FP_E_NULL, "q, k and v must all be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v))
         return fail(FP_E_ALIGN, "q, k and v must be 16-byte aligned");
     const int64_t nq = n_heads * head_dim, nkv = n_kv_heads * head_dim;
@@ -347,7 +347,7 @@ fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, con
              (hipStream_t)hip_stream};
     fp_status st = validate_common(c, "w");
     if (st != FP_OK) return st;
-    if (!out) return fail(FP_E_NULL, "out is NULL");
+    if (!out && M > 0) return fail(FP_E_NULL, "out is NULL");
     if (!aligned16(out)) return fail(FP_E_ALIGN, "out is not 16-byte aligned");
     const int eo = act_size(out_dtype), ea = act_size(act_dtype);
     std::vector<Range> ins, outs;

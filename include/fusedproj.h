@@ -22,7 +22,8 @@
  *
  * Shared conventions
  *  - Token rows are independent; M (tokens) may be any value >= 0, M == 0 is
- *    a no-op that returns FP_OK.
+ *    a no-op that returns FP_OK (the per-token pointers x, residual, h_out and
+ *    the outputs may then be NULL).
  *  - hidden (K) must be a positive multiple of 64.
  *  - Weights are [N, K] with K contiguous (the nn.Linear weight layout).
  *  - Residual add: h = x + residual, formed in fp32 (exact for 16-bit inputs).

@@ -87,10 +87,10 @@ def test_m_zero_is_a_noop():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(x=None), "FP_E_NULL"),
+    (dict(M=1, x=None), "FP_E_NULL"),
     (dict(w=None), "FP_E_NULL"),
     (dict(gamma=None), "FP_E_NULL"),
-    (dict(q=None), "FP_E_NULL"),
+    (dict(M=1, q=None), "FP_E_NULL"),
     (dict(wdt=I8), "FP_E_NULL"),                       # int8 without scales
     (dict(M=-1), "FP_E_SHAPE"),
     (dict(hidden=4000), "FP_E_SHAPE"),
@@ -120,7 +120,7 @@ def test_qkv_rejects(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(out=None), "FP_E_NULL"),
+    (dict(M=1, out=None), "FP_E_NULL"),
     (dict(ffn=1000), "FP_E_SHAPE"),
     (dict(ffn=0), "FP_E_SHAPE"),
     (dict(act=9), "FP_E_ARG"),
