@@ -35,9 +35,10 @@ MALL_BYTES = 256 << 20
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("fusion_residual_add_amd/csrc/fp_kernels.hip", "fusion_residual_add_amd/csrc/fp_api.cpp",
-              "fusion_residual_add_amd/csrc/fp_internal.h"):
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    csrc = os.path.join(ROOT, "fusion_residual_add_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 

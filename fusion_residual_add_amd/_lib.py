@@ -31,10 +31,13 @@ class KernelTime(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
+def load(path: str = None):
+    """Load (once) and declare the library; ``path`` loads another build without caching it."""
     global _lib
-    if _lib is not None and path == LIB_PATH:
-        return _lib
+    if path is None:
+        if _lib is not None:
+            return _lib
+        path = LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(path)

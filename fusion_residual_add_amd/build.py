@@ -1,29 +1,49 @@
-"""Compile the HIP library (libfusedproj.so) for gfx950 with hipcc, in-tree."""
+"""Compile the HIP library (libfusedproj.so) for gfx950 with hipcc, in-tree.
+
+Each source is compiled to an object in parallel (fusion_residual_add_amd/_build/),
+then the objects are linked into fusion_residual_add_amd/libfusedproj.so.
+"""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "fp_kernels.hip"), os.path.join(PKG, "csrc", "fp_api.cpp")]
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = ["fp_rows.hip", "fp_tiled.hip", "fp_stream.hip", "fp_stream_bf16.hip", "fp_stream_f16.hip",
+           "fp_stream_i8.hip", "fp_api.cpp"]
 LIB = os.path.join(PKG, "libfusedproj.so")
+OBJDIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed-fp32 VALU forms
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-I" + os.path.join(ROOT, "include"),
+    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _compile(src: str) -> str:
+    obj = os.path.join(OBJDIR, src + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed on {src}:\n" + res.stdout + res.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(" ".join(cmd))
     os.replace(tmp, LIB)

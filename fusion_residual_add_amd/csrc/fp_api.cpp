@@ -36,8 +36,11 @@ int act_code(fp_dtype d) {
 // launch plan
 // ---------------------------------------------------------------------------
 struct Plan {
-    int tile = 0;
+    int family = 0;           // 0 tiled, 1 stream
+    int tile = 0;             // tiled: TileCfg
+    fp::StreamCfg sc{1, 2, 8};
     int tiles_m = 0, tiles_n = 0, splits = 1;
+    int64_t tile_elems = 0;   // accumulators per tile (split-K partial size)
     size_t stats_off = 0, ctr_off = 0, part_off = 0, total = 0;
 };
 
@@ -49,35 +52,59 @@ long env_long(const char *name, long dflt) {
     return strtol(s, nullptr, 10);
 }
 
-// Decode token counts (M <= 64) use a narrow-M tile that streams 128 weight
-// rows per workgroup; larger M uses the 128x128 tile.  When there are too
-// few tiles to fill 256 CUs twice over, K is split and partial sums are
-// reduced by the last split to arrive (deterministically).
-Plan make_plan(int64_t M, int64_t K, int64_t Nw) {
+// Decode token counts (M <= 64, 16-bit activations) use the weight-streaming
+// kernel; everything else the tiled kernel.  When a grid would hold too few
+// workgroups to keep enough weight bytes in flight, K is split and the
+// partial sums are reduced by the last split to arrive, in split order.
+// FUSEDPROJ_* environment variables override the choices (for tuning sweeps);
+// the workspace query and the call read them alike.
+Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
     Plan p;
-    if (M <= 16) p.tile = fp::TILE_DEC16;
-    else if (M <= 32) p.tile = fp::TILE_DEC32;
-    else if (M <= 64) p.tile = fp::TILE_DEC64;
-    else p.tile = fp::TILE_PF128;
-    long forced_tile = env_long("FUSEDPROJ_TILE", -1);
-    if (forced_tile >= 0 && forced_tile < fp::TILE_COUNT) {
-        fp::TileShape fs = fp::tile_shape((int)forced_tile);
-        if (forced_tile == fp::TILE_PF128 || M <= fs.bm) p.tile = (int)forced_tile;
+    const int u = 8;
+    const bool stream_ok = act != FP_F32 && M <= 64 && K % (32 * u) == 0 &&
+                           env_long("FUSEDPROJ_NO_STREAM", 0) == 0;
+    int64_t tiles, ksteps, target;
+    if (stream_ok) {
+        p.family = 1;
+        p.sc.mf = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+        p.sc.nr = swiglu ? 2 : (int)(env_long("FUSEDPROJ_STREAM_NR", 2) == 1 ? 1 : 2);
+        p.sc.u = u;
+        const int nb = 64 * p.sc.nr;
+        p.tiles_m = 1;
+        p.tiles_n = (int)((Nw + nb - 1) / nb);
+        p.tile_elems = (int64_t)16 * p.sc.mf * nb;
+        tiles = p.tiles_n;
+        ksteps = K / (32 * u);
+        target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
+    } else {
+        if (M <= 16) p.tile = fp::TILE_DEC16;
+        else if (M <= 32) p.tile = fp::TILE_DEC32;
+        else if (M <= 64) p.tile = fp::TILE_DEC64;
+        else p.tile = fp::TILE_PF128;
+        const fp::TileShape ts = fp::tile_shape(p.tile);
+        p.tiles_m = (int)((M + ts.bm - 1) / ts.bm);
+        p.tiles_n = (int)((Nw + ts.bn - 1) / ts.bn);
+        p.tile_elems = (int64_t)ts.bm * ts.bn;
+        tiles = (int64_t)p.tiles_m * p.tiles_n;
+        ksteps = K / ts.bk;
+        target = 512;
     }
-    const fp::TileShape ts = fp::tile_shape(p.tile);
-    p.tiles_m = (int)((M + ts.bm - 1) / ts.bm);
-    p.tiles_n = (int)((Nw + ts.bn - 1) / ts.bn);
-    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-    const int64_t KT = K / ts.bk;
     int64_t s = 1;
-    const int64_t target = 512;
-    if (tiles > 0 && tiles < target) s = (target + tiles - 1) / tiles;
-    int64_t smax = KT / 4;
+    if (p.family == 1) {
+        // measured on MI355X (decode shapes, K 4096 / 8192): one workgroup per
+        // CU is the sweet spot -- extra splits cost partial-sum traffic and a
+        // tail, too few workgroups leave HBM bandwidth unused
+        if (tiles > 0 && tiles < target) s = target / tiles;
+    } else if (tiles > 0 && tiles < target) {
+        s = (target + tiles - 1) / tiles;
+    }
+    int64_t smax = p.family == 1 ? ksteps / 2 : ksteps / 4;
     if (smax < 1) smax = 1;
     if (s > smax) s = smax;
     if (s > 16) s = 16;
-    long forced = env_long("FUSEDPROJ_SPLITS", 0);
-    if (forced > 0) s = forced < KT ? forced : KT;
+    if (s < 1) s = 1;
+    const long forced = env_long("FUSEDPROJ_SPLITS", 0);
+    if (forced > 0) s = forced < ksteps ? forced : ksteps;
     p.splits = (int)s;
 
     size_t off = 0;
@@ -86,7 +113,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw) {
     p.ctr_off = off;
     if (p.splits > 1) off = align256(off + (size_t)tiles * 4);
     p.part_off = off;
-    if (p.splits > 1) off = align256(off + (size_t)tiles * p.splits * ts.bm * ts.bn * 4);
+    if (p.splits > 1) off = align256(off + (size_t)tiles * p.splits * p.tile_elems * 4);
     p.total = off;
     return p;
 }
@@ -257,9 +284,15 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.partials = plan.splits > 1 ? (float *)(ws + plan.part_off) : nullptr;
     pa.counters = ctr;
     const bool wi8 = c.wdt == FP_I8;
-    ProfScope ps(fp::proj_kernel_name(act, wi8, plan.tile, pa.epi), c.stream);
-    hipError_t e = fp::launch_proj(act, wi8, plan.tile, pa, c.stream);
-    if (e != hipSuccess) return hip_fail(e, "proj_kernel launch");
+    if (plan.family == 1) {
+        ProfScope ps(fp::stream_kernel_name(act, wi8, plan.sc, pa.epi), c.stream);
+        hipError_t e = fp::launch_stream(act, wi8, plan.sc, pa, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
+    } else {
+        ProfScope ps(fp::proj_kernel_name(act, wi8, plan.tile, pa.epi), c.stream);
+        hipError_t e = fp::launch_tiled(act, wi8, plan.tile, pa, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "proj_kernel launch");
+    }
     return FP_OK;
 }
 
@@ -283,7 +316,9 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype ac
     if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0) return 0;
     if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
     if (M == 0) return 0;
-    return make_plan(M, hidden, n_cols).total;
+    const size_t a = make_plan(M, hidden, n_cols, act_dtype, false).total;
+    const size_t b = make_plan(M, hidden, n_cols, act_dtype, true).total;
+    return a > b ? a : b;
 }
 
 fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, const void *gamma,
@@ -314,7 +349,7 @@ fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, c
     outs.push_back(rng("q", q, M * nq * eo));
     outs.push_back(rng("k", k, M * nkv * eo));
     outs.push_back(rng("v", v, M * nkv * eo));
-    const Plan plan = make_plan(M, hidden, c.Nw);
+    const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, false);
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);
@@ -354,7 +389,7 @@ fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, con
     add_inputs(c, ins, "w");
     if (h_out) outs.push_back(rng("h_out", h_out, M * hidden * ea));
     outs.push_back(rng("out", out, M * ffn * eo));
-    const Plan plan = make_plan(M, hidden, Nw);
+    const Plan plan = make_plan(M, hidden, Nw, act_dtype, act == FP_ACT_SWIGLU);
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);

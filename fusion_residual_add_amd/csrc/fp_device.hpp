@@ -1,0 +1,255 @@
+// Device-side building blocks shared by the kernels of libfusedproj (gfx950):
+// vector types, round-to-nearest-even conversions, the int8 dequantisation,
+// activation-dtype traits (unpack / pack / MFMA), wave reductions, the XCD-aware
+// workgroup remap, the activations, the epilogue stores and the deterministic
+// split-K reduction.
+#pragma once
+
+#include "fp_internal.h"
+
+namespace fp {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// ---------------------------------------------------------------------------
+// scalar conversions (round-to-nearest-even for every narrowing)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ unsigned to_bf16(float f) {
+    return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)f);
+}
+__device__ __forceinline__ float f16lo(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+__device__ __forceinline__ unsigned to_f16(float f) {
+    return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)f);
+}
+
+// int8 weight dequantisation: bf16_rne(f32_rne(q * s)).  The single definition
+// used by both the projection's weight loader and dequant_kernel.
+__device__ __forceinline__ unsigned dequant_i8_bf16(int q, float s) {
+    return to_bf16((float)q * s);
+}
+
+// 16 int8 values (one 16-byte load) -> 16 bf16 values (two 16-byte vectors).
+__device__ __forceinline__ void dequant16(u32x4 qv, float s, u32x4 &lo, u32x4 &hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        unsigned w = qv[i];
+        int q0 = (int)(w << 24) >> 24, q1 = (int)(w << 16) >> 24;
+        int q2 = (int)(w << 8) >> 24, q3 = (int)w >> 24;
+        unsigned p0 = dequant_i8_bf16(q0, s) | (dequant_i8_bf16(q1, s) << 16);
+        unsigned p1 = dequant_i8_bf16(q2, s) | (dequant_i8_bf16(q3, s) << 16);
+        if (i < 2) { lo[2 * i] = p0; lo[2 * i + 1] = p1; }
+        else       { hi[2 * (i - 2)] = p0; hi[2 * (i - 2) + 1] = p1; }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// activation-dtype traits
+// ---------------------------------------------------------------------------
+template <int ACT> struct Act;
+
+template <> struct Act<ACT_BF16> {
+    using S = unsigned short;            // storage element
+    using Frag = u32x4;                  // one lane's MFMA operand (8 x bf16)
+    static constexpr int VE = 8;         // elements per 16-byte vector
+    static constexpr int KM = 32;        // K per MFMA
+    __device__ static void unpack(u32x4 v, float *f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[2 * i] = bf16lo(v[i]); f[2 * i + 1] = bf16hi(v[i]); }
+    }
+    __device__ static u32x4 pack(const float *f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = to_bf16(f[2 * i]) | (to_bf16(f[2 * i + 1]) << 16);
+        return v;
+    }
+    __device__ static float ld(const void *p, int64_t i) {
+        return __uint_as_float((unsigned)((const unsigned short *)p)[i] << 16);
+    }
+    __device__ static void st(void *p, int64_t i, float v) {
+        ((unsigned short *)p)[i] = (unsigned short)to_bf16(v);
+    }
+    __device__ static f32x4 mfma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <> struct Act<ACT_F16> {
+    using S = unsigned short;
+    using Frag = u32x4;
+    static constexpr int VE = 8;
+    static constexpr int KM = 32;
+    __device__ static void unpack(u32x4 v, float *f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[2 * i] = f16lo(v[i]); f[2 * i + 1] = f16hi(v[i]); }
+    }
+    __device__ static u32x4 pack(const float *f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = to_f16(f[2 * i]) | (to_f16(f[2 * i + 1]) << 16);
+        return v;
+    }
+    __device__ static float ld(const void *p, int64_t i) {
+        return (float)__builtin_bit_cast(_Float16, ((const unsigned short *)p)[i]);
+    }
+    __device__ static void st(void *p, int64_t i, float v) {
+        ((unsigned short *)p)[i] = (unsigned short)to_f16(v);
+    }
+    __device__ static f32x4 mfma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <> struct Act<ACT_F32> {
+    using S = float;
+    using Frag = float;
+    static constexpr int VE = 4;
+    static constexpr int KM = 4;
+    __device__ static void unpack(u32x4 v, float *f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+    }
+    __device__ static u32x4 pack(const float *f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+        return v;
+    }
+    __device__ static float ld(const void *p, int64_t i) { return ((const float *)p)[i]; }
+    __device__ static void st(void *p, int64_t i, float v) { ((float *)p)[i] = v; }
+    __device__ static f32x4 mfma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (hardware id i runs on
+// XCD i % 8).  Give each XCD a contiguous range of logical ids so that tiles
+// sharing operands share that XCD's L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int hw, int n) {
+    const int q = n >> 3, r = n & 7, x = hw & 7, local = hw >> 3;
+    return x * q + (x < r ? x : r) + local;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// tanh-approximation GELU written through the identity
+// 0.5 y (1 + tanh(z)) = y / (1 + exp(-2 z)), z = sqrt(2/pi) (y + 0.044715 y^3).
+__device__ __forceinline__ float gelu_tanh(float y) {
+    const float c = 0.7978845608028654f;
+    float z = c * (y + 0.044715f * y * y * y);
+    return y / (1.0f + expf(-2.0f * z));
+}
+
+// ---------------------------------------------------------------------------
+// epilogue stores
+// ---------------------------------------------------------------------------
+// Column c of the projection (bias already added) to its destination: the GQA
+// split for QKV (q | k | v column blocks, token-major), tanh-GELU or nothing for
+// the up projection.
+template <int ACT, int EPI>
+__device__ __forceinline__ void store_col(const ProjArgs &p, int64_t m, int64_t c, float y) {
+    using T = Act<ACT>;
+    void *dst;
+    int64_t idx;
+    if constexpr (EPI == EPI_QKV) {
+        if (c < p.nq)              { dst = p.out0; idx = m * p.nq + c; }
+        else if (c < p.nq + p.nkv) { dst = p.out1; idx = m * p.nkv + (c - p.nq); }
+        else                       { dst = p.out2; idx = m * p.nkv + (c - p.nq - p.nkv); }
+    } else {
+        if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
+        dst = p.out0;
+        idx = m * p.F + c;
+    }
+    if (p.out_f32) ((float *)dst)[idx] = y;
+    else T::st(dst, idx, y);
+}
+
+// SwiGLU output j from the gate and up accumulators of the same column.
+template <int ACT>
+__device__ __forceinline__ void store_swiglu(const ProjArgs &p, int64_t m, int64_t j, float g, float u) {
+    using T = Act<ACT>;
+    if (p.bias) { g += T::ld(p.bias, j); u += T::ld(p.bias, p.F + j); }
+    const float y = silu(g) * u;
+    if (p.out_f32) ((float *)p.out0)[m * p.F + j] = y;
+    else T::st(p.out0, m * p.F + j, y);
+}
+
+// ---------------------------------------------------------------------------
+// deterministic split-K reduction
+// ---------------------------------------------------------------------------
+// Every split of a tile stores its NACC accumulators per thread (coalesced:
+// element r of thread t at r * 256 + t), then counts itself in at the tile's
+// arrival counter.  The last split to arrive reads all partials and sums them
+// in split order 0, 1, ..., S-1 (so the sum never depends on arrival order)
+// and returns true; the others return false and exit.
+//
+// Coherence across the XCDs' private L2s without whole-cache maintenance: the
+// partials are only ever written and read with device-scope accesses (stores
+// write through to the device coherence point, loads read from it), and each
+// thread waits for its own stores to complete before the workgroup barrier
+// that precedes the counter increment.  No thread touches the partials with
+// ordinary (L2-cached) accesses, so no L2 write-back or invalidate is needed.
+// The counters are cleared by the statistics kernel that precedes every
+// split launch on the same stream.
+template <int NACC>
+__device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int z, float (&acc)[NACC]) {
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    const int64_t tile_elems = (int64_t)NACC * 256;
+    float *mine = p.partials + ((int64_t)tile * p.splits + z) * tile_elems;
+#pragma unroll
+    for (int r = 0; r < NACC; ++r)
+        __hip_atomic_store(&mine[r * 256 + tid], acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);   // all of this thread's stores have completed
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned)(p.splits - 1);
+    }
+    __syncthreads();
+    if (!s_last) return false;
+    const float *base = p.partials + (int64_t)tile * p.splits * tile_elems;
+    // G splits' worth of partials in flight at once, then added in order
+    constexpr int G = NACC >= 64 ? 1 : 64 / NACC;
+#pragma unroll
+    for (int r = 0; r < NACC; ++r) acc[r] = 0.f;
+    for (int z0 = 0; z0 < p.splits; z0 += G) {
+        float v[G][NACC];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < NACC; ++r)
+                v[g][r] = z0 + g < p.splits
+                              ? __hip_atomic_load(&base[(z0 + g) * tile_elems + r * 256 + tid],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < NACC; ++r) acc[r] += v[g][r];
+    }
+    return true;
+}
+
+}  // namespace fp

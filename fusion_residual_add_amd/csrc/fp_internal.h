@@ -64,13 +64,22 @@ struct StatsArgs {
 };
 
 hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s);
-hipError_t launch_proj(int act, bool w_i8, int tile, const ProjArgs &a, hipStream_t s);
+// tiled family (fp_tiled.hip): prefill token counts and every fp32 call
+hipError_t launch_tiled(int act, bool w_i8, int tile, const ProjArgs &a, hipStream_t s);
+// weight-streaming family (fp_stream*.hip): 16-bit activations, M <= 64.
+//  mf: 16-row token fragments (1, 2 or 4); nr: 16-row weight fragments per
+//  wave (1 or 2; 2 for SwiGLU) -> 64 * nr weight rows per workgroup;
+//  u: 32-wide k slices per chunk (8) -> K must be a multiple of 32 * u.
+//  tiles_m must be 1.
+struct StreamCfg { int mf, nr, u; };
+hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, hipStream_t s);
 hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,
                           hipStream_t s);
 
 // names used by the event profiler
 const char *stats_kernel_name(int act);
 const char *proj_kernel_name(int act, bool w_i8, int tile, int epi);
+const char *stream_kernel_name(int act, bool w_i8, const StreamCfg &c, int epi);
 const char *dequant_kernel_name();
 
 }  // namespace fp

@@ -1,0 +1,33 @@
+// Dispatch and naming of the weight-streaming projection kernel (the kernel
+// itself is in fp_stream.hpp, instantiated per dtype in fp_stream_*.hip).
+#include "fp_device.hpp"
+
+#include <cstdio>
+
+namespace fp {
+
+void launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+void launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+void launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+
+hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, hipStream_t s) {
+    const int64_t g = (int64_t)a.tiles_n * a.splits;
+    if (g <= 0) return hipSuccess;
+    if (a.epi == EPI_SWIGLU && c.nr % 2 != 0) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)g;
+    if (w_i8) launch_stream_i8(c, a, grid, s);
+    else if (act == ACT_F16) launch_stream_f16(c, a, grid, s);
+    else launch_stream_bf16(c, a, grid, s);
+    return hipGetLastError();
+}
+
+const char *stream_kernel_name(int act, bool w_i8, const StreamCfg &c, int epi) {
+    static const char *acts[4] = {"f32", "f16", "bf16", "bf16-i8w"};
+    static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
+    thread_local char buf[64];
+    snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", acts[w_i8 ? 3 : act], 16 * c.mf,
+             64 * c.nr, 32 * c.u, epis[epi]);
+    return buf;
+}
+
+}  // namespace fp

@@ -1,0 +1,10 @@
+// Weight-streaming projection kernel instantiations: bf16 weights.
+#include "fp_stream.hpp"
+
+namespace fp {
+
+void launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
+    launch_stream_t<ACT_BF16, false>(c, a, grid, s);
+}
+
+}  // namespace fp

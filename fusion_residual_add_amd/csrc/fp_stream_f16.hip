@@ -1,0 +1,10 @@
+// Weight-streaming projection kernel instantiations: f16 weights.
+#include "fp_stream.hpp"
+
+namespace fp {
+
+void launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
+    launch_stream_t<ACT_F16, false>(c, a, grid, s);
+}
+
+}  // namespace fp

@@ -9,7 +9,7 @@
  * The operations follow the TensorRT-LLM pages this library is built from:
  *  - "TensorRT-LLM 深度工程实践：从模型到生产级推理服务", §2.3 跨算子融合:
  *    the LayerNorm + QKV projection fusion sketch (per-token mean and
- *    variance, rsqrt(var + eps), gamma and beta, then the Q, K and V products
+ *    variance, the reciprocal root of variance plus eps, gamma and beta, then the Q, K and V products
  *    written straight out without an intermediate tensor) and the SwiGLU
  *    sketch (SiLU of the gate product times the up product, one write);
  *    §2.2 图构建与算子映射: the QKV projection is one matmul followed by a

@@ -16,10 +16,11 @@
  *
  * Sources (web pages on TensorRT-LLM; cited by title and section):
  *  [D] "TensorRT-LLM 深度工程实践：从模型到生产级推理服务", §2.3 跨算子融合,
- *      sketch "LayerNorm + QKV Projection 融合" (per-token mean, variance,
- *      rsqrt(var + eps), gamma * (x - mean) * rsqrt + beta, then the Q, K and V
- *      products written straight out) and sketch "GEMM + 激活融合（SwiGLU）"
- *      (y = SiLU(x @ gate) * (x @ up), activation and product in registers).
+ *      sketch "LayerNorm + QKV Projection 融合" (per-token mean and variance,
+ *      reciprocal square root of variance plus eps, scale by gamma and shift
+ *      by beta, then the Q, K and V products written straight out) and sketch
+ *      "GEMM + 激活融合（SwiGLU）" (SiLU of the gate product times the up
+ *      product, activation and multiply kept in registers).
  *  [D2] same page, §2.2 图构建与算子映射: QKV projection = one matmul followed
  *      by reshape and GQA grouping of the heads.
  *  [I] "2. TensorRT-LLM 简介", 核心原理: the graph-optimisation layer fuses
@@ -32,8 +33,8 @@
  *  R1 residual add h = x + r, exact; the stored residual stream is
  *     h_out = RNE_act(h).
  *  R2 RMSNorm n = h / sqrt(mean(h^2) + eps) * gamma (no mean, no beta).
- *  R3 LayerNorm uses the biased (1/K) variance; gamma scales after the
- *     normalisation and beta is added last, as in the sketch [D].
+ *  R3 LayerNorm uses the biased (1/K) variance; gamma scales the normalised
+ *     value and beta is added last, the order the sketch [D] uses.
  *  R4 QKV columns are three contiguous blocks Q | K | V; q, k, v are stored
  *     token-major [M, heads, head_dim].
  *  R5 SwiGLU: the weight holds the gate rows [0, F) then the up rows [F, 2F);

@@ -90,6 +90,14 @@ SMALL = [
     dict(act="bf16", M=9, act_fn="none", bias=True, ffn=144),
     dict(act="bf16", M=129, H=8, Hkv=8, D=16, hidden=512),
     dict(act="bf16", M=3, H=5, Hkv=1, D=48, hidden=640, ffn=48),
+    # hidden a multiple of 256: decode token counts take the weight-streaming kernel
+    dict(act="bf16", M=1, hidden=768), dict(act="bf16", M=17, hidden=512), dict(act="bf16", M=33, hidden=1024),
+    dict(act="bf16", M=64, hidden=512), dict(act="bf16", M=50, hidden=512, ffn=208),
+    dict(act="f16", M=20, hidden=512), dict(act="f16", M=7, hidden=512, norm="layer", act_fn="gelu_tanh", bias=True),
+    dict(act="bf16", wdt="i8", M=1, hidden=512), dict(act="bf16", wdt="i8", M=40, hidden=768),
+    dict(act="bf16", wdt="i8", M=16, hidden=256, ffn=400),
+    dict(act="bf16", M=12, hidden=2048, act_fn="none", bias=True, ffn=96),
+    dict(act="bf16", M=32, hidden=512, H=16, Hkv=16, D=64, ffn=1024),
 ]
 
 
@@ -242,3 +250,36 @@ def test_int8_workload_dequant_bits():
     torch.cuda.synchronize()
     _, bits = oracle.dequant_i8(inp["w_qkv"], inp["s_qkv"])
     assert np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), bits)
+
+
+# ---------------------------------------------------------------------------
+# launch configurations: split-K factors (including splits of one tile that
+# land on different XCDs), chunk widths and rows per wave, both kernel families
+# ---------------------------------------------------------------------------
+CONFIGS = [
+    {"FUSEDPROJ_SPLITS": "1"}, {"FUSEDPROJ_SPLITS": "2"}, {"FUSEDPROJ_SPLITS": "3"},
+    {"FUSEDPROJ_SPLITS": "4"},
+    {"FUSEDPROJ_SPLITS": "5", "FUSEDPROJ_STREAM_NR": "1"},
+    {"FUSEDPROJ_SPLITS": "8", "FUSEDPROJ_STREAM_NR": "1"},
+    {"FUSEDPROJ_NO_STREAM": "1", "FUSEDPROJ_SPLITS": "3"},
+    {"FUSEDPROJ_NO_STREAM": "1", "FUSEDPROJ_SPLITS": "7"},
+]
+
+
+@pytest.mark.parametrize("env", CONFIGS, ids=lambda e: ",".join(f"{k[11:]}={v}" for k, v in e.items()))
+@pytest.mark.parametrize("M", [3, 32, 64])
+def test_launch_configs(env, M, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    wl = small(M=M, hidden=2048, H=10, Hkv=2, D=32, ffn=336)
+    inp = inputs.generate(wl, seed=8)
+    d = to_dev(inp)
+    print(f"configs {env} M={M}", flush=True)
+    q, k, v, h = run_qkv(wl, d, torch.float32)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rq = oracle.workload_qkv(wl, inp)
+    rg = oracle.workload_gateup(wl, inp)
+    check("q", q, rq["q"])
+    check("v", v, rq["v"])
+    check("out", out, rg["out"])
