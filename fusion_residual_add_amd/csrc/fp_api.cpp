@@ -36,7 +36,7 @@ int act_code(fp_dtype d) {
 // launch plan
 // ---------------------------------------------------------------------------
 struct Plan {
-    int family = 0;           // 0 tiled, 1 stream
+    int family = 0;           // 0 tiled (128 x 128), 1 stream (decode), 2 prefill (256 x 256)
     int tile = 0;             // tiled: TileCfg
     fp::StreamCfg sc{1, 2, 8};
     int tiles_m = 0, tiles_n = 0, splits = 1;
@@ -76,6 +76,15 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
         tiles = p.tiles_n;
         ksteps = K / (32 * u);
         target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
+    } else if (act != FP_F32 && M > 256 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32) &&
+               env_long("FUSEDPROJ_NO_PREFILL", 0) == 0) {
+        p.family = 2;
+        p.tiles_m = (int)((M + 255) / 256);
+        p.tiles_n = (int)((Nw + 255) / 256);
+        p.tile_elems = 256 * 256;
+        tiles = (int64_t)p.tiles_m * p.tiles_n;
+        ksteps = K / 64;
+        target = 128;
     } else {
         if (M <= 16) p.tile = fp::TILE_DEC16;
         else if (M <= 32) p.tile = fp::TILE_DEC32;
@@ -288,6 +297,10 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
         ProfScope ps(fp::stream_kernel_name(act, wi8, plan.sc, pa.epi), c.stream);
         hipError_t e = fp::launch_stream(act, wi8, plan.sc, pa, c.stream);
         if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
+    } else if (plan.family == 2) {
+        ProfScope ps(fp::prefill_kernel_name(act, wi8, pa.epi), c.stream);
+        hipError_t e = fp::launch_prefill(act, wi8, pa, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "prefill_kernel launch");
     } else {
         ProfScope ps(fp::proj_kernel_name(act, wi8, plan.tile, pa.epi), c.stream);
         hipError_t e = fp::launch_tiled(act, wi8, plan.tile, pa, c.stream);

@@ -230,10 +230,26 @@ __device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int z
     __syncthreads();
     if (!s_last) return false;
     const float *base = p.partials + (int64_t)tile * p.splits * tile_elems;
-    // G splits' worth of partials in flight at once, then added in order
-    constexpr int G = NACC >= 64 ? 1 : 64 / NACC;
 #pragma unroll
     for (int r = 0; r < NACC; ++r) acc[r] = 0.f;
+    if constexpr (NACC > 64) {
+        // large tiles: 64 values in flight at a time, split by split, in order
+        for (int zz = 0; zz < p.splits; ++zz) {
+#pragma unroll
+            for (int r0 = 0; r0 < NACC; r0 += 64) {
+                float v[64];
+#pragma unroll
+                for (int r = 0; r < 64; ++r)
+                    v[r] = __hip_atomic_load(&base[zz * tile_elems + (r0 + r) * 256 + tid], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int r = 0; r < 64; ++r) acc[r0 + r] += v[r];
+            }
+        }
+        return true;
+    }
+    // G splits' worth of partials in flight at once, then added in order
+    constexpr int G = NACC >= 64 ? 1 : 64 / NACC;
     for (int z0 = 0; z0 < p.splits; z0 += G) {
         float v[G][NACC];
 #pragma unroll

@@ -1,0 +1,411 @@
+// Prefill projection kernel of libfusedproj (gfx950): token counts where the
+// projection is bound by the matrix cores (the pages' prefill regime,
+// "TensorRT-LLM 深度工程实践…", §3.1).
+//
+// One workgroup (4 waves, 2 x 2) computes a 256 x 256 tile; each wave a
+// 128 x 128 sub-tile as 8 x 8 fragments of v_mfma_f32_16x16x32 (bf16 / f16)
+// with fp32 accumulators (256 per lane, held in AGPRs).  K advances in steps
+// of 64 through a double-buffered LDS pair of A (normalised activations) and
+// B (weights) tiles, 32 KB each per stage:
+//  * B: 16-bit weights go from HBM straight into LDS (global_load_lds, 16 bytes
+//    per lane, one 1 KB wave instruction = 8 rows x 128 bytes); int8 weights
+//    go through registers and are dequantised to bf16 on the way;
+//  * A: x and the residual are read (L2 hits: a 256-row block is shared by
+//    every column tile), re-formed as h, normalised with the row statistics
+//    and gamma / beta, rounded to the activation dtype and written to LDS -
+//    the normalised rows never reach memory (the LayerNorm + QKV fusion of
+//    §2.3).  The next K step's tile is produced while the current one feeds
+//    the MFMAs.
+// Both LDS tiles store 16-byte chunks XOR-swizzled by row, so that the 16
+// rows a fragment read touches land in 16 different bank groups.
+// The epilogue applies bias and the GQA split / SwiGLU / tanh-GELU / nothing,
+// stages the results through LDS and writes 16 bytes per lane.
+#pragma once
+
+#include "fp_device.hpp"
+
+namespace fp {
+
+namespace pf {
+// 16 bytes per lane from a buffer straight into LDS: lane l writes lds + 16 l
+// (the LDS address is taken from the wave-uniform pointer).  The builtin only
+// exists in the device pass.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char *lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+#else
+    (void)r, (void)lds, (void)voff, (void)soff;
+#endif
+}
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int ROWB = BK * 2;                 // bytes per tile row (bf16 / f16)
+constexpr int TILEB = BM * ROWB;             // 32 KB per operand tile
+// swizzled byte offset of 16-byte chunk c (0..7) of tile row r
+__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
+}  // namespace pf
+
+template <int ACT, bool WI8, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel(ProjArgs p) {
+    using T = Act<ACT>;
+    using namespace pf;
+    static_assert(ACT != ACT_F32, "16-bit activations");
+    static_assert(!WI8 || ACT == ACT_BF16, "int8 weights feed bf16 MFMA");
+    // A and B tiles of the two stages as four distinct LDS objects, so that
+    // the compiler can tell the direct-to-LDS weight loads into one stage from
+    // the fragment reads of the other (and waits for them only at the end of
+    // the step, not before the first fragment read).  The A tiles are
+    // reused as epilogue staging after the main loop.
+    __shared__ __attribute__((aligned(16))) unsigned char lA0[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char lA1[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char lB0[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char lB1[TILEB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // ---- tile of this workgroup: XCD-aware remap, then grouped raster
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = logical / p.splits, z = logical % p.splits;
+    int tm, tn;
+    {
+        constexpr int GROUP_M = 4;
+        const int group = GROUP_M * p.tiles_n;
+        const int gid = tile / group, first = gid * GROUP_M;
+        const int gsz = min(p.tiles_m - first, GROUP_M);
+        const int in = tile % group;
+        tm = first + in % gsz;
+        tn = in / gsz;
+    }
+    const int KT = (int)(p.K / BK);
+    const int kt0 = (int)((int64_t)KT * z / p.splits);
+    const int kt1 = (int)((int64_t)KT * (z + 1) / p.splits);
+
+    // ---- buffer resources: base and byte size in scalar registers, so each
+    // stream needs one 32-bit per-lane offset and the K advance is a scalar
+    // offset (keeps the vector register budget for the accumulators)
+    const unsigned ebytes_a = 2;
+    const uint32_t xbytes = (uint32_t)(p.M * p.K * ebytes_a);
+    const bool has_res = p.res != nullptr;
+    const bool has_beta = p.norm == 2 && p.beta != nullptr;
+    // absent optional operands get an empty range (their loads return zero);
+    // the arithmetic below ignores them as well
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, (short)0, xbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void *)(has_res ? p.res : p.x), (short)0,
+                                                                        has_res ? xbytes : 0u, 0x00020000);
+    const void *gsrc = p.norm != 0 ? p.gamma : p.x;
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc((void *)gsrc, (short)0,
+                                                                        p.norm != 0 ? (uint32_t)(p.K * 2) : 0u, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)(has_beta ? p.beta : gsrc), (short)0,
+                                                                        has_beta ? (uint32_t)(p.K * 2) : 0u, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, (short)0,
+                                                                        (uint32_t)(p.Nw * p.K * (WI8 ? 1 : 2)), 0x00020000);
+    // optional inputs become arithmetic: h = x + rs * r, n = ((h - mu) * rstd) * g' + b'
+    const float rs = has_res ? 1.f : 0.f;
+    const float gs = p.norm != 0 ? 1.f : 0.f, g1 = p.norm != 0 ? 0.f : 1.f;
+    const float bs = has_beta ? 1.f : 0.f;
+
+    // ---- A side: thread -> 16-byte chunk a_c of tile rows a_r0 + 32 i (i < 8)
+    const int a_c = tid & 7, a_r0 = tid >> 3;
+    const float2 *stp = p.norm != 0 ? p.stats : (const float2 *)p.x;
+    const float st_on = p.norm != 0 ? 1.f : 0.f;
+    uint32_t a_off[8];                                   // bytes, without the K step
+    float a_mu[8], a_rs[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int m = tm * BM + a_r0 + 32 * i;
+        m = m < (int)p.M ? m : (int)p.M - 1;             // rows past M only feed unstored outputs
+        a_off[i] = ((uint32_t)m * (uint32_t)p.K + a_c * 8) * 2;
+        const float2 st = stp[m];
+        a_mu[i] = st.x * st_on;
+        a_rs[i] = st_on != 0.f ? st.y : 1.f;
+    }
+
+    // ---- B side
+    // 16-bit weights: wave w loads tile rows [64 w, 64 w + 64) as 8 instructions
+    // of 8 rows; lane l of instruction i covers row 64 w + 8 i + l / 8 at LDS
+    // chunk position l % 8, i.e. global chunk (l % 8) ^ swizzle(row).
+    // int8 weights: thread -> 16-byte int8 vector (tile row (tid / 4) + 64 i,
+    // k bytes 16 (tid % 4) .. + 15), dequantised in registers.
+    constexpr int NBO = WI8 ? 4 : 8;
+    uint32_t b_off[NBO];                                 // bytes, without the K step
+    float b_sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NBO; ++i) {
+        int br;
+        if constexpr (WI8) br = (tid >> 2) + 64 * i;
+        else br = 64 * wave + 8 * i + (lane >> 3);
+        int64_t wrow;
+        if constexpr (EPI == EPI_SWIGLU) {
+            const int blk = br >> 4;
+            int64_t j = (int64_t)tn * (BN / 2) + (blk >> 1) * 16 + (br & 15);
+            j = j < p.F ? j : p.F - 1;
+            wrow = (blk & 1) ? p.F + j : j;
+        } else {
+            wrow = (int64_t)tn * BN + br;
+            wrow = wrow < p.Nw ? wrow : p.Nw - 1;
+        }
+        if constexpr (WI8) {
+            b_off[i] = (uint32_t)(wrow * p.K) + (tid & 3) * 16;
+            b_sc[i] = p.w_scale[wrow];
+        } else {
+            const int c = (lane & 7) ^ ((br >> 1) & 7);
+            b_off[i] = (uint32_t)((wrow * p.K + c * 8) * 2);
+        }
+    }
+
+    // ---- loads of one K step
+    struct ARegs { u32x4 x[8], r[8], g, b; };
+    struct BRegs { u32x4 q[4]; };   // int8 path only
+    auto ld16 = [](const __amdgpu_buffer_rsrc_t &rsrc, uint32_t voff, uint32_t soff) -> u32x4 {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+    };
+    auto aload = [&](int kt, ARegs &A) {
+        const uint32_t kb = (uint32_t)kt * (BK * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            A.x[i] = ld16(rx, a_off[i], kb);
+            A.r[i] = ld16(rr, a_off[i], kb);
+        }
+        A.g = ld16(rg, a_c * 16, kb);
+        A.b = ld16(rb, a_c * 16, kb);
+    };
+    auto astore = [&](unsigned char *la, const ARegs &A) {
+        float g[8], be[8];
+        T::unpack(A.g, g);
+        T::unpack(A.b, be);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            g[e] = g[e] * gs + g1;
+            be[e] = be[e] * bs;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float h[8], r[8];
+            T::unpack(A.x[i], h);
+            T::unpack(A.r[i], r);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float hv = fmaf(rs, r[e], h[e]);
+                const float t = (hv - a_mu[i]) * a_rs[i];
+                h[e] = fmaf(t, g[e], be[e]);
+            }
+            *(u32x4 *)(la + swz(a_r0 + 32 * i, a_c)) = T::pack(h);
+        }
+    };
+    auto bload_lds = [&](int kt, unsigned char *lb) {   // 16-bit weights, straight to LDS
+        const uint32_t kb = (uint32_t)kt * (BK * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            load_lds16(rw, lb + (64 * wave + 8 * i) * ROWB, b_off[i], kb);
+    };
+    auto bload_regs = [&](int kt, BRegs &B) {  // int8 weights
+        const uint32_t kb = (uint32_t)kt * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) B.q[i] = ld16(rw, b_off[i], kb);
+    };
+    auto bstore_regs = [&](unsigned char *lb, const BRegs &B) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 lo, hi;
+            dequant16(B.q[i], b_sc[i], lo, hi);
+            const int br = (tid >> 2) + 64 * i;
+            const int c0 = (tid & 3) * 2;
+            *(u32x4 *)(lb + swz(br, c0)) = lo;
+            *(u32x4 *)(lb + swz(br, c0 + 1)) = hi;
+        }
+    };
+
+    // ---- accumulators
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    auto mma = [&](const unsigned char *la, const unsigned char *lb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int c = s * 4 + (lane >> 4);
+            u32x4 af[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) af[i] = *(const u32x4 *)(la + swz(wm * 128 + i * 16 + (lane & 15), c));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const u32x4 bf = *(const u32x4 *)(lb + swz(wn * 128 + j * 16 + (lane & 15), c));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i][j] = T::mfma(af[i], bf, acc[i][j]);
+            }
+        }
+    };
+
+    // ---- main loop: stage kt + 1 is loaded while stage kt feeds the MFMAs.
+    // Issue order per step: activations, then weights (the normalisation waits
+    // only for the activations; loads retire in order).
+    ARegs A;
+    BRegs B;
+    auto load_next = [&](int kt, unsigned char *la, unsigned char *lb) {
+        aload(kt, A);
+        if constexpr (WI8) bload_regs(kt, B); else bload_lds(kt, lb);
+        (void)la;
+    };
+    auto store_next = [&](unsigned char *la, unsigned char *lb) {
+        astore(la, A);
+        if constexpr (WI8) bstore_regs(lb, B); else (void)lb;
+    };
+    auto step = [&](int kt, const unsigned char *ca, const unsigned char *cb, unsigned char *na, unsigned char *nb) {
+        load_next(kt + 1, na, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(ca, cb);
+        __builtin_amdgcn_sched_barrier(0);
+        store_next(na, nb);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    if (kt0 < kt1) {
+        load_next(kt0, lA0, lB0);
+        store_next(lA0, lB0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // stage identity alternates; both pointers of a pair come from one
+        // condition, so alias analysis still separates the objects
+        for (int kt = kt0; kt < kt1 - 1; ++kt) {
+            const bool odd = ((kt - kt0) & 1) != 0;
+            const unsigned char *ca = odd ? lA1 : lA0, *cb = odd ? lB1 : lB0;
+            unsigned char *na = odd ? lA0 : lA1, *nb = odd ? lB0 : lB1;
+            step(kt, ca, cb, na, nb);
+        }
+        const bool odd = ((kt1 - 1 - kt0) & 1) != 0;
+        mma(odd ? lA1 : lA0, odd ? lB1 : lB0);
+        __syncthreads();
+    }
+
+    // ---- split-K
+    if (p.splits > 1) {
+        float flat[256];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) flat[(i * 8 + j) * 4 + e] = acc[i][j][e];
+        if (!splitk_reduce(p, tile, z, flat)) return;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = flat[(i * 8 + j) * 4 + e];
+    }
+
+    // ---- epilogue, 32 token rows of the wave tile at a time: fragment values
+    // (bias and activation applied, fp32) go to this wave's own LDS area in
+    // [row][col] order, rows padded by 16 bytes so that the four row groups of
+    // a fragment hit different banks; they are then read back as runs of 8
+    // columns, converted to the output dtype and stored 16 bytes at a time.
+    constexpr int OUTC = EPI == EPI_SWIGLU ? 64 : 128;   // output columns per wave
+    constexpr int SROW = OUTC * 4 + 16;                  // staging row pitch, bytes
+    static_assert(32 * SROW <= TILEB, "staging fits one tile object");
+    unsigned char *stg = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
+    const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)tn * (BN / 2) + wn * 64 : (int64_t)tn * BN + wn * 128;
+    const int64_t ncols = EPI == EPI_SWIGLU ? p.F : p.Nw;
+    // bias of this lane's columns, zero when absent (SwiGLU: gate then up)
+    constexpr int NB = EPI == EPI_SWIGLU ? 8 : 8;
+    float bias_v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bias_v[j] = 0.f;
+    if (p.bias) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int64_t cg;
+            if constexpr (EPI == EPI_SWIGLU) {
+                const int64_t c = col0 + (j >> 1) * 16 + (lane & 15);
+                cg = (c < ncols ? c : ncols - 1) + ((j & 1) ? p.F : 0);
+            } else {
+                const int64_t c = col0 + j * 16 + (lane & 15);
+                cg = c < ncols ? c : ncols - 1;
+            }
+            bias_v[j] = T::ld(p.bias, cg);
+        }
+    }
+    const bool of32 = p.out_f32 != 0;
+    const int esz = of32 ? 4 : 2;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * g + ii;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rl = ii * 16 + (lane >> 4) * 4 + e;       // 0..31
+                if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2) {
+                        const int cl = (j / 2) * 16 + (lane & 15);    // 0..63
+                        const float gv = acc[i][j][e] + bias_v[j], uv = acc[i][j + 1][e] + bias_v[j + 1];
+                        *(float *)(stg + rl * SROW + cl * 4) = silu(gv) * uv;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int cl = j * 16 + (lane & 15);          // 0..127
+                        float y = acc[i][j][e] + bias_v[j];
+                        if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
+                        *(float *)(stg + rl * SROW + cl * 4) = y;
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0);
+        // 32 rows x OUTC columns as runs of 8 columns
+        constexpr int RUNS = OUTC / 8;
+#pragma unroll
+        for (int it = 0; it < 32 * RUNS / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int rl = idx / RUNS, ch = idx % RUNS;
+            const int64_t m = (int64_t)tm * BM + wm * 128 + g * 32 + rl;
+            const int64_t cg = col0 + ch * 8;
+            const f32x4 v0 = *(const f32x4 *)(stg + rl * SROW + ch * 32);
+            const f32x4 v1 = *(const f32x4 *)(stg + rl * SROW + ch * 32 + 16);
+            if (m >= p.M || cg >= ncols) continue;
+            char *dst;
+            if constexpr (EPI == EPI_QKV) {
+                if (cg < p.nq)              dst = (char *)p.out0 + (m * p.nq + cg) * esz;
+                else if (cg < p.nq + p.nkv) dst = (char *)p.out1 + (m * p.nkv + (cg - p.nq)) * esz;
+                else                        dst = (char *)p.out2 + (m * p.nkv + (cg - p.nq - p.nkv)) * esz;
+            } else {
+                dst = (char *)p.out0 + (m * ncols + cg) * esz;
+            }
+            if (of32) {
+                *(f32x4 *)dst = v0;
+                *(f32x4 *)(dst + 16) = v1;
+            } else {
+                const float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                *(u32x4 *)dst = T::pack(y);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+}
+
+template <int ACT, bool WI8>
+inline void launch_prefill_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    switch (a.epi) {
+    case EPI_QKV:
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_QKV>), dim3(grid), dim3(256), 0, s, a);
+        break;
+    case EPI_SWIGLU:
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a);
+        break;
+    case EPI_GELU:
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_GELU>), dim3(grid), dim3(256), 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_LINEAR>), dim3(grid), dim3(256), 0, s, a);
+        break;
+    }
+}
+
+}  // namespace fp

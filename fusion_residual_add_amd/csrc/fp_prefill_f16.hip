@@ -1,0 +1,10 @@
+// Prefill projection kernel instantiations: f16 weights.
+#include "fp_prefill.hpp"
+
+namespace fp {
+
+void launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    launch_prefill_t<ACT_F16, false>(a, grid, s);
+}
+
+}  // namespace fp

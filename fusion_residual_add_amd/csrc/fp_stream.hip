@@ -1,5 +1,6 @@
-// Dispatch and naming of the weight-streaming projection kernel (the kernel
-// itself is in fp_stream.hpp, instantiated per dtype in fp_stream_*.hip).
+// Dispatch and naming of the weight-streaming (decode) and 256 x 256 (prefill)
+// projection kernels (fp_stream.hpp / fp_prefill.hpp, instantiated per dtype
+// in fp_stream_*.hip / fp_prefill_*.hip).
 #include "fp_device.hpp"
 
 #include <cstdio>
@@ -19,6 +20,28 @@ hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs 
     else if (act == ACT_F16) launch_stream_f16(c, a, grid, s);
     else launch_stream_bf16(c, a, grid, s);
     return hipGetLastError();
+}
+
+void launch_prefill_bf16(const ProjArgs &a, unsigned grid, hipStream_t s);
+void launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s);
+void launch_prefill_i8(const ProjArgs &a, unsigned grid, hipStream_t s);
+
+hipError_t launch_prefill(int act, bool w_i8, const ProjArgs &a, hipStream_t s) {
+    const int64_t g = (int64_t)a.tiles_m * a.tiles_n * a.splits;
+    if (g <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)g;
+    if (w_i8) launch_prefill_i8(a, grid, s);
+    else if (act == ACT_F16) launch_prefill_f16(a, grid, s);
+    else launch_prefill_bf16(a, grid, s);
+    return hipGetLastError();
+}
+
+const char *prefill_kernel_name(int act, bool w_i8, int epi) {
+    static const char *acts[4] = {"f32", "f16", "bf16", "bf16-i8w"};
+    static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
+    thread_local char buf[64];
+    snprintf(buf, sizeof buf, "prefill_kernel<%s,256x256,%s>", acts[w_i8 ? 3 : act], epis[epi]);
+    return buf;
 }
 
 const char *stream_kernel_name(int act, bool w_i8, const StreamCfg &c, int epi) {

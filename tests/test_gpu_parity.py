@@ -253,6 +253,88 @@ def test_int8_workload_dequant_bits():
 
 
 # ---------------------------------------------------------------------------
+# token counts above one 256-row tile (the prefill kernel family): ragged row
+# and column tails, SwiGLU widths that split a 128-column output tile, every
+# weight dtype and epilogue
+# ---------------------------------------------------------------------------
+PREFILL = [
+    dict(act="bf16", M=300, hidden=512, H=4, Hkv=1, D=64, ffn=192),
+    dict(act="bf16", M=520, hidden=256, H=8, Hkv=2, D=32, ffn=320, act_fn="gelu_tanh", bias=True,
+         norm="layer"),
+    dict(act="f16", M=384, hidden=384, norm="layer", act_fn="gelu_tanh", bias=True, ffn=272),
+    dict(act="f16", M=290, hidden=448, H=2, Hkv=2, D=128, ffn=176),
+    dict(act="bf16", wdt="i8", M=333, hidden=512, ffn=208),
+    dict(act="bf16", wdt="i8", M=600, hidden=256, H=8, Hkv=1, D=64, ffn=400, bias=True),
+    dict(act="bf16", M=700, hidden=128, H=2, Hkv=2, D=64, act_fn="none", bias=True, ffn=144),
+    dict(act="bf16", M=1024, hidden=1024, H=16, Hkv=4, D=64, ffn=512, bias=True),
+]
+
+
+@pytest.mark.parametrize("cfg", PREFILL, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("native", [False, True], ids=["f32out", "nativeout"])
+def test_prefill(cfg, native):
+    test_small(cfg, native)
+
+
+def test_prefill_norm_none_no_residual():
+    wl = dataclasses.replace(small(M=310, hidden=256, ffn=144), norm="none")
+    inp = inputs.generate(wl, seed=14)
+    d = to_dev(inp)
+    print(f"case {wl.name} norm=none residual=None", flush=True)
+    out = fra.fused_gateup_act(d["x"], None, None, d["w_gu"], wl.ffn, "swiglu", norm="none",
+                               out_dtype=torch.float32)
+    q, k, v, h = fra.fused_add_norm_qkv(d["x"], None, None, d["w_qkv"], wl.n_heads, wl.n_kv_heads,
+                                        wl.head_dim, norm="none", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rg = oracle.gateup_act(inp["x"], None, inp["gamma"], None, "none", 0.0, inp["w_gu"], None, None,
+                           wl.ffn, "swiglu")
+    rq = oracle.add_norm_qkv(inp["x"], None, inp["gamma"], None, "none", 0.0, inp["w_qkv"], None, None,
+                             wl.n_heads, wl.n_kv_heads, wl.head_dim)
+    check("out", out, rg["out"])
+    check("q", q, rq["q"])
+    check("k", k, rq["k"])
+    check("v", v, rq["v"])
+
+
+def test_prefill_layernorm_without_beta():
+    wl = small(M=280, hidden=320, norm="layer")
+    inp = inputs.generate(wl, seed=15)
+    d = to_dev(inp)
+    print(f"case {wl.name} layer norm without beta", flush=True)
+    out = fra.fused_gateup_act(d["x"], d["r"], d["gamma"], d["w_gu"], wl.ffn, "swiglu", norm="layer",
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rg = oracle.gateup_act(inp["x"], inp["r"], inp["gamma"], None, "layer", wl.eps, inp["w_gu"], None,
+                           None, wl.ffn, "swiglu")
+    check("out", out, rg["out"])
+
+
+PREFILL_CONFIGS = [{"FUSEDPROJ_SPLITS": "1"}, {"FUSEDPROJ_SPLITS": "2"}, {"FUSEDPROJ_SPLITS": "3"},
+                   {"FUSEDPROJ_SPLITS": "5"}, {"FUSEDPROJ_SPLITS": "16"}, {"FUSEDPROJ_NO_PREFILL": "1"}]
+
+
+@pytest.mark.parametrize("env", PREFILL_CONFIGS, ids=lambda e: ",".join(f"{k[11:]}={v}" for k, v in e.items()))
+@pytest.mark.parametrize("wdt", ["bf16", "i8"])
+def test_prefill_launch_configs(env, wdt, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    wl = small(wdt=wdt, M=270, hidden=1024, H=10, Hkv=2, D=32, ffn=336, bias=True)
+    inp = inputs.generate(wl, seed=16)
+    d = to_dev(inp)
+    print(f"prefill configs {env} wdt={wdt}", flush=True)
+    q, k, v, h = run_qkv(wl, d, torch.float32)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rq = oracle.workload_qkv(wl, inp)
+    rg = oracle.workload_gateup(wl, inp)
+    check("q", q, rq["q"])
+    check("k", k, rq["k"])
+    check("v", v, rq["v"])
+    check("out", out, rg["out"])
+    assert np.array_equal(h.double().cpu().numpy(), rq["h_out"]), "h_out not bit-exact"
+
+
+# ---------------------------------------------------------------------------
 # launch configurations: split-K factors (including splits of one tile that
 # land on different XCDs), chunk widths and rows per wave, both kernel families
 # ---------------------------------------------------------------------------
