@@ -173,7 +173,7 @@ fp_status check_dtypes(fp_dtype act, fp_dtype wdt, fp_dtype odt) {
 // event profiler
 // ---------------------------------------------------------------------------
 struct ProfRec {
-    const char *name;
+    char name[64];   // a copy: the name functions reuse one buffer per thread
     hipEvent_t a, b;
 };
 bool g_prof = false;
@@ -185,7 +185,7 @@ struct ProfScope {
     bool on;
     ProfScope(const char *name, hipStream_t st) : s(st), on(g_prof) {
         if (!on) return;
-        rec.name = name;
+        snprintf(rec.name, sizeof rec.name, "%s", name);
         if (hipEventCreate(&rec.a) != hipSuccess || hipEventCreate(&rec.b) != hipSuccess) { on = false; return; }
         (void)hipEventRecord(rec.a, s);
     }

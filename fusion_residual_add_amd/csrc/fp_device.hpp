@@ -12,6 +12,7 @@ namespace fp {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 // ---------------------------------------------------------------------------
@@ -21,6 +22,17 @@ __device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ unsigned to_bf16(float f) {
     return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)f);
+}
+// two fp32 values -> one word of two 16-bit values (first in the low half),
+// round to nearest even, one packed conversion instruction each
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack2_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+__device__ __forceinline__ unsigned pack2_f16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
 }
 __device__ __forceinline__ float f16lo(unsigned w) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
@@ -66,10 +78,10 @@ template <> struct Act<ACT_BF16> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) { f[2 * i] = bf16lo(v[i]); f[2 * i + 1] = bf16hi(v[i]); }
     }
-    __device__ static u32x4 pack(const float *f) {
+    __device__ static u32x4 pack(const float *f) {   // RNE, two values per conversion
         u32x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = to_bf16(f[2 * i]) | (to_bf16(f[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; ++i) v[i] = pack2_bf16(f[2 * i], f[2 * i + 1]);
         return v;
     }
     __device__ static float ld(const void *p, int64_t i) {
@@ -82,6 +94,14 @@ template <> struct Act<ACT_BF16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
+    // 32 x 32 x 16: lane l supplies row / column l % 32, k 8 (l / 32) .. + 7
+    __device__ static f32x16 mfma32(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // the two values of a word (low half first)
+    __device__ static float lo(unsigned w) { return bf16lo(w); }
+    __device__ static float hi(unsigned w) { return bf16hi(w); }
 };
 
 template <> struct Act<ACT_F16> {
@@ -93,10 +113,10 @@ template <> struct Act<ACT_F16> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) { f[2 * i] = f16lo(v[i]); f[2 * i + 1] = f16hi(v[i]); }
     }
-    __device__ static u32x4 pack(const float *f) {
+    __device__ static u32x4 pack(const float *f) {   // RNE, two values per conversion
         u32x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = to_f16(f[2 * i]) | (to_f16(f[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; ++i) v[i] = pack2_f16(f[2 * i], f[2 * i + 1]);
         return v;
     }
     __device__ static float ld(const void *p, int64_t i) {
@@ -109,6 +129,12 @@ template <> struct Act<ACT_F16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+    __device__ static f32x16 mfma32(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static float lo(unsigned w) { return f16lo(w); }
+    __device__ static float hi(unsigned w) { return f16hi(w); }
 };
 
 template <> struct Act<ACT_F32> {

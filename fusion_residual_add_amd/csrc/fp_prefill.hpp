@@ -3,8 +3,9 @@
 // "TensorRT-LLM 深度工程实践…", §3.1).
 //
 // One workgroup (4 waves, 2 x 2) computes a 256 x 256 tile; each wave a
-// 128 x 128 sub-tile as 8 x 8 fragments of v_mfma_f32_16x16x32 (bf16 / f16)
-// with fp32 accumulators (256 per lane, held in AGPRs).  K advances in steps
+// 128 x 128 sub-tile as 4 x 4 fragments of v_mfma_f32_32x32x16 (bf16 / f16)
+// with fp32 accumulators (256 per lane, all in AGPRs: the 32 x 32 shape keeps
+// them in 16-register tuples that the allocator leaves in place).  K advances in steps
 // of 64 through a double-buffered LDS pair of A (normalised activations) and
 // B (weights) tiles, 32 KB each per stage:
 //  * B: 16-bit weights go from HBM straight into LDS (global_load_lds, 16 bytes
@@ -100,10 +101,8 @@ void prefill_kernel(ProjArgs p) {
                                                                         has_beta ? (uint32_t)(p.K * 2) : 0u, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, (short)0,
                                                                         (uint32_t)(p.Nw * p.K * (WI8 ? 1 : 2)), 0x00020000);
-    // optional inputs become arithmetic: h = x + rs * r, n = ((h - mu) * rstd) * g' + b'
-    const float rs = has_res ? 1.f : 0.f;
-    const float gs = p.norm != 0 ? 1.f : 0.f, g1 = p.norm != 0 ? 0.f : 1.f;
-    const float bs = has_beta ? 1.f : 0.f;
+    // norm none: gamma reads as zero and g1 turns it into one
+    const float g1 = p.norm != 0 ? 0.f : 1.f;
 
     // ---- A side: thread -> 16-byte chunk a_c of tile rows a_r0 + 32 i (i < 8)
     const int a_c = tid & 7, a_r0 = tid >> 3;
@@ -137,8 +136,10 @@ void prefill_kernel(ProjArgs p) {
         else br = 64 * wave + 8 * i + (lane >> 3);
         int64_t wrow;
         if constexpr (EPI == EPI_SWIGLU) {
-            const int blk = br >> 4;
-            int64_t j = (int64_t)tn * (BN / 2) + (blk >> 1) * 16 + (br & 15);
+            // 32-row blocks alternate gate / up: fragment pairs (2 j, 2 j + 1)
+            // of a wave hold the gate and up values of the same outputs
+            const int blk = br >> 5;
+            int64_t j = (int64_t)tn * (BN / 2) + (blk >> 1) * 32 + (br & 31);
             j = j < p.F ? j : p.F - 1;
             wrow = (blk & 1) ? p.F + j : j;
         } else {
@@ -154,57 +155,60 @@ void prefill_kernel(ProjArgs p) {
         }
     }
 
-    // ---- loads of one K step
+    // ---- activation side, a rolling register pipeline: the rows of stage
+    // kt + 1 are normalised into LDS while stage kt feeds the MFMAs, and each
+    // row's registers are refilled with stage kt + 2 right after use, so every
+    // load has a whole step to arrive.
     struct ARegs { u32x4 x[8], r[8], g, b; };
     struct BRegs { u32x4 q[4]; };   // int8 path only
+    ARegs A;
+    BRegs B;
+    float gv[8], bv[8];             // gamma / beta of the stage being normalised
     auto ld16 = [](const __amdgpu_buffer_rsrc_t &rsrc, uint32_t voff, uint32_t soff) -> u32x4 {
         return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
     };
-    auto aload = [&](int kt, ARegs &A) {
+    auto a_issue = [&](int kt, int i) {
         const uint32_t kb = (uint32_t)kt * (BK * 2);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            A.x[i] = ld16(rx, a_off[i], kb);
-            A.r[i] = ld16(rr, a_off[i], kb);
-        }
+        A.x[i] = ld16(rx, a_off[i], kb);
+        A.r[i] = ld16(rr, a_off[i], kb);
+    };
+    auto gb_issue = [&](int kt) {
+        const uint32_t kb = (uint32_t)kt * (BK * 2);
         A.g = ld16(rg, a_c * 16, kb);
         A.b = ld16(rb, a_c * 16, kb);
     };
-    auto astore = [&](unsigned char *la, const ARegs &A) {
-        float g[8], be[8];
-        T::unpack(A.g, g);
-        T::unpack(A.b, be);
+    auto gb_unpack = [&]() {
+        T::unpack(A.g, gv);
+        T::unpack(A.b, bv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            g[e] = g[e] * gs + g1;
-            be[e] = be[e] * bs;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float h[8], r[8];
-            T::unpack(A.x[i], h);
-            T::unpack(A.r[i], r);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float hv = fmaf(rs, r[e], h[e]);
-                const float t = (hv - a_mu[i]) * a_rs[i];
-                h[e] = fmaf(t, g[e], be[e]);
-            }
-            *(u32x4 *)(la + swz(a_r0 + 32 * i, a_c)) = T::pack(h);
-        }
+        for (int e = 0; e < 8; ++e) gv[e] += g1;
     };
+    // h = x + r (r reads as zero when absent; exact in fp32),
+    // n = (h - mu) * rstd * gamma + beta
+    auto a_norm = [&](unsigned char *la, int i) {
+        float n[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const unsigned xw = A.x[i][w], rv = A.r[i][w];
+            const float d0 = (T::lo(xw) + T::lo(rv)) - a_mu[i];
+            const float d1 = (T::hi(xw) + T::hi(rv)) - a_mu[i];
+            n[2 * w] = fmaf(d0 * a_rs[i], gv[2 * w], bv[2 * w]);
+            n[2 * w + 1] = fmaf(d1 * a_rs[i], gv[2 * w + 1], bv[2 * w + 1]);
+        }
+        *(u32x4 *)(la + swz(a_r0 + 32 * i, a_c)) = T::pack(n);
+    };
+    // ---- weight side
     auto bload_lds = [&](int kt, unsigned char *lb) {   // 16-bit weights, straight to LDS
         const uint32_t kb = (uint32_t)kt * (BK * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            load_lds16(rw, lb + (64 * wave + 8 * i) * ROWB, b_off[i], kb);
+        for (int i = 0; i < 8; ++i) load_lds16(rw, lb + (64 * wave + 8 * i) * ROWB, b_off[i], kb);
     };
-    auto bload_regs = [&](int kt, BRegs &B) {  // int8 weights
+    auto bload_regs = [&](int kt) {   // int8 weights
         const uint32_t kb = (uint32_t)kt * BK;
 #pragma unroll
         for (int i = 0; i < 4; ++i) B.q[i] = ld16(rw, b_off[i], kb);
     };
-    auto bstore_regs = [&](unsigned char *lb, const BRegs &B) {
+    auto bstore_regs = [&](unsigned char *lb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             u32x4 lo, hi;
@@ -216,67 +220,125 @@ void prefill_kernel(ProjArgs p) {
         }
     };
 
-    // ---- accumulators
-    f32x4 acc[8][8];
+    // ---- accumulators: acc[i][j][q] = D[row i*32 + 8(q/4) + 4(lane/32) + q%4]
+    //                                        [col j*32 + lane%32] of the wave tile
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    auto mma = [&](const unsigned char *la, const unsigned char *lb) {
+    // MFMAs of one stage: four K substeps of 16; lane l supplies row / column
+    // l % 32 and the 16-byte chunk 2 t + l / 32 of both operands.  A stage is
+    // run as 8 regions (substep t = r / 2, fragment columns 2 h, 2 h + 1 with
+    // h = r % 2), each 8 MFMAs with one activation row of the next stage
+    // normalised into `na` between them (and its registers refilled from
+    // stage `kn`), while the fragments of the following region are read from
+    // LDS.  Scheduling barriers keep each region's instruction mix in place:
+    // every MFMA is followed by a handful of VALU instructions, which run in
+    // the MFMA's shadow.
+    auto frag_a = [&](const unsigned char *la, int t, int i) {
+        return *(const u32x4 *)(la + swz(wm * 128 + i * 32 + (lane & 31), 2 * t + (lane >> 5)));
+    };
+    auto frag_b = [&](const unsigned char *lb, int t, int j) {
+        return *(const u32x4 *)(lb + swz(wn * 128 + j * 32 + (lane & 31), 2 * t + (lane >> 5)));
+    };
+    auto mma = [&](const unsigned char *la, const unsigned char *lb, unsigned char *na, int kn) {
+        u32x4 af[4], bf[2], nf[4], nbf[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int c = s * 4 + (lane >> 4);
-            u32x4 af[8];
+        for (int i = 0; i < 4; ++i) af[i] = frag_a(la, 0, i);
+        bf[0] = frag_b(lb, 0, 0);
+        bf[1] = frag_b(lb, 0, 1);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) af[i] = *(const u32x4 *)(la + swz(wm * 128 + i * 16 + (lane & 15), c));
+        for (int r = 0; r < 8; ++r) {
+            const int t = r >> 1, h = r & 1;
+            // fragments of region r + 1
+            if (r < 7) {
+                if (h == 0) {
+                    nbf[0] = frag_b(lb, t, 2);
+                    nbf[1] = frag_b(lb, t, 3);
+                } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const u32x4 bf = *(const u32x4 *)(lb + swz(wn * 128 + j * 16 + (lane & 15), c));
+                    for (int i = 0; i < 4; ++i) nf[i] = frag_a(la, t + 1, i);
+                    nbf[0] = frag_b(lb, t + 1, 0);
+                    nbf[1] = frag_b(lb, t + 1, 1);
+                }
+            }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i][j] = T::mfma(af[i], bf, acc[i][j]);
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i][2 * h + jj] = T::mfma32(af[i], bf[jj], acc[i][2 * h + jj]);
+            a_norm(na, r);
+            a_issue(kn, r);
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS reads
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // row loads
+            __builtin_amdgcn_sched_barrier(0);
+            if (r < 7) {
+                bf[0] = nbf[0];
+                bf[1] = nbf[1];
+                if (h == 1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) af[i] = nf[i];
+                }
             }
         }
     };
+    // wait for everything but the activation loads issued after the weights
+    // of the step (2 gamma / beta + 16 row loads), and for this thread's LDS
+    // writes; then a workgroup barrier.  The count relies on issue order:
+    // every weight load is fenced by a scheduling barrier before anything
+    // else is issued.  The empty asm statements keep the compiler from moving
+    // memory accesses across the barrier.
+    auto step_sync = [&]() {
+        constexpr int VM = 18;
+        __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
+        __asm__ __volatile__("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ __volatile__("" ::: "memory");
+    };
 
-    // ---- main loop: stage kt + 1 is loaded while stage kt feeds the MFMAs.
-    // Issue order per step: activations, then weights (the normalisation waits
-    // only for the activations; loads retire in order).
-    ARegs A;
-    BRegs B;
-    auto load_next = [&](int kt, unsigned char *la, unsigned char *lb) {
-        aload(kt, A);
-        if constexpr (WI8) bload_regs(kt, B); else bload_lds(kt, lb);
-        (void)la;
-    };
-    auto store_next = [&](unsigned char *la, unsigned char *lb) {
-        astore(la, A);
-        if constexpr (WI8) bstore_regs(lb, B); else (void)lb;
-    };
-    auto step = [&](int kt, const unsigned char *ca, const unsigned char *cb, unsigned char *na, unsigned char *nb) {
-        load_next(kt + 1, na, nb);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(ca, cb);
-        __builtin_amdgcn_sched_barrier(0);
-        store_next(na, nb);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    };
     if (kt0 < kt1) {
-        load_next(kt0, lA0, lB0);
-        store_next(lA0, lB0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // prologue: stage kt0 into LDS tile 0, then start loading stage kt0 + 1
+        if constexpr (WI8) bload_regs(kt0); else bload_lds(kt0, lB0);
+        __builtin_amdgcn_sched_barrier(0);
+        gb_issue(kt0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a_issue(kt0, i);
+        gb_unpack();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a_norm(lA0, i);
+        if constexpr (WI8) bstore_regs(lB0);
+        const int k1 = kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1;
+        gb_issue(k1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a_issue(k1, i);
+        step_sync();
         // stage identity alternates; both pointers of a pair come from one
-        // condition, so alias analysis still separates the objects
-        for (int kt = kt0; kt < kt1 - 1; ++kt) {
+        // condition, so alias analysis still separates the objects.  Every
+        // step prepares the next stage (past the end: harmless reloads of the
+        // last one, never used) so that the MFMA code exists once.
+        for (int kt = kt0; kt < kt1; ++kt) {
             const bool odd = ((kt - kt0) & 1) != 0;
             const unsigned char *ca = odd ? lA1 : lA0, *cb = odd ? lB1 : lB0;
             unsigned char *na = odd ? lA0 : lA1, *nb = odd ? lB0 : lB1;
-            step(kt, ca, cb, na, nb);
+            const int kw = kt + 1 < kt1 ? kt + 1 : kt1 - 1;
+            const int kn = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
+            if constexpr (WI8) bload_regs(kw); else bload_lds(kw, nb);
+            __builtin_amdgcn_sched_barrier(0);   // keeps the weight loads first (see step_sync)
+            gb_unpack();
+            gb_issue(kn);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(ca, cb, na, kn);
+            if constexpr (WI8) bstore_regs(nb);
+            step_sync();
         }
-        const bool odd = ((kt1 - 1 - kt0) & 1) != 0;
-        mma(odd ? lA1 : lA0, odd ? lB1 : lB0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -284,45 +346,43 @@ void prefill_kernel(ProjArgs p) {
     if (p.splits > 1) {
         float flat[256];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) flat[(i * 8 + j) * 4 + e] = acc[i][j][e];
+                for (int e = 0; e < 16; ++e) flat[(i * 4 + j) * 16 + e] = acc[i][j][e];
         if (!splitk_reduce(p, tile, z, flat)) return;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][e] = flat[(i * 8 + j) * 4 + e];
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = flat[(i * 4 + j) * 16 + e];
     }
 
-    // ---- epilogue, 32 token rows of the wave tile at a time: fragment values
-    // (bias and activation applied, fp32) go to this wave's own LDS area in
-    // [row][col] order, rows padded by 16 bytes so that the four row groups of
-    // a fragment hit different banks; they are then read back as runs of 8
-    // columns, converted to the output dtype and stored 16 bytes at a time.
+    // ---- epilogue, one 32-row fragment row (i) of the wave tile at a time:
+    // values (bias and activation applied, fp32) go to this wave's own LDS
+    // area in [row][col] order, rows padded by 32 bytes so that the two lane
+    // halves (4 rows apart) hit different banks; they are then read back as
+    // runs of 8 columns, converted to the output dtype and stored 16 bytes at
+    // a time.
     constexpr int OUTC = EPI == EPI_SWIGLU ? 64 : 128;   // output columns per wave
-    constexpr int SROW = OUTC * 4 + 16;                  // staging row pitch, bytes
+    constexpr int SROW = OUTC * 4 + 32;                  // staging row pitch, bytes
     static_assert(32 * SROW <= TILEB, "staging fits one tile object");
     unsigned char *stg = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
     const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)tn * (BN / 2) + wn * 64 : (int64_t)tn * BN + wn * 128;
     const int64_t ncols = EPI == EPI_SWIGLU ? p.F : p.Nw;
-    // bias of this lane's columns, zero when absent (SwiGLU: gate then up)
-    constexpr int NB = EPI == EPI_SWIGLU ? 8 : 8;
-    float bias_v[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) bias_v[j] = 0.f;
+    // bias of this lane's columns, zero when absent (SwiGLU: gate, up, gate, up)
+    float bias_v[4] = {0.f, 0.f, 0.f, 0.f};
     if (p.bias) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             int64_t cg;
             if constexpr (EPI == EPI_SWIGLU) {
-                const int64_t c = col0 + (j >> 1) * 16 + (lane & 15);
+                const int64_t c = col0 + (j >> 1) * 32 + (lane & 31);
                 cg = (c < ncols ? c : ncols - 1) + ((j & 1) ? p.F : 0);
             } else {
-                const int64_t c = col0 + j * 16 + (lane & 15);
+                const int64_t c = col0 + j * 32 + (lane & 31);
                 cg = c < ncols ? c : ncols - 1;
             }
             bias_v[j] = T::ld(p.bias, cg);
@@ -331,28 +391,24 @@ void prefill_kernel(ProjArgs p) {
     const bool of32 = p.out_f32 != 0;
     const int esz = of32 ? 4 : 2;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int i = 2 * g + ii;
+        for (int q = 0; q < 16; ++q) {
+            const int rl = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);   // 0..31
+            if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rl = ii * 16 + (lane >> 4) * 4 + e;       // 0..31
-                if constexpr (EPI == EPI_SWIGLU) {
+                for (int j = 0; j < 4; j += 2) {
+                    const int cl = (j >> 1) * 32 + (lane & 31);        // 0..63
+                    const float gv = acc[i][j][q] + bias_v[j], uv = acc[i][j + 1][q] + bias_v[j + 1];
+                    *(float *)(stg + rl * SROW + cl * 4) = silu(gv) * uv;
+                }
+            } else {
 #pragma unroll
-                    for (int j = 0; j < 8; j += 2) {
-                        const int cl = (j / 2) * 16 + (lane & 15);    // 0..63
-                        const float gv = acc[i][j][e] + bias_v[j], uv = acc[i][j + 1][e] + bias_v[j + 1];
-                        *(float *)(stg + rl * SROW + cl * 4) = silu(gv) * uv;
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int cl = j * 16 + (lane & 15);          // 0..127
-                        float y = acc[i][j][e] + bias_v[j];
-                        if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
-                        *(float *)(stg + rl * SROW + cl * 4) = y;
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const int cl = j * 32 + (lane & 31);               // 0..127
+                    float y = acc[i][j][q] + bias_v[j];
+                    if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
+                    *(float *)(stg + rl * SROW + cl * 4) = y;
                 }
             }
         }
@@ -364,7 +420,7 @@ void prefill_kernel(ProjArgs p) {
         for (int it = 0; it < 32 * RUNS / 64; ++it) {
             const int idx = it * 64 + lane;
             const int rl = idx / RUNS, ch = idx % RUNS;
-            const int64_t m = (int64_t)tm * BM + wm * 128 + g * 32 + rl;
+            const int64_t m = (int64_t)tm * BM + wm * 128 + i * 32 + rl;
             const int64_t cg = col0 + ch * 8;
             const f32x4 v0 = *(const f32x4 *)(stg + rl * SROW + ch * 32);
             const f32x4 v1 = *(const f32x4 *)(stg + rl * SROW + ch * 32 + 16);
