@@ -40,6 +40,8 @@ struct Plan {
     int tile = 0;             // tiled: TileCfg
     fp::StreamCfg sc{1, 2, 8};
     int tiles_m = 0, tiles_n = 0, splits = 1;
+    int grid = 0;             // stream: workgroups sharing the units evenly
+    int slots = 1;            // partial-sum slots per tile (1: none needed)
     int64_t tile_elems = 0;   // accumulators per tile (split-K partial size)
     size_t stats_off = 0, ctr_off = 0, part_off = 0, total = 0;
 };
@@ -53,9 +55,11 @@ long env_long(const char *name, long dflt) {
 }
 
 // Decode token counts (M <= 64, 16-bit activations) use the weight-streaming
-// kernel; everything else the tiled kernel.  When a grid would hold too few
-// workgroups to keep enough weight bytes in flight, K is split and the
-// partial sums are reduced by the last split to arrive, in split order.
+// kernel, which spreads (tile, K chunk) units evenly over one workgroup per
+// CU; token counts above 256 the 256 x 256 prefill kernel; everything else
+// the tiled kernel.  When a tiled grid would hold too few workgroups, K is
+// split.  Partial sums are reduced by the last contributor to arrive, in a
+// fixed order.
 // FUSEDPROJ_* environment variables override the choices (for tuning sweeps);
 // the workspace query and the call read them alike.
 Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
@@ -76,6 +80,25 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
         tiles = p.tiles_n;
         ksteps = K / (32 * u);
         target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
+        // stream-K: `grid` workgroups take equal contiguous unit ranges of at
+        // least 4 chunks (measured on MI355X: the QKV shape of Llama-3-8B
+        // decode streams fastest on 192 workgroups, the gate/up shape on one
+        // per CU; shorter ranges pay the pipeline ramp too often)
+        const int64_t units = tiles * ksteps;
+        int64_t G = units / 4 < target ? units / 4 : target;
+        const long forced = env_long("FUSEDPROJ_SPLITS", 0);
+        if (forced > 0) G = tiles * forced;
+        if (G > units) G = units;
+        if (G < 1) G = 1;
+        p.grid = (int)G;
+        // the most workgroups that share one tile
+        auto owner = [&](int64_t v) { return ((v + 1) * G - 1) / units; };
+        int64_t most = 1;
+        for (int64_t t = 0; t < tiles; ++t) {
+            const int64_t n = owner(t * ksteps + ksteps - 1) - owner(t * ksteps) + 1;
+            if (n > most) most = n;
+        }
+        p.slots = (int)most;
     } else if (act != FP_F32 && M > 256 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32) &&
                env_long("FUSEDPROJ_NO_PREFILL", 0) == 0) {
         p.family = 2;
@@ -98,31 +121,27 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
         ksteps = K / ts.bk;
         target = 512;
     }
-    int64_t s = 1;
-    if (p.family == 1) {
-        // measured on MI355X (decode shapes, K 4096 / 8192): one workgroup per
-        // CU is the sweet spot -- extra splits cost partial-sum traffic and a
-        // tail, too few workgroups leave HBM bandwidth unused
-        if (tiles > 0 && tiles < target) s = target / tiles;
-    } else if (tiles > 0 && tiles < target) {
-        s = (target + tiles - 1) / tiles;
+    if (p.family != 1) {
+        int64_t s = 1;
+        if (tiles > 0 && tiles < target) s = (target + tiles - 1) / tiles;
+        int64_t smax = ksteps / 4;
+        if (smax < 1) smax = 1;
+        if (s > smax) s = smax;
+        if (s > 16) s = 16;
+        if (s < 1) s = 1;
+        const long forced = env_long("FUSEDPROJ_SPLITS", 0);
+        if (forced > 0) s = forced < ksteps ? forced : ksteps;
+        p.splits = (int)s;
+        p.slots = (int)s;
     }
-    int64_t smax = p.family == 1 ? ksteps / 2 : ksteps / 4;
-    if (smax < 1) smax = 1;
-    if (s > smax) s = smax;
-    if (s > 16) s = 16;
-    if (s < 1) s = 1;
-    const long forced = env_long("FUSEDPROJ_SPLITS", 0);
-    if (forced > 0) s = forced < ksteps ? forced : ksteps;
-    p.splits = (int)s;
 
     size_t off = 0;
     p.stats_off = off;
     off = align256(off + (size_t)M * 8);
     p.ctr_off = off;
-    if (p.splits > 1) off = align256(off + (size_t)tiles * 4);
+    if (p.slots > 1) off = align256(off + (size_t)tiles * 4);
     p.part_off = off;
-    if (p.splits > 1) off = align256(off + (size_t)tiles * p.splits * p.tile_elems * 4);
+    if (p.slots > 1) off = align256(off + (size_t)tiles * p.slots * p.tile_elems * 4);
     p.total = off;
     return p;
 }
@@ -255,8 +274,8 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     char *ws = (char *)c.ws;
     const int act = act_code(c.act);
     float2 *stats = c.norm != FP_NORM_NONE ? (float2 *)(ws + plan.stats_off) : nullptr;
-    unsigned *ctr = plan.splits > 1 ? (unsigned *)(ws + plan.ctr_off) : nullptr;
-    const int n_ctr = plan.splits > 1 ? plan.tiles_m * plan.tiles_n : 0;
+    unsigned *ctr = plan.slots > 1 ? (unsigned *)(ws + plan.ctr_off) : nullptr;
+    const int n_ctr = plan.slots > 1 ? plan.tiles_m * plan.tiles_n : 0;
 
     if (stats || c.h_out || n_ctr) {
         fp::StatsArgs sa;
@@ -290,12 +309,13 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.tiles_m = plan.tiles_m;
     pa.tiles_n = plan.tiles_n;
     pa.splits = plan.splits;
-    pa.partials = plan.splits > 1 ? (float *)(ws + plan.part_off) : nullptr;
+    pa.slots = plan.slots;
+    pa.partials = plan.slots > 1 ? (float *)(ws + plan.part_off) : nullptr;
     pa.counters = ctr;
     const bool wi8 = c.wdt == FP_I8;
     if (plan.family == 1) {
         ProfScope ps(fp::stream_kernel_name(act, wi8, plan.sc, pa.epi), c.stream);
-        hipError_t e = fp::launch_stream(act, wi8, plan.sc, pa, c.stream);
+        hipError_t e = fp::launch_stream(act, wi8, plan.sc, pa, plan.grid, c.stream);
         if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
     } else if (plan.family == 2) {
         ProfScope ps(fp::prefill_kernel_name(act, wi8, pa.epi), c.stream);

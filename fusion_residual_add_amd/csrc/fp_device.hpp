@@ -223,11 +223,13 @@ __device__ __forceinline__ void store_swiglu(const ProjArgs &p, int64_t m, int64
 // ---------------------------------------------------------------------------
 // deterministic split-K reduction
 // ---------------------------------------------------------------------------
-// Every split of a tile stores its NACC accumulators per thread (coalesced:
-// element r of thread t at r * 256 + t), then counts itself in at the tile's
-// arrival counter.  The last split to arrive reads all partials and sums them
-// in split order 0, 1, ..., S-1 (so the sum never depends on arrival order)
-// and returns true; the others return false and exit.
+// Every contributor to a tile (a K split, or a workgroup sharing the tile in
+// the stream kernel) stores its NACC accumulators per thread in its slot
+// (coalesced: element r of thread t at r * 256 + t), then counts itself in
+// at the tile's arrival counter.  The last of the `count` contributors to
+// arrive reads all partials and sums them in slot order 0, 1, ..., count - 1
+// (so the sum never depends on arrival order) and returns true; the others
+// return false and go on without the tile.
 //
 // Coherence across the XCDs' private L2s without whole-cache maintenance: the
 // partials are only ever written and read with device-scope accesses (stores
@@ -238,11 +240,12 @@ __device__ __forceinline__ void store_swiglu(const ProjArgs &p, int64_t m, int64
 // The counters are cleared by the statistics kernel that precedes every
 // split launch on the same stream.
 template <int NACC>
-__device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int z, float (&acc)[NACC]) {
+__device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int slot, int count,
+                                              float (&acc)[NACC]) {
     __shared__ int s_last;
     const int tid = threadIdx.x;
     const int64_t tile_elems = (int64_t)NACC * 256;
-    float *mine = p.partials + ((int64_t)tile * p.splits + z) * tile_elems;
+    float *mine = p.partials + ((int64_t)tile * p.slots + slot) * tile_elems;
 #pragma unroll
     for (int r = 0; r < NACC; ++r)
         __hip_atomic_store(&mine[r * 256 + tid], acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -251,16 +254,16 @@ __device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int z
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (unsigned)(p.splits - 1);
+        s_last = prev == (unsigned)(count - 1);
     }
     __syncthreads();
     if (!s_last) return false;
-    const float *base = p.partials + (int64_t)tile * p.splits * tile_elems;
+    const float *base = p.partials + (int64_t)tile * p.slots * tile_elems;
 #pragma unroll
     for (int r = 0; r < NACC; ++r) acc[r] = 0.f;
     if constexpr (NACC > 64) {
         // large tiles: 64 values in flight at a time, split by split, in order
-        for (int zz = 0; zz < p.splits; ++zz) {
+        for (int zz = 0; zz < count; ++zz) {
 #pragma unroll
             for (int r0 = 0; r0 < NACC; r0 += 64) {
                 float v[64];
@@ -276,13 +279,13 @@ __device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int z
     }
     // G splits' worth of partials in flight at once, then added in order
     constexpr int G = NACC >= 64 ? 1 : 64 / NACC;
-    for (int z0 = 0; z0 < p.splits; z0 += G) {
+    for (int z0 = 0; z0 < count; z0 += G) {
         float v[G][NACC];
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int r = 0; r < NACC; ++r)
-                v[g][r] = z0 + g < p.splits
+                v[g][r] = z0 + g < count
                               ? __hip_atomic_load(&base[(z0 + g) * tile_elems + r * 256 + tid],
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                               : 0.f;

@@ -48,7 +48,9 @@ struct ProjArgs {
     int64_t M, K, Nw;       // Nw = weight rows
     // tiling
     int tiles_m, tiles_n, splits;
-    float *partials;        // split-K partial sums (splits > 1)
+    int slots;              // partial-sum slots per tile (split count, or the most
+                            // workgroups sharing one tile in the stream kernel)
+    float *partials;        // [tile][slot][tile elements] partial sums
     unsigned *counters;     // per-tile arrival counters (splits > 1)
 };
 
@@ -72,7 +74,8 @@ hipError_t launch_tiled(int act, bool w_i8, int tile, const ProjArgs &a, hipStre
 //  u: 32-wide k slices per chunk (8) -> K must be a multiple of 32 * u.
 //  tiles_m must be 1.
 struct StreamCfg { int mf, nr, u; };
-hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, hipStream_t s);
+// grid_wgs workgroups share the (weight tile, K chunk) units evenly
+hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s);
 hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,
                           hipStream_t s);
 

@@ -351,7 +351,7 @@ void prefill_kernel(ProjArgs p) {
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) flat[(i * 4 + j) * 16 + e] = acc[i][j][e];
-        if (!splitk_reduce(p, tile, z, flat)) return;
+        if (!splitk_reduce(p, tile, z, p.splits, flat)) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll

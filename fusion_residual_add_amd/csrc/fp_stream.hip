@@ -11,11 +11,10 @@ void launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hi
 void launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 void launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 
-hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, hipStream_t s) {
-    const int64_t g = (int64_t)a.tiles_n * a.splits;
-    if (g <= 0) return hipSuccess;
+hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s) {
+    if (grid_wgs <= 0 || a.tiles_n <= 0) return hipSuccess;
     if (a.epi == EPI_SWIGLU && c.nr % 2 != 0) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)g;
+    const unsigned grid = (unsigned)grid_wgs;
     if (w_i8) launch_stream_i8(c, a, grid, s);
     else if (act == ACT_F16) launch_stream_f16(c, a, grid, s);
     else launch_stream_bf16(c, a, grid, s);

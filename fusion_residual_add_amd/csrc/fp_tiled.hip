@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs p) {
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) flat[(i * FN + j) * 4 + e] = acc[i][j][e];
-        if (!splitk_reduce(p, tile, z, flat)) return;
+        if (!splitk_reduce(p, tile, z, p.splits, flat)) return;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
