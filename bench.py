@@ -171,6 +171,128 @@ def load_traffic(kernel_key: str):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters and kernel-trace summaries
+# ---------------------------------------------------------------------------
+_ACT = {"0": "f32", "1": "f16", "2": "bf16"}
+_EPI = {"0": "qkv", "1": "swiglu", "2": "gelu", "3": "linear"}
+
+
+def library_kernel_name(cxx: str) -> str:
+    """The library profiler's name of a kernel from the demangled C++ name rocprofv3 prints."""
+    import re
+    m = re.search(r"fp::stream_kernel<(\d), (true|false), (\d+), (\d+), (\d+), (\d)>", cxx)
+    if m:
+        act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
+        return (f"stream_kernel<{act},m{16 * int(m.group(3))},n{64 * int(m.group(4))},"
+                f"k{32 * int(m.group(5))},{_EPI[m.group(6)]}>")
+    m = re.search(r"fp::prefill_kernel<(\d), (true|false), (\d)>", cxx)
+    if m:
+        act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
+        return f"prefill_kernel<{act},256x256,{_EPI[m.group(3)]}>"
+    m = re.search(r"fp::stats_kernel<(\d), \d+>", cxx)
+    if m:
+        return f"stats_kernel<{_ACT[m.group(1)]}>"
+    return cxx
+
+
+def traffic_probe(wl_name: str) -> None:
+    """Workload run under `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE): an
+    elementwise pass over 1 GiB (reads 1 GiB, writes 1 GiB: the calibration of
+    the counters) and six calls of each projection of the workload."""
+    import torch
+    from fusion_residual_add_amd import inputs
+    n = (1 << 30) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    wl = inputs.workload(wl_name)
+    run = Runner(wl)
+    for i in range(6):
+        if wl.n_qkv:
+            run.qkv(i)
+        run.gu(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": wl_name, "calibration_bytes": 2 * n}), flush=True)
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return per
+
+
+def traffic_summarize(wl_name: str, fetch_dir: str, write_dir: str, cmds: str) -> None:
+    """profiles/traffic.json and a text summary from the two counter runs of --traffic-probe."""
+    import statistics
+    fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    calib = 1 << 30
+    cal = [k for k in fetch if "neg" in k.lower()]
+    if not cal:
+        raise SystemExit("calibration kernel not found in the counter output")
+    kf = calib / (statistics.median(fetch[cal[0]]) * 1024.0)
+    kw = calib / (statistics.median(write[cal[0]]) * 1024.0)
+    kernels, lines = {}, []
+    for name in sorted(fetch):
+        if "fp::" not in name:
+            continue
+        f_b = statistics.median(fetch[name]) * 1024.0 * kf
+        w_b = statistics.median(write.get(name, [0.0])) * 1024.0 * kw
+        lib = library_kernel_name(name)
+        kernels[f"{wl_name}:{lib}"] = {"bytes_per_launch": round(f_b + w_b), "fetch_bytes": round(f_b),
+                                       "write_bytes": round(w_b), "launches": len(fetch[name])}
+        lines.append(f"| `{lib}` | {len(fetch[name])} | {f_b / 1e6:.2f} | {w_b / 1e6:.2f} | {(f_b + w_b) / 1e6:.2f} |")
+    out = {"source_hash": kernel_source_hash(), "workload": wl_name,
+           "calibration": {"kernel": cal[0], "bytes_each_way": calib, "fetch_factor": round(kf, 4),
+                           "write_factor": round(kw, 4)},
+           "kernels": kernels}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    md = [f"# HBM traffic per launch, {wl_name}", "",
+          "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, L2 to memory), one rocprofv3 run each,",
+          "scaled by what they read for an elementwise pass that reads and writes 1 GiB",
+          f"(fetch factor {kf:.4f}, write factor {kw:.4f}).", "",
+          "Commands (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```", cmds, "```", "",
+          "| kernel | dispatches | fetch MB | write MB | total MB |", "|---|---|---|---|---|"] + lines
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl_name}.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(json.dumps(out))
+
+
+def trace_summarize(tag: str, trace_dir: str, cmd: str) -> None:
+    """profiles/kernel_trace_<tag>.md from a `rocprofv3 --kernel-trace --stats` output directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
+    rows = []
+    with open(files[0]) as fh:
+        for row in csv.DictReader(fh):
+            rows.append(row)
+    md = [f"# Kernel trace, {tag}", "", "Command (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):",
+          "", "```", cmd, "```", "", "| kernel (library name) | calls | avg us | min us | max us | share |",
+          "|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| `{library_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     import oracle
     from fusion_residual_add_amd import inputs
@@ -202,7 +324,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="calibration pass + projection calls, to run under rocprofv3 --pmc")
+    ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from the two counter runs of --traffic-probe")
+    ap.add_argument("--trace-summarize", nargs=2, metavar=("TAG", "TRACE_DIR"),
+                    help="write profiles/kernel_trace_TAG.md from a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--cmd", default="", help="the profiling command(s), recorded in the summary")
     args = ap.parse_args()
+    if args.traffic_summarize:
+        traffic_summarize(args.workload, *args.traffic_summarize, args.cmd)
+        return
+    if args.trace_summarize:
+        trace_summarize(*args.trace_summarize, args.cmd)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the projections shard by heads / by gate-up pairs without communication; "
@@ -215,6 +350,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
 
+    if args.traffic_probe:
+        traffic_probe(args.workload)
+        return
     wl = inputs.workload(args.workload)
     run = Runner(wl)
     ms = time_steps(run.step, args.steps, args.warmup)
