@@ -189,7 +189,7 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::prefill_kernel<(\d), (true|false), (\d)>", cxx)
     if m:
         act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
-        return f"prefill_kernel<{act},256x256,{_EPI[m.group(3)]}>"
+        return f"prefill_kernel<{act},128x512,{_EPI[m.group(3)]}>"
     m = re.search(r"fp::stats_kernel<(\d), \d+>", cxx)
     if m:
         return f"stats_kernel<{_ACT[m.group(1)]}>"

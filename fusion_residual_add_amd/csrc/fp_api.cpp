@@ -36,7 +36,7 @@ int act_code(fp_dtype d) {
 // launch plan
 // ---------------------------------------------------------------------------
 struct Plan {
-    int family = 0;           // 0 tiled (128 x 128), 1 stream (decode), 2 prefill (256 x 256)
+    int family = 0;           // 0 tiled (128 x 128), 1 stream (decode), 2 prefill (128 x 512)
     int tile = 0;             // tiled: TileCfg
     fp::StreamCfg sc{1, 2, 8};
     int tiles_m = 0, tiles_n = 0, splits = 1;
@@ -56,7 +56,7 @@ long env_long(const char *name, long dflt) {
 
 // Decode token counts (M <= 64, 16-bit activations) use the weight-streaming
 // kernel, which spreads (tile, K chunk) units evenly over one workgroup per
-// CU; token counts above 256 the 256 x 256 prefill kernel; everything else
+// CU; token counts above 256 the 128 x 512 prefill kernel; everything else
 // the tiled kernel.  When a tiled grid would hold too few workgroups, K is
 // split.  Partial sums are reduced by the last contributor to arrive, in a
 // fixed order.
@@ -102,9 +102,9 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
     } else if (act != FP_F32 && M > 256 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32) &&
                env_long("FUSEDPROJ_NO_PREFILL", 0) == 0) {
         p.family = 2;
-        p.tiles_m = (int)((M + 255) / 256);
-        p.tiles_n = (int)((Nw + 255) / 256);
-        p.tile_elems = 256 * 256;
+        p.tiles_m = (int)((M + 127) / 128);
+        p.tiles_n = (int)((Nw + 511) / 512);
+        p.tile_elems = 128 * 512;
         tiles = (int64_t)p.tiles_m * p.tiles_n;
         ksteps = K / 64;
         target = 128;

@@ -239,10 +239,20 @@ __device__ __forceinline__ void store_swiglu(const ProjArgs &p, int64_t m, int64
 // ordinary (L2-cached) accesses, so no L2 write-back or invalidate is needed.
 // The counters are cleared by the statistics kernel that precedes every
 // split launch on the same stream.
-template <int NACC>
+// `flag`: an int of LDS for the arrival verdict, or null for a static one
+// (kernels that use all of LDS pass a word of a tile buffer they are done
+// with)
+template <int NACC, bool EXT_FLAG = false>
 __device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int slot, int count,
-                                              float (&acc)[NACC]) {
-    __shared__ int s_last;
+                                              float (&acc)[NACC], int *flag = nullptr) {
+    int *s_last_p;
+    if constexpr (EXT_FLAG) {
+        s_last_p = flag;
+    } else {
+        __shared__ int s_last_own;
+        s_last_p = &s_last_own;
+    }
+    int &s_last = *s_last_p;
     const int tid = threadIdx.x;
     const int64_t tile_elems = (int64_t)NACC * 256;
     float *mine = p.partials + ((int64_t)tile * p.slots + slot) * tile_elems;

@@ -2,23 +2,26 @@
 // projection is bound by the matrix cores (the pages' prefill regime,
 // "TensorRT-LLM 深度工程实践…", §3.1).
 //
-// One workgroup (4 waves, 2 x 2) computes a 256 x 256 tile; each wave a
-// 128 x 128 sub-tile as 4 x 4 fragments of v_mfma_f32_32x32x16 (bf16 / f16)
-// with fp32 accumulators (256 per lane, all in AGPRs: the 32 x 32 shape keeps
-// them in 16-register tuples that the allocator leaves in place).  K advances in steps
-// of 64 through a double-buffered LDS pair of A (normalised activations) and
-// B (weights) tiles, 32 KB each per stage:
-//  * B: 16-bit weights go from HBM straight into LDS (global_load_lds, 16 bytes
-//    per lane, one 1 KB wave instruction = 8 rows x 128 bytes); int8 weights
-//    go through registers and are dequantised to bf16 on the way;
-//  * A: x and the residual are read (L2 hits: a 256-row block is shared by
+// One workgroup computes a 128 (tokens) x 512 (weight rows) tile with 4
+// waves side by side; each wave a 128 x 128 sub-tile as 4 x 4 fragments of
+// v_mfma_f32_32x32x16 (bf16 / f16) with fp32 accumulators (256 per lane, all
+// in AGPRs: the 32 x 32 shape keeps them in 16-register tuples that the
+// allocator leaves in place).  K advances in steps of 64 through two LDS
+// stages of A (normalised activations, 16 KB) and B (weights, 64 KB): the
+// whole 160 KB of LDS.
+//  * B: 16-bit weights go from HBM straight into LDS (buffer_load ... lds, 16
+//    bytes per lane, one 1 KB wave instruction = 8 rows x 128 bytes); int8
+//    weights go through registers and are dequantised to bf16 on the way.
+//  * A: x and the residual are read (L2 hits: a 128-row block is shared by
 //    every column tile), re-formed as h, normalised with the row statistics
 //    and gamma / beta, rounded to the activation dtype and written to LDS -
 //    the normalised rows never reach memory (the LayerNorm + QKV fusion of
-//    §2.3).  The next K step's tile is produced while the current one feeds
-//    the MFMAs.
-// Both LDS tiles store 16-byte chunks XOR-swizzled by row, so that the 16
-// rows a fragment read touches land in 16 different bank groups.
+//    §2.3).  A tile 4 times wider than it is tall halves the rows each
+//    workgroup normalises per MFMA compared with a square tile: the
+//    normalisation is VALU work that has to hide in the MFMAs' shadow, the
+//    weight tile costs no VALU at all.
+// Both LDS tiles store 16-byte chunks XOR-swizzled by row, so that the rows
+// of a fragment read spread over the banks.
 // The epilogue applies bias and the GQA split / SwiGLU / tanh-GELU / nothing,
 // stages the results through LDS and writes 16 bytes per lane.
 #pragma once
@@ -38,9 +41,10 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned ch
     (void)r, (void)lds, (void)voff, (void)soff;
 #endif
 }
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 128, BN = 512, BK = 64;
 constexpr int ROWB = BK * 2;                 // bytes per tile row (bf16 / f16)
-constexpr int TILEB = BM * ROWB;             // 32 KB per operand tile
+constexpr int TILEA = BM * ROWB;             // 16 KB
+constexpr int TILEB = BN * ROWB;             // 64 KB
 // swizzled byte offset of 16-byte chunk c (0..7) of tile row r
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
 }  // namespace pf
@@ -55,22 +59,21 @@ void prefill_kernel(ProjArgs p) {
     // A and B tiles of the two stages as four distinct LDS objects, so that
     // the compiler can tell the direct-to-LDS weight loads into one stage from
     // the fragment reads of the other (and waits for them only at the end of
-    // the step, not before the first fragment read).  The A tiles are
-    // reused as epilogue staging after the main loop.
-    __shared__ __attribute__((aligned(16))) unsigned char lA0[TILEB];
-    __shared__ __attribute__((aligned(16))) unsigned char lA1[TILEB];
+    // the step, not before the first fragment read).  The B tiles are reused
+    // as epilogue staging after the main loop.
+    __shared__ __attribute__((aligned(16))) unsigned char lA0[TILEA];
+    __shared__ __attribute__((aligned(16))) unsigned char lA1[TILEA];
     __shared__ __attribute__((aligned(16))) unsigned char lB0[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char lB1[TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
 
     // ---- tile of this workgroup: XCD-aware remap, then grouped raster
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = logical / p.splits, z = logical % p.splits;
     int tm, tn;
     {
-        constexpr int GROUP_M = 4;
+        constexpr int GROUP_M = 8;
         const int group = GROUP_M * p.tiles_n;
         const int gid = tile / group, first = gid * GROUP_M;
         const int gsz = min(p.tiles_m - first, GROUP_M);
@@ -84,13 +87,11 @@ void prefill_kernel(ProjArgs p) {
 
     // ---- buffer resources: base and byte size in scalar registers, so each
     // stream needs one 32-bit per-lane offset and the K advance is a scalar
-    // offset (keeps the vector register budget for the accumulators)
-    const unsigned ebytes_a = 2;
-    const uint32_t xbytes = (uint32_t)(p.M * p.K * ebytes_a);
+    // offset (keeps the vector register budget for the accumulators).
+    // Absent optional operands get an empty range: their loads return zero.
+    const uint32_t xbytes = (uint32_t)(p.M * p.K * 2);
     const bool has_res = p.res != nullptr;
     const bool has_beta = p.norm == 2 && p.beta != nullptr;
-    // absent optional operands get an empty range (their loads return zero);
-    // the arithmetic below ignores them as well
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, (short)0, xbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void *)(has_res ? p.res : p.x), (short)0,
                                                                         has_res ? xbytes : 0u, 0x00020000);
@@ -104,14 +105,14 @@ void prefill_kernel(ProjArgs p) {
     // norm none: gamma reads as zero and g1 turns it into one
     const float g1 = p.norm != 0 ? 0.f : 1.f;
 
-    // ---- A side: thread -> 16-byte chunk a_c of tile rows a_r0 + 32 i (i < 8)
+    // ---- A side: thread -> 16-byte chunk a_c of tile rows a_r0 + 32 i (i < 4)
     const int a_c = tid & 7, a_r0 = tid >> 3;
     const float2 *stp = p.norm != 0 ? p.stats : (const float2 *)p.x;
     const float st_on = p.norm != 0 ? 1.f : 0.f;
-    uint32_t a_off[8];                                   // bytes, without the K step
-    float a_mu[8], a_rs[8];
+    uint32_t a_off[4];                                   // bytes, without the K step
+    float a_mu[4], a_rs[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         int m = tm * BM + a_r0 + 32 * i;
         m = m < (int)p.M ? m : (int)p.M - 1;             // rows past M only feed unstored outputs
         a_off[i] = ((uint32_t)m * (uint32_t)p.K + a_c * 8) * 2;
@@ -121,19 +122,22 @@ void prefill_kernel(ProjArgs p) {
     }
 
     // ---- B side
-    // 16-bit weights: wave w loads tile rows [64 w, 64 w + 64) as 8 instructions
-    // of 8 rows; lane l of instruction i covers row 64 w + 8 i + l / 8 at LDS
-    // chunk position l % 8, i.e. global chunk (l % 8) ^ swizzle(row).
+    // 16-bit weights: wave w loads tile rows [128 w, 128 w + 128) as 16
+    // instructions of 8 rows; lane l of instruction i covers row
+    // 128 w + 8 i + l / 8 at LDS chunk position l % 8, i.e. global chunk
+    // (l % 8) ^ swizzle(row).
     // int8 weights: thread -> 16-byte int8 vector (tile row (tid / 4) + 64 i,
     // k bytes 16 (tid % 4) .. + 15), dequantised in registers.
-    constexpr int NBO = WI8 ? 4 : 8;
+    constexpr int NBO = WI8 ? 8 : 16;
     uint32_t b_off[NBO];                                 // bytes, without the K step
-    float b_sc[4] = {0.f, 0.f, 0.f, 0.f};
+    float b_sc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b_sc[i] = 0.f;
 #pragma unroll
     for (int i = 0; i < NBO; ++i) {
         int br;
         if constexpr (WI8) br = (tid >> 2) + 64 * i;
-        else br = 64 * wave + 8 * i + (lane >> 3);
+        else br = 128 * wave + 8 * i + (lane >> 3);
         int64_t wrow;
         if constexpr (EPI == EPI_SWIGLU) {
             // 32-row blocks alternate gate / up: fragment pairs (2 j, 2 j + 1)
@@ -159,8 +163,8 @@ void prefill_kernel(ProjArgs p) {
     // kt + 1 are normalised into LDS while stage kt feeds the MFMAs, and each
     // row's registers are refilled with stage kt + 2 right after use, so every
     // load has a whole step to arrive.
-    struct ARegs { u32x4 x[8], r[8], g, b; };
-    struct BRegs { u32x4 q[4]; };   // int8 path only
+    struct ARegs { u32x4 x[4], r[4], g, b; };
+    struct BRegs { u32x4 q[8]; };   // int8 path only
     ARegs A;
     BRegs B;
     float gv[8], bv[8];             // gamma / beta of the stage being normalised
@@ -184,33 +188,34 @@ void prefill_kernel(ProjArgs p) {
         for (int e = 0; e < 8; ++e) gv[e] += g1;
     };
     // h = x + r (r reads as zero when absent; exact in fp32),
-    // n = (h - mu) * rstd * gamma + beta
-    auto a_norm = [&](unsigned char *la, int i) {
-        float n[8];
+    // n = (h - mu) * rstd * gamma + beta, for words [w0, w0 + 2) of row i
+    auto a_norm = [&](int i, int w0, float (&n)[8]) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = w0; w < w0 + 2; ++w) {
             const unsigned xw = A.x[i][w], rv = A.r[i][w];
             const float d0 = (T::lo(xw) + T::lo(rv)) - a_mu[i];
             const float d1 = (T::hi(xw) + T::hi(rv)) - a_mu[i];
             n[2 * w] = fmaf(d0 * a_rs[i], gv[2 * w], bv[2 * w]);
             n[2 * w + 1] = fmaf(d1 * a_rs[i], gv[2 * w + 1], bv[2 * w + 1]);
         }
+    };
+    auto a_store = [&](unsigned char *la, int i, const float (&n)[8]) {
         *(u32x4 *)(la + swz(a_r0 + 32 * i, a_c)) = T::pack(n);
     };
     // ---- weight side
     auto bload_lds = [&](int kt, unsigned char *lb) {   // 16-bit weights, straight to LDS
         const uint32_t kb = (uint32_t)kt * (BK * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) load_lds16(rw, lb + (64 * wave + 8 * i) * ROWB, b_off[i], kb);
+        for (int i = 0; i < 16; ++i) load_lds16(rw, lb + (128 * wave + 8 * i) * ROWB, b_off[i], kb);
     };
     auto bload_regs = [&](int kt) {   // int8 weights
         const uint32_t kb = (uint32_t)kt * BK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) B.q[i] = ld16(rw, b_off[i], kb);
+        for (int i = 0; i < 8; ++i) B.q[i] = ld16(rw, b_off[i], kb);
     };
     auto bstore_regs = [&](unsigned char *lb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             u32x4 lo, hi;
             dequant16(B.q[i], b_sc[i], lo, hi);
             const int br = (tid >> 2) + 64 * i;
@@ -231,20 +236,21 @@ void prefill_kernel(ProjArgs p) {
     // MFMAs of one stage: four K substeps of 16; lane l supplies row / column
     // l % 32 and the 16-byte chunk 2 t + l / 32 of both operands.  A stage is
     // run as 8 regions (substep t = r / 2, fragment columns 2 h, 2 h + 1 with
-    // h = r % 2), each 8 MFMAs with one activation row of the next stage
-    // normalised into `na` between them (and its registers refilled from
-    // stage `kn`), while the fragments of the following region are read from
-    // LDS.  Scheduling barriers keep each region's instruction mix in place:
-    // every MFMA is followed by a handful of VALU instructions, which run in
-    // the MFMA's shadow.
+    // h = r % 2), each 8 MFMAs with half an activation row of the next stage
+    // normalised between them (row r / 2; after its second half the row is
+    // stored into `na` and its registers refilled from stage `kn`), while the
+    // fragments of the following region are read from LDS.  Scheduling
+    // barriers keep each region's instruction mix in place: every MFMA is
+    // followed by a few VALU instructions, which run in its shadow.
     auto frag_a = [&](const unsigned char *la, int t, int i) {
-        return *(const u32x4 *)(la + swz(wm * 128 + i * 32 + (lane & 31), 2 * t + (lane >> 5)));
+        return *(const u32x4 *)(la + swz(i * 32 + (lane & 31), 2 * t + (lane >> 5)));
     };
     auto frag_b = [&](const unsigned char *lb, int t, int j) {
-        return *(const u32x4 *)(lb + swz(wn * 128 + j * 32 + (lane & 31), 2 * t + (lane >> 5)));
+        return *(const u32x4 *)(lb + swz(wave * 128 + j * 32 + (lane & 31), 2 * t + (lane >> 5)));
     };
     auto mma = [&](const unsigned char *la, const unsigned char *lb, unsigned char *na, int kn) {
         u32x4 af[4], bf[2], nf[4], nbf[2];
+        float n[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[i] = frag_a(la, 0, i);
         bf[0] = frag_b(lb, 0, 0);
@@ -268,13 +274,16 @@ void prefill_kernel(ProjArgs p) {
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i][2 * h + jj] = T::mfma32(af[i], bf[jj], acc[i][2 * h + jj]);
-            a_norm(na, r);
-            a_issue(kn, r);
+            a_norm(r >> 1, 2 * h, n);
+            if (h == 1) {
+                a_store(na, r >> 1, n);
+                a_issue(kn, r >> 1);
+            }
             __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS reads
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // then VALU
             }
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
             __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // row loads
@@ -290,13 +299,13 @@ void prefill_kernel(ProjArgs p) {
         }
     };
     // wait for everything but the activation loads issued after the weights
-    // of the step (2 gamma / beta + 16 row loads), and for this thread's LDS
+    // of the step (2 gamma / beta + 8 row loads), and for this thread's LDS
     // writes; then a workgroup barrier.  The count relies on issue order:
     // every weight load is fenced by a scheduling barrier before anything
     // else is issued.  The empty asm statements keep the compiler from moving
     // memory accesses across the barrier.
     auto step_sync = [&]() {
-        constexpr int VM = 18;
+        constexpr int VM = 10;
         __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
         __asm__ __volatile__("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -309,15 +318,20 @@ void prefill_kernel(ProjArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         gb_issue(kt0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a_issue(kt0, i);
+        for (int i = 0; i < 4; ++i) a_issue(kt0, i);
         gb_unpack();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a_norm(lA0, i);
+        for (int i = 0; i < 4; ++i) {
+            float n[8];
+            a_norm(i, 0, n);
+            a_norm(i, 2, n);
+            a_store(lA0, i, n);
+        }
         if constexpr (WI8) bstore_regs(lB0);
         const int k1 = kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1;
         gb_issue(k1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a_issue(k1, i);
+        for (int i = 0; i < 4; ++i) a_issue(k1, i);
         step_sync();
         // stage identity alternates; both pointers of a pair come from one
         // condition, so alias analysis still separates the objects.  Every
@@ -342,7 +356,8 @@ void prefill_kernel(ProjArgs p) {
         __syncthreads();
     }
 
-    // ---- split-K
+    // ---- split-K (the arrival verdict lives in the first word of lA0, which
+    // nobody reads any more)
     if (p.splits > 1) {
         float flat[256];
 #pragma unroll
@@ -351,7 +366,7 @@ void prefill_kernel(ProjArgs p) {
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) flat[(i * 4 + j) * 16 + e] = acc[i][j][e];
-        if (!splitk_reduce(p, tile, z, p.splits, flat)) return;
+        if (!splitk_reduce<256, true>(p, tile, z, p.splits, flat, (int *)lA0)) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -368,9 +383,9 @@ void prefill_kernel(ProjArgs p) {
     // a time.
     constexpr int OUTC = EPI == EPI_SWIGLU ? 64 : 128;   // output columns per wave
     constexpr int SROW = OUTC * 4 + 32;                  // staging row pitch, bytes
-    static_assert(32 * SROW <= TILEB, "staging fits one tile object");
-    unsigned char *stg = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
-    const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)tn * (BN / 2) + wn * 64 : (int64_t)tn * BN + wn * 128;
+    static_assert(32 * SROW <= TILEB / 2, "staging fits half a B tile");
+    unsigned char *stg = (wave < 2 ? lB0 : lB1) + (wave & 1) * (TILEB / 2);
+    const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)tn * (BN / 2) + wave * 64 : (int64_t)tn * BN + wave * 128;
     const int64_t ncols = EPI == EPI_SWIGLU ? p.F : p.Nw;
     // bias of this lane's columns, zero when absent (SwiGLU: gate, up, gate, up)
     float bias_v[4] = {0.f, 0.f, 0.f, 0.f};
@@ -399,8 +414,8 @@ void prefill_kernel(ProjArgs p) {
 #pragma unroll
                 for (int j = 0; j < 4; j += 2) {
                     const int cl = (j >> 1) * 32 + (lane & 31);        // 0..63
-                    const float gv = acc[i][j][q] + bias_v[j], uv = acc[i][j + 1][q] + bias_v[j + 1];
-                    *(float *)(stg + rl * SROW + cl * 4) = silu(gv) * uv;
+                    const float gv2 = acc[i][j][q] + bias_v[j], uv = acc[i][j + 1][q] + bias_v[j + 1];
+                    *(float *)(stg + rl * SROW + cl * 4) = silu(gv2) * uv;
                 }
             } else {
 #pragma unroll
@@ -420,7 +435,7 @@ void prefill_kernel(ProjArgs p) {
         for (int it = 0; it < 32 * RUNS / 64; ++it) {
             const int idx = it * 64 + lane;
             const int rl = idx / RUNS, ch = idx % RUNS;
-            const int64_t m = (int64_t)tm * BM + wm * 128 + i * 32 + rl;
+            const int64_t m = (int64_t)tm * BM + i * 32 + rl;
             const int64_t cg = col0 + ch * 8;
             const f32x4 v0 = *(const f32x4 *)(stg + rl * SROW + ch * 32);
             const f32x4 v1 = *(const f32x4 *)(stg + rl * SROW + ch * 32 + 16);

@@ -39,7 +39,7 @@ const char *prefill_kernel_name(int act, bool w_i8, int epi) {
     static const char *acts[4] = {"f32", "f16", "bf16", "bf16-i8w"};
     static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
     thread_local char buf[64];
-    snprintf(buf, sizeof buf, "prefill_kernel<%s,256x256,%s>", acts[w_i8 ? 3 : act], epis[epi]);
+    snprintf(buf, sizeof buf, "prefill_kernel<%s,128x512,%s>", acts[w_i8 ? 3 : act], epis[epi]);
     return buf;
 }
 
