@@ -293,6 +293,34 @@ def trace_summarize(tag: str, trace_dir: str, cmd: str) -> None:
     print("\n".join(md))
 
 
+def all_configs(steps: int) -> None:
+    """One JSON line per workload: per-call kernel times and the roofline
+    fraction of each call (HBM GB/s when the call is bandwidth-bound, MFMA
+    TFLOP/s otherwise)."""
+    import torch
+    from fusion_residual_add_amd import inputs
+    for name in inputs.WORKLOADS:
+        wl = inputs.workload(name)
+        run = Runner(wl)
+        ms = time_steps(run.step, steps, 3)
+        calls = {}
+        for call in (["qkv"] if wl.n_qkv else []) + ["gu"]:
+            prof = profile_call(run, call, 20)
+            total = sum(prof.values())
+            b, f = algo_bytes(wl, call), flops(wl, call)
+            mem_bound = f / b < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+            peak = HBM_PEAK_GBS if mem_bound else (MFMA_BF16_PEAK_TFLOPS if wl.act != "f32" else 157.3)
+            rate = b / (total * 1e-3) / 1e9 if mem_bound else f / (total * 1e-3) / 1e12
+            calls[call] = {"kernels_us": {k: round(v * 1e3, 2) for k, v in prof.items()},
+                           "bound": "hbm" if mem_bound else "mfma",
+                           "rate": round(rate, 1), "unit": "GB/s" if mem_bound else "TFLOP/s",
+                           "frac": round(rate / peak, 4)}
+        print(json.dumps({"workload": name, "M": wl.M, "hidden": wl.hidden, "act": wl.act, "weights": wl.wdt,
+                          "ms_per_step": round(ms, 5), "calls": calls}), flush=True)
+        del run
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     import oracle
     from fusion_residual_add_amd import inputs
@@ -331,6 +359,8 @@ def main():
     ap.add_argument("--trace-summarize", nargs=2, metavar=("TAG", "TRACE_DIR"),
                     help="write profiles/kernel_trace_TAG.md from a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--cmd", default="", help="the profiling command(s), recorded in the summary")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="per-call times and roofline fractions of every workload, one JSON line each")
     args = ap.parse_args()
     if args.traffic_summarize:
         traffic_summarize(args.workload, *args.traffic_summarize, args.cmd)
@@ -352,6 +382,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(args.workload)
+        return
+    if args.all_configs:
+        all_configs(min(args.steps, 20))
         return
     wl = inputs.workload(args.workload)
     run = Runner(wl)

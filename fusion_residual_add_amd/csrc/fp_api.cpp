@@ -56,29 +56,36 @@ long env_long(const char *name, long dflt) {
 
 // Decode token counts (M <= 64, 16-bit activations) use the weight-streaming
 // kernel, which spreads (tile, K chunk) units evenly over one workgroup per
-// CU; token counts above 256 the 128 x 512 prefill kernel; everything else
+// CU; token counts above 64 the 128 x 512 prefill kernel; everything else
 // the tiled kernel.  When a tiled grid would hold too few workgroups, K is
 // split.  Partial sums are reduced by the last contributor to arrive, in a
 // fixed order.
 // FUSEDPROJ_* environment variables override the choices (for tuning sweeps);
 // the workspace query and the call read them alike.
-Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
+Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu) {
     Plan p;
-    const int u = 8;
-    const bool stream_ok = act != FP_F32 && M <= 64 && K % (32 * u) == 0 &&
+    const bool stream_ok = act != FP_F32 && M <= 64 && K % 256 == 0 &&
                            env_long("FUSEDPROJ_NO_STREAM", 0) == 0;
     int64_t tiles, ksteps, target;
     if (stream_ok) {
         p.family = 1;
         p.sc.mf = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-        p.sc.nr = swiglu ? 2 : (int)(env_long("FUSEDPROJ_STREAM_NR", 2) == 1 ? 1 : 2);
-        p.sc.u = u;
+        // weight rows per workgroup 64 * nr: int8 weights at 33..64 tokens take
+        // 256 when that still leaves >= 128 tiles (the A tile every workgroup
+        // normalises is then amortised over twice the weight rows; measured on
+        // MI355X: Llama-2-70B gate/up at 64 tokens 232 -> 186 us, while fewer
+        // rows per workgroup stay faster at 1 and 16 tokens and for QKV)
+        const long nr_env = env_long("FUSEDPROJ_STREAM_NR", 0);
+        p.sc.nr = wdt == FP_I8 && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
+        if (nr_env == 1 && !swiglu) p.sc.nr = 1;
+        if (nr_env == 2 || (nr_env == 4 && wdt == FP_I8)) p.sc.nr = (int)nr_env;
+        p.sc.u = p.sc.mf >= 4 ? 4 : 8;      // K chunk 32 * u: must match the launcher
         const int nb = 64 * p.sc.nr;
         p.tiles_m = 1;
         p.tiles_n = (int)((Nw + nb - 1) / nb);
         p.tile_elems = (int64_t)16 * p.sc.mf * nb;
         tiles = p.tiles_n;
-        ksteps = K / (32 * u);
+        ksteps = K / (32 * p.sc.u);
         target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
         // stream-K: `grid` workgroups take equal contiguous unit ranges of at
         // least 4 chunks (measured on MI355X: the QKV shape of Llama-3-8B
@@ -99,7 +106,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
             if (n > most) most = n;
         }
         p.slots = (int)most;
-    } else if (act != FP_F32 && M > 256 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32) &&
+    } else if (act != FP_F32 && M > 64 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32) &&
                env_long("FUSEDPROJ_NO_PREFILL", 0) == 0) {
         p.family = 2;
         p.tiles_m = (int)((M + 127) / 128);
@@ -107,7 +114,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
         p.tile_elems = 128 * 512;
         tiles = (int64_t)p.tiles_m * p.tiles_n;
         ksteps = K / 64;
-        target = 128;
+        target = 256;
     } else {
         if (M <= 16) p.tile = fp::TILE_DEC16;
         else if (M <= 32) p.tile = fp::TILE_DEC32;
@@ -124,7 +131,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, bool swiglu) {
     if (p.family != 1) {
         int64_t s = 1;
         if (tiles > 0 && tiles < target) s = (target + tiles - 1) / tiles;
-        int64_t smax = ksteps / 4;
+        // a 128 x 512 partial tile is 256 KB each way: at most 4 splits
+        int64_t smax = p.family == 2 ? (ksteps / 4 < 4 ? ksteps / 4 : 4) : ksteps / 4;
         if (smax < 1) smax = 1;
         if (s > smax) s = smax;
         if (s > 16) s = 16;
@@ -349,8 +357,8 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype ac
     if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0) return 0;
     if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
     if (M == 0) return 0;
-    const size_t a = make_plan(M, hidden, n_cols, act_dtype, false).total;
-    const size_t b = make_plan(M, hidden, n_cols, act_dtype, true).total;
+    const size_t a = make_plan(M, hidden, n_cols, act_dtype, w_dtype, false).total;
+    const size_t b = make_plan(M, hidden, n_cols, act_dtype, w_dtype, true).total;
     return a > b ? a : b;
 }
 
@@ -382,7 +390,7 @@ fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, c
     outs.push_back(rng("q", q, M * nq * eo));
     outs.push_back(rng("k", k, M * nkv * eo));
     outs.push_back(rng("v", v, M * nkv * eo));
-    const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, false);
+    const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, w_dtype, false);
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);
@@ -422,7 +430,7 @@ fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, con
     add_inputs(c, ins, "w");
     if (h_out) outs.push_back(rng("h_out", h_out, M * hidden * ea));
     outs.push_back(rng("out", out, M * ffn * eo));
-    const Plan plan = make_plan(M, hidden, Nw, act_dtype, act == FP_ACT_SWIGLU);
+    const Plan plan = make_plan(M, hidden, Nw, act_dtype, w_dtype, act == FP_ACT_SWIGLU);
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);

@@ -368,10 +368,14 @@ inline void launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStre
     }
 }
 
+// 64 token rows: 128-wide K chunks (two activation / weight register sets of
+// 256-wide chunks do not fit in the register file next to the accumulators)
 template <int ACT, bool WI8, int MF>
 inline void launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
-    if (c.nr == 1) launch_stream_cfg<ACT, WI8, MF, 1, 8>(a.epi, a, grid, s);
-    else launch_stream_cfg<ACT, WI8, MF, 2, 8>(a.epi, a, grid, s);
+    constexpr int U = MF >= 4 ? 4 : 8;
+    if (c.nr == 1) launch_stream_cfg<ACT, WI8, MF, 1, U>(a.epi, a, grid, s);
+    else if (c.nr == 2 || !WI8) launch_stream_cfg<ACT, WI8, MF, 2, U>(a.epi, a, grid, s);
+    else launch_stream_cfg<ACT, WI8, MF, 4, U>(a.epi, a, grid, s);   // int8: 256 rows share one A tile
 }
 
 template <int ACT, bool WI8>

@@ -252,6 +252,31 @@ def test_int8_workload_dequant_bits():
     assert np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), bits)
 
 
+@pytest.mark.parametrize("env", [{"FUSEDPROJ_STREAM_NR": "4"},
+                                 {"FUSEDPROJ_STREAM_NR": "4", "FUSEDPROJ_SPLITS": "3"},
+                                 {"FUSEDPROJ_STREAM_NR": "4", "FUSEDPROJ_SPLITS": "1"}],
+                         ids=lambda e: ",".join(f"{k[11:]}={v}" for k, v in e.items()))
+@pytest.mark.parametrize("M", [1, 20, 48])
+def test_stream_int8_256_rows(env, M, monkeypatch):
+    """int8 weights with 256 weight rows per stream workgroup (chosen for large
+    gate/up shapes at 33..64 tokens), forced on a small shape with ragged tiles."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    wl = small(wdt="i8", M=M, hidden=1024, H=10, Hkv=2, D=32, ffn=464)
+    inp = inputs.generate(wl, seed=17)
+    d = to_dev(inp)
+    print(f"int8 256-row stream {env} M={M}", flush=True)
+    q, k, v, h = run_qkv(wl, d, torch.float32)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rq = oracle.workload_qkv(wl, inp)
+    rg = oracle.workload_gateup(wl, inp)
+    check("q", q, rq["q"])
+    check("k", k, rq["k"])
+    check("v", v, rq["v"])
+    check("out", out, rg["out"])
+
+
 # ---------------------------------------------------------------------------
 # token counts above one 256-row tile (the prefill kernel family): ragged row
 # and column tails, SwiGLU widths that split a 128-column output tile, every
