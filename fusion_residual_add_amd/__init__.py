@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import FP_ACT, FP_NORM
 
 __all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_dequant_i8_bf16",
-           "workspace_bytes", "FusedProjError", "profile_start", "profile_stop", "library_path"]
+           "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
+           "library_path"]
 
 _DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
        torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8}
@@ -60,6 +61,22 @@ _WS: Dict[Tuple[int, int], torch.Tensor] = {}
 def workspace_bytes(M: int, hidden: int, n_cols: int, act_dtype: torch.dtype,
                     w_dtype: torch.dtype) -> int:
     return int(_lib.load().fp_workspace_bytes(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype]))
+
+
+def describe_plan(M: int, hidden: int, n_cols: int, act_dtype: torch.dtype, w_dtype: torch.dtype,
+                  act: str = "none") -> dict:
+    """The kernel and launch shape a call with these sizes would use (no device
+    work): {"family", "kernel", "grid", "splits", "slots", "workspace"}."""
+    import ctypes
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(256)
+    st = lib.fp_describe_plan(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype], _lib.FP_ACT[act], buf, 256)
+    if st != 0:
+        raise FusedProjError("fp_describe_plan", st, lib.fp_last_error().decode())
+    out = dict(kv.split("=", 1) for kv in buf.value.decode().split(" "))
+    for k in ("grid", "splits", "slots", "workspace"):
+        out[k] = int(out[k])
+    return out
 
 
 def _workspace(device: torch.device, stream: int, nbytes: int) -> Optional[torch.Tensor]:

@@ -19,7 +19,7 @@ STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_
 
 # every symbol include/fusedproj.h declares
 EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_gateup_act",
-           "fused_dequant_i8_bf16", "fp_status_str", "fp_last_error",
+           "fused_dequant_i8_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
            "fp_profile_start", "fp_profile_stop"]
 
 
@@ -52,6 +52,8 @@ def load(path: str = None):
     lib.fused_gateup_act.restype = ci
     lib.fused_dequant_i8_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.fused_dequant_i8_bf16.restype = ci
+    lib.fp_describe_plan.argtypes = [i64, i64, i64, ci, ci, ci, ctypes.c_char_p, sz]
+    lib.fp_describe_plan.restype = ci
     lib.fp_status_str.argtypes = [ci]
     lib.fp_status_str.restype = ctypes.c_char_p
     lib.fp_last_error.argtypes = []

@@ -462,6 +462,29 @@ fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_b
     return FP_OK;
 }
 
+fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
+                           fp_dtype w_dtype, fp_act act, char *buf, size_t cap) {
+    if (!buf || cap == 0) return fail(FP_E_NULL, "buf must be non-NULL with cap > 0");
+    if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0)
+        return fail(FP_E_SHAPE, "M = %lld, hidden = %lld (a positive multiple of 64), n_cols = %lld",
+                    (long long)M, (long long)hidden, (long long)n_cols);
+    if ((int)act < 0 || (int)act > 2) return fail(FP_E_ARG, "act = %d", (int)act);
+    const fp_status st = check_dtypes(act_dtype, w_dtype, act_dtype);
+    if (st != FP_OK) return st;
+    const Plan p = make_plan(M, hidden, n_cols, act_dtype, w_dtype, act == FP_ACT_SWIGLU);
+    const int a = act_code(act_dtype);
+    const bool wi8 = w_dtype == FP_I8;
+    const int epi = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
+    const char *fam = p.family == 1 ? "stream" : p.family == 2 ? "prefill" : "tiled";
+    const char *name = p.family == 1 ? fp::stream_kernel_name(a, wi8, p.sc, epi)
+                     : p.family == 2 ? fp::prefill_kernel_name(a, wi8, epi)
+                                     : fp::proj_kernel_name(a, wi8, p.tile, epi);
+    const int64_t grid = p.family == 1 ? p.grid : (int64_t)p.tiles_m * p.tiles_n * p.splits;
+    snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu", fam, name,
+             (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total);
+    return FP_OK;
+}
+
 const char *fp_status_str(fp_status s) {
     switch (s) {
     case FP_OK: return "ok";

@@ -138,6 +138,18 @@ fp_status fused_gateup_act(
 fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_bf16,
                                 int64_t N, int64_t K, void *hip_stream);
 
+/* Which kernel a call with these sizes would launch, and how: writes a
+ * NUL-terminated line such as
+ *   "family=stream kernel=stream_kernel<bf16,m32,n128,k256,swiglu> grid=256
+ *    splits=1 slots=2 workspace=4227328"
+ * into buf (truncated to cap bytes).  n_cols is the weight row count as for
+ * fp_workspace_bytes; act selects the gate/up pairing (FP_ACT_SWIGLU) or not.
+ * A diagnostic for tuning and tests: it reads the same FUSEDPROJ_* overrides
+ * as the calls, touches no device and returns FP_E_SHAPE / FP_E_DTYPE /
+ * FP_E_ARG / FP_E_NULL for arguments the calls would reject. */
+fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
+                           fp_dtype w_dtype, fp_act act, char *buf, size_t cap);
+
 /* Static text for a status code. */
 const char *fp_status_str(fp_status s);
 

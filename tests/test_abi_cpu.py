@@ -6,7 +6,9 @@ import os
 import re
 
 import pytest
+import torch
 
+import fusion_residual_add_amd as fra
 from fusion_residual_add_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -148,3 +150,68 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         fra.fused_gateup_act(x, None, torch.ones(64, dtype=torch.bfloat16),
                              torch.zeros(32, 64, dtype=torch.bfloat16), 16, "swiglu")
+
+
+# ---------------------------------------------------------------------------
+# kernel routing (host logic, no device): which family each shape takes
+# ---------------------------------------------------------------------------
+def _plan(M, K, N, act=torch.bfloat16, w=torch.bfloat16, fn="none"):
+    return fra.describe_plan(M, K, N, act, w, fn)
+
+
+def test_plan_routing_families(monkeypatch):
+    for var in ("FUSEDPROJ_SPLITS", "FUSEDPROJ_NO_STREAM", "FUSEDPROJ_NO_PREFILL", "FUSEDPROJ_STREAM_NR",
+                "FUSEDPROJ_STREAM_TARGET"):
+        monkeypatch.delenv(var, raising=False)
+    # decode token counts with K a multiple of 256: the weight-streaming kernel
+    p = _plan(32, 4096, 2 * 14336, fn="swiglu")
+    assert p["family"] == "stream" and p["kernel"] == "stream_kernel<bf16,m32,n128,k256,swiglu>"
+    assert p["grid"] == 256 and p["slots"] >= 2          # stream-K: 3584 units over 256 workgroups
+    assert _plan(1, 8192, 10240, w=torch.int8)["kernel"] == "stream_kernel<bf16-i8w,m16,n128,k256,linear>"
+    # 33..64 tokens: 128-wide chunks; int8 large-N gate/up: 256 rows per workgroup
+    assert _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")["kernel"] == "stream_kernel<bf16-i8w,m64,n256,k128,swiglu>"
+    assert _plan(64, 8192, 10240, w=torch.int8)["kernel"] == "stream_kernel<bf16-i8w,m64,n128,k128,linear>"
+    # K not a multiple of 256 at decode sizes, and every fp32 call: the tiled kernel
+    assert _plan(32, 320, 512)["family"] == "tiled"
+    assert _plan(4, 256, 512, act=torch.float32, w=torch.float32)["family"] == "tiled"
+    # more than 64 tokens: the 128 x 512 kernel
+    p = _plan(16384, 4096, 12288)
+    assert p["family"] == "prefill" and p["kernel"] == "prefill_kernel<bf16,128x512,linear>"
+    assert p["grid"] == 128 * 24 and p["splits"] == 1
+    p = _plan(256, 8192, 10240, w=torch.int8)
+    assert p["family"] == "prefill" and 1 < p["splits"] <= 4  # 40 tiles: split K, at most 4 ways
+    assert _plan(2048, 4096, 16384, act=torch.float16, w=torch.float16, fn="gelu_tanh")["kernel"] == \
+        "prefill_kernel<f16,128x512,gelu>"
+
+
+def test_plan_grid_slots_consistent(monkeypatch):
+    """The stream kernel's partial-sum slots cover the most workgroups that share
+    one tile, for unit counts that do and do not divide evenly."""
+    monkeypatch.delenv("FUSEDPROJ_STREAM_TARGET", raising=False)
+    for splits in ("1", "2", "3", "5", "7"):
+        monkeypatch.setenv("FUSEDPROJ_SPLITS", splits)
+        for M, K, N in ((1, 2048, 640), (32, 4096, 6144), (20, 1024, 928)):
+            p = _plan(M, K, N)
+            tiles = -(-N // 128)
+            chunks = K // 256
+            units = tiles * chunks
+            G = min(tiles * int(splits), units)
+            assert p["grid"] == G
+            owner = lambda v: ((v + 1) * G - 1) // units
+            most = max(owner(t * chunks + chunks - 1) - owner(t * chunks) + 1 for t in range(tiles))
+            assert p["slots"] == most
+
+
+def test_plan_env_overrides(monkeypatch):
+    monkeypatch.setenv("FUSEDPROJ_NO_STREAM", "1")
+    assert _plan(32, 4096, 6144)["family"] == "tiled"
+    monkeypatch.delenv("FUSEDPROJ_NO_STREAM")
+    monkeypatch.setenv("FUSEDPROJ_NO_PREFILL", "1")
+    assert _plan(300, 4096, 6144)["family"] == "tiled"
+
+
+def test_plan_rejects():
+    with pytest.raises(fra.FusedProjError):
+        _plan(32, 4000, 6144)                  # hidden not a multiple of 64
+    with pytest.raises(fra.FusedProjError):
+        _plan(32, 4096, 6144, act=torch.float16, w=torch.int8)
