@@ -321,6 +321,26 @@ def all_configs(steps: int) -> None:
         torch.cuda.empty_cache()
 
 
+def all_configs_summarize(path: str, cmd: str) -> None:
+    """profiles/all_configs.md from the JSON lines of --all-configs."""
+    md = ["# Every workload, per call", "", "Command (from the repository root):", "", "```", cmd, "```", "",
+          "Rates are per call, statistics kernel included: algorithmic HBM GB/s for bandwidth-bound calls",
+          "(8000 GB/s peak), MFMA TFLOP/s otherwise (2516.6 bf16/fp16, 157.3 fp32).", "",
+          "| workload | call | kernels (us) | rate | fraction of peak |", "|---|---|---|---|---|"]
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line.startswith("{"):
+                continue
+            d = json.loads(line)
+            for call, c in d["calls"].items():
+                ks = ", ".join(f"`{k}` {v}" for k, v in c["kernels_us"].items())
+                md.append(f"| {d['workload']} | {call} | {ks} | {c['rate']} {c['unit']} | {c['frac']:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "all_configs.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     import oracle
     from fusion_residual_add_amd import inputs
@@ -359,6 +379,8 @@ def main():
     ap.add_argument("--trace-summarize", nargs=2, metavar=("TAG", "TRACE_DIR"),
                     help="write profiles/kernel_trace_TAG.md from a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--cmd", default="", help="the profiling command(s), recorded in the summary")
+    ap.add_argument("--all-configs-summarize", metavar="JSON_LINES",
+                    help="write profiles/all_configs.md from the output of --all-configs")
     ap.add_argument("--all-configs", action="store_true",
                     help="per-call times and roofline fractions of every workload, one JSON line each")
     args = ap.parse_args()
@@ -367,6 +389,9 @@ def main():
         return
     if args.trace_summarize:
         trace_summarize(*args.trace_summarize, args.cmd)
+        return
+    if args.all_configs_summarize:
+        all_configs_summarize(args.all_configs_summarize, args.cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
