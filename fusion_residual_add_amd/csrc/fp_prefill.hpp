@@ -164,7 +164,7 @@ void prefill_kernel(ProjArgs p) {
     // row's registers are refilled with stage kt + 2 right after use, so every
     // load has a whole step to arrive.
     struct ARegs { u32x4 x[4], r[4], g, b; };
-    struct BRegs { u32x4 q[8]; };   // int8 path only
+    struct BRegs { u32x4 q[8]; };   // int8 path only: the thread's 8 weight vectors of a stage
     ARegs A;
     BRegs B;
     float gv[8], bv[8];             // gamma / beta of the stage being normalised
@@ -208,21 +208,16 @@ void prefill_kernel(ProjArgs p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) load_lds16(rw, lb + (128 * wave + 8 * i) * ROWB, b_off[i], kb);
     };
-    auto bload_regs = [&](int kt) {   // int8 weights
-        const uint32_t kb = (uint32_t)kt * BK;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) B.q[i] = ld16(rw, b_off[i], kb);
-    };
-    auto bstore_regs = [&](unsigned char *lb) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            u32x4 lo, hi;
-            dequant16(B.q[i], b_sc[i], lo, hi);
-            const int br = (tid >> 2) + 64 * i;
-            const int c0 = (tid & 3) * 2;
-            *(u32x4 *)(lb + swz(br, c0)) = lo;
-            *(u32x4 *)(lb + swz(br, c0 + 1)) = hi;
-        }
+    // int8 weights: vector i of stage kt into registers; dequantised into
+    // the LDS tile of its stage (16 values -> two 16-byte bf16 chunks)
+    auto bload_one = [&](int kt, int i) { B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * BK); };
+    auto bstore_one = [&](unsigned char *lb, int i) {
+        u32x4 lo, hi;
+        dequant16(B.q[i], b_sc[i], lo, hi);
+        const int br = (tid >> 2) + 64 * i;
+        const int c0 = (tid & 3) * 2;
+        *(u32x4 *)(lb + swz(br, c0)) = lo;
+        *(u32x4 *)(lb + swz(br, c0 + 1)) = hi;
     };
 
     // ---- accumulators: acc[i][j][q] = D[row i*32 + 8(q/4) + 4(lane/32) + q%4]
@@ -248,7 +243,7 @@ void prefill_kernel(ProjArgs p) {
     auto frag_b = [&](const unsigned char *lb, int t, int j) {
         return *(const u32x4 *)(lb + swz(wave * 128 + j * 32 + (lane & 31), 2 * t + (lane >> 5)));
     };
-    auto mma = [&](const unsigned char *la, const unsigned char *lb, unsigned char *na, int kn) {
+    auto mma = [&](const unsigned char *la, const unsigned char *lb, unsigned char *na, unsigned char *nb, int kn) {
         u32x4 af[4], bf[2], nf[4], nbf[2];
         float n[8];
 #pragma unroll
@@ -279,14 +274,20 @@ void prefill_kernel(ProjArgs p) {
                 a_store(na, r >> 1, n);
                 a_issue(kn, r >> 1);
             }
+            if constexpr (WI8) {
+                // weights of the next stage, one vector per region, refilled
+                // from stage kn right after
+                bstore_one(nb, r);
+                bload_one(kn, r);
+            }
             __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS reads
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // then VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, WI8 ? 8 : 3, 0);   // then VALU
             }
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // row loads
+            __builtin_amdgcn_sched_group_barrier(0x200, WI8 ? 3 : 1, 0);   // LDS writes
+            __builtin_amdgcn_sched_group_barrier(0x020, WI8 ? 3 : 2, 0);   // refill loads
             __builtin_amdgcn_sched_barrier(0);
             if (r < 7) {
                 bf[0] = nbf[0];
@@ -300,12 +301,13 @@ void prefill_kernel(ProjArgs p) {
     };
     // wait for everything but the activation loads issued after the weights
     // of the step (2 gamma / beta + 8 row loads), and for this thread's LDS
-    // writes; then a workgroup barrier.  The count relies on issue order:
+    // writes; then a workgroup barrier.  (int8 weights roll through
+    // registers like the activations: no load needs waiting for here.)  The count relies on issue order:
     // every weight load is fenced by a scheduling barrier before anything
     // else is issued.  The empty asm statements keep the compiler from moving
     // memory accesses across the barrier.
     auto step_sync = [&]() {
-        constexpr int VM = 10;
+        constexpr int VM = WI8 ? 63 : 10;   // int8: every load is a rolling register load
         __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
         __asm__ __volatile__("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -314,7 +316,12 @@ void prefill_kernel(ProjArgs p) {
 
     if (kt0 < kt1) {
         // prologue: stage kt0 into LDS tile 0, then start loading stage kt0 + 1
-        if constexpr (WI8) bload_regs(kt0); else bload_lds(kt0, lB0);
+        if constexpr (WI8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bload_one(kt0, i);
+        } else {
+            bload_lds(kt0, lB0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         gb_issue(kt0);
 #pragma unroll
@@ -327,8 +334,14 @@ void prefill_kernel(ProjArgs p) {
             a_norm(i, 2, n);
             a_store(lA0, i, n);
         }
-        if constexpr (WI8) bstore_regs(lB0);
         const int k1 = kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1;
+        if constexpr (WI8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                bstore_one(lB0, i);
+                bload_one(k1, i);
+            }
+        }
         gb_issue(k1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) a_issue(k1, i);
@@ -343,13 +356,12 @@ void prefill_kernel(ProjArgs p) {
             unsigned char *na = odd ? lA0 : lA1, *nb = odd ? lB0 : lB1;
             const int kw = kt + 1 < kt1 ? kt + 1 : kt1 - 1;
             const int kn = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
-            if constexpr (WI8) bload_regs(kw); else bload_lds(kw, nb);
+            if constexpr (!WI8) bload_lds(kw, nb);
             __builtin_amdgcn_sched_barrier(0);   // keeps the weight loads first (see step_sync)
             gb_unpack();
             gb_issue(kn);
             __builtin_amdgcn_sched_barrier(0);
-            mma(ca, cb, na, kn);
-            if constexpr (WI8) bstore_regs(nb);
+            mma(ca, cb, na, nb, kn);
             step_sync();
         }
         __builtin_amdgcn_s_waitcnt(0);
