@@ -83,7 +83,7 @@ hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_
 const char *stats_kernel_name(int act);
 const char *proj_kernel_name(int act, bool w_i8, int tile, int epi);
 const char *stream_kernel_name(int act, bool w_i8, const StreamCfg &c, int epi);
-// 256 x 256 family (fp_prefill*.hip): 16-bit activations, large M
+// 128 x 512 family (fp_prefill*.hip): 16-bit activations, more than 64 tokens
 hipError_t launch_prefill(int act, bool w_i8, const ProjArgs &a, hipStream_t s);
 const char *prefill_kernel_name(int act, bool w_i8, int epi);
 const char *dequant_kernel_name();

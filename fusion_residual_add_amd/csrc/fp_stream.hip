@@ -1,4 +1,4 @@
-// Dispatch and naming of the weight-streaming (decode) and 256 x 256 (prefill)
+// Dispatch and naming of the weight-streaming (decode) and 128 x 512 (prefill)
 // projection kernels (fp_stream.hpp / fp_prefill.hpp, instantiated per dtype
 // in fp_stream_*.hip / fp_prefill_*.hip).
 #include "fp_device.hpp"

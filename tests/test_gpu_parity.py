@@ -278,6 +278,30 @@ def test_stream_int8_256_rows(env, M, monkeypatch):
 
 
 # ---------------------------------------------------------------------------
+# degenerate shapes: the smallest hidden (one K step), head_dim and ffn (16),
+# a single head, the stream kernel's smallest K (one chunk), and token counts
+# on both sides of the decode / prefill boundary
+# ---------------------------------------------------------------------------
+DEGENERATE = [
+    dict(act="bf16", M=1, hidden=64, H=1, Hkv=1, D=16, ffn=16),
+    dict(act="bf16", M=64, hidden=64, H=1, Hkv=1, D=16, ffn=16),
+    dict(act="bf16", M=65, hidden=64, H=1, Hkv=1, D=16, ffn=16),
+    dict(act="f16", M=300, hidden=64, H=2, Hkv=1, D=16, ffn=16, norm="layer", act_fn="gelu_tanh", bias=True),
+    dict(act="bf16", M=1, hidden=256, H=2, Hkv=1, D=16, ffn=16),
+    dict(act="bf16", M=64, hidden=256, H=2, Hkv=1, D=16, ffn=16),
+    dict(act="bf16", wdt="i8", M=1, hidden=256, H=1, Hkv=1, D=16, ffn=16),
+    dict(act="bf16", wdt="i8", M=65, hidden=128, H=1, Hkv=1, D=16, ffn=16),
+    dict(act="bf16", M=64, hidden=1024, H=8, Hkv=2, D=64, ffn=384),
+    dict(act="bf16", M=65, hidden=1024, H=8, Hkv=2, D=64, ffn=384),
+]
+
+
+@pytest.mark.parametrize("cfg", DEGENERATE, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_degenerate_shapes(cfg):
+    test_small(cfg, native=False)
+
+
+# ---------------------------------------------------------------------------
 # token counts above one 256-row tile (the prefill kernel family): ragged row
 # and column tails, SwiGLU widths that split a 128-column output tile, every
 # weight dtype and epilogue
