@@ -66,7 +66,8 @@ void prefill_kernel(ProjArgs p) {
     __shared__ __attribute__((aligned(16))) unsigned char lB0[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char lB1[TILEB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
 
     // ---- tile of this workgroup: XCD-aware remap, then grouped raster
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
