@@ -93,6 +93,16 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // per CU; shorter ranges pay the pipeline ramp too often)
         const int64_t units = tiles * ksteps;
         int64_t G = units / 4 < target ? units / 4 : target;
+        // one whole tile per workgroup when that still occupies most CUs and
+        // the call is short: shared tiles cost a few us per call (partial sums
+        // out and back, and the wait for them), which outweighs the idle CUs
+        // only while the streaming itself is short (measured on MI355X:
+        // Llama-3-8B gate/up, 224 tiles of 235 MB, 51.3 -> 49.3 us with the
+        // weights in the last-level cache, 0.3 % of the decode step with them
+        // streamed from HBM; Llama-2-70B int8 gate/up, 448 tiles or 224 tiles
+        // of 470 MB, 6-10 % slower so)
+        const int64_t wbytes = Nw * K * (wdt == FP_I8 ? 1 : 2);
+        if (tiles * 100 >= target * 85 && tiles <= target && wbytes <= (int64_t(256) << 20)) G = tiles;
         const long forced = env_long("FUSEDPROJ_SPLITS", 0);
         if (forced > 0) G = tiles * forced;
         if (G > units) G = units;

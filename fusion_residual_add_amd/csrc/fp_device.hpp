@@ -176,14 +176,22 @@ __device__ __forceinline__ int xcd_remap(int hw, int n) {
     return x * q + (x < r ? x : r) + local;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// Epilogue activations on the hardware's exp2 and reciprocal (v_exp_f32,
+// v_rcp_f32: about 1 ulp each), a few instructions per value instead of a
+// range-reduced expf and an IEEE division; the outputs are rounded to 16 bits
+// afterwards.  Overflow behaves like the exact forms: exp2 -> +inf gives
+// rcp -> 0 and a zero result for large negative inputs.
+__device__ __forceinline__ float exp_neg(float x) {   // exp(-x)
+    return __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+}
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + exp_neg(g)); }
 
 // tanh-approximation GELU written through the identity
 // 0.5 y (1 + tanh(z)) = y / (1 + exp(-2 z)), z = sqrt(2/pi) (y + 0.044715 y^3).
 __device__ __forceinline__ float gelu_tanh(float y) {
-    const float c = 0.7978845608028654f;
-    float z = c * (y + 0.044715f * y * y * y);
-    return y / (1.0f + expf(-2.0f * z));
+    const float c2 = 2.0f * 0.7978845608028654f;
+    const float z2 = c2 * fmaf(0.044715f * y, y * y, y);
+    return y * __builtin_amdgcn_rcpf(1.0f + exp_neg(z2));
 }
 
 // ---------------------------------------------------------------------------

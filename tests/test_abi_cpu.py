@@ -166,7 +166,14 @@ def test_plan_routing_families(monkeypatch):
     # decode token counts with K a multiple of 256: the weight-streaming kernel
     p = _plan(32, 4096, 2 * 14336, fn="swiglu")
     assert p["family"] == "stream" and p["kernel"] == "stream_kernel<bf16,m32,n128,k256,swiglu>"
-    assert p["grid"] == 256 and p["slots"] >= 2          # stream-K: 3584 units over 256 workgroups
+    # 224 tiles of a 235 MB weight: one whole tile per workgroup, nothing shared
+    assert p["grid"] == 224 and p["slots"] == 1
+    # the same tile count on a 470 MB weight: stream-K over 256 workgroups
+    p = _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")
+    assert p["grid"] == 256 and p["slots"] >= 2
+    # few tiles (48): stream-K, at least 4 chunks per workgroup (768 units / 4)
+    p = _plan(32, 4096, 6144)
+    assert p["grid"] == 192 and p["slots"] == 4
     assert _plan(1, 8192, 10240, w=torch.int8)["kernel"] == "stream_kernel<bf16-i8w,m16,n128,k256,linear>"
     # 33..64 tokens: 128-wide chunks; int8 large-N gate/up: 256 rows per workgroup
     assert _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")["kernel"] == "stream_kernel<bf16-i8w,m64,n256,k128,swiglu>"
