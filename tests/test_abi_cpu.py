@@ -171,9 +171,12 @@ def test_plan_routing_families(monkeypatch):
     # the same tile count on a 470 MB weight: stream-K over 256 workgroups
     p = _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")
     assert p["grid"] == 256 and p["slots"] >= 2
-    # few tiles (48): stream-K, at least 4 chunks per workgroup (768 units / 4)
+    # 16-bit QKV weights at up to 32 tokens: 64-row tiles (96 of them), stream-K
+    # over 256 workgroups
     p = _plan(32, 4096, 6144)
-    assert p["grid"] == 192 and p["slots"] == 4
+    assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear>" and p["grid"] == 256 and p["slots"] >= 2
+    # 33..64 tokens keep 128-row tiles
+    assert _plan(64, 4096, 6144)["kernel"] == "stream_kernel<bf16,m64,n128,k128,linear>"
     assert _plan(1, 8192, 10240, w=torch.int8)["kernel"] == "stream_kernel<bf16-i8w,m16,n128,k256,linear>"
     # 33..64 tokens: 128-wide chunks; int8 large-N gate/up: 256 rows per workgroup
     assert _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")["kernel"] == "stream_kernel<bf16-i8w,m64,n256,k128,swiglu>"
@@ -199,7 +202,7 @@ def test_plan_grid_slots_consistent(monkeypatch):
         monkeypatch.setenv("FUSEDPROJ_SPLITS", splits)
         for M, K, N in ((1, 2048, 640), (32, 4096, 6144), (20, 1024, 928)):
             p = _plan(M, K, N)
-            tiles = -(-N // 128)
+            tiles = -(-N // 64)               # 64-row tiles: 16-bit weights, no pairing, <= 32 tokens
             chunks = K // 256
             units = tiles * chunks
             G = min(tiles * int(splits), units)
