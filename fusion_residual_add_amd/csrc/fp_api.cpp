@@ -146,9 +146,21 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     }
     if (p.family != 1) {
         int64_t s = 1;
-        if (tiles > 0 && tiles < target) s = (target + tiles - 1) / tiles;
-        // a 128 x 512 partial tile is 256 KB each way: at most 4 splits
-        int64_t smax = p.family == 2 ? (ksteps / 4 < 4 ? ksteps / 4 : 4) : ksteps / 4;
+        if (p.family == 2) {
+            // as many splits as still fit one round of workgroups (one per CU):
+            // a second round costs more than the idle CUs of the first.  At
+            // most 8 (a 128 x 512 partial tile is 256 KB each way).  Measured
+            // on MI355X, Llama-2-70B int8 at 256 tokens: QKV (40 tiles) 115 ->
+            // 103 us with 6 splits instead of 4; gate/up (224 tiles) 368 ->
+            // 322 us unsplit instead of 2 splits.
+            s = tiles > 0 ? target / tiles : 1;
+            const int64_t cap = ksteps / 4 < 8 ? ksteps / 4 : 8;
+            if (s > cap) s = cap;
+            if (s < 1) s = 1;
+        } else if (tiles > 0 && tiles < target) {
+            s = (target + tiles - 1) / tiles;
+        }
+        int64_t smax = p.family == 2 ? 8 : ksteps / 4;
         if (smax < 1) smax = 1;
         if (s > smax) s = smax;
         if (s > 16) s = 16;

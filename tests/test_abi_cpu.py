@@ -188,8 +188,12 @@ def test_plan_routing_families(monkeypatch):
     p = _plan(16384, 4096, 12288)
     assert p["family"] == "prefill" and p["kernel"] == "prefill_kernel<bf16,128x512,linear>"
     assert p["grid"] == 128 * 24 and p["splits"] == 1
+    # split K so that the workgroups fill one round of CUs: 40 tiles -> 6 splits
+    # (240 workgroups); 224 tiles -> unsplit (2 splits would take two rounds)
     p = _plan(256, 8192, 10240, w=torch.int8)
-    assert p["family"] == "prefill" and 1 < p["splits"] <= 4  # 40 tiles: split K, at most 4 ways
+    assert p["family"] == "prefill" and p["splits"] == 6 and p["grid"] == 240
+    p = _plan(256, 8192, 57344, w=torch.int8, fn="swiglu")
+    assert p["splits"] == 1 and p["grid"] == 224
     assert _plan(2048, 4096, 16384, act=torch.float16, w=torch.float16, fn="gelu_tanh")["kernel"] == \
         "prefill_kernel<f16,128x512,gelu>"
 
