@@ -94,21 +94,32 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         ksteps = K / (32 * p.sc.u);
         target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
         // stream-K: `grid` workgroups take equal contiguous unit ranges of at
-        // least 4 chunks (measured on MI355X: the QKV shape of Llama-3-8B
-        // decode streams fastest on 192 workgroups, the gate/up shape on one
-        // per CU; shorter ranges pay the pipeline ramp too often)
+        // least 512 of K each (2 chunks of 256, 4 of 128; measured on MI355X:
+        // shorter ranges pay the pipeline ramp too often, and 2 chunks of 256
+        // beat 4 on the small QKV of Llama-2-70B's 8-way shard, 16.8 -> 14.9 us)
         const int64_t units = tiles * ksteps;
-        int64_t G = units / 4 < target ? units / 4 : target;
-        // one whole tile per workgroup when that still occupies most CUs and
-        // the call is short: shared tiles cost a few us per call (partial sums
-        // out and back, and the wait for them), which outweighs the idle CUs
-        // only while the streaming itself is short (measured on MI355X:
-        // Llama-3-8B gate/up, 224 tiles of 235 MB, 51.3 -> 49.3 us with the
-        // weights in the last-level cache, 0.3 % of the decode step with them
-        // streamed from HBM; Llama-2-70B int8 gate/up, 448 tiles or 224 tiles
-        // of 470 MB, 6-10 % slower so)
+        const int64_t minc = 512 / (32 * p.sc.u);
+        int64_t G = units / minc < target ? units / minc : target;
+        // s workgroups per tile, each an equal 1/s of K, when that still
+        // occupies most CUs and the call is short: a range that straddles two
+        // tiles costs a few us (partial sums out and back, and the wait for
+        // them), which outweighs the idle CUs only while the streaming itself
+        // is short (measured on MI355X: Llama-3-8B gate/up, 224 tiles of 235
+        // MB, s = 1: 51.3 -> 49.3 us with the weights in the last-level cache,
+        // 0.3 % of the decode step with them streamed from HBM; the gate/up of
+        // Llama-2-70B's 8-way shard, 56 tiles, s = 4: 24.6 -> 23.4 us;
+        // Llama-2-70B int8 gate/up, 224 tiles of 470 MB, 6 % slower so; an
+        // uneven 1/s of K, 32 chunks in 3, 1 us slower)
         const int64_t wbytes = Nw * K * (wdt == FP_I8 ? 1 : 2);
-        if (tiles * 100 >= target * 85 && tiles <= target && wbytes <= (int64_t(256) << 20)) G = tiles;
+        if (wbytes <= (int64_t(256) << 20) && tiles > 0) {
+            for (int64_t s = target / tiles < ksteps / minc ? target / tiles : ksteps / minc; s >= 1; --s) {
+                if (tiles * s * 100 < target * 85) break;
+                if (ksteps % s == 0) {
+                    G = tiles * s;
+                    break;
+                }
+            }
+        }
         const long forced = env_long("FUSEDPROJ_SPLITS", 0);
         if (forced > 0) G = tiles * forced;
         if (G > units) G = units;

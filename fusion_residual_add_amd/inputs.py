@@ -84,6 +84,14 @@ def _llama70b(M: int) -> Workload:
         ffn=28672, act_fn="swiglu", bias_std=None)
 
 
+def _llama70b_tp8(M: int) -> Workload:
+    """One GPU's share of the Llama-2-70B int8 layer under 8-way tensor
+    parallelism: 8 of the 64 Q heads, 1 of the 8 KV heads, 3584 of the 28672
+    gate/up rows (each with its matching up row)."""
+    return dataclasses.replace(_llama70b(M), name=f"llama2-70b-int8w-tp8@M{M}", n_heads=8, n_kv_heads=1,
+                               ffn=28672 // 8)
+
+
 WORKLOADS: Dict[str, Workload] = {
     # tiny fp32 block: M=4, hidden=256, 4 Q / 2 KV heads of 64, ffn=512
     "tiny-f32": Workload(
@@ -115,6 +123,9 @@ WORKLOADS: Dict[str, Workload] = {
     "llama2-70b-int8w@M16": _llama70b(16),
     "llama2-70b-int8w@M64": _llama70b(64),
     "llama2-70b-int8w@M256": _llama70b(256),
+    "llama2-70b-int8w-tp8@M1": _llama70b_tp8(1),
+    "llama2-70b-int8w-tp8@M16": _llama70b_tp8(16),
+    "llama2-70b-int8w-tp8@M64": _llama70b_tp8(64),
 }
 
 

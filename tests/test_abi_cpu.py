@@ -177,6 +177,12 @@ def test_plan_routing_families(monkeypatch):
     assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear>" and p["grid"] == 256 and p["slots"] >= 2
     # 33..64 tokens keep 128-row tiles
     assert _plan(64, 4096, 6144)["kernel"] == "stream_kernel<bf16,m64,n128,k128,linear>"
+    # Llama-2-70B's 8-way shard: QKV (10 tiles x 32 chunks) on 160 workgroups of
+    # 2 chunks; gate/up (56 tiles x 32 chunks) 4 workgroups per tile, 8 chunks each
+    p = _plan(1, 8192, 1280, w=torch.int8)
+    assert p["grid"] == 160 and p["slots"] == 16
+    p = _plan(1, 8192, 7168, w=torch.int8, fn="swiglu")
+    assert p["grid"] == 224 and p["slots"] == 4
     assert _plan(1, 8192, 10240, w=torch.int8)["kernel"] == "stream_kernel<bf16-i8w,m16,n128,k256,linear>"
     # 33..64 tokens: 128-wide chunks; int8 large-N gate/up: 256 rows per workgroup
     assert _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")["kernel"] == "stream_kernel<bf16-i8w,m64,n256,k128,swiglu>"

@@ -208,7 +208,8 @@ def _sample_rows(M, n, seed=0):
 
 
 FULL = ["tiny-f32", "llama3-8b-decode", "llama2-7b-prefill", "gpt-fp16-gelu",
-        "llama2-70b-int8w@M1", "llama2-70b-int8w@M16", "llama2-70b-int8w@M64", "llama2-70b-int8w@M256"]
+        "llama2-70b-int8w@M1", "llama2-70b-int8w@M16", "llama2-70b-int8w@M64", "llama2-70b-int8w@M256",
+        "llama2-70b-int8w-tp8@M16"]
 N_ROWS = {"llama2-7b-prefill": 24, "gpt-fp16-gelu": 24, "llama2-70b-int8w@M256": 16,
           "llama2-70b-int8w@M64": 64}
 
