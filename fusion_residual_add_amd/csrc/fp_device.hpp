@@ -51,14 +51,17 @@ __device__ __forceinline__ unsigned dequant_i8_bf16(int q, float s) {
 }
 
 // 16 int8 values (one 16-byte load) -> 16 bf16 values (two 16-byte vectors).
+// Each pair is rounded by one packed conversion: bit for bit the words
+// dequant_i8_bf16(q0, s) | dequant_i8_bf16(q1, s) << 16, in 2.5 instructions
+// per value (sign-extending convert, multiply, half a packed conversion).
 __device__ __forceinline__ void dequant16(u32x4 qv, float s, u32x4 &lo, u32x4 &hi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         unsigned w = qv[i];
         int q0 = (int)(w << 24) >> 24, q1 = (int)(w << 16) >> 24;
         int q2 = (int)(w << 8) >> 24, q3 = (int)w >> 24;
-        unsigned p0 = dequant_i8_bf16(q0, s) | (dequant_i8_bf16(q1, s) << 16);
-        unsigned p1 = dequant_i8_bf16(q2, s) | (dequant_i8_bf16(q3, s) << 16);
+        unsigned p0 = pack2_bf16((float)q0 * s, (float)q1 * s);
+        unsigned p1 = pack2_bf16((float)q2 * s, (float)q3 * s);
         if (i < 2) { lo[2 * i] = p0; lo[2 * i + 1] = p1; }
         else       { hi[2 * (i - 2)] = p0; hi[2 * (i - 2) + 1] = p1; }
     }
