@@ -49,7 +49,9 @@ constexpr int TILEB = BN * ROWB;             // 64 KB
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
 }  // namespace pf
 
-template <int ACT, bool WI8, int EPI>
+// LN: LayerNorm (mean, beta); otherwise RMSNorm or no norm, whose
+// normalisation is two multiplies (h * rstd * gamma) and has no beta to load.
+template <int ACT, bool WI8, int EPI, bool LN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(ProjArgs p) {
     using T = Act<ACT>;
@@ -180,24 +182,30 @@ void prefill_kernel(ProjArgs p) {
     auto gb_issue = [&](int kt) {
         const uint32_t kb = (uint32_t)kt * (BK * 2);
         A.g = ld16(rg, a_c * 16, kb);
-        A.b = ld16(rb, a_c * 16, kb);
+        if constexpr (LN) A.b = ld16(rb, a_c * 16, kb);
     };
     auto gb_unpack = [&]() {
         T::unpack(A.g, gv);
-        T::unpack(A.b, bv);
+        if constexpr (LN) T::unpack(A.b, bv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) gv[e] += g1;
     };
     // h = x + r (r reads as zero when absent; exact in fp32),
     // n = (h - mu) * rstd * gamma + beta, for words [w0, w0 + 2) of row i
+    // (RMSNorm / no norm: mu = 0, no beta)
     auto a_norm = [&](int i, int w0, float (&n)[8]) {
 #pragma unroll
         for (int w = w0; w < w0 + 2; ++w) {
             const unsigned xw = A.x[i][w], rv = A.r[i][w];
-            const float d0 = (T::lo(xw) + T::lo(rv)) - a_mu[i];
-            const float d1 = (T::hi(xw) + T::hi(rv)) - a_mu[i];
-            n[2 * w] = fmaf(d0 * a_rs[i], gv[2 * w], bv[2 * w]);
-            n[2 * w + 1] = fmaf(d1 * a_rs[i], gv[2 * w + 1], bv[2 * w + 1]);
+            if constexpr (LN) {
+                const float d0 = (T::lo(xw) + T::lo(rv)) - a_mu[i];
+                const float d1 = (T::hi(xw) + T::hi(rv)) - a_mu[i];
+                n[2 * w] = fmaf(d0 * a_rs[i], gv[2 * w], bv[2 * w]);
+                n[2 * w + 1] = fmaf(d1 * a_rs[i], gv[2 * w + 1], bv[2 * w + 1]);
+            } else {
+                n[2 * w] = ((T::lo(xw) + T::lo(rv)) * a_rs[i]) * gv[2 * w];
+                n[2 * w + 1] = ((T::hi(xw) + T::hi(rv)) * a_rs[i]) * gv[2 * w + 1];
+            }
         }
     };
     auto a_store = [&](unsigned char *la, int i, const float (&n)[8]) {
@@ -304,14 +312,15 @@ void prefill_kernel(ProjArgs p) {
         }
     };
     // wait for everything but the activation loads issued after the weights
-    // of the step (2 gamma / beta + 8 row loads), and for this thread's LDS
-    // writes; then a workgroup barrier.  (int8 weights roll through
-    // registers like the activations: no load needs waiting for here.)  The count relies on issue order:
-    // every weight load is fenced by a scheduling barrier before anything
-    // else is issued.  The empty asm statements keep the compiler from moving
-    // memory accesses across the barrier.
+    // of the step (gamma, beta for LayerNorm, and 8 row loads), and for this
+    // thread's LDS writes; then a workgroup barrier.  (int8 weights roll
+    // through registers like the activations: no load needs waiting for
+    // here.)  The count relies on issue order: every weight load is fenced by
+    // a scheduling barrier before anything else is issued.  The empty asm
+    // statements keep the compiler from moving memory accesses across the
+    // barrier.
     auto step_sync = [&]() {
-        constexpr int VM = WI8 ? 63 : 10;   // int8: every load is a rolling register load
+        constexpr int VM = WI8 ? 63 : (LN ? 10 : 9);   // int8: every load is a rolling register load
         __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
         __asm__ __volatile__("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -477,22 +486,28 @@ void prefill_kernel(ProjArgs p) {
     }
 }
 
-template <int ACT, bool WI8>
-inline void launch_prefill_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
+template <int ACT, bool WI8, bool LN>
+inline void launch_prefill_n(const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (a.epi) {
     case EPI_QKV:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_QKV>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_QKV, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     case EPI_SWIGLU:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_SWIGLU, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     case EPI_GELU:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_GELU>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_GELU, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     default:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_LINEAR>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_LINEAR, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     }
+}
+
+template <int ACT, bool WI8>
+inline void launch_prefill_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    if (a.norm == 2) launch_prefill_n<ACT, WI8, true>(a, grid, s);
+    else launch_prefill_n<ACT, WI8, false>(a, grid, s);
 }
 
 }  // namespace fp
