@@ -186,7 +186,7 @@ def library_kernel_name(cxx: str) -> str:
         act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
         return (f"stream_kernel<{act},m{16 * int(m.group(3))},n{64 * int(m.group(4))},"
                 f"k{32 * int(m.group(5))},{_EPI[m.group(6)]}>")
-    m = re.search(r"fp::prefill_kernel<(\d), (true|false), (\d)>", cxx)
+    m = re.search(r"fp::prefill_kernel<(\d), (true|false), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
         return f"prefill_kernel<{act},128x512,{_EPI[m.group(3)]}>"
