@@ -181,7 +181,7 @@ _EPI = {"0": "qkv", "1": "swiglu", "2": "gelu", "3": "linear"}
 def library_kernel_name(cxx: str) -> str:
     """The library profiler's name of a kernel from the demangled C++ name rocprofv3 prints."""
     import re
-    m = re.search(r"fp::stream_kernel<(\d), (true|false), (\d+), (\d+), (\d+), (\d)>", cxx)
+    m = re.search(r"fp::stream_kernel<(\d), (true|false), (\d+), (\d+), (\d+), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
         return (f"stream_kernel<{act},m{16 * int(m.group(3))},n{64 * int(m.group(4))},"
