@@ -83,7 +83,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         const long nr_env = env_long("FUSEDPROJ_STREAM_NR", 0);
         p.sc.nr = wdt == FP_I8 && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
         if (!swiglu && wdt != FP_I8 && p.sc.mf <= 2) p.sc.nr = 1;
-        if (nr_env == 1 && !swiglu) p.sc.nr = 1;
+        if (nr_env == 1 && !swiglu && wdt != FP_I8 && p.sc.mf <= 2) p.sc.nr = 1;   // instantiated forms only
         if (nr_env == 2 || (nr_env == 4 && wdt == FP_I8)) p.sc.nr = (int)nr_env;
         p.sc.u = p.sc.mf >= 4 ? 4 : 8;      // K chunk 32 * u: must match the launcher
         const int nb = 64 * p.sc.nr;

@@ -14,6 +14,8 @@ void launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipS
 hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s) {
     if (grid_wgs <= 0 || a.tiles_n <= 0) return hipSuccess;
     if (a.epi == EPI_SWIGLU && c.nr % 2 != 0) return hipErrorInvalidValue;
+    // the instantiated row counts (see launch_stream_mf)
+    if (c.nr != 2 && !(c.nr == 1 && !w_i8 && c.mf <= 2) && !(c.nr == 4 && w_i8)) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)grid_wgs;
     if (w_i8) launch_stream_i8(c, a, grid, s);
     else if (act == ACT_F16) launch_stream_f16(c, a, grid, s);

@@ -370,12 +370,19 @@ inline void launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStre
 
 // 64 token rows: 128-wide K chunks (two activation / weight register sets of
 // 256-wide chunks do not fit in the register file next to the accumulators)
+// Weight rows per workgroup: 64 (NR = 1) only for 16-bit weights at up to 32
+// tokens, 256 (NR = 4) only for int8 weights; only those combinations are
+// instantiated.
 template <int ACT, bool WI8, int MF>
 inline void launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
     constexpr int U = MF >= 4 ? 4 : 8;
-    if (c.nr == 1) launch_stream_cfg<ACT, WI8, MF, 1, U>(a.epi, a, grid, s);
-    else if (c.nr == 2 || !WI8) launch_stream_cfg<ACT, WI8, MF, 2, U>(a.epi, a, grid, s);
-    else launch_stream_cfg<ACT, WI8, MF, 4, U>(a.epi, a, grid, s);   // int8: 256 rows share one A tile
+    if (c.nr == 2) {
+        launch_stream_cfg<ACT, WI8, MF, 2, U>(a.epi, a, grid, s);
+    } else if (c.nr == 1) {
+        if constexpr (!WI8 && MF <= 2) launch_stream_cfg<ACT, WI8, MF, 1, U>(a.epi, a, grid, s);
+    } else {
+        if constexpr (WI8) launch_stream_cfg<ACT, WI8, MF, 4, U>(a.epi, a, grid, s);   // 256 rows share one A tile
+    }
 }
 
 template <int ACT, bool WI8>
