@@ -218,6 +218,34 @@ def generate(wl: Workload, seed: int = 0, parts=("qkv", "gu")) -> Dict[str, torc
     return out
 
 
+def device_normal(shape, std: float, dtype: torch.dtype, device, seed: int) -> torch.Tensor:
+    """Seeded N(0, std) draws made on the device, for inputs too large to draw
+    on the host (past 4 GiB): torch's generator on ``device`` seeded with
+    ``seed``, float32 samples scaled by std, rounded to ``dtype`` (RNE), drawn
+    in slices of at most 2^28 elements so the float32 staging stays small."""
+    return _device_draw(shape, dtype, device, seed, lambda t, g: t.normal_(0.0, std, generator=g))
+
+
+def device_uniform(shape, lo: float, hi: float, dtype: torch.dtype, device, seed: int) -> torch.Tensor:
+    """Seeded U(lo, hi) draws made on the device; as ``device_normal``."""
+    return _device_draw(shape, dtype, device, seed, lambda t, g: t.uniform_(lo, hi, generator=g))
+
+
+def _device_draw(shape, dtype, device, seed, fill) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    step = 1 << 28
+    for i in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - i)
+        tmp = torch.empty(n, dtype=torch.float32, device=device)
+        fill(tmp, g)
+        flat[i:i + n].copy_(tmp)
+        del tmp
+    return out
+
+
 def rows(t: torch.Tensor, idx) -> torch.Tensor:
     """Gather token rows (rows are independent in every step of the path)."""
     return t[torch.as_tensor(idx, dtype=torch.long)].contiguous()

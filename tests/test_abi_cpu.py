@@ -202,6 +202,15 @@ def test_plan_routing_families(monkeypatch):
     assert p["splits"] == 1 and p["grid"] == 224
     assert _plan(2048, 4096, 16384, act=torch.float16, w=torch.float16, fn="gelu_tanh")["kernel"] == \
         "prefill_kernel<f16,128x512,gelu>"
+    # past 4 GiB of activations or of weights the 128 x 512 kernel's 32-bit
+    # buffer offsets do not reach: the tiled kernel; decode counts stream any size
+    m_big = (1 << 32) // (2 * 4096) + 64
+    assert _plan(m_big, 4096, 256)["family"] == "tiled"
+    assert _plan(m_big - 128, 4096, 256)["family"] == "prefill"
+    f_big = (1 << 32) // (2 * 2 * 8192) + 32
+    assert _plan(96, 8192, 2 * f_big, fn="swiglu")["family"] == "tiled"
+    assert _plan(96, 8192, 2 * f_big - 128, fn="swiglu")["family"] == "prefill"
+    assert _plan(8, 8192, 2 * f_big, fn="swiglu")["family"] == "stream"
 
 
 def test_plan_grid_slots_consistent(monkeypatch):
