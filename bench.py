@@ -383,6 +383,9 @@ def main():
                     help="write profiles/all_configs.md from the output of --all-configs")
     ap.add_argument("--all-configs", action="store_true",
                     help="per-call times and roofline fractions of every workload, one JSON line each")
+    ap.add_argument("--tune-file", metavar="JSON",
+                    help="install this launch-configuration table (python -m fusion_residual_add_amd.tune "
+                         "--out) before timing; the default is the built-in planner")
     args = ap.parse_args()
     if args.traffic_summarize:
         traffic_summarize(args.workload, *args.traffic_summarize, args.cmd)
@@ -405,6 +408,10 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
 
+    if args.tune_file:
+        import fusion_residual_add_amd as fra
+        from fusion_residual_add_amd import tune
+        fra.tune_install(tune.load(args.tune_file))
     if args.traffic_probe:
         traffic_probe(args.workload)
         return
@@ -454,6 +461,7 @@ def main():
                    "weight_sets_rotated": run.R},
         "roofline": roof,
         "kernel_us": per_call,
+        "tuning_table": args.tune_file,
     }
     del run
     torch.cuda.empty_cache()

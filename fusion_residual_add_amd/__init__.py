@@ -18,7 +18,7 @@ from ._lib import FP_ACT, FP_NORM
 
 __all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_dequant_i8_bf16",
            "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
-           "library_path"]
+           "library_path", "tune_install", "tune_clear", "tune_count"]
 
 _DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
        torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8}
@@ -197,3 +197,32 @@ def profile_stop() -> Dict[str, Tuple[int, float]]:
     _check("fp_profile_stop", lib.fp_profile_stop(buf, 64, ctypes.byref(n)))
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
             for i in range(min(n.value, 64))}
+
+
+_FAMILY = {None: -1, "tiled": 0, "stream": 1, "prefill": 2}
+
+
+def tune_install(entries) -> None:
+    """Install a launch-configuration table (fp_tune_install; replaces the
+    previous one).  Each entry is a dict with m_lo, m_hi, hidden, n_cols,
+    act_dtype, w_dtype (torch dtypes) and swiglu (bool), and optionally family
+    ("tiled", "stream", "prefill" or None for the planner's), rows, grid and
+    splits (0 for the planner's).  See fusion_residual_add_amd.tune for the
+    micro-benchmark that produces such tables."""
+    entries = list(entries)
+    arr = (_lib.TuneEntry * max(len(entries), 1))()
+    for i, e in enumerate(entries):
+        arr[i] = _lib.TuneEntry(int(e["m_lo"]), int(e["m_hi"]), int(e["hidden"]), int(e["n_cols"]),
+                                _DT[e["act_dtype"]], _DT[e["w_dtype"]], int(bool(e["swiglu"])),
+                                _FAMILY[e.get("family")], int(e.get("rows", 0)), int(e.get("grid", 0)),
+                                int(e.get("splits", 0)))
+    _check("fp_tune_install", _lib.load().fp_tune_install(arr, len(entries)))
+
+
+def tune_clear() -> None:
+    """Remove every tuning entry: the built-in planner decides again."""
+    tune_install([])
+
+
+def tune_count() -> int:
+    return int(_lib.load().fp_tune_count())

@@ -20,12 +20,20 @@ STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_
 # every symbol include/fusedproj.h declares
 EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_gateup_act",
            "fused_dequant_i8_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
-           "fp_profile_start", "fp_profile_stop"]
+           "fp_profile_start", "fp_profile_stop", "fp_tune_install", "fp_tune_count"]
 
 
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double)]
+
+
+class TuneEntry(ctypes.Structure):
+    """fp_tune_entry of include/fusedproj.h."""
+    _fields_ = [("m_lo", ctypes.c_int64), ("m_hi", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("n_cols", ctypes.c_int64), ("act_dtype", ctypes.c_int), ("w_dtype", ctypes.c_int),
+                ("swiglu", ctypes.c_int32), ("family", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("splits", ctypes.c_int32)]
 
 
 _lib = None
@@ -62,6 +70,10 @@ def load(path: str = None):
     lib.fp_profile_start.restype = ci
     lib.fp_profile_stop.argtypes = [ctypes.POINTER(KernelTime), ci, ctypes.POINTER(ci)]
     lib.fp_profile_stop.restype = ci
+    lib.fp_tune_install.argtypes = [ctypes.POINTER(TuneEntry), i64]
+    lib.fp_tune_install.restype = ci
+    lib.fp_tune_count.argtypes = []
+    lib.fp_tune_count.restype = i64
     if path == LIB_PATH:
         _lib = lib
     return lib

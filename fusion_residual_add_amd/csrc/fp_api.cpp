@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -54,20 +55,85 @@ long env_long(const char *name, long dflt) {
     return strtol(s, nullptr, 10);
 }
 
+// Launch-configuration overrides for one call: from the installed tuning
+// table (fp_tune_install), then from FUSEDPROJ_* environment variables, which
+// win (they are for sweeps).  Zero / -1 fields leave the planner's choice.
+struct Knobs {
+    int family = -1;          // 0 tiled, 1 stream, 2 prefill; -1 the planner's
+    long rows = 0;            // stream: weight rows per workgroup (64, 128, 256)
+    long grid = 0;            // stream: workgroups
+    long splits = 0;          // tiled / prefill: K splits
+    long stream_splits = 0;   // stream: workgroups per tile (environment only)
+    long target = 256;        // stream: workgroup budget
+    bool no_stream = false, no_prefill = false;
+};
+
+std::mutex g_tune_mu;
+std::vector<fp_tune_entry> g_tune;
+
+Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu) {
+    Knobs kb;
+    {
+        std::lock_guard<std::mutex> lk(g_tune_mu);
+        for (const fp_tune_entry &e : g_tune) {
+            if (M < e.m_lo || M > e.m_hi || e.hidden != K || e.n_cols != Nw || e.act_dtype != act ||
+                e.w_dtype != wdt || (e.swiglu != 0) != swiglu)
+                continue;
+            kb.family = e.family;
+            kb.rows = e.rows;
+            kb.grid = e.grid;
+            kb.splits = e.splits;
+            break;
+        }
+    }
+    kb.target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
+    if (env_long("FUSEDPROJ_NO_STREAM", 0) != 0) {
+        kb.no_stream = true;
+        if (kb.family == 1) kb.family = -1;
+    }
+    if (env_long("FUSEDPROJ_NO_PREFILL", 0) != 0) {
+        kb.no_prefill = true;
+        if (kb.family == 2) kb.family = -1;
+    }
+    const long nr_env = env_long("FUSEDPROJ_STREAM_NR", 0);
+    if (nr_env > 0) kb.rows = 64 * nr_env;
+    const long sp_env = env_long("FUSEDPROJ_SPLITS", 0);
+    if (sp_env > 0) {
+        kb.splits = sp_env;
+        kb.stream_splits = sp_env;
+        kb.grid = 0;
+    }
+    return kb;
+}
+
 // Decode token counts (M <= 64, 16-bit activations) use the weight-streaming
 // kernel, which spreads (tile, K chunk) units evenly over one workgroup per
-// CU; token counts above 64 the 128 x 512 prefill kernel; everything else
-// the tiled kernel.  When a tiled grid would hold too few workgroups, K is
+// CU; token counts above 64 the 128 x 512 prefill kernel while its 32-bit
+// buffer offsets reach (activations and weights under 4 GiB each);
+// everything else the tiled kernel (64-bit offsets).  When a tiled grid would hold too few workgroups, K is
 // split.  Partial sums are reduced by the last contributor to arrive, in a
 // fixed order.
-// FUSEDPROJ_* environment variables override the choices (for tuning sweeps);
-// the workspace query and the call read them alike.
+// A tuning-table entry or FUSEDPROJ_* environment variables override the
+// choices (Knobs); the workspace query and the call read them alike.  A
+// requested family is used only where it can take the call: the streaming
+// kernel needs 16-bit activations, M <= 64 and K a multiple of 256; the
+// 128 x 512 kernel 16-bit activations and operands under 4 GiB.
 Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu) {
     Plan p;
-    const bool stream_ok = act != FP_F32 && M <= 64 && K % 256 == 0 &&
-                           env_long("FUSEDPROJ_NO_STREAM", 0) == 0;
+    const Knobs kb = knobs_for(M, K, Nw, act, wdt, swiglu);
+    const bool stream_elig = act != FP_F32 && M <= 64 && K % 256 == 0;
+    const bool prefill_elig = act != FP_F32 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32);
+    int fam;
+    if (kb.family == 0 || (kb.family == 1 && stream_elig) || (kb.family == 2 && prefill_elig))
+        fam = kb.family;
+    else if (stream_elig && !kb.no_stream)
+        fam = 1;
+    else if (prefill_elig && M > 64 && !kb.no_prefill)
+        fam = 2;
+    else
+        fam = 0;
     int64_t tiles, ksteps, target;
-    if (stream_ok) {
+    if (fam == 1) {
         p.family = 1;
         p.sc.mf = M <= 16 ? 1 : M <= 32 ? 2 : 4;
         // weight rows per workgroup 64 * nr: int8 weights at 33..64 tokens take
@@ -80,11 +146,12 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // MI355X: Llama-3-8B QKV 1.1 us faster per call; with int8 weights, or
         // at 33..64 tokens where the A tile is four times as large, 64-row
         // tiles are slower)
-        const long nr_env = env_long("FUSEDPROJ_STREAM_NR", 0);
         p.sc.nr = wdt == FP_I8 && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
         if (!swiglu && wdt != FP_I8 && p.sc.mf <= 2) p.sc.nr = 1;
-        if (nr_env == 1 && !swiglu && wdt != FP_I8 && p.sc.mf <= 2) p.sc.nr = 1;   // instantiated forms only
-        if (nr_env == 2 || (nr_env == 4 && wdt == FP_I8)) p.sc.nr = (int)nr_env;
+        // requested rows: only the instantiated forms (64 for 16-bit weights
+        // without the gate/up pairing at up to 32 tokens, 256 for int8)
+        if (kb.rows == 64 && !swiglu && wdt != FP_I8 && p.sc.mf <= 2) p.sc.nr = 1;
+        if (kb.rows == 128 || (kb.rows == 256 && wdt == FP_I8)) p.sc.nr = (int)(kb.rows / 64);
         p.sc.u = p.sc.mf >= 4 ? 4 : 8;      // K chunk 32 * u: must match the launcher
         const int nb = 64 * p.sc.nr;
         p.tiles_m = 1;
@@ -92,7 +159,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         p.tile_elems = (int64_t)16 * p.sc.mf * nb;
         tiles = p.tiles_n;
         ksteps = K / (32 * p.sc.u);
-        target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
+        target = kb.target;
         // stream-K: `grid` workgroups take equal contiguous unit ranges of at
         // least 512 of K each (2 chunks of 256, 4 of 128; measured on MI355X:
         // shorter ranges pay the pipeline ramp too often, and 2 chunks of 256
@@ -120,8 +187,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
                 }
             }
         }
-        const long forced = env_long("FUSEDPROJ_SPLITS", 0);
-        if (forced > 0) G = tiles * forced;
+        if (kb.grid > 0) G = kb.grid;
+        if (kb.stream_splits > 0) G = tiles * kb.stream_splits;
         if (G > units) G = units;
         if (G < 1) G = 1;
         p.grid = (int)G;
@@ -133,8 +200,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
             if (n > most) most = n;
         }
         p.slots = (int)most;
-    } else if (act != FP_F32 && M > 64 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32) &&
-               env_long("FUSEDPROJ_NO_PREFILL", 0) == 0) {
+    } else if (fam == 2) {
         p.family = 2;
         p.tiles_m = (int)((M + 127) / 128);
         p.tiles_n = (int)((Nw + 511) / 512);
@@ -176,8 +242,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         if (s > smax) s = smax;
         if (s > 16) s = 16;
         if (s < 1) s = 1;
-        const long forced = env_long("FUSEDPROJ_SPLITS", 0);
-        if (forced > 0) s = forced < ksteps ? forced : ksteps;
+        if (kb.splits > 0) s = kb.splits < ksteps ? kb.splits : ksteps;
         p.splits = (int)s;
         p.slots = (int)s;
     }
@@ -522,6 +587,28 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu", fam, name,
              (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total);
     return FP_OK;
+}
+
+fp_status fp_tune_install(const fp_tune_entry *entries, int64_t n) {
+    if (n < 0 || n > 65536) return fail(FP_E_ARG, "n = %lld entries (0 .. 65536)", (long long)n);
+    if (n > 0 && !entries) return fail(FP_E_NULL, "entries is NULL");
+    for (int64_t i = 0; i < n; ++i) {
+        const fp_tune_entry &e = entries[i];
+        const bool ok = e.m_lo >= 0 && e.m_hi >= e.m_lo && e.hidden > 0 && e.n_cols > 0 &&
+                        e.family >= -1 && e.family <= 2 &&
+                        (e.rows == 0 || e.rows == 64 || e.rows == 128 || e.rows == 256) &&
+                        e.grid >= 0 && e.grid <= 65535 && e.splits >= 0 && e.splits <= 64 &&
+                        (e.swiglu == 0 || e.swiglu == 1) && check_dtypes(e.act_dtype, e.w_dtype, e.act_dtype) == FP_OK;
+        if (!ok) return fail(FP_E_ARG, "tuning entry %lld is out of range", (long long)i);
+    }
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tune.assign(entries, entries + n);
+    return FP_OK;
+}
+
+int64_t fp_tune_count(void) {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    return (int64_t)g_tune.size();
 }
 
 const char *fp_status_str(fp_status s) {

@@ -144,11 +144,61 @@ fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_b
  *    splits=1 slots=2 workspace=4227328"
  * into buf (truncated to cap bytes).  n_cols is the weight row count as for
  * fp_workspace_bytes; act selects the gate/up pairing (FP_ACT_SWIGLU) or not.
- * A diagnostic for tuning and tests: it reads the same FUSEDPROJ_* overrides
- * as the calls, touches no device and returns FP_E_SHAPE / FP_E_DTYPE /
+ * A diagnostic for tuning and tests: it reads the same tuning table and
+ * FUSEDPROJ_* overrides as the calls, touches no device and returns FP_E_SHAPE / FP_E_DTYPE /
  * FP_E_ARG / FP_E_NULL for arguments the calls would reject. */
 fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
                            fp_dtype w_dtype, fp_act act, char *buf, size_t cap);
+
+/* Launch-configuration tuning table.  The pages build their kernels by
+ * running candidate configurations on the target GPU for the shapes at hand
+ * and keeping the fastest ("TensorRT-LLM 深度工程实践…", §2.4 内核自动调优;
+ * "TRT-LLM deep dive", 构建阶段详解 step 2 and 面试视角: micro-benchmarks of
+ * GEMM configurations per GPU and input shape).  Here the micro-benchmark is
+ * fusion_residual_add_amd.tune (Python, timing through these calls); its
+ * result is a table of entries that override the built-in planner for calls
+ * whose sizes match.
+ *
+ * An entry matches a call when m_lo <= M <= m_hi and hidden, n_cols (the
+ * weight row count, as for fp_workspace_bytes), act_dtype, w_dtype and the
+ * gate/up pairing (swiglu = 1 for FP_ACT_SWIGLU) are equal; the first match
+ * wins.  Its fields, each 0 (or -1 for family) to keep the planner's choice:
+ *  family : 0 the tiled kernel, 1 the weight-streaming kernel, 2 the
+ *           128 x 512 kernel; ignored where that family cannot take the call
+ *           (streaming: 16-bit activations, M <= 64, hidden a multiple of
+ *           256; 128 x 512: 16-bit activations, x / residual and weight
+ *           under 4 GiB each);
+ *  rows   : streaming kernel, weight rows per workgroup: 128, 64 (16-bit
+ *           weights, no gate/up pairing, M <= 32) or 256 (int8 weights);
+ *           other values are ignored;
+ *  grid   : streaming kernel, workgroups (at most one per unit of work);
+ *  splits : tiled and 128 x 512 kernels, ways K is split.
+ * Results stay within the parity bounds for any entry (only the order of the
+ * fp32 partial sums changes) and are deterministic for a given table.
+ * fp_workspace_bytes and fp_describe_plan read the same table, so install
+ * it before sizing workspaces.  The FUSEDPROJ_* environment overrides, when
+ * set, take precedence over the table.
+ *
+ * fp_tune_install copies n entries (replacing the previous table; n = 0
+ * clears it); FP_E_ARG if a field is out of range, FP_E_NULL if entries is
+ * NULL with n > 0.  The table is process-wide and guarded by a lock; install
+ * it between calls, not while another thread is inside a call whose plan it
+ * would change.  fp_tune_count returns the number of installed entries. */
+typedef struct {
+    int64_t m_lo, m_hi;
+    int64_t hidden;
+    int64_t n_cols;
+    fp_dtype act_dtype;
+    fp_dtype w_dtype;
+    int32_t swiglu;
+    int32_t family;
+    int32_t rows;
+    int32_t grid;
+    int32_t splits;
+} fp_tune_entry;
+
+fp_status fp_tune_install(const fp_tune_entry *entries, int64_t n);
+int64_t fp_tune_count(void);
 
 /* Static text for a status code. */
 const char *fp_status_str(fp_status s);

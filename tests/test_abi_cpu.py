@@ -244,3 +244,80 @@ def test_plan_rejects():
         _plan(32, 4000, 6144)                  # hidden not a multiple of 64
     with pytest.raises(fra.FusedProjError):
         _plan(32, 4096, 6144, act=torch.float16, w=torch.int8)
+
+
+_ENV = ("FUSEDPROJ_SPLITS", "FUSEDPROJ_NO_STREAM", "FUSEDPROJ_NO_PREFILL", "FUSEDPROJ_STREAM_NR",
+        "FUSEDPROJ_STREAM_TARGET")
+
+
+def _entry(**kw):
+    e = dict(m_lo=17, m_hi=32, hidden=4096, n_cols=6144, act_dtype=torch.bfloat16,
+             w_dtype=torch.bfloat16, swiglu=False)
+    e.update(kw)
+    return e
+
+
+def test_tuning_table_overrides_matching_calls(monkeypatch):
+    for var in _ENV:
+        monkeypatch.delenv(var, raising=False)
+    base, base_gu, base_33 = _plan(32, 4096, 6144), _plan(32, 4096, 6144, fn="swiglu"), _plan(33, 4096, 6144)
+    try:
+        fra.tune_install([_entry(family="stream", rows=128, grid=192)])
+        assert fra.tune_count() == 1
+        p = _plan(32, 4096, 6144)
+        assert p["kernel"] == "stream_kernel<bf16,m32,n128,k256,linear>" and p["grid"] == 192
+        assert _plan(17, 4096, 6144)["grid"] == 192
+        # other token counts, the gate/up pairing and other sizes keep the planner's choice
+        assert _plan(33, 4096, 6144) == base_33
+        assert _plan(32, 4096, 6144, fn="swiglu") == base_gu
+        assert _plan(32, 4096, 6400) == fra.describe_plan(32, 4096, 6400, torch.bfloat16, torch.bfloat16)
+        # the workspace query reads the same table
+        assert fra.workspace_bytes(32, 4096, 6144, torch.bfloat16, torch.bfloat16) >= p["workspace"]
+        # any family that can take the call, with its split
+        fra.tune_install([_entry(family="tiled", splits=3)])
+        p = _plan(32, 4096, 6144)
+        assert p["family"] == "tiled" and p["splits"] == 3
+        fra.tune_install([_entry(family="prefill", splits=2)])
+        p = _plan(32, 4096, 6144)
+        assert p["family"] == "prefill" and p["splits"] == 2 and p["grid"] == 12 * 2
+        # a family that cannot take the call is ignored (fp32 activations stream nowhere)
+        fra.tune_install([_entry(family="stream", act_dtype=torch.float32, w_dtype=torch.float32)])
+        assert _plan(32, 4096, 6144, act=torch.float32, w=torch.float32)["family"] == "tiled"
+        # 64 rows per workgroup only where that form exists: ignored for the gate/up pairing
+        fra.tune_install([_entry(rows=64, swiglu=True)])
+        assert _plan(32, 4096, 6144, fn="swiglu") == base_gu
+        fra.tune_install([_entry(rows=128)])
+        assert _plan(32, 4096, 6144)["kernel"] == "stream_kernel<bf16,m32,n128,k256,linear>"
+        # the first matching entry wins; the environment overrides win over the table
+        fra.tune_install([_entry(grid=128), _entry(grid=64)])
+        assert _plan(32, 4096, 6144)["grid"] == 128
+        fra.tune_install([_entry(family="stream")])
+        monkeypatch.setenv("FUSEDPROJ_NO_STREAM", "1")
+        assert _plan(32, 4096, 6144)["family"] == "tiled"
+        monkeypatch.delenv("FUSEDPROJ_NO_STREAM")
+        fra.tune_clear()
+        assert fra.tune_count() == 0 and _plan(32, 4096, 6144) == base
+    finally:
+        fra.tune_clear()
+
+
+@pytest.mark.parametrize("bad", [dict(rows=96), dict(m_lo=40, m_hi=8), dict(family=3), dict(splits=65),
+                                 dict(grid=-1), dict(hidden=0), dict(act_dtype=torch.float16, w_dtype=torch.int8)],
+                         ids=lambda b: ",".join(f"{k}={v}" for k, v in b.items()))
+def test_tuning_table_rejects(bad):
+    good = _entry(grid=200)
+    try:
+        fra.tune_install([good])
+        e = dict(good)
+        if "family" in bad and bad["family"] == 3:
+            arr = (_lib.TuneEntry * 1)()
+            arr[0] = _lib.TuneEntry(17, 32, 4096, 6144, BF16, BF16, 0, 3, 0, 0, 0)
+            assert lib().fp_tune_install(arr, 1) == _lib.STATUS.index("FP_E_ARG")
+        else:
+            e.update(bad)
+            with pytest.raises(fra.FusedProjError):
+                fra.tune_install([good, e])
+        # a rejected table leaves the installed one in place
+        assert fra.tune_count() == 1 and _plan(32, 4096, 6144)["grid"] == 200
+    finally:
+        fra.tune_clear()
