@@ -20,7 +20,11 @@ Recipe (stated once, used everywhere):
 * int8 weights: a float32 weight is drawn as above, then quantised per output
   row with the symmetric max-abs rule ``s = max|w| / 127`` (float32) and
   ``q = clip(rint(w / s), -127, 127)``.  The stored inputs of the method are
-  ``(q, s)``; how they were produced is not part of the path.
+  ``(q, s)``; how they were produced is not part of the path;
+* int4 weights (4-bit weights with 16-bit activations, group 128, no zero
+  point): per output row and group of 128 consecutive k,
+  ``s = max|w| / 7`` (float32) and ``q = clip(rint(w / s), -8, 7)``, packed
+  two per byte along k (even k in the low nibble), scales ``[N, K/128]``.
 
 Workload shapes follow the five transformer-block configurations that the
 fused-projection pages are measured on: a tiny fp32 block, a Llama-3-8B decode
@@ -44,7 +48,7 @@ class Workload:
     M: int
     hidden: int
     act: str                    # "f32" | "f16" | "bf16"
-    wdt: str                    # "f32" | "f16" | "bf16" | "i8"
+    wdt: str                    # "f32" | "f16" | "bf16" | "i8" | "i4"
     norm: str                   # "rms" | "layer"
     eps: float
     x_std: float
@@ -92,6 +96,12 @@ def _llama70b_tp8(M: int) -> Workload:
                                ffn=28672 // 8)
 
 
+def _llama70b_i4(M: int) -> Workload:
+    """The Llama-2-70B layer with int4 weights, one scale per 128 k (the
+    4-bit weight-only configuration of the pages' quantisation section)."""
+    return dataclasses.replace(_llama70b(M), name=f"llama2-70b-int4w@M{M}", wdt="i4")
+
+
 WORKLOADS: Dict[str, Workload] = {
     # tiny fp32 block: M=4, hidden=256, 4 Q / 2 KV heads of 64, ffn=512
     "tiny-f32": Workload(
@@ -126,6 +136,9 @@ WORKLOADS: Dict[str, Workload] = {
     "llama2-70b-int8w-tp8@M1": _llama70b_tp8(1),
     "llama2-70b-int8w-tp8@M16": _llama70b_tp8(16),
     "llama2-70b-int8w-tp8@M64": _llama70b_tp8(64),
+    "llama2-70b-int4w@M1": _llama70b_i4(1),
+    "llama2-70b-int4w@M16": _llama70b_i4(16),
+    "llama2-70b-int4w@M256": _llama70b_i4(256),
 }
 
 
@@ -175,11 +188,45 @@ def quantize_rows_i8(w: np.ndarray):
     return torch.from_numpy(q), torch.from_numpy(s)
 
 
+I4_GROUP = 128
+
+
+def quantize_groups_i4(w: np.ndarray):
+    """Symmetric int4 storage of a float32 ``[N, K]`` weight, one scale per
+    row and group of 128 consecutive k.
+
+    ``s[j, g] = max |w[j, 128 g : 128 g + 128]| / 7`` in float32 and
+    ``q = clip(rint(w / s), -8, 7)`` (an all-zero group gets s = 0, q = 0);
+    returns ``(q packed [N, K/2] uint8, s [N, K/128] float32)`` with element
+    2i of a row in the low nibble of byte i and 2i + 1 in the high nibble,
+    each a 4-bit two's-complement value.
+    """
+    N, K = w.shape
+    assert K % I4_GROUP == 0, "int4 weights need K a multiple of 128"
+    G = K // I4_GROUP
+    q = np.empty((N, K // 2), dtype=np.uint8)
+    s = np.empty((N, G), dtype=np.float32)
+    step = max(1, (1 << 24) // max(K, 1))
+    for j0 in range(0, N, step):
+        blk = w[j0:j0 + step].reshape(-1, G, I4_GROUP)
+        amax = np.abs(blk).max(axis=2).astype(np.float32)
+        sc = (amax / np.float32(7.0)).astype(np.float32)
+        safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+        qq = np.clip(np.rint(blk / safe[:, :, None]), -8, 7)
+        qq[sc == 0] = 0
+        nib = (qq.astype(np.int16).reshape(blk.shape[0], K) & 0xF).astype(np.uint8)
+        q[j0:j0 + step] = nib[:, 0::2] | (nib[:, 1::2] << 4)
+        s[j0:j0 + step] = sc
+    return torch.from_numpy(q), torch.from_numpy(s)
+
+
 def _weight(rng, wl: Workload, N: int):
     w = _normal(rng, (N, wl.hidden), wl.w_std)
     if wl.wdt == "i8":
         q, s = quantize_rows_i8(w)
         return q, s
+    if wl.wdt == "i4":
+        return quantize_groups_i4(w)
     return _to_act(w, wl.wdt), None
 
 
@@ -188,7 +235,7 @@ def generate(wl: Workload, seed: int = 0, parts=("qkv", "gu")) -> Dict[str, torc
 
     Keys: x, r, gamma, beta (LayerNorm only), and per projection
     w_qkv / s_qkv / b_qkv and w_gu / s_gu / b_gu.  ``s_*`` is present only for
-    int8 weights; ``b_*`` only when the workload has that bias.  ``parts``
+    int8 and int4 weights; ``b_*`` only when the workload has that bias.  ``parts``
     selects which projections to draw, but the draw order (and hence every
     value) does not depend on it: skipped weights are still drawn.
     """

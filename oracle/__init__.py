@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _OUT = os.path.join(_HERE, "_build", "liboracle.so")
 
-F32, F16, BF16, I8 = 0, 1, 2, 3
+F32, F16, BF16, I8, I4 = 0, 1, 2, 3, 4
+I4_GROUP = 128
 NORM = {"none": 0, "rms": 1, "layer": 2}
 ACT = {"none": 0, "swiglu": 1, "gelu_tanh": 2}
 DT = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8}
@@ -80,6 +81,10 @@ def load(path: Optional[str] = None):
     lib.or_gelu_tanh.restype = dbl
     lib.or_num_threads.restype = ci
     lib.or_dequant_i8.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.or_dequant_i4.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.or_dequant_i4.restype = ci
+    lib.or_i4_value.argtypes = [vp, i64]
+    lib.or_i4_value.restype = ci
     lib.or_add_norm.argtypes = [vp, vp, vp, vp, ci, ci, dbl, i64, i64, vp, vp, vp]
     lib.or_add_norm.restype = ci
     lib.or_matmul_nt.argtypes = [vp, vp, ci, vp, i64, i64, i64, vp]
@@ -117,6 +122,8 @@ def _raw(t):
         return t.numpy(), F32
     if t.dtype == torch.int8:
         return t.numpy(), I8
+    if t.dtype == torch.uint8:               # int4 weights, two per byte (R9)
+        return t.numpy(), I4
     raise TypeError(f"oracle: unsupported dtype {t.dtype}")
 
 
@@ -163,6 +170,19 @@ def dequant_i8(q, s):
     w = _f64((N, K))
     bits = np.zeros((N, K), dtype=np.uint16)
     load().or_dequant_i8(_ptr(qa), _ptr(sa), N, K, _ptr(w), _ptr(bits))
+    return w, bits
+
+
+def dequant_i4(q, s):
+    """(w as float64 [N, K], bf16 bit patterns as uint16) of int4 weights q
+    [N, K/2] (uint8, two per byte, even k in the low nibble) with group scales
+    s [N, K/128] (R9)."""
+    qa, _ = _raw(q)
+    sa = np.ascontiguousarray(_raw(s)[0], dtype=np.float32)
+    N, K = qa.shape[0], 2 * qa.shape[1]
+    w = _f64((N, K))
+    bits = np.zeros((N, K), dtype=np.uint16)
+    assert load().or_dequant_i4(_ptr(qa), _ptr(sa), N, K, _ptr(w), _ptr(bits)) == 0
     return w, bits
 
 

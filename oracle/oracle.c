@@ -44,6 +44,15 @@
  *  R7 bias (when given) is added to the accumulator before the activation.
  *  R8 int8 weights: w = RNE_bf16(RNE_f32(q * s)) with s the fp32 scale of the
  *     output row; both roundings are part of the definition.
+ *  R9 int4 weights (4-bit weights with 16-bit activations, symmetric, one
+ *     scale per group of 128 consecutive k, no zero point: [Q] below): the
+ *     [N, K] weight is stored as [N, K/2] bytes, element k of a row in the
+ *     low nibble of byte k/2 for even k and in the high nibble for odd k,
+ *     each nibble a two's-complement integer in [-8, 7]; the scales are
+ *     [N, K/128] fp32; w = RNE_bf16(RNE_f32(q * s[row][k/128])), the two
+ *     roundings of R8.
+ *  [Q] "TensorRT-LLM 深度工程实践…", §3.3 FP4/FP8 动态量化加速: the W4A16
+ *      (AWQ/GPTQ) configuration with group size 128 and no zero point.
  */
 #include <math.h>
 #include <stdint.h>
@@ -53,7 +62,8 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_I4 = 4 };
+enum { OR_I4_GROUP = 128 };
 enum { OR_NORM_NONE = 0, OR_NORM_RMS = 1, OR_NORM_LAYER = 2 };
 enum { OR_ACT_NONE = 0, OR_ACT_SWIGLU = 1, OR_ACT_GELU_TANH = 2 };
 
@@ -166,6 +176,33 @@ int or_dequant_i8(const int8_t *q, const float *s, int64_t N, int64_t K,
 }
 
 /* ---------------------------------------------------------------------------
+ * int4 weight dequantisation (R9): element k of row j is the nibble
+ * (byte k/2 of the row) >> (4 (k mod 2)), read as a 4-bit two's-complement
+ * integer, times the scale of its group k / 128; then the two roundings of
+ * R8.  q * s is exact in double (4-bit times 24-bit significands).
+ * ------------------------------------------------------------------------- */
+int or_i4_value(const uint8_t *row, int64_t k) {
+    int nib = (row[k / 2] >> (4 * (int)(k % 2))) & 0xF;
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+int or_dequant_i4(const uint8_t *q, const float *s, int64_t N, int64_t K,
+                  double *w_out, uint16_t *bits_out) {
+    if (K % OR_I4_GROUP != 0) return -1;
+    const int64_t G = K / OR_I4_GROUP;
+    for (int64_t j = 0; j < N; ++j) {
+        const uint8_t *row = q + j * (K / 2);
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = (double)or_i4_value(row, k) * (double)s[j * G + k / OR_I4_GROUP];
+            double w = or_round(or_round(prod, OR_F32), OR_BF16);
+            if (w_out) w_out[j * K + k] = w;
+            if (bits_out) bits_out[j * K + k] = bf16_bits_of(w);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Residual add and row normalisation, one token row at a time ([D], [I]).
  *  h = x + r                                        (R1; r may be NULL)
  *  RMS:   n = h / sqrt(sum(h^2)/K + eps) * gamma    (R2)
@@ -221,9 +258,10 @@ int or_add_norm(const void *x, const void *r, const void *gamma, const void *bet
 
 /* ---------------------------------------------------------------------------
  * The projection product acc[m, j] = sum_k a[m, k] * w[j, k]  ([D]).
- * w is [N, K] with K contiguous, in its stored dtype; int8 weights go through
- * the dequantisation above (R8).  Each weight row is decoded once into a
- * double buffer and then used for every token row.
+ * w is [N, K] with K contiguous, in its stored dtype; int8 and int4 weights
+ * go through the dequantisations above (R8, R9; w_scale is [N] or
+ * [N, K/128]).  Each weight row is decoded once into a double buffer and then
+ * used for every token row.
  * ------------------------------------------------------------------------- */
 int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scale,
                  int64_t M, int64_t K, int64_t N, double *acc) {
@@ -234,7 +272,10 @@ int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scal
         if (!wr) { bad = 1; continue; }
         if (wdtype == OR_I8)
             or_dequant_i8((const int8_t *)w + j * K, w_scale + j, 1, K, wr, NULL);
-        else
+        else if (wdtype == OR_I4) {
+            if (or_dequant_i4((const uint8_t *)w + j * (K / 2), w_scale + j * (K / OR_I4_GROUP), 1, K, wr, NULL))
+                bad = 1;
+        } else
             for (int64_t k = 0; k < K; ++k) wr[k] = or_load(w, wdtype, j * K + k);
         for (int64_t m = 0; m < M; ++m) {
             double s = 0.0;

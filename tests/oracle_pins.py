@@ -354,6 +354,58 @@ def pin_dequant_i8_double_rounding_cases():
     assert not np.array_equal(bits, direct[rows])
 
 
+def _pack_i4(q: np.ndarray) -> np.ndarray:
+    """[N, K] ints in [-8, 7] -> [N, K/2] bytes, even k in the low nibble
+    (the storage the int4 weights are defined with), written independently of
+    the input generator."""
+    u = (q.astype(np.int64) % 16).astype(np.uint8)
+    out = np.zeros((q.shape[0], q.shape[1] // 2), dtype=np.uint8)
+    for k in range(q.shape[1]):
+        out[:, k // 2] |= u[:, k] << (4 * (k % 2))
+    return out
+
+
+def pin_dequant_i4_exhaustive():
+    # every nibble value at even and odd k in both groups of a 256-wide row,
+    # with a different scale per (row, group): catches nibble order, sign
+    # extension and group indexing
+    rng = _rng(31)
+    N, K = 40, 256
+    k = np.arange(K)
+    q = (((k[None, :] * 5 + np.arange(N)[:, None] * 3) % 16) - 8).astype(np.int8)      # [N, K]
+    s = np.concatenate([rng.uniform(1e-4, 1e-2, (N - 3, 2)).astype(np.float32),
+                        np.array([[0.0, 1.0], [2.0 ** -7, 3.0], [1.0, 0.02 / 7]], dtype=np.float32)])
+    w, bits = oracle.dequant_i4(torch.from_numpy(_pack_i4(q)), torch.from_numpy(s))
+    s_k = s[:, k // 128]
+    prod32 = q.astype(np.float32) * s_k
+    ref = torch.from_numpy(prod32).to(torch.bfloat16)
+    assert np.array_equal(bits, ref.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(w, ref.double().numpy())
+    assert np.all(w[N - 3, :128] == 0)                 # s = 0 gives zero
+    assert np.array_equal(w[N - 3, 128:], q[N - 3, 128:].astype(np.float64))   # s = 1: the integers
+
+
+def pin_dequant_i4_double_rounding_cases():
+    # every fp32 scale in [2^-9, 2^-8): keep those where rounding q * s to fp32
+    # first changes the bf16 result (a 4-bit q leaves few such scales)
+    s_all = ((np.uint32(118) << 23) | np.arange(1 << 23, dtype=np.uint32)).view(np.float32)
+    picks = []
+    for qv in (3, 5, 7, -7):
+        exact = np.float64(qv) * s_all.astype(np.float64)
+        direct = _bf16_direct_bits(exact)
+        twice = torch.from_numpy(np.float32(qv) * s_all).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        idx = np.nonzero(direct != twice)[0][:4]
+        picks += [(qv, s_all[i], twice[i], direct[i]) for i in idx]
+    assert len(picks) >= 8, "scan found too few double-rounding cases"
+    # one row per case: q in every position of a 128-wide group with that scale
+    q = np.array([[qv] * 128 for qv, _, _, _ in picks], dtype=np.int8)
+    sc = np.array([[sv] for _, sv, _, _ in picks], dtype=np.float32)
+    w, bits = oracle.dequant_i4(torch.from_numpy(_pack_i4(q)), torch.from_numpy(sc))
+    assert np.array_equal(bits[:, 0], np.array([t for _, _, t, _ in picks], dtype=np.uint16))
+    assert not np.array_equal(bits[:, 0], np.array([d for _, _, _, d in picks], dtype=np.uint16))
+    assert np.all(bits == bits[:, :1])
+
+
 # ---------------------------------------------------------------------------
 # full calls
 # ---------------------------------------------------------------------------
@@ -473,6 +525,19 @@ def pin_int8_projection_uses_dequantised_weights():
     w_deq = (q.float() * s[:, None]).to(torch.bfloat16)
     o = oracle.gateup_act(x, r, g, None, "rms", 1e-5, q, s, None, N, "none")
     _close(o["out"], a @ w_deq.double().numpy().T, rtol=1e-13, atol=1e-13, what="int8 proj")
+
+
+def pin_int4_projection_uses_dequantised_weights():
+    rng = _rng(34)
+    M, K, N = 2, 256, 10
+    x, r, g = _tiny(torch.bfloat16, M, K, seed=35)
+    q = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    s = rng.uniform(1e-3, 1e-2, (N, K // 128)).astype(np.float32)
+    _, _, a = oracle.add_norm(x, r, g, None, "rms", 1e-5)
+    w_deq = torch.from_numpy(q.astype(np.float32) * s[:, np.arange(K) // 128]).to(torch.bfloat16)
+    o = oracle.gateup_act(x, r, g, None, "rms", 1e-5, torch.from_numpy(_pack_i4(q)), torch.from_numpy(s),
+                          None, N, "none")
+    _close(o["out"], a @ w_deq.double().numpy().T, rtol=1e-13, atol=1e-13, what="int4 proj")
 
 
 def pin_rounded_vs_unrounded_reading():

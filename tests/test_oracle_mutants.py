@@ -42,6 +42,11 @@ MUTANTS = {
     "round ties away": ("double r = nearbyint(scaled);", "double r = round(scaled);"),
     "bf16 precision off by one": ("case OR_BF16: *p = 8;", "case OR_BF16: *p = 9;"),
     "fp16 subnormal decode": ("mag = ldexp((double)man, -24);", "mag = ldexp((double)man, -25);"),
+    "int4 nibble order": ("int nib = (row[k / 2] >> (4 * (int)(k % 2))) & 0xF;",
+                          "int nib = (row[k / 2] >> (4 * (int)(1 - k % 2))) & 0xF;"),
+    "int4 not sign-extended": ("return nib >= 8 ? nib - 16 : nib;", "return nib;"),
+    "int4 one scale per row": ("s[j * G + k / OR_I4_GROUP]", "s[j * G]"),
+    "int4 group of 64": ("enum { OR_I4_GROUP = 128 };", "enum { OR_I4_GROUP = 64 };"),
 }
 
 
