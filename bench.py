@@ -48,21 +48,23 @@ def algo_bytes(wl, call: str) -> int:
     written once; the normalised rows and the GEMM intermediates are not
     counted (the fusion keeps them on chip)."""
     ea = {"f32": 4, "f16": 2, "bf16": 2}[wl.act]
-    ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}[wl.wdt]
+    ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i4": 0.5}[wl.wdt]
     M, K = wl.M, wl.hidden
     b = 2 * M * K * ea + K * ea                      # x, residual, gamma
     if wl.norm == "layer":
         b += K * ea                                  # beta
     if call == "qkv":
         N = wl.n_qkv
-        b += N * K * ew + M * K * ea + M * N * ea    # weights, h_out, q/k/v
+        b += int(N * K * ew) + M * K * ea + M * N * ea    # weights, h_out, q/k/v
     else:
         N = wl.n_gu
-        b += N * K * ew + M * wl.ffn * ea            # weights, out
+        b += int(N * K * ew) + M * wl.ffn * ea       # weights, out
         if wl.bias_std is not None:
             b += N * ea
     if wl.wdt == "i8":
         b += 4 * N                                   # per-row scales
+    if wl.wdt == "i4":
+        b += 4 * N * (K // 128)                      # per-row, per-128-k group scales
     return b
 
 
@@ -181,9 +183,12 @@ _EPI = {"0": "qkv", "1": "swiglu", "2": "gelu", "3": "linear"}
 def library_kernel_name(cxx: str) -> str:
     """The library profiler's name of a kernel from the demangled C++ name rocprofv3 prints."""
     import re
-    m = re.search(r"fp::stream_kernel<(\d), (true|false), (\d+), (\d+), (\d+), (\d)(?:, (?:true|false))?>", cxx)
+    # the second template argument: the weight storage (false / 0: the
+    # activation dtype, true / 1: int8, 2: int4)
+    m = re.search(r"fp::stream_kernel<(\d), (true|false|\d), (\d+), (\d+), (\d+), (\d)(?:, (?:true|false))?>", cxx)
     if m:
-        act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
+        wq = {"true": "1", "false": "0"}.get(m.group(2), m.group(2))
+        act = {"1": "bf16-i8w", "2": "bf16-i4w"}.get(wq) or _ACT[m.group(1)]
         return (f"stream_kernel<{act},m{16 * int(m.group(3))},n{64 * int(m.group(4))},"
                 f"k{32 * int(m.group(5))},{_EPI[m.group(6)]}>")
     m = re.search(r"fp::prefill_kernel<(\d), (true|false), (\d)(?:, (?:true|false))?>", cxx)

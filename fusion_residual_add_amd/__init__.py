@@ -16,12 +16,24 @@ import torch
 from . import _lib
 from ._lib import FP_ACT, FP_NORM
 
-__all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_dequant_i8_bf16",
+__all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_dequant_i8_bf16", "fused_dequant_i4_bf16",
            "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
            "library_path", "tune_install", "tune_clear", "tune_count"]
 
+# torch.uint8 weights are int4 pairs (two values per byte, even k in the low nibble)
 _DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
-       torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8}
+       torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8, torch.uint8: _lib.FP_I4}
+
+
+def _check_weight(w: torch.Tensor, w_scale: Optional[torch.Tensor], Nw: int, K: int, name: str):
+    """Shapes of the weight and its scales for the weight dtype."""
+    want = (Nw, K // 2) if w.dtype == torch.uint8 else (Nw, K)
+    if tuple(w.shape) != want:
+        raise ValueError(f"{name} has shape {tuple(w.shape)}, expected {want}")
+    if w.dtype == torch.int8 and w_scale is not None and tuple(w_scale.shape) != (Nw,):
+        raise ValueError(f"w_scale has shape {tuple(w_scale.shape)}, expected {(Nw,)}")
+    if w.dtype == torch.uint8 and w_scale is not None and tuple(w_scale.shape) != (Nw, K // 128):
+        raise ValueError(f"w_scale has shape {tuple(w_scale.shape)}, expected {(Nw, K // 128)}")
 
 
 class FusedProjError(RuntimeError):
@@ -116,6 +128,7 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
     odt = out_dtype or act
     wdt = w_qkv.dtype
     Nw = (n_heads + 2 * n_kv_heads) * head_dim
+    _check_weight(w_qkv, w_scale, Nw, K, "w_qkv")
     if q is None:
         q = torch.empty((M, n_heads, head_dim), dtype=odt, device=dev)
     if k is None:
@@ -155,6 +168,7 @@ def fused_gateup_act(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: O
     odt = out_dtype or adt
     wdt = w.dtype
     Nw = 2 * ffn if act == "swiglu" else ffn
+    _check_weight(w, w_scale, Nw, K, "w")
     if out is None:
         out = torch.empty((M, ffn), dtype=odt, device=dev)
     stream = _stream(dev)
@@ -181,6 +195,21 @@ def fused_dequant_i8_bf16(q: torch.Tensor, scale: torch.Tensor,
     st = lib.fused_dequant_i8_bf16(_ptr(q, "q", dev, torch.int8), _ptr(scale, "scale", dev, torch.float32),
                                    _ptr(out, "out", dev, torch.bfloat16), N, K, _stream(dev))
     _check("fused_dequant_i8_bf16", st)
+    return out
+
+
+def fused_dequant_i4_bf16(q: torch.Tensor, scale: torch.Tensor,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int4 weights q [N, K/2] (uint8, two per byte) with scales [N, K/128] -> bf16 [N, K]."""
+    lib = _lib.load()
+    _ptr(q, "q")
+    dev = q.device
+    N, K = q.shape[0], 2 * q.shape[1]
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    st = lib.fused_dequant_i4_bf16(_ptr(q, "q", dev, torch.uint8), _ptr(scale, "scale", dev, torch.float32),
+                                   _ptr(out, "out", dev, torch.bfloat16), N, K, _stream(dev))
+    _check("fused_dequant_i4_bf16", st)
     return out
 
 

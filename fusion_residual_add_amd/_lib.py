@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfusedproj.so")
 
-FP_F32, FP_F16, FP_BF16, FP_I8 = 0, 1, 2, 3
+FP_F32, FP_F16, FP_BF16, FP_I8, FP_I4 = 0, 1, 2, 3, 4
 FP_NORM = {"none": 0, "rms": 1, "layer": 2}
 FP_ACT = {"none": 0, "swiglu": 1, "gelu_tanh": 2}
 STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_ALIAS",
@@ -19,7 +19,7 @@ STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_
 
 # every symbol include/fusedproj.h declares
 EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_gateup_act",
-           "fused_dequant_i8_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
+           "fused_dequant_i8_bf16", "fused_dequant_i4_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
            "fp_profile_start", "fp_profile_stop", "fp_tune_install", "fp_tune_count"]
 
 
@@ -60,6 +60,8 @@ def load(path: str = None):
     lib.fused_gateup_act.restype = ci
     lib.fused_dequant_i8_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.fused_dequant_i8_bf16.restype = ci
+    lib.fused_dequant_i4_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.fused_dequant_i4_bf16.restype = ci
     lib.fp_describe_plan.argtypes = [i64, i64, i64, ci, ci, ci, ctypes.c_char_p, sz]
     lib.fp_describe_plan.restype = ci
     lib.fp_status_str.argtypes = [ci]

@@ -45,6 +45,8 @@ struct Plan {
     int slots = 1;            // partial-sum slots per tile (1: none needed)
     int64_t tile_elems = 0;   // accumulators per tile (split-K partial size)
     size_t stats_off = 0, ctr_off = 0, part_off = 0, total = 0;
+    bool deq = false;         // int4 weights staged as bf16 in the workspace first
+    size_t deq_off = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -121,6 +123,7 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
 Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu) {
     Plan p;
     const Knobs kb = knobs_for(M, K, Nw, act, wdt, swiglu);
+    const bool i4 = wdt == FP_I4;
     const bool stream_elig = act != FP_F32 && M <= 64 && K % 256 == 0;
     const bool prefill_elig = act != FP_F32 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32);
     int fam;
@@ -132,6 +135,11 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         fam = 2;
     else
         fam = 0;
+    // int4 weights: streamed and dequantised in registers by the streaming
+    // kernel; for the other families dequantised into the workspace first and
+    // then run as bf16 weights
+    if (i4 && fam != 1) wdt = FP_BF16;
+    const bool qw = wdt == FP_I8 || wdt == FP_I4;   // weights dequantised in the loader
     int64_t tiles, ksteps, target;
     if (fam == 1) {
         p.family = 1;
@@ -146,12 +154,12 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // MI355X: Llama-3-8B QKV 1.1 us faster per call; with int8 weights, or
         // at 33..64 tokens where the A tile is four times as large, 64-row
         // tiles are slower)
-        p.sc.nr = wdt == FP_I8 && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
-        if (!swiglu && wdt != FP_I8 && p.sc.mf <= 2) p.sc.nr = 1;
+        p.sc.nr = qw && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
+        if (!swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
         // requested rows: only the instantiated forms (64 for 16-bit weights
-        // without the gate/up pairing at up to 32 tokens, 256 for int8)
-        if (kb.rows == 64 && !swiglu && wdt != FP_I8 && p.sc.mf <= 2) p.sc.nr = 1;
-        if (kb.rows == 128 || (kb.rows == 256 && wdt == FP_I8)) p.sc.nr = (int)(kb.rows / 64);
+        // without the gate/up pairing at up to 32 tokens, 256 for int8 / int4)
+        if (kb.rows == 64 && !swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
+        if (kb.rows == 128 || (kb.rows == 256 && qw)) p.sc.nr = (int)(kb.rows / 64);
         p.sc.u = p.sc.mf >= 4 ? 4 : 8;      // K chunk 32 * u: must match the launcher
         const int nb = 64 * p.sc.nr;
         p.tiles_m = 1;
@@ -177,7 +185,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // Llama-2-70B's 8-way shard, 56 tiles, s = 4: 24.6 -> 23.4 us;
         // Llama-2-70B int8 gate/up, 224 tiles of 470 MB, 6 % slower so; an
         // uneven 1/s of K, 32 chunks in 3, 1 us slower)
-        const int64_t wbytes = Nw * K * (wdt == FP_I8 ? 1 : 2);
+        const int64_t wbytes = wdt == FP_I4 ? Nw * K / 2 : Nw * K * (wdt == FP_I8 ? 1 : 2);
         if (wbytes <= (int64_t(256) << 20) && tiles > 0) {
             for (int64_t s = target / tiles < ksteps / minc ? target / tiles : ksteps / minc; s >= 1; --s) {
                 if (tiles * s * 100 < target * 85) break;
@@ -254,6 +262,11 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     if (p.slots > 1) off = align256(off + (size_t)tiles * 4);
     p.part_off = off;
     if (p.slots > 1) off = align256(off + (size_t)tiles * p.slots * p.tile_elems * 4);
+    if (i4 && p.family != 1) {
+        p.deq = true;
+        p.deq_off = off;
+        off = align256(off + (size_t)Nw * (size_t)K * 2);
+    }
     p.total = off;
     return p;
 }
@@ -292,8 +305,8 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 fp_status check_dtypes(fp_dtype act, fp_dtype wdt, fp_dtype odt) {
     if (act != FP_F32 && act != FP_F16 && act != FP_BF16)
         return fail(FP_E_DTYPE, "act_dtype %d not in {F32, F16, BF16}", (int)act);
-    if (!(wdt == act || (wdt == FP_I8 && act == FP_BF16)))
-        return fail(FP_E_DTYPE, "w_dtype %d must equal act_dtype %d, or be I8 with BF16 activations",
+    if (!(wdt == act || ((wdt == FP_I8 || wdt == FP_I4) && act == FP_BF16)))
+        return fail(FP_E_DTYPE, "w_dtype %d must equal act_dtype %d, or be I8 / I4 with BF16 activations",
                     (int)wdt, (int)act);
     if (!(odt == act || odt == FP_F32))
         return fail(FP_E_DTYPE, "out_dtype %d must equal act_dtype or be F32", (int)odt);
@@ -361,7 +374,10 @@ fp_status validate_common(const Common &c, const char *wname) {
     if (!c.x && c.M > 0) return fail(FP_E_NULL, "x is NULL");
     if (!c.w) return fail(FP_E_NULL, "%s is NULL", wname);
     if (c.norm != FP_NORM_NONE && !c.gamma) return fail(FP_E_NULL, "gamma is NULL but norm is not NONE");
-    if (c.wdt == FP_I8 && !c.w_scale) return fail(FP_E_NULL, "w_scale is NULL for int8 weights");
+    if ((c.wdt == FP_I8 || c.wdt == FP_I4) && !c.w_scale)
+        return fail(FP_E_NULL, "w_scale is NULL for int8 / int4 weights");
+    if (c.wdt == FP_I4 && c.K % 128 != 0)
+        return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 weights", (long long)c.K);
     if (!(c.eps >= 0.0f) || c.eps > 1e30f) return fail(FP_E_ARG, "eps must be a finite value >= 0");
     const void *ptrs[] = {c.x, c.residual, c.h_out, c.gamma, c.beta, c.w, c.w_scale, c.bias, c.ws};
     const char *names[] = {"x", "residual", "h_out", "gamma", "beta", wname, "w_scale", "bias", "workspace"};
@@ -376,8 +392,9 @@ void add_inputs(const Common &c, std::vector<Range> &ins, const char *wname) {
     if (c.residual) ins.push_back(rng("residual", c.residual, c.M * c.K * ea));
     if (c.gamma && c.norm != FP_NORM_NONE) ins.push_back(rng("gamma", c.gamma, c.K * ea));
     if (c.beta && c.norm == FP_NORM_LAYER) ins.push_back(rng("beta", c.beta, c.K * ea));
-    ins.push_back(rng(wname, c.w, c.Nw * c.K * ew));
+    ins.push_back(rng(wname, c.w, c.wdt == FP_I4 ? c.Nw * c.K / 2 : c.Nw * c.K * ew));
     if (c.w_scale && c.wdt == FP_I8) ins.push_back(rng("w_scale", c.w_scale, c.Nw * 4));
+    if (c.w_scale && c.wdt == FP_I4) ins.push_back(rng("w_scale", c.w_scale, c.Nw * (c.K / 128) * 4));
     if (c.bias) ins.push_back(rng("bias", c.bias, c.Nw * ea));
 }
 
@@ -413,6 +430,16 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.norm = (int)c.norm;
     pa.w = c.w;
     pa.w_scale = c.w_scale;
+    const bool wi8 = c.wdt == FP_I8;
+    const int wq = c.wdt == FP_I8 ? 1 : (c.wdt == FP_I4 && !plan.deq) ? 2 : 0;
+    if (plan.deq) {
+        void *wb = ws + plan.deq_off;
+        ProfScope ps(fp::dequant_i4_kernel_name(), c.stream);
+        hipError_t e = fp::launch_dequant_i4((const uint8_t *)c.w, c.w_scale, wb, c.Nw, c.K, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "dequant_i4_kernel launch");
+        pa.w = wb;
+        pa.w_scale = nullptr;
+    }
     pa.bias = c.bias;
     pa.out_f32 = c.odt == FP_F32;
     pa.M = c.M;
@@ -424,10 +451,9 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.slots = plan.slots;
     pa.partials = plan.slots > 1 ? (float *)(ws + plan.part_off) : nullptr;
     pa.counters = ctr;
-    const bool wi8 = c.wdt == FP_I8;
     if (plan.family == 1) {
-        ProfScope ps(fp::stream_kernel_name(act, wi8, plan.sc, pa.epi), c.stream);
-        hipError_t e = fp::launch_stream(act, wi8, plan.sc, pa, plan.grid, c.stream);
+        ProfScope ps(fp::stream_kernel_name(act, wq, plan.sc, pa.epi), c.stream);
+        hipError_t e = fp::launch_stream(act, wq, plan.sc, pa, plan.grid, c.stream);
         if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
     } else if (plan.family == 2) {
         ProfScope ps(fp::prefill_kernel_name(act, wi8, pa.epi), c.stream);
@@ -460,6 +486,7 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype ac
                           fp_dtype w_dtype) {
     if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0) return 0;
     if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
+    if (w_dtype == FP_I4 && hidden % 128 != 0) return 0;
     if (M == 0) return 0;
     const size_t a = make_plan(M, hidden, n_cols, act_dtype, w_dtype, false).total;
     const size_t b = make_plan(M, hidden, n_cols, act_dtype, w_dtype, true).total;
@@ -566,6 +593,25 @@ fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_b
     return FP_OK;
 }
 
+fp_status fused_dequant_i4_bf16(const void *q, const float *scale, void *out_bf16, int64_t N,
+                                int64_t K, void *hip_stream) {
+    if (N < 0) return fail(FP_E_SHAPE, "N = %lld is negative", (long long)N);
+    if (K <= 0 || K % 128 != 0) return fail(FP_E_SHAPE, "K = %lld must be a positive multiple of 128", (long long)K);
+    if (!q || !scale || !out_bf16) return fail(FP_E_NULL, "q, scale and out_bf16 must be non-NULL");
+    if (!aligned16(q) || !aligned16(scale) || !aligned16(out_bf16))
+        return fail(FP_E_ALIGN, "q, scale and out_bf16 must be 16-byte aligned");
+    std::vector<Range> ins{rng("q", q, N * K / 2), rng("scale", scale, N * (K / 128) * 4)};
+    std::vector<Range> outs{rng("out_bf16", out_bf16, N * K * 2)};
+    fp_status st = check_alias(ins, outs);
+    if (st != FP_OK) return st;
+    if (N == 0) return FP_OK;
+    hipStream_t s = (hipStream_t)hip_stream;
+    ProfScope ps(fp::dequant_i4_kernel_name(), s);
+    hipError_t e = fp::launch_dequant_i4((const uint8_t *)q, scale, out_bf16, N, K, s);
+    if (e != hipSuccess) return hip_fail(e, "dequant_i4_kernel launch");
+    return FP_OK;
+}
+
 fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
                            fp_dtype w_dtype, fp_act act, char *buf, size_t cap) {
     if (!buf || cap == 0) return fail(FP_E_NULL, "buf must be non-NULL with cap > 0");
@@ -575,17 +621,21 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     if ((int)act < 0 || (int)act > 2) return fail(FP_E_ARG, "act = %d", (int)act);
     const fp_status st = check_dtypes(act_dtype, w_dtype, act_dtype);
     if (st != FP_OK) return st;
+    if (w_dtype == FP_I4 && hidden % 128 != 0)
+        return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 weights", (long long)hidden);
     const Plan p = make_plan(M, hidden, n_cols, act_dtype, w_dtype, act == FP_ACT_SWIGLU);
     const int a = act_code(act_dtype);
     const bool wi8 = w_dtype == FP_I8;
+    const int wq = wi8 ? 1 : (w_dtype == FP_I4 && !p.deq) ? 2 : 0;
     const int epi = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
     const char *fam = p.family == 1 ? "stream" : p.family == 2 ? "prefill" : "tiled";
-    const char *name = p.family == 1 ? fp::stream_kernel_name(a, wi8, p.sc, epi)
+    const char *name = p.family == 1 ? fp::stream_kernel_name(a, wq, p.sc, epi)
                      : p.family == 2 ? fp::prefill_kernel_name(a, wi8, epi)
                                      : fp::proj_kernel_name(a, wi8, p.tile, epi);
     const int64_t grid = p.family == 1 ? p.grid : (int64_t)p.tiles_m * p.tiles_n * p.splits;
-    snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu", fam, name,
-             (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total);
+    snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s", fam, name,
+             (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total,
+             p.deq ? " prep=dequant_i4_kernel" : "");
     return FP_OK;
 }
 

@@ -75,17 +75,20 @@ hipError_t launch_tiled(int act, bool w_i8, int tile, const ProjArgs &a, hipStre
 //  tiles_m must be 1.
 struct StreamCfg { int mf, nr, u; };
 // grid_wgs workgroups share the (weight tile, K chunk) units evenly
-hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s);
+hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s);
 hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,
                           hipStream_t s);
 
 // names used by the event profiler
 const char *stats_kernel_name(int act);
 const char *proj_kernel_name(int act, bool w_i8, int tile, int epi);
-const char *stream_kernel_name(int act, bool w_i8, const StreamCfg &c, int epi);
+const char *stream_kernel_name(int act, int wq, const StreamCfg &c, int epi);
 // 128 x 512 family (fp_prefill*.hip): 16-bit activations, more than 64 tokens
 hipError_t launch_prefill(int act, bool w_i8, const ProjArgs &a, hipStream_t s);
 const char *prefill_kernel_name(int act, bool w_i8, int epi);
 const char *dequant_kernel_name();
+hipError_t launch_dequant_i4(const uint8_t *q, const float *scale, void *out, int64_t N, int64_t K,
+                             hipStream_t s);
+const char *dequant_i4_kernel_name();
 
 }  // namespace fp

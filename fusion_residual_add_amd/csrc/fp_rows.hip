@@ -1,5 +1,6 @@
 // Row kernels of libfusedproj: the per-token prologue statistics and the
-// stand-alone int8 dequantisation.
+// stand-alone int8 / int4 weight dequantisation (int4 also stages the weight
+// of calls that the weight-streaming kernel does not take).
 //
 // stats_kernel: h = x + residual in fp32 (exact for 16-bit inputs), the
 // residual-stream write h_out = rne(h), and the norm statistics of the token
@@ -106,11 +107,30 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t *q, const flo
     }
 }
 
+// int4 weights, 32 values (one 16-byte load) per thread: out[j, k] =
+// bf16_rne(f32_rne(q[j, k] * scale[j, k / 128])), q packed two per byte.
+__global__ __launch_bounds__(256) void dequant_i4_kernel(const uint8_t *q, const float *scale,
+                                                         unsigned short *out, int64_t N, int64_t K) {
+    const int64_t per_row = K / 32;
+    const int64_t nv = N * per_row;
+    const int64_t groups = K / 128;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (int64_t)gridDim.x * 256) {
+        const int64_t row = i / per_row, k0 = (i % per_row) * 32;
+        const u32x4 qv = *(const u32x4 *)(q + i * 16);
+        u32x4 o[4];
+        dequant32_i4(qv, scale[row * groups + k0 / 128], o);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) *(u32x4 *)(out + i * 32 + 8 * w) = o[w];
+    }
+}
+
 static const char *kStatsNames[3] = {"stats_kernel<f32>", "stats_kernel<f16>", "stats_kernel<bf16>"};
 
 const char *stats_kernel_name(int act) { return kStatsNames[act]; }
 
 const char *dequant_kernel_name() { return "dequant_kernel"; }
+
+const char *dequant_i4_kernel_name() { return "dequant_i4_kernel"; }
 
 template <int ACT>
 static void launch_stats_t(const StatsArgs &a, hipStream_t s) {
@@ -135,6 +155,17 @@ hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s) {
     case ACT_F16: launch_stats_t<ACT_F16>(a, s); break;
     default:      launch_stats_t<ACT_BF16>(a, s); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_i4(const uint8_t *q, const float *scale, void *out, int64_t N, int64_t K,
+                             hipStream_t s) {
+    const int64_t nv = N * (K / 32);
+    if (nv == 0) return hipSuccess;
+    int64_t blocks = (nv + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(dequant_i4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, scale,
+                       (unsigned short *)out, N, K);
     return hipGetLastError();
 }
 

@@ -10,14 +10,17 @@ namespace fp {
 void launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 void launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 void launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+void launch_stream_i4(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 
-hipError_t launch_stream(int act, bool w_i8, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s) {
+// wq: 0 weights in the activation dtype, 1 int8, 2 int4
+hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s) {
     if (grid_wgs <= 0 || a.tiles_n <= 0) return hipSuccess;
     if (a.epi == EPI_SWIGLU && c.nr % 2 != 0) return hipErrorInvalidValue;
     // the instantiated row counts (see launch_stream_mf)
-    if (c.nr != 2 && !(c.nr == 1 && !w_i8 && c.mf <= 2) && !(c.nr == 4 && w_i8)) return hipErrorInvalidValue;
+    if (c.nr != 2 && !(c.nr == 1 && wq == 0 && c.mf <= 2) && !(c.nr == 4 && wq != 0)) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)grid_wgs;
-    if (w_i8) launch_stream_i8(c, a, grid, s);
+    if (wq == 1) launch_stream_i8(c, a, grid, s);
+    else if (wq == 2) launch_stream_i4(c, a, grid, s);
     else if (act == ACT_F16) launch_stream_f16(c, a, grid, s);
     else launch_stream_bf16(c, a, grid, s);
     return hipGetLastError();
@@ -45,11 +48,11 @@ const char *prefill_kernel_name(int act, bool w_i8, int epi) {
     return buf;
 }
 
-const char *stream_kernel_name(int act, bool w_i8, const StreamCfg &c, int epi) {
-    static const char *acts[4] = {"f32", "f16", "bf16", "bf16-i8w"};
+const char *stream_kernel_name(int act, int wq, const StreamCfg &c, int epi) {
+    static const char *acts[5] = {"f32", "f16", "bf16", "bf16-i8w", "bf16-i4w"};
     static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
     thread_local char buf[64];
-    snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", acts[w_i8 ? 3 : act], 16 * c.mf,
+    snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", acts[wq ? 2 + wq : act], 16 * c.mf,
              64 * c.nr, 32 * c.u, epis[epi]);
     return buf;
 }

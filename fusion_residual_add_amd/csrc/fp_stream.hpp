@@ -14,7 +14,9 @@
 //    (lane l: row l % 16, eight consecutive k at group l / 16), a whole chunk
 //    per wave in flight (NR * U 16-byte loads per lane), reloaded slice by
 //    slice as the MFMAs consume them.  int8 weights are dequantised in
-//    registers; one 16-byte load then feeds two MFMAs.
+//    registers; one 16-byte load then feeds two MFMAs.  int4 weights likewise,
+//    one 16-byte load (32 values of one 128-wide scale group) feeding four
+//    MFMAs, the group scales loaded with the chunk.
 //  * The activation side of each chunk -- x and the residual for all M token
 //    rows -- is read (an L2 hit: every workgroup reads it), re-formed as
 //    h = x + r, normalised with the row statistics and gamma / beta, rounded to
@@ -31,19 +33,23 @@
 
 namespace fp {
 
-template <int ACT, bool WI8, int MF, int NR, int U, int EPI>
+// WQ: weight storage -- 0 the activation dtype, 1 int8 (one scale per row),
+// 2 int4 (one scale per row and group of 128 k, two values per byte).
+template <int ACT, int WQ, int MF, int NR, int U, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(ProjArgs p) {
     using T = Act<ACT>;
+    constexpr bool WI8 = WQ == 1, WI4 = WQ == 2;
     static_assert(ACT != ACT_F32, "the stream kernel takes 16-bit activations");
-    static_assert(!WI8 || ACT == ACT_BF16, "int8 weights feed bf16 MFMA");
+    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 weights feed bf16 MFMA");
     static_assert(EPI != EPI_SWIGLU || NR % 2 == 0, "gate/up fragments come in pairs");
     static_assert(!WI8 || U % 2 == 0, "one int8 load covers two k slices");
+    static_assert(!WI4 || U % 4 == 0, "one int4 load covers four k slices (one scale group)");
     constexpr int BMP = 16 * MF;                 // padded token rows
     constexpr int NB = 64 * NR;                  // weight rows per workgroup
     constexpr int CK = 32 * U;                   // k per chunk
     constexpr int LDA = CK + 8;                  // LDS row stride (elements), +16 B pad
-    constexpr int NL = WI8 ? U / 2 : U;          // weight loads per fragment per chunk
+    constexpr int NL = WI8 ? U / 2 : WI4 ? U / 4 : U;   // weight loads per fragment per chunk
     constexpr int KVR = CK / 8;                  // 16-byte activation vectors per row per chunk
     constexpr int AV = (BMP * KVR + 255) / 256;  // activation vectors per thread per chunk
     constexpr int AR = 256 / KVR;                // row step between a thread's vectors
@@ -67,6 +73,7 @@ void stream_kernel(ProjArgs p) {
         // count outstanding loads exactly instead of draining them.
         const char *wrow[NR];
         float wsc[NR];
+        const float *wsr[NR];   // int4: the row's group scales
     #pragma unroll
         for (int n = 0; n < NR; ++n) {
             int64_t r;
@@ -79,13 +86,17 @@ void stream_kernel(ProjArgs p) {
                 r = (int64_t)tn * NB + wave * (NR * 16) + n * 16 + (lane & 15);
                 r = r < p.Nw ? r : p.Nw - 1;
             }
-            wrow[n] = (const char *)p.w + r * p.K * (WI8 ? 1 : 2);
+            wrow[n] = (const char *)p.w + (WI4 ? r * (p.K / 2) : r * p.K * (WI8 ? 1 : 2));
             wsc[n] = 0.f;
+            wsr[n] = nullptr;
             if constexpr (WI8) wsc[n] = p.w_scale[r];
+            if constexpr (WI4) wsr[n] = p.w_scale + r * (p.K / 128);
         }
         auto wload = [&](int c, int n, int u) -> u32x4 {
             if constexpr (WI8)
                 return *(const u32x4 *)(wrow[n] + (int64_t)c * CK + u * 64 + (lane >> 4) * 16);
+            else if constexpr (WI4)   // 128 k (one scale group) per u; lane group g: k 32 g .. 32 g + 31
+                return *(const u32x4 *)(wrow[n] + (int64_t)c * (CK / 2) + u * 64 + (lane >> 4) * 16);
             else
                 return *(const u32x4 *)(wrow[n] + ((int64_t)c * CK + u * 32 + (lane >> 4) * 8) * 2);
         };
@@ -168,15 +179,28 @@ void stream_kernel(ProjArgs p) {
     #pragma unroll
             for (int n = 0; n < NR; ++n) acc[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-        // weight registers of one chunk
+        // weight registers of one chunk (int4: with the group scales of the chunk)
         struct WRegs {
             u32x4 w[NR][NL];
+            float s[NR][WI4 ? NL : 1];
         };
         auto wload_all = [&](int c, WRegs &W) {
     #pragma unroll
             for (int u = 0; u < NL; ++u)
     #pragma unroll
                 for (int n = 0; n < NR; ++n) W.w[n][u] = wload(c, n, u);
+            if constexpr (WI4) {
+    #pragma unroll
+                for (int n = 0; n < NR; ++n) {
+                    if constexpr (NL == 2) {   // groups 2c, 2c + 1: adjacent, 8-byte aligned
+                        const float2 sv = *(const float2 *)(wsr[n] + 2 * c);
+                        W.s[n][0] = sv.x;
+                        W.s[n][1] = sv.y;
+                    } else {
+                        W.s[n][0] = wsr[n][c];
+                    }
+                }
+            }
         };
         // MFMAs of chunk c on the weights in W; when PF, W is then refilled with
         // chunk c + 2 as one burst of loads (a burst keeps each row's 512 contiguous
@@ -186,7 +210,22 @@ void stream_kernel(ProjArgs p) {
             const unsigned short *la = lds_a[buf];
     #pragma unroll
             for (int u = 0; u < NL; ++u) {
-                if constexpr (WI8) {
+                if constexpr (WI4) {
+                    u32x4 b[NR][4];
+    #pragma unroll
+                    for (int n = 0; n < NR; ++n) dequant32_i4(W.w[n][u], W.s[n][u], b[n]);
+                    // a lane's 32 int4 are k = 128u + 32 (lane / 16) + [0, 32): four MFMA k slices
+    #pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const int koff = u * 128 + (lane >> 4) * 32 + qq * 8;
+    #pragma unroll
+                        for (int m = 0; m < MF; ++m) {
+                            const u32x4 a = *(const u32x4 *)&la[(m * 16 + (lane & 15)) * LDA + koff];
+    #pragma unroll
+                            for (int n = 0; n < NR; ++n) acc[m][n] = T::mfma(a, b[n][qq], acc[m][n]);
+                        }
+                    }
+                } else if constexpr (WI8) {
                     u32x4 lo[NR], hi[NR];
     #pragma unroll
                     for (int n = 0; n < NR; ++n) dequant16(W.w[n][u], wsc[n], lo[n], hi[n]);
@@ -349,21 +388,21 @@ void stream_kernel(ProjArgs p) {
 // ---------------------------------------------------------------------------
 // launch helpers (instantiated per activation / weight dtype in fp_stream_*.hip)
 // ---------------------------------------------------------------------------
-template <int ACT, bool WI8, int MF, int NR, int U>
+template <int ACT, int WQ, int MF, int NR, int U>
 inline void launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (epi) {
     case EPI_QKV:
-        hipLaunchKernelGGL((stream_kernel<ACT, WI8, MF, NR, U, EPI_QKV>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_QKV>), dim3(grid), dim3(256), 0, s, a);
         break;
     case EPI_SWIGLU:
         if constexpr (NR % 2 == 0)
-            hipLaunchKernelGGL((stream_kernel<ACT, WI8, MF, NR, U, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a);
         break;
     case EPI_GELU:
-        hipLaunchKernelGGL((stream_kernel<ACT, WI8, MF, NR, U, EPI_GELU>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_GELU>), dim3(grid), dim3(256), 0, s, a);
         break;
     default:
-        hipLaunchKernelGGL((stream_kernel<ACT, WI8, MF, NR, U, EPI_LINEAR>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_LINEAR>), dim3(grid), dim3(256), 0, s, a);
         break;
     }
 }
@@ -371,26 +410,26 @@ inline void launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStre
 // 64 token rows: 128-wide K chunks (two activation / weight register sets of
 // 256-wide chunks do not fit in the register file next to the accumulators)
 // Weight rows per workgroup: 64 (NR = 1) only for 16-bit weights at up to 32
-// tokens, 256 (NR = 4) only for int8 weights; only those combinations are
-// instantiated.
-template <int ACT, bool WI8, int MF>
+// tokens, 256 (NR = 4) only for int8 / int4 weights; only those combinations
+// are instantiated.
+template <int ACT, int WQ, int MF>
 inline void launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
     constexpr int U = MF >= 4 ? 4 : 8;
     if (c.nr == 2) {
-        launch_stream_cfg<ACT, WI8, MF, 2, U>(a.epi, a, grid, s);
+        launch_stream_cfg<ACT, WQ, MF, 2, U>(a.epi, a, grid, s);
     } else if (c.nr == 1) {
-        if constexpr (!WI8 && MF <= 2) launch_stream_cfg<ACT, WI8, MF, 1, U>(a.epi, a, grid, s);
+        if constexpr (WQ == 0 && MF <= 2) launch_stream_cfg<ACT, WQ, MF, 1, U>(a.epi, a, grid, s);
     } else {
-        if constexpr (WI8) launch_stream_cfg<ACT, WI8, MF, 4, U>(a.epi, a, grid, s);   // 256 rows share one A tile
+        if constexpr (WQ != 0) launch_stream_cfg<ACT, WQ, MF, 4, U>(a.epi, a, grid, s);   // 256 rows share one A tile
     }
 }
 
-template <int ACT, bool WI8>
+template <int ACT, int WQ>
 inline void launch_stream_t(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (c.mf) {
-    case 1: launch_stream_mf<ACT, WI8, 1>(c, a, grid, s); break;
-    case 2: launch_stream_mf<ACT, WI8, 2>(c, a, grid, s); break;
-    default: launch_stream_mf<ACT, WI8, 4>(c, a, grid, s); break;
+    case 1: launch_stream_mf<ACT, WQ, 1>(c, a, grid, s); break;
+    case 2: launch_stream_mf<ACT, WQ, 2>(c, a, grid, s); break;
+    default: launch_stream_mf<ACT, WQ, 4>(c, a, grid, s); break;
     }
 }
 

@@ -4,7 +4,7 @@
 namespace fp {
 
 void launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_stream_t<ACT_BF16, false>(c, a, grid, s);
+    launch_stream_t<ACT_BF16, 0>(c, a, grid, s);
 }
 
 }  // namespace fp

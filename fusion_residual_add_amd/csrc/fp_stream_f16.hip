@@ -4,7 +4,7 @@
 namespace fp {
 
 void launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_stream_t<ACT_F16, false>(c, a, grid, s);
+    launch_stream_t<ACT_F16, 0>(c, a, grid, s);
 }
 
 }  // namespace fp

@@ -4,7 +4,7 @@
 namespace fp {
 
 void launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_stream_t<ACT_BF16, true>(c, a, grid, s);
+    launch_stream_t<ACT_BF16, 1>(c, a, grid, s);
 }
 
 }  // namespace fp

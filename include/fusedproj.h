@@ -40,9 +40,21 @@
  *  - Int8 weights (w_dtype FP_I8, act_dtype FP_BF16 only): each element is
  *    dequantised as bf16_rne(f32_rne(q * w_scale[row])), bit-exactly the
  *    result of fused_dequant_i8_bf16.
- *  - Dtypes: act_dtype in {F32, F16, BF16}; w_dtype == act_dtype, or FP_I8
- *    with act_dtype FP_BF16; out_dtype == act_dtype or FP_F32.  gamma, beta
- *    and bias are act_dtype; w_scale is fp32.
+ *  - Int4 weights (w_dtype FP_I4, act_dtype FP_BF16 only; the 4-bit
+ *    weight-only configuration of "TensorRT-LLM 深度工程实践…" §3.3: group
+ *    size 128, no zero point): the [N, hidden] weight is stored as
+ *    [N, hidden/2] bytes, element k of a row in the low nibble of byte k/2
+ *    for even k and in the high nibble for odd k, each nibble a
+ *    two's-complement integer in [-8, 7]; w_scale is [N, hidden/128] fp32,
+ *    one scale per row and group of 128 consecutive k; each element is
+ *    dequantised as bf16_rne(f32_rne(q * w_scale[row][k / 128])), a zero
+ *    result being +0, bit-exactly the result of fused_dequant_i4_bf16.  hidden must be a
+ *    multiple of 128.  Calls that the weight-streaming kernel does not take
+ *    (see fp_describe_plan) first dequantise the weight into the workspace
+ *    (N * hidden * 2 bytes of it).
+ *  - Dtypes: act_dtype in {F32, F16, BF16}; w_dtype == act_dtype, or FP_I8 /
+ *    FP_I4 with act_dtype FP_BF16; out_dtype == act_dtype or FP_F32.  gamma,
+ *    beta and bias are act_dtype; w_scale is fp32.
  *  - Every pointer must be 16-byte aligned.  No output range may overlap an
  *    input range, another output, or the workspace.
  *  - Execution is asynchronous on hip_stream (NULL = the default stream);
@@ -66,7 +78,7 @@
 extern "C" {
 #endif
 
-typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3 } fp_dtype;
+typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4 } fp_dtype;
 typedef enum { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
 typedef enum { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
 typedef enum {
@@ -94,7 +106,8 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols,
  *  h_out       : [M, hidden] act_dtype or NULL
  *  gamma, beta : [hidden] act_dtype (gamma required unless FP_NORM_NONE)
  *  w_qkv       : [(H + 2 Hkv) * D, hidden], rows = Q heads, then K, then V
- *  w_scale     : [(H + 2 Hkv) * D] fp32, required iff w_dtype == FP_I8
+ *  w_scale     : fp32, required iff w_dtype is FP_I8 ([(H + 2 Hkv) * D]) or
+ *                FP_I4 ([(H + 2 Hkv) * D, hidden / 128])
  *  bias        : [(H + 2 Hkv) * D] act_dtype or NULL
  *  q           : [M, H, D]   out_dtype, token-major
  *  k, v        : [M, Hkv, D] out_dtype, token-major
@@ -136,6 +149,15 @@ fp_status fused_gateup_act(
  *  q : [N, K] int8, scale : [N] fp32, out_bf16 : [N, K] bf16.
  *  Requires K a positive multiple of 16, N >= 0. */
 fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_bf16,
+                                int64_t N, int64_t K, void *hip_stream);
+
+/* int4 group-wise weight dequantisation to bf16, the same device function
+ * the projections use for int4 weights:
+ * out[j, k] = bf16_rne(f32_rne(q[j, k] * scale[j, k / 128])), zero as +0.
+ *  q : [N, K/2] bytes (two values per byte, even k in the low nibble),
+ *  scale : [N, K/128] fp32, out_bf16 : [N, K] bf16.
+ *  Requires K a positive multiple of 128, N >= 0. */
+fp_status fused_dequant_i4_bf16(const void *q, const float *scale, void *out_bf16,
                                 int64_t N, int64_t K, void *hip_stream);
 
 /* Which kernel a call with these sizes would launch, and how: writes a

@@ -50,7 +50,9 @@
  *     low nibble of byte k/2 for even k and in the high nibble for odd k,
  *     each nibble a two's-complement integer in [-8, 7]; the scales are
  *     [N, K/128] fp32; w = RNE_bf16(RNE_f32(q * s[row][k/128])), the two
- *     roundings of R8.
+ *     roundings of R8.  A zero product is +0: the value is exactly zero (the
+ *     format defines no signed zero; only a zero scale with a negative q
+ *     could give an IEEE -0).
  *  [Q] "TensorRT-LLM 深度工程实践…", §3.3 FP4/FP8 动态量化加速: the W4A16
  *      (AWQ/GPTQ) configuration with group size 128 and no zero point.
  */
@@ -195,6 +197,7 @@ int or_dequant_i4(const uint8_t *q, const float *s, int64_t N, int64_t K,
         for (int64_t k = 0; k < K; ++k) {
             double prod = (double)or_i4_value(row, k) * (double)s[j * G + k / OR_I4_GROUP];
             double w = or_round(or_round(prod, OR_F32), OR_BF16);
+            if (w == 0.0) w = 0.0;   /* +0 (R9) */
             if (w_out) w_out[j * K + k] = w;
             if (bits_out) bits_out[j * K + k] = bf16_bits_of(w);
         }

@@ -378,10 +378,11 @@ def pin_dequant_i4_exhaustive():
     w, bits = oracle.dequant_i4(torch.from_numpy(_pack_i4(q)), torch.from_numpy(s))
     s_k = s[:, k // 128]
     prod32 = q.astype(np.float32) * s_k
+    prod32[prod32 == 0] = 0.0                           # a zero product is +0 (reading R9)
     ref = torch.from_numpy(prod32).to(torch.bfloat16)
     assert np.array_equal(bits, ref.view(torch.int16).numpy().view(np.uint16))
     assert np.array_equal(w, ref.double().numpy())
-    assert np.all(w[N - 3, :128] == 0)                 # s = 0 gives zero
+    assert np.all(bits[N - 3, :128] == 0)              # s = 0 gives +0, also for negative q
     assert np.array_equal(w[N - 3, 128:], q[N - 3, 128:].astype(np.float64))   # s = 1: the integers
 
 

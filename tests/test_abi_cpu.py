@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fusedproj.h")
 
 FAKE = 0x10000           # 16-byte aligned, never dereferenced
-F32, F16, BF16, I8 = 0, 1, 2, 3
+F32, F16, BF16, I8, I4 = 0, 1, 2, 3, 4
 
 
 def lib():
@@ -94,6 +94,9 @@ def test_m_zero_is_a_noop():
     (dict(gamma=None), "FP_E_NULL"),
     (dict(M=1, q=None), "FP_E_NULL"),
     (dict(wdt=I8), "FP_E_NULL"),                       # int8 without scales
+    (dict(wdt=I4), "FP_E_NULL"),                       # int4 without scales
+    (dict(wdt=I4, hidden=320, w_scale=FAKE + 0x70000000), "FP_E_SHAPE"),   # int4: hidden % 128
+    (dict(act=F16, wdt=I4, w_scale=FAKE + 0x70000000), "FP_E_DTYPE"),
     (dict(M=-1), "FP_E_SHAPE"),
     (dict(hidden=4000), "FP_E_SHAPE"),
     (dict(hidden=0), "FP_E_SHAPE"),
@@ -141,6 +144,35 @@ def test_dequant_rejects():
     assert _lib.STATUS[L.fused_dequant_i8_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 60, None)] == "FP_E_SHAPE"
     assert _lib.STATUS[L.fused_dequant_i8_bf16(None, FAKE + 0x1000000, FAKE + 0x2000000, 4, 64, None)] == "FP_E_NULL"
     assert _lib.STATUS[L.fused_dequant_i8_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x80, 4, 64, None)] == "FP_E_ALIAS"
+
+
+def test_dequant_i4_rejects():
+    L = lib()
+    f = L.fused_dequant_i4_bf16
+    assert _lib.STATUS[f(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 0, 128, None)] == "FP_OK"
+    assert _lib.STATUS[f(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 192, None)] == "FP_E_SHAPE"
+    assert _lib.STATUS[f(FAKE, None, FAKE + 0x2000000, 4, 128, None)] == "FP_E_NULL"
+    assert _lib.STATUS[f(FAKE, FAKE + 0x1000000, FAKE + 0x8, 4, 128, None)] == "FP_E_ALIGN"
+    # the [4, 128] bf16 output (1 KB) over the packed weight ([4, 64] bytes)
+    assert _lib.STATUS[f(FAKE, FAKE + 0x1000000, FAKE - 0x100, 4, 128, None)] == "FP_E_ALIAS"
+
+
+def test_int4_plans():
+    for var in _ENV:
+        os.environ.pop(var, None)
+    u8 = torch.uint8
+    # decode token counts, hidden a multiple of 256: streamed, dequantised in registers
+    p = _plan(16, 8192, 57344, w=u8, fn="swiglu")
+    assert p["kernel"] == "stream_kernel<bf16-i4w,m16,n128,k256,swiglu>" and "prep" not in p
+    assert _plan(64, 8192, 57344, w=u8, fn="swiglu")["kernel"] == "stream_kernel<bf16-i4w,m64,n256,k128,swiglu>"
+    # every other call: dequantised into the workspace, then the bf16 kernels
+    p = _plan(256, 8192, 57344, w=u8, fn="swiglu")
+    assert p["family"] == "prefill" and p["kernel"] == "prefill_kernel<bf16,128x512,swiglu>"
+    assert p["prep"] == "dequant_i4_kernel" and p["workspace"] >= 57344 * 8192 * 2
+    p = _plan(8, 384, 512, w=u8)
+    assert p["family"] == "tiled" and p["prep"] == "dequant_i4_kernel"
+    assert fra.workspace_bytes(8, 384, 512, torch.bfloat16, u8) >= 512 * 384 * 2
+    assert fra.workspace_bytes(16, 8192, 57344, torch.bfloat16, u8) < 57344 * 8192
 
 
 def test_binding_refuses_cpu_tensors():

@@ -47,6 +47,7 @@ MUTANTS = {
     "int4 not sign-extended": ("return nib >= 8 ? nib - 16 : nib;", "return nib;"),
     "int4 one scale per row": ("s[j * G + k / OR_I4_GROUP]", "s[j * G]"),
     "int4 group of 64": ("enum { OR_I4_GROUP = 128 };", "enum { OR_I4_GROUP = 64 };"),
+    "int4 signed zero kept": ("if (w == 0.0) w = 0.0;   /* +0 (R9) */", "(void)0;"),
 }
 
 
