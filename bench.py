@@ -49,6 +49,14 @@ def algo_bytes(wl, call: str) -> int:
     counted (the fusion keeps them on chip)."""
     ea = {"f32": 4, "f16": 2, "bf16": 2}[wl.act]
     ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i4": 0.5}[wl.wdt]
+    if call == "down":                               # a [M, ffn], residual and out [M, hidden], weights
+        N, K = wl.hidden, wl.ffn
+        b = wl.M * K * ea + 2 * wl.M * N * ea + int(N * K * ew)
+        if wl.wdt == "i8":
+            b += 4 * N
+        if wl.wdt == "i4":
+            b += 4 * N * (K // 128)
+        return b
     M, K = wl.M, wl.hidden
     b = 2 * M * K * ea + K * ea                      # x, residual, gamma
     if wl.norm == "layer":
@@ -69,6 +77,8 @@ def algo_bytes(wl, call: str) -> int:
 
 
 def flops(wl, call: str) -> int:
+    if call == "down":
+        return 2 * wl.M * wl.ffn * wl.hidden
     N = wl.n_qkv if call == "qkv" else wl.n_gu
     return 2 * wl.M * wl.hidden * N
 
@@ -76,12 +86,12 @@ def flops(wl, call: str) -> int:
 class Runner:
     """Device copies of a workload with R rotating weight sets."""
 
-    def __init__(self, wl, seed=0, min_sets=1):
+    def __init__(self, wl, seed=0, min_sets=1, down=False):
         import torch
         from fusion_residual_add_amd import inputs
         self.wl = wl
         dev = torch.device("cuda:0")
-        host = inputs.generate(wl, seed=seed)
+        host = inputs.generate(wl, seed=seed, parts=("qkv", "gu", "down") if down else ("qkv", "gu"))
         self.base = {k: v.to(dev) for k, v in host.items()}
         wbytes = sum(t.numel() * t.element_size() for k, t in self.base.items() if k.startswith("w_"))
         self.R = max(min_sets, (2 * MALL_BYTES) // max(wbytes, 1) + 1)
@@ -100,6 +110,8 @@ class Runner:
         self.v = torch.empty_like(self.k)
         self.h = torch.empty_like(self.base["x"])
         self.out = torch.empty((M, wl.ffn), dtype=self.base["x"].dtype, device=dev)
+        # the residual stream the down projection updates in place
+        self.h_down = self.base["r"].clone() if down else None
         self.ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
         need = 0
         act_t = self.base["x"].dtype
@@ -107,6 +119,8 @@ class Runner:
             if N:
                 w = self.base["w_qkv" if call == "qkv" else "w_gu"]
                 need = max(need, fra.workspace_bytes(M, wl.hidden, N, act_t, w.dtype))
+        if down:
+            need = max(need, fra.workspace_bytes(M, wl.ffn, wl.hidden, act_t, self.base["w_down"].dtype))
         if need > self.ws.numel():
             self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
@@ -122,6 +136,11 @@ class Runner:
         self.fra.fused_gateup_act(s["x"], s["r"], s["gamma"], s["w_gu"], wl.ffn, wl.act_fn,
                                   beta=s.get("beta"), norm=wl.norm, eps=wl.eps, w_scale=s.get("s_gu"),
                                   bias=s.get("b_gu"), out=self.out, workspace=self.ws)
+
+    def down(self, i):
+        s = self.sets[i % self.R]
+        self.fra.fused_down_residual(s["a_down"], s["w_down"], self.h_down, w_scale=s.get("s_down"),
+                                     out=self.h_down)
 
     def step(self, i):
         if self.wl.n_qkv:
@@ -147,7 +166,7 @@ def time_steps(fn, steps, warmup):
 def profile_call(runner, call: str, n: int):
     """Average duration (ms) of each library kernel over n calls of one kind."""
     import torch
-    fn = runner.qkv if call == "qkv" else runner.gu
+    fn = {"qkv": runner.qkv, "gu": runner.gu, "down": runner.down}[call]
     for i in range(3):
         fn(i)
     torch.cuda.synchronize()
@@ -306,10 +325,10 @@ def all_configs(steps: int) -> None:
     from fusion_residual_add_amd import inputs
     for name in inputs.WORKLOADS:
         wl = inputs.workload(name)
-        run = Runner(wl)
+        run = Runner(wl, down=True)
         ms = time_steps(run.step, steps, 3)
         calls = {}
-        for call in (["qkv"] if wl.n_qkv else []) + ["gu"]:
+        for call in (["qkv"] if wl.n_qkv else []) + ["gu", "down"]:
             prof = profile_call(run, call, 20)
             total = sum(prof.values())
             b, f = algo_bytes(wl, call), flops(wl, call)

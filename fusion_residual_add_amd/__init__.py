@@ -16,7 +16,8 @@ import torch
 from . import _lib
 from ._lib import FP_ACT, FP_NORM
 
-__all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_dequant_i8_bf16", "fused_dequant_i4_bf16",
+__all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_down_residual", "fused_dequant_i8_bf16",
+           "fused_dequant_i4_bf16",
            "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
            "library_path", "tune_install", "tune_clear", "tune_count"]
 
@@ -181,6 +182,34 @@ def fused_gateup_act(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: O
         _ptr(out, "out", dev, odt), M, K, ffn, FP_ACT[act], _DT[adt], _DT[wdt], _DT[odt],
         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
     _check("fused_gateup_act", st)
+    return out
+
+
+def fused_down_residual(a: torch.Tensor, w: torch.Tensor, residual: Optional[torch.Tensor] = None, *,
+                        w_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                        out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Down projection plus residual: out = residual + bias + a @ w^T; returns out [M, hidden].
+    ``out`` may be ``residual`` itself (updated in place) when the dtypes match."""
+    lib = _lib.load()
+    _ptr(a, "a")
+    dev = a.device
+    M, F = a.shape
+    adt = a.dtype
+    odt = out_dtype or adt
+    Nw = w.shape[0]
+    _check_weight(w, w_scale, Nw, F, "w")
+    if out is None:
+        out = torch.empty((M, Nw), dtype=odt, device=dev)
+    stream = _stream(dev)
+    need = int(lib.fp_workspace_bytes(M, F, Nw, _DT[adt], _DT[w.dtype]))
+    ws = workspace if workspace is not None else _workspace(dev, stream, need)
+    st = lib.fused_down_residual(
+        _ptr(a, "a", dev, adt), _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, torch.float32),
+        _ptr(bias, "bias", dev, adt), _ptr(residual, "residual", dev, adt), _ptr(out, "out", dev, odt),
+        M, F, Nw, _DT[adt], _DT[w.dtype], _DT[odt],
+        None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
+    _check("fused_down_residual", st)
     return out
 
 

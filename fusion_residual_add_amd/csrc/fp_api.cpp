@@ -574,6 +574,45 @@ fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, con
     return run(c, plan, pa);
 }
 
+fp_status fused_down_residual(const void *a, const void *w, const float *w_scale, const void *bias,
+                              const void *residual, void *out, int64_t M, int64_t ffn, int64_t hidden,
+                              fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype, void *workspace,
+                              size_t workspace_bytes, void *hip_stream) {
+    if (hidden <= 0 || hidden % 16 != 0)
+        return fail(FP_E_SHAPE, "hidden = %lld must be a positive multiple of 16", (long long)hidden);
+    // the projection of a (K = ffn) onto hidden output columns, no norm prologue
+    Common c{a, nullptr, nullptr, nullptr, nullptr, FP_NORM_NONE, 0.0f, w, w_scale, bias,
+             M, ffn, hidden, act_dtype, w_dtype, out_dtype, workspace, workspace_bytes,
+             (hipStream_t)hip_stream};
+    if (ffn <= 0 || ffn % 64 != 0)
+        return fail(FP_E_SHAPE, "ffn = %lld must be a positive multiple of 64", (long long)ffn);
+    fp_status st = validate_common(c, "w");
+    if (st != FP_OK) return st;
+    if (!out && M > 0) return fail(FP_E_NULL, "out is NULL");
+    if (!aligned16(out) || !aligned16(residual)) return fail(FP_E_ALIGN, "out and residual must be 16-byte aligned");
+    const int eo = act_size(out_dtype), ea = act_size(act_dtype);
+    // in place (out == residual, same dtype): every output element is written by
+    // the thread that read its residual element
+    const bool in_place = residual && out == residual && out_dtype == act_dtype;
+    std::vector<Range> ins, outs;
+    add_inputs(c, ins, "w");
+    ins[0].name = "a";
+    if (residual && !in_place) ins.push_back(rng("residual", residual, M * hidden * ea));
+    outs.push_back(rng("out", out, M * hidden * eo));
+    const Plan plan = make_plan(M, ffn, hidden, act_dtype, w_dtype, false);
+    st = check_workspace(c, plan, outs);
+    if (st != FP_OK) return st;
+    st = check_alias(ins, outs);
+    if (st != FP_OK) return st;
+
+    fp::ProjArgs pa{};
+    pa.epi = fp::EPI_LINEAR;
+    pa.out0 = out;
+    pa.F = hidden;
+    pa.res_epi = residual;
+    return run(c, plan, pa);
+}
+
 fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_bf16, int64_t N,
                                 int64_t K, void *hip_stream) {
     if (N < 0) return fail(FP_E_SHAPE, "N = %lld is negative", (long long)N);

@@ -232,7 +232,9 @@ __device__ __forceinline__ float gelu_tanh(float y) {
 // ---------------------------------------------------------------------------
 // Column c of the projection (bias already added) to its destination: the GQA
 // split for QKV (q | k | v column blocks, token-major), tanh-GELU or nothing for
-// the up projection.
+// the up projection, plus the residual for the down projection.  The residual
+// element is read by the thread that writes the output element, so the output
+// may be the residual buffer itself.
 template <int ACT, int EPI>
 __device__ __forceinline__ void store_col(const ProjArgs &p, int64_t m, int64_t c, float y) {
     using T = Act<ACT>;
@@ -246,6 +248,8 @@ __device__ __forceinline__ void store_col(const ProjArgs &p, int64_t m, int64_t 
         if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
         dst = p.out0;
         idx = m * p.F + c;
+        if constexpr (EPI == EPI_LINEAR)
+            if (p.res_epi) y += T::ld(p.res_epi, idx);   // the down projection's residual add
     }
     if (p.out_f32) ((float *)dst)[idx] = y;
     else T::st(dst, idx, y);

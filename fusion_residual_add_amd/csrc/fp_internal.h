@@ -36,6 +36,7 @@ struct ProjArgs {
     const void *w;          // [Nw, K] act or int8
     const float *w_scale;   // [Nw] (int8 only)
     const void *bias;       // [Nw] act or null
+    const void *res_epi;    // EPI_LINEAR: [M, F] act added to the output (residual stream), or null
     // epilogue
     int epi;                // EpiKind
     int out_f32;            // 1: store fp32, 0: store act dtype

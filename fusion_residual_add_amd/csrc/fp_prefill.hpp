@@ -473,11 +473,19 @@ void prefill_kernel(ProjArgs p) {
             } else {
                 dst = (char *)p.out0 + (m * ncols + cg) * esz;
             }
+            float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            if constexpr (EPI == EPI_LINEAR) {
+                if (p.res_epi) {   // the down projection's residual add (this lane reads what it writes)
+                    float r[8];
+                    T::unpack(*(const u32x4 *)((const char *)p.res_epi + (m * ncols + cg) * 2), r);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] += r[e];
+                }
+            }
             if (of32) {
-                *(f32x4 *)dst = v0;
-                *(f32x4 *)(dst + 16) = v1;
+                *(f32x4 *)dst = (f32x4){y[0], y[1], y[2], y[3]};
+                *(f32x4 *)(dst + 16) = (f32x4){y[4], y[5], y[6], y[7]};
             } else {
-                const float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                 *(u32x4 *)dst = T::pack(y);
             }
         }

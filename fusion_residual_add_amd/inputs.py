@@ -262,6 +262,20 @@ def generate(wl: Workload, seed: int = 0, parts=("qkv", "gu")) -> Dict[str, torc
     del w, s
     if wl.bias_std is not None:
         out["b_gu"] = _to_act(_normal(rng, (wl.n_gu,), wl.bias_std), wl.act)
+    if "down" in parts:
+        # the down projection (drawn last, so asking for it changes no other
+        # value): its input a [M, ffn] ~ N(0, 1) stands for the gate/up output,
+        # its weight [hidden, ffn] has the workload's weight distribution, and
+        # r doubles as the residual it adds
+        out["a_down"] = _to_act(_normal(rng, (M, wl.ffn), 1.0), wl.act)
+        w = _normal(rng, (wl.hidden, wl.ffn), wl.w_std)
+        if wl.wdt == "i8":
+            out["w_down"], out["s_down"] = quantize_rows_i8(w)
+        elif wl.wdt == "i4":
+            out["w_down"], out["s_down"] = quantize_groups_i4(w)
+        else:
+            out["w_down"] = _to_act(w, wl.wdt)
+        del w
     return out
 
 

@@ -143,6 +143,31 @@ fp_status fused_gateup_act(
     fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
     void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Down projection with the residual add in its epilogue: the projection
+ * after SwiGLU, whose output is added to the residual stream (the MLP's
+ * down projection of "TensorRT-LLM 深度工程实践…" §4.1, and the Add folded
+ * into its neighbouring kernel in the Layer Fusion figure of "TRT-LLM deep
+ * dive", 构建阶段详解 §3):
+ *   out[m, c] = residual[m, c] + bias[c] + sum_k a[m, k] * w[c, k]
+ * accumulated in fp32 and rounded once to out_dtype.
+ *  a        : [M, ffn] act_dtype (e.g. the fused_gateup_act output), used as
+ *             given (no norm)
+ *  w        : [hidden, ffn] act_dtype, or int8 / int4 with w_scale as for
+ *             the other calls (K = ffn)
+ *  bias     : [hidden] act_dtype or NULL
+ *  residual : [M, hidden] act_dtype or NULL (no add)
+ *  out      : [M, hidden] out_dtype; may be the residual buffer itself when
+ *             out_dtype == act_dtype (the residual stream updated in place;
+ *             each element is read and written by the same thread).  Any
+ *             other overlap is FP_E_ALIAS.
+ *  Requires ffn a positive multiple of 64 (128 for int4), hidden a positive
+ *  multiple of 16.  Dtypes, alignment, workspace (fp_workspace_bytes(M, ffn,
+ *  hidden, act_dtype, w_dtype)) and errors as for the other calls. */
+fp_status fused_down_residual(const void *a, const void *w, const float *w_scale, const void *bias,
+                              const void *residual, void *out, int64_t M, int64_t ffn, int64_t hidden,
+                              fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
+                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* int8 per-output-row weight dequantisation to bf16, the same device
  * function the projection kernels use in their weight loader:
  * out[j, k] = bf16_rne(f32_rne(q[j, k] * scale[j])).

@@ -95,6 +95,8 @@ def load(path: Optional[str] = None):
     lib.or_gateup_act.argtypes = [vp, vp, vp, vp, ci, ci, dbl, vp, ci, vp, vp,
                                   i64, i64, i64, ci, vp, vp, ci]
     lib.or_gateup_act.restype = ci
+    lib.or_down_residual.argtypes = [vp, ci, vp, ci, vp, vp, vp, i64, i64, i64, vp]
+    lib.or_down_residual.restype = ci
     if path is None:
         _lib = lib
     return lib
@@ -252,6 +254,21 @@ def gateup_act(x, r, gamma, beta, norm: str, eps: float, w, w_scale, bias,
                               M, K, ffn, ACT[act_fn], _ptr(out), _ptr(h), int(rounded))
     assert rc == 0
     return {"out": out, "h_out": h}
+
+
+def down_residual(a, w, w_scale, bias, residual) -> np.ndarray:
+    """out = residual + bias + a @ w^T in float64 (a [M, K] as stored, w [N, K])."""
+    aa, act = _raw(a)
+    M, K = aa.shape
+    wa, wdt = _raw(w)
+    N = wa.shape[0]
+    sa = None if w_scale is None else np.ascontiguousarray(_raw(w_scale)[0], dtype=np.float32)
+    ba, _ = _raw(bias)
+    ra, _ = _raw(residual)
+    out = _f64((M, N))
+    assert load().or_down_residual(_ptr(aa), act, _ptr(wa), wdt, _ptr(sa), _ptr(ba), _ptr(ra),
+                                   M, K, N, _ptr(out)) == 0
+    return out
 
 
 def workload_qkv(wl, inp, row_idx=None, rounded=True):

@@ -363,3 +363,27 @@ int or_gateup_act(const void *x, const void *r, const void *gamma, const void *b
     free(acc);
     return 0;
 }
+
+/* Down projection with the residual add ([T] below):
+ * out[m, c] = residual[m, c] + bias[c] + sum_k a[m, k] * w[c, k], in double.
+ * a is [M, K] in the activation dtype and used as stored (no norm, no
+ * rounding: it is already an activation-dtype tensor); w is [N, K] as for the
+ * other products (R8, R9); residual and bias may be NULL.
+ * [T] "TensorRT-LLM 深度工程实践…", §4.1: the MLP's gate/up projection
+ *     followed by the down projection; "TRT-LLM deep dive", 构建阶段详解 §3:
+ *     the Add folded into the neighbouring kernel. */
+int or_down_residual(const void *a, int act, const void *w, int wdtype, const float *w_scale,
+                     const void *bias, const void *residual, int64_t M, int64_t K, int64_t N,
+                     double *out) {
+    double *ad = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!ad) return -1;
+    or_decode_array(a, act, M * K, ad);
+    if (or_matmul_nt(ad, w, wdtype, w_scale, M, K, N, out)) { free(ad); return -1; }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < N; ++c) {
+            if (bias) out[m * N + c] += or_load(bias, act, c);
+            if (residual) out[m * N + c] += or_load(residual, act, m * N + c);
+        }
+    free(ad);
+    return 0;
+}

@@ -541,6 +541,33 @@ def pin_int4_projection_uses_dequantised_weights():
     _close(o["out"], a @ w_deq.double().numpy().T, rtol=1e-13, atol=1e-13, what="int4 proj")
 
 
+def pin_down_residual():
+    rng = _rng(41)
+    M, K, N = 3, 64, 10
+    a = _t(rng.standard_normal((M, K)), torch.bfloat16)
+    w = _t(rng.standard_normal((N, K)) / 8, torch.bfloat16)
+    res = _t(rng.standard_normal((M, N)), torch.bfloat16)
+    b = _t(rng.standard_normal(N) / 4, torch.bfloat16)
+    ad, wd, rd, bd = (t.double().numpy() for t in (a, w, res, b))
+    # the plain definition, the product by numpy
+    _close(oracle.down_residual(a, w, None, b, res), rd + bd[None, :] + ad @ wd.T, rtol=1e-13, atol=1e-13,
+           what="down + residual")
+    # no residual, no bias: the product alone; zero weight: the residual (+ bias) exactly
+    _close(oracle.down_residual(a, w, None, None, None), ad @ wd.T, rtol=1e-13, atol=1e-13, what="down")
+    z = oracle.down_residual(a, torch.zeros_like(w), None, b, res)
+    assert np.array_equal(z, rd + bd[None, :])
+    # a one-hot row picks one weight column (catches a transposed operand)
+    oh = torch.zeros(M, K, dtype=torch.bfloat16)
+    oh[1, 7] = 1.0
+    o = oracle.down_residual(oh, w, None, None, res)
+    assert np.array_equal(o[1], rd[1] + wd[:, 7]) and np.array_equal(o[0], rd[0])
+    # int8 weights go through their dequantisation
+    q = torch.from_numpy(rng.integers(-127, 128, (N, K)).astype(np.int8))
+    sc = torch.from_numpy(rng.uniform(1e-3, 1e-2, N).astype(np.float32))
+    w_deq = (q.float() * sc[:, None]).to(torch.bfloat16).double().numpy()
+    _close(oracle.down_residual(a, q, sc, None, res), rd + ad @ w_deq.T, rtol=1e-13, atol=1e-13, what="int8 down")
+
+
 def pin_rounded_vs_unrounded_reading():
     # rounding the A operand is the only difference between the two readings
     dt = torch.bfloat16

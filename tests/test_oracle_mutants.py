@@ -47,6 +47,11 @@ MUTANTS = {
     "int4 not sign-extended": ("return nib >= 8 ? nib - 16 : nib;", "return nib;"),
     "int4 one scale per row": ("s[j * G + k / OR_I4_GROUP]", "s[j * G]"),
     "int4 group of 64": ("enum { OR_I4_GROUP = 128 };", "enum { OR_I4_GROUP = 64 };"),
+    "down residual dropped": ("if (residual) out[m * N + c] += or_load(residual, act, m * N + c);", "(void)residual;"),
+    "down residual transposed": ("if (residual) out[m * N + c] += or_load(residual, act, m * N + c);",
+                                 "if (residual) out[m * N + c] += or_load(residual, act, c * M + m);"),
+    "down bias shifted": ("if (bias) out[m * N + c] += or_load(bias, act, c);",
+                          "if (bias) out[m * N + c] += or_load(bias, act, (c + 1) % N);"),
     "int4 signed zero kept": ("if (w == 0.0) w = 0.0;   /* +0 (R9) */", "(void)0;"),
 }
 
