@@ -210,9 +210,10 @@ def library_kernel_name(cxx: str) -> str:
         act = {"1": "bf16-i8w", "2": "bf16-i4w"}.get(wq) or _ACT[m.group(1)]
         return (f"stream_kernel<{act},m{16 * int(m.group(3))},n{64 * int(m.group(4))},"
                 f"k{32 * int(m.group(5))},{_EPI[m.group(6)]}>")
-    m = re.search(r"fp::prefill_kernel<(\d), (true|false), (\d)(?:, (?:true|false))?>", cxx)
+    m = re.search(r"fp::prefill_kernel<(\d), (true|false|\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
-        act = "bf16-i8w" if m.group(2) == "true" else _ACT[m.group(1)]
+        wq = {"true": "1", "false": "0"}.get(m.group(2), m.group(2))
+        act = {"1": "bf16-i8w", "2": "bf16-i4w"}.get(wq) or _ACT[m.group(1)]
         return f"prefill_kernel<{act},128x512,{_EPI[m.group(3)]}>"
     m = re.search(r"fp::stats_kernel<(\d), \d+>", cxx)
     if m:

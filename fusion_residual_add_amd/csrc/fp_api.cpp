@@ -135,10 +135,10 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         fam = 2;
     else
         fam = 0;
-    // int4 weights: streamed and dequantised in registers by the streaming
-    // kernel; for the other families dequantised into the workspace first and
+    // int4 weights: dequantised in registers by the streaming and 128 x 512
+    // kernels; for the tiled family dequantised into the workspace first and
     // then run as bf16 weights
-    if (i4 && fam != 1) wdt = FP_BF16;
+    if (i4 && fam == 0) wdt = FP_BF16;
     const bool qw = wdt == FP_I8 || wdt == FP_I4;   // weights dequantised in the loader
     int64_t tiles, ksteps, target;
     if (fam == 1) {
@@ -262,7 +262,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     if (p.slots > 1) off = align256(off + (size_t)tiles * 4);
     p.part_off = off;
     if (p.slots > 1) off = align256(off + (size_t)tiles * p.slots * p.tile_elems * 4);
-    if (i4 && p.family != 1) {
+    if (i4 && p.family == 0) {
         p.deq = true;
         p.deq_off = off;
         off = align256(off + (size_t)Nw * (size_t)K * 2);
@@ -456,8 +456,8 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
         hipError_t e = fp::launch_stream(act, wq, plan.sc, pa, plan.grid, c.stream);
         if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
     } else if (plan.family == 2) {
-        ProfScope ps(fp::prefill_kernel_name(act, wi8, pa.epi), c.stream);
-        hipError_t e = fp::launch_prefill(act, wi8, pa, c.stream);
+        ProfScope ps(fp::prefill_kernel_name(act, wq, pa.epi), c.stream);
+        hipError_t e = fp::launch_prefill(act, wq, pa, c.stream);
         if (e != hipSuccess) return hip_fail(e, "prefill_kernel launch");
     } else {
         ProfScope ps(fp::proj_kernel_name(act, wi8, plan.tile, pa.epi), c.stream);
@@ -669,7 +669,7 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     const int epi = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
     const char *fam = p.family == 1 ? "stream" : p.family == 2 ? "prefill" : "tiled";
     const char *name = p.family == 1 ? fp::stream_kernel_name(a, wq, p.sc, epi)
-                     : p.family == 2 ? fp::prefill_kernel_name(a, wi8, epi)
+                     : p.family == 2 ? fp::prefill_kernel_name(a, wq, epi)
                                      : fp::proj_kernel_name(a, wi8, p.tile, epi);
     const int64_t grid = p.family == 1 ? p.grid : (int64_t)p.tiles_m * p.tiles_n * p.splits;
     snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s", fam, name,

@@ -77,24 +77,29 @@ __device__ __forceinline__ void dequant16(u32x4 qv, float s, u32x4 &lo, u32x4 &h
 // fma rounds u * s - 8 s = q * s once, as the definition does (a zero
 // result is +0, which the definition fixes).  About 3 instructions per value.  The single definition used by the weight loader
 // and dequant_i4_kernel.
+// 8 int4 values (one word) -> one 16-byte vector of 8 bf16 values
+__device__ __forceinline__ u32x4 dequant8_i4(unsigned word, float s, float m8s) {
+    const unsigned v = word ^ 0x88888888u;
+    unsigned ev = v & 0x0F0F0F0Fu;                 // elements 0, 2, 4, 6
+    unsigned od = (v >> 4) & 0x0F0F0F0Fu;          // elements 1, 3, 5, 7
+    // keep the two spread words as they are: otherwise the compiler folds
+    // the masks into a bit-field extract per value instead of using the
+    // byte-select conversions (v_cvt_f32_ubyte1..3)
+    asm("" : "+v"(ev), "+v"(od));
+    u32x4 out;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float f0 = fmaf((float)((ev >> (8 * b)) & 0xFFu), s, m8s);
+        const float f1 = fmaf((float)((od >> (8 * b)) & 0xFFu), s, m8s);
+        out[b] = pack2_bf16(f0, f1);
+    }
+    return out;
+}
+
 __device__ __forceinline__ void dequant32_i4(u32x4 qv, float s, u32x4 (&out)[4]) {
     const float m8s = -8.0f * s;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const unsigned v = qv[w] ^ 0x88888888u;
-        unsigned ev = v & 0x0F0F0F0Fu;                 // elements 8w + 0, 2, 4, 6
-        unsigned od = (v >> 4) & 0x0F0F0F0Fu;          // elements 8w + 1, 3, 5, 7
-        // keep the two spread words as they are: otherwise the compiler folds
-        // the masks into a bit-field extract per value instead of using the
-        // byte-select conversions (v_cvt_f32_ubyte1..3)
-        asm("" : "+v"(ev), "+v"(od));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float f0 = fmaf((float)((ev >> (8 * b)) & 0xFFu), s, m8s);
-            const float f1 = fmaf((float)((od >> (8 * b)) & 0xFFu), s, m8s);
-            out[w][b] = pack2_bf16(f0, f1);
-        }
-    }
+    for (int w = 0; w < 4; ++w) out[w] = dequant8_i4(qv[w], s, m8s);
 }
 
 // ---------------------------------------------------------------------------

@@ -85,8 +85,8 @@ const char *stats_kernel_name(int act);
 const char *proj_kernel_name(int act, bool w_i8, int tile, int epi);
 const char *stream_kernel_name(int act, int wq, const StreamCfg &c, int epi);
 // 128 x 512 family (fp_prefill*.hip): 16-bit activations, more than 64 tokens
-hipError_t launch_prefill(int act, bool w_i8, const ProjArgs &a, hipStream_t s);
-const char *prefill_kernel_name(int act, bool w_i8, int epi);
+hipError_t launch_prefill(int act, int wq, const ProjArgs &a, hipStream_t s);
+const char *prefill_kernel_name(int act, int wq, int epi);
 const char *dequant_kernel_name();
 hipError_t launch_dequant_i4(const uint8_t *q, const float *scale, void *out, int64_t N, int64_t K,
                              hipStream_t s);

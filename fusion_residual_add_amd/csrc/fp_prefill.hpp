@@ -11,7 +11,8 @@
 // whole 160 KB of LDS.
 //  * B: 16-bit weights go from HBM straight into LDS (buffer_load ... lds, 16
 //    bytes per lane, one 1 KB wave instruction = 8 rows x 128 bytes); int8
-//    weights go through registers and are dequantised to bf16 on the way.
+//    and int4 weights go through registers and are dequantised to bf16 on
+//    the way.
 //  * A: x and the residual are read (L2 hits: a 128-row block is shared by
 //    every column tile), re-formed as h, normalised with the row statistics
 //    and gamma / beta, rounded to the activation dtype and written to LDS -
@@ -51,13 +52,16 @@ __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >
 
 // LN: LayerNorm (mean, beta); otherwise RMSNorm or no norm, whose
 // normalisation is two multiplies (h * rstd * gamma) and has no beta to load.
-template <int ACT, bool WI8, int EPI, bool LN>
+// WQ: weight storage -- 0 the activation dtype (straight into LDS), 1 int8,
+// 2 int4 (both through registers, dequantised into LDS).
+template <int ACT, int WQ, int EPI, bool LN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(ProjArgs p) {
     using T = Act<ACT>;
     using namespace pf;
+    constexpr bool WI8 = WQ == 1, WI4 = WQ == 2, WREG = WQ != 0;
     static_assert(ACT != ACT_F32, "16-bit activations");
-    static_assert(!WI8 || ACT == ACT_BF16, "int8 weights feed bf16 MFMA");
+    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 weights feed bf16 MFMA");
     // A and B tiles of the two stages as four distinct LDS objects, so that
     // the compiler can tell the direct-to-LDS weight loads into one stage from
     // the fragment reads of the other (and waits for them only at the end of
@@ -103,8 +107,12 @@ void prefill_kernel(ProjArgs p) {
                                                                         p.norm != 0 ? (uint32_t)(p.K * 2) : 0u, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)(has_beta ? p.beta : gsrc), (short)0,
                                                                         has_beta ? (uint32_t)(p.K * 2) : 0u, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, (short)0,
-                                                                        (uint32_t)(p.Nw * p.K * (WI8 ? 1 : 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)p.w, (short)0, (uint32_t)(WI4 ? p.Nw * p.K / 2 : p.Nw * p.K * (WI8 ? 1 : 2)), 0x00020000);
+    // int4: the group scales [Nw, K / 128]
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(WI4 ? (const void *)p.w_scale : p.w), (short)0, WI4 ? (uint32_t)(p.Nw * (p.K / 128) * 4) : 0u,
+        0x00020000);
     // norm none: gamma reads as zero and g1 turns it into one
     const float g1 = p.norm != 0 ? 0.f : 1.f;
 
@@ -131,15 +139,21 @@ void prefill_kernel(ProjArgs p) {
     // (l % 8) ^ swizzle(row).
     // int8 weights: thread -> 16-byte int8 vector (tile row (tid / 4) + 64 i,
     // k bytes 16 (tid % 4) .. + 15), dequantised in registers.
-    constexpr int NBO = WI8 ? 8 : 16;
+    // int4 weights: thread -> 16-byte vector of 32 values (tile row
+    // (tid / 2) + 128 i, k 32 (tid % 2) .. + 31 of the stage), with the row's
+    // scale of the stage's group (a stage of 64 k lies in one group of 128).
+    constexpr int NBO = WI8 ? 8 : WI4 ? 4 : 16;
     uint32_t b_off[NBO];                                 // bytes, without the K step
+    uint32_t b_soff[WI4 ? 4 : 1];                        // int4: byte offset of the row's scales
     float b_sc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) b_sc[i] = 0.f;
+    b_soff[0] = 0;
 #pragma unroll
     for (int i = 0; i < NBO; ++i) {
         int br;
         if constexpr (WI8) br = (tid >> 2) + 64 * i;
+        else if constexpr (WI4) br = (tid >> 1) + 128 * i;
         else br = 128 * wave + 8 * i + (lane >> 3);
         int64_t wrow;
         if constexpr (EPI == EPI_SWIGLU) {
@@ -156,6 +170,9 @@ void prefill_kernel(ProjArgs p) {
         if constexpr (WI8) {
             b_off[i] = (uint32_t)(wrow * p.K) + (tid & 3) * 16;
             b_sc[i] = p.w_scale[wrow];
+        } else if constexpr (WI4) {
+            b_off[i] = (uint32_t)(wrow * (p.K / 2)) + (tid & 1) * 16;
+            b_soff[i] = (uint32_t)(wrow * (p.K / 128) * 4);
         } else {
             const int c = (lane & 7) ^ ((br >> 1) & 7);
             b_off[i] = (uint32_t)((wrow * p.K + c * 8) * 2);
@@ -167,7 +184,10 @@ void prefill_kernel(ProjArgs p) {
     // row's registers are refilled with stage kt + 2 right after use, so every
     // load has a whole step to arrive.
     struct ARegs { u32x4 x[4], r[4], g, b; };
-    struct BRegs { u32x4 q[8]; };   // int8 path only: the thread's 8 weight vectors of a stage
+    struct BRegs {                  // int8 / int4: the thread's weight vectors of a stage
+        u32x4 q[WI4 ? 4 : 8];
+        float s[WI4 ? 4 : 1];       // int4: their rows' scales for the stage
+    };
     ARegs A;
     BRegs B;
     float gv[8], bv[8];             // gamma / beta of the stage being normalised
@@ -219,7 +239,15 @@ void prefill_kernel(ProjArgs p) {
     };
     // int8 weights: vector i of stage kt into registers; dequantised into
     // the LDS tile of its stage (16 values -> two 16-byte bf16 chunks)
-    auto bload_one = [&](int kt, int i) { B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * BK); };
+    auto bload_one = [&](int kt, int i) {
+        if constexpr (WI4) {
+            B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * (BK / 2));
+            B.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, b_soff[i],
+                                                                                    (uint32_t)(kt / 2) * 4, 0));
+        } else {
+            B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * BK);
+        }
+    };
     auto bstore_one = [&](unsigned char *lb, int i) {
         u32x4 lo, hi;
         dequant16(B.q[i], b_sc[i], lo, hi);
@@ -227,6 +255,14 @@ void prefill_kernel(ProjArgs p) {
         const int c0 = (tid & 3) * 2;
         *(u32x4 *)(lb + swz(br, c0)) = lo;
         *(u32x4 *)(lb + swz(br, c0 + 1)) = hi;
+    };
+    // int4: half hf of vector i (16 values, two 16-byte chunks) into the LDS tile
+    auto bstore_half = [&](unsigned char *lb, int i, int hf) {
+        const float s = B.s[i], m8s = -8.0f * s;
+        const int br = (tid >> 1) + 128 * i;
+        const int c0 = (tid & 1) * 4 + hf * 2;
+        *(u32x4 *)(lb + swz(br, c0)) = dequant8_i4(B.q[i][2 * hf], s, m8s);
+        *(u32x4 *)(lb + swz(br, c0 + 1)) = dequant8_i4(B.q[i][2 * hf + 1], s, m8s);
     };
 
     // ---- accumulators: acc[i][j][q] = D[row i*32 + 8(q/4) + 4(lane/32) + q%4]
@@ -288,6 +324,11 @@ void prefill_kernel(ProjArgs p) {
                 // from stage kn right after
                 bstore_one(nb, r);
                 bload_one(kn, r);
+            } else if constexpr (WI4) {
+                // half a vector (16 values) per region, the vector refilled
+                // after its second half
+                bstore_half(nb, r >> 1, r & 1);
+                if (r & 1) bload_one(kn, r >> 1);
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -296,10 +337,10 @@ void prefill_kernel(ProjArgs p) {
                 // first three MFMAs (measured on MI355X: 1-3 % faster than all
                 // six ahead of the first)
                 if (m < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, WI8 ? 8 : 4, 0);   // then VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, WREG ? 8 : 4, 0);   // then VALU
             }
-            __builtin_amdgcn_sched_group_barrier(0x200, WI8 ? 3 : 1, 0);   // LDS writes
-            __builtin_amdgcn_sched_group_barrier(0x020, WI8 ? 3 : 2, 0);   // refill loads
+            __builtin_amdgcn_sched_group_barrier(0x200, WREG ? 3 : 1, 0);   // LDS writes
+            __builtin_amdgcn_sched_group_barrier(0x020, WREG ? 3 : 2, 0);   // refill loads
             __builtin_amdgcn_sched_barrier(0);
             if (r < 7) {
                 bf[0] = nbf[0];
@@ -320,7 +361,7 @@ void prefill_kernel(ProjArgs p) {
     // statements keep the compiler from moving memory accesses across the
     // barrier.
     auto step_sync = [&]() {
-        constexpr int VM = WI8 ? 63 : (LN ? 10 : 9);   // int8: every load is a rolling register load
+        constexpr int VM = WREG ? 63 : (LN ? 10 : 9);   // int8 / int4: every load is a rolling register load
         __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
         __asm__ __volatile__("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -329,9 +370,9 @@ void prefill_kernel(ProjArgs p) {
 
     if (kt0 < kt1) {
         // prologue: stage kt0 into LDS tile 0, then start loading stage kt0 + 1
-        if constexpr (WI8) {
+        if constexpr (WREG) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) bload_one(kt0, i);
+            for (int i = 0; i < NBO; ++i) bload_one(kt0, i);
         } else {
             bload_lds(kt0, lB0);
         }
@@ -354,6 +395,13 @@ void prefill_kernel(ProjArgs p) {
                 bstore_one(lB0, i);
                 bload_one(k1, i);
             }
+        } else if constexpr (WI4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bstore_half(lB0, i, 0);
+                bstore_half(lB0, i, 1);
+                bload_one(k1, i);
+            }
         }
         gb_issue(k1);
 #pragma unroll
@@ -369,7 +417,7 @@ void prefill_kernel(ProjArgs p) {
             unsigned char *na = odd ? lA0 : lA1, *nb = odd ? lB0 : lB1;
             const int kw = kt + 1 < kt1 ? kt + 1 : kt1 - 1;
             const int kn = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
-            if constexpr (!WI8) bload_lds(kw, nb);
+            if constexpr (!WREG) bload_lds(kw, nb);
             __builtin_amdgcn_sched_barrier(0);   // keeps the weight loads first (see step_sync)
             gb_unpack();
             gb_issue(kn);
@@ -494,28 +542,28 @@ void prefill_kernel(ProjArgs p) {
     }
 }
 
-template <int ACT, bool WI8, bool LN>
+template <int ACT, int WQ, bool LN>
 inline void launch_prefill_n(const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (a.epi) {
     case EPI_QKV:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_QKV, LN>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_QKV, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     case EPI_SWIGLU:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_SWIGLU, LN>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_SWIGLU, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     case EPI_GELU:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_GELU, LN>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_GELU, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     default:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WI8, EPI_LINEAR, LN>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_LINEAR, LN>), dim3(grid), dim3(256), 0, s, a);
         break;
     }
 }
 
-template <int ACT, bool WI8>
+template <int ACT, int WQ>
 inline void launch_prefill_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    if (a.norm == 2) launch_prefill_n<ACT, WI8, true>(a, grid, s);
-    else launch_prefill_n<ACT, WI8, false>(a, grid, s);
+    if (a.norm == 2) launch_prefill_n<ACT, WQ, true>(a, grid, s);
+    else launch_prefill_n<ACT, WQ, false>(a, grid, s);
 }
 
 }  // namespace fp

@@ -4,7 +4,7 @@
 namespace fp {
 
 void launch_prefill_bf16(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_prefill_t<ACT_BF16, false>(a, grid, s);
+    launch_prefill_t<ACT_BF16, 0>(a, grid, s);
 }
 
 }  // namespace fp

@@ -4,7 +4,7 @@
 namespace fp {
 
 void launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_prefill_t<ACT_F16, false>(a, grid, s);
+    launch_prefill_t<ACT_F16, 0>(a, grid, s);
 }
 
 }  // namespace fp

@@ -29,22 +29,25 @@ hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a,
 void launch_prefill_bf16(const ProjArgs &a, unsigned grid, hipStream_t s);
 void launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s);
 void launch_prefill_i8(const ProjArgs &a, unsigned grid, hipStream_t s);
+void launch_prefill_i4(const ProjArgs &a, unsigned grid, hipStream_t s);
 
-hipError_t launch_prefill(int act, bool w_i8, const ProjArgs &a, hipStream_t s) {
+// wq: 0 weights in the activation dtype, 1 int8, 2 int4
+hipError_t launch_prefill(int act, int wq, const ProjArgs &a, hipStream_t s) {
     const int64_t g = (int64_t)a.tiles_m * a.tiles_n * a.splits;
     if (g <= 0) return hipSuccess;
     const unsigned grid = (unsigned)g;
-    if (w_i8) launch_prefill_i8(a, grid, s);
+    if (wq == 1) launch_prefill_i8(a, grid, s);
+    else if (wq == 2) launch_prefill_i4(a, grid, s);
     else if (act == ACT_F16) launch_prefill_f16(a, grid, s);
     else launch_prefill_bf16(a, grid, s);
     return hipGetLastError();
 }
 
-const char *prefill_kernel_name(int act, bool w_i8, int epi) {
-    static const char *acts[4] = {"f32", "f16", "bf16", "bf16-i8w"};
+const char *prefill_kernel_name(int act, int wq, int epi) {
+    static const char *acts[5] = {"f32", "f16", "bf16", "bf16-i8w", "bf16-i4w"};
     static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
     thread_local char buf[64];
-    snprintf(buf, sizeof buf, "prefill_kernel<%s,128x512,%s>", acts[w_i8 ? 3 : act], epis[epi]);
+    snprintf(buf, sizeof buf, "prefill_kernel<%s,128x512,%s>", acts[wq ? 2 + wq : act], epis[epi]);
     return buf;
 }
 

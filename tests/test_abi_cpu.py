@@ -165,10 +165,11 @@ def test_int4_plans():
     p = _plan(16, 8192, 57344, w=u8, fn="swiglu")
     assert p["kernel"] == "stream_kernel<bf16-i4w,m16,n128,k256,swiglu>" and "prep" not in p
     assert _plan(64, 8192, 57344, w=u8, fn="swiglu")["kernel"] == "stream_kernel<bf16-i4w,m64,n256,k128,swiglu>"
-    # every other call: dequantised into the workspace, then the bf16 kernels
+    # more than 64 tokens: the 128 x 512 kernel, dequantised in registers too
     p = _plan(256, 8192, 57344, w=u8, fn="swiglu")
-    assert p["family"] == "prefill" and p["kernel"] == "prefill_kernel<bf16,128x512,swiglu>"
-    assert p["prep"] == "dequant_i4_kernel" and p["workspace"] >= 57344 * 8192 * 2
+    assert p["family"] == "prefill" and p["kernel"] == "prefill_kernel<bf16-i4w,128x512,swiglu>"
+    assert "prep" not in p and p["workspace"] < 57344 * 8192
+    # the tiled kernel: dequantised into the workspace, then the bf16 kernel
     p = _plan(8, 384, 512, w=u8)
     assert p["family"] == "tiled" and p["prep"] == "dequant_i4_kernel"
     assert fra.workspace_bytes(8, 384, 512, torch.bfloat16, u8) >= 512 * 384 * 2

@@ -1,9 +1,10 @@
 """int4 group-wise weights (4-bit weights, 16-bit activations, one scale per
 row and group of 128 k, no zero point) through the C ABI against the oracle.
 
-At decode token counts with hidden a multiple of 256 the weight-streaming
-kernel dequantises the weights in registers; every other call dequantises
-them into the workspace and runs the bf16 kernels.  Both paths, both calls,
+The weight-streaming kernel (decode token counts, hidden a multiple of 256)
+and the 128 x 512 kernel (more than 64 tokens) dequantise the weights in
+registers; the tiled kernel's calls dequantise them into the workspace and
+run the bf16 kernel.  Both paths, both calls,
 fp32 and bf16 outputs, the 256-row streaming form, and the dequantisation
 bits (the same device function in both paths) are checked; tolerances as in
 test_gpu_parity.
@@ -39,7 +40,8 @@ INT4 = [
     dict(M=1, hidden=512), dict(M=5, hidden=768, ffn=208), dict(M=17, hidden=1024, H=8, Hkv=2, D=64),
     dict(M=32, hidden=512), dict(M=40, hidden=768), dict(M=64, hidden=1024, ffn=336),
     dict(M=3, hidden=384),                       # hidden not a multiple of 256: staged, tiled kernel
-    dict(M=100, hidden=512), dict(M=300, hidden=1024, ffn=400),   # staged, 128 x 512 kernel
+    dict(M=100, hidden=512), dict(M=300, hidden=1024, ffn=400),   # 128 x 512 kernel
+    dict(M=257, hidden=384, ffn=208, act_fn="none", bias=True),
     dict(M=9, hidden=512, act_fn="none", bias=True, ffn=144),
 ]
 
@@ -55,8 +57,9 @@ def test_int4_small(cfg, native):
     odt = None if native else torch.float32
     plan = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, torch.bfloat16, torch.uint8, wl.act_fn)
     print(f"int4 {wl.name} {plan['kernel']} {plan.get('prep', '')} native={native}", flush=True)
-    native_path = wl.M <= 64 and wl.hidden % 256 == 0
-    assert (plan["family"] == "stream") == native_path and ("prep" in plan) == (not native_path)
+    stream = wl.M <= 64 and wl.hidden % 256 == 0
+    assert (plan["family"] == "stream") == stream
+    assert ("prep" in plan) == (plan["family"] == "tiled")        # staged only for the tiled kernel
     q, k, v, h = run_qkv(wl, d, odt)
     out = run_gu(wl, d, odt)
     torch.cuda.synchronize()
@@ -69,7 +72,8 @@ def test_int4_small(cfg, native):
     assert np.array_equal(h.double().cpu().numpy(), rq["h_out"]), "h_out not bit-exact"
 
 
-@pytest.mark.parametrize("env", [{"FUSEDPROJ_STREAM_NR": "4"}, {"FUSEDPROJ_STREAM_NR": "4", "FUSEDPROJ_SPLITS": "3"}],
+@pytest.mark.parametrize("env", [{"FUSEDPROJ_STREAM_NR": "4"}, {"FUSEDPROJ_STREAM_NR": "4", "FUSEDPROJ_SPLITS": "3"},
+                                 {"FUSEDPROJ_NO_STREAM": "1", "FUSEDPROJ_SPLITS": "3"}],
                          ids=lambda e: ",".join(f"{k[10:]}={v}" for k, v in e.items()))
 @pytest.mark.parametrize("M", [1, 48])
 def test_int4_256_rows(env, M, monkeypatch):
@@ -112,3 +116,21 @@ def test_int4_workload_full_size(name):
         print(name, native, "q", check("q", q, rq["q"]), "k", check("k", k, rq["k"]), "v", check("v", v, rq["v"]),
               "out", check("out", res[("gu", native)], rg["out"]), flush=True)
         assert np.array_equal(h.double().numpy(), rq["h_out"]), "h_out not bit-exact"
+
+
+@pytest.mark.parametrize("splits", ["1", "2", "3", "5"])
+def test_int4_prefill_splits(splits, monkeypatch):
+    """The 128 x 512 kernel's int4 path with K split (group scales per stage of each split)."""
+    monkeypatch.setenv("FUSEDPROJ_SPLITS", splits)
+    wl = small(wdt="i4", M=200, hidden=1024, H=8, Hkv=2, D=64, ffn=336)
+    inp = inputs.generate(wl, seed=8)
+    d = to_dev(inp)
+    print(f"int4 prefill splits={splits}", flush=True)
+    q, k, v, h = run_qkv(wl, d, torch.float32)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rq = oracle.workload_qkv(wl, inp)
+    rg = oracle.workload_gateup(wl, inp)
+    check("q", q, rq["q"])
+    check("k", k, rq["k"])
+    check("out", out, rg["out"])
