@@ -39,7 +39,8 @@ import fusion_residual_add_amd as fra
 from fusion_residual_add_amd import inputs
 
 MALL_BYTES = 256 << 20            # MI355X last-level (Infinity) cache
-_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
+           "i4": torch.uint8}
 _NAMES = {v: k for k, v in _DTYPES.items()}
 
 
@@ -52,10 +53,11 @@ def candidates(M: int, hidden: int, n_cols: int, act: torch.dtype, wdt: torch.dt
     stream_ok = act != torch.float32 and M <= 64 and hidden % 256 == 0
     big = M * hidden * 2 >= (1 << 32) or n_cols * hidden * 2 >= (1 << 32)
     if stream_ok:
+        quant = wdt in (torch.int8, torch.uint8)      # int8 / int4 weights
         rows = [128]
-        if not swiglu and wdt != torch.int8 and M <= 32:
+        if not swiglu and not quant and M <= 32:
             rows.append(64)
-        if wdt == torch.int8:
+        if quant:
             rows.append(256)
         for r in rows:
             for g in (128, 160, 192, 224, 240, 256):

@@ -354,3 +354,32 @@ def test_tuning_table_rejects(bad):
         assert fra.tune_count() == 1 and _plan(32, 4096, 6144)["grid"] == 200
     finally:
         fra.tune_clear()
+
+
+def test_tuning_table_json_round_trip(tmp_path):
+    from fusion_residual_add_amd import tune
+    entries = [_entry(family="stream", rows=256, grid=240, w_dtype=torch.uint8, hidden=8192, n_cols=10240),
+               _entry(family="tiled", splits=4, act_dtype=torch.float32, w_dtype=torch.float32),
+               _entry(rows=256, w_dtype=torch.int8)]
+    path = str(tmp_path / "table.json")
+    tune.save(entries, path)
+    back = tune.load(path)
+    assert back == entries
+    try:
+        fra.tune_install(back)
+        assert fra.tune_count() == 3
+        p = _plan(20, 8192, 10240, w=torch.uint8)
+        assert p["kernel"] == "stream_kernel<bf16-i4w,m32,n256,k256,linear>" and p["grid"] == 240
+    finally:
+        fra.tune_clear()
+
+
+def test_tuner_candidates_cover_every_family():
+    from fusion_residual_add_amd import tune
+    for w in (torch.bfloat16, torch.int8, torch.uint8):
+        fams = {c["plan"]["family"] for c in tune.candidates(16, 1024, 1024, torch.bfloat16, w, False)}
+        assert fams == {"stream", "prefill", "tiled"}, (w, fams)
+        kernels = {c["plan"]["kernel"] for c in tune.candidates(16, 1024, 1024, torch.bfloat16, w, False)}
+        if w != torch.bfloat16:
+            assert any(",n256," in k for k in kernels), kernels   # 256 rows per workgroup for int8 / int4
+    assert fra.tune_count() == 0
