@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _OUT = os.path.join(_HERE, "_build", "liboracle.so")
 
-F32, F16, BF16, I8, I4 = 0, 1, 2, 3, 4
+F32, F16, BF16, I8, I4, E4M3 = 0, 1, 2, 3, 4, 5
+E4M3_MAX = 448.0
 I4_GROUP = 128
 NORM = {"none": 0, "rms": 1, "layer": 2}
 ACT = {"none": 0, "swiglu": 1, "gelu_tanh": 2}
@@ -85,6 +86,12 @@ def load(path: Optional[str] = None):
     lib.or_dequant_i4.restype = ci
     lib.or_i4_value.argtypes = [vp, i64]
     lib.or_i4_value.restype = ci
+    lib.or_e4m3_value.argtypes = [ci]
+    lib.or_e4m3_value.restype = dbl
+    lib.or_e4m3_encode.argtypes = [dbl]
+    lib.or_e4m3_encode.restype = ci
+    lib.or_quant_rows_e4m3.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.or_quant_rows_e4m3.restype = ci
     lib.or_add_norm.argtypes = [vp, vp, vp, vp, ci, ci, dbl, i64, i64, vp, vp, vp]
     lib.or_add_norm.restype = ci
     lib.or_matmul_nt.argtypes = [vp, vp, ci, vp, i64, i64, i64, vp]
@@ -124,6 +131,8 @@ def _raw(t):
         return t.numpy(), F32
     if t.dtype == torch.int8:
         return t.numpy(), I8
+    if t.dtype == torch.float8_e4m3fn:       # E4M3 weight codes (R10)
+        return t.view(torch.uint8).numpy(), E4M3
     if t.dtype == torch.uint8:               # int4 weights, two per byte (R9)
         return t.numpy(), I4
     raise TypeError(f"oracle: unsupported dtype {t.dtype}")
@@ -186,6 +195,27 @@ def dequant_i4(q, s):
     bits = np.zeros((N, K), dtype=np.uint16)
     assert load().or_dequant_i4(_ptr(qa), _ptr(sa), N, K, _ptr(w), _ptr(bits)) == 0
     return w, bits
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 code (R10)."""
+    return load().or_e4m3_value(int(code))
+
+
+def e4m3_encode(t: float) -> int:
+    """Nearest E4M3 code of t (ties to the even code, magnitudes past 448 as 448)."""
+    return load().or_e4m3_encode(float(t))
+
+
+def quant_rows_e4m3(n):
+    """Per-token E4M3 quantisation of float64 rows n [M, K] (R10):
+    (codes uint8 [M, K], a = e4m3(code) * s_a float64 [M, K], s_a float64 [M])."""
+    n = np.ascontiguousarray(n, dtype=np.float64)
+    M, K = n.shape
+    codes = np.zeros((M, K), dtype=np.uint8)
+    a, s = _f64((M, K)), _f64((M,))
+    assert load().or_quant_rows_e4m3(_ptr(n), M, K, _ptr(codes), _ptr(a), _ptr(s)) == 0
+    return codes, a, s
 
 
 def add_norm(x, r, gamma, beta, norm: str, eps: float):

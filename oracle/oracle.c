@@ -53,8 +53,21 @@
  *     roundings of R8.  A zero product is +0: the value is exactly zero (the
  *     format defines no signed zero; only a zero scale with a negative q
  *     could give an IEEE -0).
+ *  R10 FP8 W8A8 ([Q]: the full-FP8 configuration, whose activation range is
+ *     taken from the data at run time rather than from a calibration): the
+ *     weights are E4M3 codes [N, K] with one fp32 scale per output row,
+ *     w = e4m3(code) * s[row] (exact in double); the activations are
+ *     quantised per token at run time from the unrounded normalised row n:
+ *     amax = max_k |n[k]|, s_a = amax / 448, t = n * (448 / amax) clamped to
+ *     [-448, 448], code = E4M3 nearest (ties to the even code), a =
+ *     e4m3(code) * s_a; a row with amax = 0 quantises to zeros.  The product
+ *     then uses a and w as above.  E4M3 here is the OCP 8-bit format with
+ *     1 sign, 4 exponent (bias 7) and 3 mantissa bits: exponent field 0
+ *     holds the subnormals m * 2^-9, there are no infinities, S.1111.111 is
+ *     NaN and 448 is the largest finite value.
  *  [Q] "TensorRT-LLM 深度工程实践…", §3.3 FP4/FP8 动态量化加速: the W4A16
- *      (AWQ/GPTQ) configuration with group size 128 and no zero point.
+ *      (AWQ/GPTQ) configuration with group size 128 and no zero point, and
+ *      the W8A8 FP8 configuration with online activation ranges.
  */
 #include <math.h>
 #include <stdint.h>
@@ -64,7 +77,8 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_I4 = 4 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_I4 = 4, OR_E4M3 = 5 };
+enum { OR_E4M3_MAX = 448 };
 enum { OR_I4_GROUP = 128 };
 enum { OR_NORM_NONE = 0, OR_NORM_RMS = 1, OR_NORM_LAYER = 2 };
 enum { OR_ACT_NONE = 0, OR_ACT_SWIGLU = 1, OR_ACT_GELU_TANH = 2 };
@@ -206,6 +220,58 @@ int or_dequant_i4(const uint8_t *q, const float *s, int64_t N, int64_t K,
 }
 
 /* ---------------------------------------------------------------------------
+ * E4M3 (R10).
+ * ------------------------------------------------------------------------- */
+/* value of an E4M3 code (NaN for S.1111.111) */
+double or_e4m3_value(int code) {
+    code &= 0xFF;
+    const int e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    /* normal: (1 + m/8) 2^(e-7) = (8 + m) 2^(e-10); subnormal: m 2^-9 */
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return (code & 0x80) ? -v : v;
+}
+
+/* nearest E4M3 code of t, ties to the even code; magnitudes beyond 448 are
+ * taken as 448 (the quantiser clamps before it rounds) */
+int or_e4m3_encode(double t) {
+    const int sign = signbit(t) ? 0x80 : 0;
+    double a = fabs(t);
+    if (a > (double)OR_E4M3_MAX) a = (double)OR_E4M3_MAX;
+    if (a < ldexp(1.0, -6))                       /* below the smallest normal: */
+        return sign | (int)nearbyint(ldexp(a, 9)); /* a multiple of 2^-9; 8 is the smallest normal */
+    int e;
+    const double f = frexp(a, &e);                /* a = f 2^e, f in [0.5, 1) */
+    double q = nearbyint(16.0 * f - 8.0);         /* 3 mantissa bits, exact argument */
+    int field = e - 1 + 7;
+    if (q == 8.0) { q = 0.0; field += 1; }
+    return sign | (field << 3) | (int)q;
+}
+
+/* per-token quantisation of the rows of n [M, K] (R10): codes (or NULL),
+ * a = e4m3(code) * s_a (or NULL; may be n itself) and s_a [M] (or NULL) */
+int or_quant_rows_e4m3(const double *n, int64_t M, int64_t K, uint8_t *codes, double *a,
+                       double *s_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            if (fabs(n[m * K + k]) > amax) amax = fabs(n[m * K + k]);
+        const double s = amax / OR_E4M3_MAX, inv = amax > 0.0 ? OR_E4M3_MAX / amax : 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double t = n[m * K + k] * inv;
+            if (t > OR_E4M3_MAX) t = OR_E4M3_MAX;
+            if (t < -OR_E4M3_MAX) t = -OR_E4M3_MAX;
+            const int c = or_e4m3_encode(t);
+            if (codes) codes[m * K + k] = (uint8_t)c;
+            if (a) a[m * K + k] = or_e4m3_value(c) * s;
+        }
+        if (s_out) s_out[m] = s;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Residual add and row normalisation, one token row at a time ([D], [I]).
  *  h = x + r                                        (R1; r may be NULL)
  *  RMS:   n = h / sqrt(sum(h^2)/K + eps) * gamma    (R2)
@@ -261,9 +327,9 @@ int or_add_norm(const void *x, const void *r, const void *gamma, const void *bet
 
 /* ---------------------------------------------------------------------------
  * The projection product acc[m, j] = sum_k a[m, k] * w[j, k]  ([D]).
- * w is [N, K] with K contiguous, in its stored dtype; int8 and int4 weights
- * go through the dequantisations above (R8, R9; w_scale is [N] or
- * [N, K/128]).  Each weight row is decoded once into a double buffer and then
+ * w is [N, K] with K contiguous, in its stored dtype; int8, int4 and E4M3
+ * weights go through the dequantisations above (R8, R9, R10; w_scale is [N]
+ * or [N, K/128]).  Each weight row is decoded once into a double buffer and then
  * used for every token row.
  * ------------------------------------------------------------------------- */
 int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scale,
@@ -275,6 +341,9 @@ int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scal
         if (!wr) { bad = 1; continue; }
         if (wdtype == OR_I8)
             or_dequant_i8((const int8_t *)w + j * K, w_scale + j, 1, K, wr, NULL);
+        else if (wdtype == OR_E4M3)
+            for (int64_t k = 0; k < K; ++k)
+                wr[k] = or_e4m3_value(((const uint8_t *)w)[j * K + k]) * (double)w_scale[j];
         else if (wdtype == OR_I4) {
             if (or_dequant_i4((const uint8_t *)w + j * (K / 2), w_scale + j * (K / OR_I4_GROUP), 1, K, wr, NULL))
                 bad = 1;
@@ -293,13 +362,17 @@ int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scal
 /* ---------------------------------------------------------------------------
  * Full calls.
  * ------------------------------------------------------------------------- */
+/* the GEMM A operand: the normalised rows rounded to the activation dtype
+ * (reading A), quantised per token for E4M3 weights (R10), or unrounded */
 static double *prologue(const void *x, const void *r, const void *gamma, const void *beta,
                         int act, int norm, double eps, int64_t M, int64_t K,
-                        double *h_out, int rounded) {
+                        double *h_out, int rounded, int wdtype) {
     double *a = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
     if (!a) return NULL;
-    int rc = rounded ? or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, NULL, a)
-                     : or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, a, NULL);
+    const int fp8 = rounded && wdtype == OR_E4M3;
+    int rc = rounded && !fp8 ? or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, NULL, a)
+                             : or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, a, NULL);
+    if (!rc && fp8) rc = or_quant_rows_e4m3(a, M, K, NULL, a, NULL);
     if (rc) { free(a); return NULL; }
     return a;
 }
@@ -313,7 +386,7 @@ int or_add_norm_qkv(const void *x, const void *r, const void *gamma, const void 
                     int64_t M, int64_t K, int64_t H, int64_t Hkv, int64_t D,
                     double *q, double *k, double *v, double *h_out, int rounded) {
     int64_t N = (H + 2 * Hkv) * D, nq = H * D, nkv = Hkv * D;
-    double *a = prologue(x, r, gamma, beta, act, norm, eps, M, K, h_out, rounded);
+    double *a = prologue(x, r, gamma, beta, act, norm, eps, M, K, h_out, rounded, wdtype);
     double *acc = (double *)malloc(sizeof(double) * (size_t)(M * N > 0 ? M * N : 1));
     if (!a || !acc) { free(a); free(acc); return -1; }
     if (or_matmul_nt(a, w, wdtype, w_scale, M, K, N, acc)) { free(a); free(acc); return -1; }
@@ -340,7 +413,7 @@ int or_gateup_act(const void *x, const void *r, const void *gamma, const void *b
                   int64_t M, int64_t K, int64_t F, int actfn,
                   double *out, double *h_out, int rounded) {
     int64_t N = actfn == OR_ACT_SWIGLU ? 2 * F : F;
-    double *a = prologue(x, r, gamma, beta, act, norm, eps, M, K, h_out, rounded);
+    double *a = prologue(x, r, gamma, beta, act, norm, eps, M, K, h_out, rounded, wdtype);
     double *acc = (double *)malloc(sizeof(double) * (size_t)(M * N > 0 ? M * N : 1));
     if (!a || !acc) { free(a); free(acc); return -1; }
     if (or_matmul_nt(a, w, wdtype, w_scale, M, K, N, acc)) { free(a); free(acc); return -1; }
@@ -367,8 +440,9 @@ int or_gateup_act(const void *x, const void *r, const void *gamma, const void *b
 /* Down projection with the residual add ([T] below):
  * out[m, c] = residual[m, c] + bias[c] + sum_k a[m, k] * w[c, k], in double.
  * a is [M, K] in the activation dtype and used as stored (no norm, no
- * rounding: it is already an activation-dtype tensor); w is [N, K] as for the
- * other products (R8, R9); residual and bias may be NULL.
+ * rounding: it is already an activation-dtype tensor; with E4M3 weights it
+ * is quantised per token, R10); w is [N, K] as for the other products (R8,
+ * R9, R10); residual and bias may be NULL.
  * [T] "TensorRT-LLM 深度工程实践…", §4.1: the MLP's gate/up projection
  *     followed by the down projection; "TRT-LLM deep dive", 构建阶段详解 §3:
  *     the Add folded into the neighbouring kernel. */
@@ -378,6 +452,7 @@ int or_down_residual(const void *a, int act, const void *w, int wdtype, const fl
     double *ad = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
     if (!ad) return -1;
     or_decode_array(a, act, M * K, ad);
+    if (wdtype == OR_E4M3) or_quant_rows_e4m3(ad, M, K, NULL, ad, NULL);   /* R10 */
     if (or_matmul_nt(ad, w, wdtype, w_scale, M, K, N, out)) { free(ad); return -1; }
     for (int64_t m = 0; m < M; ++m)
         for (int64_t c = 0; c < N; ++c) {

@@ -582,4 +582,113 @@ def pin_rounded_vs_unrounded_reading():
     assert not np.array_equal(oa["out"], ob["out"])
 
 
+# ---------------------------------------------------------------------------
+# E4M3 weights and per-token activation quantisation (R10)
+# ---------------------------------------------------------------------------
+def _e4m3_torch(codes) -> np.ndarray:
+    """Values of E4M3 codes through torch's float8_e4m3fn dtype (a library cast)."""
+    c = torch.as_tensor(np.asarray(codes, dtype=np.uint8))
+    return c.view(torch.float8_e4m3fn).double().numpy()
+
+
+def _finite_e4m3():
+    """(codes, values) of every finite E4M3 code, from torch's decoding."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    return codes, _e4m3_torch(codes)
+
+
+def pin_e4m3_decode_exhaustive():
+    vals = np.array([oracle.e4m3_value(c) for c in range(256)])
+    ref = _e4m3_torch(np.arange(256))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(vals), nan) and nan.sum() == 2          # S.1111.111 only
+    assert np.array_equal(vals[~nan], ref[~nan])
+    # landmarks of the format: largest finite, smallest normal and subnormal, one
+    assert vals[0x7E] == 448.0 and vals[0xFE] == -448.0
+    assert vals[0x08] == 2.0 ** -6 and vals[0x01] == 2.0 ** -9 and vals[0x38] == 1.0
+    # positive codes increase strictly with their value
+    assert np.all(np.diff(vals[:0x7F]) > 0)
+
+
+def pin_e4m3_encode_nearest_even():
+    codes, vals = _finite_e4m3()
+    pos = np.sort(np.unique(vals[vals >= 0]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = _rng(51)
+    ts = np.concatenate([pos, -pos, mids, -mids, rng.uniform(-448, 448, 3000),
+                         rng.standard_normal(2000) * 2.0 ** rng.integers(-12, 6, 2000)])
+    got = np.array([oracle.e4m3_encode(t) for t in ts], dtype=np.uint8)
+    # brute force: the nearest finite value, ties to the code with an even
+    # mantissa, the sign of t kept
+    for t, c in zip(ts, got):
+        d = np.abs(vals - t)
+        cand = codes[d == d.min()]
+        cand = cand[(cand & 0x80) == (0x80 if np.signbit(t) else 0)] if len(cand) > 1 else cand
+        if len(cand) > 1:
+            cand = cand[(cand & 1) == 0]
+        assert c == cand[0], (t, c, cand)
+    # torch's cast agrees inside the range; past 448 the encoder saturates
+    inr = np.abs(ts) <= 448
+    assert np.array_equal(got[inr], torch.tensor(ts[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert oracle.e4m3_encode(1e6) == 0x7E and oracle.e4m3_encode(-470.0) == 0xFE
+
+
+def pin_e4m3_row_quantisation():
+    rng = _rng(52)
+    M, K = 5, 96
+    n = rng.standard_normal((M, K)) * rng.uniform(0.01, 30, (M, 1))
+    n[3] = 0.0                                                           # a zero row
+    codes, a, s = oracle.quant_rows_e4m3(n)
+    amax = np.abs(n).max(1)
+    assert np.array_equal(s, amax / 448.0)
+    # the independent route: scale by 448 / amax, clamp, torch's cast, decode
+    for m in range(M):
+        if amax[m] == 0:
+            assert not codes[m].any() and not a[m].any()
+            continue
+        t = np.clip(n[m] * (448.0 / amax[m]), -448, 448)
+        ref = torch.tensor(t).to(torch.float8_e4m3fn)
+        assert np.array_equal(codes[m], ref.view(torch.uint8).numpy())
+        assert np.array_equal(a[m], ref.double().numpy() * s[m])
+        # the largest magnitude lands on +-448 exactly
+        k = np.abs(n[m]).argmax()
+        assert abs(oracle.e4m3_value(codes[m, k])) == 448.0
+    # a power-of-two rescale of a row keeps its codes and scales s_a
+    c2, a2, s2 = oracle.quant_rows_e4m3(n * 2.0 ** 7)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, s * 2.0 ** 7)
+    # relative error of a quantised element: at most half a step of 3 mantissa bits
+    big = np.abs(n) >= amax[:, None] * 2.0 ** -6
+    assert np.all(np.abs(a - n)[big] <= np.abs(n)[big] * 2.0 ** -4)
+
+
+def pin_fp8_projection():
+    rng = _rng(53)
+    M, K, F = 3, 128, 6
+    x, r, g = _tiny(torch.bfloat16, M, K, seed=54)
+    wf = rng.standard_normal((2 * F, K)) / 8
+    s_w = (np.abs(wf).max(1) / 448.0).astype(np.float32)
+    wq = torch.tensor(wf / s_w[:, None]).to(torch.float8_e4m3fn)
+    w_val = wq.double().numpy() * s_w.astype(np.float64)[:, None]
+    _, n, _ = oracle.add_norm(x, r, g, None, "rms", 1e-5)
+    amax = np.abs(n).max(1, keepdims=True)
+    a = torch.tensor(np.clip(n * (448.0 / amax), -448, 448)).to(torch.float8_e4m3fn).double().numpy() * (amax / 448.0)
+    acc = a @ w_val.T
+    o = oracle.gateup_act(x, r, g, None, "rms", 1e-5, wq, torch.from_numpy(s_w), None, F, "swiglu")
+    ref = acc[:, :F] / (1 + np.exp(-acc[:, :F])) * acc[:, F:]
+    _close(o["out"], ref, rtol=1e-12, atol=1e-14, what="fp8 swiglu")
+    # the QKV call takes the same A operand
+    oq = oracle.add_norm_qkv(x, r, g, None, "rms", 1e-5, wq[:8].contiguous(), torch.from_numpy(s_w[:8]), None,
+                             2, 1, 2)
+    _close(np.concatenate([oq["q"].reshape(M, -1), oq["k"].reshape(M, -1), oq["v"].reshape(M, -1)], 1),
+           acc[:, :8], rtol=1e-12, atol=1e-14, what="fp8 qkv")
+    # the down projection quantises its input rows the same way
+    ad = _t(rng.standard_normal((M, K)), torch.bfloat16)
+    res = _t(rng.standard_normal((M, 2 * F)), torch.bfloat16)
+    av = ad.double().numpy()
+    am = np.abs(av).max(1, keepdims=True)
+    aq = torch.tensor(np.clip(av * (448.0 / am), -448, 448)).to(torch.float8_e4m3fn).double().numpy() * (am / 448.0)
+    _close(oracle.down_residual(ad, wq, torch.from_numpy(s_w), None, res), res.double().numpy() + aq @ w_val.T,
+           rtol=1e-12, atol=1e-14, what="fp8 down")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -53,6 +53,17 @@ MUTANTS = {
     "down bias shifted": ("if (bias) out[m * N + c] += or_load(bias, act, c);",
                           "if (bias) out[m * N + c] += or_load(bias, act, (c + 1) % N);"),
     "int4 signed zero kept": ("if (w == 0.0) w = 0.0;   /* +0 (R9) */", "(void)0;"),
+    "e4m3 exponent bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
+    "e4m3 subnormal step": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "e4m3 ties away": ("double q = nearbyint(16.0 * f - 8.0);", "double q = round(16.0 * f - 8.0);"),
+    "e4m3 no mantissa carry": ("if (q == 8.0) { q = 0.0; field += 1; }", "(void)0;"),
+    "fp8 activation scale dropped": ("if (a) a[m * K + k] = or_e4m3_value(c) * s;",
+                                     "if (a) a[m * K + k] = or_e4m3_value(c);"),
+    "fp8 activations not quantised": ("if (!rc && fp8) rc = or_quant_rows_e4m3(a, M, K, NULL, a, NULL);", "(void)0;"),
+    "fp8 weight scale dropped": ("wr[k] = or_e4m3_value(((const uint8_t *)w)[j * K + k]) * (double)w_scale[j];",
+                                 "wr[k] = or_e4m3_value(((const uint8_t *)w)[j * K + k]);"),
+    "fp8 down input not quantised": ("if (wdtype == OR_E4M3) or_quant_rows_e4m3(ad, M, K, NULL, ad, NULL);",
+                                     "(void)0;"),
 }
 
 
