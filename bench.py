@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 MFMA
 MALL_BYTES = 256 << 20
 
 
@@ -48,11 +49,11 @@ def algo_bytes(wl, call: str) -> int:
     written once; the normalised rows and the GEMM intermediates are not
     counted (the fusion keeps them on chip)."""
     ea = {"f32": 4, "f16": 2, "bf16": 2}[wl.act]
-    ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i4": 0.5}[wl.wdt]
+    ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i4": 0.5, "e4m3": 1}[wl.wdt]
     if call == "down":                               # a [M, ffn], residual and out [M, hidden], weights
         N, K = wl.hidden, wl.ffn
         b = wl.M * K * ea + 2 * wl.M * N * ea + int(N * K * ew)
-        if wl.wdt == "i8":
+        if wl.wdt in ("i8", "e4m3"):
             b += 4 * N
         if wl.wdt == "i4":
             b += 4 * N * (K // 128)
@@ -69,7 +70,7 @@ def algo_bytes(wl, call: str) -> int:
         b += int(N * K * ew) + M * wl.ffn * ea       # weights, out
         if wl.bias_std is not None:
             b += N * ea
-    if wl.wdt == "i8":
+    if wl.wdt in ("i8", "e4m3"):
         b += 4 * N                                   # per-row scales
     if wl.wdt == "i4":
         b += 4 * N * (K // 128)                      # per-row, per-128-k group scales
@@ -100,7 +101,9 @@ class Runner:
             s = dict(self.base)
             for k in list(s):
                 if k.startswith("w_"):
-                    s[k] = self.base[k].roll(i, 0).contiguous()   # distinct buffers, same statistics
+                    w = self.base[k]                              # distinct buffers, same statistics
+                    s[k] = w.view(torch.uint8).roll(i, 0).contiguous().view(w.dtype) if w.element_size() == 1 \
+                        else w.roll(i, 0).contiguous()
             self.sets.append(s)
         import fusion_residual_add_amd as fra
         self.fra = fra
@@ -218,6 +221,12 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::stats_kernel<(\d), \d+>", cxx)
     if m:
         return f"stats_kernel<{_ACT[m.group(1)]}>"
+    m = re.search(r"fp::quant8_kernel<(\d), \d+>", cxx)
+    if m:
+        return f"quant8_kernel<{_ACT[m.group(1)]}>"
+    m = re.search(r"fp::gemm8_kernel<(\d), (\d)>", cxx)
+    if m:
+        return f"gemm8_kernel<{_ACT[m.group(1)]},{_EPI[m.group(2)]}>"
     return cxx
 
 
@@ -333,8 +342,10 @@ def all_configs(steps: int) -> None:
             prof = profile_call(run, call, 20)
             total = sum(prof.values())
             b, f = algo_bytes(wl, call), flops(wl, call)
-            mem_bound = f / b < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-            peak = HBM_PEAK_GBS if mem_bound else (MFMA_BF16_PEAK_TFLOPS if wl.act != "f32" else 157.3)
+            mfma_peak = MFMA_FP8_PEAK_TFLOPS if wl.wdt == "e4m3" else \
+                MFMA_BF16_PEAK_TFLOPS if wl.act != "f32" else 157.3
+            mem_bound = f / b < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+            peak = HBM_PEAK_GBS if mem_bound else mfma_peak
             rate = b / (total * 1e-3) / 1e9 if mem_bound else f / (total * 1e-3) / 1e12
             calls[call] = {"kernels_us": {k: round(v * 1e3, 2) for k, v in prof.items()},
                            "bound": "hbm" if mem_bound else "mfma",

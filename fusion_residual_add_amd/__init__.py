@@ -23,7 +23,8 @@ __all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_down_residual", "fus
 
 # torch.uint8 weights are int4 pairs (two values per byte, even k in the low nibble)
 _DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
-       torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8, torch.uint8: _lib.FP_I4}
+       torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8, torch.uint8: _lib.FP_I4,
+       torch.float8_e4m3fn: _lib.FP_E4M3}
 
 
 def _check_weight(w: torch.Tensor, w_scale: Optional[torch.Tensor], Nw: int, K: int, name: str):
@@ -31,7 +32,7 @@ def _check_weight(w: torch.Tensor, w_scale: Optional[torch.Tensor], Nw: int, K: 
     want = (Nw, K // 2) if w.dtype == torch.uint8 else (Nw, K)
     if tuple(w.shape) != want:
         raise ValueError(f"{name} has shape {tuple(w.shape)}, expected {want}")
-    if w.dtype == torch.int8 and w_scale is not None and tuple(w_scale.shape) != (Nw,):
+    if w.dtype in (torch.int8, torch.float8_e4m3fn) and w_scale is not None and tuple(w_scale.shape) != (Nw,):
         raise ValueError(f"w_scale has shape {tuple(w_scale.shape)}, expected {(Nw,)}")
     if w.dtype == torch.uint8 and w_scale is not None and tuple(w_scale.shape) != (Nw, K // 128):
         raise ValueError(f"w_scale has shape {tuple(w_scale.shape)}, expected {(Nw, K // 128)}")

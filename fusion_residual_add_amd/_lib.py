@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfusedproj.so")
 
-FP_F32, FP_F16, FP_BF16, FP_I8, FP_I4 = 0, 1, 2, 3, 4
+FP_F32, FP_F16, FP_BF16, FP_I8, FP_I4, FP_E4M3 = 0, 1, 2, 3, 4, 5
 FP_NORM = {"none": 0, "rms": 1, "layer": 2}
 FP_ACT = {"none": 0, "swiglu": 1, "gelu_tanh": 2}
 STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_ALIAS",

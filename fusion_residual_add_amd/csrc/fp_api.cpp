@@ -27,7 +27,7 @@ fp_status fail(fp_status s, const char *fmt, ...) {
     return s;
 }
 
-int act_size(int dt) { return dt == FP_F32 ? 4 : dt == FP_I8 ? 1 : 2; }
+int act_size(int dt) { return dt == FP_F32 ? 4 : (dt == FP_I8 || dt == FP_E4M3) ? 1 : 2; }
 
 int act_code(fp_dtype d) {
     return d == FP_F32 ? fp::ACT_F32 : d == FP_F16 ? fp::ACT_F16 : fp::ACT_BF16;
@@ -37,7 +37,8 @@ int act_code(fp_dtype d) {
 // launch plan
 // ---------------------------------------------------------------------------
 struct Plan {
-    int family = 0;           // 0 tiled (128 x 128), 1 stream (decode), 2 prefill (128 x 512)
+    int family = 0;           // 0 tiled (128 x 128), 1 stream (decode), 2 prefill (128 x 512),
+                              // 3 FP8 (per-token E4M3 quantisation, then the 128 x 128 FP8 GEMM)
     int tile = 0;             // tiled: TileCfg
     fp::StreamCfg sc{1, 2, 8};
     int tiles_m = 0, tiles_n = 0, splits = 1;
@@ -47,6 +48,7 @@ struct Plan {
     size_t stats_off = 0, ctr_off = 0, part_off = 0, total = 0;
     bool deq = false;         // int4 weights staged as bf16 in the workspace first
     size_t deq_off = 0;
+    size_t q_off = 0, qs_off = 0;   // FP8: activation codes [M, K] and row scales [M]
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -123,6 +125,34 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
 Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu) {
     Plan p;
     const Knobs kb = knobs_for(M, K, Nw, act, wdt, swiglu);
+    if (wdt == FP_E4M3) {
+        // FP8 W8A8: one family whatever the token count.  128 x 128 tiles
+        // (SwiGLU: 64 gate + 64 up rows), two workgroups per CU; K is split
+        // while fewer than two rounds of workgroups would run, at most 8 ways
+        // and at least 4 K steps of 128 per split.
+        p.family = 3;
+        p.tiles_m = (int)((M + 127) / 128);
+        p.tiles_n = (int)(swiglu ? (Nw / 2 + 63) / 64 : (Nw + 127) / 128);
+        p.tile_elems = 128 * 128;
+        const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n, ksteps = K / 128;
+        int64_t s = tiles > 0 ? 512 / tiles : 1;
+        const int64_t cap = ksteps / 4 < 8 ? ksteps / 4 : 8;
+        if (s > cap) s = cap;
+        if (kb.splits > 0) s = kb.splits < ksteps ? kb.splits : ksteps;
+        if (s < 1) s = 1;
+        p.splits = p.slots = (int)s;
+        size_t off = 0;
+        p.ctr_off = off;
+        if (p.slots > 1) off = align256(off + (size_t)tiles * 4);
+        p.part_off = off;
+        if (p.slots > 1) off = align256(off + (size_t)tiles * p.slots * p.tile_elems * 4);
+        p.q_off = off;
+        off = align256(off + (size_t)M * (size_t)K);
+        p.qs_off = off;
+        off = align256(off + (size_t)M * 4);
+        p.total = off;
+        return p;
+    }
     const bool i4 = wdt == FP_I4;
     const bool stream_elig = act != FP_F32 && M <= 64 && K % 256 == 0;
     const bool prefill_elig = act != FP_F32 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32);
@@ -305,9 +335,10 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 fp_status check_dtypes(fp_dtype act, fp_dtype wdt, fp_dtype odt) {
     if (act != FP_F32 && act != FP_F16 && act != FP_BF16)
         return fail(FP_E_DTYPE, "act_dtype %d not in {F32, F16, BF16}", (int)act);
-    if (!(wdt == act || ((wdt == FP_I8 || wdt == FP_I4) && act == FP_BF16)))
-        return fail(FP_E_DTYPE, "w_dtype %d must equal act_dtype %d, or be I8 / I4 with BF16 activations",
-                    (int)wdt, (int)act);
+    if (!(wdt == act || ((wdt == FP_I8 || wdt == FP_I4) && act == FP_BF16) ||
+          (wdt == FP_E4M3 && (act == FP_BF16 || act == FP_F16))))
+        return fail(FP_E_DTYPE, "w_dtype %d must equal act_dtype %d, or be I8 / I4 with BF16 activations, "
+                    "or E4M3 with BF16 / F16 activations", (int)wdt, (int)act);
     if (!(odt == act || odt == FP_F32))
         return fail(FP_E_DTYPE, "out_dtype %d must equal act_dtype or be F32", (int)odt);
     return FP_OK;
@@ -374,10 +405,12 @@ fp_status validate_common(const Common &c, const char *wname) {
     if (!c.x && c.M > 0) return fail(FP_E_NULL, "x is NULL");
     if (!c.w) return fail(FP_E_NULL, "%s is NULL", wname);
     if (c.norm != FP_NORM_NONE && !c.gamma) return fail(FP_E_NULL, "gamma is NULL but norm is not NONE");
-    if ((c.wdt == FP_I8 || c.wdt == FP_I4) && !c.w_scale)
-        return fail(FP_E_NULL, "w_scale is NULL for int8 / int4 weights");
-    if (c.wdt == FP_I4 && c.K % 128 != 0)
-        return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 weights", (long long)c.K);
+    if ((c.wdt == FP_I8 || c.wdt == FP_I4 || c.wdt == FP_E4M3) && !c.w_scale)
+        return fail(FP_E_NULL, "w_scale is NULL for int8 / int4 / E4M3 weights");
+    if ((c.wdt == FP_I4 || c.wdt == FP_E4M3) && c.K % 128 != 0)
+        return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 / E4M3 weights", (long long)c.K);
+    if (c.wdt == FP_E4M3 && (c.M * c.K >= (int64_t(1) << 32) || c.Nw * c.K >= (int64_t(1) << 32)))
+        return fail(FP_E_SHAPE, "E4M3: M * hidden and the weight's rows * hidden must be below 2^32");
     if (!(c.eps >= 0.0f) || c.eps > 1e30f) return fail(FP_E_ARG, "eps must be a finite value >= 0");
     const void *ptrs[] = {c.x, c.residual, c.h_out, c.gamma, c.beta, c.w, c.w_scale, c.bias, c.ws};
     const char *names[] = {"x", "residual", "h_out", "gamma", "beta", wname, "w_scale", "bias", "workspace"};
@@ -393,13 +426,60 @@ void add_inputs(const Common &c, std::vector<Range> &ins, const char *wname) {
     if (c.gamma && c.norm != FP_NORM_NONE) ins.push_back(rng("gamma", c.gamma, c.K * ea));
     if (c.beta && c.norm == FP_NORM_LAYER) ins.push_back(rng("beta", c.beta, c.K * ea));
     ins.push_back(rng(wname, c.w, c.wdt == FP_I4 ? c.Nw * c.K / 2 : c.Nw * c.K * ew));
-    if (c.w_scale && c.wdt == FP_I8) ins.push_back(rng("w_scale", c.w_scale, c.Nw * 4));
+    if (c.w_scale && (c.wdt == FP_I8 || c.wdt == FP_E4M3)) ins.push_back(rng("w_scale", c.w_scale, c.Nw * 4));
     if (c.w_scale && c.wdt == FP_I4) ins.push_back(rng("w_scale", c.w_scale, c.Nw * (c.K / 128) * 4));
     if (c.bias) ins.push_back(rng("bias", c.bias, c.Nw * ea));
 }
 
+fp_status run_fp8(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
+    char *ws = (char *)c.ws;
+    const int act = act_code(c.act);
+    unsigned *ctr = plan.slots > 1 ? (unsigned *)(ws + plan.ctr_off) : nullptr;
+    unsigned char *codes = (unsigned char *)(ws + plan.q_off);
+    float *qscale = (float *)(ws + plan.qs_off);
+    fp::StatsArgs sa{};
+    sa.x = c.x;
+    sa.res = c.residual;
+    sa.h_out = c.h_out;
+    sa.norm = (int)c.norm;
+    sa.eps = c.eps;
+    sa.M = c.M;
+    sa.K = c.K;
+    sa.counters = ctr;
+    sa.n_counters = plan.slots > 1 ? plan.tiles_m * plan.tiles_n : 0;
+    sa.gamma = c.gamma;
+    sa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
+    sa.codes = codes;
+    sa.qscale = qscale;
+    {
+        ProfScope ps(fp::quant8_kernel_name(act), c.stream);
+        hipError_t e = fp::launch_quant8(act, sa, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "quant8_kernel launch");
+    }
+    pa.x = codes;
+    pa.a_scale = qscale;
+    pa.w = c.w;
+    pa.w_scale = c.w_scale;
+    pa.bias = c.bias;
+    pa.out_f32 = c.odt == FP_F32;
+    pa.M = c.M;
+    pa.K = c.K;
+    pa.Nw = c.Nw;
+    pa.tiles_m = plan.tiles_m;
+    pa.tiles_n = plan.tiles_n;
+    pa.splits = plan.splits;
+    pa.slots = plan.slots;
+    pa.partials = plan.slots > 1 ? (float *)(ws + plan.part_off) : nullptr;
+    pa.counters = ctr;
+    ProfScope ps(fp::gemm8_kernel_name(act, pa.epi), c.stream);
+    hipError_t e = fp::launch_gemm8(act, pa, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm8_kernel launch");
+    return FP_OK;
+}
+
 fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     if (c.M == 0) return FP_OK;
+    if (plan.family == 3) return run_fp8(c, plan, pa);
     char *ws = (char *)c.ws;
     const int act = act_code(c.act);
     float2 *stats = c.norm != FP_NORM_NONE ? (float2 *)(ws + plan.stats_off) : nullptr;
@@ -486,7 +566,7 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype ac
                           fp_dtype w_dtype) {
     if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0) return 0;
     if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
-    if (w_dtype == FP_I4 && hidden % 128 != 0) return 0;
+    if ((w_dtype == FP_I4 || w_dtype == FP_E4M3) && hidden % 128 != 0) return 0;
     if (M == 0) return 0;
     const size_t a = make_plan(M, hidden, n_cols, act_dtype, w_dtype, false).total;
     const size_t b = make_plan(M, hidden, n_cols, act_dtype, w_dtype, true).total;
@@ -660,9 +740,17 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     if ((int)act < 0 || (int)act > 2) return fail(FP_E_ARG, "act = %d", (int)act);
     const fp_status st = check_dtypes(act_dtype, w_dtype, act_dtype);
     if (st != FP_OK) return st;
-    if (w_dtype == FP_I4 && hidden % 128 != 0)
-        return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 weights", (long long)hidden);
+    if ((w_dtype == FP_I4 || w_dtype == FP_E4M3) && hidden % 128 != 0)
+        return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 / E4M3 weights", (long long)hidden);
     const Plan p = make_plan(M, hidden, n_cols, act_dtype, w_dtype, act == FP_ACT_SWIGLU);
+    if (p.family == 3) {
+        const int a8 = act_code(act_dtype);
+        const int e8 = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
+        snprintf(buf, cap, "family=fp8 kernel=%s grid=%lld splits=%d slots=%d workspace=%zu prep=%s",
+                 fp::gemm8_kernel_name(a8, e8), (long long)p.tiles_m * p.tiles_n * p.splits, p.splits, p.slots,
+                 M == 0 ? (size_t)0 : p.total, fp::quant8_kernel_name(a8));
+        return FP_OK;
+    }
     const int a = act_code(act_dtype);
     const bool wi8 = w_dtype == FP_I8;
     const int wq = wi8 ? 1 : (w_dtype == FP_I4 && !p.deq) ? 2 : 0;

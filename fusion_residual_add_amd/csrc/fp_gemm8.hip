@@ -1,0 +1,305 @@
+// FP8 (W8A8, E4M3) projection kernel of libfusedproj (gfx950): the product of
+// the per-token quantised activation rows (quant8_kernel) with E4M3 weights on
+// the double-rate v_mfma_f32_32x32x64_f8f6f4, then the same epilogues as the
+// 16-bit kernels ("TensorRT-LLM 深度工程实践…", §3.3: the full-FP8 configuration
+// with activation ranges taken online; §2.3 for the epilogues).
+//
+//   y[m, c] = (sum_k e4m3(a[m, k]) e4m3(w[c, k])) * a_scale[m] * w_scale[c]
+//             (+ bias[c]), then the GQA split / SwiGLU / tanh-GELU / residual.
+//
+// One workgroup computes a 128 (tokens) x 128 (weight rows) tile with 4 waves
+// in a 2 x 2 layout, each wave 64 x 64 as 2 x 2 fragments of 32 x 32 with fp32
+// accumulators.  For SwiGLU the 128 weight rows are 64 gate rows and the 64
+// matching up rows, and each wave holds a gate and an up fragment of the same
+// columns, so SiLU(g) * u is formed in registers.  K advances 128 codes (128
+// bytes) per step through two LDS stages of A and B (16 KB each), both loaded
+// straight from HBM / L2 into LDS (buffer_load ... lds, 16 bytes per lane,
+// 16-byte chunks XOR-swizzled by row); 64 KB of LDS, two workgroups per CU.
+// The quantised activations are read as 1-byte codes: the per-token scale
+// needs the whole normalised row (its amax) before any element is coded, so
+// the quantisation runs in the kernel before this one and writes the codes
+// once (half the bytes of the 16-bit rows the other kernels re-read per
+// column tile).
+#include "fp_device.hpp"
+
+namespace fp {
+
+namespace g8 {
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int TILE = BM * BK;   // 16 KB per operand and stage
+// swizzled byte offset of 16-byte chunk c (0..7) of tile row r
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char *lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+#else
+    (void)r, (void)lds, (void)voff, (void)soff;
+#endif
+}
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+}  // namespace g8
+
+template <int ACT, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm8_kernel(ProjArgs p) {
+    using T = Act<ACT>;
+    using namespace g8;
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    __shared__ __attribute__((aligned(16))) unsigned char lA0[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lA1[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lB0[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lB1[TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+
+    // ---- tile: XCD-aware remap, then grouped raster (8 row tiles per group)
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = logical / p.splits, z = logical % p.splits;
+    int tm, tn;
+    {
+        constexpr int GROUP_M = 8;
+        const int group = GROUP_M * p.tiles_n;
+        const int gid = tile / group, first = gid * GROUP_M;
+        const int gsz = min(p.tiles_m - first, GROUP_M);
+        const int in = tile % group;
+        tm = first + in % gsz;
+        tn = in / gsz;
+    }
+    const int KT = (int)(p.K / BK);
+    const int kt0 = (int)((int64_t)KT * z / p.splits);
+    const int kt1 = (int)((int64_t)KT * (z + 1) / p.splits);
+
+    // ---- loads: wave w fills tile rows [32 w, 32 w + 32) of A and of B with
+    // 4 instructions each per stage; lane l of instruction i covers row
+    // 32 w + 8 i + l / 8 at LDS chunk position l % 8, which holds the row's
+    // global chunk (l % 8) ^ (row % 8).  Rows past the operand are clamped to
+    // its last row (they only feed outputs that are not stored), so every
+    // offset stays inside the operand and below 2^32 (checked by the host).
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, (short)0,
+                                                                        (uint32_t)(p.M * p.K), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, (short)0,
+                                                                        (uint32_t)(p.Nw * p.K), 0x00020000);
+    uint32_t a_off[4], b_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 32 * wave + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        int64_t ma = (int64_t)tm * BM + r;
+        ma = ma < p.M ? ma : p.M - 1;
+        int64_t wr;
+        if constexpr (SW) wr = r < 64 ? (int64_t)tn * 64 + r : p.F + (int64_t)tn * 64 + (r - 64);
+        else wr = (int64_t)tn * BN + r;
+        wr = wr < p.Nw ? wr : p.Nw - 1;
+        a_off[i] = (uint32_t)(ma * p.K) + c * 16;
+        b_off[i] = (uint32_t)(wr * p.K) + c * 16;
+    }
+    auto issue = [&](int kt, unsigned char *la, unsigned char *lb) {
+        const uint32_t soff = (uint32_t)kt * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_lds16(ra, la + (4 * wave + i) * 1024, a_off[i], soff);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_lds16(rw, lb + (4 * wave + i) * 1024, b_off[i], soff);
+    };
+
+    // ---- fragments: A rows 64 wm + 32 f + l % 32; B tile rows: SwiGLU the
+    // gate block 32 wn (f = 0) and the matching up block 64 + 32 wn (f = 1),
+    // otherwise 64 wn + 32 f.  Lane l supplies k [64 kb + 32 (l / 32), +32)
+    // of K sub-step kb as two 16-byte chunks (A and B alike, so the k order
+    // inside the operand is the same on both sides).
+    const int fr = lane & 31, kh = lane >> 5;
+    int arow[2], brow[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        arow[f] = 64 * wm + 32 * f + fr;
+        brow[f] = SW ? 64 * f + 32 * wn + fr : 64 * wn + 32 * f + fr;
+    }
+    auto frag = [&](const unsigned char *l, int row, int kb) -> i32x8 {
+        const int c = 4 * kb + 2 * kh;
+        const u32x4 lo = *(const u32x4 *)(l + swz(row, c));
+        const u32x4 hi = *(const u32x4 *)(l + swz(row, c + 1));
+        return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto compute = [&](const unsigned char *la, const unsigned char *lb) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            i32x8 af[2], bf[2];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                af[f] = frag(la, arow[f], kb);
+                bf[f] = frag(lb, brow[f], kb);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)   // formats: 0 = E4M3 for both operands
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0,
+                                                                               0, 0, 0, 0);
+        }
+    };
+    // wait for this wave's loads (the current stage) and LDS reads (the
+    // previous step's fragments), then a workgroup barrier: the stage has
+    // landed for every wave and every wave is done with the other stage.
+    // The empty asm statements keep the compiler from moving memory accesses
+    // across the barrier.
+    auto step_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (0 << 8));
+        __asm__ __volatile__("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ __volatile__("" ::: "memory");
+    };
+
+    // Stage identity alternates; both pointers of a pair come from one
+    // condition, so alias analysis still tells the stages apart and the
+    // fragment reads of one stage do not wait for the loads into the other.
+    // Each step first loads the next stage (past the end: a harmless reload
+    // of the last one, never read), then computes on the current one.
+    if (kt0 < kt1) {
+        issue(kt0, lA0, lB0);
+        for (int kt = kt0; kt < kt1; ++kt) {
+            const bool odd = ((kt - kt0) & 1) != 0;
+            const unsigned char *ca = odd ? lA1 : lA0, *cb = odd ? lB1 : lB0;
+            unsigned char *na = odd ? lA0 : lA1, *nb = odd ? lB0 : lB1;
+            step_sync();
+            issue(kt + 1 < kt1 ? kt + 1 : kt1 - 1, na, nb);
+            compute(ca, cb);
+        }
+        step_sync();   // the last reload has landed before the epilogue reuses the LDS
+    }
+
+    // ---- split K: the last contributor of a tile sums the partials in order
+    if (p.splits > 1) {
+        float flat[64];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) flat[(i * 2 + j) * 16 + e] = acc[i][j][e];
+        if (!splitk_reduce<64>(p, tile, z, p.splits, flat)) return;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = flat[(i * 2 + j) * 16 + e];
+    }
+
+    // ---- epilogue: scales, bias, activation; staged per wave through LDS in
+    // [row][col] order (rows padded by 32 bytes), then stored as runs of 8
+    // columns (16 bytes of 16-bit outputs)
+    constexpr int OUTC = SW ? 32 : 64;          // output columns per wave
+    constexpr int SROW = OUTC * 4 + 32;         // staging row pitch, bytes
+    static_assert(32 * SROW <= TILE, "staging fits one tile buffer");
+    unsigned char *stg = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
+    const int64_t col0 = SW ? (int64_t)tn * 64 + 32 * wn : (int64_t)tn * BN + 64 * wn;
+    const int64_t ncols = SW ? p.F : p.Nw;
+    // per-column weight scale and bias of this lane (SwiGLU: gate, up)
+    float cs[2], cb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int64_t c = SW ? col0 + fr : col0 + 32 * j + fr;
+        c = c < ncols ? c : ncols - 1;
+        const int64_t cw = SW ? c + (j ? p.F : 0) : c;
+        cs[j] = p.w_scale[cw];
+        cb[j] = p.bias ? T::ld(p.bias, cw) : 0.f;
+    }
+    const bool of32 = p.out_f32 != 0;
+    const int esz = of32 ? 4 : 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t mrow0 = (int64_t)tm * BM + 64 * wm + 32 * i;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int rl = 8 * (q >> 2) + 4 * kh + (q & 3);   // 0..31
+            const int64_t mr = mrow0 + rl;
+            const float as = p.a_scale[mr < p.M ? mr : p.M - 1];
+            if constexpr (SW) {
+                const float g = acc[i][0][q] * as * cs[0] + cb[0];
+                const float u = acc[i][1][q] * as * cs[1] + cb[1];
+                *(float *)(stg + rl * SROW + fr * 4) = silu(g) * u;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float y = acc[i][j][q] * as * cs[j] + cb[j];
+                    if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
+                    *(float *)(stg + rl * SROW + (32 * j + fr) * 4) = y;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0);
+        constexpr int RUNS = OUTC / 8;
+#pragma unroll
+        for (int it = 0; it < 32 * RUNS / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int rl = idx / RUNS, ch = idx % RUNS;
+            const int64_t m = mrow0 + rl;
+            const int64_t cg = col0 + ch * 8;
+            const f32x4 v0 = *(const f32x4 *)(stg + rl * SROW + ch * 32);
+            const f32x4 v1 = *(const f32x4 *)(stg + rl * SROW + ch * 32 + 16);
+            if (m >= p.M || cg >= ncols) continue;
+            char *dst;
+            if constexpr (EPI == EPI_QKV) {
+                if (cg < p.nq)              dst = (char *)p.out0 + (m * p.nq + cg) * esz;
+                else if (cg < p.nq + p.nkv) dst = (char *)p.out1 + (m * p.nkv + (cg - p.nq)) * esz;
+                else                        dst = (char *)p.out2 + (m * p.nkv + (cg - p.nq - p.nkv)) * esz;
+            } else {
+                dst = (char *)p.out0 + (m * ncols + cg) * esz;
+            }
+            float y[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            if constexpr (EPI == EPI_LINEAR) {
+                if (p.res_epi) {   // the down projection's residual add (this lane reads what it writes)
+                    float r[8];
+                    T::unpack(*(const u32x4 *)((const char *)p.res_epi + (m * ncols + cg) * 2), r);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] += r[e];
+                }
+            }
+            if (of32) {
+                *(f32x4 *)dst = (f32x4){y[0], y[1], y[2], y[3]};
+                *(f32x4 *)(dst + 16) = (f32x4){y[4], y[5], y[6], y[7]};
+            } else {
+                *(u32x4 *)dst = T::pack(y);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+}
+
+template <int ACT>
+static void launch_gemm8_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    switch (a.epi) {
+    case EPI_QKV:    hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_QKV>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_GELU:   hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_GELU>), dim3(grid), dim3(256), 0, s, a); break;
+    default:         hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_LINEAR>), dim3(grid), dim3(256), 0, s, a); break;
+    }
+}
+
+hipError_t launch_gemm8(int act, const ProjArgs &a, hipStream_t s) {
+    const unsigned grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n * a.splits);
+    if (grid == 0) return hipSuccess;
+    if (act == ACT_F16) launch_gemm8_t<ACT_F16>(a, grid, s);
+    else launch_gemm8_t<ACT_BF16>(a, grid, s);
+    return hipGetLastError();
+}
+
+const char *gemm8_kernel_name(int act, int epi) {
+    static const char *names[2][4] = {
+        {"gemm8_kernel<bf16,qkv>", "gemm8_kernel<bf16,swiglu>", "gemm8_kernel<bf16,gelu>", "gemm8_kernel<bf16,linear>"},
+        {"gemm8_kernel<f16,qkv>", "gemm8_kernel<f16,swiglu>", "gemm8_kernel<f16,gelu>", "gemm8_kernel<f16,linear>"}};
+    return names[act == ACT_F16 ? 1 : 0][epi & 3];
+}
+
+}  // namespace fp

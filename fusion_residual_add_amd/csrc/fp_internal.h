@@ -37,6 +37,7 @@ struct ProjArgs {
     const float *w_scale;   // [Nw] (int8 only)
     const void *bias;       // [Nw] act or null
     const void *res_epi;    // EPI_LINEAR: [M, F] act added to the output (residual stream), or null
+    const float *a_scale;   // E4M3 path: [M] per-token scale of the quantised rows in x
     // epilogue
     int epi;                // EpiKind
     int out_f32;            // 1: store fp32, 0: store act dtype
@@ -64,6 +65,10 @@ struct StatsArgs {
     int64_t M, K;
     unsigned *counters;
     int n_counters;
+    // per-token E4M3 quantisation (quant8_kernel only)
+    const void *gamma, *beta;   // [K] act; beta LayerNorm only, may be null
+    unsigned char *codes;       // [M, K] E4M3 codes of the normalised rows
+    float *qscale;              // [M] dequantisation scale of each row
 };
 
 hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s);
@@ -91,5 +96,11 @@ const char *dequant_kernel_name();
 hipError_t launch_dequant_i4(const uint8_t *q, const float *scale, void *out, int64_t N, int64_t K,
                              hipStream_t s);
 const char *dequant_i4_kernel_name();
+// E4M3 (W8A8) path: per-token quantisation of the normalised rows, then the
+// FP8 GEMM on the codes (x = codes, a_scale, w = E4M3 weights, w_scale [Nw])
+hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s);
+const char *quant8_kernel_name(int act);
+hipError_t launch_gemm8(int act, const ProjArgs &a, hipStream_t s);
+const char *gemm8_kernel_name(int act, int epi);
 
 }  // namespace fp

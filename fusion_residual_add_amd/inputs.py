@@ -39,7 +39,8 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "workload", "generate", "quantize_rows_i8"]
+__all__ = ["Workload", "WORKLOADS", "workload", "generate", "quantize_rows_i8", "quantize_groups_i4",
+           "quantize_rows_e4m3"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -48,7 +49,7 @@ class Workload:
     M: int
     hidden: int
     act: str                    # "f32" | "f16" | "bf16"
-    wdt: str                    # "f32" | "f16" | "bf16" | "i8" | "i4"
+    wdt: str                    # "f32" | "f16" | "bf16" | "i8" | "i4" | "e4m3"
     norm: str                   # "rms" | "layer"
     eps: float
     x_std: float
@@ -102,6 +103,12 @@ def _llama70b_i4(M: int) -> Workload:
     return dataclasses.replace(_llama70b(M), name=f"llama2-70b-int4w@M{M}", wdt="i4")
 
 
+def _fp8(base: Workload, name: str) -> Workload:
+    """A workload's shapes with E4M3 weights (per-row scales) and per-token
+    E4M3 activations (the pages' full-FP8 configuration)."""
+    return dataclasses.replace(base, name=name, wdt="e4m3")
+
+
 WORKLOADS: Dict[str, Workload] = {
     # tiny fp32 block: M=4, hidden=256, 4 Q / 2 KV heads of 64, ffn=512
     "tiny-f32": Workload(
@@ -140,6 +147,11 @@ WORKLOADS: Dict[str, Workload] = {
     "llama2-70b-int4w@M16": _llama70b_i4(16),
     "llama2-70b-int4w@M256": _llama70b_i4(256),
 }
+
+
+WORKLOADS["llama2-7b-prefill-fp8"] = _fp8(WORKLOADS["llama2-7b-prefill"], "llama2-7b-prefill-fp8")
+WORKLOADS["llama3-8b-decode-fp8"] = _fp8(WORKLOADS["llama3-8b-decode"], "llama3-8b-decode-fp8")
+WORKLOADS["gpt-fp16-gelu-fp8"] = _fp8(WORKLOADS["gpt-fp16-gelu"], "gpt-fp16-gelu-fp8")
 
 
 def workload(name: str) -> Workload:
@@ -220,8 +232,37 @@ def quantize_groups_i4(w: np.ndarray):
     return torch.from_numpy(q), torch.from_numpy(s)
 
 
+E4M3_MAX = 448.0
+
+
+def quantize_rows_e4m3(w: np.ndarray):
+    """E4M3 storage of a float32 ``[N, K]`` weight, one scale per output row.
+
+    ``s[j] = max_k |w[j, k]| / 448`` in float32 and the codes are torch's
+    nearest-even float8_e4m3fn conversion of ``w / s`` (clipped to +-448); a
+    zero row gets s = 0 and zero codes.  Returns ``(codes [N, K]
+    float8_e4m3fn, s [N] float32)``; the method only ever reads them.
+    """
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.float8_e4m3fn)
+    s = np.empty((N,), dtype=np.float32)
+    step = max(1, (1 << 24) // max(K, 1))
+    for j0 in range(0, N, step):
+        blk = w[j0:j0 + step]
+        amax = np.abs(blk).max(axis=1).astype(np.float32)
+        sc = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+        t = np.clip(blk / safe[:, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+        t[sc == 0] = 0
+        q[j0:j0 + step] = torch.from_numpy(t).to(torch.float8_e4m3fn)
+        s[j0:j0 + step] = sc
+    return q, torch.from_numpy(s)
+
+
 def _weight(rng, wl: Workload, N: int):
     w = _normal(rng, (N, wl.hidden), wl.w_std)
+    if wl.wdt == "e4m3":
+        return quantize_rows_e4m3(w)
     if wl.wdt == "i8":
         q, s = quantize_rows_i8(w)
         return q, s
@@ -235,7 +276,7 @@ def generate(wl: Workload, seed: int = 0, parts=("qkv", "gu")) -> Dict[str, torc
 
     Keys: x, r, gamma, beta (LayerNorm only), and per projection
     w_qkv / s_qkv / b_qkv and w_gu / s_gu / b_gu.  ``s_*`` is present only for
-    int8 and int4 weights; ``b_*`` only when the workload has that bias.  ``parts``
+    int8, int4 and E4M3 weights; ``b_*`` only when the workload has that bias.  ``parts``
     selects which projections to draw, but the draw order (and hence every
     value) does not depend on it: skipped weights are still drawn.
     """
@@ -273,6 +314,8 @@ def generate(wl: Workload, seed: int = 0, parts=("qkv", "gu")) -> Dict[str, torc
             out["w_down"], out["s_down"] = quantize_rows_i8(w)
         elif wl.wdt == "i4":
             out["w_down"], out["s_down"] = quantize_groups_i4(w)
+        elif wl.wdt == "e4m3":
+            out["w_down"], out["s_down"] = quantize_rows_e4m3(w)
         else:
             out["w_down"] = _to_act(w, wl.wdt)
         del w

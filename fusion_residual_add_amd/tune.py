@@ -40,7 +40,7 @@ from fusion_residual_add_amd import inputs
 
 MALL_BYTES = 256 << 20            # MI355X last-level (Infinity) cache
 _DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
-           "i4": torch.uint8}
+           "i4": torch.uint8, "e4m3": torch.float8_e4m3fn}
 _NAMES = {v: k for k, v in _DTYPES.items()}
 
 
@@ -102,7 +102,9 @@ class _Call:
         w = self.d[wkey]
         wbytes = w.numel() * w.element_size()
         n_sets = max(1, (2 * MALL_BYTES) // max(wbytes, 1) + 1)
-        self.ws = [w] + [w.roll(i, 0).contiguous() for i in range(1, n_sets)]
+        roll = (lambda i: w.view(torch.uint8).roll(i, 0).contiguous().view(w.dtype)) if w.element_size() == 1 \
+            else (lambda i: w.roll(i, 0).contiguous())
+        self.ws = [w] + [roll(i) for i in range(1, n_sets)]
         self.wkey = wkey
         self.n_cols = w.shape[0]
         self.swiglu = call == "gu" and wl.act_fn == "swiglu"

@@ -52,9 +52,23 @@
  *    multiple of 128.  Calls that the weight-streaming kernel does not take
  *    (see fp_describe_plan) first dequantise the weight into the workspace
  *    (N * hidden * 2 bytes of it).
+ *  - FP8 W8A8 (w_dtype FP_E4M3, act_dtype FP_BF16 or FP_F16; the full-FP8
+ *    configuration of "TensorRT-LLM 深度工程实践…" §3.3, whose activation
+ *    range is taken from the data at run time): the weight is [N, hidden]
+ *    E4M3 codes (the OCP 8-bit format: 1 sign, 4 exponent bits with bias 7,
+ *    3 mantissa bits, no infinities, largest finite 448; torch's
+ *    float8_e4m3fn) with w_scale [N] fp32, w = e4m3(code) * w_scale[row].
+ *    Instead of rounding n to act_dtype, each token row of n (fp32) is
+ *    quantised at run time: amax = max |n|, a_scale = amax / 448 and
+ *    code = E4M3_rne(clamp(n * (448 / amax), -448, 448)) (a zero row gives
+ *    zero codes); the product is then sum_k e4m3(a) e4m3(w) in fp32, times
+ *    a_scale[m] * w_scale[c].  The codes and scales live in the workspace
+ *    (M * hidden + 4 M bytes of it).  hidden must be a multiple of 128, and
+ *    M * hidden and N * hidden must be below 2^32.
  *  - Dtypes: act_dtype in {F32, F16, BF16}; w_dtype == act_dtype, or FP_I8 /
- *    FP_I4 with act_dtype FP_BF16; out_dtype == act_dtype or FP_F32.  gamma,
- *    beta and bias are act_dtype; w_scale is fp32.
+ *    FP_I4 with act_dtype FP_BF16, or FP_E4M3 with act_dtype FP_BF16 /
+ *    FP_F16; out_dtype == act_dtype or FP_F32.  gamma, beta and bias are
+ *    act_dtype; w_scale is fp32.
  *  - Every pointer must be 16-byte aligned.  No output range may overlap an
  *    input range, another output, or the workspace.
  *  - Execution is asynchronous on hip_stream (NULL = the default stream);
@@ -78,7 +92,7 @@
 extern "C" {
 #endif
 
-typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4 } fp_dtype;
+typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4, FP_E4M3 = 5 } fp_dtype;
 typedef enum { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
 typedef enum { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
 typedef enum {
@@ -106,8 +120,8 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols,
  *  h_out       : [M, hidden] act_dtype or NULL
  *  gamma, beta : [hidden] act_dtype (gamma required unless FP_NORM_NONE)
  *  w_qkv       : [(H + 2 Hkv) * D, hidden], rows = Q heads, then K, then V
- *  w_scale     : fp32, required iff w_dtype is FP_I8 ([(H + 2 Hkv) * D]) or
- *                FP_I4 ([(H + 2 Hkv) * D, hidden / 128])
+ *  w_scale     : fp32, required iff w_dtype is FP_I8 or FP_E4M3
+ *                ([(H + 2 Hkv) * D]) or FP_I4 ([(H + 2 Hkv) * D, hidden / 128])
  *  bias        : [(H + 2 Hkv) * D] act_dtype or NULL
  *  q           : [M, H, D]   out_dtype, token-major
  *  k, v        : [M, Hkv, D] out_dtype, token-major
@@ -152,15 +166,16 @@ fp_status fused_gateup_act(
  * accumulated in fp32 and rounded once to out_dtype.
  *  a        : [M, ffn] act_dtype (e.g. the fused_gateup_act output), used as
  *             given (no norm)
- *  w        : [hidden, ffn] act_dtype, or int8 / int4 with w_scale as for
- *             the other calls (K = ffn)
+ *  w        : [hidden, ffn] act_dtype, or int8 / int4 / E4M3 with w_scale as
+ *             for the other calls (K = ffn; with E4M3 the rows of a are
+ *             quantised per token as n is there)
  *  bias     : [hidden] act_dtype or NULL
  *  residual : [M, hidden] act_dtype or NULL (no add)
  *  out      : [M, hidden] out_dtype; may be the residual buffer itself when
  *             out_dtype == act_dtype (the residual stream updated in place;
  *             each element is read and written by the same thread).  Any
  *             other overlap is FP_E_ALIAS.
- *  Requires ffn a positive multiple of 64 (128 for int4), hidden a positive
+ *  Requires ffn a positive multiple of 64 (128 for int4 and E4M3), hidden a positive
  *  multiple of 16.  Dtypes, alignment, workspace (fp_workspace_bytes(M, ffn,
  *  hidden, act_dtype, w_dtype)) and errors as for the other calls. */
 fp_status fused_down_residual(const void *a, const void *w, const float *w_scale, const void *bias,

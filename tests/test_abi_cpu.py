@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fusedproj.h")
 
 FAKE = 0x10000           # 16-byte aligned, never dereferenced
-F32, F16, BF16, I8, I4 = 0, 1, 2, 3, 4
+F32, F16, BF16, I8, I4, E4M3 = 0, 1, 2, 3, 4, 5
 
 
 def lib():
@@ -97,6 +97,9 @@ def test_m_zero_is_a_noop():
     (dict(wdt=I4), "FP_E_NULL"),                       # int4 without scales
     (dict(wdt=I4, hidden=320, w_scale=FAKE + 0x70000000), "FP_E_SHAPE"),   # int4: hidden % 128
     (dict(act=F16, wdt=I4, w_scale=FAKE + 0x70000000), "FP_E_DTYPE"),
+    (dict(wdt=E4M3), "FP_E_NULL"),                     # E4M3 without scales
+    (dict(wdt=E4M3, hidden=320, w_scale=FAKE + 0x70000000), "FP_E_SHAPE"),   # E4M3: hidden % 128
+    (dict(act=F32, odt=F32, wdt=E4M3, w_scale=FAKE + 0x70000000), "FP_E_DTYPE"),   # fp32 activations
     (dict(M=-1), "FP_E_SHAPE"),
     (dict(hidden=4000), "FP_E_SHAPE"),
     (dict(hidden=0), "FP_E_SHAPE"),
@@ -174,6 +177,30 @@ def test_int4_plans():
     assert p["family"] == "tiled" and p["prep"] == "dequant_i4_kernel"
     assert fra.workspace_bytes(8, 384, 512, torch.bfloat16, u8) >= 512 * 384 * 2
     assert fra.workspace_bytes(16, 8192, 57344, torch.bfloat16, u8) < 57344 * 8192
+
+
+def test_fp8_plans():
+    for var in _ENV:
+        os.environ.pop(var, None)
+    e = torch.float8_e4m3fn
+    # one family at every token count: per-token quantisation, then the FP8 GEMM
+    p = _plan(32, 4096, 28672, w=e, fn="swiglu")
+    assert p["family"] == "fp8" and p["kernel"] == "gemm8_kernel<bf16,swiglu>" and p["prep"] == "quant8_kernel<bf16>"
+    assert p["splits"] == 2 and p["grid"] == 224 * 2          # 224 tiles of 64 gate + 64 up rows, split in two
+    p = _plan(1, 4096, 6144, w=e)
+    assert p["splits"] == 8 and p["grid"] == 48 * 8
+    p = _plan(16384, 4096, 22016, w=e, fn="swiglu")
+    assert p["splits"] == 1 and p["grid"] == 128 * 172
+    assert _plan(100, 512, 512, act=torch.float16, w=e, fn="gelu_tanh")["kernel"] == "gemm8_kernel<f16,gelu>"
+    # the workspace holds the codes and row scales (and the partials when split)
+    assert fra.workspace_bytes(16384, 4096, 22016, torch.bfloat16, e) >= 16384 * 4096 + 16384 * 4
+    assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 224 * 2 * 128 * 128 * 4
+    assert fra.workspace_bytes(8, 320, 512, torch.bfloat16, e) == 0      # hidden % 128
+    os.environ["FUSEDPROJ_SPLITS"] = "3"
+    try:
+        assert _plan(1, 4096, 6144, w=e)["splits"] == 3
+    finally:
+        os.environ.pop("FUSEDPROJ_SPLITS")
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,165 @@
+"""FP8 W8A8 (E4M3 weights with per-row scales, per-token E4M3 activations)
+through the C ABI against the oracle: both projections and the down
+projection, bf16 and fp16 activations, every norm and epilogue, ragged token
+and column counts, split K, rows that quantise to zero, and the workloads at
+full size on sampled token rows.
+
+The oracle quantises the exactly normalised row (double precision); the
+kernels quantise the fp32-normalised row, so a code can differ where a
+scaled value sits within fp32 rounding of a midpoint between two E4M3 values
+(about one element in 2^19), which moves an output by far less than the
+tolerances of test_gpu_parity used here.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fusion_residual_add_amd as fra
+from fusion_residual_add_amd import inputs
+from test_gpu_parity import DEV, check, run_gu, run_qkv, small, to_dev, _sample_rows
+
+pytestmark = pytest.mark.gpu
+
+FP8 = [
+    dict(M=1, hidden=256), dict(M=5, hidden=384, ffn=208), dict(M=17, hidden=512, H=8, Hkv=2, D=64),
+    dict(M=33, hidden=256), dict(M=64, hidden=1024, ffn=336), dict(M=65, hidden=384),
+    dict(M=130, hidden=512, ffn=400), dict(M=257, hidden=256, ffn=208, act_fn="none", bias=True),
+    dict(M=40, hidden=512, norm="layer"), dict(M=90, hidden=256, norm="layer", act_fn="gelu_tanh", bias=True),
+    dict(act="f16", M=37, hidden=384), dict(act="f16", M=150, hidden=512, norm="layer", act_fn="gelu_tanh",
+                                            bias=True, ffn=272),
+    dict(M=3, H=5, Hkv=1, D=48, hidden=640, ffn=48), dict(M=129, H=8, Hkv=8, D=16, hidden=512),
+]
+
+
+def _fp8(**cfg):
+    bias = cfg.pop("bias", False)
+    return small(wdt="e4m3", bias=bias, **cfg)
+
+
+@pytest.mark.parametrize("cfg", FP8, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("native", [False, True], ids=["f32out", "nativeout"])
+def test_fp8_small(cfg, native):
+    wl = _fp8(**dict(cfg))
+    inp = inputs.generate(wl, seed=7)
+    d = to_dev(inp)
+    odt = None if native else torch.float32
+    adt = d["x"].dtype
+    plan = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, adt, torch.float8_e4m3fn, wl.act_fn)
+    print(f"fp8 {wl.name} {plan['kernel']} splits={plan['splits']} native={native}", flush=True)
+    assert plan["family"] == "fp8"
+    q, k, v, h = run_qkv(wl, d, odt)
+    out = run_gu(wl, d, odt)
+    torch.cuda.synchronize()
+    rq = oracle.workload_qkv(wl, inp)
+    rg = oracle.workload_gateup(wl, inp)
+    check("q", q, rq["q"])
+    check("k", k, rq["k"])
+    check("v", v, rq["v"])
+    check("out", out, rg["out"])
+    assert np.array_equal(h.double().cpu().numpy(), rq["h_out"]), "h_out not bit-exact"
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8])
+@pytest.mark.parametrize("M", [1, 48, 200])
+def test_fp8_splits(splits, M, monkeypatch):
+    monkeypatch.setenv("FUSEDPROJ_SPLITS", str(splits))
+    wl = _fp8(M=M, hidden=1024, ffn=208)
+    inp = inputs.generate(wl, seed=8)
+    d = to_dev(inp)
+    plan = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, torch.bfloat16, torch.float8_e4m3fn, "swiglu")
+    assert plan["splits"] == splits, plan
+    q, k, v, _ = run_qkv(wl, d, torch.float32)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rq = oracle.workload_qkv(wl, inp)
+    rg = oracle.workload_gateup(wl, inp)
+    check("q", q, rq["q"])
+    check("v", v, rq["v"])
+    check("out", out, rg["out"])
+
+
+def test_fp8_zero_rows_and_bias():
+    # rows whose normalised values are all zero quantise to zero codes with a
+    # zero scale: the output is the bias alone
+    wl = _fp8(M=20, hidden=256, ffn=64, act_fn="none", bias=True, norm="none")
+    inp = inputs.generate(wl, seed=9)
+    inp["r"][3] = -inp["x"][3]
+    inp["x"][11] = 0
+    inp["r"][11] = 0
+    d = to_dev(inp)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rg = oracle.workload_gateup(wl, inp)
+    check("out", out, rg["out"])
+    b = inp["b_gu"].double().numpy()
+    assert np.array_equal(out[3].double().cpu().numpy(), b)
+    assert np.array_equal(out[11].double().cpu().numpy(), b)
+
+
+def test_fp8_deterministic_and_m_zero(monkeypatch):
+    monkeypatch.setenv("FUSEDPROJ_SPLITS", "4")
+    wl = _fp8(M=24, hidden=512, ffn=144)
+    d = to_dev(inputs.generate(wl, seed=10))
+    a = run_gu(wl, d)
+    b = run_gu(wl, d)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    e = fra.fused_gateup_act(d["x"][:0], d["r"][:0], d["gamma"], d["w_gu"], wl.ffn, "swiglu", w_scale=d["s_gu"])
+    assert e.shape == (0, wl.ffn)
+
+
+DOWN8 = [dict(M=1, hidden=320, ffn=512), dict(M=20, hidden=512, ffn=1024), dict(M=150, hidden=256, ffn=768),
+         dict(act="f16", M=40, hidden=512, ffn=512)]
+
+
+@pytest.mark.parametrize("cfg", DOWN8, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("mode", ["f32out", "nativeout", "inplace"])
+def test_fp8_down(cfg, mode):
+    wl = _fp8(**dict(cfg))
+    inp = inputs.generate(wl, seed=12, parts=("down",))
+    d = to_dev(inp)
+    plan = fra.describe_plan(wl.M, wl.ffn, wl.hidden, d["a_down"].dtype, torch.float8_e4m3fn)
+    print(f"fp8 down {wl.name} {mode}: {plan['kernel']}", flush=True)
+    if mode == "inplace":
+        res = d["r"].clone()
+        out = fra.fused_down_residual(d["a_down"], d["w_down"], res, w_scale=d["s_down"], out=res)
+        assert out.data_ptr() == res.data_ptr()
+    else:
+        out = fra.fused_down_residual(d["a_down"], d["w_down"], d["r"], w_scale=d["s_down"],
+                                      out_dtype=torch.float32 if mode == "f32out" else None)
+    torch.cuda.synchronize()
+    ref = oracle.down_residual(inp["a_down"], inp["w_down"], inp["s_down"], None, inp["r"])
+    check("out", out, ref)
+
+
+FULL8 = ["llama3-8b-decode-fp8", "llama2-7b-prefill-fp8", "gpt-fp16-gelu-fp8"]
+
+
+@pytest.mark.parametrize("name", FULL8)
+def test_fp8_workload_full_size(name):
+    wl = inputs.workload(name)
+    print(f"workload {name}: generating", flush=True)
+    inp = inputs.generate(wl, seed=0)
+    d = to_dev(inp)
+    rows = _sample_rows(wl.M, 24 if wl.M > 64 else wl.M)
+    print(f"workload {name}: GPU", flush=True)
+    res = {}
+    for native in (False, True):
+        odt = None if native else torch.float32
+        if wl.n_qkv:
+            q, k, v, h = run_qkv(wl, d, odt)
+            res[("qkv", native)] = (q[rows].cpu(), k[rows].cpu(), v[rows].cpu(), h[rows].cpu())
+        res[("gu", native)] = run_gu(wl, d, odt)[rows].cpu()
+    torch.cuda.synchronize()
+    print(f"workload {name}: oracle on {len(rows)} rows", flush=True)
+    if wl.n_qkv:
+        rq = oracle.workload_qkv(wl, inp, row_idx=rows)
+    rg = oracle.workload_gateup(wl, inp, row_idx=rows)
+    for native in (False, True):
+        if wl.n_qkv:
+            q, k, v, h = res[("qkv", native)]
+            print(name, native, "q", check("q", q, rq["q"]), "k", check("k", k, rq["k"]),
+                  "v", check("v", v, rq["v"]), flush=True)
+            assert np.array_equal(h.double().numpy(), rq["h_out"]), "h_out not bit-exact"
+        print(name, native, "out", check("out", res[("gu", native)], rg["out"]), flush=True)
