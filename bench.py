@@ -221,12 +221,13 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::stats_kernel<(\d), \d+>", cxx)
     if m:
         return f"stats_kernel<{_ACT[m.group(1)]}>"
-    m = re.search(r"fp::quant8_kernel<(\d), \d+>", cxx)
+    m = re.search(r"fp::quant8_kernel<(\d), \d+, \d+>", cxx)
     if m:
         return f"quant8_kernel<{_ACT[m.group(1)]}>"
-    m = re.search(r"fp::gemm8_kernel<(\d), (\d)>", cxx)
+    m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), \d>", cxx)
     if m:
-        return f"gemm8_kernel<{_ACT[m.group(1)]},{_EPI[m.group(2)]}>"
+        t = 64 * int(m.group(3))
+        return f"gemm8_kernel<{_ACT[m.group(1)]},{t}x{t},{_EPI[m.group(2)]}>"
     return cxx
 
 
@@ -459,7 +460,8 @@ def main():
     ms = time_steps(run.step, args.steps, args.warmup)
     step_bytes = (algo_bytes(wl, "qkv") if wl.n_qkv else 0) + algo_bytes(wl, "gu")
     step_flops = (flops(wl, "qkv") if wl.n_qkv else 0) + flops(wl, "gu")
-    decode = step_flops / step_bytes < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_peak = MFMA_FP8_PEAK_TFLOPS if wl.wdt == "e4m3" else MFMA_BF16_PEAK_TFLOPS
+    decode = step_flops / step_bytes < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
 
     # dominant kernel: the gate/up projection
     prof_gu = profile_call(run, "gu", 50)
@@ -476,8 +478,8 @@ def main():
         value, unit = step_bytes / (ms * 1e-3) / 1e9, "GB/s"
     else:
         achieved = flops(wl, "gu") / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4)}
         value, unit = step_flops / (ms * 1e-3) / 1e12, "TFLOP/s"
     roof["kernel"] = gu_kernel
     roof["kernel_avg_us"] = round(gu_ms * 1e3, 2)
@@ -488,7 +490,7 @@ def main():
         "metric": "fused-layer TFLOP/s (prefill) and HBM GB/s (decode), % of MI355X roofline",
         "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.act, "data": "synthetic",
+        "dtype": "e4m3" if wl.wdt == "e4m3" else wl.act, "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "hidden": wl.hidden, "n_heads": wl.n_heads,
                    "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "ffn": wl.ffn,
                    "act_fn": wl.act_fn, "norm": wl.norm, "weights": wl.wdt,
@@ -504,8 +506,9 @@ def main():
 
     if not args.no_secondary:
         sec = {}
-        for name in ("llama2-7b-prefill",):
+        for name in ("llama2-7b-prefill", "llama2-7b-prefill-fp8"):
             pwl = inputs.workload(name)
+            ppeak = MFMA_FP8_PEAK_TFLOPS if pwl.wdt == "e4m3" else MFMA_BF16_PEAK_TFLOPS
             pr = Runner(pwl)
             pms = time_steps(pr.step, args.prefill_steps, 3)
             pfl = flops(pwl, "qkv") + flops(pwl, "gu")
@@ -514,7 +517,8 @@ def main():
             pq = profile_call(pr, "qkv", 5)
             sec[name] = {"value": round(pfl / (pms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                          "ms_per_step": round(pms, 4),
-                         "frac_of_bf16_peak": round(pfl / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "dtype": "e4m3" if pwl.wdt == "e4m3" else pwl.act, "peak": ppeak,
+                         "frac_of_peak": round(pfl / (pms * 1e-3) / 1e12 / ppeak, 4),
                          "kernel_us": {"gu": {k: round(v * 1e3, 1) for k, v in pprof.items()},
                                        "qkv": {k: round(v * 1e3, 1) for k, v in pq.items()}}}
             del pr

@@ -7,14 +7,17 @@
 //   y[m, c] = (sum_k e4m3(a[m, k]) e4m3(w[c, k])) * a_scale[m] * w_scale[c]
 //             (+ bias[c]), then the GQA split / SwiGLU / tanh-GELU / residual.
 //
-// One workgroup computes a 128 (tokens) x 128 (weight rows) tile with 4 waves
-// in a 2 x 2 layout, each wave 64 x 64 as 2 x 2 fragments of 32 x 32 with fp32
-// accumulators.  For SwiGLU the 128 weight rows are 64 gate rows and the 64
-// matching up rows, and each wave holds a gate and an up fragment of the same
-// columns, so SiLU(g) * u is formed in registers.  K advances 128 codes (128
-// bytes) per step through two LDS stages of A and B (16 KB each), both loaded
-// straight from HBM / L2 into LDS (buffer_load ... lds, 16 bytes per lane,
-// 16-byte chunks XOR-swizzled by row); 64 KB of LDS, two workgroups per CU.
+// One workgroup computes a (64 FM) tokens x (64 FN) weight rows tile with 4
+// waves in a 2 x 2 layout, each wave FM x FN fragments of 32 x 32 with fp32
+// accumulators: 128 x 128 (FM = FN = 2; two workgroups per CU, for token counts
+// whose tiles would not fill the chip) or 256 x 256 (FM = FN = 4; the 256
+// accumulators per lane live in AGPRs, one workgroup per CU, half the LDS
+// bytes read per MFMA).  For SwiGLU the weight rows of a tile are BN / 2 gate
+// rows and the BN / 2 matching up rows, and each wave holds gate and up
+// fragments of the same columns, so SiLU(g) * u is formed in registers.  K
+// advances 128 codes (128 bytes) per step through two LDS stages of A and B,
+// both loaded straight from HBM / L2 into LDS (buffer_load ... lds, 16 bytes
+// per lane, 16-byte chunks XOR-swizzled by row).
 // The quantised activations are read as 1-byte codes: the per-token scale
 // needs the whole normalised row (its amax) before any element is coded, so
 // the quantisation runs in the kernel before this one and writes the codes
@@ -25,8 +28,7 @@
 namespace fp {
 
 namespace g8 {
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int TILE = BM * BK;   // 16 KB per operand and stage
+constexpr int BK = 128;
 // swizzled byte offset of 16-byte chunk c (0..7) of tile row r
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char *lds, uint32_t voff, uint32_t soff) {
@@ -39,15 +41,19 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned ch
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 }  // namespace g8
 
-template <int ACT, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm8_kernel(ProjArgs p) {
+template <int ACT, int EPI, int FM, int FN>
+__global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjArgs p) {
     using T = Act<ACT>;
     using namespace g8;
     constexpr bool SW = EPI == EPI_SWIGLU;
-    __shared__ __attribute__((aligned(16))) unsigned char lA0[TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lA1[TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lB0[TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lB1[TILE];
+    constexpr int BM = 64 * FM, BN = 64 * FN;
+    constexpr int TILEA = BM * BK, TILEB = BN * BK;
+    constexpr int IA = BM / 32, IB = BN / 32;   // load instructions per wave and stage
+    static_assert(!SW || FN % 2 == 0, "gate and up fragments in pairs");
+    __shared__ __attribute__((aligned(16))) unsigned char lA0[TILEA];
+    __shared__ __attribute__((aligned(16))) unsigned char lA1[TILEA];
+    __shared__ __attribute__((aligned(16))) unsigned char lB0[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char lB1[TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,50 +76,58 @@ __global__ __launch_bounds__(256, 2) void gemm8_kernel(ProjArgs p) {
     const int kt0 = (int)((int64_t)KT * z / p.splits);
     const int kt1 = (int)((int64_t)KT * (z + 1) / p.splits);
 
-    // ---- loads: wave w fills tile rows [32 w, 32 w + 32) of A and of B with
-    // 4 instructions each per stage; lane l of instruction i covers row
-    // 32 w + 8 i + l / 8 at LDS chunk position l % 8, which holds the row's
-    // global chunk (l % 8) ^ (row % 8).  Rows past the operand are clamped to
-    // its last row (they only feed outputs that are not stored), so every
-    // offset stays inside the operand and below 2^32 (checked by the host).
+    // ---- loads: wave w fills tile rows [BM/4 w, BM/4 (w + 1)) of A and
+    // [BN/4 w, BN/4 (w + 1)) of B with 1 KB instructions (8 rows); lane l of
+    // instruction i covers row BM/4 w + 8 i + l / 8 at LDS chunk position
+    // l % 8, which holds the row's global chunk (l % 8) ^ (row % 8).  Rows past
+    // the operand are clamped to its last row (they only feed outputs that are
+    // not stored), so every offset stays inside the operand and below 2^32
+    // (checked by the host).
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, (short)0,
                                                                         (uint32_t)(p.M * p.K), 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, (short)0,
                                                                         (uint32_t)(p.Nw * p.K), 0x00020000);
-    uint32_t a_off[4], b_off[4];
+    uint32_t a_off[IA], b_off[IB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 32 * wave + 8 * i + (lane >> 3);
+    for (int i = 0; i < IA; ++i) {
+        const int r = (BM / 4) * wave + 8 * i + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
         int64_t ma = (int64_t)tm * BM + r;
         ma = ma < p.M ? ma : p.M - 1;
+        a_off[i] = (uint32_t)(ma * p.K) + c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+        const int r = (BN / 4) * wave + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
         int64_t wr;
-        if constexpr (SW) wr = r < 64 ? (int64_t)tn * 64 + r : p.F + (int64_t)tn * 64 + (r - 64);
+        if constexpr (SW) wr = r < BN / 2 ? (int64_t)tn * (BN / 2) + r : p.F + (int64_t)tn * (BN / 2) + (r - BN / 2);
         else wr = (int64_t)tn * BN + r;
         wr = wr < p.Nw ? wr : p.Nw - 1;
-        a_off[i] = (uint32_t)(ma * p.K) + c * 16;
         b_off[i] = (uint32_t)(wr * p.K) + c * 16;
     }
     auto issue = [&](int kt, unsigned char *la, unsigned char *lb) {
         const uint32_t soff = (uint32_t)kt * BK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_lds16(ra, la + (4 * wave + i) * 1024, a_off[i], soff);
+        for (int i = 0; i < IA; ++i) load_lds16(ra, la + (IA * wave + i) * 1024, a_off[i], soff);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_lds16(rw, lb + (4 * wave + i) * 1024, b_off[i], soff);
+        for (int i = 0; i < IB; ++i) load_lds16(rw, lb + (IB * wave + i) * 1024, b_off[i], soff);
     };
 
-    // ---- fragments: A rows 64 wm + 32 f + l % 32; B tile rows: SwiGLU the
-    // gate block 32 wn (f = 0) and the matching up block 64 + 32 wn (f = 1),
-    // otherwise 64 wn + 32 f.  Lane l supplies k [64 kb + 32 (l / 32), +32)
-    // of K sub-step kb as two 16-byte chunks (A and B alike, so the k order
-    // inside the operand is the same on both sides).
+    // ---- fragments: A rows 32 (FM wm + f) + l % 32; B tile rows: SwiGLU the
+    // gate blocks 32 (FN/2 wn + f) for f < FN/2 and the matching up blocks
+    // BN/2 + 32 (FN/2 wn + f - FN/2), otherwise 32 (FN wn + f).  Lane l
+    // supplies k [64 kb + 32 (l / 32), +32) of K sub-step kb as two 16-byte
+    // chunks (A and B alike, so the k order inside the operand is the same on
+    // both sides).
     const int fr = lane & 31, kh = lane >> 5;
-    int arow[2], brow[2];
+    int arow[FM], brow[FN];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        arow[f] = 64 * wm + 32 * f + fr;
-        brow[f] = SW ? 64 * f + 32 * wn + fr : 64 * wn + 32 * f + fr;
-    }
+    for (int f = 0; f < FM; ++f) arow[f] = 32 * (FM * wm + f) + fr;
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+        brow[f] = SW ? (f < FN / 2 ? 32 * (FN / 2 * wn + f) : BN / 2 + 32 * (FN / 2 * wn + f - FN / 2)) + fr
+                     : 32 * (FN * wn + f) + fr;
     auto frag = [&](const unsigned char *l, int row, int kb) -> i32x8 {
         const int c = 4 * kb + 2 * kh;
         const u32x4 lo = *(const u32x4 *)(l + swz(row, c));
@@ -121,27 +135,26 @@ __global__ __launch_bounds__(256, 2) void gemm8_kernel(ProjArgs p) {
         return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     auto compute = [&](const unsigned char *la, const unsigned char *lb) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            i32x8 af[2], bf[2];
+            i32x8 af[FM], bf[FN];
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                af[f] = frag(la, arow[f], kb);
-                bf[f] = frag(lb, brow[f], kb);
-            }
+            for (int f = 0; f < FM; ++f) af[f] = frag(la, arow[f], kb);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int f = 0; f < FN; ++f) bf[f] = frag(lb, brow[f], kb);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)   // formats: 0 = E4M3 for both operands
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)   // formats: 0 = E4M3 for both operands
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0,
                                                                                0, 0, 0, 0);
         }
@@ -176,64 +189,69 @@ __global__ __launch_bounds__(256, 2) void gemm8_kernel(ProjArgs p) {
         step_sync();   // the last reload has landed before the epilogue reuses the LDS
     }
 
-    // ---- split K: the last contributor of a tile sums the partials in order
-    if (p.splits > 1) {
-        float flat[64];
+    // ---- split K (128 x 128 tiles only): the last contributor of a tile
+    // sums the partials in order
+    if (FM * FN < 16 && p.splits > 1) {
+        constexpr int NACC = FM * FN * 16;
+        float flat[NACC];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) flat[(i * 2 + j) * 16 + e] = acc[i][j][e];
-        if (!splitk_reduce<64>(p, tile, z, p.splits, flat)) return;
+                for (int e = 0; e < 16; ++e) flat[(i * FN + j) * 16 + e] = acc[i][j][e];
+        if (!splitk_reduce<NACC>(p, tile, z, p.splits, flat)) return;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = flat[(i * 2 + j) * 16 + e];
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = flat[(i * FN + j) * 16 + e];
     }
 
     // ---- epilogue: scales, bias, activation; staged per wave through LDS in
     // [row][col] order (rows padded by 32 bytes), then stored as runs of 8
     // columns (16 bytes of 16-bit outputs)
-    constexpr int OUTC = SW ? 32 : 64;          // output columns per wave
-    constexpr int SROW = OUTC * 4 + 32;         // staging row pitch, bytes
-    static_assert(32 * SROW <= TILE, "staging fits one tile buffer");
+    constexpr int OUTC = SW ? 16 * FN : 32 * FN;   // output columns per wave
+    constexpr int NJ = SW ? FN / 2 : FN;            // output fragments per wave
+    constexpr int SROW = OUTC * 4 + 32;             // staging row pitch, bytes
+    static_assert(32 * SROW <= TILEA && 32 * SROW <= TILEB, "staging fits one tile buffer");
     unsigned char *stg = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
-    const int64_t col0 = SW ? (int64_t)tn * 64 + 32 * wn : (int64_t)tn * BN + 64 * wn;
+    const int64_t col0 = SW ? (int64_t)tn * (BN / 2) + OUTC * wn : (int64_t)tn * BN + OUTC * wn;
     const int64_t ncols = SW ? p.F : p.Nw;
-    // per-column weight scale and bias of this lane (SwiGLU: gate, up)
-    float cs[2], cb[2];
+    // per-column weight scale and bias of this lane (SwiGLU: gate, then up)
+    float cs[FN], cb[FN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        int64_t c = SW ? col0 + fr : col0 + 32 * j + fr;
+    for (int j = 0; j < FN; ++j) {
+        const int jo = SW ? j % (FN / 2) : j;
+        int64_t c = col0 + 32 * jo + fr;
         c = c < ncols ? c : ncols - 1;
-        const int64_t cw = SW ? c + (j ? p.F : 0) : c;
+        const int64_t cw = SW && j >= FN / 2 ? c + p.F : c;
         cs[j] = p.w_scale[cw];
         cb[j] = p.bias ? T::ld(p.bias, cw) : 0.f;
     }
     const bool of32 = p.out_f32 != 0;
     const int esz = of32 ? 4 : 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t mrow0 = (int64_t)tm * BM + 64 * wm + 32 * i;
+    for (int i = 0; i < FM; ++i) {
+        const int64_t mrow0 = (int64_t)tm * BM + 32 * (FM * wm + i);
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int rl = 8 * (q >> 2) + 4 * kh + (q & 3);   // 0..31
             const int64_t mr = mrow0 + rl;
             const float as = p.a_scale[mr < p.M ? mr : p.M - 1];
-            if constexpr (SW) {
-                const float g = acc[i][0][q] * as * cs[0] + cb[0];
-                const float u = acc[i][1][q] * as * cs[1] + cb[1];
-                *(float *)(stg + rl * SROW + fr * 4) = silu(g) * u;
-            } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float y = acc[i][j][q] * as * cs[j] + cb[j];
+            for (int j = 0; j < NJ; ++j) {
+                float y;
+                if constexpr (SW) {
+                    const float g = acc[i][j][q] * as * cs[j] + cb[j];
+                    const float u = acc[i][j + FN / 2][q] * as * cs[j + FN / 2] + cb[j + FN / 2];
+                    y = silu(g) * u;
+                } else {
+                    y = acc[i][j][q] * as * cs[j] + cb[j];
                     if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
-                    *(float *)(stg + rl * SROW + (32 * j + fr) * 4) = y;
                 }
+                *(float *)(stg + rl * SROW + (32 * j + fr) * 4) = y;
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -277,29 +295,40 @@ __global__ __launch_bounds__(256, 2) void gemm8_kernel(ProjArgs p) {
     }
 }
 
-template <int ACT>
+template <int ACT, int F>
 static void launch_gemm8_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (a.epi) {
-    case EPI_QKV:    hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_QKV>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_GELU:   hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_GELU>), dim3(grid), dim3(256), 0, s, a); break;
-    default:         hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_LINEAR>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_QKV:    hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_QKV, F, F>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_SWIGLU, F, F>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_GELU:   hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_GELU, F, F>), dim3(grid), dim3(256), 0, s, a); break;
+    default:         hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_LINEAR, F, F>), dim3(grid), dim3(256), 0, s, a); break;
     }
 }
 
-hipError_t launch_gemm8(int act, const ProjArgs &a, hipStream_t s) {
+hipError_t launch_gemm8(int act, bool big, const ProjArgs &a, hipStream_t s) {
     const unsigned grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n * a.splits);
     if (grid == 0) return hipSuccess;
-    if (act == ACT_F16) launch_gemm8_t<ACT_F16>(a, grid, s);
-    else launch_gemm8_t<ACT_BF16>(a, grid, s);
+    if (act == ACT_F16) {
+        if (big) launch_gemm8_t<ACT_F16, 4>(a, grid, s);
+        else launch_gemm8_t<ACT_F16, 2>(a, grid, s);
+    } else {
+        if (big) launch_gemm8_t<ACT_BF16, 4>(a, grid, s);
+        else launch_gemm8_t<ACT_BF16, 2>(a, grid, s);
+    }
     return hipGetLastError();
 }
 
-const char *gemm8_kernel_name(int act, int epi) {
-    static const char *names[2][4] = {
-        {"gemm8_kernel<bf16,qkv>", "gemm8_kernel<bf16,swiglu>", "gemm8_kernel<bf16,gelu>", "gemm8_kernel<bf16,linear>"},
-        {"gemm8_kernel<f16,qkv>", "gemm8_kernel<f16,swiglu>", "gemm8_kernel<f16,gelu>", "gemm8_kernel<f16,linear>"}};
-    return names[act == ACT_F16 ? 1 : 0][epi & 3];
+const char *gemm8_kernel_name(int act, bool big, int epi) {
+    static const char *names[2][2][4] = {
+        {{"gemm8_kernel<bf16,128x128,qkv>", "gemm8_kernel<bf16,128x128,swiglu>", "gemm8_kernel<bf16,128x128,gelu>",
+          "gemm8_kernel<bf16,128x128,linear>"},
+         {"gemm8_kernel<bf16,256x256,qkv>", "gemm8_kernel<bf16,256x256,swiglu>", "gemm8_kernel<bf16,256x256,gelu>",
+          "gemm8_kernel<bf16,256x256,linear>"}},
+        {{"gemm8_kernel<f16,128x128,qkv>", "gemm8_kernel<f16,128x128,swiglu>", "gemm8_kernel<f16,128x128,gelu>",
+          "gemm8_kernel<f16,128x128,linear>"},
+         {"gemm8_kernel<f16,256x256,qkv>", "gemm8_kernel<f16,256x256,swiglu>", "gemm8_kernel<f16,256x256,gelu>",
+          "gemm8_kernel<f16,256x256,linear>"}}};
+    return names[act == ACT_F16 ? 1 : 0][big ? 1 : 0][epi & 3];
 }
 
 }  // namespace fp

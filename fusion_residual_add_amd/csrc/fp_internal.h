@@ -100,7 +100,8 @@ const char *dequant_i4_kernel_name();
 // FP8 GEMM on the codes (x = codes, a_scale, w = E4M3 weights, w_scale [Nw])
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s);
 const char *quant8_kernel_name(int act);
-hipError_t launch_gemm8(int act, const ProjArgs &a, hipStream_t s);
-const char *gemm8_kernel_name(int act, int epi);
+// big: 256 x 256 tiles (one workgroup per CU), otherwise 128 x 128
+hipError_t launch_gemm8(int act, bool big, const ProjArgs &a, hipStream_t s);
+const char *gemm8_kernel_name(int act, bool big, int epi);
 
 }  // namespace fp

@@ -116,7 +116,10 @@ __device__ __forceinline__ float round_to_odd_f32(double t) {
     return __uint_as_float(u | 1u);
 }
 
-template <int ACT, int TPR>
+// NV > 0: each thread keeps its NV vectors of 8 elements of h in registers
+// after the first pass (rows of at most TPR * 8 * NV elements); NV == 0: every
+// pass reads the row again.
+template <int ACT, int TPR, int NV>
 __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
     using T = Act<ACT>;
     using S = typename T::S;
@@ -137,6 +140,19 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
     S *hr = a.h_out ? (S *)a.h_out + (active ? m : 0) * a.K : nullptr;
     const S *gr = (const S *)a.gamma, *br = (const S *)a.beta;
 
+    // fn(j, k) for this thread's vectors j (elements k .. k + 7) of the row
+    auto each = [&](auto fn) {
+        if (!active) return;
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int64_t k = ((int64_t)j * TPR + t) * VE;
+                if (k < a.K) fn(j, k);
+            }
+        } else {
+            for (int64_t k = (int64_t)t * VE; k < a.K; k += TPR * VE) fn(0, k);
+        }
+    };
     auto load_h = [&](int64_t k, float *h) {   // exact: 16-bit x + 16-bit r fits fp32
         T::unpack(*(const u32x4 *)(xr + k), h);
         if (rr) {
@@ -144,6 +160,15 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
             T::unpack(*(const u32x4 *)(rr + k), r);
 #pragma unroll
             for (int e = 0; e < VE; ++e) h[e] += r[e];
+        }
+    };
+    float hc[NV > 0 ? NV : 1][VE];
+    auto get_h = [&](int j, int64_t k, float *h) {
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) h[e] = hc[j][e];
+        } else {
+            load_h(k, h);
         }
     };
     // a row-wide reduction over the WPR waves of the row (sum or max)
@@ -167,42 +192,42 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
     };
 
     double sum = 0.0, ssq = 0.0;
-    if (active) {
-        for (int64_t k = (int64_t)t * VE; k < a.K; k += TPR * VE) {
-            float h[VE];
-            load_h(k, h);
-            if (hr) *(u32x4 *)(hr + k) = T::pack(h);
+    each([&](int j, int64_t k) {
+        float h[VE];
+        load_h(k, h);
+        if constexpr (NV > 0) {
 #pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                const double d = (double)h[e];
-                sum = __dadd_rn(sum, d);
-                ssq = __dadd_rn(ssq, __dmul_rn(d, d));
-            }
+            for (int e = 0; e < VE; ++e) hc[j][e] = h[e];
         }
-    }
+        if (hr) *(u32x4 *)(hr + k) = T::pack(h);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            const double d = (double)h[e];
+            sum = __dadd_rn(sum, d);
+            ssq = __dadd_rn(ssq, __dmul_rn(d, d));
+        }
+    });
     const double K = (double)a.K, eps = (double)a.eps;
     double mean = 0.0, rstd = 1.0;
     if (a.norm == 2) {
         mean = row_red(sum, 0, false) / K;
         double dev = 0.0;
-        if (active) {
-            for (int64_t k = (int64_t)t * VE; k < a.K; k += TPR * VE) {
-                float h[VE];
-                load_h(k, h);
+        each([&](int j, int64_t k) {
+            float h[VE];
+            get_h(j, k, h);
 #pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    const double d = __dadd_rn((double)h[e], -mean);
-                    dev = __dadd_rn(dev, __dmul_rn(d, d));
-                }
+            for (int e = 0; e < VE; ++e) {
+                const double d = __dadd_rn((double)h[e], -mean);
+                dev = __dadd_rn(dev, __dmul_rn(d, d));
             }
-        }
+        });
         rstd = 1.0 / sqrt(__dadd_rn(row_red(dev, 1, false) / K, eps));
     } else if (a.norm == 1) {
         rstd = 1.0 / sqrt(__dadd_rn(row_red(ssq, 1, false) / K, eps));
     }
-    auto load_n = [&](int64_t k, double *n) {
+    auto get_n = [&](int j, int64_t k, double *n) {
         float h[VE];
-        load_h(k, h);
+        get_h(j, k, h);
         if (a.norm == 0) {
 #pragma unroll
             for (int e = 0; e < VE; ++e) n[e] = (double)h[e];
@@ -222,38 +247,34 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
         }
     };
     double amax = 0.0;
-    if (active) {
-        for (int64_t k = (int64_t)t * VE; k < a.K; k += TPR * VE) {
-            double n[VE];
-            load_n(k, n);
+    each([&](int j, int64_t k) {
+        double n[VE];
+        get_n(j, k, n);
 #pragma unroll
-            for (int e = 0; e < VE; ++e) amax = fmax(amax, fabs(n[e]));
-        }
-    }
+        for (int e = 0; e < VE; ++e) amax = fmax(amax, fabs(n[e]));
+    });
     amax = row_red(amax, 2, true);
     const double mult = amax > 0.0 ? 448.0 / amax : 0.0;
-    if (active) {
-        if (t == 0) a.qscale[m] = (float)(amax / 448.0);
-        unsigned char *cr = a.codes + m * a.K;
-        for (int64_t k = (int64_t)t * VE; k < a.K; k += TPR * VE) {
-            double n[VE];
-            load_n(k, n);
-            unsigned w[2];
+    if (active && t == 0) a.qscale[m] = (float)(amax / 448.0);
+    unsigned char *cr = a.codes + (active ? m : 0) * a.K;
+    each([&](int j, int64_t k) {
+        double n[VE];
+        get_n(j, k, n);
+        unsigned w[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                float v[4];
+        for (int i = 0; i < 2; ++i) {
+            float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = round_to_odd_f32(fmin(fmax(__dmul_rn(n[4 * i + e], mult), -448.0), 448.0));
-                // two conversions of two values each: bytes 0, 1 then 2, 3
-                // (the first operand of each in the lower byte), nearest even
-                int p = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-                p = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], p, true);
-                w[i] = (unsigned)p;
-            }
-            *(uint2 *)(cr + k) = make_uint2(w[0], w[1]);
+            for (int e = 0; e < 4; ++e)
+                v[e] = round_to_odd_f32(fmin(fmax(__dmul_rn(n[4 * i + e], mult), -448.0), 448.0));
+            // two conversions of two values each: bytes 0, 1 then 2, 3
+            // (the first operand of each in the lower byte), nearest even
+            int p = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], p, true);
+            w[i] = (unsigned)p;
         }
-    }
+        *(uint2 *)(cr + k) = make_uint2(w[0], w[1]);
+    });
 }
 
 // out[j, k] = dequant_i8_bf16(q[j, k], scale[j]) for 16 k per thread.
@@ -322,16 +343,34 @@ hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int ACT, int TPR, int NV>
+static void launch_quant8_g(const StatsArgs &a, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((quant8_kernel<ACT, TPR, NV>), dim3(grid), dim3(256), 0, s, a);
+}
+
+// few tokens: a whole workgroup per row; many tokens: one wave per row.  The
+// row stays in registers when each thread's share is at most 16 vectors.
+template <int ACT, int TPR>
+static void launch_quant8_r(const StatsArgs &a, unsigned grid, hipStream_t s) {
+    const int64_t nv = (a.K + TPR * 8 - 1) / (TPR * 8);
+    if (nv <= 1) launch_quant8_g<ACT, TPR, 1>(a, grid, s);
+    else if (nv <= 2) launch_quant8_g<ACT, TPR, 2>(a, grid, s);
+    else if (nv <= 4) launch_quant8_g<ACT, TPR, 4>(a, grid, s);
+    else if (nv <= 8) launch_quant8_g<ACT, TPR, 8>(a, grid, s);
+    else if (nv <= 16) launch_quant8_g<ACT, TPR, 16>(a, grid, s);
+    else launch_quant8_g<ACT, TPR, 0>(a, grid, s);
+}
+
 template <int ACT>
 static void launch_quant8_t(const StatsArgs &a, hipStream_t s) {
     const int64_t ctr = (a.n_counters + 255) / 256;
     if (a.M <= 1024) {
         const unsigned grid = (unsigned)(a.M > ctr ? a.M : ctr);
-        if (grid) hipLaunchKernelGGL((quant8_kernel<ACT, 256>), dim3(grid), dim3(256), 0, s, a);
+        if (grid) launch_quant8_r<ACT, 256>(a, grid, s);
     } else {
         const int64_t blocks = (a.M + 3) / 4;
         const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) hipLaunchKernelGGL((quant8_kernel<ACT, 64>), dim3(grid), dim3(256), 0, s, a);
+        if (grid) launch_quant8_r<ACT, 64>(a, grid, s);
     }
 }
 

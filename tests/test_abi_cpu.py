@@ -185,13 +185,17 @@ def test_fp8_plans():
     e = torch.float8_e4m3fn
     # one family at every token count: per-token quantisation, then the FP8 GEMM
     p = _plan(32, 4096, 28672, w=e, fn="swiglu")
-    assert p["family"] == "fp8" and p["kernel"] == "gemm8_kernel<bf16,swiglu>" and p["prep"] == "quant8_kernel<bf16>"
+    assert p["family"] == "fp8" and p["prep"] == "quant8_kernel<bf16>"
+    assert p["kernel"] == "gemm8_kernel<bf16,128x128,swiglu>"
     assert p["splits"] == 2 and p["grid"] == 224 * 2          # 224 tiles of 64 gate + 64 up rows, split in two
     p = _plan(1, 4096, 6144, w=e)
     assert p["splits"] == 8 and p["grid"] == 48 * 8
+    # enough 256 x 256 tiles for a round of CUs: the large tiles, unsplit
     p = _plan(16384, 4096, 22016, w=e, fn="swiglu")
-    assert p["splits"] == 1 and p["grid"] == 128 * 172
-    assert _plan(100, 512, 512, act=torch.float16, w=e, fn="gelu_tanh")["kernel"] == "gemm8_kernel<f16,gelu>"
+    assert p["kernel"] == "gemm8_kernel<bf16,256x256,swiglu>" and p["splits"] == 1 and p["grid"] == 64 * 86
+    assert _plan(16384, 4096, 12288, w=e)["grid"] == 64 * 48
+    p = _plan(100, 512, 512, act=torch.float16, w=e, fn="gelu_tanh")
+    assert p["kernel"] == "gemm8_kernel<f16,128x128,gelu>"
     # the workspace holds the codes and row scales (and the partials when split)
     assert fra.workspace_bytes(16384, 4096, 22016, torch.bfloat16, e) >= 16384 * 4096 + 16384 * 4
     assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 224 * 2 * 128 * 128 * 4
@@ -307,7 +311,7 @@ def test_plan_rejects():
 
 
 _ENV = ("FUSEDPROJ_SPLITS", "FUSEDPROJ_NO_STREAM", "FUSEDPROJ_NO_PREFILL", "FUSEDPROJ_STREAM_NR",
-        "FUSEDPROJ_STREAM_TARGET")
+        "FUSEDPROJ_STREAM_TARGET", "FUSEDPROJ_FP8_TILE")
 
 
 def _entry(**kw):

@@ -4,11 +4,12 @@ projection, bf16 and fp16 activations, every norm and epilogue, ragged token
 and column counts, split K, rows that quantise to zero, and the workloads at
 full size on sampled token rows.
 
-The oracle quantises the exactly normalised row (double precision); the
-kernels quantise the fp32-normalised row, so a code can differ where a
-scaled value sits within fp32 rounding of a midpoint between two E4M3 values
-(about one element in 2^19), which moves an output by far less than the
-tolerances of test_gpu_parity used here.
+Both sides decide every activation code in double precision (the oracle's
+exact normalisation, the quantisation kernel's fp64 statistics and scaling
+narrowed with round-to-odd), so the codes agree unless a scaled value lies
+within double rounding of a midpoint between two E4M3 values; the outputs
+then differ only by the fp32 accumulation and scaling, and the tolerances of
+test_gpu_parity apply.
 """
 import numpy as np
 import pytest
@@ -163,3 +164,24 @@ def test_fp8_workload_full_size(name):
                   "v", check("v", v, rq["v"]), flush=True)
             assert np.array_equal(h.double().numpy(), rq["h_out"]), "h_out not bit-exact"
         print(name, native, "out", check("out", res[("gu", native)], rg["out"]), flush=True)
+
+
+# the quantisation kernel's forms: one workgroup per row (up to 1024 tokens)
+# or one wave per row, the row kept in registers (up to 16 vectors of 8 per
+# thread) or read again for every pass
+@pytest.mark.parametrize("M,hidden", [(3, 33024), (1030, 8192), (1100, 8320), (1500, 512)],
+                         ids=["wg-reload", "wave-regs16", "wave-reload", "wave-regs1"])
+def test_fp8_quant_forms(M, hidden):
+    wl = _fp8(M=M, hidden=hidden, ffn=32, H=2, Hkv=1, D=16, norm="layer")
+    inp = inputs.generate(wl, seed=14)
+    d = to_dev(inp)
+    q, k, v, h = run_qkv(wl, d, torch.float32)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, 16)
+    rq = oracle.workload_qkv(wl, inp, row_idx=rows)
+    rg = oracle.workload_gateup(wl, inp, row_idx=rows)
+    check("q", q[rows], rq["q"])
+    check("v", v[rows], rq["v"])
+    check("out", out[rows], rg["out"])
+    assert np.array_equal(h[rows].double().cpu().numpy(), rq["h_out"])
