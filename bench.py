@@ -224,10 +224,10 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::quant8_kernel<(\d), \d+, \d+>", cxx)
     if m:
         return f"quant8_kernel<{_ACT[m.group(1)]}>"
-    m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), \d>", cxx)
+    m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), (\d), (\d)>", cxx)
     if m:
-        t = 64 * int(m.group(3))
-        return f"gemm8_kernel<{_ACT[m.group(1)]},{t}x{t},{_EPI[m.group(2)]}>"
+        fm, fn, wgm = int(m.group(3)), int(m.group(4)), int(m.group(5))
+        return f"gemm8_kernel<{_ACT[m.group(1)]},{32 * fm * wgm}x{32 * fn * (4 // wgm)},{_EPI[m.group(2)]}>"
     return cxx
 
 

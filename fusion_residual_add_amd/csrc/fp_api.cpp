@@ -49,7 +49,7 @@ struct Plan {
     bool deq = false;         // int4 weights staged as bf16 in the workspace first
     size_t deq_off = 0;
     size_t q_off = 0, qs_off = 0;   // FP8: activation codes [M, K] and row scales [M]
-    bool big8 = false;              // FP8: 256 x 256 tiles instead of 128 x 128
+    int tile8 = 0;                  // FP8: fp::Gemm8Tile
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -127,26 +127,40 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     Plan p;
     const Knobs kb = knobs_for(M, K, Nw, act, wdt, swiglu);
     if (wdt == FP_E4M3) {
-        // FP8 W8A8: one family whatever the token count.  256 x 256 tiles
-        // (SwiGLU: 128 gate + 128 up rows), one workgroup per CU, when they
-        // fill at least one round of CUs; otherwise 128 x 128 tiles, two
-        // workgroups per CU, with K split while fewer than two rounds of
-        // workgroups would run (at most 8 ways, at least 4 K steps of 128 per
-        // split).  FUSEDPROJ_FP8_TILE=128 / 256 forces a tile size.
+        // FP8 W8A8: one family whatever the token count.  Up to 32 / 64
+        // tokens: 32 x 256 / 64 x 256 tiles (the four waves share the token
+        // rows), K split while fewer than one workgroup per CU runs, at most
+        // 8 ways and at least 4 K steps of 128 per split (measured on MI355X,
+        // Llama-3-8B decode shapes: gate/up, 112 tiles, 41.7 / 31.0 / 33.8 /
+        // 46.6 us at 1 / 2 / 4 / 8 splits; QKV, 24 tiles, 26.2 / 19.2 / 15.5 /
+        // 17.2 / 25.0 us at 1 / 2 / 4 / 8 / 16: the partial sums cost more
+        // than a second workgroup per CU gains).  More tokens: 256 x 256
+        // tiles (SwiGLU: 128 gate + 128 up rows), one workgroup per CU, when
+        // they fill at least one round of CUs; otherwise 128 x 128 tiles, two
+        // workgroups per CU, K split while fewer than two rounds of
+        // workgroups run (same limits).  FUSEDPROJ_FP8_TILE = 32, 64,
+        // 128 or 256 forces a tile.
         p.family = 3;
         const int64_t big_tiles = ((M + 255) / 256) * (swiglu ? (Nw / 2 + 127) / 128 : (Nw + 255) / 256);
         const long tile_env = env_long("FUSEDPROJ_FP8_TILE", 0);
-        p.big8 = tile_env == 256 || (tile_env != 128 && big_tiles >= 256);
-        const int bt = p.big8 ? 256 : 128;
-        p.tiles_m = (int)((M + bt - 1) / bt);
-        p.tiles_n = (int)(swiglu ? (Nw / 2 + bt / 2 - 1) / (bt / 2) : (Nw + bt - 1) / bt);
-        p.tile_elems = (int64_t)bt * bt;
+        if (tile_env == 32) p.tile8 = fp::G8_32x256;
+        else if (tile_env == 64) p.tile8 = fp::G8_64x256;
+        else if (tile_env == 128) p.tile8 = fp::G8_128x128;
+        else if (tile_env == 256) p.tile8 = fp::G8_256x256;
+        else if (M <= 32) p.tile8 = fp::G8_32x256;
+        else if (M <= 64) p.tile8 = fp::G8_64x256;
+        else p.tile8 = big_tiles >= 256 ? fp::G8_256x256 : fp::G8_128x128;
+        static const int BMS[4] = {128, 256, 32, 64}, BNS[4] = {128, 256, 256, 256};
+        const int bm = BMS[p.tile8], bn = BNS[p.tile8];
+        p.tiles_m = (int)((M + bm - 1) / bm);
+        p.tiles_n = (int)(swiglu ? (Nw / 2 + bn / 2 - 1) / (bn / 2) : (Nw + bn - 1) / bn);
+        p.tile_elems = (int64_t)bm * bn;
         const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n, ksteps = K / 128;
-        int64_t s = tiles > 0 ? (p.big8 ? 256 : 512) / tiles : 1;
+        int64_t s = tiles > 0 ? (p.tile8 == fp::G8_128x128 ? 512 : 256) / tiles : 1;
         const int64_t cap = ksteps / 4 < 8 ? ksteps / 4 : 8;
         if (s > cap) s = cap;
         if (kb.splits > 0) s = kb.splits < ksteps ? kb.splits : ksteps;
-        if (s < 1 || p.big8) s = 1;   // the 256 x 256 kernel does not split K
+        if (s < 1 || p.tile8 == fp::G8_256x256) s = 1;   // the 256 x 256 kernel does not split K
         p.splits = p.slots = (int)s;
         size_t off = 0;
         p.ctr_off = off;
@@ -478,8 +492,8 @@ fp_status run_fp8(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.slots = plan.slots;
     pa.partials = plan.slots > 1 ? (float *)(ws + plan.part_off) : nullptr;
     pa.counters = ctr;
-    ProfScope ps(fp::gemm8_kernel_name(act, plan.big8, pa.epi), c.stream);
-    hipError_t e = fp::launch_gemm8(act, plan.big8, pa, c.stream);
+    ProfScope ps(fp::gemm8_kernel_name(act, plan.tile8, pa.epi), c.stream);
+    hipError_t e = fp::launch_gemm8(act, plan.tile8, pa, c.stream);
     if (e != hipSuccess) return hip_fail(e, "gemm8_kernel launch");
     return FP_OK;
 }
@@ -754,7 +768,7 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
         const int a8 = act_code(act_dtype);
         const int e8 = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
         snprintf(buf, cap, "family=fp8 kernel=%s grid=%lld splits=%d slots=%d workspace=%zu prep=%s",
-                 fp::gemm8_kernel_name(a8, p.big8, e8), (long long)p.tiles_m * p.tiles_n * p.splits, p.splits, p.slots,
+                 fp::gemm8_kernel_name(a8, p.tile8, e8), (long long)p.tiles_m * p.tiles_n * p.splits, p.splits, p.slots,
                  M == 0 ? (size_t)0 : p.total, fp::quant8_kernel_name(a8));
         return FP_OK;
     }

@@ -7,12 +7,15 @@
 //   y[m, c] = (sum_k e4m3(a[m, k]) e4m3(w[c, k])) * a_scale[m] * w_scale[c]
 //             (+ bias[c]), then the GQA split / SwiGLU / tanh-GELU / residual.
 //
-// One workgroup computes a (64 FM) tokens x (64 FN) weight rows tile with 4
-// waves in a 2 x 2 layout, each wave FM x FN fragments of 32 x 32 with fp32
-// accumulators: 128 x 128 (FM = FN = 2; two workgroups per CU, for token counts
-// whose tiles would not fill the chip) or 256 x 256 (FM = FN = 4; the 256
+// One workgroup computes a (32 FM WGM) tokens x (32 FN WGN) weight rows tile
+// with 4 waves in a WGM x WGN layout (WGN = 4 / WGM), each wave FM x FN
+// fragments of 32 x 32 with fp32 accumulators: 128 x 128 (2 x 2 waves of
+// 2 x 2 fragments; two workgroups per CU, for token counts whose large tiles
+// would not fill the chip), 256 x 256 (2 x 2 waves of 4 x 4 fragments; the 256
 // accumulators per lane live in AGPRs, one workgroup per CU, half the LDS
-// bytes read per MFMA).  For SwiGLU the weight rows of a tile are BN / 2 gate
+// bytes read per MFMA), and for decode token counts 32 x 256 or 64 x 256 (1 x 4
+// waves sharing the token rows, so no MFMA work goes to padding rows and most
+// of each stage is weights).  For SwiGLU the weight rows of a tile are BN / 2 gate
 // rows and the BN / 2 matching up rows, and each wave holds gate and up
 // fragments of the same columns, so SiLU(g) * u is formed in registers.  K
 // advances 128 codes (128 bytes) per step through two LDS stages of A and B,
@@ -24,6 +27,8 @@
 // once (half the bytes of the 16-bit rows the other kernels re-read per
 // column tile).
 #include "fp_device.hpp"
+
+#include <cstdio>
 
 namespace fp {
 
@@ -41,14 +46,16 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned ch
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 }  // namespace g8
 
-template <int ACT, int EPI, int FM, int FN>
+template <int ACT, int EPI, int FM, int FN, int WGM>
 __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjArgs p) {
     using T = Act<ACT>;
     using namespace g8;
     constexpr bool SW = EPI == EPI_SWIGLU;
-    constexpr int BM = 64 * FM, BN = 64 * FN;
+    constexpr int WGN = 4 / WGM;
+    constexpr int BM = 32 * FM * WGM, BN = 32 * FN * WGN;
     constexpr int TILEA = BM * BK, TILEB = BN * BK;
     constexpr int IA = BM / 32, IB = BN / 32;   // load instructions per wave and stage
+    static_assert(BM % 32 == 0 && BN % 32 == 0, "whole load instructions per wave");
     static_assert(!SW || FN % 2 == 0, "gate and up fragments in pairs");
     __shared__ __attribute__((aligned(16))) unsigned char lA0[TILEA];
     __shared__ __attribute__((aligned(16))) unsigned char lA1[TILEA];
@@ -57,7 +64,7 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WGM, wn = wave / WGM;
 
     // ---- tile: XCD-aware remap, then grouped raster (8 row tiles per group)
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -192,6 +199,7 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
     // ---- split K (128 x 128 tiles only): the last contributor of a tile
     // sums the partials in order
     if (FM * FN < 16 && p.splits > 1) {
+        static_assert(FM * FN * 16 * 256 == BM * BN || FM * FN >= 16, "one accumulator slot per tile element");
         constexpr int NACC = FM * FN * 16;
         float flat[NACC];
 #pragma unroll
@@ -215,8 +223,12 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
     constexpr int OUTC = SW ? 16 * FN : 32 * FN;   // output columns per wave
     constexpr int NJ = SW ? FN / 2 : FN;            // output fragments per wave
     constexpr int SROW = OUTC * 4 + 32;             // staging row pitch, bytes
-    static_assert(32 * SROW <= TILEA && 32 * SROW <= TILEB, "staging fits one tile buffer");
-    unsigned char *stg = wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
+    // each wave stages in its own half of a B tile buffer, or, where half of
+    // one is too small, in a whole tile buffer of its own
+    constexpr bool STG_B = 2 * 32 * SROW <= TILEB;
+    static_assert(STG_B || (32 * SROW <= TILEA && 32 * SROW <= TILEB), "staging fits");
+    unsigned char *stg = STG_B ? (wave < 2 ? lB0 : lB1) + (wave & 1) * (TILEB / 2)
+                               : wave == 0 ? lA0 : wave == 1 ? lA1 : wave == 2 ? lB0 : lB1;
     const int64_t col0 = SW ? (int64_t)tn * (BN / 2) + OUTC * wn : (int64_t)tn * BN + OUTC * wn;
     const int64_t ncols = SW ? p.F : p.Nw;
     // per-column weight scale and bias of this lane (SwiGLU: gate, then up)
@@ -295,40 +307,40 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
     }
 }
 
-template <int ACT, int F>
+template <int ACT, int FM, int FN, int WGM>
 static void launch_gemm8_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (a.epi) {
-    case EPI_QKV:    hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_QKV, F, F>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_SWIGLU, F, F>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_GELU:   hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_GELU, F, F>), dim3(grid), dim3(256), 0, s, a); break;
-    default:         hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_LINEAR, F, F>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_QKV:    hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_QKV, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_SWIGLU, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_GELU:   hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_GELU, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
+    default:         hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_LINEAR, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
     }
 }
 
-hipError_t launch_gemm8(int act, bool big, const ProjArgs &a, hipStream_t s) {
+template <int ACT>
+static void launch_gemm8_v(int tile, const ProjArgs &a, unsigned grid, hipStream_t s) {
+    switch (tile) {
+    case G8_256x256: launch_gemm8_t<ACT, 4, 4, 2>(a, grid, s); break;
+    case G8_32x256:  launch_gemm8_t<ACT, 1, 2, 1>(a, grid, s); break;
+    case G8_64x256:  launch_gemm8_t<ACT, 2, 2, 1>(a, grid, s); break;
+    default:         launch_gemm8_t<ACT, 2, 2, 2>(a, grid, s); break;
+    }
+}
+
+hipError_t launch_gemm8(int act, int tile, const ProjArgs &a, hipStream_t s) {
     const unsigned grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n * a.splits);
     if (grid == 0) return hipSuccess;
-    if (act == ACT_F16) {
-        if (big) launch_gemm8_t<ACT_F16, 4>(a, grid, s);
-        else launch_gemm8_t<ACT_F16, 2>(a, grid, s);
-    } else {
-        if (big) launch_gemm8_t<ACT_BF16, 4>(a, grid, s);
-        else launch_gemm8_t<ACT_BF16, 2>(a, grid, s);
-    }
+    if (act == ACT_F16) launch_gemm8_v<ACT_F16>(tile, a, grid, s);
+    else launch_gemm8_v<ACT_BF16>(tile, a, grid, s);
     return hipGetLastError();
 }
 
-const char *gemm8_kernel_name(int act, bool big, int epi) {
-    static const char *names[2][2][4] = {
-        {{"gemm8_kernel<bf16,128x128,qkv>", "gemm8_kernel<bf16,128x128,swiglu>", "gemm8_kernel<bf16,128x128,gelu>",
-          "gemm8_kernel<bf16,128x128,linear>"},
-         {"gemm8_kernel<bf16,256x256,qkv>", "gemm8_kernel<bf16,256x256,swiglu>", "gemm8_kernel<bf16,256x256,gelu>",
-          "gemm8_kernel<bf16,256x256,linear>"}},
-        {{"gemm8_kernel<f16,128x128,qkv>", "gemm8_kernel<f16,128x128,swiglu>", "gemm8_kernel<f16,128x128,gelu>",
-          "gemm8_kernel<f16,128x128,linear>"},
-         {"gemm8_kernel<f16,256x256,qkv>", "gemm8_kernel<f16,256x256,swiglu>", "gemm8_kernel<f16,256x256,gelu>",
-          "gemm8_kernel<f16,256x256,linear>"}}};
-    return names[act == ACT_F16 ? 1 : 0][big ? 1 : 0][epi & 3];
+const char *gemm8_kernel_name(int act, int tile, int epi) {
+    static const char *tiles[4] = {"128x128", "256x256", "32x256", "64x256"};
+    static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
+    static thread_local char buf[64];
+    snprintf(buf, sizeof buf, "gemm8_kernel<%s,%s,%s>", act == ACT_F16 ? "f16" : "bf16", tiles[tile & 3], epis[epi & 3]);
+    return buf;
 }
 
 }  // namespace fp

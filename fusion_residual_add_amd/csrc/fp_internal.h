@@ -100,8 +100,9 @@ const char *dequant_i4_kernel_name();
 // FP8 GEMM on the codes (x = codes, a_scale, w = E4M3 weights, w_scale [Nw])
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s);
 const char *quant8_kernel_name(int act);
-// big: 256 x 256 tiles (one workgroup per CU), otherwise 128 x 128
-hipError_t launch_gemm8(int act, bool big, const ProjArgs &a, hipStream_t s);
-const char *gemm8_kernel_name(int act, bool big, int epi);
+// FP8 GEMM tiles (tokens x weight rows)
+enum Gemm8Tile { G8_128x128 = 0, G8_256x256 = 1, G8_32x256 = 2, G8_64x256 = 3 };
+hipError_t launch_gemm8(int act, int tile, const ProjArgs &a, hipStream_t s);
+const char *gemm8_kernel_name(int act, int tile, int epi);
 
 }  // namespace fp

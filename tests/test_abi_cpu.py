@@ -186,10 +186,13 @@ def test_fp8_plans():
     # one family at every token count: per-token quantisation, then the FP8 GEMM
     p = _plan(32, 4096, 28672, w=e, fn="swiglu")
     assert p["family"] == "fp8" and p["prep"] == "quant8_kernel<bf16>"
-    assert p["kernel"] == "gemm8_kernel<bf16,128x128,swiglu>"
-    assert p["splits"] == 2 and p["grid"] == 224 * 2          # 224 tiles of 64 gate + 64 up rows, split in two
+    assert p["kernel"] == "gemm8_kernel<bf16,32x256,swiglu>"
+    assert p["splits"] == 2 and p["grid"] == 112 * 2          # 112 tiles of 128 gate + 128 up rows, split in two
+    assert _plan(64, 4096, 28672, w=e, fn="swiglu")["kernel"] == "gemm8_kernel<bf16,64x256,swiglu>"
     p = _plan(1, 4096, 6144, w=e)
-    assert p["splits"] == 8 and p["grid"] == 48 * 8
+    assert p["splits"] == 8 and p["grid"] == 24 * 8
+    p = _plan(200, 4096, 6144, w=e)
+    assert p["kernel"] == "gemm8_kernel<bf16,128x128,linear>" and p["splits"] == 5 and p["grid"] == 2 * 48 * 5
     # enough 256 x 256 tiles for a round of CUs: the large tiles, unsplit
     p = _plan(16384, 4096, 22016, w=e, fn="swiglu")
     assert p["kernel"] == "gemm8_kernel<bf16,256x256,swiglu>" and p["splits"] == 1 and p["grid"] == 64 * 86
@@ -198,13 +201,18 @@ def test_fp8_plans():
     assert p["kernel"] == "gemm8_kernel<f16,128x128,gelu>"
     # the workspace holds the codes and row scales (and the partials when split)
     assert fra.workspace_bytes(16384, 4096, 22016, torch.bfloat16, e) >= 16384 * 4096 + 16384 * 4
-    assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 224 * 2 * 128 * 128 * 4
+    assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 112 * 2 * 32 * 256 * 4
     assert fra.workspace_bytes(8, 320, 512, torch.bfloat16, e) == 0      # hidden % 128
     os.environ["FUSEDPROJ_SPLITS"] = "3"
+    os.environ["FUSEDPROJ_FP8_TILE"] = "128"
     try:
-        assert _plan(1, 4096, 6144, w=e)["splits"] == 3
+        p = _plan(1, 4096, 6144, w=e)
+        assert p["splits"] == 3 and p["kernel"] == "gemm8_kernel<bf16,128x128,linear>"
+        os.environ["FUSEDPROJ_FP8_TILE"] = "256"
+        assert _plan(1, 4096, 6144, w=e)["splits"] == 1      # the 256 x 256 kernel does not split K
     finally:
         os.environ.pop("FUSEDPROJ_SPLITS")
+        os.environ.pop("FUSEDPROJ_FP8_TILE")
 
 
 def test_binding_refuses_cpu_tensors():

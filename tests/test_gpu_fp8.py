@@ -80,6 +80,28 @@ def test_fp8_splits(splits, M, monkeypatch):
     check("out", out, rg["out"])
 
 
+@pytest.mark.parametrize("tile", ["32", "64", "128", "256"])
+@pytest.mark.parametrize("M", [1, 40, 100, 300])
+def test_fp8_tiles(tile, M, monkeypatch):
+    # every tile form at token counts below, inside and above its own height
+    monkeypatch.setenv("FUSEDPROJ_FP8_TILE", tile)
+    wl = _fp8(M=M, hidden=512, ffn=272, H=6, Hkv=2, D=32, act_fn="swiglu", bias=True)
+    inp = inputs.generate(wl, seed=15)
+    d = to_dev(inp)
+    plan = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, torch.bfloat16, torch.float8_e4m3fn, "swiglu")
+    print(f"fp8 tile {tile} M={M}: {plan['kernel']} splits={plan['splits']}", flush=True)
+    assert f",{tile}x" in plan["kernel"]
+    q, k, v, _ = run_qkv(wl, d, torch.float32)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    rq = oracle.workload_qkv(wl, inp)
+    rg = oracle.workload_gateup(wl, inp)
+    check("q", q, rq["q"])
+    check("k", k, rq["k"])
+    check("v", v, rq["v"])
+    check("out", out, rg["out"])
+
+
 def test_fp8_zero_rows_and_bias():
     # rows whose normalised values are all zero quantise to zero codes with a
     # zero scale: the output is the bias alone

@@ -1,5 +1,5 @@
 """Seeded random configurations against the oracle: token counts, widths,
-head layouts, dtypes (bf16, fp16, fp32, int8, int4 weights), norms,
+head layouts, dtypes (bf16, fp16, fp32, int8, int4 and E4M3 weights), norms,
 epilogues, bias, residual and output dtype drawn at random (fixed seeds), so
 that combinations no hand-written case names still meet the parity bounds.
 Each case prints its configuration before running."""
@@ -38,7 +38,33 @@ def _config(seed):
 
 @pytest.mark.parametrize("seed", range(48))
 def test_random_configuration(seed):
-    cfg, native = _config(seed)
+    _run_case(seed, *_config(seed))
+
+
+def _config_fp8(seed):
+    rng = np.random.default_rng(2000 + seed)
+    act = str(rng.choice(["bf16", "bf16", "f16"]))
+    hidden = 128 * int(rng.integers(1, 33))
+    M = int(rng.choice([rng.integers(1, 65), rng.integers(65, 600)]))
+    Hkv = int(rng.integers(1, 5))
+    H = Hkv * int(rng.integers(1, 5))
+    D = 16 * int(rng.integers(1, 9))
+    ffn = 16 * int(rng.integers(1, 40))
+    norm = str(rng.choice(["rms", "rms", "layer", "none"]))
+    act_fn = str(rng.choice(["swiglu", "swiglu", "gelu_tanh", "none"]))
+    bias = bool(rng.integers(0, 2))
+    native = bool(rng.integers(0, 2))
+    return dict(act=act, wdt="e4m3", M=M, hidden=hidden, H=H, Hkv=Hkv, D=D, ffn=ffn, norm=norm, act_fn=act_fn,
+                bias=bias), native
+
+
+# E4M3 weights with per-token E4M3 activations (FP8 W8A8), 24 more seeds
+@pytest.mark.parametrize("seed", range(24))
+def test_random_fp8_configuration(seed):
+    _run_case(seed, *_config_fp8(seed))
+
+
+def _run_case(seed, cfg, native):
     wl = small(**cfg)
     inp = inputs.generate(wl, seed=seed)
     if cfg["bias"]:
