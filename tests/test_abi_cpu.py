@@ -399,18 +399,26 @@ def test_tuning_table_json_round_trip(tmp_path):
     from fusion_residual_add_amd import tune
     entries = [_entry(family="stream", rows=256, grid=240, w_dtype=torch.uint8, hidden=8192, n_cols=10240),
                _entry(family="tiled", splits=4, act_dtype=torch.float32, w_dtype=torch.float32),
-               _entry(rows=256, w_dtype=torch.int8)]
+               _entry(rows=256, w_dtype=torch.int8), _entry(splits=3, w_dtype=torch.float8_e4m3fn)]
     path = str(tmp_path / "table.json")
     tune.save(entries, path)
     back = tune.load(path)
     assert back == entries
     try:
         fra.tune_install(back)
-        assert fra.tune_count() == 3
+        assert fra.tune_count() == 4
         p = _plan(20, 8192, 10240, w=torch.uint8)
         assert p["kernel"] == "stream_kernel<bf16-i4w,m32,n256,k256,linear>" and p["grid"] == 240
     finally:
         fra.tune_clear()
+
+
+def test_tuner_candidates_fp8_splits():
+    from fusion_residual_add_amd import tune
+    c = tune.candidates(32, 4096, 28672, torch.bfloat16, torch.float8_e4m3fn, True)
+    assert {x["plan"]["family"] for x in c} == {"fp8"}
+    assert sorted(x["plan"]["splits"] for x in c) == [1, 2, 3, 4, 6, 8]
+    assert fra.tune_count() == 0
 
 
 def test_tuner_candidates_cover_every_family():

@@ -2,7 +2,8 @@
 
 Every candidate configuration the tuner can install for a shape (kernel
 family, rows per workgroup, workgroup count, K split; including the 128 x 512
-kernel at decode token counts and the tiled kernel at any count) must give
+kernel at decode token counts and the tiled kernel at any count; the K split
+of the FP8 kernel) must give
 results within the parity bounds against the oracle; the tuner itself must
 time the candidates and return a valid entry or keep the planner's choice.
 """
@@ -33,7 +34,7 @@ def _check(name, got, ref):
     assert rel <= 5e-3 and err.max() <= 2e-2, f"{name}: max-abs {err.max():.3e} rel-fro {rel:.3e}"
 
 
-@pytest.mark.parametrize("M,wdt", [(5, "bf16"), (40, "i8"), (100, "bf16")])
+@pytest.mark.parametrize("M,wdt", [(5, "bf16"), (40, "i8"), (100, "bf16"), (5, "e4m3"), (100, "e4m3")])
 def test_every_candidate_meets_parity(M, wdt):
     wl = _wl(M, wdt)
     inp = inputs.generate(wl, seed=4)
@@ -80,3 +81,13 @@ def test_tuner_times_candidates_and_returns_an_entry_or_none():
         finally:
             fra.tune_clear()
     assert fra.tune_count() == 0
+
+
+def test_tuner_fp8_splits():
+    # E4M3 weights: the candidates differ in their K split only
+    wl = _wl(24, "e4m3")
+    r = tune.tune_call(wl, "gu", reps=3, rounds=2, log=lambda s: print(s, flush=True))
+    assert r["default_us"] > 0 and len(r["results"]) >= 3
+    assert all(c["kernel"].startswith("gemm8_kernel") for c, _ in r["results"])
+    assert fra.tune_count() == 0
+
