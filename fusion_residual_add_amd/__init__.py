@@ -117,8 +117,9 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
                        write_h: bool = True, out_dtype: Optional[torch.dtype] = None,
                        h_out: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
                        k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None):
-    """residual add + norm -> QKV projection (+bias) -> q [M,H,D], k/v [M,Hkv,D].
+                       workspace: Optional[torch.Tensor] = None, head_major: bool = False):
+    """residual add + norm -> QKV projection (+bias) -> q [M,H,D], k/v [M,Hkv,D]
+    (``head_major``: q [H,M,D], k/v [Hkv,M,D], through fused_add_norm_qkv_hm).
 
     Returns (q, k, v, h_out) where h_out = rne(x + residual) (None when
     ``write_h`` is False and no h_out tensor was passed)."""
@@ -131,18 +132,24 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
     wdt = w_qkv.dtype
     Nw = (n_heads + 2 * n_kv_heads) * head_dim
     _check_weight(w_qkv, w_scale, Nw, K, "w_qkv")
+    qs = (n_heads, M, head_dim) if head_major else (M, n_heads, head_dim)
+    kvs = (n_kv_heads, M, head_dim) if head_major else (M, n_kv_heads, head_dim)
     if q is None:
-        q = torch.empty((M, n_heads, head_dim), dtype=odt, device=dev)
+        q = torch.empty(qs, dtype=odt, device=dev)
     if k is None:
-        k = torch.empty((M, n_kv_heads, head_dim), dtype=odt, device=dev)
+        k = torch.empty(kvs, dtype=odt, device=dev)
     if v is None:
-        v = torch.empty((M, n_kv_heads, head_dim), dtype=odt, device=dev)
+        v = torch.empty(kvs, dtype=odt, device=dev)
+    for t, shape, name in ((q, qs, "q"), (k, kvs, "k"), (v, kvs, "v")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
     if h_out is None and write_h:
         h_out = torch.empty_like(x)
     stream = _stream(dev)
     need = int(lib.fp_workspace_bytes(M, K, Nw, _DT[act], _DT[wdt]))
     ws = workspace if workspace is not None else _workspace(dev, stream, need)
-    st = lib.fused_add_norm_qkv(
+    fn = lib.fused_add_norm_qkv_hm if head_major else lib.fused_add_norm_qkv
+    st = fn(
         _ptr(x, "x", dev, act), _ptr(residual, "residual", dev, act), _ptr(h_out, "h_out", dev, act),
         _ptr(gamma, "gamma", dev, act), _ptr(beta, "beta", dev, act), FP_NORM[norm], float(eps),
         _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, torch.float32),

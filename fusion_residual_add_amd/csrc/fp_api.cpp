@@ -594,13 +594,17 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype ac
     return a > b ? a : b;
 }
 
-fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, const void *gamma,
-                             const void *beta, fp_norm norm, float eps, const void *w_qkv,
-                             const float *w_scale, const void *bias, void *q, void *k, void *v,
-                             int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
-                             int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
-                             fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
-                             void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const void *gamma,
+                       const void *beta, fp_norm norm, float eps, const void *w_qkv,
+                       const float *w_scale, const void *bias, void *q, void *k, void *v,
+                       int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
+                       int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
+                       fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                       void *hip_stream, bool head_major) {
     if (n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads != 0)
         return fail(FP_E_SHAPE, "n_heads = %lld, n_kv_heads = %lld: both must be > 0 and n_heads a multiple of n_kv_heads",
                     (long long)n_heads, (long long)n_kv_heads);
@@ -635,8 +639,38 @@ fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, c
     pa.out2 = v;
     pa.nq = nq;
     pa.nkv = nkv;
+    pa.qkv_hm = head_major ? 1 : 0;
+    pa.head_dim = head_dim;
     pa.F = c.Nw;
     return run(c, plan, pa);
+}
+
+}  // namespace
+
+extern "C" {
+
+fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, const void *gamma,
+                             const void *beta, fp_norm norm, float eps, const void *w_qkv,
+                             const float *w_scale, const void *bias, void *q, void *k, void *v,
+                             int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
+                             int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
+                             fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+    return add_norm_qkv(x, residual, h_out, gamma, beta, norm, eps, w_qkv, w_scale, bias, q, k, v, M, hidden,
+                        n_heads, n_kv_heads, head_dim, act_dtype, w_dtype, out_dtype, workspace,
+                        workspace_bytes, hip_stream, false);
+}
+
+fp_status fused_add_norm_qkv_hm(const void *x, const void *residual, void *h_out, const void *gamma,
+                                const void *beta, fp_norm norm, float eps, const void *w_qkv,
+                                const float *w_scale, const void *bias, void *q, void *k, void *v,
+                                int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
+                                int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
+                                fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                                void *hip_stream) {
+    return add_norm_qkv(x, residual, h_out, gamma, beta, norm, eps, w_qkv, w_scale, bias, q, k, v, M, hidden,
+                        n_heads, n_kv_heads, head_dim, act_dtype, w_dtype, out_dtype, workspace,
+                        workspace_bytes, hip_stream, true);
 }
 
 fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, const void *gamma,

@@ -235,8 +235,20 @@ __device__ __forceinline__ float gelu_tanh(float y) {
 // ---------------------------------------------------------------------------
 // epilogue stores
 // ---------------------------------------------------------------------------
+// Element index of column cc (relative to its block) of token m in the q, k
+// or v output whose block is `width` columns wide: token-major
+// [M, heads, D] -> m * width + cc, or head-major [heads, M, D] ->
+// (h * M + m) * D + d with h = cc / D, d = cc % D.  A run of 8 columns
+// starting at a multiple of 8 stays inside one head (D is a multiple of 16)
+// and is contiguous in both layouts.
+__device__ __forceinline__ int64_t qkv_index(const ProjArgs &p, int64_t m, int64_t cc, int64_t width) {
+    if (!p.qkv_hm) return m * width + cc;
+    const int h = (int)cc / (int)p.head_dim;
+    return ((int64_t)h * p.M + m) * p.head_dim + (cc - (int64_t)h * p.head_dim);
+}
+
 // Column c of the projection (bias already added) to its destination: the GQA
-// split for QKV (q | k | v column blocks, token-major), tanh-GELU or nothing for
+// split for QKV (q | k | v column blocks, token- or head-major), tanh-GELU or nothing for
 // the up projection, plus the residual for the down projection.  The residual
 // element is read by the thread that writes the output element, so the output
 // may be the residual buffer itself.
@@ -246,9 +258,9 @@ __device__ __forceinline__ void store_col(const ProjArgs &p, int64_t m, int64_t 
     void *dst;
     int64_t idx;
     if constexpr (EPI == EPI_QKV) {
-        if (c < p.nq)              { dst = p.out0; idx = m * p.nq + c; }
-        else if (c < p.nq + p.nkv) { dst = p.out1; idx = m * p.nkv + (c - p.nq); }
-        else                       { dst = p.out2; idx = m * p.nkv + (c - p.nq - p.nkv); }
+        if (c < p.nq)              { dst = p.out0; idx = qkv_index(p, m, c, p.nq); }
+        else if (c < p.nq + p.nkv) { dst = p.out1; idx = qkv_index(p, m, c - p.nq, p.nkv); }
+        else                       { dst = p.out2; idx = qkv_index(p, m, c - p.nq - p.nkv, p.nkv); }
     } else {
         if constexpr (EPI == EPI_GELU) y = gelu_tanh(y);
         dst = p.out0;

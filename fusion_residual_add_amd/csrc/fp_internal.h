@@ -45,6 +45,8 @@ struct ProjArgs {
     void *out1;             // k (QKV)
     void *out2;             // v (QKV)
     int64_t nq, nkv;        // QKV column split: [0,nq) q, [nq,nq+nkv) k, rest v
+    int qkv_hm;             // QKV outputs head-major [heads, M, head_dim] (else token-major)
+    int64_t head_dim;       // QKV: D (head-major addressing)
     int64_t F;              // SwiGLU / GELU / linear output width
     // sizes
     int64_t M, K, Nw;       // Nw = weight rows

@@ -515,9 +515,9 @@ void prefill_kernel(ProjArgs p) {
             if (m >= p.M || cg >= ncols) continue;
             char *dst;
             if constexpr (EPI == EPI_QKV) {
-                if (cg < p.nq)              dst = (char *)p.out0 + (m * p.nq + cg) * esz;
-                else if (cg < p.nq + p.nkv) dst = (char *)p.out1 + (m * p.nkv + (cg - p.nq)) * esz;
-                else                        dst = (char *)p.out2 + (m * p.nkv + (cg - p.nq - p.nkv)) * esz;
+                if (cg < p.nq)              dst = (char *)p.out0 + qkv_index(p, m, cg, p.nq) * esz;
+                else if (cg < p.nq + p.nkv) dst = (char *)p.out1 + qkv_index(p, m, cg - p.nq, p.nkv) * esz;
+                else                        dst = (char *)p.out2 + qkv_index(p, m, cg - p.nq - p.nkv, p.nkv) * esz;
             } else {
                 dst = (char *)p.out0 + (m * ncols + cg) * esz;
             }

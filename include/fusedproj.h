@@ -136,6 +136,23 @@ fp_status fused_add_norm_qkv(
     fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
     void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* fused_add_norm_qkv with head-major outputs, for an attention kernel that
+ * reads one head's rows contiguously (each tensor-parallel rank computes
+ * attention for its own group of heads: "TensorRT-LLM 深度工程实践…" §4.1;
+ * the reshape into GQA head groups of §2.2):
+ *  q    : [H, M, D]   out_dtype, q[h, m, d] = column h * D + d of token m
+ *  k, v : [Hkv, M, D] out_dtype, likewise for the K and V column blocks
+ * Every other argument, requirement and error as for fused_add_norm_qkv; the
+ * values are the same, only their positions differ. */
+fp_status fused_add_norm_qkv_hm(
+    const void *x, const void *residual, void *h_out,
+    const void *gamma, const void *beta, fp_norm norm, float eps,
+    const void *w_qkv, const float *w_scale, const void *bias,
+    void *q, void *k, void *v,
+    int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+    fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
+    void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* (Residual add + norm ->) gate/up or up projection (+ bias) -> activation.
  * ("TensorRT-LLM 深度工程实践…", §2.3 SwiGLU fusion sketch; "TRT-LLM deep
  * dive", Layer Fusion figure / LayerNorm + Linear + GELU.)

@@ -64,7 +64,8 @@ def qkv(**kw):
              q=FAKE + 0x40000000, k=FAKE + 0x50000000, v=FAKE + 0x60000000, M=0, hidden=4096,
              H=32, Hkv=8, D=128, act=BF16, wdt=BF16, odt=BF16, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
-    st = lib().fused_add_norm_qkv(a["x"], a["residual"], a["h_out"], a["gamma"], a["beta"], a["norm"],
+    fn = lib().fused_add_norm_qkv_hm if a.pop("head_major", False) else lib().fused_add_norm_qkv
+    st = fn(a["x"], a["residual"], a["h_out"], a["gamma"], a["beta"], a["norm"],
                                   a["eps"], a["w"], a["w_scale"], a["bias"], a["q"], a["k"], a["v"],
                                   a["M"], a["hidden"], a["H"], a["Hkv"], a["D"], a["act"], a["wdt"],
                                   a["odt"], a["ws"], a["ws_bytes"], a["stream"])
@@ -85,6 +86,7 @@ def gu(**kw):
 
 def test_m_zero_is_a_noop():
     assert qkv(M=0)[0] == "FP_OK"
+    assert qkv(M=0, head_major=True)[0] == "FP_OK"
     assert gu(M=0)[0] == "FP_OK"
 
 
@@ -125,6 +127,9 @@ def test_qkv_rejects(kw, status):
     got, msg = qkv(**kw)
     assert got == status, msg
     assert msg
+    # the head-major entry point validates alike (same sizes, same ranges)
+    got_hm, _ = qkv(head_major=True, **kw)
+    assert got_hm == status
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -415,3 +415,49 @@ def test_launch_configs(env, M, monkeypatch):
     check("q", q, rq["q"])
     check("v", v, rq["v"])
     check("out", out, rg["out"])
+
+
+# ---------------------------------------------------------------------------
+# head-major q / k / v (fused_add_norm_qkv_hm): the same values as the
+# token-major call, q[h, m, d] = q_token_major[m, h, d], on every kernel family
+# ---------------------------------------------------------------------------
+HEAD_MAJOR = [
+    dict(act="bf16", M=17, hidden=512),                         # weight-streaming kernel
+    dict(act="bf16", M=5, hidden=320),                          # tiled kernel (hidden % 256)
+    dict(act="bf16", M=130, hidden=512, H=8, Hkv=8, D=16),      # 128 x 512 kernel, MHA
+    dict(act="f16", M=200, hidden=320, norm="layer"),
+    dict(act="f32", M=40, hidden=256),
+    dict(act="bf16", wdt="i8", M=33, hidden=512),
+    dict(act="bf16", wdt="e4m3", M=9, hidden=512),               # FP8 kernel, decode tile
+    dict(act="bf16", wdt="e4m3", M=300, hidden=384, H=5, Hkv=1, D=48),
+]
+
+
+@pytest.mark.parametrize("cfg", HEAD_MAJOR, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("native", [False, True], ids=["f32out", "nativeout"])
+def test_qkv_head_major(cfg, native):
+    if cfg["act"] == "f32" and native:
+        pytest.skip("fp32 activations: the native output is the fp32 output")
+    wl = small(bias=True, **cfg)
+    inp = inputs.generate(wl, seed=16)
+    inp["b_qkv"] = inputs._to_act(np.random.default_rng(16).standard_normal(wl.n_qkv).astype(np.float32)
+                                  * np.float32(0.1), wl.act)
+    d = to_dev(inp)
+    odt = None if native else torch.float32
+    kw = dict(beta=d.get("beta"), norm=wl.norm, eps=wl.eps, w_scale=d.get("s_qkv"), bias=d["b_qkv"],
+              out_dtype=odt)
+    q, k, v, h = fra.fused_add_norm_qkv(d["x"], d["r"], d["gamma"], d["w_qkv"], wl.n_heads, wl.n_kv_heads,
+                                        wl.head_dim, head_major=True, **kw)
+    qt, kt, vt, _ = fra.fused_add_norm_qkv(d["x"], d["r"], d["gamma"], d["w_qkv"], wl.n_heads, wl.n_kv_heads,
+                                           wl.head_dim, **kw)
+    torch.cuda.synchronize()
+    assert q.shape == (wl.n_heads, wl.M, wl.head_dim) and k.shape == (wl.n_kv_heads, wl.M, wl.head_dim)
+    rq = oracle.workload_qkv(wl, inp)
+    # against the oracle, head-major positions
+    check("q", q, rq["q"].transpose(1, 0, 2))
+    check("k", k, rq["k"].transpose(1, 0, 2))
+    check("v", v, rq["v"].transpose(1, 0, 2))
+    # and bit for bit the token-major call's values
+    for a, b in ((q, qt), (k, kt), (v, vt)):
+        assert torch.equal(a.transpose(0, 1).contiguous().view(torch.int8), b.contiguous().view(torch.int8))
+    assert np.array_equal(h.double().cpu().numpy(), rq["h_out"])
