@@ -506,19 +506,24 @@ def main():
 
     if not args.no_secondary:
         sec = {}
-        for name in ("llama2-7b-prefill", "llama2-7b-prefill-fp8"):
+        for name in ("llama2-7b-prefill", "llama2-7b-prefill-fp8", "llama3-8b-decode-fp8"):
             pwl = inputs.workload(name)
-            ppeak = MFMA_FP8_PEAK_TFLOPS if pwl.wdt == "e4m3" else MFMA_BF16_PEAK_TFLOPS
             pr = Runner(pwl)
-            pms = time_steps(pr.step, args.prefill_steps, 3)
+            pms = time_steps(pr.step, args.prefill_steps if pwl.M > 64 else 100, 3)
             pfl = flops(pwl, "qkv") + flops(pwl, "gu")
+            pby = algo_bytes(wl=pwl, call="qkv") + algo_bytes(wl=pwl, call="gu")
             pprof = profile_call(pr, "gu", 5)
             pk = max(pprof, key=lambda k: pprof[k])
             pq = profile_call(pr, "qkv", 5)
-            sec[name] = {"value": round(pfl / (pms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            if pwl.M > 64:      # prefill: matrix-core bound
+                ppeak = MFMA_FP8_PEAK_TFLOPS if pwl.wdt == "e4m3" else MFMA_BF16_PEAK_TFLOPS
+                pval, punit = pfl / (pms * 1e-3) / 1e12, "TFLOP/s"
+            else:               # decode: HBM bound (algorithmic bytes)
+                ppeak, pval, punit = HBM_PEAK_GBS, pby / (pms * 1e-3) / 1e9, "GB/s"
+            sec[name] = {"value": round(pval, 2), "unit": punit,
                          "ms_per_step": round(pms, 4),
                          "dtype": "e4m3" if pwl.wdt == "e4m3" else pwl.act, "peak": ppeak,
-                         "frac_of_peak": round(pfl / (pms * 1e-3) / 1e12 / ppeak, 4),
+                         "frac_of_peak": round(pval / ppeak, 4),
                          "kernel_us": {"gu": {k: round(v * 1e3, 1) for k, v in pprof.items()},
                                        "qkv": {k: round(v * 1e3, 1) for k, v in pq.items()}}}
             del pr
