@@ -129,8 +129,9 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     if (wdt == FP_E4M3) {
         // FP8 W8A8: one family whatever the token count.  Up to 32 / 64
         // tokens: 32 x 256 / 64 x 256 tiles (the four waves share the token
-        // rows), K split while fewer than one workgroup per CU runs, at most
-        // 8 ways and at least 4 K steps of 128 per split (measured on MI355X,
+        // rows), K split while fewer than one workgroup per CU runs and each
+        // workgroup still streams at least 256 KB of weights, at most 8 ways
+        // and at least 4 K steps of 128 per split (measured on MI355X,
         // Llama-3-8B decode shapes: gate/up, 112 tiles, 41.7 / 31.0 / 33.8 /
         // 46.6 us at 1 / 2 / 4 / 8 splits; QKV, 24 tiles, 26.2 / 19.2 / 15.5 /
         // 17.2 / 25.0 us at 1 / 2 / 4 / 8 / 16: the partial sums cost more
@@ -159,6 +160,10 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         int64_t s = tiles > 0 ? (p.tile8 == fp::G8_128x128 ? 512 : 256) / tiles : 1;
         const int64_t cap = ksteps / 4 < 8 ? ksteps / 4 : 8;
         if (s > cap) s = cap;
+        if (p.tile8 == fp::G8_32x256 || p.tile8 == fp::G8_64x256) {
+            const int64_t by_bytes = tiles > 0 ? Nw * K / (tiles * (int64_t(256) << 10)) : 1;
+            if (s > by_bytes) s = by_bytes;
+        }
         if (kb.splits > 0) s = kb.splits < ksteps ? kb.splits : ksteps;
         if (s < 1 || p.tile8 == fp::G8_256x256) s = 1;   // the 256 x 256 kernel does not split K
         p.splits = p.slots = (int)s;
