@@ -434,7 +434,7 @@ def main():
         all_configs_summarize(args.all_configs_summarize, args.cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the projections shard by heads / by gate-up pairs without communication; "
               "see the design notes).", file=sys.stderr)
         sys.exit(2)

@@ -1,0 +1,62 @@
+"""The benchmark's host-side accounting (no GPU): the algorithmic bytes and
+flops each roofline figure divides by, the mapping from the demangled kernel
+names rocprofv3 prints to the library's own names (the profiles are keyed by
+them), and the refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from fusion_residual_add_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algo_bytes_decode_gate_up():
+    wl = inputs.workload("llama3-8b-decode")
+    # weights 28672 x 4096 bf16, x and r for 32 tokens, gamma, the 32 x 14336 output
+    assert bench.algo_bytes(wl, "gu") == 28672 * 4096 * 2 + 2 * 32 * 4096 * 2 + 4096 * 2 + 32 * 14336 * 2
+    # QKV adds h_out and stores q, k, v
+    assert bench.algo_bytes(wl, "qkv") == (6144 * 4096 * 2 + 2 * 32 * 4096 * 2 + 4096 * 2 + 32 * 4096 * 2
+                                           + 32 * 6144 * 2)
+    assert bench.flops(wl, "gu") == 2 * 32 * 4096 * 28672
+
+
+@pytest.mark.parametrize("name,wbytes,scales", [("llama2-70b-int8w@M16", 1, 4), ("llama2-70b-int4w@M16", 0.5, 4 * 64),
+                                                 ("llama3-8b-decode-fp8", 1, 4)])
+def test_algo_bytes_quantised_weights(name, wbytes, scales):
+    wl = inputs.workload(name)
+    base = bench.algo_bytes(wl, "gu") - int(wl.n_gu * wl.hidden * wbytes) - wl.n_gu * scales
+    assert base == 2 * wl.M * wl.hidden * 2 + wl.hidden * 2 + wl.M * wl.ffn * 2
+
+
+def test_algo_bytes_down():
+    wl = inputs.workload("llama3-8b-decode")
+    assert bench.algo_bytes(wl, "down") == 32 * 14336 * 2 + 2 * 32 * 4096 * 2 + 4096 * 14336 * 2
+    assert bench.flops(wl, "down") == 2 * 32 * 14336 * 4096
+
+
+@pytest.mark.parametrize("cxx,name", [
+    ("void fp::stream_kernel<2, 0, 2, 2, 8, 1>(fp::ProjArgs)", "stream_kernel<bf16,m32,n128,k256,swiglu>"),
+    ("void fp::stream_kernel<2, 1, 4, 4, 4, 0>(fp::ProjArgs)", "stream_kernel<bf16-i8w,m64,n256,k128,qkv>"),
+    ("void fp::stream_kernel<2, 2, 1, 2, 8, 1>(fp::ProjArgs)", "stream_kernel<bf16-i4w,m16,n128,k256,swiglu>"),
+    ("void fp::prefill_kernel<1, 0, 2, true>(fp::ProjArgs)", "prefill_kernel<f16,128x512,gelu>"),
+    ("void fp::prefill_kernel<2, 1, 1, false>(fp::ProjArgs)", "prefill_kernel<bf16-i8w,128x512,swiglu>"),
+    ("void fp::stats_kernel<2, 256>(fp::StatsArgs)", "stats_kernel<bf16>"),
+    ("void fp::quant8_kernel<1, 64, 8>(fp::StatsArgs)", "quant8_kernel<f16>"),
+    ("void fp::gemm8_kernel<2, 1, 4, 4, 2>(fp::ProjArgs)", "gemm8_kernel<bf16,256x256,swiglu>"),
+    ("void fp::gemm8_kernel<2, 0, 1, 2, 1>(fp::ProjArgs)", "gemm8_kernel<bf16,32x256,qkv>"),
+    ("void fp::gemm8_kernel<1, 3, 2, 2, 2>(fp::ProjArgs)", "gemm8_kernel<f16,128x128,linear>"),
+    ("void fp::gemm8_kernel<2, 2, 2, 2, 1>(fp::ProjArgs)", "gemm8_kernel<bf16,64x256,gelu>"),
+])
+def test_library_kernel_names(cxx, name):
+    assert bench.library_kernel_name(cxx) == name
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
