@@ -376,10 +376,16 @@ void stream_kernel(ProjArgs p) {
 
     int64_t u = units * g / G;
     const int64_t u_end = units * (g + 1) / G;
+    bool first_segment = true;
     while (u < u_end) {
         const int tn = (int)(u / nchunks), c0 = (int)(u % nchunks);
         const int64_t left = u_end - u;
         const int c1 = left < nchunks - c0 ? c0 + (int)left : nchunks;
+        // a segment that no other workgroup shares ends without a barrier, its
+        // last chunk possibly read from LDS buffer 0: every wave must be done
+        // with it before the next segment's prologue normalises into buffer 0
+        if (!first_segment) __syncthreads();
+        first_segment = false;
         segment(tn, c0, c1);
         u += c1 - c0;
     }
@@ -389,21 +395,17 @@ void stream_kernel(ProjArgs p) {
 // launch helpers (instantiated per activation / weight dtype in fp_stream_*.hip)
 // ---------------------------------------------------------------------------
 template <int ACT, int WQ, int MF, int NR, int U>
-inline void launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStream_t s) {
+inline hipError_t launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (epi) {
     case EPI_QKV:
-        hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_QKV>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_QKV>, grid, s, a);
     case EPI_SWIGLU:
-        if constexpr (NR % 2 == 0)
-            hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_SWIGLU>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        if constexpr (NR % 2 == 0) return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_SWIGLU>, grid, s, a);
+        return hipErrorInvalidValue;
     case EPI_GELU:
-        hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_GELU>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_GELU>, grid, s, a);
     default:
-        hipLaunchKernelGGL((stream_kernel<ACT, WQ, MF, NR, U, EPI_LINEAR>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_LINEAR>, grid, s, a);
     }
 }
 
@@ -413,23 +415,23 @@ inline void launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStre
 // tokens, 256 (NR = 4) only for int8 / int4 weights; only those combinations
 // are instantiated.
 template <int ACT, int WQ, int MF>
-inline void launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
+inline hipError_t launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
     constexpr int U = MF >= 4 ? 4 : 8;
-    if (c.nr == 2) {
-        launch_stream_cfg<ACT, WQ, MF, 2, U>(a.epi, a, grid, s);
-    } else if (c.nr == 1) {
-        if constexpr (WQ == 0 && MF <= 2) launch_stream_cfg<ACT, WQ, MF, 1, U>(a.epi, a, grid, s);
-    } else {
-        if constexpr (WQ != 0) launch_stream_cfg<ACT, WQ, MF, 4, U>(a.epi, a, grid, s);   // 256 rows share one A tile
+    if (c.nr == 2) return launch_stream_cfg<ACT, WQ, MF, 2, U>(a.epi, a, grid, s);
+    if (c.nr == 1) {
+        if constexpr (WQ == 0 && MF <= 2) return launch_stream_cfg<ACT, WQ, MF, 1, U>(a.epi, a, grid, s);
+        return hipErrorInvalidValue;
     }
+    if constexpr (WQ != 0) return launch_stream_cfg<ACT, WQ, MF, 4, U>(a.epi, a, grid, s);   // 256 rows share one A tile
+    return hipErrorInvalidValue;
 }
 
 template <int ACT, int WQ>
-inline void launch_stream_t(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
+inline hipError_t launch_stream_t(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (c.mf) {
-    case 1: launch_stream_mf<ACT, WQ, 1>(c, a, grid, s); break;
-    case 2: launch_stream_mf<ACT, WQ, 2>(c, a, grid, s); break;
-    default: launch_stream_mf<ACT, WQ, 4>(c, a, grid, s); break;
+    case 1: return launch_stream_mf<ACT, WQ, 1>(c, a, grid, s);
+    case 2: return launch_stream_mf<ACT, WQ, 2>(c, a, grid, s);
+    default: return launch_stream_mf<ACT, WQ, 4>(c, a, grid, s);
     }
 }
 

@@ -207,41 +207,75 @@ def _sample_rows(M, n, seed=0):
     return np.sort(np.concatenate([[0, M - 1], mid]))
 
 
-FULL = ["tiny-f32", "llama3-8b-decode", "llama2-7b-prefill", "gpt-fp16-gelu",
-        "llama2-70b-int8w@M1", "llama2-70b-int8w@M16", "llama2-70b-int8w@M64", "llama2-70b-int8w@M256",
-        "llama2-70b-int8w-tp8@M16"]
-N_ROWS = {"llama2-7b-prefill": 24, "gpt-fp16-gelu": 24, "llama2-70b-int8w@M256": 16,
-          "llama2-70b-int8w@M64": 64}
+def tile_rows(M, seed, n_min=16, tile=128):
+    """Token rows to compare at full size: every row up to 64 tokens; otherwise
+    one random row in every 128-row tile (so every row tile of every kernel
+    family meets the oracle at least once, and with it every column tile), the
+    first and last rows, and at least n_min rows in all."""
+    if M <= 64:
+        return np.arange(M)
+    rng = np.random.default_rng(1000 + seed)
+    starts = np.arange(0, M, tile)
+    per = starts + rng.integers(0, tile, len(starts)) % np.minimum(tile, M - starts)
+    rows = np.unique(np.concatenate([per, [0, M - 1], _sample_rows(M, n_min, seed)]))
+    return rows
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_workload_full_size(name):
-    wl = inputs.workload(name)
-    print(f"workload {name}: generating", flush=True)
-    inp = inputs.generate(wl, seed=0)
+def full_size_check(wl, seed):
+    """One workload at full size, fp32 and native outputs: outputs start as NaN
+    (so that an element no kernel writes fails), every output element must be
+    finite afterwards, and the rows of tile_rows are compared with the oracle."""
+    print(f"workload {wl.name} seed {seed}: generating", flush=True)
+    inp = inputs.generate(wl, seed=seed)
     d = to_dev(inp)
-    rows = _sample_rows(wl.M, N_ROWS.get(name, 64))
-    print(f"workload {name}: GPU", flush=True)
+    rows = tile_rows(wl.M, seed)
+    rows_d = torch.from_numpy(rows).to(DEV)
+    act = TDT[wl.act]
+    print(f"workload {wl.name} seed {seed}: GPU, {len(rows)} rows compared", flush=True)
     res = {}
     for native in (False, True):
-        odt = None if native else torch.float32
+        odt = act if native else torch.float32
         if wl.n_qkv:
-            q, k, v, h = run_qkv(wl, d, odt)
-            res[("qkv", native)] = (q[rows].cpu(), k[rows].cpu(), v[rows].cpu(), h[rows].cpu())
-        out = run_gu(wl, d, odt)
-        res[("gu", native)] = out[rows].cpu()
+            q = torch.full((wl.M, wl.n_heads, wl.head_dim), float("nan"), dtype=odt, device=DEV)
+            k = torch.full((wl.M, wl.n_kv_heads, wl.head_dim), float("nan"), dtype=odt, device=DEV)
+            v = torch.full_like(k, float("nan"))
+            h = torch.full_like(d["x"], float("nan"))
+            fra.fused_add_norm_qkv(d["x"], d.get("r"), d["gamma"], d["w_qkv"], wl.n_heads, wl.n_kv_heads,
+                                   wl.head_dim, beta=d.get("beta"), norm=wl.norm, eps=wl.eps,
+                                   w_scale=d.get("s_qkv"), bias=d.get("b_qkv"), h_out=h, q=q, k=k, v=v)
+            for name, t in (("q", q), ("k", k), ("v", v), ("h_out", h)):
+                assert bool(torch.isfinite(t).all()), f"{wl.name}: {name} has unwritten or non-finite elements"
+            res[("qkv", native)] = tuple(t.index_select(0, rows_d).cpu() for t in (q, k, v, h))
+        out = torch.full((wl.M, wl.ffn), float("nan"), dtype=odt, device=DEV)
+        fra.fused_gateup_act(d["x"], d.get("r"), d["gamma"], d["w_gu"], wl.ffn, wl.act_fn, beta=d.get("beta"),
+                             norm=wl.norm, eps=wl.eps, w_scale=d.get("s_gu"), bias=d.get("b_gu"), out=out)
+        assert bool(torch.isfinite(out).all()), f"{wl.name}: out has unwritten or non-finite elements"
+        res[("gu", native)] = out.index_select(0, rows_d).cpu()
     torch.cuda.synchronize()
-    print(f"workload {name}: oracle on {len(rows)} rows", flush=True)
+    del d
+    print(f"workload {wl.name} seed {seed}: oracle on {len(rows)} rows", flush=True)
     if wl.n_qkv:
         rq = oracle.workload_qkv(wl, inp, row_idx=rows)
     rg = oracle.workload_gateup(wl, inp, row_idx=rows)
     for native in (False, True):
         if wl.n_qkv:
             q, k, v, h = res[("qkv", native)]
-            print(name, native, "q", check("q", q, rq["q"]), "k", check("k", k, rq["k"]),
+            print(wl.name, seed, native, "q", check("q", q, rq["q"]), "k", check("k", k, rq["k"]),
                   "v", check("v", v, rq["v"]), flush=True)
             assert np.array_equal(h.double().numpy(), rq["h_out"]), "h_out not bit-exact"
-        print(name, native, "out", check("out", res[("gu", native)], rg["out"]), flush=True)
+        print(wl.name, seed, native, "out", check("out", res[("gu", native)], rg["out"]), flush=True)
+    torch.cuda.empty_cache()
+
+
+FULL = ["tiny-f32", "llama3-8b-decode", "llama2-7b-prefill", "llama2-7b-prefill-w16", "gpt-fp16-gelu",
+        "llama2-70b-int8w@M1", "llama2-70b-int8w@M16", "llama2-70b-int8w@M64", "llama2-70b-int8w@M256",
+        "llama2-70b-int8w-tp8@M16"]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_size(name, seed):
+    full_size_check(inputs.workload(name), seed)
 
 
 def test_int8_workload_dequant_bits():
@@ -253,16 +287,15 @@ def test_int8_workload_dequant_bits():
     assert np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), bits)
 
 
-@pytest.mark.parametrize("env", [{"FUSEDPROJ_STREAM_NR": "4"},
-                                 {"FUSEDPROJ_STREAM_NR": "4", "FUSEDPROJ_SPLITS": "3"},
-                                 {"FUSEDPROJ_STREAM_NR": "4", "FUSEDPROJ_SPLITS": "1"}],
-                         ids=lambda e: ",".join(f"{k[11:]}={v}" for k, v in e.items()))
+@pytest.mark.parametrize("env", [{"stream_nr": 4},
+                                 {"stream_nr": 4, "splits": 3},
+                                 {"stream_nr": 4, "splits": 1}],
+                         ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
 @pytest.mark.parametrize("M", [1, 20, 48])
-def test_stream_int8_256_rows(env, M, monkeypatch):
+def test_stream_int8_256_rows(env, M, plan_override):
     """int8 weights with 256 weight rows per stream workgroup (chosen for large
     gate/up shapes at 33..64 tokens), forced on a small shape with ragged tiles."""
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+    plan_override(**env)
     wl = small(wdt="i8", M=M, hidden=1024, H=10, Hkv=2, D=32, ffn=464)
     inp = inputs.generate(wl, seed=17)
     d = to_dev(inp)
@@ -276,6 +309,33 @@ def test_stream_int8_256_rows(env, M, monkeypatch):
     check("k", k, rq["k"])
     check("v", v, rq["v"])
     check("out", out, rg["out"])
+
+
+# ---------------------------------------------------------------------------
+# the streaming kernel with workgroups whose range holds a whole tile of an
+# odd number of K chunks followed by another tile: the second segment's first
+# normalisation must wait until every wave has read the last chunk of the
+# first (a CPU model of the unit split finds 64 such workgroups for the
+# 1280-wide linear case and 16 for the 2304-wide gate/up with 128 workgroups)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [dict(M=8, hidden=1280, ffn=20480, act_fn="none"),
+                                  dict(M=32, hidden=1280, ffn=20480, act_fn="none"),
+                                  dict(M=8, hidden=2304, ffn=9216, target=128),
+                                  dict(M=20, hidden=2304, ffn=9216, target=128)],
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_stream_consecutive_segments(case, plan_override):
+    case = dict(case)
+    target = case.pop("target", 0)
+    plan_override(stream_target=target)
+    wl = small(H=4, Hkv=2, D=64, **case)
+    plan = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, torch.bfloat16, torch.bfloat16, wl.act_fn)
+    print(f"consecutive segments {case} target={target}: {plan}", flush=True)
+    assert plan["family"] == "stream"
+    inp = inputs.generate(wl, seed=21, parts=("gu",))
+    d = to_dev(inp)
+    out = run_gu(wl, d, torch.float32)
+    torch.cuda.synchronize()
+    check("out", out, oracle.workload_gateup(wl, inp)["out"])
 
 
 # ---------------------------------------------------------------------------
@@ -359,15 +419,14 @@ def test_prefill_layernorm_without_beta():
     check("out", out, rg["out"])
 
 
-PREFILL_CONFIGS = [{"FUSEDPROJ_SPLITS": "1"}, {"FUSEDPROJ_SPLITS": "2"}, {"FUSEDPROJ_SPLITS": "3"},
-                   {"FUSEDPROJ_SPLITS": "5"}, {"FUSEDPROJ_SPLITS": "16"}, {"FUSEDPROJ_NO_PREFILL": "1"}]
+PREFILL_CONFIGS = [{"splits": 1}, {"splits": 2}, {"splits": 3},
+                   {"splits": 5}, {"splits": 16}, {"no_prefill": 1}]
 
 
-@pytest.mark.parametrize("env", PREFILL_CONFIGS, ids=lambda e: ",".join(f"{k[11:]}={v}" for k, v in e.items()))
+@pytest.mark.parametrize("env", PREFILL_CONFIGS, ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
 @pytest.mark.parametrize("wdt", ["bf16", "i8"])
-def test_prefill_launch_configs(env, wdt, monkeypatch):
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+def test_prefill_launch_configs(env, wdt, plan_override):
+    plan_override(**env)
     wl = small(wdt=wdt, M=270, hidden=1024, H=10, Hkv=2, D=32, ffn=336, bias=True)
     inp = inputs.generate(wl, seed=16)
     d = to_dev(inp)
@@ -389,20 +448,19 @@ def test_prefill_launch_configs(env, wdt, monkeypatch):
 # land on different XCDs), chunk widths and rows per wave, both kernel families
 # ---------------------------------------------------------------------------
 CONFIGS = [
-    {"FUSEDPROJ_SPLITS": "1"}, {"FUSEDPROJ_SPLITS": "2"}, {"FUSEDPROJ_SPLITS": "3"},
-    {"FUSEDPROJ_SPLITS": "4"},
-    {"FUSEDPROJ_SPLITS": "5", "FUSEDPROJ_STREAM_NR": "1"},
-    {"FUSEDPROJ_SPLITS": "8", "FUSEDPROJ_STREAM_NR": "1"},
-    {"FUSEDPROJ_NO_STREAM": "1", "FUSEDPROJ_SPLITS": "3"},
-    {"FUSEDPROJ_NO_STREAM": "1", "FUSEDPROJ_SPLITS": "7"},
+    {"splits": 1}, {"splits": 2}, {"splits": 3},
+    {"splits": 4},
+    {"splits": 5, "stream_nr": 1},
+    {"splits": 8, "stream_nr": 1},
+    {"no_stream": 1, "splits": 3},
+    {"no_stream": 1, "splits": 7},
 ]
 
 
-@pytest.mark.parametrize("env", CONFIGS, ids=lambda e: ",".join(f"{k[11:]}={v}" for k, v in e.items()))
+@pytest.mark.parametrize("env", CONFIGS, ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
 @pytest.mark.parametrize("M", [3, 32, 64])
-def test_launch_configs(env, M, monkeypatch):
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+def test_launch_configs(env, M, plan_override):
+    plan_override(**env)
     wl = small(M=M, hidden=2048, H=10, Hkv=2, D=32, ffn=336)
     inp = inputs.generate(wl, seed=8)
     d = to_dev(inp)
