@@ -19,7 +19,8 @@ from ._lib import FP_ACT, FP_NORM
 __all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_down_residual", "fused_dequant_i8_bf16",
            "fused_dequant_i4_bf16",
            "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
-           "library_path", "tune_install", "tune_clear", "tune_count"]
+           "library_path", "tune_install", "tune_clear", "tune_count", "plan_override",
+           "set_plan_override", "get_plan_override"]
 
 # torch.uint8 weights are int4 pairs (two values per byte, even k in the low nibble)
 _DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
@@ -292,3 +293,49 @@ def tune_clear() -> None:
 
 def tune_count() -> int:
     return int(_lib.load().fp_tune_count())
+
+
+_OVERRIDE_FIELDS = ("splits", "stream_nr", "stream_target", "no_stream", "no_prefill", "fp8_tile")
+
+
+def get_plan_override() -> dict:
+    """The current plan overrides (fp_plan_override_get)."""
+    o = _lib.PlanOverride()
+    _check("fp_plan_override_get", _lib.load().fp_plan_override_get(o))
+    return {k: int(getattr(o, k)) for k in _OVERRIDE_FIELDS}
+
+
+def set_plan_override(values: Optional[dict]) -> None:
+    """Replace the plan overrides (fp_plan_override_set): a dict with any of
+    splits, stream_nr, stream_target, no_stream, no_prefill, fp8_tile (missing
+    fields 0 = the planner's choice); None restores the values the FUSEDPROJ_*
+    environment variables held when the library first planned a call."""
+    import ctypes
+    lib = _lib.load()
+    if values is None:
+        _check("fp_plan_override_set", lib.fp_plan_override_set(None))
+        return
+    unknown = set(values) - set(_OVERRIDE_FIELDS)
+    if unknown:
+        raise ValueError(f"unknown plan override fields {sorted(unknown)}")
+    o = _lib.PlanOverride(*(int(values.get(k, 0)) for k in _OVERRIDE_FIELDS))
+    _check("fp_plan_override_set", lib.fp_plan_override_set(ctypes.byref(o)))
+
+
+class plan_override:
+    """Context manager: ``with plan_override(splits=3, no_stream=1): ...``
+    forces those launch choices on every call inside, then restores the
+    previous overrides."""
+
+    def __init__(self, **values):
+        self.values = values
+        self.prev = None
+
+    def __enter__(self):
+        self.prev = get_plan_override()
+        set_plan_override(self.values)
+        return self
+
+    def __exit__(self, *exc):
+        set_plan_override(self.prev)
+        return False

@@ -15,12 +15,13 @@ FP_F32, FP_F16, FP_BF16, FP_I8, FP_I4, FP_E4M3 = 0, 1, 2, 3, 4, 5
 FP_NORM = {"none": 0, "rms": 1, "layer": 2}
 FP_ACT = {"none": 0, "swiglu": 1, "gelu_tanh": 2}
 STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_ALIAS",
-          "FP_E_WORKSPACE", "FP_E_ARG", "FP_E_HIP"]
+          "FP_E_HIP", "FP_E_WORKSPACE", "FP_E_ARG"]
 
 # every symbol include/fusedproj.h declares
 EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_add_norm_qkv_hm", "fused_gateup_act", "fused_down_residual",
            "fused_dequant_i8_bf16", "fused_dequant_i4_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
-           "fp_profile_start", "fp_profile_stop", "fp_tune_install", "fp_tune_count"]
+           "fp_profile_start", "fp_profile_stop", "fp_tune_install", "fp_tune_count",
+           "fp_plan_override_set", "fp_plan_override_get"]
 
 
 class KernelTime(ctypes.Structure):
@@ -34,6 +35,12 @@ class TuneEntry(ctypes.Structure):
                 ("n_cols", ctypes.c_int64), ("act_dtype", ctypes.c_int), ("w_dtype", ctypes.c_int),
                 ("swiglu", ctypes.c_int32), ("family", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("splits", ctypes.c_int32)]
+
+
+class PlanOverride(ctypes.Structure):
+    """fp_plan_override of include/fusedproj.h."""
+    _fields_ = [("splits", ctypes.c_int32), ("stream_nr", ctypes.c_int32), ("stream_target", ctypes.c_int32),
+                ("no_stream", ctypes.c_int32), ("no_prefill", ctypes.c_int32), ("fp8_tile", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,6 +88,10 @@ def load(path: str = None):
     lib.fp_tune_install.restype = ci
     lib.fp_tune_count.argtypes = []
     lib.fp_tune_count.restype = i64
+    lib.fp_plan_override_set.argtypes = [ctypes.POINTER(PlanOverride)]
+    lib.fp_plan_override_set.restype = ci
+    lib.fp_plan_override_get.argtypes = [ctypes.POINTER(PlanOverride)]
+    lib.fp_plan_override_get.restype = ci
     if path == LIB_PATH:
         _lib = lib
     return lib

@@ -61,53 +61,79 @@ long env_long(const char *name, long dflt) {
 }
 
 // Launch-configuration overrides for one call: from the installed tuning
-// table (fp_tune_install), then from FUSEDPROJ_* environment variables, which
-// win (they are for sweeps).  Zero / -1 fields leave the planner's choice.
+// table (fp_tune_install), then from the plan overrides (fp_plan_override_set,
+// initially the FUSEDPROJ_* environment variables), which win.  Zero / -1
+// fields leave the planner's choice.
 struct Knobs {
     int family = -1;          // 0 tiled, 1 stream, 2 prefill; -1 the planner's
     long rows = 0;            // stream: weight rows per workgroup (64, 128, 256)
     long grid = 0;            // stream: workgroups
-    long splits = 0;          // tiled / prefill: K splits
-    long stream_splits = 0;   // stream: workgroups per tile (environment only)
+    long splits = 0;          // tiled / prefill / FP8: K splits
+    long stream_splits = 0;   // stream: workgroups per tile (overrides only)
     long target = 256;        // stream: workgroup budget
+    int fp8_tile = 0;         // FP8 GEMM tile by token rows (overrides only)
     bool no_stream = false, no_prefill = false;
 };
 
 std::mutex g_tune_mu;
 std::vector<fp_tune_entry> g_tune;
 
+// the FUSEDPROJ_* environment, read once (thread-safe static initialisation)
+const fp_plan_override &env_overrides() {
+    static const fp_plan_override v = [] {
+        fp_plan_override o{};
+        o.splits = (int32_t)env_long("FUSEDPROJ_SPLITS", 0);
+        o.stream_nr = (int32_t)env_long("FUSEDPROJ_STREAM_NR", 0);
+        o.stream_target = (int32_t)env_long("FUSEDPROJ_STREAM_TARGET", 0);
+        o.no_stream = env_long("FUSEDPROJ_NO_STREAM", 0) != 0;
+        o.no_prefill = env_long("FUSEDPROJ_NO_PREFILL", 0) != 0;
+        o.fp8_tile = (int32_t)env_long("FUSEDPROJ_FP8_TILE", 0);
+        return o;
+    }();
+    return v;
+}
+
+bool g_ov_set = false;          // guarded by g_tune_mu
+fp_plan_override g_ov{};        // guarded by g_tune_mu; valid when g_ov_set
+
+const fp_plan_override &overrides_locked() {
+    if (!g_ov_set) {
+        g_ov = env_overrides();
+        g_ov_set = true;
+    }
+    return g_ov;
+}
+
 Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu) {
     Knobs kb;
-    {
-        std::lock_guard<std::mutex> lk(g_tune_mu);
-        for (const fp_tune_entry &e : g_tune) {
-            if (M < e.m_lo || M > e.m_hi || e.hidden != K || e.n_cols != Nw || e.act_dtype != act ||
-                e.w_dtype != wdt || (e.swiglu != 0) != swiglu)
-                continue;
-            kb.family = e.family;
-            kb.rows = e.rows;
-            kb.grid = e.grid;
-            kb.splits = e.splits;
-            break;
-        }
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    for (const fp_tune_entry &e : g_tune) {
+        if (M < e.m_lo || M > e.m_hi || e.hidden != K || e.n_cols != Nw || e.act_dtype != act ||
+            e.w_dtype != wdt || (e.swiglu != 0) != swiglu)
+            continue;
+        kb.family = e.family;
+        kb.rows = e.rows;
+        kb.grid = e.grid;
+        kb.splits = e.splits;
+        break;
     }
-    kb.target = env_long("FUSEDPROJ_STREAM_TARGET", 256);
-    if (env_long("FUSEDPROJ_NO_STREAM", 0) != 0) {
+    const fp_plan_override &o = overrides_locked();
+    if (o.stream_target > 0) kb.target = o.stream_target;
+    if (o.no_stream) {
         kb.no_stream = true;
         if (kb.family == 1) kb.family = -1;
     }
-    if (env_long("FUSEDPROJ_NO_PREFILL", 0) != 0) {
+    if (o.no_prefill) {
         kb.no_prefill = true;
         if (kb.family == 2) kb.family = -1;
     }
-    const long nr_env = env_long("FUSEDPROJ_STREAM_NR", 0);
-    if (nr_env > 0) kb.rows = 64 * nr_env;
-    const long sp_env = env_long("FUSEDPROJ_SPLITS", 0);
-    if (sp_env > 0) {
-        kb.splits = sp_env;
-        kb.stream_splits = sp_env;
+    if (o.stream_nr > 0) kb.rows = 64 * o.stream_nr;
+    if (o.splits > 0) {
+        kb.splits = o.splits;
+        kb.stream_splits = o.splits;
         kb.grid = 0;
     }
+    kb.fp8_tile = o.fp8_tile;
     return kb;
 }
 
@@ -139,11 +165,11 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // tiles (SwiGLU: 128 gate + 128 up rows), one workgroup per CU, when
         // they fill at least one round of CUs; otherwise 128 x 128 tiles, two
         // workgroups per CU, K split while fewer than two rounds of
-        // workgroups run (same limits).  FUSEDPROJ_FP8_TILE = 32, 64,
-        // 128 or 256 forces a tile.
+        // workgroups run (same limits).  The fp8_tile override (32, 64,
+        // 128 or 256) forces a tile.
         p.family = 3;
         const int64_t big_tiles = ((M + 255) / 256) * (swiglu ? (Nw / 2 + 127) / 128 : (Nw + 255) / 256);
-        const long tile_env = env_long("FUSEDPROJ_FP8_TILE", 0);
+        const long tile_env = kb.fp8_tile;
         if (tile_env == 32) p.tile8 = fp::G8_32x256;
         else if (tile_env == 64) p.tile8 = fp::G8_64x256;
         else if (tile_env == 128) p.tile8 = fp::G8_128x128;
@@ -846,6 +872,27 @@ fp_status fp_tune_install(const fp_tune_entry *entries, int64_t n) {
 int64_t fp_tune_count(void) {
     std::lock_guard<std::mutex> lk(g_tune_mu);
     return (int64_t)g_tune.size();
+}
+
+fp_status fp_plan_override_set(const fp_plan_override *o) {
+    const fp_plan_override v = o ? *o : env_overrides();
+    const bool ok = v.splits >= 0 && v.splits <= 64 &&
+                    (v.stream_nr == 0 || v.stream_nr == 1 || v.stream_nr == 2 || v.stream_nr == 4) &&
+                    v.stream_target >= 0 && v.stream_target <= 65535 && (v.no_stream == 0 || v.no_stream == 1) &&
+                    (v.no_prefill == 0 || v.no_prefill == 1) &&
+                    (v.fp8_tile == 0 || v.fp8_tile == 32 || v.fp8_tile == 64 || v.fp8_tile == 128 || v.fp8_tile == 256);
+    if (!ok) return fail(FP_E_ARG, "a plan override is out of range");
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_ov = v;
+    g_ov_set = true;
+    return FP_OK;
+}
+
+fp_status fp_plan_override_get(fp_plan_override *o) {
+    if (!o) return fail(FP_E_NULL, "o is NULL");
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    *o = overrides_locked();
+    return FP_OK;
 }
 
 const char *fp_status_str(fp_status s) {

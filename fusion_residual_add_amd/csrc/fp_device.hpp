@@ -293,12 +293,16 @@ __device__ __forceinline__ void store_swiglu(const ProjArgs &p, int64_t m, int64
 // (so the sum never depends on arrival order) and returns true; the others
 // return false and go on without the tile.
 //
-// Coherence across the XCDs' private L2s without whole-cache maintenance: the
-// partials are only ever written and read with device-scope accesses (stores
-// write through to the device coherence point, loads read from it), and each
-// thread waits for its own stores to complete before the workgroup barrier
-// that precedes the counter increment.  No thread touches the partials with
-// ordinary (L2-cached) accesses, so no L2 write-back or invalidate is needed.
+// Publication, in the HIP (HSA) memory model: the partials are written and
+// read with agent-scope atomic accesses (they bypass the XCDs' private,
+// mutually non-coherent L2s).  The workgroup barrier orders every thread's
+// stores before thread 0's arrival, an agent-scope acq_rel read-modify-write
+// of the tile's counter: its release half publishes everything that happens
+// before it (the compiler emits an L2 write-back and a wait for the memory
+// operations in flight), its acquire half makes the other contributors'
+// releases visible to the last arriver.  The second barrier passes that on to
+// the workgroup's other threads, and each thread's agent-scope acquire fence
+// (an L2 invalidate) precedes its loads of the partials.
 // The counters are cleared by the statistics kernel that precedes every
 // split launch on the same stream.
 // `flag`: an int of LDS for the arrival verdict, or null for a static one
@@ -321,15 +325,15 @@ __device__ __forceinline__ bool splitk_reduce(const ProjArgs &p, int tile, int s
 #pragma unroll
     for (int r = 0; r < NACC; ++r)
         __hip_atomic_store(&mine[r * 256 + tid], acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);   // all of this thread's stores have completed
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED,
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_ACQ_REL,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == (unsigned)(count - 1);
     }
     __syncthreads();
     if (!s_last) return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const float *base = p.partials + (int64_t)tile * p.slots * tile_elems;
 #pragma unroll
     for (int r = 0; r < NACC; ++r) acc[r] = 0.f;

@@ -308,31 +308,30 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
 }
 
 template <int ACT, int FM, int FN, int WGM>
-static void launch_gemm8_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
+static hipError_t launch_gemm8_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (a.epi) {
-    case EPI_QKV:    hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_QKV, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_SWIGLU, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_GELU:   hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_GELU, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
-    default:         hipLaunchKernelGGL((gemm8_kernel<ACT, EPI_LINEAR, FM, FN, WGM>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_QKV:    return launch_k(gemm8_kernel<ACT, EPI_QKV, FM, FN, WGM>, grid, s, a);
+    case EPI_SWIGLU: return launch_k(gemm8_kernel<ACT, EPI_SWIGLU, FM, FN, WGM>, grid, s, a);
+    case EPI_GELU:   return launch_k(gemm8_kernel<ACT, EPI_GELU, FM, FN, WGM>, grid, s, a);
+    default:         return launch_k(gemm8_kernel<ACT, EPI_LINEAR, FM, FN, WGM>, grid, s, a);
     }
 }
 
 template <int ACT>
-static void launch_gemm8_v(int tile, const ProjArgs &a, unsigned grid, hipStream_t s) {
+static hipError_t launch_gemm8_v(int tile, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (tile) {
-    case G8_256x256: launch_gemm8_t<ACT, 4, 4, 2>(a, grid, s); break;
-    case G8_32x256:  launch_gemm8_t<ACT, 1, 2, 1>(a, grid, s); break;
-    case G8_64x256:  launch_gemm8_t<ACT, 2, 2, 1>(a, grid, s); break;
-    default:         launch_gemm8_t<ACT, 2, 2, 2>(a, grid, s); break;
+    case G8_256x256: return launch_gemm8_t<ACT, 4, 4, 2>(a, grid, s);
+    case G8_32x256:  return launch_gemm8_t<ACT, 1, 2, 1>(a, grid, s);
+    case G8_64x256:  return launch_gemm8_t<ACT, 2, 2, 1>(a, grid, s);
+    default:         return launch_gemm8_t<ACT, 2, 2, 2>(a, grid, s);
     }
 }
 
 hipError_t launch_gemm8(int act, int tile, const ProjArgs &a, hipStream_t s) {
     const unsigned grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n * a.splits);
     if (grid == 0) return hipSuccess;
-    if (act == ACT_F16) launch_gemm8_v<ACT_F16>(tile, a, grid, s);
-    else launch_gemm8_v<ACT_BF16>(tile, a, grid, s);
-    return hipGetLastError();
+    if (act == ACT_F16) return launch_gemm8_v<ACT_F16>(tile, a, grid, s);
+    return launch_gemm8_v<ACT_BF16>(tile, a, grid, s);
 }
 
 const char *gemm8_kernel_name(int act, int tile, int epi) {

@@ -73,6 +73,16 @@ struct StatsArgs {
     float *qscale;              // [M] dequantisation scale of each row
 };
 
+// Launch a kernel of 256-thread workgroups and return the status of this
+// launch itself (hipLaunchKernel's return value), never an error that an
+// earlier, unrelated HIP call left pending on the thread.
+template <typename T> struct launch_arg { using type = T; };   // keeps P deduced from the kernel alone
+template <typename... P>
+inline hipError_t launch_k(void (*kernel)(P...), unsigned grid, hipStream_t s, typename launch_arg<P>::type... args) {
+    void *argv[] = {(void *)&args...};
+    return hipLaunchKernel((const void *)kernel, dim3(grid), dim3(256), argv, 0, s);
+}
+
 hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s);
 // tiled family (fp_tiled.hip): prefill token counts and every fp32 call
 hipError_t launch_tiled(int act, bool w_i8, int tile, const ProjArgs &a, hipStream_t s);

@@ -543,27 +543,23 @@ void prefill_kernel(ProjArgs p) {
 }
 
 template <int ACT, int WQ, bool LN>
-inline void launch_prefill_n(const ProjArgs &a, unsigned grid, hipStream_t s) {
+inline hipError_t launch_prefill_n(const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (a.epi) {
     case EPI_QKV:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_QKV, LN>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(prefill_kernel<ACT, WQ, EPI_QKV, LN>, grid, s, a);
     case EPI_SWIGLU:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_SWIGLU, LN>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(prefill_kernel<ACT, WQ, EPI_SWIGLU, LN>, grid, s, a);
     case EPI_GELU:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_GELU, LN>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(prefill_kernel<ACT, WQ, EPI_GELU, LN>, grid, s, a);
     default:
-        hipLaunchKernelGGL((prefill_kernel<ACT, WQ, EPI_LINEAR, LN>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(prefill_kernel<ACT, WQ, EPI_LINEAR, LN>, grid, s, a);
     }
 }
 
 template <int ACT, int WQ>
-inline void launch_prefill_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    if (a.norm == 2) launch_prefill_n<ACT, WQ, true>(a, grid, s);
-    else launch_prefill_n<ACT, WQ, false>(a, grid, s);
+inline hipError_t launch_prefill_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    if (a.norm == 2) return launch_prefill_n<ACT, WQ, true>(a, grid, s);
+    return launch_prefill_n<ACT, WQ, false>(a, grid, s);
 }
 
 }  // namespace fp

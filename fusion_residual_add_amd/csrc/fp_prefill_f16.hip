@@ -3,8 +3,8 @@
 
 namespace fp {
 
-void launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_prefill_t<ACT_F16, 0>(a, grid, s);
+hipError_t launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    return launch_prefill_t<ACT_F16, 0>(a, grid, s);
 }
 
 }  // namespace fp

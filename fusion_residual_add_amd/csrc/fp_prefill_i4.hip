@@ -4,8 +4,8 @@
 
 namespace fp {
 
-void launch_prefill_i4(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_prefill_t<ACT_BF16, 2>(a, grid, s);
+hipError_t launch_prefill_i4(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    return launch_prefill_t<ACT_BF16, 2>(a, grid, s);
 }
 
 }  // namespace fp

@@ -3,8 +3,8 @@
 
 namespace fp {
 
-void launch_prefill_i8(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_prefill_t<ACT_BF16, 1>(a, grid, s);
+hipError_t launch_prefill_i8(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    return launch_prefill_t<ACT_BF16, 1>(a, grid, s);
 }
 
 }  // namespace fp

@@ -318,66 +318,66 @@ const char *dequant_kernel_name() { return "dequant_kernel"; }
 const char *dequant_i4_kernel_name() { return "dequant_i4_kernel"; }
 
 template <int ACT>
-static void launch_stats_t(const StatsArgs &a, hipStream_t s) {
+static hipError_t launch_stats_t(const StatsArgs &a, hipStream_t s) {
     // few tokens: a whole workgroup per row keeps every load of the row in
     // flight at once; many tokens: one wave per row
     if (a.M <= 1024) {
         const int64_t blocks = a.M > 0 ? a.M : 0;
         const int64_t ctr = (a.n_counters + 255) / 256;
         const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) hipLaunchKernelGGL((stats_kernel<ACT, 256>), dim3(grid), dim3(256), 0, s, a);
+        if (grid) return launch_k(stats_kernel<ACT, 256>, grid, s, a);
     } else {
         const int64_t blocks = (a.M + 3) / 4;
         const int64_t ctr = (a.n_counters + 255) / 256;
         const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) hipLaunchKernelGGL((stats_kernel<ACT, 64>), dim3(grid), dim3(256), 0, s, a);
+        if (grid) return launch_k(stats_kernel<ACT, 64>, grid, s, a);
     }
+    return hipSuccess;
 }
 
 hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s) {
     switch (act) {
-    case ACT_F32: launch_stats_t<ACT_F32>(a, s); break;
-    case ACT_F16: launch_stats_t<ACT_F16>(a, s); break;
-    default:      launch_stats_t<ACT_BF16>(a, s); break;
+    case ACT_F32: return launch_stats_t<ACT_F32>(a, s);
+    case ACT_F16: return launch_stats_t<ACT_F16>(a, s);
+    default:      return launch_stats_t<ACT_BF16>(a, s);
     }
-    return hipGetLastError();
 }
 
 template <int ACT, int TPR, int NV>
-static void launch_quant8_g(const StatsArgs &a, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((quant8_kernel<ACT, TPR, NV>), dim3(grid), dim3(256), 0, s, a);
+static hipError_t launch_quant8_g(const StatsArgs &a, unsigned grid, hipStream_t s) {
+    return launch_k(quant8_kernel<ACT, TPR, NV>, grid, s, a);
 }
 
 // few tokens: a whole workgroup per row; many tokens: one wave per row.  The
 // row stays in registers when each thread's share is at most 16 vectors.
 template <int ACT, int TPR>
-static void launch_quant8_r(const StatsArgs &a, unsigned grid, hipStream_t s) {
+static hipError_t launch_quant8_r(const StatsArgs &a, unsigned grid, hipStream_t s) {
     const int64_t nv = (a.K + TPR * 8 - 1) / (TPR * 8);
-    if (nv <= 1) launch_quant8_g<ACT, TPR, 1>(a, grid, s);
-    else if (nv <= 2) launch_quant8_g<ACT, TPR, 2>(a, grid, s);
-    else if (nv <= 4) launch_quant8_g<ACT, TPR, 4>(a, grid, s);
-    else if (nv <= 8) launch_quant8_g<ACT, TPR, 8>(a, grid, s);
-    else if (nv <= 16) launch_quant8_g<ACT, TPR, 16>(a, grid, s);
-    else launch_quant8_g<ACT, TPR, 0>(a, grid, s);
+    if (nv <= 1) return launch_quant8_g<ACT, TPR, 1>(a, grid, s);
+    else if (nv <= 2) return launch_quant8_g<ACT, TPR, 2>(a, grid, s);
+    else if (nv <= 4) return launch_quant8_g<ACT, TPR, 4>(a, grid, s);
+    else if (nv <= 8) return launch_quant8_g<ACT, TPR, 8>(a, grid, s);
+    else if (nv <= 16) return launch_quant8_g<ACT, TPR, 16>(a, grid, s);
+    return launch_quant8_g<ACT, TPR, 0>(a, grid, s);
 }
 
 template <int ACT>
-static void launch_quant8_t(const StatsArgs &a, hipStream_t s) {
+static hipError_t launch_quant8_t(const StatsArgs &a, hipStream_t s) {
     const int64_t ctr = (a.n_counters + 255) / 256;
     if (a.M <= 1024) {
         const unsigned grid = (unsigned)(a.M > ctr ? a.M : ctr);
-        if (grid) launch_quant8_r<ACT, 256>(a, grid, s);
+        if (grid) return launch_quant8_r<ACT, 256>(a, grid, s);
     } else {
         const int64_t blocks = (a.M + 3) / 4;
         const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) launch_quant8_r<ACT, 64>(a, grid, s);
+        if (grid) return launch_quant8_r<ACT, 64>(a, grid, s);
     }
+    return hipSuccess;
 }
 
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s) {
-    if (act == ACT_F16) launch_quant8_t<ACT_F16>(a, s);
-    else launch_quant8_t<ACT_BF16>(a, s);
-    return hipGetLastError();
+    if (act == ACT_F16) return launch_quant8_t<ACT_F16>(a, s);
+    return launch_quant8_t<ACT_BF16>(a, s);
 }
 
 const char *quant8_kernel_name(int act) {
@@ -390,9 +390,7 @@ hipError_t launch_dequant_i4(const uint8_t *q, const float *scale, void *out, in
     if (nv == 0) return hipSuccess;
     int64_t blocks = (nv + 255) / 256;
     if (blocks > 16384) blocks = 16384;
-    hipLaunchKernelGGL(dequant_i4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, scale,
-                       (unsigned short *)out, N, K);
-    return hipGetLastError();
+    return launch_k(dequant_i4_kernel, (unsigned)blocks, s, q, scale, (unsigned short *)out, N, K);
 }
 
 hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,
@@ -401,9 +399,7 @@ hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_
     if (nv == 0) return hipSuccess;
     int64_t blocks = (nv + 255) / 256;
     if (blocks > 16384) blocks = 16384;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, scale,
-                       (unsigned short *)out, N, K);
-    return hipGetLastError();
+    return launch_k(dequant_kernel, (unsigned)blocks, s, q, scale, (unsigned short *)out, N, K);
 }
 
 }  // namespace fp

@@ -7,10 +7,10 @@
 
 namespace fp {
 
-void launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
-void launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
-void launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
-void launch_stream_i4(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_stream_i4(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 
 // wq: 0 weights in the activation dtype, 1 int8, 2 int4
 hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s) {
@@ -19,28 +19,26 @@ hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a,
     // the instantiated row counts (see launch_stream_mf)
     if (c.nr != 2 && !(c.nr == 1 && wq == 0 && c.mf <= 2) && !(c.nr == 4 && wq != 0)) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)grid_wgs;
-    if (wq == 1) launch_stream_i8(c, a, grid, s);
-    else if (wq == 2) launch_stream_i4(c, a, grid, s);
-    else if (act == ACT_F16) launch_stream_f16(c, a, grid, s);
-    else launch_stream_bf16(c, a, grid, s);
-    return hipGetLastError();
+    if (wq == 1) return launch_stream_i8(c, a, grid, s);
+    if (wq == 2) return launch_stream_i4(c, a, grid, s);
+    if (act == ACT_F16) return launch_stream_f16(c, a, grid, s);
+    return launch_stream_bf16(c, a, grid, s);
 }
 
-void launch_prefill_bf16(const ProjArgs &a, unsigned grid, hipStream_t s);
-void launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s);
-void launch_prefill_i8(const ProjArgs &a, unsigned grid, hipStream_t s);
-void launch_prefill_i4(const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_prefill_bf16(const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_prefill_i8(const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_prefill_i4(const ProjArgs &a, unsigned grid, hipStream_t s);
 
 // wq: 0 weights in the activation dtype, 1 int8, 2 int4
 hipError_t launch_prefill(int act, int wq, const ProjArgs &a, hipStream_t s) {
     const int64_t g = (int64_t)a.tiles_m * a.tiles_n * a.splits;
     if (g <= 0) return hipSuccess;
     const unsigned grid = (unsigned)g;
-    if (wq == 1) launch_prefill_i8(a, grid, s);
-    else if (wq == 2) launch_prefill_i4(a, grid, s);
-    else if (act == ACT_F16) launch_prefill_f16(a, grid, s);
-    else launch_prefill_bf16(a, grid, s);
-    return hipGetLastError();
+    if (wq == 1) return launch_prefill_i8(a, grid, s);
+    if (wq == 2) return launch_prefill_i4(a, grid, s);
+    if (act == ACT_F16) return launch_prefill_f16(a, grid, s);
+    return launch_prefill_bf16(a, grid, s);
 }
 
 const char *prefill_kernel_name(int act, int wq, int epi) {

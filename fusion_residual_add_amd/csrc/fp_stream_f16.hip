@@ -3,8 +3,8 @@
 
 namespace fp {
 
-void launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_stream_t<ACT_F16, 0>(c, a, grid, s);
+hipError_t launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
+    return launch_stream_t<ACT_F16, 0>(c, a, grid, s);
 }
 
 }  // namespace fp

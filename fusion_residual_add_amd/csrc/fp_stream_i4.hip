@@ -4,8 +4,8 @@
 
 namespace fp {
 
-void launch_stream_i4(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
-    launch_stream_t<ACT_BF16, 2>(c, a, grid, s);
+hipError_t launch_stream_i4(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
+    return launch_stream_t<ACT_BF16, 2>(c, a, grid, s);
 }
 
 }  // namespace fp

@@ -304,19 +304,14 @@ template <int ACT, bool WI8, int EPI>
 static hipError_t launch_proj_e(int tile, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (tile) {
     case TILE_DEC16:
-        hipLaunchKernelGGL((proj_kernel<ACT, WI8, 16, 128, 64, 1, 4, EPI>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(proj_kernel<ACT, WI8, 16, 128, 64, 1, 4, EPI>, grid, s, a);
     case TILE_DEC32:
-        hipLaunchKernelGGL((proj_kernel<ACT, WI8, 32, 128, 64, 1, 4, EPI>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(proj_kernel<ACT, WI8, 32, 128, 64, 1, 4, EPI>, grid, s, a);
     case TILE_DEC64:
-        hipLaunchKernelGGL((proj_kernel<ACT, WI8, 64, 128, 64, 1, 4, EPI>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(proj_kernel<ACT, WI8, 64, 128, 64, 1, 4, EPI>, grid, s, a);
     default:
-        hipLaunchKernelGGL((proj_kernel<ACT, WI8, 128, 128, 64, 2, 2, EPI>), dim3(grid), dim3(256), 0, s, a);
-        break;
+        return launch_k(proj_kernel<ACT, WI8, 128, 128, 64, 2, 2, EPI>, grid, s, a);
     }
-    return hipGetLastError();
 }
 
 template <int ACT, bool WI8>

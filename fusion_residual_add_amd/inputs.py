@@ -149,6 +149,10 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+# the same prefill batch with the tiny block's weight spread taken literally
+# (std 1/16 = 1/sqrt(256)): outputs about four times larger
+WORKLOADS["llama2-7b-prefill-w16"] = dataclasses.replace(WORKLOADS["llama2-7b-prefill"],
+                                                         name="llama2-7b-prefill-w16", w_std=1.0 / 16.0)
 WORKLOADS["llama2-7b-prefill-fp8"] = _fp8(WORKLOADS["llama2-7b-prefill"], "llama2-7b-prefill-fp8")
 WORKLOADS["llama3-8b-decode-fp8"] = _fp8(WORKLOADS["llama3-8b-decode"], "llama3-8b-decode-fp8")
 WORKLOADS["gpt-fp16-gelu-fp8"] = _fp8(WORKLOADS["gpt-fp16-gelu"], "gpt-fp16-gelu-fp8")

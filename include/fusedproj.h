@@ -95,6 +95,8 @@ extern "C" {
 typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4, FP_E4M3 = 5 } fp_dtype;
 typedef enum { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
 typedef enum { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
+/* Codes 0-6 keep the numbering of the boundary's first specification;
+ * 7 and 8 were added after it (the workspace arguments and enum checks). */
 typedef enum {
     FP_OK = 0,
     FP_E_NULL = 1,      /* a required pointer is NULL */
@@ -102,9 +104,9 @@ typedef enum {
     FP_E_DTYPE = 3,     /* dtype combination not supported */
     FP_E_ALIGN = 4,     /* a pointer is not 16-byte aligned */
     FP_E_ALIAS = 5,     /* an output overlaps an input, another output or the workspace */
-    FP_E_WORKSPACE = 6, /* workspace missing or smaller than fp_workspace_bytes() */
-    FP_E_ARG = 7,       /* an enum value is out of range */
-    FP_E_HIP = 8        /* a HIP call failed; see fp_last_error() */
+    FP_E_HIP = 6,       /* a kernel launch failed; see fp_last_error() */
+    FP_E_WORKSPACE = 7, /* workspace missing or smaller than fp_workspace_bytes() */
+    FP_E_ARG = 8        /* an enum or override value is out of range */
 } fp_status;
 
 /* Bytes of workspace a call with these sizes needs.  n_cols is the number of
@@ -224,7 +226,7 @@ fp_status fused_dequant_i4_bf16(const void *q, const float *scale, void *out_bf1
  * into buf (truncated to cap bytes).  n_cols is the weight row count as for
  * fp_workspace_bytes; act selects the gate/up pairing (FP_ACT_SWIGLU) or not.
  * A diagnostic for tuning and tests: it reads the same tuning table and
- * FUSEDPROJ_* overrides as the calls, touches no device and returns FP_E_SHAPE / FP_E_DTYPE /
+ * plan overrides as the calls, touches no device and returns FP_E_SHAPE / FP_E_DTYPE /
  * FP_E_ARG / FP_E_NULL for arguments the calls would reject. */
 fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
                            fp_dtype w_dtype, fp_act act, char *buf, size_t cap);
@@ -255,8 +257,8 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
  * Results stay within the parity bounds for any entry (only the order of the
  * fp32 partial sums changes) and are deterministic for a given table.
  * fp_workspace_bytes and fp_describe_plan read the same table, so install
- * it before sizing workspaces.  The FUSEDPROJ_* environment overrides, when
- * set, take precedence over the table.
+ * it before sizing workspaces.  The plan overrides below, when set, take
+ * precedence over the table.
  *
  * fp_tune_install copies n entries (replacing the previous table; n = 0
  * clears it); FP_E_ARG if a field is out of range, FP_E_NULL if entries is
@@ -278,6 +280,37 @@ typedef struct {
 
 fp_status fp_tune_install(const fp_tune_entry *entries, int64_t n);
 int64_t fp_tune_count(void);
+
+/* Plan overrides, for experiments and tests that force a launch
+ * configuration on every call (the tuning table above is the per-shape
+ * form).  Each field 0 keeps the planner's (or the table's) choice:
+ *  splits        : K splits of the tiled, 128 x 512 and FP8 kernels, and
+ *                  workgroups per weight tile of the streaming kernel (1..64)
+ *  stream_nr     : streaming kernel, weight rows per workgroup / 64 (1, 2, 4;
+ *                  only the instantiated forms are taken, as for the table)
+ *  stream_target : streaming kernel, workgroup budget (1..65535; 0 = 256)
+ *  no_stream     : 1 = never the streaming kernel
+ *  no_prefill    : 1 = never the 128 x 512 kernel
+ *  fp8_tile      : FP8 GEMM tile by token rows: 32, 64, 128 or 256
+ * The initial values come from the environment variables FUSEDPROJ_SPLITS,
+ * FUSEDPROJ_STREAM_NR, FUSEDPROJ_STREAM_TARGET, FUSEDPROJ_NO_STREAM,
+ * FUSEDPROJ_NO_PREFILL and FUSEDPROJ_FP8_TILE, read once, at the first call
+ * that plans a launch; no call reads the environment after that.
+ * fp_plan_override_set replaces the overrides (NULL restores the values read
+ * from the environment); FP_E_ARG if a field is out of range.  Process-wide,
+ * under the tuning table's lock; like the table, set it between calls.
+ * fp_plan_override_get copies the current values. */
+typedef struct {
+    int32_t splits;
+    int32_t stream_nr;
+    int32_t stream_target;
+    int32_t no_stream;
+    int32_t no_prefill;
+    int32_t fp8_tile;
+} fp_plan_override;
+
+fp_status fp_plan_override_set(const fp_plan_override *o);
+fp_status fp_plan_override_get(fp_plan_override *o);
 
 /* Static text for a status code. */
 const char *fp_status_str(fp_status s);

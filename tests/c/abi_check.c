@@ -31,6 +31,22 @@ int main(void) {
     CHECK(fused_gateup_act(NULL, NULL, NULL, NULL, NULL, FP_NORM_RMS, 1e-5f, NULL, NULL, NULL, NULL,
                            32, 4095, 14336, FP_ACT_SWIGLU, FP_BF16, FP_BF16, FP_BF16, NULL, 0, NULL) != FP_OK);
     CHECK(strcmp(fp_status_str(FP_OK), "ok") == 0);
+    /* the boundary's status numbering: 0-6 as first specified, 7 and 8 appended */
+    CHECK(FP_E_ALIAS == 5 && FP_E_HIP == 6 && FP_E_WORKSPACE == 7 && FP_E_ARG == 8);
+    /* plan overrides: set, read back, reject out-of-range values, restore */
+    {
+        fp_plan_override o, back;
+        memset(&o, 0, sizeof o);
+        o.no_stream = 1;
+        CHECK(fp_plan_override_set(&o) == FP_OK);
+        CHECK(fp_plan_override_get(&back) == FP_OK && back.no_stream == 1);
+        CHECK(fp_describe_plan(32, 4096, 6144, FP_BF16, FP_BF16, FP_ACT_NONE, buf, sizeof buf) == FP_OK);
+        CHECK(strstr(buf, "family=tiled") != NULL);
+        o.stream_nr = 3;
+        CHECK(fp_plan_override_set(&o) == FP_E_ARG);
+        CHECK(fp_plan_override_set(NULL) == FP_OK);
+        CHECK(fp_plan_override_get(NULL) == FP_E_NULL);
+    }
     if (fails == 0) printf("abi_check ok\n");
     return fails != 0;
 }

@@ -165,9 +165,8 @@ def test_dequant_i4_rejects():
     assert _lib.STATUS[f(FAKE, FAKE + 0x1000000, FAKE - 0x100, 4, 128, None)] == "FP_E_ALIAS"
 
 
-def test_int4_plans():
-    for var in _ENV:
-        os.environ.pop(var, None)
+def test_int4_plans(plan_override):
+    plan_override()
     u8 = torch.uint8
     # decode token counts, hidden a multiple of 256: streamed, dequantised in registers
     p = _plan(16, 8192, 57344, w=u8, fn="swiglu")
@@ -184,9 +183,8 @@ def test_int4_plans():
     assert fra.workspace_bytes(16, 8192, 57344, torch.bfloat16, u8) < 57344 * 8192
 
 
-def test_fp8_plans():
-    for var in _ENV:
-        os.environ.pop(var, None)
+def test_fp8_plans(plan_override):
+    plan_override()
     e = torch.float8_e4m3fn
     # one family at every token count: per-token quantisation, then the FP8 GEMM
     p = _plan(32, 4096, 28672, w=e, fn="swiglu")
@@ -208,16 +206,11 @@ def test_fp8_plans():
     assert fra.workspace_bytes(16384, 4096, 22016, torch.bfloat16, e) >= 16384 * 4096 + 16384 * 4
     assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 112 * 2 * 32 * 256 * 4
     assert fra.workspace_bytes(8, 320, 512, torch.bfloat16, e) == 0      # hidden % 128
-    os.environ["FUSEDPROJ_SPLITS"] = "3"
-    os.environ["FUSEDPROJ_FP8_TILE"] = "128"
-    try:
+    with fra.plan_override(splits=3, fp8_tile=128):
         p = _plan(1, 4096, 6144, w=e)
         assert p["splits"] == 3 and p["kernel"] == "gemm8_kernel<bf16,128x128,linear>"
-        os.environ["FUSEDPROJ_FP8_TILE"] = "256"
+    with fra.plan_override(splits=3, fp8_tile=256):
         assert _plan(1, 4096, 6144, w=e)["splits"] == 1      # the 256 x 256 kernel does not split K
-    finally:
-        os.environ.pop("FUSEDPROJ_SPLITS")
-        os.environ.pop("FUSEDPROJ_FP8_TILE")
 
 
 def test_binding_refuses_cpu_tensors():
@@ -236,10 +229,8 @@ def _plan(M, K, N, act=torch.bfloat16, w=torch.bfloat16, fn="none"):
     return fra.describe_plan(M, K, N, act, w, fn)
 
 
-def test_plan_routing_families(monkeypatch):
-    for var in ("FUSEDPROJ_SPLITS", "FUSEDPROJ_NO_STREAM", "FUSEDPROJ_NO_PREFILL", "FUSEDPROJ_STREAM_NR",
-                "FUSEDPROJ_STREAM_TARGET"):
-        monkeypatch.delenv(var, raising=False)
+def test_plan_routing_families(plan_override):
+    plan_override()
     # decode token counts with K a multiple of 256: the weight-streaming kernel
     p = _plan(32, 4096, 2 * 14336, fn="swiglu")
     assert p["family"] == "stream" and p["kernel"] == "stream_kernel<bf16,m32,n128,k256,swiglu>"
@@ -290,12 +281,11 @@ def test_plan_routing_families(monkeypatch):
     assert _plan(8, 8192, 2 * f_big, fn="swiglu")["family"] == "stream"
 
 
-def test_plan_grid_slots_consistent(monkeypatch):
+def test_plan_grid_slots_consistent(plan_override):
     """The stream kernel's partial-sum slots cover the most workgroups that share
     one tile, for unit counts that do and do not divide evenly."""
-    monkeypatch.delenv("FUSEDPROJ_STREAM_TARGET", raising=False)
     for splits in ("1", "2", "3", "5", "7"):
-        monkeypatch.setenv("FUSEDPROJ_SPLITS", splits)
+        plan_override(splits=int(splits))
         for M, K, N in ((1, 2048, 640), (32, 4096, 6144), (20, 1024, 928)):
             p = _plan(M, K, N)
             tiles = -(-N // 64)               # 64-row tiles: 16-bit weights, no pairing, <= 32 tokens
@@ -308,12 +298,61 @@ def test_plan_grid_slots_consistent(monkeypatch):
             assert p["slots"] == most
 
 
-def test_plan_env_overrides(monkeypatch):
-    monkeypatch.setenv("FUSEDPROJ_NO_STREAM", "1")
+def test_plan_overrides(plan_override):
+    plan_override(no_stream=1)
     assert _plan(32, 4096, 6144)["family"] == "tiled"
-    monkeypatch.delenv("FUSEDPROJ_NO_STREAM")
-    monkeypatch.setenv("FUSEDPROJ_NO_PREFILL", "1")
+    plan_override(no_prefill=1)
     assert _plan(300, 4096, 6144)["family"] == "tiled"
+    assert _plan(32, 4096, 6144)["family"] == "stream"
+    plan_override(stream_nr=2)
+    assert _plan(8, 4096, 6144)["kernel"] == "stream_kernel<bf16,m16,n128,k256,linear>"
+    plan_override(stream_target=64)
+    assert _plan(8, 4096, 28672, fn="swiglu")["grid"] == 64
+    plan_override()
+    assert fra.get_plan_override() == dict(splits=0, stream_nr=0, stream_target=0, no_stream=0, no_prefill=0,
+                                           fp8_tile=0)
+    # out-of-range values are rejected and leave the overrides as they were
+    plan_override(splits=2)
+    for bad in (dict(splits=65), dict(splits=-1), dict(stream_nr=3), dict(no_stream=2), dict(fp8_tile=100),
+                dict(stream_target=70000)):
+        with pytest.raises(fra.FusedProjError) as ei:
+            fra.set_plan_override(bad)
+        assert ei.value.status == 8                     # FP_E_ARG
+        assert fra.get_plan_override()["splits"] == 2
+    with pytest.raises(ValueError):
+        fra.set_plan_override(dict(bogus=1))
+
+
+def test_plan_overrides_read_environment_once():
+    """The FUSEDPROJ_* variables are read once, at the library's first plan, in
+    a fresh process; changing them afterwards has no effect."""
+    import subprocess
+    import sys
+    code = (
+        "import os, torch, fusion_residual_add_amd as fra\n"
+        "p = fra.describe_plan(32, 4096, 6144, torch.bfloat16, torch.bfloat16)\n"
+        "assert p['family'] == 'tiled' and p['splits'] == 3, p\n"
+        "os.environ['FUSEDPROJ_NO_STREAM'] = '0'\n"
+        "os.environ['FUSEDPROJ_SPLITS'] = '5'\n"
+        "assert fra.describe_plan(32, 4096, 6144, torch.bfloat16, torch.bfloat16) == p\n"
+        "fra.set_plan_override({})\n"
+        "assert fra.describe_plan(32, 4096, 6144, torch.bfloat16, torch.bfloat16)['family'] == 'stream'\n"
+        "fra.set_plan_override(None)\n"
+        "assert fra.describe_plan(32, 4096, 6144, torch.bfloat16, torch.bfloat16) == p\n"
+        "print('env-once ok')\n")
+    env = dict(os.environ, FUSEDPROJ_NO_STREAM="1", FUSEDPROJ_SPLITS="3")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode == 0 and "env-once ok" in res.stdout, res.stdout + res.stderr
+
+
+def test_status_numbering():
+    """Codes 0-6 as the boundary's specification numbers them; 7 and 8 appended."""
+    assert _lib.STATUS[:7] == ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_ALIAS",
+                               "FP_E_HIP"]
+    assert _lib.STATUS[7:] == ["FP_E_WORKSPACE", "FP_E_ARG"]
+    texts = [lib().fp_status_str(i).decode() for i in range(9)]
+    assert texts[6] == "HIP error" and texts[7].startswith("workspace") and texts[8].startswith("invalid")
 
 
 def test_plan_rejects():
@@ -323,10 +362,6 @@ def test_plan_rejects():
         _plan(32, 4096, 6144, act=torch.float16, w=torch.int8)
 
 
-_ENV = ("FUSEDPROJ_SPLITS", "FUSEDPROJ_NO_STREAM", "FUSEDPROJ_NO_PREFILL", "FUSEDPROJ_STREAM_NR",
-        "FUSEDPROJ_STREAM_TARGET", "FUSEDPROJ_FP8_TILE")
-
-
 def _entry(**kw):
     e = dict(m_lo=17, m_hi=32, hidden=4096, n_cols=6144, act_dtype=torch.bfloat16,
              w_dtype=torch.bfloat16, swiglu=False)
@@ -334,9 +369,8 @@ def _entry(**kw):
     return e
 
 
-def test_tuning_table_overrides_matching_calls(monkeypatch):
-    for var in _ENV:
-        monkeypatch.delenv(var, raising=False)
+def test_tuning_table_overrides_matching_calls(plan_override):
+    plan_override()
     base, base_gu, base_33 = _plan(32, 4096, 6144), _plan(32, 4096, 6144, fn="swiglu"), _plan(33, 4096, 6144)
     try:
         fra.tune_install([_entry(family="stream", rows=128, grid=192)])
@@ -365,13 +399,13 @@ def test_tuning_table_overrides_matching_calls(monkeypatch):
         assert _plan(32, 4096, 6144, fn="swiglu") == base_gu
         fra.tune_install([_entry(rows=128)])
         assert _plan(32, 4096, 6144)["kernel"] == "stream_kernel<bf16,m32,n128,k256,linear>"
-        # the first matching entry wins; the environment overrides win over the table
+        # the first matching entry wins; the plan overrides win over the table
         fra.tune_install([_entry(grid=128), _entry(grid=64)])
         assert _plan(32, 4096, 6144)["grid"] == 128
         fra.tune_install([_entry(family="stream")])
-        monkeypatch.setenv("FUSEDPROJ_NO_STREAM", "1")
+        plan_override(no_stream=1)
         assert _plan(32, 4096, 6144)["family"] == "tiled"
-        monkeypatch.delenv("FUSEDPROJ_NO_STREAM")
+        plan_override()
         fra.tune_clear()
         assert fra.tune_count() == 0 and _plan(32, 4096, 6144) == base
     finally:

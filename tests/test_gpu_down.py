@@ -13,12 +13,12 @@ import torch
 import oracle
 import fusion_residual_add_amd as fra
 from fusion_residual_add_amd import inputs
-from test_gpu_parity import DEV, check, small, to_dev, _sample_rows
+from test_gpu_parity import DEV, check, small, tile_rows, to_dev, _sample_rows
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(d, native, bias=None, in_place=False):
+def _run(d, native, bias=None, in_place=False, out=None):
     odt = None if native else torch.float32
     if in_place:
         res = d["r_down"].clone()
@@ -26,7 +26,7 @@ def _run(d, native, bias=None, in_place=False):
         assert out.data_ptr() == res.data_ptr()
         return out
     return fra.fused_down_residual(d["a_down"], d["w_down"], d.get("r_down"), w_scale=d.get("s_down"),
-                                   bias=bias, out_dtype=odt)
+                                   bias=bias, out_dtype=odt, out=out)
 
 
 def _inputs(wl, seed, residual=True):
@@ -81,17 +81,22 @@ def test_down_rejects_partial_overlap():
         fra.fused_down_residual(d["a_down"], d["w_down"], d["r_down"], out=d["a_down"].view(-1)[:16 * 256].view(16, 256))
 
 
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", ["llama3-8b-decode", "llama2-7b-prefill", "llama2-70b-int8w@M16",
                                   "llama2-70b-int4w@M16"])
-def test_down_workload_full_size(name):
+def test_down_workload_full_size(name, seed):
     wl = inputs.workload(name)
-    print(f"down {name}: generating", flush=True)
-    inp = _inputs(wl, seed=0)
+    print(f"down {name} seed {seed}: generating", flush=True)
+    inp = _inputs(wl, seed=seed)
     d = to_dev(inp)
-    rows = _sample_rows(wl.M, 16)
+    rows = tile_rows(wl.M, seed)
     got = {}
     for native in (False, True):
-        got[native] = _run(d, native)[rows].cpu()
+        o = torch.full((wl.M, wl.hidden), float("nan"), dtype=torch.float32 if not native else d["a_down"].dtype,
+                       device=DEV)
+        _run(d, native, out=o)
+        assert bool(torch.isfinite(o).all()), f"down {name}: unwritten or non-finite elements"
+        got[native] = o[torch.from_numpy(rows).to(DEV)].cpu()
     torch.cuda.synchronize()
     print(f"down {name}: oracle on {len(rows)} rows", flush=True)
     idx = torch.as_tensor(rows, dtype=torch.long)

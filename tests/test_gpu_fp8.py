@@ -18,7 +18,7 @@ import torch
 import oracle
 import fusion_residual_add_amd as fra
 from fusion_residual_add_amd import inputs
-from test_gpu_parity import DEV, check, run_gu, run_qkv, small, to_dev, _sample_rows
+from test_gpu_parity import DEV, check, full_size_check, run_gu, run_qkv, small, to_dev, _sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -63,8 +63,8 @@ def test_fp8_small(cfg, native):
 
 @pytest.mark.parametrize("splits", [1, 3, 8])
 @pytest.mark.parametrize("M", [1, 48, 200])
-def test_fp8_splits(splits, M, monkeypatch):
-    monkeypatch.setenv("FUSEDPROJ_SPLITS", str(splits))
+def test_fp8_splits(splits, M, plan_override):
+    plan_override(splits=int(splits))
     wl = _fp8(M=M, hidden=1024, ffn=208)
     inp = inputs.generate(wl, seed=8)
     d = to_dev(inp)
@@ -82,9 +82,9 @@ def test_fp8_splits(splits, M, monkeypatch):
 
 @pytest.mark.parametrize("tile", ["32", "64", "128", "256"])
 @pytest.mark.parametrize("M", [1, 40, 100, 300])
-def test_fp8_tiles(tile, M, monkeypatch):
+def test_fp8_tiles(tile, M, plan_override):
     # every tile form at token counts below, inside and above its own height
-    monkeypatch.setenv("FUSEDPROJ_FP8_TILE", tile)
+    plan_override(fp8_tile=int(tile))
     wl = _fp8(M=M, hidden=512, ffn=272, H=6, Hkv=2, D=32, act_fn="swiglu", bias=True)
     inp = inputs.generate(wl, seed=15)
     d = to_dev(inp)
@@ -120,8 +120,8 @@ def test_fp8_zero_rows_and_bias():
     assert np.array_equal(out[11].double().cpu().numpy(), b)
 
 
-def test_fp8_deterministic_and_m_zero(monkeypatch):
-    monkeypatch.setenv("FUSEDPROJ_SPLITS", "4")
+def test_fp8_deterministic_and_m_zero(plan_override):
+    plan_override(splits=4)
     wl = _fp8(M=24, hidden=512, ffn=144)
     d = to_dev(inputs.generate(wl, seed=10))
     a = run_gu(wl, d)
@@ -159,33 +159,10 @@ def test_fp8_down(cfg, mode):
 FULL8 = ["llama3-8b-decode-fp8", "llama2-7b-prefill-fp8", "gpt-fp16-gelu-fp8"]
 
 
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", FULL8)
-def test_fp8_workload_full_size(name):
-    wl = inputs.workload(name)
-    print(f"workload {name}: generating", flush=True)
-    inp = inputs.generate(wl, seed=0)
-    d = to_dev(inp)
-    rows = _sample_rows(wl.M, 24 if wl.M > 64 else wl.M)
-    print(f"workload {name}: GPU", flush=True)
-    res = {}
-    for native in (False, True):
-        odt = None if native else torch.float32
-        if wl.n_qkv:
-            q, k, v, h = run_qkv(wl, d, odt)
-            res[("qkv", native)] = (q[rows].cpu(), k[rows].cpu(), v[rows].cpu(), h[rows].cpu())
-        res[("gu", native)] = run_gu(wl, d, odt)[rows].cpu()
-    torch.cuda.synchronize()
-    print(f"workload {name}: oracle on {len(rows)} rows", flush=True)
-    if wl.n_qkv:
-        rq = oracle.workload_qkv(wl, inp, row_idx=rows)
-    rg = oracle.workload_gateup(wl, inp, row_idx=rows)
-    for native in (False, True):
-        if wl.n_qkv:
-            q, k, v, h = res[("qkv", native)]
-            print(name, native, "q", check("q", q, rq["q"]), "k", check("k", k, rq["k"]),
-                  "v", check("v", v, rq["v"]), flush=True)
-            assert np.array_equal(h.double().numpy(), rq["h_out"]), "h_out not bit-exact"
-        print(name, native, "out", check("out", res[("gu", native)], rg["out"]), flush=True)
+def test_fp8_workload_full_size(name, seed):
+    full_size_check(inputs.workload(name), seed)
 
 
 # the quantisation kernel's forms: one workgroup per row (up to 1024 tokens)

@@ -16,7 +16,7 @@ import torch
 import oracle
 import fusion_residual_add_amd as fra
 from fusion_residual_add_amd import inputs
-from test_gpu_parity import DEV, check, run_gu, run_qkv, small, to_dev, _sample_rows
+from test_gpu_parity import DEV, check, full_size_check, run_gu, run_qkv, small, to_dev, _sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -72,13 +72,12 @@ def test_int4_small(cfg, native):
     assert np.array_equal(h.double().cpu().numpy(), rq["h_out"]), "h_out not bit-exact"
 
 
-@pytest.mark.parametrize("env", [{"FUSEDPROJ_STREAM_NR": "4"}, {"FUSEDPROJ_STREAM_NR": "4", "FUSEDPROJ_SPLITS": "3"},
-                                 {"FUSEDPROJ_NO_STREAM": "1", "FUSEDPROJ_SPLITS": "3"}],
+@pytest.mark.parametrize("env", [{"stream_nr": 4}, {"stream_nr": 4, "splits": 3},
+                                 {"no_stream": 1, "splits": 3}],
                          ids=lambda e: ",".join(f"{k[10:]}={v}" for k, v in e.items()))
 @pytest.mark.parametrize("M", [1, 48])
-def test_int4_256_rows(env, M, monkeypatch):
-    for key, val in env.items():
-        monkeypatch.setenv(key, val)
+def test_int4_256_rows(env, M, plan_override):
+    plan_override(**env)
     wl = small(wdt="i4", M=M, hidden=1024, H=10, Hkv=2, D=32, ffn=464)
     inp = inputs.generate(wl, seed=7)
     d = to_dev(inp)
@@ -93,35 +92,16 @@ def test_int4_256_rows(env, M, monkeypatch):
     check("out", out, rg["out"])
 
 
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", ["llama2-70b-int4w@M1", "llama2-70b-int4w@M16", "llama2-70b-int4w@M256"])
-def test_int4_workload_full_size(name):
-    wl = inputs.workload(name)
-    print(f"workload {name}: generating", flush=True)
-    inp = inputs.generate(wl, seed=0)
-    d = to_dev(inp)
-    rows = _sample_rows(wl.M, 16)
-    print(f"workload {name}: GPU", flush=True)
-    res = {}
-    for native in (False, True):
-        odt = None if native else torch.float32
-        q, k, v, h = run_qkv(wl, d, odt)
-        res[("qkv", native)] = (q[rows].cpu(), k[rows].cpu(), v[rows].cpu(), h[rows].cpu())
-        res[("gu", native)] = run_gu(wl, d, odt)[rows].cpu()
-    torch.cuda.synchronize()
-    print(f"workload {name}: oracle on {len(rows)} rows", flush=True)
-    rq = oracle.workload_qkv(wl, inp, row_idx=rows)
-    rg = oracle.workload_gateup(wl, inp, row_idx=rows)
-    for native in (False, True):
-        q, k, v, h = res[("qkv", native)]
-        print(name, native, "q", check("q", q, rq["q"]), "k", check("k", k, rq["k"]), "v", check("v", v, rq["v"]),
-              "out", check("out", res[("gu", native)], rg["out"]), flush=True)
-        assert np.array_equal(h.double().numpy(), rq["h_out"]), "h_out not bit-exact"
+def test_int4_workload_full_size(name, seed):
+    full_size_check(inputs.workload(name), seed)
 
 
 @pytest.mark.parametrize("splits", ["1", "2", "3", "5"])
-def test_int4_prefill_splits(splits, monkeypatch):
+def test_int4_prefill_splits(splits, plan_override):
     """The 128 x 512 kernel's int4 path with K split (group scales per stage of each split)."""
-    monkeypatch.setenv("FUSEDPROJ_SPLITS", splits)
+    plan_override(splits=int(splits))
     wl = small(wdt="i4", M=200, hidden=1024, H=8, Hkv=2, D=64, ffn=336)
     inp = inputs.generate(wl, seed=8)
     d = to_dev(inp)
