@@ -55,7 +55,9 @@ def build(src: Optional[str] = None, out: Optional[str] = None) -> str:
     out = out or _OUT
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+    # no contraction: the single-precision steps of R11 round after every
+    # operation except the one written as fmaf
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-ffp-contract=off",
            "-D_GNU_SOURCE", src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
@@ -92,7 +94,7 @@ def load(path: Optional[str] = None):
     lib.or_e4m3_encode.restype = ci
     lib.or_quant_rows_e4m3.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.or_quant_rows_e4m3.restype = ci
-    lib.or_add_norm.argtypes = [vp, vp, vp, vp, ci, ci, dbl, i64, i64, vp, vp, vp]
+    lib.or_add_norm.argtypes = [vp, vp, vp, vp, ci, ci, dbl, i64, i64, vp, vp, vp, vp]
     lib.or_add_norm.restype = ci
     lib.or_matmul_nt.argtypes = [vp, vp, ci, vp, i64, i64, i64, vp]
     lib.or_matmul_nt.restype = ci
@@ -219,18 +221,30 @@ def quant_rows_e4m3(n):
 
 
 def add_norm(x, r, gamma, beta, norm: str, eps: float):
-    """(h_out, n, a) for the rows of x: exact sum, rounded residual stream,
-    unrounded normalised rows, and rows rounded to the activation dtype."""
+    """(h_out, n, a) for the rows of x: the rounded residual stream, the
+    double-precision normalised rows (R2 / R3), and the single-precision
+    normalised rows of R11 rounded to the activation dtype (the GEMM operand
+    of reading A)."""
+    h, n, _, a = _add_norm(x, r, gamma, beta, norm, eps)
+    return h, n, a
+
+
+def add_norm_f32(x, r, gamma, beta, norm: str, eps: float) -> np.ndarray:
+    """The single-precision normalised rows n32 of R11 (as float64 values)."""
+    return _add_norm(x, r, gamma, beta, norm, eps)[2]
+
+
+def _add_norm(x, r, gamma, beta, norm: str, eps: float):
     xa, act = _raw(x)
     M, K = xa.shape
     ra, _ = _raw(r)
     ga, _ = _raw(gamma)
     ba, _ = _raw(beta)
-    h, n, a = _f64((M, K)), _f64((M, K)), _f64((M, K))
+    h, n, n32, a = _f64((M, K)), _f64((M, K)), _f64((M, K)), _f64((M, K))
     rc = load().or_add_norm(_ptr(xa), _ptr(ra), _ptr(ga), _ptr(ba), act, NORM[norm],
-                            float(np.float32(eps)), M, K, _ptr(h), _ptr(n), _ptr(a))
+                            float(np.float32(eps)), M, K, _ptr(h), _ptr(n), _ptr(n32), _ptr(a))
     assert rc == 0
-    return h, n, a
+    return h, n, n32, a
 
 
 def matmul_nt(a: np.ndarray, w, w_scale=None) -> np.ndarray:

@@ -7,12 +7,14 @@
  * library.
  *
  * Everything is computed in IEEE double precision with plain loops, in the
- * order the method states its steps.  The one deliberate rounding is the GEMM
- * A-operand: a fused kernel feeds the matrix unit in the activation dtype, so
- * the normalised row is rounded (round-to-nearest-even) to that dtype before
- * the product ("reading A"); the unrounded variant is available too
- * ("reading B", rounded = 0).  Weights are used exactly as stored (int8
- * weights through their documented dequantisation).
+ * order the method states its steps, except where the pages fix the
+ * precision: the normalised value that feeds the product is formed in single
+ * precision from single-precision statistics, as the LayerNorm + QKV sketch
+ * [D] declares them (R11), and then rounded to the activation dtype: a fused
+ * kernel feeds the matrix unit in that dtype ("reading A").  The unrounded
+ * double-precision normalised row is available too ("reading B",
+ * rounded = 0).  Weights are used exactly as stored (int8 weights through
+ * their documented dequantisation).
  *
  * Sources (web pages on TensorRT-LLM; cited by title and section):
  *  [D] "TensorRT-LLM 深度工程实践：从模型到生产级推理服务", §2.3 跨算子融合,
@@ -57,14 +59,29 @@
  *     taken from the data at run time rather than from a calibration): the
  *     weights are E4M3 codes [N, K] with one fp32 scale per output row,
  *     w = e4m3(code) * s[row] (exact in double); the activations are
- *     quantised per token at run time from the unrounded normalised row n:
- *     amax = max_k |n[k]|, s_a = amax / 448, t = n * (448 / amax) clamped to
- *     [-448, 448], code = E4M3 nearest (ties to the even code), a =
+ *     quantised per token at run time from the single-precision normalised
+ *     row n32 of R11, in single precision: amax = max_k |n32[k]|,
+ *     s_a = fp32(amax / 448), t = fp32(n32 * fp32(448 / amax)) clamped to
+ *     [-448, 448], code = E4M3 nearest of t (ties to the even code), a =
  *     e4m3(code) * s_a; a row with amax = 0 quantises to zeros.  The product
  *     then uses a and w as above.  E4M3 here is the OCP 8-bit format with
  *     1 sign, 4 exponent (bias 7) and 3 mantissa bits: exponent field 0
  *     holds the subnormals m * 2^-9, there are no infinities, S.1111.111 is
  *     NaN and 448 is the largest finite value.
+ *  R11 precision of the normalisation (the sketch [D] holds the mean, the
+ *     variance and the reciprocal root as float and forms the normalised
+ *     value from them before storing it as half): the row statistics are
+ *     accumulated in double and rounded once to fp32, mu32 = fp32(mean) and
+ *     rs32 = fp32(1 / sqrt(var + eps)) (RMS: mean(h^2) for var, mu32 = 0);
+ *     h32 = fp32(x + r); the normalised value is then evaluated in fp32 as
+ *       RMS:   n32 = fp32(fp32(h32 * rs32) * gamma)
+ *       LAYER: n32 = fma32(fp32(fp32(h32 - mu32) * rs32), gamma, beta or 0)
+ *       NONE:  n32 = h32
+ *     and the GEMM operand is a = RNE_act(n32).  Every rounding that decides
+ *     a stored value (the activation dtype, an E4M3 code) thus starts from a
+ *     value both implementations compute with the same single-precision
+ *     operations; the double-precision n of R2 / R3 stays the reference that
+ *     n32 is pinned to.
  *  [Q] "TensorRT-LLM 深度工程实践…", §3.3 FP4/FP8 动态量化加速: the W4A16
  *      (AWQ/GPTQ) configuration with group size 128 and no zero point, and
  *      the W8A8 FP8 configuration with online activation ranges.
@@ -248,25 +265,28 @@ int or_e4m3_encode(double t) {
     return sign | (field << 3) | (int)q;
 }
 
-/* per-token quantisation of the rows of n [M, K] (R10): codes (or NULL),
+/* per-token quantisation of the rows of n [M, K] (R10), in single
+ * precision: each value is taken as fp32 (the rows are the fp32 values n32 of
+ * R11, or activations of a 16-bit dtype, both exact in fp32); codes (or NULL),
  * a = e4m3(code) * s_a (or NULL; may be n itself) and s_a [M] (or NULL) */
 int or_quant_rows_e4m3(const double *n, int64_t M, int64_t K, uint8_t *codes, double *a,
                        double *s_out) {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
-        double amax = 0.0;
+        float amax = 0.0f;
         for (int64_t k = 0; k < K; ++k)
-            if (fabs(n[m * K + k]) > amax) amax = fabs(n[m * K + k]);
-        const double s = amax / OR_E4M3_MAX, inv = amax > 0.0 ? OR_E4M3_MAX / amax : 0.0;
+            if (fabsf((float)n[m * K + k]) > amax) amax = fabsf((float)n[m * K + k]);
+        const float s = amax / (float)OR_E4M3_MAX;
+        const float inv = amax > 0.0f ? (float)OR_E4M3_MAX / amax : 0.0f;
         for (int64_t k = 0; k < K; ++k) {
-            double t = n[m * K + k] * inv;
-            if (t > OR_E4M3_MAX) t = OR_E4M3_MAX;
-            if (t < -OR_E4M3_MAX) t = -OR_E4M3_MAX;
-            const int c = or_e4m3_encode(t);
+            float t = (float)n[m * K + k] * inv;
+            if (t > (float)OR_E4M3_MAX) t = (float)OR_E4M3_MAX;
+            if (t < -(float)OR_E4M3_MAX) t = -(float)OR_E4M3_MAX;
+            const int c = or_e4m3_encode((double)t);
             if (codes) codes[m * K + k] = (uint8_t)c;
-            if (a) a[m * K + k] = or_e4m3_value(c) * s;
+            if (a) a[m * K + k] = or_e4m3_value(c) * (double)s;
         }
-        if (s_out) s_out[m] = s;
+        if (s_out) s_out[m] = (double)s;
     }
     return 0;
 }
@@ -278,11 +298,13 @@ int or_quant_rows_e4m3(const double *n, int64_t M, int64_t K, uint8_t *codes, do
  *  LAYER: mu = sum(h)/K, var = sum((h-mu)^2)/K,
  *         n = (h - mu) / sqrt(var + eps) * gamma + beta   (R3; beta may be NULL)
  *  NONE:  n = h
- * Outputs (each may be NULL): h_out = RNE_act(h), n_out = n, a_out = RNE_act(n).
+ * Outputs (each may be NULL): h_out = RNE_act(h), n_out = n (double),
+ * n32_out = the single-precision normalised value of R11 (as double),
+ * a_out = RNE_act(n32).
  * ------------------------------------------------------------------------- */
 int or_add_norm(const void *x, const void *r, const void *gamma, const void *beta,
                 int act, int norm, double eps, int64_t M, int64_t K,
-                double *h_out, double *n_out, double *a_out) {
+                double *h_out, double *n_out, double *n32_out, double *a_out) {
     int bad = 0;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
@@ -307,18 +329,29 @@ int or_add_norm(const void *x, const void *r, const void *gamma, const void *bet
             for (int64_t k = 0; k < K; ++k) vs += (h[k] - mu) * (h[k] - mu);
             inv = 1.0 / sqrt(vs / (double)K + eps);
         }
+        /* R11: the statistics rounded once to single precision */
+        const float mu32 = (float)mu, rs32 = (float)inv;
         for (int64_t k = 0; k < K; ++k) {
             double n;
+            const float h32 = (float)h[k];
+            float n32;
             if (norm == OR_NORM_RMS) {
                 n = h[k] * inv * or_load(gamma, act, k);
+                const float t = h32 * rs32;
+                n32 = t * (float)or_load(gamma, act, k);
             } else if (norm == OR_NORM_LAYER) {
                 n = (h[k] - mu) * inv * or_load(gamma, act, k);
                 if (beta) n += or_load(beta, act, k);
+                const float d = h32 - mu32;
+                const float t = d * rs32;
+                n32 = fmaf(t, (float)or_load(gamma, act, k), beta ? (float)or_load(beta, act, k) : 0.0f);
             } else {
                 n = h[k];
+                n32 = h32;
             }
             if (n_out) n_out[m * K + k] = n;
-            if (a_out) a_out[m * K + k] = or_round(n, act);
+            if (n32_out) n32_out[m * K + k] = (double)n32;
+            if (a_out) a_out[m * K + k] = or_round((double)n32, act);
         }
         free(h);
     }
@@ -362,16 +395,18 @@ int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scal
 /* ---------------------------------------------------------------------------
  * Full calls.
  * ------------------------------------------------------------------------- */
-/* the GEMM A operand: the normalised rows rounded to the activation dtype
- * (reading A), quantised per token for E4M3 weights (R10), or unrounded */
+/* the GEMM A operand: the single-precision normalised rows (R11) rounded to
+ * the activation dtype (reading A) or quantised per token for E4M3 weights
+ * (R10), or the unrounded double-precision rows (reading B) */
 static double *prologue(const void *x, const void *r, const void *gamma, const void *beta,
                         int act, int norm, double eps, int64_t M, int64_t K,
                         double *h_out, int rounded, int wdtype) {
     double *a = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
     if (!a) return NULL;
     const int fp8 = rounded && wdtype == OR_E4M3;
-    int rc = rounded && !fp8 ? or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, NULL, a)
-                             : or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, a, NULL);
+    int rc = !rounded ? or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, a, NULL, NULL)
+           : fp8      ? or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, NULL, a, NULL)
+                      : or_add_norm(x, r, gamma, beta, act, norm, eps, M, K, h_out, NULL, NULL, a);
     if (!rc && fp8) rc = or_quant_rows_e4m3(a, M, K, NULL, a, NULL);
     if (rc) { free(a); return NULL; }
     return a;

@@ -256,16 +256,50 @@ def pin_a_operand_is_rounded_normalised_row():
         r = _t(rng.standard_normal((4, K)), dt)
         g = _t(rng.uniform(0.8, 1.2, K), dt)
         _, n, a = oracle.add_norm(x, r, g, None, "rms", 1e-5)
-        # every a is representable in the dtype and within half an ulp of n
+        # every a is representable in the dtype and within half an ulp (plus
+        # the single-precision evaluation error of R11) of n
         back = torch.from_numpy(a).to(dt).double().numpy()
         assert np.array_equal(back, a)
         ulp = 2.0 ** (np.floor(np.log2(np.abs(n))) - (7 if name == "bf16" else 10))
-        assert np.all(np.abs(a - n) <= ulp / 2)
+        assert np.all(np.abs(a - n) <= ulp / 2 + np.abs(n) * 2.0 ** -21)
 
 
-# ---------------------------------------------------------------------------
-# the projection product
-# ---------------------------------------------------------------------------
+def pin_single_precision_normalisation():
+    """R11: the normalised value the product consumes is a single-precision
+    evaluation: within a few fp32 roundings of the double-precision n (whose
+    own pins are the closed forms above), exactly h for NONE, and the GEMM
+    operand is that fp32 value cast to the activation dtype by torch."""
+    rng = _rng(8)
+    M, K = 256, 1024
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
+        x = _t(rng.standard_normal((M, K)) * 1.5 + 0.7, dt)      # a mean far from zero
+        r = _t(rng.standard_normal((M, K)), dt)
+        g = _t(rng.uniform(0.5, 1.5, K), dt)
+        b = _t(rng.standard_normal(K) * 0.3, dt)
+        h = x.double() + r.double()
+        for norm, beta in (("rms", None), ("layer", b), ("layer", None), ("none", None)):
+            _, n, a = oracle.add_norm(x, r, g, beta, norm, 1e-5)
+            n32 = oracle.add_norm_f32(x, r, g, beta, norm, 1e-5)
+            # fp32 values
+            assert np.array_equal(n32.astype(np.float32).astype(np.float64), n32)
+            if norm == "none":
+                assert np.array_equal(n32, h.float().double().numpy())
+            else:
+                hv = h.numpy()
+                mu = hv.mean(1, keepdims=True) if norm == "layer" else 0.0
+                var = ((hv - mu) ** 2).mean(1, keepdims=True)
+                rstd = 1.0 / np.sqrt(var + float(np.float32(1e-5)))
+                slack = np.abs(n) + np.abs(mu) * rstd * g.double().numpy() + \
+                    (np.abs(b.double().numpy()) if beta is not None else 0.0)
+                err = np.abs(n32 - n)
+                assert np.all(err <= slack * 2.0 ** -21), (dt, norm, err.max())
+                # and not the double value itself: single-precision rounding shows
+                assert not np.array_equal(n32, n)
+            # the operand is torch's cast of the fp32 values
+            ref = torch.from_numpy(n32.astype(np.float32)).to(dt).double().numpy()
+            assert np.array_equal(a, ref), (dt, norm)
+
+
 def pin_matmul_special_cases():
     rng = _rng(8)
     M, K = 3, 16
@@ -633,32 +667,46 @@ def pin_e4m3_encode_nearest_even():
     assert oracle.e4m3_encode(1e6) == 0x7E and oracle.e4m3_encode(-470.0) == 0xFE
 
 
+def _q8_route(v):
+    """Per-row E4M3 quantisation in float32 arithmetic (R10 on fp32 rows):
+    scale by fp32(448 / amax), clamp, torch's cast; returns (codes, values, s)."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.abs(v).max(1, keepdims=True)
+    s = amax / np.float32(448.0)
+    inv = np.where(amax > 0, np.float32(448.0) / np.where(amax > 0, amax, np.float32(1)), np.float32(0))
+    t = np.clip(v * inv, np.float32(-448.0), np.float32(448.0))
+    q = torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), q.double().numpy() * s.astype(np.float64), s[:, 0].astype(np.float64)
+
+
 def pin_e4m3_row_quantisation():
     rng = _rng(52)
     M, K = 5, 96
-    n = rng.standard_normal((M, K)) * rng.uniform(0.01, 30, (M, 1))
+    n = (rng.standard_normal((M, K)) * rng.uniform(0.01, 30, (M, 1))).astype(np.float32).astype(np.float64)
     n[3] = 0.0                                                           # a zero row
     codes, a, s = oracle.quant_rows_e4m3(n)
-    amax = np.abs(n).max(1)
-    assert np.array_equal(s, amax / 448.0)
-    # the independent route: scale by 448 / amax, clamp, torch's cast, decode
+    rc, ra, rs = _q8_route(n)
+    assert np.array_equal(s, rs)
     for m in range(M):
-        if amax[m] == 0:
+        if rs[m] == 0:
             assert not codes[m].any() and not a[m].any()
             continue
-        t = np.clip(n[m] * (448.0 / amax[m]), -448, 448)
-        ref = torch.tensor(t).to(torch.float8_e4m3fn)
-        assert np.array_equal(codes[m], ref.view(torch.uint8).numpy())
-        assert np.array_equal(a[m], ref.double().numpy() * s[m])
+        assert np.array_equal(codes[m], rc[m])
+        assert np.array_equal(a[m], ra[m])
         # the largest magnitude lands on +-448 exactly
         k = np.abs(n[m]).argmax()
         assert abs(oracle.e4m3_value(codes[m, k])) == 448.0
     # a power-of-two rescale of a row keeps its codes and scales s_a
     c2, a2, s2 = oracle.quant_rows_e4m3(n * 2.0 ** 7)
     assert np.array_equal(c2, codes) and np.array_equal(s2, s * 2.0 ** 7)
-    # relative error of a quantised element: at most half a step of 3 mantissa bits
+    # relative error of a quantised element: at most half a step of 3 mantissa
+    # bits (plus the fp32 scaling)
+    amax = np.abs(n).max(1)
     big = np.abs(n) >= amax[:, None] * 2.0 ** -6
-    assert np.all(np.abs(a - n)[big] <= np.abs(n)[big] * 2.0 ** -4)
+    assert np.all(np.abs(a - n)[big] <= np.abs(n)[big] * (2.0 ** -4 + 2.0 ** -20))
+    # rows given in double are taken at their fp32 values
+    c3, _, _ = oracle.quant_rows_e4m3(n + 1e-12 * np.sign(n))
+    assert np.array_equal(c3, codes)
 
 
 def pin_fp8_projection():
@@ -669,9 +717,8 @@ def pin_fp8_projection():
     s_w = (np.abs(wf).max(1) / 448.0).astype(np.float32)
     wq = torch.tensor(wf / s_w[:, None]).to(torch.float8_e4m3fn)
     w_val = wq.double().numpy() * s_w.astype(np.float64)[:, None]
-    _, n, _ = oracle.add_norm(x, r, g, None, "rms", 1e-5)
-    amax = np.abs(n).max(1, keepdims=True)
-    a = torch.tensor(np.clip(n * (448.0 / amax), -448, 448)).to(torch.float8_e4m3fn).double().numpy() * (amax / 448.0)
+    n32 = oracle.add_norm_f32(x, r, g, None, "rms", 1e-5)      # R11, pinned above
+    _, a, _ = _q8_route(n32)
     acc = a @ w_val.T
     o = oracle.gateup_act(x, r, g, None, "rms", 1e-5, wq, torch.from_numpy(s_w), None, F, "swiglu")
     ref = acc[:, :F] / (1 + np.exp(-acc[:, :F])) * acc[:, F:]
@@ -684,9 +731,7 @@ def pin_fp8_projection():
     # the down projection quantises its input rows the same way
     ad = _t(rng.standard_normal((M, K)), torch.bfloat16)
     res = _t(rng.standard_normal((M, 2 * F)), torch.bfloat16)
-    av = ad.double().numpy()
-    am = np.abs(av).max(1, keepdims=True)
-    aq = torch.tensor(np.clip(av * (448.0 / am), -448, 448)).to(torch.float8_e4m3fn).double().numpy() * (am / 448.0)
+    _, aq, _ = _q8_route(ad.double().numpy())
     _close(oracle.down_residual(ad, wq, torch.from_numpy(s_w), None, res), res.double().numpy() + aq @ w_val.T,
            rtol=1e-12, atol=1e-14, what="fp8 down")
 

@@ -26,8 +26,19 @@ MUTANTS = {
     "beta dropped": ("if (beta) n += or_load(beta, act, k);", "(void)beta;"),
     "gamma index shifted": ("n = h[k] * inv * or_load(gamma, act, k);",
                             "n = h[k] * inv * or_load(gamma, act, (k + 1) % K);"),
-    "A operand not rounded": ("if (a_out) a_out[m * K + k] = or_round(n, act);",
-                              "if (a_out) a_out[m * K + k] = n;"),
+    "A operand not rounded": ("if (a_out) a_out[m * K + k] = or_round((double)n32, act);",
+                              "if (a_out) a_out[m * K + k] = (double)n32;"),
+    "A operand from the double value": ("if (a_out) a_out[m * K + k] = or_round((double)n32, act);",
+                                        "if (a_out) a_out[m * K + k] = or_round(n, act);"),
+    "fp32 path mean sign": ("const float d = h32 - mu32;", "const float d = h32 + mu32;"),
+    "fp32 path beta dropped": ("beta ? (float)or_load(beta, act, k) : 0.0f);", "0.0f);"),
+    "fp32 path rstd dropped": ("const float t = h32 * rs32;", "const float t = h32;"),
+    "fp32 statistics from the wrong root": ("const float mu32 = (float)mu, rs32 = (float)inv;",
+                                           "const float mu32 = (float)mu, rs32 = (float)(inv * inv);"),
+    "fp8 scale not rounded to fp32": ("if (a) a[m * K + k] = or_e4m3_value(c) * (double)s;",
+                                      "if (a) a[m * K + k] = or_e4m3_value(c) * ((double)amax / 448.0);"),
+    "fp8 quantised from the double rows": ("float t = (float)n[m * K + k] * inv;",
+                                           "float t = (float)(n[m * K + k] * ((double)OR_E4M3_MAX / (double)amax));"),
     "weight transposed": ("s += a[m * K + k] * wr[k];", "s += a[m * K + k] * or_load(w, wdtype, k * N + j);"),
     "qkv k/v swapped": ("else if (c < nq + nkv) k[m * nkv + (c - nq)] = y;",
                         "else if (c < nq + nkv) v[m * nkv + (c - nq)] = y;"),
@@ -57,7 +68,7 @@ MUTANTS = {
     "e4m3 subnormal step": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
     "e4m3 ties away": ("double q = nearbyint(16.0 * f - 8.0);", "double q = round(16.0 * f - 8.0);"),
     "e4m3 no mantissa carry": ("if (q == 8.0) { q = 0.0; field += 1; }", "(void)0;"),
-    "fp8 activation scale dropped": ("if (a) a[m * K + k] = or_e4m3_value(c) * s;",
+    "fp8 activation scale dropped": ("if (a) a[m * K + k] = or_e4m3_value(c) * (double)s;",
                                      "if (a) a[m * K + k] = or_e4m3_value(c);"),
     "fp8 activations not quantised": ("if (!rc && fp8) rc = or_quant_rows_e4m3(a, M, K, NULL, a, NULL);", "(void)0;"),
     "fp8 weight scale dropped": ("wr[k] = or_e4m3_value(((const uint8_t *)w)[j * K + k]) * (double)w_scale[j];",
