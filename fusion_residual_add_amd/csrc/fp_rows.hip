@@ -7,8 +7,13 @@
 // row -- mean and 1/sqrt(var + eps) for LayerNorm (two passes over the row),
 // 0 and 1/sqrt(mean(h^2) + eps) for RMSNorm -- as in the per-token mean /
 // variance / reciprocal-root steps of the LayerNorm + QKV fusion sketch
-// ("TensorRT-LLM 深度工程实践…", §2.3).  It also clears the split-K arrival
-// counters of the projection that follows on the same stream.
+// ("TensorRT-LLM 深度工程实践…", §2.3), which holds them as float: the sums
+// are accumulated in double and the statistics rounded once to fp32 from the
+// correctly rounded double division and square root, so that they do not
+// depend on the order of the reduction (the projection kernels then form
+// the normalised value from them in fp32, in a fixed order).  It also
+// clears the split-K arrival counters of the projection that follows on the
+// same stream.
 #include "fp_device.hpp"
 
 namespace fp {
@@ -21,7 +26,7 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
     constexpr int VE = T::VE;
     constexpr int RPW = 256 / TPR;
     constexpr int WPR = TPR / 64;          // waves per row
-    __shared__ float red[4][2];
+    __shared__ double red[4][2];
     const int tid = threadIdx.x;
     for (int i = blockIdx.x * 256 + tid; i < a.n_counters; i += gridDim.x * 256) a.counters[i] = 0u;
 
@@ -33,7 +38,7 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
     const S *rr = a.res ? (const S *)a.res + (active ? m : 0) * a.K : nullptr;
     S *hr = a.h_out ? (S *)a.h_out + (active ? m : 0) * a.K : nullptr;
 
-    float sum = 0.f, ssq = 0.f;
+    double sum = 0.0, ssq = 0.0;
     if (active) {
 #pragma unroll 4
         for (int64_t k = (int64_t)t * VE; k < a.K; k += TPR * VE) {
@@ -46,31 +51,36 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
             }
             if (hr) *(u32x4 *)(hr + k) = T::pack(h);
 #pragma unroll
-            for (int e = 0; e < VE; ++e) { sum += h[e]; ssq += h[e] * h[e]; }
+            for (int e = 0; e < VE; ++e) {
+                const double d = (double)h[e];
+                sum += d;
+                ssq = fma(d, d, ssq);
+            }
         }
     }
     if (a.norm == 0 || a.stats == nullptr) return;   // uniform over the grid
 
-    // row sum / sum of squares over the WPR waves of the row
-    auto row_sum = [&](float v, int slot) -> float {
-        v = wave_sum(v);
+    // row sum over the WPR waves of the row
+    auto row_sum = [&](double v, int slot) -> double {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
         if constexpr (WPR == 1) {
             return v;
         } else {
             if (lane == 0) red[wave][slot] = v;
             __syncthreads();
             const int w0 = (wave / WPR) * WPR;
-            float s = 0.f;
+            double s = 0.0;
 #pragma unroll
             for (int i = 0; i < WPR; ++i) s += red[w0 + i][slot];
             return s;
         }
     };
-    const float invK = 1.0f / (float)a.K;
-    float mean = 0.f, var;
+    const double K = (double)a.K;
+    double mean = 0.0, var;
     if (a.norm == 2) {
-        mean = row_sum(sum, 0) * invK;
-        float dev = 0.f;
+        mean = row_sum(sum, 0) / K;
+        double dev = 0.0;
         if (active) {
 #pragma unroll 4
             for (int64_t k = (int64_t)t * VE; k < a.K; k += TPR * VE) {
@@ -82,40 +92,34 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
                     for (int e = 0; e < VE; ++e) h[e] += r[e];
                 }
 #pragma unroll
-                for (int e = 0; e < VE; ++e) { const float d = h[e] - mean; dev += d * d; }
+                for (int e = 0; e < VE; ++e) {
+                    const double d = (double)h[e] - mean;
+                    dev = fma(d, d, dev);
+                }
             }
         }
-        var = row_sum(dev, 1) * invK;
+        var = row_sum(dev, 1) / K;
     } else {
-        var = row_sum(ssq, 1) * invK;
+        var = row_sum(ssq, 1) / K;
     }
-    if (active && t == 0) a.stats[m] = make_float2(mean, 1.0f / sqrtf(var + a.eps));
+    // correctly rounded double division and square root, then one rounding to fp32
+    if (active && t == 0) a.stats[m] = make_float2((float)mean, (float)(1.0 / sqrt(var + (double)a.eps)));
 }
 
 // Per-token E4M3 quantisation for the W8A8 FP8 projection ("TensorRT-LLM
 // 深度工程实践…", §3.3: the full-FP8 configuration, whose activation range
 // comes from the data at run time).  Per token row: the residual add (h_out
-// written, as stats_kernel does), the row statistics, the normalised row n
-// (LayerNorm ((h - mean) * rstd) * gamma + beta, RMSNorm (h * rstd) * gamma,
-// none: h), amax = max |n|, the row's scale amax / 448 and the codes
-// E4M3_rne(clamp(n * (448 / amax), +-448)); a zero row gets scale 0 and zero
-// codes.  Everything that decides a code (statistics, n, amax, the scaled
-// value) is computed in double precision without contractions, so the code
-// is the correctly rounded E4M3 value of the exactly normalised element up to
-// double rounding error (about 1e-16 relative), not of an fp32 approximation
-// that can sit on the other side of a rounding midpoint.  The double is
-// narrowed to fp32 with round-to-odd (24 bits are more than the 3 + 2 that
-// make the following nearest-even E4M3 conversion exact) and converted by the
-// hardware.  The row is read from memory once per pass (L2 hits after the
-// first); the kernel is bound by memory and latency, not by the fp64 rate.
-__device__ __forceinline__ float round_to_odd_f32(double t) {
-    const float f = (float)t;   // nearest even
-    if ((double)f == t) return f;
-    unsigned u = __float_as_uint(f);
-    if (fabs((double)f) > fabs(t)) u -= 1u;   // toward zero: the truncated value
-    return __uint_as_float(u | 1u);
-}
-
+// written, as stats_kernel does), the row statistics (double sums, rounded
+// once to fp32 as stats_kernel rounds them), the normalised row n formed in
+// fp32 in the order of the projection kernels (LayerNorm
+// fma(fp32(fp32(h - mean) * rstd), gamma, beta), RMSNorm
+// fp32(fp32(h * rstd) * gamma), none: h), amax = max |n|, the row's scale
+// fp32(amax / 448) and the codes E4M3_rne(clamp(fp32(n * fp32(448 / amax)),
+// +-448)); a zero row gets scale 0 and zero codes.  Every value that
+// decides a code is thus a fixed sequence of correctly rounded fp32
+// operations on fp32 statistics that do not depend on the reduction order,
+// and the hardware's nearest-even conversion of an fp32 value decides the
+// code.
 // NV > 0: each thread keeps its NV vectors of 8 elements of h in registers
 // after the first pass (rows of at most TPR * 8 * NV elements); NV == 0: every
 // pass reads the row again.
@@ -225,12 +229,13 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
     } else if (a.norm == 1) {
         rstd = 1.0 / sqrt(__dadd_rn(row_red(ssq, 1, false) / K, eps));
     }
-    auto get_n = [&](int j, int64_t k, double *n) {
+    const float mu32 = (float)mean, rs32 = (float)rstd;
+    auto get_n = [&](int j, int64_t k, float *n) {
         float h[VE];
         get_h(j, k, h);
         if (a.norm == 0) {
 #pragma unroll
-            for (int e = 0; e < VE; ++e) n[e] = (double)h[e];
+            for (int e = 0; e < VE; ++e) n[e] = h[e];
             return;
         }
         float g[VE], b[VE];
@@ -239,34 +244,33 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
             if (a.norm == 2) {
-                n[e] = __dmul_rn(__dmul_rn(__dadd_rn((double)h[e], -mean), rstd), (double)g[e]);
-                if (br) n[e] = __dadd_rn(n[e], (double)b[e]);
+                const float t = __fmul_rn(__fsub_rn(h[e], mu32), rs32);
+                n[e] = fmaf(t, g[e], br ? b[e] : 0.f);
             } else {
-                n[e] = __dmul_rn(__dmul_rn((double)h[e], rstd), (double)g[e]);
+                n[e] = __fmul_rn(__fmul_rn(h[e], rs32), g[e]);
             }
         }
     };
-    double amax = 0.0;
+    float amax = 0.f;
     each([&](int j, int64_t k) {
-        double n[VE];
+        float n[VE];
         get_n(j, k, n);
 #pragma unroll
-        for (int e = 0; e < VE; ++e) amax = fmax(amax, fabs(n[e]));
+        for (int e = 0; e < VE; ++e) amax = fmaxf(amax, fabsf(n[e]));
     });
-    amax = row_red(amax, 2, true);
-    const double mult = amax > 0.0 ? 448.0 / amax : 0.0;
-    if (active && t == 0) a.qscale[m] = (float)(amax / 448.0);
+    amax = (float)row_red((double)amax, 2, true);
+    const float mult = amax > 0.f ? __fdiv_rn(448.f, amax) : 0.f;
+    if (active && t == 0) a.qscale[m] = __fdiv_rn(amax, 448.f);
     unsigned char *cr = a.codes + (active ? m : 0) * a.K;
     each([&](int j, int64_t k) {
-        double n[VE];
+        float n[VE];
         get_n(j, k, n);
         unsigned w[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = round_to_odd_f32(fmin(fmax(__dmul_rn(n[4 * i + e], mult), -448.0), 448.0));
+            for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(__fmul_rn(n[4 * i + e], mult), -448.f), 448.f);
             // two conversions of two values each: bytes 0, 1 then 2, 3
             // (the first operand of each in the lower byte), nearest even
             int p = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);

@@ -161,12 +161,12 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs p) {
                     for (int e = 0; e < VE; ++e) h[e] += r[e];
                 }
                 if (p.norm != 0) {
+                    // fp32(fp32(h - mu) * rstd), then gamma and beta with one
+                    // rounding: the order every kernel of the library uses
 #pragma unroll
                     for (int e = 0; e < VE; ++e) {
-                        float n = (h[e] - a_mu[i]) * a_rs[i];
-                        n = n * g[e];
-                        if (has_beta) n += be[e];
-                        h[e] = n;
+                        const float t = (h[e] - a_mu[i]) * a_rs[i];
+                        h[e] = fmaf(t, g[e], has_beta ? be[e] : 0.f);
                     }
                 }
                 out = T::pack(h);
