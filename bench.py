@@ -150,8 +150,37 @@ class Runner:
             self.qkv(i)
         self.gu(i)
 
+    def unfused(self, i):
+        """The same step as separate torch ops on the same tensors (16-bit
+        weights only): h = x + r, the norm, the projection through
+        torch.nn.functional.linear (hipBLASLt), q / k / v as views of its
+        output, then the norm again for the gate/up projection and SiLU(g) * u
+        (or bias + tanh-GELU) as elementwise ops.  Every intermediate goes
+        through HBM, which is what the fused calls avoid."""
+        import torch.nn.functional as Fn
+        s, wl = self.sets[i % self.R], self.wl
+        K = wl.hidden
+
+        def norm(h):
+            if wl.norm == "rms":
+                return Fn.rms_norm(h, (K,), s["gamma"], wl.eps)
+            return Fn.layer_norm(h, (K,), s["gamma"], s.get("beta"), wl.eps)
+
+        h = s["x"] + s["r"]
+        if wl.n_qkv:
+            qkv = Fn.linear(norm(h), s["w_qkv"], s.get("b_qkv"))
+            qkv.split([wl.n_heads * wl.head_dim, wl.n_kv_heads * wl.head_dim, wl.n_kv_heads * wl.head_dim], 1)
+        gu = Fn.linear(norm(h), s["w_gu"], s.get("b_gu"))
+        if wl.act_fn == "swiglu":
+            return Fn.silu(gu[:, :wl.ffn]) * gu[:, wl.ffn:]
+        if wl.act_fn == "gelu_tanh":
+            return Fn.gelu(gu, approximate="tanh")
+        return gu
+
 
 def time_steps(fn, steps, warmup):
+    """Mean ms per step over exactly `steps` steps after `warmup` untimed ones,
+    bracketed by device synchronisation on both sides."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -164,6 +193,131 @@ def time_steps(fn, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def repeat_stats(fn, steps, repeats=5):
+    """`repeats` more timed runs of `steps` steps each: median / p10 / p90 of
+    their ms per step (the spread the single timed run does not show)."""
+    import statistics
+    runs = sorted(time_steps(fn, steps, 2) for _ in range(repeats))
+    q = statistics.quantiles(runs, n=10, method="inclusive") if len(runs) > 1 else runs * 9
+    return {"n": repeats, "steps_each": steps, "ms_per_step_median": round(statistics.median(runs), 5),
+            "ms_per_step_p10": round(q[0], 5), "ms_per_step_p90": round(q[-1], 5),
+            "ms_per_step_min": round(runs[0], 5), "ms_per_step_max": round(runs[-1], 5)}
+
+
+class ClockSampler:
+    """GPU clocks and power while the timed repeats run (the pages insist that
+    throughput be compared at a stated clock): sysfs pp_dpm_sclk / pp_dpm_mclk
+    (current level marked '*') and hwmon power of the device's PCI function,
+    sampled every 5 ms by a thread; without sysfs access, rocm-smi's clock
+    report before and after."""
+
+    def __init__(self):
+        import glob
+        self.dev = None
+        self.samples = {"sclk_mhz": [], "mclk_mhz": [], "power_w": []}
+        self.smi = []
+        try:
+            import torch
+            p = torch.cuda.get_device_properties(0)
+            bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+            cand = f"/sys/bus/pci/devices/{bdf}"
+            if os.path.exists(os.path.join(cand, "pp_dpm_sclk")):
+                self.dev = cand
+        except Exception:
+            pass
+        if self.dev is None:
+            found = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+            if len(found) == 1:
+                self.dev = os.path.dirname(found[0])
+        self.hwmon = None
+        if self.dev:
+            for name in ("power1_average", "power1_input"):
+                g = glob.glob(os.path.join(self.dev, "hwmon", "hwmon*", name))
+                if g:
+                    self.hwmon = g[0]
+                    break
+
+    @staticmethod
+    def _cur(path):
+        import re
+        with open(path) as fh:
+            for line in fh:
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    if m:
+                        return int(m.group(1))
+        return None
+
+    def _smi(self):
+        import re
+        import subprocess
+        try:
+            out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+        except (OSError, subprocess.SubprocessError):
+            return None
+        return {k: int(v) for k, v in re.findall(r"(\w+) clock level: \d+: \((\d+)Mhz\)", out)}
+
+    def _run(self):
+        import time as _t
+        while not self._stop:
+            for key, fn in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+                try:
+                    v = self._cur(os.path.join(self.dev, fn))
+                    if v is not None:
+                        self.samples[key].append(v)
+                except OSError:
+                    pass
+            if self.hwmon:
+                try:
+                    with open(self.hwmon) as fh:
+                        self.samples["power_w"].append(int(fh.read()) / 1e6)
+                except (OSError, ValueError):
+                    pass
+            _t.sleep(0.005)
+
+    def __enter__(self):
+        import threading
+        self._stop = False
+        if self.dev:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        else:
+            self.smi.append(self._smi())
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        if self.dev:
+            self._t.join()
+        else:
+            self.smi.append(self._smi())
+        return False
+
+    def report(self):
+        import statistics
+        if self.dev:
+            out = {"source": f"sysfs {self.dev} (pp_dpm_sclk / pp_dpm_mclk current level, hwmon power), "
+                             "sampled every 5 ms over the timed repeats"}
+            for k, v in self.samples.items():
+                out[k] = None if not v else {"median": statistics.median(v), "min": min(v), "max": max(v),
+                                             "samples": len(v)}
+            return out
+        return {"source": "rocm-smi --showclocks before and after the timed repeats (no sysfs access)",
+                "before": self.smi[0] if self.smi else None, "after": self.smi[-1] if self.smi else None}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def profile_call(runner, call: str, n: int):
@@ -378,6 +532,96 @@ def all_configs_summarize(path: str, cmd: str) -> None:
     print("\n".join(md))
 
 
+def fusion_gain(steps: int, repeats: int) -> None:
+    """Fused calls against the same step as torch ops on the same GPU, per
+    16-bit workload (the pages' fusion-gain comparison), with hipBLASLt's
+    plain GEMMs of the same shapes (torch.nn.functional.linear on an
+    already-normalised input: the GEMM alone, no add / norm / activation) and
+    torch's own streaming kernels as context for the HBM rate (a float32 sum
+    over 1 GiB of bf16: reads only; a 1 GiB copy: reads and writes).  One
+    JSON line per workload, medians of `repeats` runs of `steps` steps, with
+    the clocks sampled during the fused runs."""
+    import torch
+    import torch.nn.functional as Fn
+    from fusion_residual_add_amd import inputs
+    import statistics
+    src = torch.ones((1 << 30) // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    def med(fn, n):
+        return statistics.median(time_steps(fn, n, 3) for _ in range(repeats))
+    rd = med(lambda i: src.sum(dtype=torch.float32), 20)
+    cp = med(lambda i: dst.copy_(src), 20)
+    print(json.dumps({"stream_context": {"sum_read_GBps": round((1 << 30) / (rd * 1e-3) / 1e9, 1),
+                                         "copy_GBps": round(2 * (1 << 30) / (cp * 1e-3) / 1e9, 1)}}), flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
+    for name in ("llama3-8b-decode", "llama2-7b-prefill", "gpt-fp16-gelu"):
+        wl = inputs.workload(name)
+        run = Runner(wl)
+        n = steps if wl.M <= 64 else max(20, steps // 10)
+        with ClockSampler() as clk:
+            fused = med(run.step, n)
+        unf = med(run.unfused, n)
+        s0 = run.sets
+        gemm = {}
+        for call, key in (("qkv", "w_qkv"), ("gu", "w_gu")):
+            if key not in run.base:
+                continue
+            a = torch.randn((wl.M, wl.hidden), dtype=run.base["x"].dtype, device="cuda")
+            t = med(lambda i: Fn.linear(a, s0[i % run.R][key]), n)
+            gemm[call] = {"us": round(t * 1e3, 2), "TFLOP/s": round(flops(wl, call) / (t * 1e-3) / 1e12, 1)}
+        prof = {c: profile_call(run, c, n) for c in (["qkv"] if wl.n_qkv else []) + ["gu"]}
+        fused_kernels = {c: {k: round(v * 1e3, 2) for k, v in p.items()} for c, p in prof.items()}
+        step_flops = (flops(wl, "qkv") if wl.n_qkv else 0) + flops(wl, "gu")
+        step_bytes = (algo_bytes(wl, "qkv") if wl.n_qkv else 0) + algo_bytes(wl, "gu")
+        print(json.dumps({"workload": name, "M": wl.M, "steps": n, "repeats": repeats,
+                          "fused_ms": round(fused, 5), "unfused_ms": round(unf, 5),
+                          "fused_speedup": round(unf / fused, 3),
+                          "fused_TFLOPs": round(step_flops / (fused * 1e-3) / 1e12, 1),
+                          "fused_GBps": round(step_bytes / (fused * 1e-3) / 1e9, 1),
+                          "fused_kernels_us": fused_kernels, "hipblaslt_gemm_only": gemm,
+                          "clocks": clk.report()}), flush=True)
+        del run
+        torch.cuda.empty_cache()
+
+
+def fusion_gain_summarize(path: str, cmd: str) -> None:
+    """profiles/fusion_gain.md from the JSON lines of --fusion-gain."""
+    ctx, rows = None, []
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line.startswith("{"):
+                continue
+            d = json.loads(line)
+            if "stream_context" in d:
+                ctx = d["stream_context"]
+            else:
+                rows.append(d)
+    md = ["# Fused calls against the unfused torch step, same GPU", "", "Command (from the repository root):", "",
+          "```", cmd, "```", "",
+          "Unfused = the same step as torch ops on the same tensors: h = x + r, the norm, F.linear (hipBLASLt),",
+          "q / k / v as views, the norm again, F.linear, SiLU(g) * u (or bias + tanh-GELU).  `hipBLASLt GEMM",
+          "only` = F.linear of the same shapes on an already-normalised input.  Medians of the repeats.", ""]
+    if ctx:
+        md += [f"torch streaming kernels on this GPU: float32 sum over 1 GiB of bf16 {ctx['sum_read_GBps']} GB/s "
+               f"(reads), 1 GiB copy {ctx['copy_GBps']} GB/s (reads + writes).", ""]
+    md += ["| workload | fused ms | unfused ms | fused speedup | fused rate | fused kernels (us) | "
+           "hipBLASLt GEMM only | sclk MHz (median, min-max) |", "|---|---|---|---|---|---|---|---|"]
+    for d in rows:
+        rate = f"{d['fused_GBps']} GB/s" if d["M"] <= 64 else f"{d['fused_TFLOPs']} TFLOP/s"
+        ks = "; ".join(f"{c}: " + ", ".join(f"`{k}` {v}" for k, v in kk.items())
+                       for c, kk in d["fused_kernels_us"].items())
+        gm = ", ".join(f"{c} {g['us']} us ({g['TFLOP/s']} TFLOP/s)" for c, g in d["hipblaslt_gemm_only"].items())
+        c = d["clocks"].get("sclk_mhz") if isinstance(d["clocks"], dict) else None
+        clk = f"{c['median']} ({c['min']}-{c['max']})" if c else json.dumps(d["clocks"].get("after"))
+        md.append(f"| {d['workload']} | {d['fused_ms']} | {d['unfused_ms']} | {d['fused_speedup']} | {rate} | "
+                  f"{ks} | {gm} | {clk} |")
+    with open(os.path.join(ROOT, "profiles", "fusion_gain.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     import oracle
     from fusion_residual_add_amd import inputs
@@ -395,9 +639,31 @@ def cpu_baseline(wl, budget_s: float = 12.0):
     per_step = el / n
     step_bytes = (algo_bytes(wl, "qkv") if wl.n_qkv else 0) + algo_bytes(wl, "gu")
     return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"the full {wl.name} step (both calls, all {wl.M} tokens) run {n} times "
                       f"in {el:.1f} s, {per_step * 1e3:.1f} ms per step"}
+
+
+def cpu_baseline_rows(wl, n_rows: int = 64):
+    """The oracle on a sample of token rows of a prefill-sized step (rows are
+    independent, so the time scales with the row count): both calls on
+    n_rows evenly spaced rows, reported as the FLOP rate of that sample."""
+    import numpy as np
+    import oracle
+    from fusion_residual_add_amd import inputs
+    inp = inputs.generate(wl, seed=0)
+    oracle.load()
+    rows = np.linspace(0, wl.M - 1, n_rows).astype(np.int64)
+    t0 = time.perf_counter()
+    if wl.n_qkv:
+        oracle.workload_qkv(wl, inp, row_idx=rows)
+    oracle.workload_gateup(wl, inp, row_idx=rows)
+    el = time.perf_counter() - t0
+    fl = 2 * n_rows * wl.hidden * ((wl.n_qkv or 0) + wl.n_gu)
+    return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"both calls of {wl.name} on {n_rows} of its {wl.M} token rows in {el:.2f} s "
+                      f"({fl / 1e9:.1f} GFLOP); the full step would take about {el * wl.M / n_rows:.0f} s"}
 
 
 def main():
@@ -408,7 +674,9 @@ def main():
     ap.add_argument("--workload", default="llama3-8b-decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="extra timed runs of --steps steps each, for the median / p10 / p90 spread")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="calibration pass + projection calls, to run under rocprofv3 --pmc")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -420,6 +688,10 @@ def main():
                     help="write profiles/all_configs.md from the output of --all-configs")
     ap.add_argument("--all-configs", action="store_true",
                     help="per-call times and roofline fractions of every workload, one JSON line each")
+    ap.add_argument("--fusion-gain", action="store_true",
+                    help="fused against unfused torch steps and hipBLASLt GEMMs, one JSON line per workload")
+    ap.add_argument("--fusion-gain-summarize", metavar="JSON_LINES",
+                    help="write profiles/fusion_gain.md from the output of --fusion-gain")
     ap.add_argument("--tune-file", metavar="JSON",
                     help="install this launch-configuration table (python -m fusion_residual_add_amd.tune "
                          "--out) before timing; the default is the built-in planner")
@@ -432,6 +704,9 @@ def main():
         return
     if args.all_configs_summarize:
         all_configs_summarize(args.all_configs_summarize, args.cmd)
+        return
+    if args.fusion_gain_summarize:
+        fusion_gain_summarize(args.fusion_gain_summarize, args.cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -455,9 +730,14 @@ def main():
     if args.all_configs:
         all_configs(min(args.steps, 20))
         return
+    if args.fusion_gain:
+        fusion_gain(args.steps, args.repeats)
+        return
     wl = inputs.workload(args.workload)
     run = Runner(wl)
     ms = time_steps(run.step, args.steps, args.warmup)
+    with ClockSampler() as clk:
+        reps = repeat_stats(run.step, args.steps, args.repeats)
     step_bytes = (algo_bytes(wl, "qkv") if wl.n_qkv else 0) + algo_bytes(wl, "gu")
     step_flops = (flops(wl, "qkv") if wl.n_qkv else 0) + flops(wl, "gu")
     mfma_peak = MFMA_FP8_PEAK_TFLOPS if wl.wdt == "e4m3" else MFMA_BF16_PEAK_TFLOPS
@@ -485,6 +765,11 @@ def main():
     roof["kernel_avg_us"] = round(gu_ms * 1e3, 2)
     roof["algo_bytes_per_launch"] = algo_bytes(wl, "gu")
     roof["traffic"] = load_traffic(f"{wl.name}:{gu_kernel}")
+    unfused = None
+    if wl.wdt == wl.act:
+        ums = time_steps(run.unfused, args.steps, args.warmup)
+        unfused = {"ms_per_step": round(ums, 5), "fused_speedup": round(ums / ms, 3),
+                   "what": "the same step as torch ops (add, norm, F.linear through hipBLASLt, SiLU * up)"}
 
     line = {
         "metric": "fused-layer TFLOP/s (prefill) and HBM GB/s (decode), % of MI355X roofline",
@@ -498,7 +783,10 @@ def main():
                    "step_algo_bytes": step_bytes, "step_flops": step_flops,
                    "weight_sets_rotated": run.R},
         "roofline": roof,
+        "repeats": reps,
+        "clocks": clk.report(),
         "kernel_us": per_call,
+        "unfused_torch": unfused,
         "tuning_table": args.tune_file,
     }
     del run
@@ -509,25 +797,33 @@ def main():
         for name in ("llama2-7b-prefill", "llama2-7b-prefill-fp8", "llama3-8b-decode-fp8"):
             pwl = inputs.workload(name)
             pr = Runner(pwl)
-            pms = time_steps(pr.step, args.prefill_steps if pwl.M > 64 else 100, 3)
+            nsteps = args.prefill_steps if pwl.M > 64 else 100
+            pms = time_steps(pr.step, nsteps, 3)
+            with ClockSampler() as pclk:
+                preps = repeat_stats(pr.step, nsteps, args.repeats)
             pfl = flops(pwl, "qkv") + flops(pwl, "gu")
             pby = algo_bytes(wl=pwl, call="qkv") + algo_bytes(wl=pwl, call="gu")
             pprof = profile_call(pr, "gu", 5)
-            pk = max(pprof, key=lambda k: pprof[k])
             pq = profile_call(pr, "qkv", 5)
             if pwl.M > 64:      # prefill: matrix-core bound
                 ppeak = MFMA_FP8_PEAK_TFLOPS if pwl.wdt == "e4m3" else MFMA_BF16_PEAK_TFLOPS
                 pval, punit = pfl / (pms * 1e-3) / 1e12, "TFLOP/s"
             else:               # decode: HBM bound (algorithmic bytes)
                 ppeak, pval, punit = HBM_PEAK_GBS, pby / (pms * 1e-3) / 1e9, "GB/s"
-            sec[name] = {"value": round(pval, 2), "unit": punit,
-                         "ms_per_step": round(pms, 4),
-                         "dtype": "e4m3" if pwl.wdt == "e4m3" else pwl.act, "peak": ppeak,
-                         "frac_of_peak": round(pval / ppeak, 4),
-                         "kernel_us": {"gu": {k: round(v * 1e3, 1) for k, v in pprof.items()},
-                                       "qkv": {k: round(v * 1e3, 1) for k, v in pq.items()}}}
+            ent = {"value": round(pval, 2), "unit": punit, "steps": nsteps,
+                   "ms_per_step": round(pms, 4), "repeats": preps, "clocks": pclk.report(),
+                   "dtype": "e4m3" if pwl.wdt == "e4m3" else pwl.act, "peak": ppeak,
+                   "frac_of_peak": round(pval / ppeak, 4),
+                   "kernel_us": {"gu": {k: round(v * 1e3, 1) for k, v in pprof.items()},
+                                 "qkv": {k: round(v * 1e3, 1) for k, v in pq.items()}}}
+            if pwl.wdt == pwl.act:
+                ums = time_steps(pr.unfused, nsteps, 3)
+                ent["unfused_torch"] = {"ms_per_step": round(ums, 4), "fused_speedup": round(ums / pms, 3)}
+            sec[name] = ent
             del pr
             torch.cuda.empty_cache()
+            if not args.no_cpu_baseline and name == "llama2-7b-prefill":
+                sec[name]["cpu_baseline"] = cpu_baseline_rows(pwl)
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
