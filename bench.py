@@ -460,23 +460,47 @@ def traffic_summarize(wl_name: str, fetch_dir: str, write_dir: str, cmds: str) -
     print(json.dumps(out))
 
 
-def trace_summarize(tag: str, trace_dir: str, cmd: str) -> None:
-    """profiles/kernel_trace_<tag>.md from a `rocprofv3 --kernel-trace --stats` output directory."""
+def _trace_rows(trace_dir: str):
+    """Per-kernel rows (name, calls, avg / min / max ns, share, grid, workgroup,
+    VGPRs, LDS) from a rocprofv3 --kernel-trace output directory: the rocpd
+    SQLite database (this ROCm's default) or a *kernel_stats.csv."""
     import csv
     import glob
+    dbs = glob.glob(os.path.join(trace_dir, "**", "*_results.db"), recursive=True)
+    if dbs:
+        import sqlite3
+        con = sqlite3.connect(dbs[0])
+        q = ("select name, count(*), avg(duration), min(duration), max(duration), sum(duration), grid_x, "
+             "workgroup_x, vgpr_count, accum_vgpr_count, lds_size from kernels group by name, grid_x "
+             "order by sum(duration) desc")
+        rows = list(con.execute(q))
+        total = sum(r[5] for r in rows) or 1
+        return [dict(name=r[0], calls=r[1], avg=r[2], min=r[3], max=r[4], share=100.0 * r[5] / total,
+                     grid=r[6] // max(r[7], 1), vgpr=r[8] + r[9], lds=r[10]) for r in rows]
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
-        raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
-    rows = []
+        raise SystemExit(f"no *_results.db or *kernel_stats.csv under {trace_dir}")
+    out = []
     with open(files[0]) as fh:
         for row in csv.DictReader(fh):
-            rows.append(row)
+            out.append(dict(name=row["Name"], calls=int(row["Calls"]), avg=float(row["AverageNs"]),
+                            min=float(row["MinNs"]), max=float(row["MaxNs"]), share=float(row["Percentage"]),
+                            grid=None, vgpr=None, lds=None))
+    return out
+
+
+def trace_summarize(tag: str, trace_dir: str, cmd: str) -> None:
+    """profiles/kernel_trace_<tag>.md from a `rocprofv3 --kernel-trace --stats` output directory."""
+    rows = _trace_rows(trace_dir)
     md = [f"# Kernel trace, {tag}", "", "Command (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):",
-          "", "```", cmd, "```", "", "| kernel (library name) | calls | avg us | min us | max us | share |",
-          "|---|---|---|---|---|---|"]
+          "", "```", cmd, "```", "",
+          "| kernel (library name, or the first 100 characters) | calls | avg us | min us | max us | share | "
+          "workgroups | VGPRs | LDS bytes |", "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        md.append(f"| `{library_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        name = library_kernel_name(r["name"])
+        name = name if len(name) <= 100 else name[:100] + "..."
+        md.append(f"| `{name}` | {r['calls']} | {r['avg'] / 1e3:.2f} | {r['min'] / 1e3:.2f} | {r['max'] / 1e3:.2f} | "
+                  f"{r['share']:.1f}% | {r['grid']} | {r['vgpr']} | {r['lds']} |")
     with open(os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print("\n".join(md))
