@@ -16,7 +16,7 @@ import torch
 from . import _lib
 from ._lib import FP_ACT, FP_NORM
 
-__all__ = ["fused_add_norm_qkv", "fused_gateup_act", "fused_down_residual", "fused_dequant_i8_bf16",
+__all__ = ["fused_add_norm_qkv", "fused_add_norm_qkv_noalloc", "fused_gateup_act", "fused_down_residual", "fused_dequant_i8_bf16",
            "fused_dequant_i4_bf16",
            "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
            "library_path", "tune_install", "tune_clear", "tune_count", "plan_override",
@@ -159,6 +159,41 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
         _DT[act], _DT[wdt], _DT[odt],
         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
     _check("fused_add_norm_qkv", st)
+    return q, k, v, h_out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20     # FP_NOALLOC_SCRATCH_BYTES of include/fusedproj.h
+
+
+def fused_add_norm_qkv_noalloc(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: Optional[torch.Tensor],
+                               w_qkv: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int, *,
+                               q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               h_out: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                               norm: str = "rms", eps: float = 1e-5, w_scale: Optional[torch.Tensor] = None,
+                               bias: Optional[torch.Tensor] = None):
+    """fused_add_norm_qkv_noalloc: the QKV call with the library's static device
+    scratch instead of a workspace.  The caller passes every output (q, k, v
+    token-major, h_out or None) so that nothing is allocated here either."""
+    lib = _lib.load()
+    _ptr(x, "x")
+    dev = x.device
+    M, K = x.shape
+    act = x.dtype
+    odt = q.dtype
+    Nw = (n_heads + 2 * n_kv_heads) * head_dim
+    _check_weight(w_qkv, w_scale, Nw, K, "w_qkv")
+    for t, shape, name in ((q, (M, n_heads, head_dim), "q"), (k, (M, n_kv_heads, head_dim), "k"),
+                           (v, (M, n_kv_heads, head_dim), "v")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    st = lib.fused_add_norm_qkv_noalloc(
+        _ptr(x, "x", dev, act), _ptr(residual, "residual", dev, act), _ptr(h_out, "h_out", dev, act),
+        _ptr(gamma, "gamma", dev, act), _ptr(beta, "beta", dev, act), FP_NORM[norm], float(eps),
+        _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, torch.float32),
+        _ptr(bias, "bias", dev, act), _ptr(q, "q", dev, odt), _ptr(k, "k", dev, odt),
+        _ptr(v, "v", dev, odt), M, K, n_heads, n_kv_heads, head_dim,
+        _DT[act], _DT[w_qkv.dtype], _DT[odt], _stream(dev))
+    _check("fused_add_norm_qkv_noalloc", st)
     return q, k, v, h_out
 
 

@@ -18,7 +18,7 @@ STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_
           "FP_E_HIP", "FP_E_WORKSPACE", "FP_E_ARG"]
 
 # every symbol include/fusedproj.h declares
-EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_add_norm_qkv_hm", "fused_gateup_act", "fused_down_residual",
+EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_add_norm_qkv_hm", "fused_add_norm_qkv_noalloc", "fused_gateup_act", "fused_down_residual",
            "fused_dequant_i8_bf16", "fused_dequant_i4_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
            "fp_profile_start", "fp_profile_stop", "fp_tune_install", "fp_tune_count",
            "fp_plan_override_set", "fp_plan_override_get"]
@@ -65,6 +65,9 @@ def load(path: str = None):
     lib.fused_add_norm_qkv_hm.argtypes = [vp, vp, vp, vp, vp, ci, f32, vp, vp, vp, vp, vp, vp,
                                        i64, i64, i64, i64, i64, ci, ci, ci, vp, sz, vp]
     lib.fused_add_norm_qkv_hm.restype = ci
+    lib.fused_add_norm_qkv_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, f32, vp, vp, vp, vp, vp, vp,
+                                               i64, i64, i64, i64, i64, ci, ci, ci, vp]
+    lib.fused_add_norm_qkv_noalloc.restype = ci
     lib.fused_gateup_act.argtypes = [vp, vp, vp, vp, vp, ci, f32, vp, vp, vp, vp,
                                      i64, i64, i64, ci, ci, ci, ci, vp, sz, vp]
     lib.fused_gateup_act.restype = ci

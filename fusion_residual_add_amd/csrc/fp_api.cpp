@@ -635,7 +635,7 @@ fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const v
                        int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
                        int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
                        fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
-                       void *hip_stream, bool head_major) {
+                       void *hip_stream, bool head_major, fp::WorkspaceSource source = nullptr) {
     if (n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads != 0)
         return fail(FP_E_SHAPE, "n_heads = %lld, n_kv_heads = %lld: both must be > 0 and n_heads a multiple of n_kv_heads",
                     (long long)n_heads, (long long)n_kv_heads);
@@ -658,6 +658,17 @@ fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const v
     outs.push_back(rng("k", k, M * nkv * eo));
     outs.push_back(rng("v", v, M * nkv * eo));
     const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, w_dtype, false);
+    // the workspace of a call that brings none: from the source, once every
+    // argument has been checked (it may touch the device)
+    if (source) {
+        st = check_alias(ins, outs);
+        if (st != FP_OK) return st;
+        if (M > 0 && plan.total > 0) {
+            char msg[256] = "";
+            st = source(plan.total, &c.ws, &c.ws_bytes, msg, sizeof msg);
+            if (st != FP_OK) return fail(st, "%s", msg);
+        }
+    }
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);
@@ -677,6 +688,19 @@ fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const v
 }
 
 }  // namespace
+
+namespace fp {
+fp_status add_norm_qkv_with_source(const void *x, const void *residual, void *h_out, const void *gamma,
+                                   const void *beta, fp_norm norm, float eps, const void *w_qkv,
+                                   const float *w_scale, const void *bias, void *q, void *k, void *v,
+                                   int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
+                                   int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
+                                   fp_dtype out_dtype, void *hip_stream, WorkspaceSource source) {
+    return add_norm_qkv(x, residual, h_out, gamma, beta, norm, eps, w_qkv, w_scale, bias, q, k, v, M, hidden,
+                        n_heads, n_kv_heads, head_dim, act_dtype, w_dtype, out_dtype, nullptr, 0, hip_stream,
+                        false, source);
+}
+}  // namespace fp
 
 extern "C" {
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fusedproj.h"
+
 namespace fp {
 
 enum ActT { ACT_F32 = 0, ACT_F16 = 1, ACT_BF16 = 2 };
@@ -116,5 +118,16 @@ const char *quant8_kernel_name(int act);
 enum Gemm8Tile { G8_128x128 = 0, G8_256x256 = 1, G8_32x256 = 2, G8_64x256 = 3 };
 hipError_t launch_gemm8(int act, int tile, const ProjArgs &a, hipStream_t s);
 const char *gemm8_kernel_name(int act, int tile, int epi);
+
+// A workspace for a call that brings none (fused_add_norm_qkv_noalloc):
+// given the bytes the plan needs, sets *ws / *ws_bytes or returns a status
+// with a message in msg.  Called after every argument has been validated.
+typedef fp_status (*WorkspaceSource)(size_t need, void **ws, size_t *ws_bytes, char *msg, size_t cap);
+fp_status add_norm_qkv_with_source(const void *x, const void *residual, void *h_out, const void *gamma,
+                                   const void *beta, fp_norm norm, float eps, const void *w_qkv,
+                                   const float *w_scale, const void *bias, void *q, void *k, void *v,
+                                   int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
+                                   int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
+                                   fp_dtype out_dtype, void *hip_stream, WorkspaceSource source);
 
 }  // namespace fp

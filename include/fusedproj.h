@@ -155,6 +155,29 @@ fp_status fused_add_norm_qkv_hm(
     fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
     void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* fused_add_norm_qkv without a workspace argument and without any device
+ * allocation, for callers that cannot allocate device memory: work recorded
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The call's scratch (row statistics, split-K partial sums and
+ * arrival counters) lives in a static device array of
+ * FP_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends; its device address is taken once per device, on the first
+ * call there.  Arguments, results and errors as for fused_add_norm_qkv,
+ * except that a call needing more scratch than the array holds (see
+ * fp_workspace_bytes) returns FP_E_WORKSPACE before touching the device.
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU
+ * (on two streams, or from two threads) race and must be ordered by the
+ * caller.  The array's previous contents never matter. */
+#define FP_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+fp_status fused_add_norm_qkv_noalloc(
+    const void *x, const void *residual, void *h_out,
+    const void *gamma, const void *beta, fp_norm norm, float eps,
+    const void *w_qkv, const float *w_scale, const void *bias,
+    void *q, void *k, void *v,
+    int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+    fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype, void *hip_stream);
+
 /* (Residual add + norm ->) gate/up or up projection (+ bias) -> activation.
  * ("TensorRT-LLM 深度工程实践…", §2.3 SwiGLU fusion sketch; "TRT-LLM deep
  * dive", Layer Fusion figure / LayerNorm + Linear + GELU.)

@@ -84,6 +84,40 @@ def gu(**kw):
     return _lib.STATUS[st], lib().fp_last_error().decode()
 
 
+def qkv_noalloc(**kw):
+    a = dict(x=FAKE, residual=FAKE + 0x1000000, h_out=None, gamma=FAKE + 0x2000000, beta=None,
+             norm=1, eps=1e-5, w=FAKE + 0x3000000, w_scale=None, bias=None,
+             q=FAKE + 0x40000000, k=FAKE + 0x50000000, v=FAKE + 0x60000000, M=0, hidden=4096,
+             H=32, Hkv=8, D=128, act=BF16, wdt=BF16, odt=BF16, stream=None)
+    a.update(kw)
+    st = lib().fused_add_norm_qkv_noalloc(a["x"], a["residual"], a["h_out"], a["gamma"], a["beta"], a["norm"],
+                                          a["eps"], a["w"], a["w_scale"], a["bias"], a["q"], a["k"], a["v"],
+                                          a["M"], a["hidden"], a["H"], a["Hkv"], a["D"], a["act"], a["wdt"],
+                                          a["odt"], a["stream"])
+    return _lib.STATUS[st], lib().fp_last_error().decode()
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """The allocation-free QKV call validates every argument, and the scratch
+    it would need, before any HIP call (only error paths run here: a valid
+    call would launch kernels on these fake addresses)."""
+    assert qkv_noalloc(M=0)[0] == "FP_OK"
+    # Llama-2-70B int8 QKV at 256 tokens needs 60 MiB of partial sums: more than the static scratch
+    st, msg = qkv_noalloc(M=256, hidden=8192, H=64, Hkv=8, D=128, wdt=I8, w_scale=FAKE + 0x70000000)
+    assert st == "FP_E_WORKSPACE" and "static scratch holds 16777216" in msg, msg
+    assert fra.workspace_bytes(256, 8192, 10240, torch.bfloat16, torch.int8) > fra.NOALLOC_SCRATCH_BYTES
+    assert qkv_noalloc(M=1, x=None)[0] == "FP_E_NULL"
+    assert qkv_noalloc(M=32, hidden=4000)[0] == "FP_E_SHAPE"
+    assert qkv_noalloc(M=32, D=100)[0] == "FP_E_SHAPE"
+    assert qkv_noalloc(M=32, wdt=I8)[0] == "FP_E_NULL"                       # int8 without scales
+    assert qkv_noalloc(M=32, act=F16, wdt=BF16)[0] == "FP_E_DTYPE"
+    assert qkv_noalloc(M=32, q=FAKE + 0x3000000)[0] == "FP_E_ALIAS"         # q over the weight
+    assert qkv_noalloc(M=32, x=FAKE + 8)[0] == "FP_E_ALIGN"
+    # the header's limit is the binding's
+    text = open(HEADER).read()
+    assert "#define FP_NOALLOC_SCRATCH_BYTES (16u << 20)" in text and fra.NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
 def test_m_zero_is_a_noop():
     assert qkv(M=0)[0] == "FP_OK"
     assert qkv(M=0, head_major=True)[0] == "FP_OK"
