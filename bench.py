@@ -489,6 +489,68 @@ def _trace_rows(trace_dir: str):
     return out
 
 
+def counters_summarize(tag: str, dirs, cmd: str) -> None:
+    """profiles/counters_<tag>.md from rocprofv3 --pmc runs (csv output) of
+    --traffic-probe: per library kernel, the median of each counter over its
+    dispatches, and what follows from them.  GRBM_GUI_ACTIVE is summed over the
+    8 XCDs (each has its own graphics register block), so the shader clock is
+    GRBM_GUI_ACTIVE / 8 over the dispatch's duration; SQ_VALU_MFMA_BUSY_CYCLES
+    is summed over the 1024 SIMDs, so MFMA busy = it / (1024 x cycles)."""
+    import csv
+    import glob
+    import statistics
+    per, dur = {}, {}
+    for d in dirs:
+        for fpath in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fpath) as fh:
+                for row in csv.DictReader(fh):
+                    n = row["Kernel_Name"]
+                    if "fp::" not in n:
+                        continue
+                    per.setdefault(n, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                    dur.setdefault(n, []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    md = [f"# Hardware counters, {tag}", "", "Commands (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):",
+          "", "```", cmd, "```", "",
+          "Medians over the dispatches of each kernel.  GRBM_GUI_ACTIVE is summed over the 8 XCDs: the shader clock",
+          "is GRBM_GUI_ACTIVE / 8 / duration.  SQ_VALU_MFMA_BUSY_CYCLES is summed over the 1024 SIMDs: MFMA busy =",
+          "it / (1024 x GRBM_GUI_ACTIVE / 8).  SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: the share of wave time spent",
+          "waiting at s_waitcnt.  Clock-based ratios only for dispatches longer than 200 us (for short ones",
+          "GRBM_GUI_ACTIVE counts beyond the dispatch's timestamps).", ""]
+    for n in sorted(per):
+        c = {k: statistics.median(v) for k, v in per[n].items()}
+        t = statistics.median(dur[n]) * 1e-9
+        md.append(f"## `{library_kernel_name(n)}`")
+        md.append("")
+        md.append(f"median duration under the profiler {t * 1e6:.1f} us")
+        # for short dispatches GRBM_GUI_ACTIVE also counts activity outside the
+        # dispatch's own timestamps (the implied clock exceeds the part's
+        # 2.4 GHz), so the clock-based ratios are given for long ones only
+        if "GRBM_GUI_ACTIVE" in c and t > 200e-6:
+            cyc = c["GRBM_GUI_ACTIVE"] / 8
+            md.append(f"; shader clock {cyc / t / 1e9:.2f} GHz")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                md.append(f"; MFMA busy {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cyc):.3f} of SIMD cycles")
+            if "TA_TA_BUSY" in c:
+                md.append(f"; TA busy {c['TA_TA_BUSY'] / (256 * cyc):.3f} of CU cycles")
+            if "TCP_PENDING_STALL_CYCLES" in c:
+                md.append(f"; TCP pending-stall {c['TCP_PENDING_STALL_CYCLES'] / (256 * cyc):.3f} of CU cycles")
+        if "SQ_WAIT_INST_ANY" in c and c.get("SQ_WAVE_CYCLES"):
+            md.append(f"; waiting at s_waitcnt {c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.3f} of wave time")
+        if "TCC_HIT" in c and "TCC_MISS" in c:
+            md.append(f"; L2 hit rate {c['TCC_HIT'] / max(c['TCC_HIT'] + c['TCC_MISS'], 1):.3f}")
+        md.append("")
+        md.append("")
+        md.append("| counter | median per dispatch |")
+        md.append("|---|---|")
+        for k in sorted(c):
+            md.append(f"| {k} | {c[k]:.0f} |")
+        md.append("")
+    path = os.path.join(ROOT, "profiles", f"counters_{tag}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def trace_summarize(tag: str, trace_dir: str, cmd: str) -> None:
     """profiles/kernel_trace_<tag>.md from a `rocprofv3 --kernel-trace --stats` output directory."""
     rows = _trace_rows(trace_dir)
@@ -707,6 +769,8 @@ def main():
                     help="write profiles/traffic.json from the two counter runs of --traffic-probe")
     ap.add_argument("--trace-summarize", nargs=2, metavar=("TAG", "TRACE_DIR"),
                     help="write profiles/kernel_trace_TAG.md from a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--counters-summarize", nargs="+", metavar=("TAG", "PMC_DIR"),
+                    help="write profiles/counters_TAG.md from rocprofv3 --pmc csv runs of --traffic-probe")
     ap.add_argument("--cmd", default="", help="the profiling command(s), recorded in the summary")
     ap.add_argument("--all-configs-summarize", metavar="JSON_LINES",
                     help="write profiles/all_configs.md from the output of --all-configs")
@@ -725,6 +789,9 @@ def main():
         return
     if args.trace_summarize:
         trace_summarize(*args.trace_summarize, args.cmd)
+        return
+    if args.counters_summarize:
+        counters_summarize(args.counters_summarize[0], args.counters_summarize[1:], args.cmd)
         return
     if args.all_configs_summarize:
         all_configs_summarize(args.all_configs_summarize, args.cmd)
