@@ -24,7 +24,12 @@ Recipe (stated once, used everywhere):
 * int4 weights (4-bit weights with 16-bit activations, group 128, no zero
   point): per output row and group of 128 consecutive k,
   ``s = max|w| / 7`` (float32) and ``q = clip(rint(w / s), -8, 7)``, packed
-  two per byte along k (even k in the low nibble), scales ``[N, K/128]``.
+  two per byte along k (even k in the low nibble), scales ``[N, K/128]``;
+* MXFP4 weights (FP4 weights with 16-bit activations, one 8-bit power-of-two
+  scale per 32 consecutive k): per row and block, the shared exponent
+  ``e = floor(log2(max|w|)) - 2`` (2 being the largest E2M1 exponent), scale
+  code ``e + 127``, element codes the nearest E2M1 value (ties to the even
+  code) of ``w / 2^e`` saturated at +-6, packed two per byte along k.
 
 Workload shapes follow the five transformer-block configurations that the
 fused-projection pages are measured on: a tiny fp32 block, a Llama-3-8B decode
@@ -40,7 +45,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "workload", "generate", "quantize_rows_i8", "quantize_groups_i4",
-           "quantize_rows_e4m3"]
+           "quantize_rows_e4m3", "quantize_blocks_mxfp4"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,7 +54,7 @@ class Workload:
     M: int
     hidden: int
     act: str                    # "f32" | "f16" | "bf16"
-    wdt: str                    # "f32" | "f16" | "bf16" | "i8" | "i4" | "e4m3"
+    wdt: str                    # "f32" | "f16" | "bf16" | "i8" | "i4" | "e4m3" | "mxfp4"
     norm: str                   # "rms" | "layer"
     eps: float
     x_std: float
@@ -103,6 +108,12 @@ def _llama70b_i4(M: int) -> Workload:
     return dataclasses.replace(_llama70b(M), name=f"llama2-70b-int4w@M{M}", wdt="i4")
 
 
+def _llama70b_mxfp4(M: int) -> Workload:
+    """The Llama-2-70B layer with MXFP4 weights (E2M1 elements, one E8M0 scale
+    per 32 k) and bf16 activations (the pages' FP4 weight configuration)."""
+    return dataclasses.replace(_llama70b(M), name=f"llama2-70b-mxfp4w@M{M}", wdt="mxfp4")
+
+
 def _fp8(base: Workload, name: str) -> Workload:
     """A workload's shapes with E4M3 weights (per-row scales) and per-token
     E4M3 activations (the pages' full-FP8 configuration)."""
@@ -146,6 +157,10 @@ WORKLOADS: Dict[str, Workload] = {
     "llama2-70b-int4w@M1": _llama70b_i4(1),
     "llama2-70b-int4w@M16": _llama70b_i4(16),
     "llama2-70b-int4w@M256": _llama70b_i4(256),
+    "llama2-70b-mxfp4w@M1": _llama70b_mxfp4(1),
+    "llama2-70b-mxfp4w@M16": _llama70b_mxfp4(16),
+    "llama2-70b-mxfp4w@M64": _llama70b_mxfp4(64),
+    "llama2-70b-mxfp4w@M256": _llama70b_mxfp4(256),
 }
 
 
@@ -263,6 +278,49 @@ def quantize_rows_e4m3(w: np.ndarray):
     return q, torch.from_numpy(s)
 
 
+MX_BLOCK = 32
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def _e2m1_codes(t: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code of each value (ties to the even code, i.e. the one
+    with mantissa bit 0), magnitudes saturated at 6, sign kept (-0 for
+    negative values that round to zero)."""
+    a = np.minimum(np.abs(t), 6.0)
+    d = np.abs(a[..., None] - _E2M1)                       # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # among equally near magnitudes prefer the even code (index & 1 == 0)
+    idx = np.where(cand[..., 0::2].any(-1), np.argmax(np.where(cand, (np.arange(8) % 2 == 0), False), -1),
+                   np.argmax(cand, -1))
+    return (idx | np.where(np.signbit(t), 8, 0)).astype(np.uint8)
+
+
+def quantize_blocks_mxfp4(w: np.ndarray):
+    """MXFP4 storage of a float32 ``[N, K]`` weight: per row and block of 32
+    consecutive k, the shared exponent e = floor(log2(max |w|)) - 2 (clamped to
+    the E8M0 range; an all-zero block takes e = 0), the scale code e + 127 and
+    the element codes _e2m1_codes(w / 2^e).  Returns ``(codes [N, K/2]
+    float4_e2m1fn_x2, element 2i of a row in the low nibble of byte i,
+    scales [N, K/32] float8_e8m0fnu)``; the method only ever reads them."""
+    N, K = w.shape
+    assert K % MX_BLOCK == 0, "MXFP4 weights need K a multiple of 32"
+    G = K // MX_BLOCK
+    q = np.empty((N, K // 2), dtype=np.uint8)
+    s = np.empty((N, G), dtype=np.uint8)
+    step = max(1, (1 << 22) // max(K, 1))
+    for j0 in range(0, N, step):
+        blk = w[j0:j0 + step].astype(np.float64).reshape(-1, G, MX_BLOCK)
+        amax = np.abs(blk).max(axis=2)
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0).astype(np.int64)
+        e = np.clip(e, -127, 127)
+        codes = _e2m1_codes(blk / np.exp2(e)[:, :, None]).reshape(blk.shape[0], K)
+        q[j0:j0 + step] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+        s[j0:j0 + step] = (e + 127).astype(np.uint8)
+    return (torch.from_numpy(q).view(torch.float4_e2m1fn_x2),
+            torch.from_numpy(s).view(torch.float8_e8m0fnu))
+
+
 def _weight(rng, wl: Workload, N: int):
     w = _normal(rng, (N, wl.hidden), wl.w_std)
     if wl.wdt == "e4m3":
@@ -272,6 +330,8 @@ def _weight(rng, wl: Workload, N: int):
         return q, s
     if wl.wdt == "i4":
         return quantize_groups_i4(w)
+    if wl.wdt == "mxfp4":
+        return quantize_blocks_mxfp4(w)
     return _to_act(w, wl.wdt), None
 
 
@@ -320,6 +380,8 @@ def generate(wl: Workload, seed: int = 0, parts=("qkv", "gu")) -> Dict[str, torc
             out["w_down"], out["s_down"] = quantize_groups_i4(w)
         elif wl.wdt == "e4m3":
             out["w_down"], out["s_down"] = quantize_rows_e4m3(w)
+        elif wl.wdt == "mxfp4":
+            out["w_down"], out["s_down"] = quantize_blocks_mxfp4(w)
         else:
             out["w_down"] = _to_act(w, wl.wdt)
         del w

@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _OUT = os.path.join(_HERE, "_build", "liboracle.so")
 
-F32, F16, BF16, I8, I4, E4M3 = 0, 1, 2, 3, 4, 5
+F32, F16, BF16, I8, I4, E4M3, MXFP4 = 0, 1, 2, 3, 4, 5, 6
+MX_BLOCK = 32
 E4M3_MAX = 448.0
 I4_GROUP = 128
 NORM = {"none": 0, "rms": 1, "layer": 2}
@@ -92,6 +93,12 @@ def load(path: Optional[str] = None):
     lib.or_e4m3_value.restype = dbl
     lib.or_e4m3_encode.argtypes = [dbl]
     lib.or_e4m3_encode.restype = ci
+    lib.or_e2m1_value.argtypes = [ci]
+    lib.or_e2m1_value.restype = dbl
+    lib.or_e8m0_value.argtypes = [ci]
+    lib.or_e8m0_value.restype = dbl
+    lib.or_dequant_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.or_dequant_mxfp4.restype = ci
     lib.or_quant_rows_e4m3.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.or_quant_rows_e4m3.restype = ci
     lib.or_add_norm.argtypes = [vp, vp, vp, vp, ci, ci, dbl, i64, i64, vp, vp, vp, vp]
@@ -137,7 +144,20 @@ def _raw(t):
         return t.view(torch.uint8).numpy(), E4M3
     if t.dtype == torch.uint8:               # int4 weights, two per byte (R9)
         return t.numpy(), I4
+    if t.dtype == torch.float4_e2m1fn_x2:    # MXFP4 element codes, two per byte (R12)
+        return t.view(torch.uint8).numpy(), MXFP4
     raise TypeError(f"oracle: unsupported dtype {t.dtype}")
+
+
+def _scales(s):
+    """Weight scales as the C functions take them: E8M0 bytes for MXFP4
+    (torch float8_e8m0fnu), float32 otherwise."""
+    if s is None:
+        return None
+    import torch
+    if isinstance(s, torch.Tensor) and s.dtype == torch.float8_e8m0fnu:
+        return np.ascontiguousarray(s.detach().cpu().contiguous().view(torch.uint8).numpy())
+    return np.ascontiguousarray(_raw(s)[0], dtype=np.float32)
 
 
 def _ptr(a):
@@ -199,6 +219,29 @@ def dequant_i4(q, s):
     return w, bits
 
 
+def dequant_mxfp4(q, s):
+    """(w as float64 [N, K], bf16 bit patterns as uint16) of MXFP4 weights q
+    [N, K/2] (float4_e2m1fn_x2: two E2M1 codes per byte, even k in the low
+    nibble) with E8M0 block scales s [N, K/32] (float8_e8m0fnu) (R12)."""
+    qa, _ = _raw(q)
+    sa = _scales(s)
+    N, K = qa.shape[0], 2 * qa.shape[1]
+    w = _f64((N, K))
+    bits = np.zeros((N, K), dtype=np.uint16)
+    assert load().or_dequant_mxfp4(_ptr(qa), _ptr(sa), N, K, _ptr(w), _ptr(bits)) == 0
+    return w, bits
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one E2M1 code (R12)."""
+    return load().or_e2m1_value(int(code))
+
+
+def e8m0_value(code: int) -> float:
+    """Value of one E8M0 scale code (R12)."""
+    return load().or_e8m0_value(int(code))
+
+
 def e4m3_value(code: int) -> float:
     """Value of one E4M3 code (R10)."""
     return load().or_e4m3_value(int(code))
@@ -250,7 +293,7 @@ def _add_norm(x, r, gamma, beta, norm: str, eps: float):
 def matmul_nt(a: np.ndarray, w, w_scale=None) -> np.ndarray:
     a = np.ascontiguousarray(a, dtype=np.float64)
     wa, wdt = _raw(w)
-    sa = None if w_scale is None else np.ascontiguousarray(_raw(w_scale)[0], dtype=np.float32)
+    sa = _scales(w_scale)
     M, K = a.shape
     N = wa.shape[0]
     acc = _f64((M, N))
@@ -267,7 +310,7 @@ def add_norm_qkv(x, r, gamma, beta, norm: str, eps: float, w, w_scale, bias,
     ga, _ = _raw(gamma)
     ba, _ = _raw(beta)
     wa, wdt = _raw(w)
-    sa = None if w_scale is None else np.ascontiguousarray(_raw(w_scale)[0], dtype=np.float32)
+    sa = _scales(w_scale)
     bia, _ = _raw(bias)
     q = _f64((M, n_heads, head_dim))
     k = _f64((M, n_kv_heads, head_dim))
@@ -289,7 +332,7 @@ def gateup_act(x, r, gamma, beta, norm: str, eps: float, w, w_scale, bias,
     ga, _ = _raw(gamma)
     ba, _ = _raw(beta)
     wa, wdt = _raw(w)
-    sa = None if w_scale is None else np.ascontiguousarray(_raw(w_scale)[0], dtype=np.float32)
+    sa = _scales(w_scale)
     bia, _ = _raw(bias)
     out = _f64((M, ffn))
     h = _f64((M, K))
@@ -306,7 +349,7 @@ def down_residual(a, w, w_scale, bias, residual) -> np.ndarray:
     M, K = aa.shape
     wa, wdt = _raw(w)
     N = wa.shape[0]
-    sa = None if w_scale is None else np.ascontiguousarray(_raw(w_scale)[0], dtype=np.float32)
+    sa = _scales(w_scale)
     ba, _ = _raw(bias)
     ra, _ = _raw(residual)
     out = _f64((M, N))

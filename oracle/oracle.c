@@ -82,6 +82,21 @@
  *     value both implementations compute with the same single-precision
  *     operations; the double-precision n of R2 / R3 stays the reference that
  *     n32 is pinned to.
+ *  R12 MXFP4 weights with 16-bit activations ([Q]: the W4A16_FP4
+ *     configuration; [B]: microscaling, 32 FP4 elements sharing one 8-bit
+ *     scale): the [N, K] weight is stored as [N, K/2] bytes of E2M1 codes,
+ *     element k of a row in the low nibble of byte k/2 for even k and in the
+ *     high nibble for odd k, with [N, K/32] E8M0 scales, one per row and
+ *     block of 32 consecutive k.  E2M1 is 1 sign, 2 exponent (bias 1) and
+ *     1 mantissa bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}, no infinities or NaN,
+ *     code 8 is -0; E8M0 is an unsigned exponent, 2^(s - 127), s = 255 NaN
+ *     (out of contract).  w = e2m1(code) * 2^(s - 127), exact in double; the
+ *     GEMM operand is RNE_bf16(w), w itself for every s up to 252 (larger
+ *     scales can overflow bf16 to +-inf).  Activations stay bf16 (the
+ *     sixteen-bit half of W4A16), normalised and rounded as R11.
+ *  [B] same page, §7.1 FP4 精度与第五代 Tensor Core: two-level (block and
+ *      element) quantisation; MXFP4, each 32 FP4 elements sharing one 8-bit
+ *      scale.
  *  [Q] "TensorRT-LLM 深度工程实践…", §3.3 FP4/FP8 动态量化加速: the W4A16
  *      (AWQ/GPTQ) configuration with group size 128 and no zero point, and
  *      the W8A8 FP8 configuration with online activation ranges.
@@ -94,9 +109,10 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_I4 = 4, OR_E4M3 = 5 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_I4 = 4, OR_E4M3 = 5, OR_MXFP4 = 6 };
 enum { OR_E4M3_MAX = 448 };
 enum { OR_I4_GROUP = 128 };
+enum { OR_MX_BLOCK = 32 };
 enum { OR_NORM_NONE = 0, OR_NORM_RMS = 1, OR_NORM_LAYER = 2 };
 enum { OR_ACT_NONE = 0, OR_ACT_SWIGLU = 1, OR_ACT_GELU_TANH = 2 };
 
@@ -237,6 +253,45 @@ int or_dequant_i4(const uint8_t *q, const float *s, int64_t N, int64_t K,
 }
 
 /* ---------------------------------------------------------------------------
+ * MXFP4 weights (R12): E2M1 element codes with one E8M0 scale per block of 32
+ * consecutive k of a row.
+ * ------------------------------------------------------------------------- */
+double or_e2m1_value(int code) {
+    code &= 0xF;
+    const int e = (code >> 1) & 3, m = code & 1;
+    /* subnormal (e = 0): m * 0.5; normal: (1 + m/2) 2^(e-1) = (2 + m) 2^(e-2) */
+    const double v = e == 0 ? 0.5 * m : ldexp(2.0 + m, e - 2);
+    return (code & 8) ? -v : v;
+}
+
+double or_e8m0_value(int s) {
+    s &= 0xFF;
+    return s == 255 ? NAN : ldexp(1.0, s - 127);
+}
+
+int or_mxfp4_code(const uint8_t *row, int64_t k) {
+    return (row[k >> 1] >> ((k & 1) << 2)) & 0xF;   /* even k: low nibble */
+}
+
+int or_dequant_mxfp4(const uint8_t *q, const uint8_t *s, int64_t N, int64_t K,
+                     double *w_out, uint16_t *bits_out) {
+    if (K % OR_MX_BLOCK != 0) return -1;
+    const int64_t G = K / OR_MX_BLOCK;
+    for (int64_t j = 0; j < N; ++j) {
+        const uint8_t *row = q + j * (K / 2);
+        for (int64_t k = 0; k < K; ++k) {
+            /* exact product (2-bit significand times a power of two), then the
+             * bf16 operand */
+            const double prod = or_e2m1_value(or_mxfp4_code(row, k)) * or_e8m0_value(s[j * G + k / OR_MX_BLOCK]);
+            const double w = or_round(prod, OR_BF16);
+            if (w_out) w_out[j * K + k] = w;
+            if (bits_out) bits_out[j * K + k] = bf16_bits_of(w);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * E4M3 (R10).
  * ------------------------------------------------------------------------- */
 /* value of an E4M3 code (NaN for S.1111.111) */
@@ -365,14 +420,19 @@ int or_add_norm(const void *x, const void *r, const void *gamma, const void *bet
  * or [N, K/128]).  Each weight row is decoded once into a double buffer and then
  * used for every token row.
  * ------------------------------------------------------------------------- */
-int or_matmul_nt(const double *a, const void *w, int wdtype, const float *w_scale,
+int or_matmul_nt(const double *a, const void *w, int wdtype, const void *w_scale_v,
                  int64_t M, int64_t K, int64_t N, double *acc) {
     int bad = 0;
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < N; ++j) {
         double *wr = (double *)malloc(sizeof(double) * (size_t)K);
         if (!wr) { bad = 1; continue; }
-        if (wdtype == OR_I8)
+        const float *w_scale = (const float *)w_scale_v;
+        if (wdtype == OR_MXFP4) {
+            if (or_dequant_mxfp4((const uint8_t *)w + j * (K / 2), (const uint8_t *)w_scale_v + j * (K / OR_MX_BLOCK),
+                                 1, K, wr, NULL))
+                bad = 1;
+        } else if (wdtype == OR_I8)
             or_dequant_i8((const int8_t *)w + j * K, w_scale + j, 1, K, wr, NULL);
         else if (wdtype == OR_E4M3)
             for (int64_t k = 0; k < K; ++k)
@@ -417,7 +477,7 @@ static double *prologue(const void *x, const void *r, const void *gamma, const v
  * q[m, c / D, c % D] for c < H*D, then k, then v (R4, [D2]). */
 int or_add_norm_qkv(const void *x, const void *r, const void *gamma, const void *beta,
                     int act, int norm, double eps,
-                    const void *w, int wdtype, const float *w_scale, const void *bias,
+                    const void *w, int wdtype, const void *w_scale, const void *bias,
                     int64_t M, int64_t K, int64_t H, int64_t Hkv, int64_t D,
                     double *q, double *k, double *v, double *h_out, int rounded) {
     int64_t N = (H + 2 * Hkv) * D, nq = H * D, nkv = Hkv * D;
@@ -444,7 +504,7 @@ int or_add_norm_qkv(const void *x, const void *r, const void *gamma, const void 
  * GELU_TANH / NONE: w is [F, K], out = GELU(acc + b) or acc + b (R6, R7, [F]). */
 int or_gateup_act(const void *x, const void *r, const void *gamma, const void *beta,
                   int act, int norm, double eps,
-                  const void *w, int wdtype, const float *w_scale, const void *bias,
+                  const void *w, int wdtype, const void *w_scale, const void *bias,
                   int64_t M, int64_t K, int64_t F, int actfn,
                   double *out, double *h_out, int rounded) {
     int64_t N = actfn == OR_ACT_SWIGLU ? 2 * F : F;
@@ -481,7 +541,7 @@ int or_gateup_act(const void *x, const void *r, const void *gamma, const void *b
  * [T] "TensorRT-LLM 深度工程实践…", §4.1: the MLP's gate/up projection
  *     followed by the down projection; "TRT-LLM deep dive", 构建阶段详解 §3:
  *     the Add folded into the neighbouring kernel. */
-int or_down_residual(const void *a, int act, const void *w, int wdtype, const float *w_scale,
+int or_down_residual(const void *a, int act, const void *w, int wdtype, const void *w_scale,
                      const void *bias, const void *residual, int64_t M, int64_t K, int64_t N,
                      double *out) {
     double *ad = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));

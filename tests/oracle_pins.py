@@ -736,4 +736,78 @@ def pin_fp8_projection():
            rtol=1e-12, atol=1e-14, what="fp8 down")
 
 
+# ---------------------------------------------------------------------------
+# MXFP4 weights (R12)
+# ---------------------------------------------------------------------------
+# E2M1 magnitudes of codes 0..7 as the OCP microscaling format lists them
+_E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def pin_e2m1_decode_exhaustive():
+    vals = [oracle.e2m1_value(c) for c in range(16)]
+    assert vals[:8] == _E2M1_TABLE and vals[8:] == [-v for v in _E2M1_TABLE]
+    assert np.signbit(vals[8]) and not np.signbit(vals[0])                  # code 8 is -0
+    # the normal codes as fp32 bit patterns: sign, exponent e - 1 + 127, one mantissa bit
+    for c in range(16):
+        e, m = (c >> 1) & 3, c & 1
+        if e == 0:
+            continue
+        bits = ((c >> 3) << 31) | ((e - 1 + 127) << 23) | (m << 22)
+        assert np.array([bits], dtype=np.uint32).view(np.float32)[0] == vals[c], c
+
+
+def pin_e8m0_decode_exhaustive():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).double().numpy()                # torch's decoding
+    got = np.array([oracle.e8m0_value(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def pin_mxfp4_dequant_exhaustive():
+    """Every E2M1 code at every scale 0..254, placed so that the nibble order
+    and the block indexing matter: row j has scale j in its first block and
+    scale 254 - j in its second; element k holds code k % 16."""
+    N, K = 255, 64
+    codes = np.tile(np.arange(16, dtype=np.uint8), (N, K // 16))
+    scales = np.stack([np.arange(255), 254 - np.arange(255)], 1).astype(np.uint8)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    q = torch.from_numpy(packed).view(torch.float4_e2m1fn_x2)
+    s = torch.from_numpy(scales).view(torch.float8_e8m0fnu)
+    w, bits = oracle.dequant_mxfp4(q, s)
+    table = np.array(_E2M1_TABLE + [-v for v in _E2M1_TABLE])
+    sv = s.double().numpy()                                                  # torch's E8M0 decoding
+    exact = table[codes] * np.repeat(sv, 32, axis=1)
+    ref = torch.from_numpy(exact).to(torch.bfloat16)                        # torch's bf16 cast
+    assert np.array_equal(bits, ref.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(w, ref.double().numpy(), equal_nan=True)
+    # exact wherever bf16 reaches (no overflow below scale 253)
+    assert np.array_equal(w[:253, :32], exact[:253, :32])
+
+
+def pin_mxfp4_projection():
+    rng = _rng(61)
+    M, K, F = 3, 128, 6
+    x, r, g = _tiny(torch.bfloat16, M, K, seed=62)
+    codes = rng.integers(0, 16, (2 * F, K)).astype(np.uint8)
+    scales = rng.integers(118, 128, (2 * F, K // 32)).astype(np.uint8)
+    q = torch.from_numpy(codes[:, 0::2] | (codes[:, 1::2] << 4)).view(torch.float4_e2m1fn_x2)
+    s = torch.from_numpy(scales).view(torch.float8_e8m0fnu)
+    table = np.array(_E2M1_TABLE + [-v for v in _E2M1_TABLE])
+    w_val = table[codes] * np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, axis=1))
+    _, _, a = oracle.add_norm(x, r, g, None, "rms", 1e-5)
+    acc = a @ w_val.T
+    o = oracle.gateup_act(x, r, g, None, "rms", 1e-5, q, s, None, F, "swiglu")
+    ref = acc[:, :F] / (1 + np.exp(-acc[:, :F])) * acc[:, F:]
+    _close(o["out"], ref, rtol=1e-12, atol=1e-14, what="mxfp4 swiglu")
+    oq = oracle.add_norm_qkv(x, r, g, None, "rms", 1e-5, q[:8].contiguous(), s[:8].contiguous(), None, 2, 1, 2)
+    _close(np.concatenate([oq["q"].reshape(M, -1), oq["k"].reshape(M, -1), oq["v"].reshape(M, -1)], 1),
+           acc[:, :8], rtol=1e-12, atol=1e-14, what="mxfp4 qkv")
+    ad = _t(rng.standard_normal((M, K)), torch.bfloat16)
+    res = _t(rng.standard_normal((M, 2 * F)), torch.bfloat16)
+    _close(oracle.down_residual(ad, q, s, None, res), res.double().numpy() + ad.double().numpy() @ w_val.T,
+           rtol=1e-12, atol=1e-14, what="mxfp4 down")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -73,6 +73,14 @@ MUTANTS = {
     "fp8 activations not quantised": ("if (!rc && fp8) rc = or_quant_rows_e4m3(a, M, K, NULL, a, NULL);", "(void)0;"),
     "fp8 weight scale dropped": ("wr[k] = or_e4m3_value(((const uint8_t *)w)[j * K + k]) * (double)w_scale[j];",
                                  "wr[k] = or_e4m3_value(((const uint8_t *)w)[j * K + k]);"),
+    "e2m1 exponent bias": ("ldexp(2.0 + m, e - 2)", "ldexp(2.0 + m, e - 1)"),
+    "e2m1 subnormal step": ("e == 0 ? 0.5 * m", "e == 0 ? 1.0 * m"),
+    "e2m1 sign dropped": ("return (code & 8) ? -v : v;", "return v;"),
+    "e8m0 bias": ("ldexp(1.0, s - 127)", "ldexp(1.0, s - 128)"),
+    "mxfp4 nibble order": ("(row[k >> 1] >> ((k & 1) << 2)) & 0xF", "(row[k >> 1] >> ((1 - (k & 1)) << 2)) & 0xF"),
+    "mxfp4 block of 16": ("enum { OR_MX_BLOCK = 32 };", "enum { OR_MX_BLOCK = 16 };"),
+    "mxfp4 one scale per row": ("s[j * G + k / OR_MX_BLOCK]", "s[j * G]"),
+    "mxfp4 operand not rounded": ("const double w = or_round(prod, OR_BF16);", "const double w = prod;"),
     "fp8 down input not quantised": ("if (wdtype == OR_E4M3) or_quant_rows_e4m3(ad, M, K, NULL, ad, NULL);",
                                      "(void)0;"),
 }
