@@ -49,7 +49,7 @@ def algo_bytes(wl, call: str) -> int:
     written once; the normalised rows and the GEMM intermediates are not
     counted (the fusion keeps them on chip)."""
     ea = {"f32": 4, "f16": 2, "bf16": 2}[wl.act]
-    ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i4": 0.5, "e4m3": 1}[wl.wdt]
+    ew = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i4": 0.5, "e4m3": 1, "mxfp4": 0.5}[wl.wdt]
     if call == "down":                               # a [M, ffn], residual and out [M, hidden], weights
         N, K = wl.hidden, wl.ffn
         b = wl.M * K * ea + 2 * wl.M * N * ea + int(N * K * ew)
@@ -57,6 +57,8 @@ def algo_bytes(wl, call: str) -> int:
             b += 4 * N
         if wl.wdt == "i4":
             b += 4 * N * (K // 128)
+        if wl.wdt == "mxfp4":
+            b += N * (K // 32)
         return b
     M, K = wl.M, wl.hidden
     b = 2 * M * K * ea + K * ea                      # x, residual, gamma
@@ -74,6 +76,8 @@ def algo_bytes(wl, call: str) -> int:
         b += 4 * N                                   # per-row scales
     if wl.wdt == "i4":
         b += 4 * N * (K // 128)                      # per-row, per-128-k group scales
+    if wl.wdt == "mxfp4":
+        b += N * (K // 32)                           # one E8M0 byte per row and 32 k
     return b
 
 
@@ -364,13 +368,13 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::stream_kernel<(\d), (true|false|\d), (\d+), (\d+), (\d+), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         wq = {"true": "1", "false": "0"}.get(m.group(2), m.group(2))
-        act = {"1": "bf16-i8w", "2": "bf16-i4w"}.get(wq) or _ACT[m.group(1)]
+        act = {"1": "bf16-i8w", "2": "bf16-i4w", "3": "bf16-mxfp4w"}.get(wq) or _ACT[m.group(1)]
         return (f"stream_kernel<{act},m{16 * int(m.group(3))},n{64 * int(m.group(4))},"
                 f"k{32 * int(m.group(5))},{_EPI[m.group(6)]}>")
     m = re.search(r"fp::prefill_kernel<(\d), (true|false|\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         wq = {"true": "1", "false": "0"}.get(m.group(2), m.group(2))
-        act = {"1": "bf16-i8w", "2": "bf16-i4w"}.get(wq) or _ACT[m.group(1)]
+        act = {"1": "bf16-i8w", "2": "bf16-i4w", "3": "bf16-mxfp4w"}.get(wq) or _ACT[m.group(1)]
         return f"prefill_kernel<{act},128x512,{_EPI[m.group(3)]}>"
     m = re.search(r"fp::stats_kernel<(\d), \d+>", cxx)
     if m:

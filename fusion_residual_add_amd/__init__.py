@@ -17,26 +17,35 @@ from . import _lib
 from ._lib import FP_ACT, FP_NORM
 
 __all__ = ["fused_add_norm_qkv", "fused_add_norm_qkv_noalloc", "fused_gateup_act", "fused_down_residual", "fused_dequant_i8_bf16",
-           "fused_dequant_i4_bf16",
+           "fused_dequant_i4_bf16", "fused_dequant_mxfp4_bf16",
            "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
            "library_path", "tune_install", "tune_clear", "tune_count", "plan_override",
            "set_plan_override", "get_plan_override"]
 
 # torch.uint8 weights are int4 pairs (two values per byte, even k in the low nibble)
+# torch.float4_e2m1fn_x2 weights are MXFP4 element pairs (two per byte, even
+# k in the low nibble), with torch.float8_e8m0fnu block scales
 _DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
        torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8, torch.uint8: _lib.FP_I4,
-       torch.float8_e4m3fn: _lib.FP_E4M3}
+       torch.float8_e4m3fn: _lib.FP_E4M3, torch.float4_e2m1fn_x2: _lib.FP_MXFP4}
+_PACKED4 = (torch.uint8, torch.float4_e2m1fn_x2)
+
+
+def _scale_dtype(w: torch.Tensor) -> torch.dtype:
+    return torch.float8_e8m0fnu if w.dtype == torch.float4_e2m1fn_x2 else torch.float32
 
 
 def _check_weight(w: torch.Tensor, w_scale: Optional[torch.Tensor], Nw: int, K: int, name: str):
     """Shapes of the weight and its scales for the weight dtype."""
-    want = (Nw, K // 2) if w.dtype == torch.uint8 else (Nw, K)
+    want = (Nw, K // 2) if w.dtype in _PACKED4 else (Nw, K)
     if tuple(w.shape) != want:
         raise ValueError(f"{name} has shape {tuple(w.shape)}, expected {want}")
     if w.dtype in (torch.int8, torch.float8_e4m3fn) and w_scale is not None and tuple(w_scale.shape) != (Nw,):
         raise ValueError(f"w_scale has shape {tuple(w_scale.shape)}, expected {(Nw,)}")
     if w.dtype == torch.uint8 and w_scale is not None and tuple(w_scale.shape) != (Nw, K // 128):
         raise ValueError(f"w_scale has shape {tuple(w_scale.shape)}, expected {(Nw, K // 128)}")
+    if w.dtype == torch.float4_e2m1fn_x2 and w_scale is not None and tuple(w_scale.shape) != (Nw, K // 32):
+        raise ValueError(f"w_scale has shape {tuple(w_scale.shape)}, expected {(Nw, K // 32)}")
 
 
 class FusedProjError(RuntimeError):
@@ -153,7 +162,7 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
     st = fn(
         _ptr(x, "x", dev, act), _ptr(residual, "residual", dev, act), _ptr(h_out, "h_out", dev, act),
         _ptr(gamma, "gamma", dev, act), _ptr(beta, "beta", dev, act), FP_NORM[norm], float(eps),
-        _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, torch.float32),
+        _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w_qkv)),
         _ptr(bias, "bias", dev, act), _ptr(q, "q", dev, odt), _ptr(k, "k", dev, odt),
         _ptr(v, "v", dev, odt), M, K, n_heads, n_kv_heads, head_dim,
         _DT[act], _DT[wdt], _DT[odt],
@@ -189,7 +198,7 @@ def fused_add_norm_qkv_noalloc(x: torch.Tensor, residual: Optional[torch.Tensor]
     st = lib.fused_add_norm_qkv_noalloc(
         _ptr(x, "x", dev, act), _ptr(residual, "residual", dev, act), _ptr(h_out, "h_out", dev, act),
         _ptr(gamma, "gamma", dev, act), _ptr(beta, "beta", dev, act), FP_NORM[norm], float(eps),
-        _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, torch.float32),
+        _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w_qkv)),
         _ptr(bias, "bias", dev, act), _ptr(q, "q", dev, odt), _ptr(k, "k", dev, odt),
         _ptr(v, "v", dev, odt), M, K, n_heads, n_kv_heads, head_dim,
         _DT[act], _DT[w_qkv.dtype], _DT[odt], _stream(dev))
@@ -222,7 +231,7 @@ def fused_gateup_act(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: O
     st = lib.fused_gateup_act(
         _ptr(x, "x", dev, adt), _ptr(residual, "residual", dev, adt), _ptr(h_out, "h_out", dev, adt),
         _ptr(gamma, "gamma", dev, adt), _ptr(beta, "beta", dev, adt), FP_NORM[norm], float(eps),
-        _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, torch.float32), _ptr(bias, "bias", dev, adt),
+        _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w)), _ptr(bias, "bias", dev, adt),
         _ptr(out, "out", dev, odt), M, K, ffn, FP_ACT[act], _DT[adt], _DT[wdt], _DT[odt],
         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
     _check("fused_gateup_act", st)
@@ -249,7 +258,7 @@ def fused_down_residual(a: torch.Tensor, w: torch.Tensor, residual: Optional[tor
     need = int(lib.fp_workspace_bytes(M, F, Nw, _DT[adt], _DT[w.dtype]))
     ws = workspace if workspace is not None else _workspace(dev, stream, need)
     st = lib.fused_down_residual(
-        _ptr(a, "a", dev, adt), _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, torch.float32),
+        _ptr(a, "a", dev, adt), _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w)),
         _ptr(bias, "bias", dev, adt), _ptr(residual, "residual", dev, adt), _ptr(out, "out", dev, odt),
         M, F, Nw, _DT[adt], _DT[w.dtype], _DT[odt],
         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
@@ -283,6 +292,23 @@ def fused_dequant_i4_bf16(q: torch.Tensor, scale: torch.Tensor,
     st = lib.fused_dequant_i4_bf16(_ptr(q, "q", dev, torch.uint8), _ptr(scale, "scale", dev, torch.float32),
                                    _ptr(out, "out", dev, torch.bfloat16), N, K, _stream(dev))
     _check("fused_dequant_i4_bf16", st)
+    return out
+
+
+def fused_dequant_mxfp4_bf16(q: torch.Tensor, scale: torch.Tensor,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MXFP4 weights q [N, K/2] (float4_e2m1fn_x2, two codes per byte) with E8M0
+    block scales [N, K/32] (float8_e8m0fnu) -> bf16 [N, K]."""
+    lib = _lib.load()
+    _ptr(q, "q")
+    dev = q.device
+    N, K = q.shape[0], 2 * q.shape[1]
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    st = lib.fused_dequant_mxfp4_bf16(_ptr(q, "q", dev, torch.float4_e2m1fn_x2),
+                                      _ptr(scale, "scale", dev, torch.float8_e8m0fnu),
+                                      _ptr(out, "out", dev, torch.bfloat16), N, K, _stream(dev))
+    _check("fused_dequant_mxfp4_bf16", st)
     return out
 
 

@@ -46,7 +46,7 @@ struct Plan {
     int slots = 1;            // partial-sum slots per tile (1: none needed)
     int64_t tile_elems = 0;   // accumulators per tile (split-K partial size)
     size_t stats_off = 0, ctr_off = 0, part_off = 0, total = 0;
-    bool deq = false;         // int4 weights staged as bf16 in the workspace first
+    bool deq = false;         // int4 / MXFP4 weights staged as bf16 in the workspace first
     size_t deq_off = 0;
     size_t q_off = 0, qs_off = 0;   // FP8: activation codes [M, K] and row scales [M]
     int tile8 = 0;                  // FP8: fp::Gemm8Tile
@@ -205,7 +205,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         p.total = off;
         return p;
     }
-    const bool i4 = wdt == FP_I4;
+    const bool w4 = wdt == FP_I4 || wdt == FP_MXFP4;   // 4-bit weights, [N, K/2] bytes
+    const fp_dtype wdt_stored = wdt;
     const bool stream_elig = act != FP_F32 && M <= 64 && K % 256 == 0;
     const bool prefill_elig = act != FP_F32 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32);
     int fam;
@@ -217,11 +218,11 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         fam = 2;
     else
         fam = 0;
-    // int4 weights: dequantised in registers by the streaming and 128 x 512
+    // int4 / MXFP4 weights: dequantised in registers by the streaming and 128 x 512
     // kernels; for the tiled family dequantised into the workspace first and
     // then run as bf16 weights
-    if (i4 && fam == 0) wdt = FP_BF16;
-    const bool qw = wdt == FP_I8 || wdt == FP_I4;   // weights dequantised in the loader
+    if (w4 && fam == 0) wdt = FP_BF16;
+    const bool qw = wdt == FP_I8 || wdt == FP_I4 || wdt == FP_MXFP4;   // weights dequantised in the loader
     int64_t tiles, ksteps, target;
     if (fam == 1) {
         p.family = 1;
@@ -267,7 +268,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // Llama-2-70B's 8-way shard, 56 tiles, s = 4: 24.6 -> 23.4 us;
         // Llama-2-70B int8 gate/up, 224 tiles of 470 MB, 6 % slower so; an
         // uneven 1/s of K, 32 chunks in 3, 1 us slower)
-        const int64_t wbytes = wdt == FP_I4 ? Nw * K / 2 : Nw * K * (wdt == FP_I8 ? 1 : 2);
+        const int64_t wbytes = (wdt == FP_I4 || wdt == FP_MXFP4) ? Nw * K / 2 : Nw * K * (wdt == FP_I8 ? 1 : 2);
         if (wbytes <= (int64_t(256) << 20) && tiles > 0) {
             for (int64_t s = target / tiles < ksteps / minc ? target / tiles : ksteps / minc; s >= 1; --s) {
                 if (tiles * s * 100 < target * 85) break;
@@ -344,7 +345,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     if (p.slots > 1) off = align256(off + (size_t)tiles * 4);
     p.part_off = off;
     if (p.slots > 1) off = align256(off + (size_t)tiles * p.slots * p.tile_elems * 4);
-    if (i4 && p.family == 0) {
+    (void)wdt_stored;
+    if (w4 && p.family == 0) {
         p.deq = true;
         p.deq_off = off;
         off = align256(off + (size_t)Nw * (size_t)K * 2);
@@ -387,7 +389,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 fp_status check_dtypes(fp_dtype act, fp_dtype wdt, fp_dtype odt) {
     if (act != FP_F32 && act != FP_F16 && act != FP_BF16)
         return fail(FP_E_DTYPE, "act_dtype %d not in {F32, F16, BF16}", (int)act);
-    if (!(wdt == act || ((wdt == FP_I8 || wdt == FP_I4) && act == FP_BF16) ||
+    if (!(wdt == act || ((wdt == FP_I8 || wdt == FP_I4 || wdt == FP_MXFP4) && act == FP_BF16) ||
           (wdt == FP_E4M3 && (act == FP_BF16 || act == FP_F16))))
         return fail(FP_E_DTYPE, "w_dtype %d must equal act_dtype %d, or be I8 / I4 with BF16 activations, "
                     "or E4M3 with BF16 / F16 activations", (int)wdt, (int)act);
@@ -437,7 +439,7 @@ struct Common {
     fp_norm norm;
     float eps;
     const void *w;
-    const float *w_scale;
+    const void *w_scale;      // fp32 (int8, int4, E4M3) or E8M0 bytes (MXFP4)
     const void *bias;
     int64_t M, K, Nw;
     fp_dtype act, wdt, odt;
@@ -457,8 +459,8 @@ fp_status validate_common(const Common &c, const char *wname) {
     if (!c.x && c.M > 0) return fail(FP_E_NULL, "x is NULL");
     if (!c.w) return fail(FP_E_NULL, "%s is NULL", wname);
     if (c.norm != FP_NORM_NONE && !c.gamma) return fail(FP_E_NULL, "gamma is NULL but norm is not NONE");
-    if ((c.wdt == FP_I8 || c.wdt == FP_I4 || c.wdt == FP_E4M3) && !c.w_scale)
-        return fail(FP_E_NULL, "w_scale is NULL for int8 / int4 / E4M3 weights");
+    if ((c.wdt == FP_I8 || c.wdt == FP_I4 || c.wdt == FP_E4M3 || c.wdt == FP_MXFP4) && !c.w_scale)
+        return fail(FP_E_NULL, "w_scale is NULL for int8 / int4 / E4M3 / MXFP4 weights");
     if ((c.wdt == FP_I4 || c.wdt == FP_E4M3) && c.K % 128 != 0)
         return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 / E4M3 weights", (long long)c.K);
     if (c.wdt == FP_E4M3 && (c.M * c.K >= (int64_t(1) << 32) || c.Nw * c.K >= (int64_t(1) << 32)))
@@ -477,9 +479,10 @@ void add_inputs(const Common &c, std::vector<Range> &ins, const char *wname) {
     if (c.residual) ins.push_back(rng("residual", c.residual, c.M * c.K * ea));
     if (c.gamma && c.norm != FP_NORM_NONE) ins.push_back(rng("gamma", c.gamma, c.K * ea));
     if (c.beta && c.norm == FP_NORM_LAYER) ins.push_back(rng("beta", c.beta, c.K * ea));
-    ins.push_back(rng(wname, c.w, c.wdt == FP_I4 ? c.Nw * c.K / 2 : c.Nw * c.K * ew));
+    ins.push_back(rng(wname, c.w, (c.wdt == FP_I4 || c.wdt == FP_MXFP4) ? c.Nw * c.K / 2 : c.Nw * c.K * ew));
     if (c.w_scale && (c.wdt == FP_I8 || c.wdt == FP_E4M3)) ins.push_back(rng("w_scale", c.w_scale, c.Nw * 4));
     if (c.w_scale && c.wdt == FP_I4) ins.push_back(rng("w_scale", c.w_scale, c.Nw * (c.K / 128) * 4));
+    if (c.w_scale && c.wdt == FP_MXFP4) ins.push_back(rng("w_scale", c.w_scale, c.Nw * (c.K / 32)));
     if (c.bias) ins.push_back(rng("bias", c.bias, c.Nw * ea));
 }
 
@@ -511,7 +514,7 @@ fp_status run_fp8(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.x = codes;
     pa.a_scale = qscale;
     pa.w = c.w;
-    pa.w_scale = c.w_scale;
+    pa.w_scale = (const float *)c.w_scale;
     pa.bias = c.bias;
     pa.out_f32 = c.odt == FP_F32;
     pa.M = c.M;
@@ -561,14 +564,22 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
     pa.norm = (int)c.norm;
     pa.w = c.w;
-    pa.w_scale = c.w_scale;
+    pa.w_scale = (const float *)c.w_scale;
     const bool wi8 = c.wdt == FP_I8;
-    const int wq = c.wdt == FP_I8 ? 1 : (c.wdt == FP_I4 && !plan.deq) ? 2 : 0;
+    const int wq = c.wdt == FP_I8 ? 1 : plan.deq ? 0 : c.wdt == FP_I4 ? 2 : c.wdt == FP_MXFP4 ? 3 : 0;
     if (plan.deq) {
         void *wb = ws + plan.deq_off;
-        ProfScope ps(fp::dequant_i4_kernel_name(), c.stream);
-        hipError_t e = fp::launch_dequant_i4((const uint8_t *)c.w, c.w_scale, wb, c.Nw, c.K, c.stream);
-        if (e != hipSuccess) return hip_fail(e, "dequant_i4_kernel launch");
+        if (c.wdt == FP_MXFP4) {
+            ProfScope ps(fp::dequant_mxfp4_kernel_name(), c.stream);
+            hipError_t e = fp::launch_dequant_mxfp4((const uint8_t *)c.w, (const uint8_t *)c.w_scale, wb, c.Nw, c.K,
+                                                    c.stream);
+            if (e != hipSuccess) return hip_fail(e, "dequant_mxfp4_kernel launch");
+        } else {
+            ProfScope ps(fp::dequant_i4_kernel_name(), c.stream);
+            hipError_t e = fp::launch_dequant_i4((const uint8_t *)c.w, (const float *)c.w_scale, wb, c.Nw, c.K,
+                                                 c.stream);
+            if (e != hipSuccess) return hip_fail(e, "dequant_i4_kernel launch");
+        }
         pa.w = wb;
         pa.w_scale = nullptr;
     }
@@ -631,7 +642,7 @@ namespace {
 
 fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const void *gamma,
                        const void *beta, fp_norm norm, float eps, const void *w_qkv,
-                       const float *w_scale, const void *bias, void *q, void *k, void *v,
+                       const void *w_scale, const void *bias, void *q, void *k, void *v,
                        int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
                        int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
                        fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
@@ -692,7 +703,7 @@ fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const v
 namespace fp {
 fp_status add_norm_qkv_with_source(const void *x, const void *residual, void *h_out, const void *gamma,
                                    const void *beta, fp_norm norm, float eps, const void *w_qkv,
-                                   const float *w_scale, const void *bias, void *q, void *k, void *v,
+                                   const void *w_scale, const void *bias, void *q, void *k, void *v,
                                    int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
                                    int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
                                    fp_dtype out_dtype, void *hip_stream, WorkspaceSource source) {
@@ -706,7 +717,7 @@ extern "C" {
 
 fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, const void *gamma,
                              const void *beta, fp_norm norm, float eps, const void *w_qkv,
-                             const float *w_scale, const void *bias, void *q, void *k, void *v,
+                             const void *w_scale, const void *bias, void *q, void *k, void *v,
                              int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
                              int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
                              fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
@@ -718,7 +729,7 @@ fp_status fused_add_norm_qkv(const void *x, const void *residual, void *h_out, c
 
 fp_status fused_add_norm_qkv_hm(const void *x, const void *residual, void *h_out, const void *gamma,
                                 const void *beta, fp_norm norm, float eps, const void *w_qkv,
-                                const float *w_scale, const void *bias, void *q, void *k, void *v,
+                                const void *w_scale, const void *bias, void *q, void *k, void *v,
                                 int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
                                 int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
                                 fp_dtype out_dtype, void *workspace, size_t workspace_bytes,
@@ -730,7 +741,7 @@ fp_status fused_add_norm_qkv_hm(const void *x, const void *residual, void *h_out
 
 fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, const void *gamma,
                            const void *beta, fp_norm norm, float eps, const void *w,
-                           const float *w_scale, const void *bias, void *out, int64_t M,
+                           const void *w_scale, const void *bias, void *out, int64_t M,
                            int64_t hidden, int64_t ffn, fp_act act, fp_dtype act_dtype,
                            fp_dtype w_dtype, fp_dtype out_dtype, void *workspace,
                            size_t workspace_bytes, void *hip_stream) {
@@ -764,7 +775,7 @@ fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, con
     return run(c, plan, pa);
 }
 
-fp_status fused_down_residual(const void *a, const void *w, const float *w_scale, const void *bias,
+fp_status fused_down_residual(const void *a, const void *w, const void *w_scale, const void *bias,
                               const void *residual, void *out, int64_t M, int64_t ffn, int64_t hidden,
                               fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype, void *workspace,
                               size_t workspace_bytes, void *hip_stream) {
@@ -841,6 +852,24 @@ fp_status fused_dequant_i4_bf16(const void *q, const float *scale, void *out_bf1
     return FP_OK;
 }
 
+fp_status fused_dequant_mxfp4_bf16(const void *q, const void *scale, void *out_bf16, int64_t N, int64_t K,
+                                   void *hip_stream) {
+    if (N < 0) return fail(FP_E_SHAPE, "N = %lld is negative", (long long)N);
+    if (K <= 0 || K % 32 != 0) return fail(FP_E_SHAPE, "K = %lld must be a positive multiple of 32", (long long)K);
+    if (!q || !scale || !out_bf16) return fail(FP_E_NULL, "q, scale and out_bf16 must be non-NULL");
+    if (!aligned16(q) || !aligned16(out_bf16)) return fail(FP_E_ALIGN, "q and out_bf16 must be 16-byte aligned");
+    std::vector<Range> ins{rng("q", q, N * K / 2), rng("scale", scale, N * (K / 32))};
+    std::vector<Range> outs{rng("out_bf16", out_bf16, N * K * 2)};
+    fp_status st = check_alias(ins, outs);
+    if (st != FP_OK) return st;
+    if (N == 0) return FP_OK;
+    hipStream_t s = (hipStream_t)hip_stream;
+    ProfScope ps(fp::dequant_mxfp4_kernel_name(), s);
+    hipError_t e = fp::launch_dequant_mxfp4((const uint8_t *)q, (const uint8_t *)scale, out_bf16, N, K, s);
+    if (e != hipSuccess) return hip_fail(e, "dequant_mxfp4_kernel launch");
+    return FP_OK;
+}
+
 fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
                            fp_dtype w_dtype, fp_act act, char *buf, size_t cap) {
     if (!buf || cap == 0) return fail(FP_E_NULL, "buf must be non-NULL with cap > 0");
@@ -863,7 +892,7 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     }
     const int a = act_code(act_dtype);
     const bool wi8 = w_dtype == FP_I8;
-    const int wq = wi8 ? 1 : (w_dtype == FP_I4 && !p.deq) ? 2 : 0;
+    const int wq = wi8 ? 1 : p.deq ? 0 : w_dtype == FP_I4 ? 2 : w_dtype == FP_MXFP4 ? 3 : 0;
     const int epi = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
     const char *fam = p.family == 1 ? "stream" : p.family == 2 ? "prefill" : "tiled";
     const char *name = p.family == 1 ? fp::stream_kernel_name(a, wq, p.sc, epi)
@@ -872,7 +901,7 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     const int64_t grid = p.family == 1 ? p.grid : (int64_t)p.tiles_m * p.tiles_n * p.splits;
     snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s", fam, name,
              (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total,
-             p.deq ? " prep=dequant_i4_kernel" : "");
+             !p.deq ? "" : w_dtype == FP_MXFP4 ? " prep=dequant_mxfp4_kernel" : " prep=dequant_i4_kernel");
     return FP_OK;
 }
 

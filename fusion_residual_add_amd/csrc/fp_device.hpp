@@ -102,6 +102,33 @@ __device__ __forceinline__ void dequant32_i4(u32x4 qv, float s, u32x4 (&out)[4])
     for (int w = 0; w < 4; ++w) out[w] = dequant8_i4(qv[w], s, m8s);
 }
 
+// MXFP4 weights ("TensorRT-LLM 深度工程实践…", §3.3: FP4 weights with 16-bit
+// activations; §7.1: 32 FP4 elements sharing one 8-bit scale): E2M1 codes,
+// element 2i of a word in the low nibble of byte i, times the block's E8M0
+// scale 2^(s - 127).  The product is a 2-bit significand times a power of
+// two, so the bf16 value is exact wherever bf16 reaches.  The scale code
+// becomes its fp32 power of two (s = 0: the fp32 subnormal 2^-127), and one
+// hardware conversion (v_cvt_scalef32_pk_bf16_fp4) turns each byte into two
+// bf16 values.  The single definition used by the weight loaders and
+// dequant_mxfp4_kernel.
+__device__ __forceinline__ float e8m0_to_f32(unsigned s) {
+    return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+__device__ __forceinline__ u32x4 dequant8_mxfp4(unsigned word, float scale) {
+    u32x4 out;
+    out[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0));
+    out[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1));
+    out[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2));
+    out[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3));
+    return out;
+}
+// 32 codes of one 16-byte load (one MXFP4 block) -> four vectors of 8 bf16
+__device__ __forceinline__ void dequant32_mxfp4(u32x4 qv, unsigned scale_code, u32x4 (&out)[4]) {
+    const float sc = e8m0_to_f32(scale_code);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) out[w] = dequant8_mxfp4(qv[w], sc);
+}
+
 // ---------------------------------------------------------------------------
 // activation-dtype traits
 // ---------------------------------------------------------------------------

@@ -36,7 +36,7 @@ struct ProjArgs {
     int norm;               // 0 none, 1 rms, 2 layer
     // weights
     const void *w;          // [Nw, K] act or int8
-    const float *w_scale;   // [Nw] (int8 only)
+    const float *w_scale;   // int8 / E4M3: [Nw] fp32; int4: [Nw, K/128] fp32; MXFP4: [Nw, K/32] E8M0 bytes
     const void *bias;       // [Nw] act or null
     const void *res_epi;    // EPI_LINEAR: [M, F] act added to the output (residual stream), or null
     const float *a_scale;   // E4M3 path: [M] per-token scale of the quantised rows in x
@@ -110,6 +110,9 @@ const char *dequant_kernel_name();
 hipError_t launch_dequant_i4(const uint8_t *q, const float *scale, void *out, int64_t N, int64_t K,
                              hipStream_t s);
 const char *dequant_i4_kernel_name();
+hipError_t launch_dequant_mxfp4(const uint8_t *q, const uint8_t *scale, void *out, int64_t N, int64_t K,
+                                hipStream_t s);
+const char *dequant_mxfp4_kernel_name();
 // E4M3 (W8A8) path: per-token quantisation of the normalised rows, then the
 // FP8 GEMM on the codes (x = codes, a_scale, w = E4M3 weights, w_scale [Nw])
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s);
@@ -125,7 +128,7 @@ const char *gemm8_kernel_name(int act, int tile, int epi);
 typedef fp_status (*WorkspaceSource)(size_t need, void **ws, size_t *ws_bytes, char *msg, size_t cap);
 fp_status add_norm_qkv_with_source(const void *x, const void *residual, void *h_out, const void *gamma,
                                    const void *beta, fp_norm norm, float eps, const void *w_qkv,
-                                   const float *w_scale, const void *bias, void *q, void *k, void *v,
+                                   const void *w_scale, const void *bias, void *q, void *k, void *v,
                                    int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads,
                                    int64_t head_dim, fp_dtype act_dtype, fp_dtype w_dtype,
                                    fp_dtype out_dtype, void *hip_stream, WorkspaceSource source);

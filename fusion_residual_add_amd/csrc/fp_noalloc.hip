@@ -62,7 +62,7 @@ fp_status static_scratch(size_t need, void **ws, size_t *ws_bytes, char *msg, si
 
 extern "C" fp_status fused_add_norm_qkv_noalloc(
     const void *x, const void *residual, void *h_out, const void *gamma, const void *beta, fp_norm norm,
-    float eps, const void *w_qkv, const float *w_scale, const void *bias, void *q, void *k, void *v, int64_t M,
+    float eps, const void *w_qkv, const void *w_scale, const void *bias, void *q, void *k, void *v, int64_t M,
     int64_t hidden, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, fp_dtype act_dtype,
     fp_dtype w_dtype, fp_dtype out_dtype, void *hip_stream) {
     return fp::add_norm_qkv_with_source(x, residual, h_out, gamma, beta, norm, eps, w_qkv, w_scale, bias, q, k, v,

@@ -53,15 +53,16 @@ __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >
 // LN: LayerNorm (mean, beta); otherwise RMSNorm or no norm, whose
 // normalisation is two multiplies (h * rstd * gamma) and has no beta to load.
 // WQ: weight storage -- 0 the activation dtype (straight into LDS), 1 int8,
-// 2 int4 (both through registers, dequantised into LDS).
+// 2 int4, 3 MXFP4 (all three through registers, dequantised into LDS).
 template <int ACT, int WQ, int EPI, bool LN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(ProjArgs p) {
     using T = Act<ACT>;
     using namespace pf;
-    constexpr bool WI8 = WQ == 1, WI4 = WQ == 2, WREG = WQ != 0;
+    // WI4: 4-bit weights of either kind ([N, K/2] bytes, 32 values per 16-byte vector)
+    constexpr bool WI8 = WQ == 1, WMX = WQ == 3, WI4 = WQ == 2 || WMX, WREG = WQ != 0;
     static_assert(ACT != ACT_F32, "16-bit activations");
-    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 weights feed bf16 MFMA");
+    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 / MXFP4 weights feed bf16 MFMA");
     // A and B tiles of the two stages as four distinct LDS objects, so that
     // the compiler can tell the direct-to-LDS weight loads into one stage from
     // the fragment reads of the other (and waits for them only at the end of
@@ -109,10 +110,10 @@ void prefill_kernel(ProjArgs p) {
                                                                         has_beta ? (uint32_t)(p.K * 2) : 0u, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void *)p.w, (short)0, (uint32_t)(WI4 ? p.Nw * p.K / 2 : p.Nw * p.K * (WI8 ? 1 : 2)), 0x00020000);
-    // int4: the group scales [Nw, K / 128]
+    // int4: the group scales [Nw, K / 128] fp32; MXFP4: the block scales [Nw, K / 32] E8M0
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(WI4 ? (const void *)p.w_scale : p.w), (short)0, WI4 ? (uint32_t)(p.Nw * (p.K / 128) * 4) : 0u,
-        0x00020000);
+        (void *)(WI4 ? (const void *)p.w_scale : p.w), (short)0,
+        WMX ? (uint32_t)(p.Nw * (p.K / 32)) : WI4 ? (uint32_t)(p.Nw * (p.K / 128) * 4) : 0u, 0x00020000);
     // norm none: gamma reads as zero and g1 turns it into one
     const float g1 = p.norm != 0 ? 0.f : 1.f;
 
@@ -172,7 +173,8 @@ void prefill_kernel(ProjArgs p) {
             b_sc[i] = p.w_scale[wrow];
         } else if constexpr (WI4) {
             b_off[i] = (uint32_t)(wrow * (p.K / 2)) + (tid & 1) * 16;
-            b_soff[i] = (uint32_t)(wrow * (p.K / 128) * 4);
+            // MXFP4: the thread's 32 values of a stage are block 2 kt + (tid & 1) of the row
+            b_soff[i] = WMX ? (uint32_t)(wrow * (p.K / 32)) + (tid & 1) : (uint32_t)(wrow * (p.K / 128) * 4);
         } else {
             const int c = (lane & 7) ^ ((br >> 1) & 7);
             b_off[i] = (uint32_t)((wrow * p.K + c * 8) * 2);
@@ -184,9 +186,10 @@ void prefill_kernel(ProjArgs p) {
     // row's registers are refilled with stage kt + 2 right after use, so every
     // load has a whole step to arrive.
     struct ARegs { u32x4 x[4], r[4], g, b; };
-    struct BRegs {                  // int8 / int4: the thread's weight vectors of a stage
+    struct BRegs {                  // int8 / int4 / MXFP4: the thread's weight vectors of a stage
         u32x4 q[WI4 ? 4 : 8];
         float s[WI4 ? 4 : 1];       // int4: their rows' scales for the stage
+        unsigned sm[WMX ? 4 : 1];   // MXFP4: their blocks' scale codes
     };
     ARegs A;
     BRegs B;
@@ -240,7 +243,10 @@ void prefill_kernel(ProjArgs p) {
     // int8 weights: vector i of stage kt into registers; dequantised into
     // the LDS tile of its stage (16 values -> two 16-byte bf16 chunks)
     auto bload_one = [&](int kt, int i) {
-        if constexpr (WI4) {
+        if constexpr (WMX) {
+            B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * (BK / 2));
+            B.sm[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, b_soff[i], (uint32_t)kt * 2, 0);
+        } else if constexpr (WI4) {
             B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * (BK / 2));
             B.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, b_soff[i],
                                                                                     (uint32_t)(kt / 2) * 4, 0));
@@ -256,13 +262,19 @@ void prefill_kernel(ProjArgs p) {
         *(u32x4 *)(lb + swz(br, c0)) = lo;
         *(u32x4 *)(lb + swz(br, c0 + 1)) = hi;
     };
-    // int4: half hf of vector i (16 values, two 16-byte chunks) into the LDS tile
+    // int4 / MXFP4: half hf of vector i (16 values, two 16-byte chunks) into the LDS tile
     auto bstore_half = [&](unsigned char *lb, int i, int hf) {
-        const float s = B.s[i], m8s = -8.0f * s;
         const int br = (tid >> 1) + 128 * i;
         const int c0 = (tid & 1) * 4 + hf * 2;
-        *(u32x4 *)(lb + swz(br, c0)) = dequant8_i4(B.q[i][2 * hf], s, m8s);
-        *(u32x4 *)(lb + swz(br, c0 + 1)) = dequant8_i4(B.q[i][2 * hf + 1], s, m8s);
+        if constexpr (WMX) {
+            const float sc = e8m0_to_f32(B.sm[i]);
+            *(u32x4 *)(lb + swz(br, c0)) = dequant8_mxfp4(B.q[i][2 * hf], sc);
+            *(u32x4 *)(lb + swz(br, c0 + 1)) = dequant8_mxfp4(B.q[i][2 * hf + 1], sc);
+        } else {
+            const float s = B.s[i], m8s = -8.0f * s;
+            *(u32x4 *)(lb + swz(br, c0)) = dequant8_i4(B.q[i][2 * hf], s, m8s);
+            *(u32x4 *)(lb + swz(br, c0 + 1)) = dequant8_i4(B.q[i][2 * hf + 1], s, m8s);
+        }
     };
 
     // ---- accumulators: acc[i][j][q] = D[row i*32 + 8(q/4) + 4(lane/32) + q%4]

@@ -313,6 +313,21 @@ __global__ __launch_bounds__(256) void dequant_i4_kernel(const uint8_t *q, const
     }
 }
 
+// MXFP4 weights, 32 values (one 16-byte load, one block) per thread:
+// out[j, k] = bf16(e2m1(q[j, k]) * 2^(scale[j, k / 32] - 127)), two codes per byte.
+__global__ __launch_bounds__(256) void dequant_mxfp4_kernel(const uint8_t *q, const uint8_t *scale,
+                                                            unsigned short *out, int64_t N, int64_t K) {
+    const int64_t per_row = K / 32;
+    const int64_t nv = N * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (int64_t)gridDim.x * 256) {
+        const u32x4 qv = *(const u32x4 *)(q + i * 16);
+        u32x4 o[4];
+        dequant32_mxfp4(qv, scale[i], o);   // block i of the [N, K/32] scales
+#pragma unroll
+        for (int w = 0; w < 4; ++w) *(u32x4 *)(out + i * 32 + 8 * w) = o[w];
+    }
+}
+
 static const char *kStatsNames[3] = {"stats_kernel<f32>", "stats_kernel<f16>", "stats_kernel<bf16>"};
 
 const char *stats_kernel_name(int act) { return kStatsNames[act]; }
@@ -320,6 +335,8 @@ const char *stats_kernel_name(int act) { return kStatsNames[act]; }
 const char *dequant_kernel_name() { return "dequant_kernel"; }
 
 const char *dequant_i4_kernel_name() { return "dequant_i4_kernel"; }
+
+const char *dequant_mxfp4_kernel_name() { return "dequant_mxfp4_kernel"; }
 
 template <int ACT>
 static hipError_t launch_stats_t(const StatsArgs &a, hipStream_t s) {
@@ -395,6 +412,15 @@ hipError_t launch_dequant_i4(const uint8_t *q, const float *scale, void *out, in
     int64_t blocks = (nv + 255) / 256;
     if (blocks > 16384) blocks = 16384;
     return launch_k(dequant_i4_kernel, (unsigned)blocks, s, q, scale, (unsigned short *)out, N, K);
+}
+
+hipError_t launch_dequant_mxfp4(const uint8_t *q, const uint8_t *scale, void *out, int64_t N, int64_t K,
+                                hipStream_t s) {
+    const int64_t nv = N * (K / 32);
+    if (nv == 0) return hipSuccess;
+    int64_t blocks = (nv + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    return launch_k(dequant_mxfp4_kernel, (unsigned)blocks, s, q, scale, (unsigned short *)out, N, K);
 }
 
 hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,

@@ -11,8 +11,9 @@ hipError_t launch_stream_bf16(const StreamCfg &c, const ProjArgs &a, unsigned gr
 hipError_t launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 hipError_t launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 hipError_t launch_stream_i4(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_stream_mx(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 
-// wq: 0 weights in the activation dtype, 1 int8, 2 int4
+// wq: 0 weights in the activation dtype, 1 int8, 2 int4, 3 MXFP4
 hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s) {
     if (grid_wgs <= 0 || a.tiles_n <= 0) return hipSuccess;
     if (a.epi == EPI_SWIGLU && c.nr % 2 != 0) return hipErrorInvalidValue;
@@ -21,6 +22,7 @@ hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a,
     const unsigned grid = (unsigned)grid_wgs;
     if (wq == 1) return launch_stream_i8(c, a, grid, s);
     if (wq == 2) return launch_stream_i4(c, a, grid, s);
+    if (wq == 3) return launch_stream_mx(c, a, grid, s);
     if (act == ACT_F16) return launch_stream_f16(c, a, grid, s);
     return launch_stream_bf16(c, a, grid, s);
 }
@@ -29,20 +31,22 @@ hipError_t launch_prefill_bf16(const ProjArgs &a, unsigned grid, hipStream_t s);
 hipError_t launch_prefill_f16(const ProjArgs &a, unsigned grid, hipStream_t s);
 hipError_t launch_prefill_i8(const ProjArgs &a, unsigned grid, hipStream_t s);
 hipError_t launch_prefill_i4(const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_prefill_mx(const ProjArgs &a, unsigned grid, hipStream_t s);
 
-// wq: 0 weights in the activation dtype, 1 int8, 2 int4
+// wq: 0 weights in the activation dtype, 1 int8, 2 int4, 3 MXFP4
 hipError_t launch_prefill(int act, int wq, const ProjArgs &a, hipStream_t s) {
     const int64_t g = (int64_t)a.tiles_m * a.tiles_n * a.splits;
     if (g <= 0) return hipSuccess;
     const unsigned grid = (unsigned)g;
     if (wq == 1) return launch_prefill_i8(a, grid, s);
     if (wq == 2) return launch_prefill_i4(a, grid, s);
+    if (wq == 3) return launch_prefill_mx(a, grid, s);
     if (act == ACT_F16) return launch_prefill_f16(a, grid, s);
     return launch_prefill_bf16(a, grid, s);
 }
 
 const char *prefill_kernel_name(int act, int wq, int epi) {
-    static const char *acts[5] = {"f32", "f16", "bf16", "bf16-i8w", "bf16-i4w"};
+    static const char *acts[6] = {"f32", "f16", "bf16", "bf16-i8w", "bf16-i4w", "bf16-mxfp4w"};
     static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
     thread_local char buf[64];
     snprintf(buf, sizeof buf, "prefill_kernel<%s,128x512,%s>", acts[wq ? 2 + wq : act], epis[epi]);
@@ -50,7 +54,7 @@ const char *prefill_kernel_name(int act, int wq, int epi) {
 }
 
 const char *stream_kernel_name(int act, int wq, const StreamCfg &c, int epi) {
-    static const char *acts[5] = {"f32", "f16", "bf16", "bf16-i8w", "bf16-i4w"};
+    static const char *acts[6] = {"f32", "f16", "bf16", "bf16-i8w", "bf16-i4w", "bf16-mxfp4w"};
     static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
     thread_local char buf[64];
     snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", acts[wq ? 2 + wq : act], 16 * c.mf,

@@ -34,14 +34,15 @@
 namespace fp {
 
 // WQ: weight storage -- 0 the activation dtype, 1 int8 (one scale per row),
-// 2 int4 (one scale per row and group of 128 k, two values per byte).
+// 2 int4 (one scale per row and group of 128 k, two values per byte),
+// 3 MXFP4 (E2M1 codes two per byte, one E8M0 scale per row and 32 k).
 template <int ACT, int WQ, int MF, int NR, int U, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(ProjArgs p) {
     using T = Act<ACT>;
-    constexpr bool WI8 = WQ == 1, WI4 = WQ == 2;
+    constexpr bool WI8 = WQ == 1, WMX = WQ == 3, WI4 = WQ == 2 || WMX;   // WI4: 4-bit weights of either kind
     static_assert(ACT != ACT_F32, "the stream kernel takes 16-bit activations");
-    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 weights feed bf16 MFMA");
+    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 / MXFP4 weights feed bf16 MFMA");
     static_assert(EPI != EPI_SWIGLU || NR % 2 == 0, "gate/up fragments come in pairs");
     static_assert(!WI8 || U % 2 == 0, "one int8 load covers two k slices");
     static_assert(!WI4 || U % 4 == 0, "one int4 load covers four k slices (one scale group)");
@@ -74,6 +75,7 @@ void stream_kernel(ProjArgs p) {
         const char *wrow[NR];
         float wsc[NR];
         const float *wsr[NR];   // int4: the row's group scales
+        const unsigned char *wsm[NR];   // MXFP4: the row's block scales
     #pragma unroll
         for (int n = 0; n < NR; ++n) {
             int64_t r;
@@ -89,8 +91,10 @@ void stream_kernel(ProjArgs p) {
             wrow[n] = (const char *)p.w + (WI4 ? r * (p.K / 2) : r * p.K * (WI8 ? 1 : 2));
             wsc[n] = 0.f;
             wsr[n] = nullptr;
+            wsm[n] = nullptr;
             if constexpr (WI8) wsc[n] = p.w_scale[r];
-            if constexpr (WI4) wsr[n] = p.w_scale + r * (p.K / 128);
+            if constexpr (WQ == 2) wsr[n] = p.w_scale + r * (p.K / 128);
+            if constexpr (WMX) wsm[n] = (const unsigned char *)p.w_scale + r * (p.K / 32);
         }
         auto wload = [&](int c, int n, int u) -> u32x4 {
             if constexpr (WI8)
@@ -179,17 +183,26 @@ void stream_kernel(ProjArgs p) {
     #pragma unroll
             for (int n = 0; n < NR; ++n) acc[m][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-        // weight registers of one chunk (int4: with the group scales of the chunk)
+        // weight registers of one chunk (int4: with the group scales of the
+        // chunk; MXFP4: with the block scale code of each lane's load)
         struct WRegs {
             u32x4 w[NR][NL];
             float s[NR][WI4 ? NL : 1];
+            unsigned sm[NR][WMX ? NL : 1];
         };
         auto wload_all = [&](int c, WRegs &W) {
     #pragma unroll
             for (int u = 0; u < NL; ++u)
     #pragma unroll
                 for (int n = 0; n < NR; ++n) W.w[n][u] = wload(c, n, u);
-            if constexpr (WI4) {
+            if constexpr (WMX) {
+                // lane group g of load u covers the 32-k block 4 (c * U / 4 + u) + g
+    #pragma unroll
+                for (int u = 0; u < NL; ++u)
+    #pragma unroll
+                    for (int n = 0; n < NR; ++n)
+                        W.sm[n][u] = wsm[n][(int64_t)c * (CK / 32) + u * 4 + (lane >> 4)];
+            } else if constexpr (WI4) {
     #pragma unroll
                 for (int n = 0; n < NR; ++n) {
                     if constexpr (NL == 2) {   // groups 2c, 2c + 1: adjacent, 8-byte aligned
@@ -213,7 +226,10 @@ void stream_kernel(ProjArgs p) {
                 if constexpr (WI4) {
                     u32x4 b[NR][4];
     #pragma unroll
-                    for (int n = 0; n < NR; ++n) dequant32_i4(W.w[n][u], W.s[n][u], b[n]);
+                    for (int n = 0; n < NR; ++n) {
+                        if constexpr (WMX) dequant32_mxfp4(W.w[n][u], W.sm[n][u], b[n]);
+                        else dequant32_i4(W.w[n][u], W.s[n][u], b[n]);
+                    }
                     // a lane's 32 int4 are k = 128u + 32 (lane / 16) + [0, 32): four MFMA k slices
     #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) {

@@ -282,18 +282,20 @@ MX_BLOCK = 32
 _E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
 
 
-def _e2m1_codes(t: np.ndarray) -> np.ndarray:
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+_E2M1_MID_UP = (False, True, False, True, False, True, False)   # midpoints whose lower code is odd
+
+
+def _e2m1_codes(t: torch.Tensor) -> torch.Tensor:
     """Nearest E2M1 code of each value (ties to the even code, i.e. the one
     with mantissa bit 0), magnitudes saturated at 6, sign kept (-0 for
-    negative values that round to zero)."""
-    a = np.minimum(np.abs(t), 6.0)
-    d = np.abs(a[..., None] - _E2M1)                       # distance to each magnitude
-    best = d.min(axis=-1, keepdims=True)
-    cand = d == best
-    # among equally near magnitudes prefer the even code (index & 1 == 0)
-    idx = np.where(cand[..., 0::2].any(-1), np.argmax(np.where(cand, (np.arange(8) % 2 == 0), False), -1),
-                   np.argmax(cand, -1))
-    return (idx | np.where(np.signbit(t), 8, 0)).astype(np.uint8)
+    negative values that round to zero): the number of midpoints below the
+    magnitude, plus one at a midpoint whose lower neighbour is odd."""
+    a = t.abs()
+    idx = torch.zeros(t.shape, dtype=torch.uint8)
+    for mid, up in zip(_E2M1_MIDS, _E2M1_MID_UP):
+        idx += (a > mid) | (a == mid) & up
+    return idx | torch.signbit(t).to(torch.uint8) * 8
 
 
 def quantize_blocks_mxfp4(w: np.ndarray):
@@ -306,19 +308,18 @@ def quantize_blocks_mxfp4(w: np.ndarray):
     N, K = w.shape
     assert K % MX_BLOCK == 0, "MXFP4 weights need K a multiple of 32"
     G = K // MX_BLOCK
-    q = np.empty((N, K // 2), dtype=np.uint8)
-    s = np.empty((N, G), dtype=np.uint8)
-    step = max(1, (1 << 22) // max(K, 1))
+    q = torch.empty((N, K // 2), dtype=torch.uint8)
+    s = torch.empty((N, G), dtype=torch.uint8)
+    step = max(1, (1 << 24) // max(K, 1))
     for j0 in range(0, N, step):
-        blk = w[j0:j0 + step].astype(np.float64).reshape(-1, G, MX_BLOCK)
-        amax = np.abs(blk).max(axis=2)
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0).astype(np.int64)
-        e = np.clip(e, -127, 127)
-        codes = _e2m1_codes(blk / np.exp2(e)[:, :, None]).reshape(blk.shape[0], K)
+        blk = torch.from_numpy(np.ascontiguousarray(w[j0:j0 + step], dtype=np.float32)).view(-1, G, MX_BLOCK)
+        amax = blk.abs().amax(dim=2)
+        # floor(log2(amax)) exactly: amax = f 2^x with f in [0.5, 1) gives x - 1
+        e = torch.where(amax > 0, torch.frexp(amax).exponent - 3, 0).clamp(-127, 127)
+        codes = _e2m1_codes(torch.ldexp(blk, -e[:, :, None].to(torch.float32))).view(blk.shape[0], K)
         q[j0:j0 + step] = codes[:, 0::2] | (codes[:, 1::2] << 4)
-        s[j0:j0 + step] = (e + 127).astype(np.uint8)
-    return (torch.from_numpy(q).view(torch.float4_e2m1fn_x2),
-            torch.from_numpy(s).view(torch.float8_e8m0fnu))
+        s[j0:j0 + step] = (e + 127).to(torch.uint8)
+    return q.view(torch.float4_e2m1fn_x2), s.view(torch.float8_e8m0fnu)
 
 
 def _weight(rng, wl: Workload, N: int):

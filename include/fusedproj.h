@@ -52,6 +52,20 @@
  *    multiple of 128.  Calls that the weight-streaming kernel does not take
  *    (see fp_describe_plan) first dequantise the weight into the workspace
  *    (N * hidden * 2 bytes of it).
+ *  - MXFP4 weights (w_dtype FP_MXFP4, act_dtype FP_BF16 only; the FP4
+ *    weight configuration with 16-bit activations of "TensorRT-LLM
+ *    深度工程实践…" §3.3, in the microscaling layout of §7.1: 32 FP4
+ *    elements sharing one 8-bit scale): the [N, hidden] weight is stored as
+ *    [N, hidden/2] bytes of E2M1 codes (1 sign, 2 exponent bits with bias 1,
+ *    1 mantissa bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}), element k of a row in
+ *    the low nibble of byte k/2 for even k and in the high nibble for odd k;
+ *    w_scale points to [N, hidden/32] E8M0 bytes (scale 2^(s - 127); 255,
+ *    NaN, is not accepted as data), one per row and block of 32 consecutive
+ *    k; each element is dequantised as bf16_rne(e2m1(code) * 2^(s - 127)),
+ *    exact for every s up to 252, bit-exactly the result of
+ *    fused_dequant_mxfp4_bf16.  Calls that the streaming and 128 x 512
+ *    kernels do not take dequantise the weight into the workspace first
+ *    (N * hidden * 2 bytes of it).
  *  - FP8 W8A8 (w_dtype FP_E4M3, act_dtype FP_BF16 or FP_F16; the full-FP8
  *    configuration of "TensorRT-LLM 深度工程实践…" §3.3, whose activation
  *    range is taken from the data at run time): the weight is [N, hidden]
@@ -66,9 +80,9 @@
  *    (M * hidden + 4 M bytes of it).  hidden must be a multiple of 128, and
  *    M * hidden and N * hidden must be below 2^32.
  *  - Dtypes: act_dtype in {F32, F16, BF16}; w_dtype == act_dtype, or FP_I8 /
- *    FP_I4 with act_dtype FP_BF16, or FP_E4M3 with act_dtype FP_BF16 /
- *    FP_F16; out_dtype == act_dtype or FP_F32.  gamma, beta and bias are
- *    act_dtype; w_scale is fp32.
+ *    FP_I4 / FP_MXFP4 with act_dtype FP_BF16, or FP_E4M3 with act_dtype
+ *    FP_BF16 / FP_F16; out_dtype == act_dtype or FP_F32.  gamma, beta and
+ *    bias are act_dtype; w_scale is fp32, except E8M0 bytes for FP_MXFP4.
  *  - Every pointer must be 16-byte aligned.  No output range may overlap an
  *    input range, another output, or the workspace.
  *  - Execution is asynchronous on hip_stream (NULL = the default stream);
@@ -92,7 +106,7 @@
 extern "C" {
 #endif
 
-typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4, FP_E4M3 = 5 } fp_dtype;
+typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4, FP_E4M3 = 5, FP_MXFP4 = 6 } fp_dtype;
 typedef enum { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
 typedef enum { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
 /* Codes 0-6 keep the numbering of the boundary's first specification;
@@ -122,8 +136,9 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols,
  *  h_out       : [M, hidden] act_dtype or NULL
  *  gamma, beta : [hidden] act_dtype (gamma required unless FP_NORM_NONE)
  *  w_qkv       : [(H + 2 Hkv) * D, hidden], rows = Q heads, then K, then V
- *  w_scale     : fp32, required iff w_dtype is FP_I8 or FP_E4M3
- *                ([(H + 2 Hkv) * D]) or FP_I4 ([(H + 2 Hkv) * D, hidden / 128])
+ *  w_scale     : required iff w_dtype is FP_I8 or FP_E4M3 (fp32
+ *                [(H + 2 Hkv) * D]), FP_I4 (fp32 [(H + 2 Hkv) * D, hidden / 128])
+ *                or FP_MXFP4 (E8M0 bytes [(H + 2 Hkv) * D, hidden / 32])
  *  bias        : [(H + 2 Hkv) * D] act_dtype or NULL
  *  q           : [M, H, D]   out_dtype, token-major
  *  k, v        : [M, Hkv, D] out_dtype, token-major
@@ -132,7 +147,7 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols,
 fp_status fused_add_norm_qkv(
     const void *x, const void *residual, void *h_out,
     const void *gamma, const void *beta, fp_norm norm, float eps,
-    const void *w_qkv, const float *w_scale, const void *bias,
+    const void *w_qkv, const void *w_scale, const void *bias,
     void *q, void *k, void *v,
     int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
     fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
@@ -149,7 +164,7 @@ fp_status fused_add_norm_qkv(
 fp_status fused_add_norm_qkv_hm(
     const void *x, const void *residual, void *h_out,
     const void *gamma, const void *beta, fp_norm norm, float eps,
-    const void *w_qkv, const float *w_scale, const void *bias,
+    const void *w_qkv, const void *w_scale, const void *bias,
     void *q, void *k, void *v,
     int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
     fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
@@ -173,7 +188,7 @@ fp_status fused_add_norm_qkv_hm(
 fp_status fused_add_norm_qkv_noalloc(
     const void *x, const void *residual, void *h_out,
     const void *gamma, const void *beta, fp_norm norm, float eps,
-    const void *w_qkv, const float *w_scale, const void *bias,
+    const void *w_qkv, const void *w_scale, const void *bias,
     void *q, void *k, void *v,
     int64_t M, int64_t hidden, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
     fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype, void *hip_stream);
@@ -194,7 +209,7 @@ fp_status fused_add_norm_qkv_noalloc(
 fp_status fused_gateup_act(
     const void *x, const void *residual, void *h_out,
     const void *gamma, const void *beta, fp_norm norm, float eps,
-    const void *w, const float *w_scale, const void *bias, void *out,
+    const void *w, const void *w_scale, const void *bias, void *out,
     int64_t M, int64_t hidden, int64_t ffn, fp_act act,
     fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
     void *workspace, size_t workspace_bytes, void *hip_stream);
@@ -220,7 +235,7 @@ fp_status fused_gateup_act(
  *  Requires ffn a positive multiple of 64 (128 for int4 and E4M3), hidden a positive
  *  multiple of 16.  Dtypes, alignment, workspace (fp_workspace_bytes(M, ffn,
  *  hidden, act_dtype, w_dtype)) and errors as for the other calls. */
-fp_status fused_down_residual(const void *a, const void *w, const float *w_scale, const void *bias,
+fp_status fused_down_residual(const void *a, const void *w, const void *w_scale, const void *bias,
                               const void *residual, void *out, int64_t M, int64_t ffn, int64_t hidden,
                               fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
                               void *workspace, size_t workspace_bytes, void *hip_stream);
@@ -241,6 +256,16 @@ fp_status fused_dequant_i8_bf16(const int8_t *q, const float *scale, void *out_b
  *  Requires K a positive multiple of 128, N >= 0. */
 fp_status fused_dequant_i4_bf16(const void *q, const float *scale, void *out_bf16,
                                 int64_t N, int64_t K, void *hip_stream);
+
+/* MXFP4 weight dequantisation to bf16, the same device function the
+ * projections use for MXFP4 weights:
+ * out[j, k] = bf16_rne(e2m1(q[j, k]) * 2^(scale[j, k / 32] - 127)).
+ *  q : [N, K/2] bytes (two E2M1 codes per byte, even k in the low nibble),
+ *  scale : [N, K/32] E8M0 bytes, out_bf16 : [N, K] bf16.
+ *  Requires K a positive multiple of 32, N >= 0; q and out_bf16 16-byte
+ *  aligned. */
+fp_status fused_dequant_mxfp4_bf16(const void *q, const void *scale, void *out_bf16,
+                                   int64_t N, int64_t K, void *hip_stream);
 
 /* Which kernel a call with these sizes would launch, and how: writes a
  * NUL-terminated line such as

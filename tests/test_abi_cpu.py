@@ -217,6 +217,34 @@ def test_int4_plans(plan_override):
     assert fra.workspace_bytes(16, 8192, 57344, torch.bfloat16, u8) < 57344 * 8192
 
 
+def test_mxfp4_plans_and_rejections(plan_override):
+    plan_override()
+    mx = torch.float4_e2m1fn_x2
+    # decode token counts, hidden a multiple of 256: streamed, dequantised in registers
+    p = _plan(16, 8192, 57344, w=mx, fn="swiglu")
+    assert p["kernel"] == "stream_kernel<bf16-mxfp4w,m16,n128,k256,swiglu>" and "prep" not in p
+    assert _plan(64, 8192, 57344, w=mx, fn="swiglu")["kernel"] == "stream_kernel<bf16-mxfp4w,m64,n256,k128,swiglu>"
+    # more than 64 tokens: the 128 x 512 kernel, any hidden that is a multiple of 64
+    p = _plan(256, 8192, 10240, w=mx)
+    assert p["kernel"] == "prefill_kernel<bf16-mxfp4w,128x512,linear>" and p["splits"] == 6
+    assert _plan(300, 320, 512, w=mx)["kernel"] == "prefill_kernel<bf16-mxfp4w,128x512,linear>"
+    # the tiled kernel: staged as bf16 in the workspace
+    p = _plan(8, 320, 512, w=mx)
+    assert p["family"] == "tiled" and p["prep"] == "dequant_mxfp4_kernel"
+    assert fra.workspace_bytes(8, 320, 512, torch.bfloat16, mx) >= 512 * 320 * 2
+    # MXFP4 weights take bf16 activations and need their scales
+    assert qkv(M=4, wdt=6)[0] == "FP_E_NULL"
+    assert qkv(M=4, act=F16, wdt=6, w_scale=FAKE + 0x70000000)[0] == "FP_E_DTYPE"
+    # the E8M0 scales [N, K/32] are an input range: a q over them is an alias
+    st, msg = qkv(M=4, wdt=6, w_scale=FAKE + 0x40000000 + 64, ws=FAKE + 0x7000000, ws_bytes=1 << 30)
+    assert st == "FP_E_ALIAS" and "w_scale" in msg
+    L = lib()
+    assert _lib.STATUS[L.fused_dequant_mxfp4_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 48, None)] == "FP_E_SHAPE"
+    assert _lib.STATUS[L.fused_dequant_mxfp4_bf16(FAKE, None, FAKE + 0x2000000, 4, 64, None)] == "FP_E_NULL"
+    assert _lib.STATUS[L.fused_dequant_mxfp4_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x2000008, 4, 64, None)] == "FP_E_ALIGN"
+    assert _lib.STATUS[L.fused_dequant_mxfp4_bf16(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 0, 64, None)] == "FP_OK"
+
+
 def test_fp8_plans(plan_override):
     plan_override()
     e = torch.float8_e4m3fn

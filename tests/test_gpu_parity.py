@@ -242,13 +242,15 @@ def full_size_check(wl, seed):
             h = torch.full_like(d["x"], float("nan"))
             fra.fused_add_norm_qkv(d["x"], d.get("r"), d["gamma"], d["w_qkv"], wl.n_heads, wl.n_kv_heads,
                                    wl.head_dim, beta=d.get("beta"), norm=wl.norm, eps=wl.eps,
-                                   w_scale=d.get("s_qkv"), bias=d.get("b_qkv"), h_out=h, q=q, k=k, v=v)
+                                   w_scale=d.get("s_qkv"), bias=d.get("b_qkv"), h_out=h, q=q, k=k, v=v,
+                                   out_dtype=odt)
             for name, t in (("q", q), ("k", k), ("v", v), ("h_out", h)):
                 assert bool(torch.isfinite(t).all()), f"{wl.name}: {name} has unwritten or non-finite elements"
             res[("qkv", native)] = tuple(t.index_select(0, rows_d).cpu() for t in (q, k, v, h))
         out = torch.full((wl.M, wl.ffn), float("nan"), dtype=odt, device=DEV)
         fra.fused_gateup_act(d["x"], d.get("r"), d["gamma"], d["w_gu"], wl.ffn, wl.act_fn, beta=d.get("beta"),
-                             norm=wl.norm, eps=wl.eps, w_scale=d.get("s_gu"), bias=d.get("b_gu"), out=out)
+                             norm=wl.norm, eps=wl.eps, w_scale=d.get("s_gu"), bias=d.get("b_gu"), out=out,
+                             out_dtype=odt)
         assert bool(torch.isfinite(out).all()), f"{wl.name}: out has unwritten or non-finite elements"
         res[("gu", native)] = out.index_select(0, rows_d).cpu()
     torch.cuda.synchronize()
