@@ -9,7 +9,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libfusedproj.so")
+# FUSEDPROJ_LIBRARY selects another build of the library (the sanitizer build
+# the CPU tests make); by default the one built in this directory
+LIB_PATH = os.environ.get("FUSEDPROJ_LIBRARY") or os.path.join(PKG, "libfusedproj.so")
 
 FP_F32, FP_F16, FP_BF16, FP_I8, FP_I4, FP_E4M3, FP_MXFP4 = 0, 1, 2, 3, 4, 5, 6
 FP_NORM = {"none": 0, "rms": 1, "layer": 2}

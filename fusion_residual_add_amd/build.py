@@ -51,5 +51,40 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZED = ["fp_api.cpp", "fp_noalloc.hip"]   # the host code of the C ABI
+
+
+def build_host_sanitized(out: str) -> str:
+    """The library with its C-ABI host code (argument validation, planning,
+    workspace layout, the static scratch lookup) compiled with AddressSanitizer
+    and UndefinedBehaviorSanitizer, host side only, linked with the objects of
+    build(); load it into a process whose first library is clang's ASan runtime.
+    Device code is not instrumented."""
+    if not all(os.path.exists(os.path.join(OBJDIR, s + ".o")) for s in SOURCES):
+        build()
+    sdir = os.path.join(OBJDIR, "host_sanitized")
+    os.makedirs(sdir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-g"]
+    objs = []
+    for src in SOURCES:
+        if src in SANITIZED:
+            obj = os.path.join(sdir, src + ".o")
+            res = subprocess.run([HIPCC, *FLAGS, *san, "-c", os.path.join(CSRC, src), "-o", obj],
+                                 capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n" + res.stdout + res.stderr)
+            objs.append(obj)
+        else:
+            objs.append(os.path.join(OBJDIR, src + ".o"))
+    res = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                          "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *objs, "-o", out],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + res.stdout + res.stderr)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

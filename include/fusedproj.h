@@ -106,12 +106,22 @@
 extern "C" {
 #endif
 
-typedef enum { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4, FP_E4M3 = 5, FP_MXFP4 = 6 } fp_dtype;
-typedef enum { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
-typedef enum { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
+/* The enums are ints in C.  In C++ they get int as their underlying type, so
+ * that any int a C caller passes is a value of the type until validation
+ * rejects it (an enum without one only holds the values of its enumerators'
+ * bit range). */
+#ifdef __cplusplus
+#define FP_ENUM(tag) enum tag : int
+#else
+#define FP_ENUM(tag) enum tag
+#endif
+
+typedef FP_ENUM(fp_dtype_e) { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4, FP_E4M3 = 5, FP_MXFP4 = 6 } fp_dtype;
+typedef FP_ENUM(fp_norm_e) { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
+typedef FP_ENUM(fp_act_e) { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
 /* Codes 0-6 keep the numbering of the boundary's first specification;
  * 7 and 8 were added after it (the workspace arguments and enum checks). */
-typedef enum {
+typedef FP_ENUM(fp_status_e) {
     FP_OK = 0,
     FP_E_NULL = 1,      /* a required pointer is NULL */
     FP_E_SHAPE = 2,     /* a size is negative, zero where it must not be, or not a required multiple */

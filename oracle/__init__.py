@@ -50,15 +50,19 @@ class using:
         return False
 
 
-def build(src: Optional[str] = None, out: Optional[str] = None) -> str:
-    """Compile oracle.c (or another copy of it) with gcc into a shared library."""
+def build(src: Optional[str] = None, out: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile oracle.c (or another copy of it) with gcc into a shared library
+    (``sanitize``: with AddressSanitizer and UndefinedBehaviorSanitizer, for a
+    process whose first library is gcc's libasan)."""
     src = src or _SRC
     out = out or _OUT
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"] \
+        if sanitize else []
     # no contraction: the single-precision steps of R11 round after every
     # operation except the one written as fmaf
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-ffp-contract=off",
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-ffp-contract=off", *san,
            "-D_GNU_SOURCE", src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
