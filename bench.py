@@ -382,6 +382,12 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::quant8_kernel<(\d), \d+, \d+>", cxx)
     if m:
         return f"quant8_kernel<{_ACT[m.group(1)]}>"
+    m = re.search(r"fp::norm_kernel<(\d), \d+, \d+>", cxx)
+    if m:
+        return f"norm_kernel<{_ACT[m.group(1)]}>"
+    m = re.search(r"fp::gemm16_kernel<(\d), (\d), (\d)>", cxx)
+    if m:
+        return f"gemm16_kernel<{_ACT[m.group(1)]},256x256,{m.group(3)}st,{_EPI[m.group(2)]}>"
     m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), (\d), (\d)>", cxx)
     if m:
         fm, fn, wgm = int(m.group(3)), int(m.group(4)), int(m.group(5))

@@ -87,6 +87,10 @@ def workspace_bytes(M: int, hidden: int, n_cols: int, act_dtype: torch.dtype,
     return int(_lib.load().fp_workspace_bytes(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype]))
 
 
+def down_workspace_bytes(M: int, ffn: int, hidden: int, act_dtype: torch.dtype, w_dtype: torch.dtype) -> int:
+    return int(_lib.load().fp_down_workspace_bytes(M, ffn, hidden, _DT[act_dtype], _DT[w_dtype]))
+
+
 def describe_plan(M: int, hidden: int, n_cols: int, act_dtype: torch.dtype, w_dtype: torch.dtype,
                   act: str = "none") -> dict:
     """The kernel and launch shape a call with these sizes would use (no device
@@ -255,7 +259,7 @@ def fused_down_residual(a: torch.Tensor, w: torch.Tensor, residual: Optional[tor
     if out is None:
         out = torch.empty((M, Nw), dtype=odt, device=dev)
     stream = _stream(dev)
-    need = int(lib.fp_workspace_bytes(M, F, Nw, _DT[adt], _DT[w.dtype]))
+    need = int(lib.fp_down_workspace_bytes(M, F, Nw, _DT[adt], _DT[w.dtype]))
     ws = workspace if workspace is not None else _workspace(dev, stream, need)
     st = lib.fused_down_residual(
         _ptr(a, "a", dev, adt), _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w)),
@@ -327,14 +331,14 @@ def profile_stop() -> Dict[str, Tuple[int, float]]:
             for i in range(min(n.value, 64))}
 
 
-_FAMILY = {None: -1, "tiled": 0, "stream": 1, "prefill": 2}
+_FAMILY = {None: -1, "tiled": 0, "stream": 1, "prefill": 2, "gemm16": 4}
 
 
 def tune_install(entries) -> None:
     """Install a launch-configuration table (fp_tune_install; replaces the
     previous one).  Each entry is a dict with m_lo, m_hi, hidden, n_cols,
     act_dtype, w_dtype (torch dtypes) and swiglu (bool), and optionally family
-    ("tiled", "stream", "prefill" or None for the planner's), rows, grid and
+    ("tiled", "stream", "prefill", "gemm16" or None for the planner's), rows, grid and
     splits (0 for the planner's).  See fusion_residual_add_amd.tune for the
     micro-benchmark that produces such tables."""
     entries = list(entries)
@@ -356,7 +360,8 @@ def tune_count() -> int:
     return int(_lib.load().fp_tune_count())
 
 
-_OVERRIDE_FIELDS = ("splits", "stream_nr", "stream_target", "no_stream", "no_prefill", "fp8_tile")
+_OVERRIDE_FIELDS = ("splits", "stream_nr", "stream_target", "no_stream", "no_prefill", "fp8_tile", "no_gemm16",
+                    "gemm16_stages")
 
 
 def get_plan_override() -> dict:
@@ -368,7 +373,7 @@ def get_plan_override() -> dict:
 
 def set_plan_override(values: Optional[dict]) -> None:
     """Replace the plan overrides (fp_plan_override_set): a dict with any of
-    splits, stream_nr, stream_target, no_stream, no_prefill, fp8_tile (missing
+    splits, stream_nr, stream_target, no_stream, no_prefill, fp8_tile, no_gemm16, gemm16_stages (missing
     fields 0 = the planner's choice); None restores the values the FUSEDPROJ_*
     environment variables held when the library first planned a call."""
     import ctypes

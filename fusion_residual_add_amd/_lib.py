@@ -20,7 +20,7 @@ STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_
           "FP_E_HIP", "FP_E_WORKSPACE", "FP_E_ARG"]
 
 # every symbol include/fusedproj.h declares
-EXPORTS = ["fp_workspace_bytes", "fused_add_norm_qkv", "fused_add_norm_qkv_hm", "fused_add_norm_qkv_noalloc", "fused_gateup_act", "fused_down_residual",
+EXPORTS = ["fp_workspace_bytes", "fp_down_workspace_bytes", "fused_add_norm_qkv", "fused_add_norm_qkv_hm", "fused_add_norm_qkv_noalloc", "fused_gateup_act", "fused_down_residual",
            "fused_dequant_i8_bf16", "fused_dequant_i4_bf16", "fused_dequant_mxfp4_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
            "fp_profile_start", "fp_profile_stop", "fp_tune_install", "fp_tune_count",
            "fp_plan_override_set", "fp_plan_override_get"]
@@ -42,7 +42,8 @@ class TuneEntry(ctypes.Structure):
 class PlanOverride(ctypes.Structure):
     """fp_plan_override of include/fusedproj.h."""
     _fields_ = [("splits", ctypes.c_int32), ("stream_nr", ctypes.c_int32), ("stream_target", ctypes.c_int32),
-                ("no_stream", ctypes.c_int32), ("no_prefill", ctypes.c_int32), ("fp8_tile", ctypes.c_int32)]
+                ("no_stream", ctypes.c_int32), ("no_prefill", ctypes.c_int32), ("fp8_tile", ctypes.c_int32),
+                ("no_gemm16", ctypes.c_int32), ("gemm16_stages", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,6 +62,8 @@ def load(path: str = None):
     vp, i64, f32, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     lib.fp_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
     lib.fp_workspace_bytes.restype = sz
+    lib.fp_down_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
+    lib.fp_down_workspace_bytes.restype = sz
     lib.fused_add_norm_qkv.argtypes = [vp, vp, vp, vp, vp, ci, f32, vp, vp, vp, vp, vp, vp,
                                        i64, i64, i64, i64, i64, ci, ci, ci, vp, sz, vp]
     lib.fused_add_norm_qkv.restype = ci

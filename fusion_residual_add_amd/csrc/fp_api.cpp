@@ -38,7 +38,9 @@ int act_code(fp_dtype d) {
 // ---------------------------------------------------------------------------
 struct Plan {
     int family = 0;           // 0 tiled (128 x 128), 1 stream (decode), 2 prefill (128 x 512),
-                              // 3 FP8 (per-token E4M3 quantisation, then the 128 x 128 FP8 GEMM)
+                              // 3 FP8 (per-token E4M3 quantisation, then the 128 x 128 FP8 GEMM),
+                              // 4 gemm16 (the row pass writes the normalised rows, then the
+                              //   256 x 256 16-bit GEMM reads them)
     int tile = 0;             // tiled: TileCfg
     fp::StreamCfg sc{1, 2, 8};
     int tiles_m = 0, tiles_n = 0, splits = 1;
@@ -50,6 +52,9 @@ struct Plan {
     size_t deq_off = 0;
     size_t q_off = 0, qs_off = 0;   // FP8: activation codes [M, K] and row scales [M]
     int tile8 = 0;                  // FP8: fp::Gemm8Tile
+    int nst = 4;                    // gemm16: LDS stages
+    bool rows = false;              // gemm16: the row pass forms A (else A is the call's input)
+    size_t rows_off = 0;            // gemm16: normalised rows [M, K]
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -65,14 +70,15 @@ long env_long(const char *name, long dflt) {
 // initially the FUSEDPROJ_* environment variables), which win.  Zero / -1
 // fields leave the planner's choice.
 struct Knobs {
-    int family = -1;          // 0 tiled, 1 stream, 2 prefill; -1 the planner's
+    int family = -1;          // 0 tiled, 1 stream, 2 prefill, 4 gemm16; -1 the planner's
     long rows = 0;            // stream: weight rows per workgroup (64, 128, 256)
     long grid = 0;            // stream: workgroups
     long splits = 0;          // tiled / prefill / FP8: K splits
     long stream_splits = 0;   // stream: workgroups per tile (overrides only)
     long target = 256;        // stream: workgroup budget
     int fp8_tile = 0;         // FP8 GEMM tile by token rows (overrides only)
-    bool no_stream = false, no_prefill = false;
+    int gemm16_stages = 0;    // gemm16: LDS stages (overrides only)
+    bool no_stream = false, no_prefill = false, no_gemm16 = false;
 };
 
 std::mutex g_tune_mu;
@@ -88,6 +94,8 @@ const fp_plan_override &env_overrides() {
         o.no_stream = env_long("FUSEDPROJ_NO_STREAM", 0) != 0;
         o.no_prefill = env_long("FUSEDPROJ_NO_PREFILL", 0) != 0;
         o.fp8_tile = (int32_t)env_long("FUSEDPROJ_FP8_TILE", 0);
+        o.no_gemm16 = env_long("FUSEDPROJ_NO_GEMM16", 0) != 0;
+        o.gemm16_stages = (int32_t)env_long("FUSEDPROJ_GEMM16_STAGES", 0);
         return o;
     }();
     return v;
@@ -127,6 +135,11 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
         kb.no_prefill = true;
         if (kb.family == 2) kb.family = -1;
     }
+    if (o.no_gemm16) {
+        kb.no_gemm16 = true;
+        if (kb.family == 4) kb.family = -1;
+    }
+    kb.gemm16_stages = o.gemm16_stages;
     if (o.stream_nr > 0) kb.rows = 64 * o.stream_nr;
     if (o.splits > 0) {
         kb.splits = o.splits;
@@ -149,7 +162,17 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
 // requested family is used only where it can take the call: the streaming
 // kernel needs 16-bit activations, M <= 64 and K a multiple of 256; the
 // 128 x 512 kernel 16-bit activations and operands under 4 GiB.
-Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu) {
+// The 256 x 256 GEMM (family 4) takes 16-bit weights of the activation
+// dtype from 512 tokens on (fewer leave too much of a 256-row tile as
+// padding), when the call's 256 x 256 tiles fill the CUs at least once (at these
+// sizes the 128 x 512 kernel is bound by the x and residual bytes it re-reads
+// per column tile); the rows it reads are formed once by the row pass, in a
+// workspace region of M * K 16-bit values (form_rows; the down projection
+// reads its input as is).  Where that region would exceed ws_cap (the
+// allocation-free entry point's static scratch) the 128 x 512 kernel takes
+// the call instead.
+Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu, bool form_rows = true,
+               size_t ws_cap = SIZE_MAX) {
     Plan p;
     const Knobs kb = knobs_for(M, K, Nw, act, wdt, swiglu);
     if (wdt == FP_E4M3) {
@@ -209,15 +232,32 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     const fp_dtype wdt_stored = wdt;
     const bool stream_elig = act != FP_F32 && M <= 64 && K % 256 == 0;
     const bool prefill_elig = act != FP_F32 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32);
+    const int64_t tiles256 = ((M + 255) / 256) * (swiglu ? (Nw / 2 + 127) / 128 : (Nw + 255) / 256);
+    const size_t rows_bytes = form_rows ? align256((size_t)M * (size_t)K * 2) : 0;
+    const bool g16_elig = prefill_elig && wdt == act && rows_bytes <= ws_cap;
     int fam;
-    if (kb.family == 0 || (kb.family == 1 && stream_elig) || (kb.family == 2 && prefill_elig))
+    if (kb.family == 0 || (kb.family == 1 && stream_elig) || (kb.family == 2 && prefill_elig) ||
+        (kb.family == 4 && g16_elig))
         fam = kb.family;
     else if (stream_elig && !kb.no_stream)
         fam = 1;
+    else if (g16_elig && M >= 512 && tiles256 >= 256 && !kb.no_gemm16)
+        fam = 4;
     else if (prefill_elig && M > 64 && !kb.no_prefill)
         fam = 2;
     else
         fam = 0;
+    if (fam == 4) {
+        p.family = 4;
+        p.nst = kb.gemm16_stages == 5 ? 5 : 4;
+        p.tiles_m = (int)((M + 255) / 256);
+        p.tiles_n = (int)(swiglu ? (Nw / 2 + 127) / 128 : (Nw + 255) / 256);
+        p.tile_elems = 256 * 256;
+        p.rows = form_rows;
+        p.rows_off = 0;
+        p.total = rows_bytes;
+        return p;
+    }
     // int4 / MXFP4 weights: dequantised in registers by the streaming and 128 x 512
     // kernels; for the tiled family dequantised into the workspace first and
     // then run as bf16 weights
@@ -532,9 +572,52 @@ fp_status run_fp8(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     return FP_OK;
 }
 
+// family 4: the row pass (h_out, the normalised rows) unless the call's
+// input is the operand, then the 256 x 256 GEMM on the rows
+fp_status run_gemm16(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
+    const int act = act_code(c.act);
+    const void *rows = c.x;
+    if (plan.rows) {
+        fp::StatsArgs sa{};
+        sa.x = c.x;
+        sa.res = c.residual;
+        sa.h_out = c.h_out;
+        sa.norm = (int)c.norm;
+        sa.eps = c.eps;
+        sa.M = c.M;
+        sa.K = c.K;
+        sa.gamma = c.gamma;
+        sa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
+        sa.rows = (char *)c.ws + plan.rows_off;
+        ProfScope ps(fp::norm_kernel_name(act), c.stream);
+        hipError_t e = fp::launch_norm(act, sa, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "norm_kernel launch");
+        rows = sa.rows;
+    }
+    pa.x = rows;
+    pa.res = nullptr;
+    pa.stats = nullptr;
+    pa.norm = 0;
+    pa.w = c.w;
+    pa.bias = c.bias;
+    pa.out_f32 = c.odt == FP_F32;
+    pa.M = c.M;
+    pa.K = c.K;
+    pa.Nw = c.Nw;
+    pa.tiles_m = plan.tiles_m;
+    pa.tiles_n = plan.tiles_n;
+    pa.splits = 1;
+    pa.slots = 1;
+    ProfScope ps(fp::gemm16_kernel_name(act, plan.nst, pa.epi), c.stream);
+    hipError_t e = fp::launch_gemm16(act, plan.nst, pa, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm16_kernel launch");
+    return FP_OK;
+}
+
 fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     if (c.M == 0) return FP_OK;
     if (plan.family == 3) return run_fp8(c, plan, pa);
+    if (plan.family == 4) return run_gemm16(c, plan, pa);
     char *ws = (char *)c.ws;
     const int act = act_code(c.act);
     float2 *stats = c.norm != FP_NORM_NONE ? (float2 *)(ws + plan.stats_off) : nullptr;
@@ -636,6 +719,13 @@ size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype ac
     return a > b ? a : b;
 }
 
+size_t fp_down_workspace_bytes(int64_t M, int64_t ffn, int64_t hidden, fp_dtype act_dtype, fp_dtype w_dtype) {
+    if (M <= 0 || ffn <= 0 || ffn % 64 != 0 || hidden <= 0) return 0;
+    if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
+    if ((w_dtype == FP_I4 || w_dtype == FP_E4M3) && ffn % 128 != 0) return 0;
+    return make_plan(M, ffn, hidden, act_dtype, w_dtype, false, false).total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -668,7 +758,8 @@ fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const v
     outs.push_back(rng("q", q, M * nq * eo));
     outs.push_back(rng("k", k, M * nkv * eo));
     outs.push_back(rng("v", v, M * nkv * eo));
-    const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, w_dtype, false);
+    const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, w_dtype, false, true,
+                                source ? (size_t)FP_NOALLOC_SCRATCH_BYTES : SIZE_MAX);
     // the workspace of a call that brings none: from the source, once every
     // argument has been checked (it may touch the device)
     if (source) {
@@ -800,7 +891,7 @@ fp_status fused_down_residual(const void *a, const void *w, const void *w_scale,
     ins[0].name = "a";
     if (residual && !in_place) ins.push_back(rng("residual", residual, M * hidden * ea));
     outs.push_back(rng("out", out, M * hidden * eo));
-    const Plan plan = make_plan(M, ffn, hidden, act_dtype, w_dtype, false);
+    const Plan plan = make_plan(M, ffn, hidden, act_dtype, w_dtype, false, false);
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);
@@ -894,6 +985,12 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     const bool wi8 = w_dtype == FP_I8;
     const int wq = wi8 ? 1 : p.deq ? 0 : w_dtype == FP_I4 ? 2 : w_dtype == FP_MXFP4 ? 3 : 0;
     const int epi = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
+    if (p.family == 4) {
+        snprintf(buf, cap, "family=gemm16 kernel=%s grid=%lld splits=1 slots=1 workspace=%zu prep=%s",
+                 fp::gemm16_kernel_name(a, p.nst, epi), (long long)p.tiles_m * p.tiles_n, M == 0 ? (size_t)0 : p.total,
+                 fp::norm_kernel_name(a));
+        return FP_OK;
+    }
     const char *fam = p.family == 1 ? "stream" : p.family == 2 ? "prefill" : "tiled";
     const char *name = p.family == 1 ? fp::stream_kernel_name(a, wq, p.sc, epi)
                      : p.family == 2 ? fp::prefill_kernel_name(a, wq, epi)
@@ -911,7 +1008,7 @@ fp_status fp_tune_install(const fp_tune_entry *entries, int64_t n) {
     for (int64_t i = 0; i < n; ++i) {
         const fp_tune_entry &e = entries[i];
         const bool ok = e.m_lo >= 0 && e.m_hi >= e.m_lo && e.hidden > 0 && e.n_cols > 0 &&
-                        e.family >= -1 && e.family <= 2 &&
+                        e.family >= -1 && e.family <= 4 && e.family != 3 &&
                         (e.rows == 0 || e.rows == 64 || e.rows == 128 || e.rows == 256) &&
                         e.grid >= 0 && e.grid <= 65535 && e.splits >= 0 && e.splits <= 64 &&
                         (e.swiglu == 0 || e.swiglu == 1) && check_dtypes(e.act_dtype, e.w_dtype, e.act_dtype) == FP_OK;
@@ -933,7 +1030,9 @@ fp_status fp_plan_override_set(const fp_plan_override *o) {
                     (v.stream_nr == 0 || v.stream_nr == 1 || v.stream_nr == 2 || v.stream_nr == 4) &&
                     v.stream_target >= 0 && v.stream_target <= 65535 && (v.no_stream == 0 || v.no_stream == 1) &&
                     (v.no_prefill == 0 || v.no_prefill == 1) &&
-                    (v.fp8_tile == 0 || v.fp8_tile == 32 || v.fp8_tile == 64 || v.fp8_tile == 128 || v.fp8_tile == 256);
+                    (v.fp8_tile == 0 || v.fp8_tile == 32 || v.fp8_tile == 64 || v.fp8_tile == 128 || v.fp8_tile == 256) &&
+                    (v.no_gemm16 == 0 || v.no_gemm16 == 1) &&
+                    (v.gemm16_stages == 0 || v.gemm16_stages == 4 || v.gemm16_stages == 5);
     if (!ok) return fail(FP_E_ARG, "a plan override is out of range");
     std::lock_guard<std::mutex> lk(g_tune_mu);
     g_ov = v;

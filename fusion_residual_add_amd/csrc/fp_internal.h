@@ -73,6 +73,8 @@ struct StatsArgs {
     const void *gamma, *beta;   // [K] act; beta LayerNorm only, may be null
     unsigned char *codes;       // [M, K] E4M3 codes of the normalised rows
     float *qscale;              // [M] dequantisation scale of each row
+    // normalised rows in the activation dtype (norm_kernel only)
+    void *rows;                 // [M, K] act
 };
 
 // Launch a kernel of 256-thread workgroups and return the status of this
@@ -117,6 +119,13 @@ const char *dequant_mxfp4_kernel_name();
 // FP8 GEMM on the codes (x = codes, a_scale, w = E4M3 weights, w_scale [Nw])
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s);
 const char *quant8_kernel_name(int act);
+// 256 x 256 prefill path: the row pass writes the normalised rows (h_out as
+// stats_kernel, the rows into StatsArgs::rows), then the 16-bit GEMM reads
+// them (x = rows, no norm) with the weights straight into LDS
+hipError_t launch_norm(int act, const StatsArgs &a, hipStream_t s);
+const char *norm_kernel_name(int act);
+hipError_t launch_gemm16(int act, int nst, const ProjArgs &a, hipStream_t s);
+const char *gemm16_kernel_name(int act, int nst, int epi);
 // FP8 GEMM tiles (tokens x weight rows)
 enum Gemm8Tile { G8_128x128 = 0, G8_256x256 = 1, G8_32x256 = 2, G8_64x256 = 3 };
 hipError_t launch_gemm8(int act, int tile, const ProjArgs &a, hipStream_t s);

@@ -123,8 +123,12 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
 // NV > 0: each thread keeps its NV vectors of 8 elements of h in registers
 // after the first pass (rows of at most TPR * 8 * NV elements); NV == 0: every
 // pass reads the row again.
-template <int ACT, int TPR, int NV>
-__global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
+// Q8 false (norm_kernel): the same row pass up to n, which is then rounded
+// to the activation dtype (nearest even) and written as the row of the
+// normalised activations -- the operand the 256 x 256 prefill GEMM reads.
+// The values are those the other projection kernels form in registers.
+template <int ACT, int TPR, int NV, bool Q8>
+__device__ __forceinline__ void rows_body(const StatsArgs &a) {
     using T = Act<ACT>;
     using S = typename T::S;
     constexpr int VE = T::VE;
@@ -251,6 +255,15 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
             }
         }
     };
+    if constexpr (!Q8) {
+        S *nr = (S *)a.rows + (active ? m : 0) * a.K;
+        each([&](int j, int64_t k) {
+            float n[VE];
+            get_n(j, k, n);
+            *(u32x4 *)(nr + k) = T::pack(n);
+        });
+        return;
+    }
     float amax = 0.f;
     each([&](int j, int64_t k) {
         float n[VE];
@@ -280,6 +293,12 @@ __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
         *(uint2 *)(cr + k) = make_uint2(w[0], w[1]);
     });
 }
+
+template <int ACT, int TPR, int NV>
+__global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) { rows_body<ACT, TPR, NV, true>(a); }
+
+template <int ACT, int TPR, int NV>
+__global__ __launch_bounds__(256) void norm_kernel(StatsArgs a) { rows_body<ACT, TPR, NV, false>(a); }
 
 // out[j, k] = dequant_i8_bf16(q[j, k], scale[j]) for 16 k per thread.
 __global__ __launch_bounds__(256) void dequant_kernel(const int8_t *q, const float *scale,
@@ -364,41 +383,51 @@ hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s) {
     }
 }
 
-template <int ACT, int TPR, int NV>
-static hipError_t launch_quant8_g(const StatsArgs &a, unsigned grid, hipStream_t s) {
-    return launch_k(quant8_kernel<ACT, TPR, NV>, grid, s, a);
+template <int ACT, int TPR, int NV, bool Q8>
+static hipError_t launch_rows_g(const StatsArgs &a, unsigned grid, hipStream_t s) {
+    if constexpr (Q8) return launch_k(quant8_kernel<ACT, TPR, NV>, grid, s, a);
+    else return launch_k(norm_kernel<ACT, TPR, NV>, grid, s, a);
 }
 
 // few tokens: a whole workgroup per row; many tokens: one wave per row.  The
 // row stays in registers when each thread's share is at most 16 vectors.
-template <int ACT, int TPR>
-static hipError_t launch_quant8_r(const StatsArgs &a, unsigned grid, hipStream_t s) {
+template <int ACT, int TPR, bool Q8>
+static hipError_t launch_rows_r(const StatsArgs &a, unsigned grid, hipStream_t s) {
     const int64_t nv = (a.K + TPR * 8 - 1) / (TPR * 8);
-    if (nv <= 1) return launch_quant8_g<ACT, TPR, 1>(a, grid, s);
-    else if (nv <= 2) return launch_quant8_g<ACT, TPR, 2>(a, grid, s);
-    else if (nv <= 4) return launch_quant8_g<ACT, TPR, 4>(a, grid, s);
-    else if (nv <= 8) return launch_quant8_g<ACT, TPR, 8>(a, grid, s);
-    else if (nv <= 16) return launch_quant8_g<ACT, TPR, 16>(a, grid, s);
-    return launch_quant8_g<ACT, TPR, 0>(a, grid, s);
+    if (nv <= 1) return launch_rows_g<ACT, TPR, 1, Q8>(a, grid, s);
+    else if (nv <= 2) return launch_rows_g<ACT, TPR, 2, Q8>(a, grid, s);
+    else if (nv <= 4) return launch_rows_g<ACT, TPR, 4, Q8>(a, grid, s);
+    else if (nv <= 8) return launch_rows_g<ACT, TPR, 8, Q8>(a, grid, s);
+    else if (nv <= 16) return launch_rows_g<ACT, TPR, 16, Q8>(a, grid, s);
+    return launch_rows_g<ACT, TPR, 0, Q8>(a, grid, s);
 }
 
-template <int ACT>
-static hipError_t launch_quant8_t(const StatsArgs &a, hipStream_t s) {
+template <int ACT, bool Q8>
+static hipError_t launch_rows_t(const StatsArgs &a, hipStream_t s) {
     const int64_t ctr = (a.n_counters + 255) / 256;
     if (a.M <= 1024) {
         const unsigned grid = (unsigned)(a.M > ctr ? a.M : ctr);
-        if (grid) return launch_quant8_r<ACT, 256>(a, grid, s);
+        if (grid) return launch_rows_r<ACT, 256, Q8>(a, grid, s);
     } else {
         const int64_t blocks = (a.M + 3) / 4;
         const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) return launch_quant8_r<ACT, 64>(a, grid, s);
+        if (grid) return launch_rows_r<ACT, 64, Q8>(a, grid, s);
     }
     return hipSuccess;
 }
 
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s) {
-    if (act == ACT_F16) return launch_quant8_t<ACT_F16>(a, s);
-    return launch_quant8_t<ACT_BF16>(a, s);
+    if (act == ACT_F16) return launch_rows_t<ACT_F16, true>(a, s);
+    return launch_rows_t<ACT_BF16, true>(a, s);
+}
+
+hipError_t launch_norm(int act, const StatsArgs &a, hipStream_t s) {
+    if (act == ACT_F16) return launch_rows_t<ACT_F16, false>(a, s);
+    return launch_rows_t<ACT_BF16, false>(a, s);
+}
+
+const char *norm_kernel_name(int act) {
+    return act == ACT_F16 ? "norm_kernel<f16>" : "norm_kernel<bf16>";
 }
 
 const char *quant8_kernel_name(int act) {

@@ -40,7 +40,7 @@ from fusion_residual_add_amd import inputs
 
 MALL_BYTES = 256 << 20            # MI355X last-level (Infinity) cache
 _DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
-           "i4": torch.uint8, "e4m3": torch.float8_e4m3fn}
+           "i4": torch.uint8, "e4m3": torch.float8_e4m3fn, "mxfp4": torch.float4_e2m1fn_x2}
 _NAMES = {v: k for k, v in _DTYPES.items()}
 
 
@@ -65,6 +65,8 @@ def candidates(M: int, hidden: int, n_cols: int, act: torch.dtype, wdt: torch.dt
     if act != torch.float32 and not big:
         for s in (1, 2, 3, 4, 6, 8):
             raw.append(dict(family="prefill", splits=s))
+        if wdt == act:
+            raw.append(dict(family="gemm16"))
     for s in (1, 2, 4, 8):
         raw.append(dict(family="tiled", splits=s))
     seen, out = set(), []

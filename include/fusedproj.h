@@ -35,7 +35,11 @@
  *                             (biased variance; beta may be NULL = 0)
  *               FP_NORM_NONE  n = h (gamma and beta ignored)
  *    Row statistics are fp32.  n is rounded to act_dtype (RNE) and fed to the
- *    matrix cores; it never goes to memory.
+ *    matrix cores.  In most calls it never goes to memory; calls that the
+ *    256 x 256 GEMM takes (weights of the activation dtype and enough tokens
+ *    to fill the GPU with 256 x 256 tiles: prefill; see fp_describe_plan)
+ *    have a row pass write the rounded rows once into the workspace
+ *    (M * hidden * 2 bytes of it), which the GEMM reads: the same values.
  *  - Product: fp32 accumulation of n * W^T.
  *  - Int8 weights (w_dtype FP_I8, act_dtype FP_BF16 only): each element is
  *    dequantised as bf16_rne(f32_rne(q * w_scale[row])), bit-exactly the
@@ -91,8 +95,8 @@
  *  - Errors: every argument is validated before any HIP call; on any status
  *    other than FP_OK nothing has been enqueued and no memory was touched,
  *    except FP_E_HIP (a launch failed; fp_last_error() has the HIP text).
- *  - The workspace holds per-row statistics, split-K partial sums and
- *    arrival counters.  Its contents on entry do not matter.  Two calls that
+ *  - The workspace holds per-row statistics, normalised rows, split-K
+ *    partial sums and arrival counters.  Its contents on entry do not matter.  Two calls that
  *    run concurrently must not share a workspace.
  *  - Results are deterministic: the same inputs give the same bits.
  */
@@ -139,6 +143,12 @@ typedef FP_ENUM(fp_status_e) {
  * otherwise.  Returns 0 for invalid sizes or dtypes. */
 size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols,
                           fp_dtype act_dtype, fp_dtype w_dtype);
+
+/* Bytes of workspace fused_down_residual needs (K = ffn, hidden output
+ * columns).  Returns 0 for invalid sizes or dtypes, and where the call needs
+ * none. */
+size_t fp_down_workspace_bytes(int64_t M, int64_t ffn, int64_t hidden,
+                               fp_dtype act_dtype, fp_dtype w_dtype);
 
 /* Residual add + norm -> QKV projection (+ bias) -> GQA split.
  * ("TensorRT-LLM 深度工程实践…", §2.3 LayerNorm + QKV fusion sketch; §2.2.)
@@ -243,8 +253,10 @@ fp_status fused_gateup_act(
  *             each element is read and written by the same thread).  Any
  *             other overlap is FP_E_ALIAS.
  *  Requires ffn a positive multiple of 64 (128 for int4 and E4M3), hidden a positive
- *  multiple of 16.  Dtypes, alignment, workspace (fp_workspace_bytes(M, ffn,
- *  hidden, act_dtype, w_dtype)) and errors as for the other calls. */
+ *  multiple of 16.  Dtypes, alignment, workspace (fp_down_workspace_bytes(M,
+ *  ffn, hidden, act_dtype, w_dtype); fp_workspace_bytes(M, ffn, hidden,
+ *  act_dtype, w_dtype), which also covers a normalised-row region this call
+ *  never uses, is always enough) and errors as for the other calls. */
 fp_status fused_down_residual(const void *a, const void *w, const void *w_scale, const void *bias,
                               const void *residual, void *out, int64_t M, int64_t ffn, int64_t hidden,
                               fp_dtype act_dtype, fp_dtype w_dtype, fp_dtype out_dtype,
@@ -303,10 +315,11 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
  * gate/up pairing (swiglu = 1 for FP_ACT_SWIGLU) are equal; the first match
  * wins.  Its fields, each 0 (or -1 for family) to keep the planner's choice:
  *  family : 0 the tiled kernel, 1 the weight-streaming kernel, 2 the
- *           128 x 512 kernel; ignored where that family cannot take the call
- *           (streaming: 16-bit activations, M <= 64, hidden a multiple of
- *           256; 128 x 512: 16-bit activations, x / residual and weight
- *           under 4 GiB each);
+ *           128 x 512 kernel, 4 the row pass + 256 x 256 GEMM; ignored
+ *           where that family cannot take the call (streaming: 16-bit
+ *           activations, M <= 64, hidden a multiple of 256; 128 x 512:
+ *           16-bit activations, x / residual and weight under 4 GiB each;
+ *           256 x 256: as 128 x 512, with weights of the activation dtype);
  *  rows   : streaming kernel, weight rows per workgroup: 128, 64 (16-bit
  *           weights, no gate/up pairing, M <= 32) or 256 (int8 weights);
  *           other values are ignored;
@@ -350,10 +363,13 @@ int64_t fp_tune_count(void);
  *  no_stream     : 1 = never the streaming kernel
  *  no_prefill    : 1 = never the 128 x 512 kernel
  *  fp8_tile      : FP8 GEMM tile by token rows: 32, 64, 128 or 256
+ *  no_gemm16     : 1 = never the row pass + 256 x 256 GEMM
+ *  gemm16_stages : 256 x 256 GEMM, LDS stages: 4 or 5
  * The initial values come from the environment variables FUSEDPROJ_SPLITS,
  * FUSEDPROJ_STREAM_NR, FUSEDPROJ_STREAM_TARGET, FUSEDPROJ_NO_STREAM,
- * FUSEDPROJ_NO_PREFILL and FUSEDPROJ_FP8_TILE, read once, at the first call
- * that plans a launch; no call reads the environment after that.
+ * FUSEDPROJ_NO_PREFILL, FUSEDPROJ_FP8_TILE, FUSEDPROJ_NO_GEMM16 and
+ * FUSEDPROJ_GEMM16_STAGES, read once, at the first call that plans a
+ * launch; no call reads the environment after that.
  * fp_plan_override_set replaces the overrides (NULL restores the values read
  * from the environment); FP_E_ARG if a field is out of range.  Process-wide,
  * under the tuning table's lock; like the table, set it between calls.
@@ -365,6 +381,8 @@ typedef struct {
     int32_t no_stream;
     int32_t no_prefill;
     int32_t fp8_tile;
+    int32_t no_gemm16;
+    int32_t gemm16_stages;
 } fp_plan_override;
 
 fp_status fp_plan_override_set(const fp_plan_override *o);

@@ -320,10 +320,18 @@ def test_plan_routing_families(plan_override):
     # K not a multiple of 256 at decode sizes, and every fp32 call: the tiled kernel
     assert _plan(32, 320, 512)["family"] == "tiled"
     assert _plan(4, 256, 512, act=torch.float32, w=torch.float32)["family"] == "tiled"
-    # more than 64 tokens: the 128 x 512 kernel
+    # more than 64 tokens, 16-bit weights, at least 256 tiles of 256 x 256: the
+    # row pass writes the normalised rows, the 256 x 256 GEMM reads them
     p = _plan(16384, 4096, 12288)
+    assert p["family"] == "gemm16" and p["kernel"] == "gemm16_kernel<bf16,256x256,4st,linear>"
+    assert p["grid"] == 64 * 48 and p["splits"] == 1 and p["prep"] == "norm_kernel<bf16>"
+    assert p["workspace"] == 16384 * 4096 * 2
+    p = _plan(16384, 4096, 2 * 11008, fn="swiglu")
+    assert p["kernel"] == "gemm16_kernel<bf16,256x256,4st,swiglu>" and p["grid"] == 64 * 86
+    # fewer tiles: the 128 x 512 kernel (192 tiles of 256 x 256 here)
+    p = _plan(1024, 4096, 12288)
     assert p["family"] == "prefill" and p["kernel"] == "prefill_kernel<bf16,128x512,linear>"
-    assert p["grid"] == 128 * 24 and p["splits"] == 1
+    assert p["grid"] == 8 * 24 and p["splits"] == 1
     # split K so that the workgroups fill one round of CUs: 40 tiles -> 6 splits
     # (240 workgroups); 224 tiles -> unsplit (2 splits would take two rounds)
     p = _plan(256, 8192, 10240, w=torch.int8)
@@ -331,12 +339,15 @@ def test_plan_routing_families(plan_override):
     p = _plan(256, 8192, 57344, w=torch.int8, fn="swiglu")
     assert p["splits"] == 1 and p["grid"] == 224
     assert _plan(2048, 4096, 16384, act=torch.float16, w=torch.float16, fn="gelu_tanh")["kernel"] == \
+        "gemm16_kernel<f16,256x256,4st,gelu>"
+    assert _plan(512, 4096, 16384, act=torch.float16, w=torch.float16, fn="gelu_tanh")["kernel"] == \
         "prefill_kernel<f16,128x512,gelu>"
     # past 4 GiB of activations or of weights the 128 x 512 kernel's 32-bit
     # buffer offsets do not reach: the tiled kernel; decode counts stream any size
     m_big = (1 << 32) // (2 * 4096) + 64
     assert _plan(m_big, 4096, 256)["family"] == "tiled"
-    assert _plan(m_big - 128, 4096, 256)["family"] == "prefill"
+    assert _plan(m_big - 128, 4096, 256)["family"] == "gemm16"
+    assert _plan(m_big - 128, 4096, 256, w=torch.int8)["family"] == "prefill"
     f_big = (1 << 32) // (2 * 2 * 8192) + 32
     assert _plan(96, 8192, 2 * f_big, fn="swiglu")["family"] == "tiled"
     assert _plan(96, 8192, 2 * f_big - 128, fn="swiglu")["family"] == "prefill"
@@ -370,13 +381,19 @@ def test_plan_overrides(plan_override):
     assert _plan(8, 4096, 6144)["kernel"] == "stream_kernel<bf16,m16,n128,k256,linear>"
     plan_override(stream_target=64)
     assert _plan(8, 4096, 28672, fn="swiglu")["grid"] == 64
+    plan_override(no_gemm16=1)
+    assert _plan(16384, 4096, 12288)["family"] == "prefill"
+    plan_override(gemm16_stages=5)
+    assert _plan(16384, 4096, 12288)["kernel"] == "gemm16_kernel<bf16,256x256,5st,linear>"
+    plan_override(no_gemm16=1, no_prefill=1)
+    assert _plan(16384, 4096, 12288)["family"] == "tiled"
     plan_override()
     assert fra.get_plan_override() == dict(splits=0, stream_nr=0, stream_target=0, no_stream=0, no_prefill=0,
-                                           fp8_tile=0)
+                                           fp8_tile=0, no_gemm16=0, gemm16_stages=0)
     # out-of-range values are rejected and leave the overrides as they were
     plan_override(splits=2)
     for bad in (dict(splits=65), dict(splits=-1), dict(stream_nr=3), dict(no_stream=2), dict(fp8_tile=100),
-                dict(stream_target=70000)):
+                dict(stream_target=70000), dict(no_gemm16=2), dict(gemm16_stages=3)):
         with pytest.raises(fra.FusedProjError) as ei:
             fra.set_plan_override(bad)
         assert ei.value.status == 8                     # FP_E_ARG
@@ -526,7 +543,7 @@ def test_tuner_candidates_cover_every_family():
     from fusion_residual_add_amd import tune
     for w in (torch.bfloat16, torch.int8, torch.uint8):
         fams = {c["plan"]["family"] for c in tune.candidates(16, 1024, 1024, torch.bfloat16, w, False)}
-        assert fams == {"stream", "prefill", "tiled"}, (w, fams)
+        assert fams == {"stream", "prefill", "tiled"} | ({"gemm16"} if w == torch.bfloat16 else set()), (w, fams)
         kernels = {c["plan"]["kernel"] for c in tune.candidates(16, 1024, 1024, torch.bfloat16, w, False)}
         if w != torch.bfloat16:
             assert any(",n256," in k for k in kernels), kernels   # 256 rows per workgroup for int8 / int4
