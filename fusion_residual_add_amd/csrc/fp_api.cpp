@@ -77,7 +77,7 @@ struct Knobs {
     long stream_splits = 0;   // stream: workgroups per tile (overrides only)
     long target = 256;        // stream: workgroup budget
     int fp8_tile = 0;         // FP8 GEMM tile by token rows (overrides only)
-    int gemm16_stages = 0;    // gemm16: LDS stages (overrides only)
+    int gemm16_stages = 0;    // gemm16: LDS stages, 2, 4 or 5 (overrides only)
     bool no_stream = false, no_prefill = false, no_gemm16 = false;
 };
 
@@ -249,7 +249,10 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         fam = 0;
     if (fam == 4) {
         p.family = 4;
-        p.nst = kb.gemm16_stages == 5 ? 5 : 4;
+        // two stages of K 64 need an even number of K steps (K a multiple
+        // of 128); otherwise four stages of K 32
+        const bool two = K % 128 == 0;
+        p.nst = kb.gemm16_stages == 5 ? 5 : kb.gemm16_stages == 4 || !two ? 4 : 2;
         p.tiles_m = (int)((M + 255) / 256);
         p.tiles_n = (int)(swiglu ? (Nw / 2 + 127) / 128 : (Nw + 255) / 256);
         p.tile_elems = 256 * 256;
@@ -1032,7 +1035,7 @@ fp_status fp_plan_override_set(const fp_plan_override *o) {
                     (v.no_prefill == 0 || v.no_prefill == 1) &&
                     (v.fp8_tile == 0 || v.fp8_tile == 32 || v.fp8_tile == 64 || v.fp8_tile == 128 || v.fp8_tile == 256) &&
                     (v.no_gemm16 == 0 || v.no_gemm16 == 1) &&
-                    (v.gemm16_stages == 0 || v.gemm16_stages == 4 || v.gemm16_stages == 5);
+                    (v.gemm16_stages == 0 || v.gemm16_stages == 2 || v.gemm16_stages == 4 || v.gemm16_stages == 5);
     if (!ok) return fail(FP_E_ARG, "a plan override is out of range");
     std::lock_guard<std::mutex> lk(g_tune_mu);
     g_ov = v;

@@ -364,7 +364,8 @@ int64_t fp_tune_count(void);
  *  no_prefill    : 1 = never the 128 x 512 kernel
  *  fp8_tile      : FP8 GEMM tile by token rows: 32, 64, 128 or 256
  *  no_gemm16     : 1 = never the row pass + 256 x 256 GEMM
- *  gemm16_stages : 256 x 256 GEMM, LDS stages: 4 or 5
+ *  gemm16_stages : 256 x 256 GEMM, LDS stages: 2 (K 64 per stage; taken
+ *                  where hidden is a multiple of 128), 4 or 5 (K 32)
  * The initial values come from the environment variables FUSEDPROJ_SPLITS,
  * FUSEDPROJ_STREAM_NR, FUSEDPROJ_STREAM_TARGET, FUSEDPROJ_NO_STREAM,
  * FUSEDPROJ_NO_PREFILL, FUSEDPROJ_FP8_TILE, FUSEDPROJ_NO_GEMM16 and

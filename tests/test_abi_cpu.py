@@ -323,11 +323,13 @@ def test_plan_routing_families(plan_override):
     # more than 64 tokens, 16-bit weights, at least 256 tiles of 256 x 256: the
     # row pass writes the normalised rows, the 256 x 256 GEMM reads them
     p = _plan(16384, 4096, 12288)
-    assert p["family"] == "gemm16" and p["kernel"] == "gemm16_kernel<bf16,256x256,4st,linear>"
+    assert p["family"] == "gemm16" and p["kernel"] == "gemm16_kernel<bf16,256x256,2st,linear>"
     assert p["grid"] == 64 * 48 and p["splits"] == 1 and p["prep"] == "norm_kernel<bf16>"
     assert p["workspace"] == 16384 * 4096 * 2
     p = _plan(16384, 4096, 2 * 11008, fn="swiglu")
-    assert p["kernel"] == "gemm16_kernel<bf16,256x256,4st,swiglu>" and p["grid"] == 64 * 86
+    assert p["kernel"] == "gemm16_kernel<bf16,256x256,2st,swiglu>" and p["grid"] == 64 * 86
+    # hidden not a multiple of 128: four stages of K 32
+    assert _plan(16384, 4160, 12288)["kernel"] == "gemm16_kernel<bf16,256x256,4st,linear>"
     # fewer tiles: the 128 x 512 kernel (192 tiles of 256 x 256 here)
     p = _plan(1024, 4096, 12288)
     assert p["family"] == "prefill" and p["kernel"] == "prefill_kernel<bf16,128x512,linear>"
@@ -339,7 +341,7 @@ def test_plan_routing_families(plan_override):
     p = _plan(256, 8192, 57344, w=torch.int8, fn="swiglu")
     assert p["splits"] == 1 and p["grid"] == 224
     assert _plan(2048, 4096, 16384, act=torch.float16, w=torch.float16, fn="gelu_tanh")["kernel"] == \
-        "gemm16_kernel<f16,256x256,4st,gelu>"
+        "gemm16_kernel<f16,256x256,2st,gelu>"
     assert _plan(512, 4096, 16384, act=torch.float16, w=torch.float16, fn="gelu_tanh")["kernel"] == \
         "prefill_kernel<f16,128x512,gelu>"
     # past 4 GiB of activations or of weights the 128 x 512 kernel's 32-bit
@@ -385,6 +387,11 @@ def test_plan_overrides(plan_override):
     assert _plan(16384, 4096, 12288)["family"] == "prefill"
     plan_override(gemm16_stages=5)
     assert _plan(16384, 4096, 12288)["kernel"] == "gemm16_kernel<bf16,256x256,5st,linear>"
+    plan_override(gemm16_stages=4)
+    assert _plan(16384, 4096, 12288)["kernel"] == "gemm16_kernel<bf16,256x256,4st,linear>"
+    plan_override(gemm16_stages=2)
+    assert _plan(16384, 4096, 12288)["kernel"] == "gemm16_kernel<bf16,256x256,2st,linear>"
+    assert _plan(16384, 4160, 12288)["kernel"] == "gemm16_kernel<bf16,256x256,4st,linear>"
     plan_override(no_gemm16=1, no_prefill=1)
     assert _plan(16384, 4096, 12288)["family"] == "tiled"
     plan_override()
