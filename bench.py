@@ -376,7 +376,7 @@ def library_kernel_name(cxx: str) -> str:
         wq = {"true": "1", "false": "0"}.get(m.group(2), m.group(2))
         act = {"1": "bf16-i8w", "2": "bf16-i4w", "3": "bf16-mxfp4w"}.get(wq) or _ACT[m.group(1)]
         return f"prefill_kernel<{act},128x512,{_EPI[m.group(3)]}>"
-    m = re.search(r"fp::stats_kernel<(\d), \d+>", cxx)
+    m = re.search(r"fp::stats_kernel<(\d), \d+(?:, \d+)?>", cxx)
     if m:
         return f"stats_kernel<{_ACT[m.group(1)]}>"
     m = re.search(r"fp::quant8_kernel<(\d), \d+, \d+>", cxx)

@@ -18,9 +18,15 @@
 
 namespace fp {
 
+// Output of the row pass (rows_fast): the statistics only (stats_kernel),
+// the normalised rows in the activation dtype (norm_kernel), or their E4M3
+// codes and row scales (quant8_kernel).
+enum RowOut { OUT_STATS = 0, OUT_ROWS = 1, OUT_CODES = 2 };
+
 // TPR threads per token row (a multiple of 64); 256 / TPR rows per workgroup.
+// The form for rows longer than the registers hold (NV == 0 below).
 template <int ACT, int TPR>
-__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+__device__ __forceinline__ void stats_body(const StatsArgs &a) {
     using T = Act<ACT>;
     using S = typename T::S;
     constexpr int VE = T::VE;
@@ -302,8 +308,9 @@ __device__ __forceinline__ void rows_body(const StatsArgs &a) {
 // stores are dropped) and all loads of a phase are in flight together.  The
 // uniform choices (residual present, norm type, h_out wanted) are taken
 // outside the per-vector loops.
-template <int ACT, int TPR, int NV, bool Q8>
+template <int ACT, int TPR, int NV, int OUT>
 __device__ __forceinline__ void rows_fast(const StatsArgs &a) {
+    constexpr bool Q8 = OUT == OUT_CODES;
     using T = Act<ACT>;
     using S = typename T::S;
     constexpr int VE = T::VE;
@@ -326,7 +333,7 @@ __device__ __forceinline__ void rows_fast(const StatsArgs &a) {
     const __amdgpu_buffer_rsrc_t rx = rsrc((const S *)a.x + mr * a.K, rowb);
     const bool has_res = a.res != nullptr;
     const __amdgpu_buffer_rsrc_t rr = rsrc(has_res ? (const S *)a.res + mr * a.K : a.x, has_res ? rowb : 0u);
-    const bool has_g = a.norm != 0, has_b = a.norm == 2 && a.beta != nullptr;
+    const bool has_g = OUT != OUT_STATS && a.norm != 0, has_b = OUT != OUT_STATS && a.norm == 2 && a.beta != nullptr;
     const __amdgpu_buffer_rsrc_t rg = rsrc(has_g ? a.gamma : a.x, has_g ? (uint32_t)(a.K * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rb = rsrc(has_b ? a.beta : a.x, has_b ? (uint32_t)(a.K * 2) : 0u);
     auto ld = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> u32x4 {
@@ -425,6 +432,10 @@ __device__ __forceinline__ void rows_fast(const StatsArgs &a) {
     }
     // n in place of h: fp32, in the order of the projection kernels
     const float mu32 = (float)mean, rs32 = (float)rstd;
+    if constexpr (OUT == OUT_STATS) {
+        if (active && t == 0 && a.stats && a.norm != 0) a.stats[m] = make_float2(mu32, rs32);
+        return;
+    }
     if (a.norm == 2) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -484,14 +495,21 @@ __device__ __forceinline__ void rows_fast(const StatsArgs &a) {
 
 template <int ACT, int TPR, int NV>
 __global__ __launch_bounds__(256) void quant8_kernel(StatsArgs a) {
-    if constexpr (NV > 0) rows_fast<ACT, TPR, NV, true>(a);
+    if constexpr (NV > 0) rows_fast<ACT, TPR, NV, OUT_CODES>(a);
     else rows_body<ACT, TPR, NV, true>(a);
 }
 
 template <int ACT, int TPR, int NV>
 __global__ __launch_bounds__(256) void norm_kernel(StatsArgs a) {
-    if constexpr (NV > 0) rows_fast<ACT, TPR, NV, false>(a);
+    if constexpr (NV > 0) rows_fast<ACT, TPR, NV, OUT_ROWS>(a);
     else rows_body<ACT, TPR, NV, false>(a);
+}
+
+// fp32 activations and rows longer than the registers hold: stats_body
+template <int ACT, int TPR, int NV>
+__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+    if constexpr (NV > 0 && ACT != ACT_F32) rows_fast<ACT, TPR, NV, OUT_STATS>(a);
+    else stats_body<ACT, TPR>(a);
 }
 
 // out[j, k] = dequant_i8_bf16(q[j, k], scale[j]) for 16 k per thread.
@@ -551,73 +569,74 @@ const char *dequant_i4_kernel_name() { return "dequant_i4_kernel"; }
 
 const char *dequant_mxfp4_kernel_name() { return "dequant_mxfp4_kernel"; }
 
-template <int ACT>
-static hipError_t launch_stats_t(const StatsArgs &a, hipStream_t s) {
-    // few tokens: a whole workgroup per row keeps every load of the row in
-    // flight at once; many tokens: one wave per row
+// fp32 activations: the looping form, a workgroup per row up to 1024 tokens,
+// one wave per row beyond
+static hipError_t launch_stats_f32(const StatsArgs &a, hipStream_t s) {
+    const int64_t ctr = (a.n_counters + 255) / 256;
     if (a.M <= 1024) {
-        const int64_t blocks = a.M > 0 ? a.M : 0;
-        const int64_t ctr = (a.n_counters + 255) / 256;
-        const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) return launch_k(stats_kernel<ACT, 256>, grid, s, a);
+        const unsigned grid = (unsigned)(a.M > ctr ? a.M : ctr);
+        if (grid) return launch_k(stats_kernel<ACT_F32, 256, 0>, grid, s, a);
     } else {
         const int64_t blocks = (a.M + 3) / 4;
-        const int64_t ctr = (a.n_counters + 255) / 256;
         const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) return launch_k(stats_kernel<ACT, 64>, grid, s, a);
+        if (grid) return launch_k(stats_kernel<ACT_F32, 64, 0>, grid, s, a);
     }
     return hipSuccess;
 }
 
+template <int ACT, int OUT>
+static hipError_t launch_rows_t(const StatsArgs &a, hipStream_t s);
+
 hipError_t launch_stats(int act, const StatsArgs &a, hipStream_t s) {
     switch (act) {
-    case ACT_F32: return launch_stats_t<ACT_F32>(a, s);
-    case ACT_F16: return launch_stats_t<ACT_F16>(a, s);
-    default:      return launch_stats_t<ACT_BF16>(a, s);
+    case ACT_F32: return launch_stats_f32(a, s);
+    case ACT_F16: return launch_rows_t<ACT_F16, OUT_STATS>(a, s);
+    default:      return launch_rows_t<ACT_BF16, OUT_STATS>(a, s);
     }
 }
 
-template <int ACT, int TPR, int NV, bool Q8>
+template <int ACT, int TPR, int NV, int OUT>
 static hipError_t launch_rows_g(const StatsArgs &a, unsigned grid, hipStream_t s) {
-    if constexpr (Q8) return launch_k(quant8_kernel<ACT, TPR, NV>, grid, s, a);
-    else return launch_k(norm_kernel<ACT, TPR, NV>, grid, s, a);
+    if constexpr (OUT == OUT_CODES) return launch_k(quant8_kernel<ACT, TPR, NV>, grid, s, a);
+    else if constexpr (OUT == OUT_ROWS) return launch_k(norm_kernel<ACT, TPR, NV>, grid, s, a);
+    else return launch_k(stats_kernel<ACT, TPR, NV>, grid, s, a);
 }
 
 // few tokens: a whole workgroup per row; many tokens: one wave per row.  The
 // row stays in registers when each thread's share is at most 16 vectors.
-template <int ACT, int TPR, bool Q8>
+template <int ACT, int TPR, int OUT>
 static hipError_t launch_rows_r(const StatsArgs &a, unsigned grid, hipStream_t s) {
     const int64_t nv = (a.K + TPR * 8 - 1) / (TPR * 8);
-    if (nv <= 1) return launch_rows_g<ACT, TPR, 1, Q8>(a, grid, s);
-    else if (nv <= 2) return launch_rows_g<ACT, TPR, 2, Q8>(a, grid, s);
-    else if (nv <= 4) return launch_rows_g<ACT, TPR, 4, Q8>(a, grid, s);
-    else if (nv <= 8) return launch_rows_g<ACT, TPR, 8, Q8>(a, grid, s);
-    else if (nv <= 16) return launch_rows_g<ACT, TPR, 16, Q8>(a, grid, s);
-    return launch_rows_g<ACT, TPR, 0, Q8>(a, grid, s);
+    if (nv <= 1) return launch_rows_g<ACT, TPR, 1, OUT>(a, grid, s);
+    else if (nv <= 2) return launch_rows_g<ACT, TPR, 2, OUT>(a, grid, s);
+    else if (nv <= 4) return launch_rows_g<ACT, TPR, 4, OUT>(a, grid, s);
+    else if (nv <= 8) return launch_rows_g<ACT, TPR, 8, OUT>(a, grid, s);
+    else if (nv <= 16) return launch_rows_g<ACT, TPR, 16, OUT>(a, grid, s);
+    return launch_rows_g<ACT, TPR, 0, OUT>(a, grid, s);
 }
 
-template <int ACT, bool Q8>
+template <int ACT, int OUT>
 static hipError_t launch_rows_t(const StatsArgs &a, hipStream_t s) {
     const int64_t ctr = (a.n_counters + 255) / 256;
     if (a.M <= 1024) {
         const unsigned grid = (unsigned)(a.M > ctr ? a.M : ctr);
-        if (grid) return launch_rows_r<ACT, 256, Q8>(a, grid, s);
+        if (grid) return launch_rows_r<ACT, 256, OUT>(a, grid, s);
     } else {
         const int64_t blocks = (a.M + 3) / 4;
         const unsigned grid = (unsigned)(blocks > ctr ? blocks : ctr);
-        if (grid) return launch_rows_r<ACT, 64, Q8>(a, grid, s);
+        if (grid) return launch_rows_r<ACT, 64, OUT>(a, grid, s);
     }
     return hipSuccess;
 }
 
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s) {
-    if (act == ACT_F16) return launch_rows_t<ACT_F16, true>(a, s);
-    return launch_rows_t<ACT_BF16, true>(a, s);
+    if (act == ACT_F16) return launch_rows_t<ACT_F16, OUT_CODES>(a, s);
+    return launch_rows_t<ACT_BF16, OUT_CODES>(a, s);
 }
 
 hipError_t launch_norm(int act, const StatsArgs &a, hipStream_t s) {
-    if (act == ACT_F16) return launch_rows_t<ACT_F16, false>(a, s);
-    return launch_rows_t<ACT_BF16, false>(a, s);
+    if (act == ACT_F16) return launch_rows_t<ACT_F16, OUT_ROWS>(a, s);
+    return launch_rows_t<ACT_BF16, OUT_ROWS>(a, s);
 }
 
 const char *norm_kernel_name(int act) {

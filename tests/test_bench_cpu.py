@@ -45,6 +45,9 @@ def test_algo_bytes_down():
     ("void fp::prefill_kernel<1, 0, 2, true>(fp::ProjArgs)", "prefill_kernel<f16,128x512,gelu>"),
     ("void fp::prefill_kernel<2, 1, 1, false>(fp::ProjArgs)", "prefill_kernel<bf16-i8w,128x512,swiglu>"),
     ("void fp::stats_kernel<2, 256>(fp::StatsArgs)", "stats_kernel<bf16>"),
+    ("void fp::stats_kernel<1, 64, 8>(fp::StatsArgs)", "stats_kernel<f16>"),
+    ("void fp::norm_kernel<2, 64, 8>(fp::StatsArgs)", "norm_kernel<bf16>"),
+    ("void fp::gemm16_kernel<2, 1, 2>(fp::ProjArgs)", "gemm16_kernel<bf16,256x256,2st,swiglu>"),
     ("void fp::quant8_kernel<1, 64, 8>(fp::StatsArgs)", "quant8_kernel<f16>"),
     ("void fp::gemm8_kernel<2, 1, 4, 4, 2>(fp::ProjArgs)", "gemm8_kernel<bf16,256x256,swiglu>"),
     ("void fp::gemm8_kernel<2, 0, 1, 2, 1>(fp::ProjArgs)", "gemm8_kernel<bf16,32x256,qkv>"),
