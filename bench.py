@@ -419,6 +419,30 @@ def traffic_probe(wl_name: str) -> None:
     print(json.dumps({"traffic_probe": wl_name, "calibration_bytes": 2 * n}), flush=True)
 
 
+def blas_probe(wl_name: str) -> None:
+    """hipBLASLt's plain GEMMs of the workload's projection shapes (torch's
+    F.linear on an already normalised 16-bit input), six calls of each, to run
+    under rocprofv3 --pmc beside --traffic-probe: the counters of the library
+    GEMM the fused kernels are compared with."""
+    import torch
+    import torch.nn.functional as F
+    from fusion_residual_add_amd import inputs
+    wl = inputs.workload(wl_name)
+    if wl.wdt != wl.act:
+        raise SystemExit("--blas-probe: 16-bit weights of the activation dtype only")
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[wl.act]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(wl.M, wl.hidden, device="cuda", dtype=torch.float32, generator=g).to(dt)
+    shapes = ([wl.n_qkv] if wl.n_qkv else []) + [wl.n_gu]
+    for n in shapes:
+        w = (torch.randn(n, wl.hidden, device="cuda", dtype=torch.float32, generator=g) * wl.w_std).to(dt)
+        for _ in range(6):
+            F.linear(a, w)
+        torch.cuda.synchronize()
+        del w
+    print(json.dumps({"blas_probe": wl_name, "shapes": [[wl.M, n, wl.hidden] for n in shapes]}), flush=True)
+
+
 def _counter_rows(d: str):
     import csv
     import glob
@@ -515,10 +539,14 @@ def counters_summarize(tag: str, dirs, cmd: str) -> None:
             with open(fpath) as fh:
                 for row in csv.DictReader(fh):
                     n = row["Kernel_Name"]
-                    if "fp::" not in n:
+                    if "fp::" in n:
+                        key = n
+                    elif "Cijk" in n:   # hipBLASLt: one name for several shapes, told apart by the grid
+                        key = f"{n[:100]} (grid {int(row['Grid_Size']) // 256} workgroups)"
+                    else:
                         continue
-                    per.setdefault(n, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
-                    dur.setdefault(n, []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+                    per.setdefault(key, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                    dur.setdefault(key, []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
     md = [f"# Hardware counters, {tag}", "", "Commands (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):",
           "", "```", cmd, "```", "",
           "Medians over the dispatches of each kernel.  GRBM_GUI_ACTIVE is summed over the 8 XCDs: the shader clock",
@@ -773,6 +801,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra timed runs of --steps steps each, for the median / p10 / p90 spread")
+    ap.add_argument("--blas-probe", action="store_true",
+                    help="hipBLASLt GEMMs of the workload's shapes, to run under rocprofv3 --pmc")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="calibration pass + projection calls, to run under rocprofv3 --pmc")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -827,6 +857,9 @@ def main():
         fra.tune_install(tune.load(args.tune_file))
     if args.traffic_probe:
         traffic_probe(args.workload)
+        return
+    if args.blas_probe:
+        blas_probe(args.workload)
         return
     if args.all_configs:
         all_configs(min(args.steps, 20))
