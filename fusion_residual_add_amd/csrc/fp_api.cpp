@@ -52,6 +52,7 @@ struct Plan {
     size_t deq_off = 0;
     size_t q_off = 0, qs_off = 0;   // FP8: activation codes [M, K] and row scales [M]
     int tile8 = 0;                  // FP8: fp::Gemm8Tile
+    bool stream8 = false;           // FP8: the weight-streaming kernel on the codes (sc, grid) instead
     int nst = 4;                    // gemm16: LDS stages
     bool rows = false;              // gemm16: the row pass forms A (else A is the call's input)
     size_t rows_off = 0;            // gemm16: normalised rows [M, K]
@@ -150,6 +151,83 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
     return kb;
 }
 
+// The weight-streaming kernel's shape for one call (family 1, and the FP8
+// call at decode token counts): token fragments, weight rows per
+// workgroup, K chunk, the stream-K grid and the partial-sum slots.  qw:
+// one-byte or 4-bit weights, dequantised or decoded in registers.
+// K must be a multiple of the chunk (stream_chunk).  (Chunks twice as wide
+// for E4M3, which the smaller activation registers would allow, measured
+// slower on MI355X: Llama-3-8B decode QKV 20.2 -> 24.6 us, gate/up 32.5 ->
+// 33.8 us: a longer pipeline ramp for the few chunks per workgroup.)
+int stream_chunk(int64_t M) { return M > 32 ? 128 : 256; }
+
+void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool qw, bool swiglu, const Knobs &kb) {
+    p.sc.mf = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    // weight rows per workgroup 64 * nr: int8 weights at 33..64 tokens take
+    // 256 when that still leaves >= 128 tiles (the A tile every workgroup
+    // normalises is then amortised over twice the weight rows; measured on
+    // MI355X: Llama-2-70B gate/up at 64 tokens 232 -> 186 us, while fewer
+    // rows per workgroup stay faster at 1 and 16 tokens and for QKV)
+    // 16-bit weights without the gate/up pairing at up to 32 tokens: 64
+    // rows, so that more workgroups share the (smaller) weight (measured on
+    // MI355X: Llama-3-8B QKV 1.1 us faster per call; with int8 weights, or
+    // at 33..64 tokens where the A tile is four times as large, 64-row
+    // tiles are slower)
+    p.sc.nr = qw && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
+    if (!swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
+    // requested rows: only the instantiated forms (64 for 16-bit weights
+    // without the gate/up pairing at up to 32 tokens, 256 for quantised weights)
+    if (kb.rows == 64 && !swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
+    if (kb.rows == 128 || (kb.rows == 256 && qw)) p.sc.nr = (int)(kb.rows / 64);
+    p.sc.u = stream_chunk(M) / 32;   // K chunk 32 * u: must match the launcher
+    const int nb = 64 * p.sc.nr;
+    p.tiles_m = 1;
+    p.tiles_n = (int)((Nw + nb - 1) / nb);
+    p.tile_elems = (int64_t)16 * p.sc.mf * nb;
+    const int64_t tiles = p.tiles_n, ksteps = K / (32 * p.sc.u), target = kb.target;
+    // stream-K: `grid` workgroups take equal contiguous unit ranges of at
+    // least 512 of K each (2 chunks of 256, 4 of 128; measured on MI355X:
+    // shorter ranges pay the pipeline ramp too often, and 2 chunks of 256
+    // beat 4 on the small QKV of Llama-2-70B's 8-way shard, 16.8 -> 14.9 us)
+    const int64_t units = tiles * ksteps;
+    const int64_t minc = 512 / (32 * p.sc.u);
+    int64_t G = units / minc < target ? units / minc : target;
+    // s workgroups per tile, each an equal 1/s of K, when that still
+    // occupies most CUs and the call is short: a range that straddles two
+    // tiles costs a few us (partial sums out and back, and the wait for
+    // them), which outweighs the idle CUs only while the streaming itself
+    // is short (measured on MI355X: Llama-3-8B gate/up, 224 tiles of 235
+    // MB, s = 1: 51.3 -> 49.3 us with the weights in the last-level cache,
+    // 0.3 % of the decode step with them streamed from HBM; the gate/up of
+    // Llama-2-70B's 8-way shard, 56 tiles, s = 4: 24.6 -> 23.4 us;
+    // Llama-2-70B int8 gate/up, 224 tiles of 470 MB, 6 % slower so; an
+    // uneven 1/s of K, 32 chunks in 3, 1 us slower)
+    const int64_t wbytes = (wdt == FP_I4 || wdt == FP_MXFP4) ? Nw * K / 2
+                           : Nw * K * ((wdt == FP_I8 || wdt == FP_E4M3) ? 1 : 2);
+    if (wbytes <= (int64_t(256) << 20) && tiles > 0) {
+        for (int64_t s = target / tiles < ksteps / minc ? target / tiles : ksteps / minc; s >= 1; --s) {
+            if (tiles * s * 100 < target * 85) break;
+            if (ksteps % s == 0) {
+                G = tiles * s;
+                break;
+            }
+        }
+    }
+    if (kb.grid > 0) G = kb.grid;
+    if (kb.stream_splits > 0) G = tiles * kb.stream_splits;
+    if (G > units) G = units;
+    if (G < 1) G = 1;
+    p.grid = (int)G;
+    // the most workgroups that share one tile
+    auto owner = [&](int64_t v) { return ((v + 1) * G - 1) / units; };
+    int64_t most = 1;
+    for (int64_t t = 0; t < tiles; ++t) {
+        const int64_t n = owner(t * ksteps + ksteps - 1) - owner(t * ksteps) + 1;
+        if (n > most) most = n;
+    }
+    p.slots = (int)most;
+}
+
 // Decode token counts (M <= 64, 16-bit activations) use the weight-streaming
 // kernel, which spreads (tile, K chunk) units evenly over one workgroup per
 // CU; token counts above 64 the 128 x 512 prefill kernel while its 32-bit
@@ -191,6 +269,29 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // workgroups run (same limits).  The fp8_tile override (32, 64,
         // 128 or 256) forces a tile.
         p.family = 3;
+        // Requested (family 1), up to 64 tokens with K a multiple of the
+        // chunk and no tile requested: the weight-streaming kernel on the
+        // codes, E4M3 weights decoded in registers, shaped like a call with
+        // int8 weights (the same bytes per weight).  Not the default on
+        // row-major weights: measured on MI355X, Llama-3-8B decode, the FP8
+        // tiles below are faster (step 53.3 against 56.0 us; QKV 15.5
+        // against 18.3 us, gate/up 31.0 against 29.8 us)
+        if (M <= 64 && K % stream_chunk(M) == 0 && kb.fp8_tile == 0 && !kb.no_stream && kb.family == 1) {
+            p.stream8 = true;
+            plan_stream(p, M, K, Nw, wdt, true, swiglu, kb);
+            const int64_t tiles = p.tiles_n;
+            size_t off = 0;
+            p.ctr_off = off;
+            if (p.slots > 1) off = align256(off + (size_t)tiles * 4);
+            p.part_off = off;
+            if (p.slots > 1) off = align256(off + (size_t)tiles * p.slots * p.tile_elems * 4);
+            p.q_off = off;
+            off = align256(off + (size_t)M * (size_t)K);
+            p.qs_off = off;
+            off = align256(off + (size_t)M * 4);
+            p.total = off;
+            return p;
+        }
         const int64_t big_tiles = ((M + 255) / 256) * (swiglu ? (Nw / 2 + 127) / 128 : (Nw + 255) / 256);
         const long tile_env = kb.fp8_tile;
         if (tile_env == 32) p.tile8 = fp::G8_32x256;
@@ -269,71 +370,8 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     int64_t tiles, ksteps, target;
     if (fam == 1) {
         p.family = 1;
-        p.sc.mf = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-        // weight rows per workgroup 64 * nr: int8 weights at 33..64 tokens take
-        // 256 when that still leaves >= 128 tiles (the A tile every workgroup
-        // normalises is then amortised over twice the weight rows; measured on
-        // MI355X: Llama-2-70B gate/up at 64 tokens 232 -> 186 us, while fewer
-        // rows per workgroup stay faster at 1 and 16 tokens and for QKV)
-        // 16-bit weights without the gate/up pairing at up to 32 tokens: 64
-        // rows, so that more workgroups share the (smaller) weight (measured on
-        // MI355X: Llama-3-8B QKV 1.1 us faster per call; with int8 weights, or
-        // at 33..64 tokens where the A tile is four times as large, 64-row
-        // tiles are slower)
-        p.sc.nr = qw && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
-        if (!swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
-        // requested rows: only the instantiated forms (64 for 16-bit weights
-        // without the gate/up pairing at up to 32 tokens, 256 for int8 / int4)
-        if (kb.rows == 64 && !swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
-        if (kb.rows == 128 || (kb.rows == 256 && qw)) p.sc.nr = (int)(kb.rows / 64);
-        p.sc.u = p.sc.mf >= 4 ? 4 : 8;      // K chunk 32 * u: must match the launcher
-        const int nb = 64 * p.sc.nr;
-        p.tiles_m = 1;
-        p.tiles_n = (int)((Nw + nb - 1) / nb);
-        p.tile_elems = (int64_t)16 * p.sc.mf * nb;
+        plan_stream(p, M, K, Nw, wdt, qw, swiglu, kb);
         tiles = p.tiles_n;
-        ksteps = K / (32 * p.sc.u);
-        target = kb.target;
-        // stream-K: `grid` workgroups take equal contiguous unit ranges of at
-        // least 512 of K each (2 chunks of 256, 4 of 128; measured on MI355X:
-        // shorter ranges pay the pipeline ramp too often, and 2 chunks of 256
-        // beat 4 on the small QKV of Llama-2-70B's 8-way shard, 16.8 -> 14.9 us)
-        const int64_t units = tiles * ksteps;
-        const int64_t minc = 512 / (32 * p.sc.u);
-        int64_t G = units / minc < target ? units / minc : target;
-        // s workgroups per tile, each an equal 1/s of K, when that still
-        // occupies most CUs and the call is short: a range that straddles two
-        // tiles costs a few us (partial sums out and back, and the wait for
-        // them), which outweighs the idle CUs only while the streaming itself
-        // is short (measured on MI355X: Llama-3-8B gate/up, 224 tiles of 235
-        // MB, s = 1: 51.3 -> 49.3 us with the weights in the last-level cache,
-        // 0.3 % of the decode step with them streamed from HBM; the gate/up of
-        // Llama-2-70B's 8-way shard, 56 tiles, s = 4: 24.6 -> 23.4 us;
-        // Llama-2-70B int8 gate/up, 224 tiles of 470 MB, 6 % slower so; an
-        // uneven 1/s of K, 32 chunks in 3, 1 us slower)
-        const int64_t wbytes = (wdt == FP_I4 || wdt == FP_MXFP4) ? Nw * K / 2 : Nw * K * (wdt == FP_I8 ? 1 : 2);
-        if (wbytes <= (int64_t(256) << 20) && tiles > 0) {
-            for (int64_t s = target / tiles < ksteps / minc ? target / tiles : ksteps / minc; s >= 1; --s) {
-                if (tiles * s * 100 < target * 85) break;
-                if (ksteps % s == 0) {
-                    G = tiles * s;
-                    break;
-                }
-            }
-        }
-        if (kb.grid > 0) G = kb.grid;
-        if (kb.stream_splits > 0) G = tiles * kb.stream_splits;
-        if (G > units) G = units;
-        if (G < 1) G = 1;
-        p.grid = (int)G;
-        // the most workgroups that share one tile
-        auto owner = [&](int64_t v) { return ((v + 1) * G - 1) / units; };
-        int64_t most = 1;
-        for (int64_t t = 0; t < tiles; ++t) {
-            const int64_t n = owner(t * ksteps + ksteps - 1) - owner(t * ksteps) + 1;
-            if (n > most) most = n;
-        }
-        p.slots = (int)most;
     } else if (fam == 2) {
         p.family = 2;
         p.tiles_m = (int)((M + 127) / 128);
@@ -569,6 +607,15 @@ fp_status run_fp8(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.slots = plan.slots;
     pa.partials = plan.slots > 1 ? (float *)(ws + plan.part_off) : nullptr;
     pa.counters = ctr;
+    if (plan.stream8) {
+        pa.res = nullptr;
+        pa.stats = nullptr;
+        pa.norm = 0;
+        ProfScope ps(fp::stream_kernel_name(act, 4, plan.sc, pa.epi), c.stream);
+        hipError_t e = fp::launch_stream(act, 4, plan.sc, pa, plan.grid, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
+        return FP_OK;
+    }
     ProfScope ps(fp::gemm8_kernel_name(act, plan.tile8, pa.epi), c.stream);
     hipError_t e = fp::launch_gemm8(act, plan.tile8, pa, c.stream);
     if (e != hipSuccess) return hip_fail(e, "gemm8_kernel launch");
@@ -979,9 +1026,14 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     if (p.family == 3) {
         const int a8 = act_code(act_dtype);
         const int e8 = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
-        snprintf(buf, cap, "family=fp8 kernel=%s grid=%lld splits=%d slots=%d workspace=%zu prep=%s",
-                 fp::gemm8_kernel_name(a8, p.tile8, e8), (long long)p.tiles_m * p.tiles_n * p.splits, p.splits, p.slots,
-                 M == 0 ? (size_t)0 : p.total, fp::quant8_kernel_name(a8));
+        if (p.stream8)
+            snprintf(buf, cap, "family=fp8 kernel=%s grid=%d splits=1 slots=%d workspace=%zu prep=%s",
+                     fp::stream_kernel_name(a8, 4, p.sc, e8), p.grid, p.slots, M == 0 ? (size_t)0 : p.total,
+                     fp::quant8_kernel_name(a8));
+        else
+            snprintf(buf, cap, "family=fp8 kernel=%s grid=%lld splits=%d slots=%d workspace=%zu prep=%s",
+                     fp::gemm8_kernel_name(a8, p.tile8, e8), (long long)p.tiles_m * p.tiles_n * p.splits, p.splits,
+                     p.slots, M == 0 ? (size_t)0 : p.total, fp::quant8_kernel_name(a8));
         return FP_OK;
     }
     const int a = act_code(act_dtype);

@@ -114,6 +114,19 @@ __device__ __forceinline__ void dequant32_i4(u32x4 qv, float s, u32x4 (&out)[4])
 __device__ __forceinline__ float e8m0_to_f32(unsigned s) {
     return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
+// E4M3 codes to bf16, exactly (every E4M3 value, subnormals included, is a
+// bf16 value): two codes per conversion, the first code of each pair in the
+// lower half (the hardware's scaled FP8 conversion with scale 1)
+template <bool HIGH>
+__device__ __forceinline__ unsigned e4m3x2_to_bf16x2(unsigned word) {
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HIGH));
+}
+// 8 codes (two words) -> 8 bf16
+__device__ __forceinline__ u32x4 decode8_e4m3(unsigned w0, unsigned w1) {
+    return (u32x4){e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
+                   e4m3x2_to_bf16x2<true>(w1)};
+}
+
 __device__ __forceinline__ u32x4 dequant8_mxfp4(unsigned word, float scale) {
     u32x4 out;
     out[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0));

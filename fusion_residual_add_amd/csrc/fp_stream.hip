@@ -12,8 +12,9 @@ hipError_t launch_stream_f16(const StreamCfg &c, const ProjArgs &a, unsigned gri
 hipError_t launch_stream_i8(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 hipError_t launch_stream_i4(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 hipError_t launch_stream_mx(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
+hipError_t launch_stream_f8(int act, const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s);
 
-// wq: 0 weights in the activation dtype, 1 int8, 2 int4, 3 MXFP4
+// wq: 0 weights in the activation dtype, 1 int8, 2 int4, 3 MXFP4, 4 E4M3 (with E4M3 activation codes)
 hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s) {
     if (grid_wgs <= 0 || a.tiles_n <= 0) return hipSuccess;
     if (a.epi == EPI_SWIGLU && c.nr % 2 != 0) return hipErrorInvalidValue;
@@ -23,6 +24,7 @@ hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a,
     if (wq == 1) return launch_stream_i8(c, a, grid, s);
     if (wq == 2) return launch_stream_i4(c, a, grid, s);
     if (wq == 3) return launch_stream_mx(c, a, grid, s);
+    if (wq == 4) return launch_stream_f8(act, c, a, grid, s);
     if (act == ACT_F16) return launch_stream_f16(c, a, grid, s);
     return launch_stream_bf16(c, a, grid, s);
 }
@@ -57,7 +59,8 @@ const char *stream_kernel_name(int act, int wq, const StreamCfg &c, int epi) {
     static const char *acts[6] = {"f32", "f16", "bf16", "bf16-i8w", "bf16-i4w", "bf16-mxfp4w"};
     static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
     thread_local char buf[64];
-    snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", acts[wq ? 2 + wq : act], 16 * c.mf,
+    const char *an = wq == 4 ? (act == ACT_F16 ? "f16-e4m3" : "bf16-e4m3") : acts[wq ? 2 + wq : act];
+    snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", an, 16 * c.mf,
              64 * c.nr, 32 * c.u, epis[epi]);
     return buf;
 }

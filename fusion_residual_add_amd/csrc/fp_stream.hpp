@@ -35,14 +35,21 @@ namespace fp {
 
 // WQ: weight storage -- 0 the activation dtype, 1 int8 (one scale per row),
 // 2 int4 (one scale per row and group of 128 k, two values per byte),
-// 3 MXFP4 (E2M1 codes two per byte, one E8M0 scale per row and 32 k).
+// 3 MXFP4 (E2M1 codes two per byte, one E8M0 scale per row and 32 k),
+// 4 E4M3 with one scale per row, for the FP8 W8A8 call: the A side is then
+//   the per-token E4M3 codes of the quantisation pass (x = codes [M, K],
+//   a_scale [M]) instead of x + residual and the norm, both operands are
+//   decoded exactly to bf16 in registers (the products are those of the FP8
+//   matrix cores), and the epilogue scales by a_scale[m] * w_scale[c].
 template <int ACT, int WQ, int MF, int NR, int U, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(ProjArgs p) {
-    using T = Act<ACT>;
-    constexpr bool WI8 = WQ == 1, WMX = WQ == 3, WI4 = WQ == 2 || WMX;   // WI4: 4-bit weights of either kind
+    constexpr bool WF8 = WQ == 4;
+    using T = Act<ACT>;                          // activation dtype: bias, outputs
+    using TM = Act<WF8 ? ACT_BF16 : ACT>;        // MFMA operands (decoded E4M3 are bf16)
+    constexpr bool WI8 = WQ == 1 || WF8, WMX = WQ == 3, WI4 = WQ == 2 || WMX;   // WI8: one byte per weight; WI4: 4-bit weights of either kind
     static_assert(ACT != ACT_F32, "the stream kernel takes 16-bit activations");
-    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 / MXFP4 weights feed bf16 MFMA");
+    static_assert(WQ == 0 || WF8 || ACT == ACT_BF16, "int8 / int4 / MXFP4 weights feed bf16 MFMA");
     static_assert(EPI != EPI_SWIGLU || NR % 2 == 0, "gate/up fragments come in pairs");
     static_assert(!WI8 || U % 2 == 0, "one int8 load covers two k slices");
     static_assert(!WI4 || U % 4 == 0, "one int4 load covers four k slices (one scale group)");
@@ -92,7 +99,7 @@ void stream_kernel(ProjArgs p) {
             wsc[n] = 0.f;
             wsr[n] = nullptr;
             wsm[n] = nullptr;
-            if constexpr (WI8) wsc[n] = p.w_scale[r];
+            if constexpr (WI8) wsc[n] = p.w_scale[r];   // int8: applied when dequantising; E4M3: in the epilogue
             if constexpr (WQ == 2) wsr[n] = p.w_scale + r * (p.K / 128);
             if constexpr (WMX) wsm[n] = (const unsigned char *)p.w_scale + r * (p.K / 32);
         }
@@ -142,6 +149,15 @@ void stream_kernel(ProjArgs p) {
         };
         auto aload = [&](int c, ARegs &A) {
             const int64_t k = (int64_t)c * CK + a_kv * 8;
+            if constexpr (WF8) {   // 8 codes per vector
+                const unsigned char *cp = (const unsigned char *)p.x;
+    #pragma unroll
+                for (int i = 0; i < AV; ++i) {
+                    const uint2 v = *(const uint2 *)(cp + a_off[i] + k);
+                    A.x[i] = (u32x4){v.x, v.y, 0u, 0u};
+                }
+                return;
+            }
     #pragma unroll
             for (int i = 0; i < AV; ++i) {
                 A.x[i] = *(const u32x4 *)(xp + a_off[i] + k);
@@ -151,6 +167,16 @@ void stream_kernel(ProjArgs p) {
             A.b = *(const u32x4 *)(bp + k);
         };
         auto astore = [&](int buf, const ARegs &A) {
+            if constexpr (WF8) {
+    #pragma unroll
+                for (int i = 0; i < AV; ++i) {
+                    if constexpr (AV * AR > BMP) {
+                        if (a_r0 + i * AR >= BMP) continue;
+                    }
+                    *(u32x4 *)&lds_a[buf][(a_r0 + i * AR) * LDA + a_kv * 8] = decode8_e4m3(A.x[i][0], A.x[i][1]);
+                }
+                return;
+            }
             float g[8], be[8];
             T::unpack(A.g, g);
             T::unpack(A.b, be);
@@ -238,13 +264,20 @@ void stream_kernel(ProjArgs p) {
                         for (int m = 0; m < MF; ++m) {
                             const u32x4 a = *(const u32x4 *)&la[(m * 16 + (lane & 15)) * LDA + koff];
     #pragma unroll
-                            for (int n = 0; n < NR; ++n) acc[m][n] = T::mfma(a, b[n][qq], acc[m][n]);
+                            for (int n = 0; n < NR; ++n) acc[m][n] = TM::mfma(a, b[n][qq], acc[m][n]);
                         }
                     }
                 } else if constexpr (WI8) {
                     u32x4 lo[NR], hi[NR];
     #pragma unroll
-                    for (int n = 0; n < NR; ++n) dequant16(W.w[n][u], wsc[n], lo[n], hi[n]);
+                    for (int n = 0; n < NR; ++n) {
+                        if constexpr (WF8) {
+                            lo[n] = decode8_e4m3(W.w[n][u][0], W.w[n][u][1]);
+                            hi[n] = decode8_e4m3(W.w[n][u][2], W.w[n][u][3]);
+                        } else {
+                            dequant16(W.w[n][u], wsc[n], lo[n], hi[n]);
+                        }
+                    }
                     // a lane's 16 int8 are k = 64u + 16 (lane / 16) + [0, 16): two MFMA k slices
     #pragma unroll
                     for (int half = 0; half < 2; ++half) {
@@ -253,7 +286,7 @@ void stream_kernel(ProjArgs p) {
                         for (int m = 0; m < MF; ++m) {
                             const u32x4 a = *(const u32x4 *)&la[(m * 16 + (lane & 15)) * LDA + koff];
     #pragma unroll
-                            for (int n = 0; n < NR; ++n) acc[m][n] = T::mfma(a, half ? hi[n] : lo[n], acc[m][n]);
+                            for (int n = 0; n < NR; ++n) acc[m][n] = TM::mfma(a, half ? hi[n] : lo[n], acc[m][n]);
                         }
                     }
                 } else {
@@ -262,7 +295,7 @@ void stream_kernel(ProjArgs p) {
                     for (int m = 0; m < MF; ++m) {
                         const u32x4 a = *(const u32x4 *)&la[(m * 16 + (lane & 15)) * LDA + koff];
     #pragma unroll
-                        for (int n = 0; n < NR; ++n) acc[m][n] = T::mfma(a, W.w[n][u], acc[m][n]);
+                        for (int n = 0; n < NR; ++n) acc[m][n] = TM::mfma(a, W.w[n][u], acc[m][n]);
                     }
                 }
             }
@@ -307,11 +340,13 @@ void stream_kernel(ProjArgs p) {
             // chunk c0 (needed first), then the weights of c0, the activations and
             // weights of c0 + 1; the fences keep the scheduler from moving a weight
             // burst in front of the loads that the first normalisation waits for
+            if constexpr (!WF8) {
     #pragma unroll
-            for (int i = 0; i < AV; ++i) {
-                const float2 st = stp[a_row[i]];
-                a_mu[i] = st.x * st_on;
-                a_rs[i] = st_on != 0.f ? st.y : 1.f;
+                for (int i = 0; i < AV; ++i) {
+                    const float2 st = stp[a_row[i]];
+                    a_mu[i] = st.x * st_on;
+                    a_rs[i] = st_on != 0.f ? st.y : 1.f;
+                }
             }
             aload(c0, A0);
             __builtin_amdgcn_sched_barrier(0);
@@ -370,18 +405,21 @@ void stream_kernel(ProjArgs p) {
             for (int e = 0; e < 4; ++e) {
                 const int64_t row = m * 16 + (lane >> 4) * 4 + e;
                 if (row >= p.M) continue;
+                // E4M3: the products' sum times the token's and the weight row's scales
+                const float as = WF8 ? p.a_scale[row] : 1.f;
+                auto scaled = [&](int n) { return WF8 ? acc[m][n][e] * as * wsc[n] : acc[m][n][e]; };
                 if constexpr (EPI == EPI_SWIGLU) {
     #pragma unroll
                     for (int n = 0; n < NR; n += 2) {
                         const int64_t j = (int64_t)tn * (NB / 2) + wave * (NR * 8) + (n / 2) * 16 + (lane & 15);
-                        if (j < p.F) store_swiglu<ACT>(p, row, j, acc[m][n][e], acc[m][n + 1][e]);
+                        if (j < p.F) store_swiglu<ACT>(p, row, j, scaled(n), scaled(n + 1));
                     }
                 } else {
     #pragma unroll
                     for (int n = 0; n < NR; ++n) {
                         const int64_t c = (int64_t)tn * NB + wave * (NR * 16) + n * 16 + (lane & 15);
                         if (c >= p.Nw) continue;
-                        float y = acc[m][n][e];
+                        float y = scaled(n);
                         if (p.bias) y += T::ld(p.bias, c);
                         store_col<ACT, EPI>(p, row, c, y);
                     }

@@ -53,7 +53,7 @@ def candidates(M: int, hidden: int, n_cols: int, act: torch.dtype, wdt: torch.dt
     stream_ok = act != torch.float32 and M <= 64 and hidden % 256 == 0
     big = M * hidden * 2 >= (1 << 32) or n_cols * hidden * 2 >= (1 << 32)
     if stream_ok:
-        quant = wdt in (torch.int8, torch.uint8)      # int8 / int4 weights
+        quant = wdt in (torch.int8, torch.uint8, torch.float8_e4m3fn)      # int8 / int4 / E4M3 weights
         rows = [128]
         if not swiglu and not quant and M <= 32:
             rows.append(64)

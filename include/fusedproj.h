@@ -82,7 +82,11 @@
  *    zero codes); the product is then sum_k e4m3(a) e4m3(w) in fp32, times
  *    a_scale[m] * w_scale[c].  The codes and scales live in the workspace
  *    (M * hidden + 4 M bytes of it).  hidden must be a multiple of 128, and
- *    M * hidden and N * hidden must be below 2^32.
+ *    M * hidden and N * hidden must be below 2^32.  Up to 64 tokens with
+ *    hidden a multiple of 256 the product runs in the weight-streaming
+ *    kernel (both operands decoded exactly to bf16 in registers), otherwise
+ *    in the FP8 GEMM tiles; the results are the same up to the order of the
+ *    fp32 sums.
  *  - Dtypes: act_dtype in {F32, F16, BF16}; w_dtype == act_dtype, or FP_I8 /
  *    FP_I4 / FP_MXFP4 with act_dtype FP_BF16, or FP_E4M3 with act_dtype
  *    FP_BF16 / FP_F16; out_dtype == act_dtype or FP_F32.  gamma, beta and
@@ -319,12 +323,15 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
  *           where that family cannot take the call (streaming: 16-bit
  *           activations, M <= 64, hidden a multiple of 256; 128 x 512:
  *           16-bit activations, x / residual and weight under 4 GiB each;
- *           256 x 256: as 128 x 512, with weights of the activation dtype);
+ *           256 x 256: as 128 x 512, with weights of the activation dtype).
+ *           E4M3 weights: 1 (or -1 where the planner would) the
+ *           weight-streaming kernel on the codes, any other value the FP8
+ *           GEMM tiles;
  *  rows   : streaming kernel, weight rows per workgroup: 128, 64 (16-bit
- *           weights, no gate/up pairing, M <= 32) or 256 (int8 weights);
- *           other values are ignored;
+ *           weights, no gate/up pairing, M <= 32) or 256 (int8, int4, MXFP4
+ *           and E4M3 weights); other values are ignored;
  *  grid   : streaming kernel, workgroups (at most one per unit of work);
- *  splits : tiled and 128 x 512 kernels, ways K is split.
+ *  splits : tiled, 128 x 512 and FP8 GEMM kernels, ways K is split.
  * Results stay within the parity bounds for any entry (only the order of the
  * fp32 partial sums changes) and are deterministic for a given table.
  * fp_workspace_bytes and fp_describe_plan read the same table, so install
@@ -360,9 +367,11 @@ int64_t fp_tune_count(void);
  *  stream_nr     : streaming kernel, weight rows per workgroup / 64 (1, 2, 4;
  *                  only the instantiated forms are taken, as for the table)
  *  stream_target : streaming kernel, workgroup budget (1..65535; 0 = 256)
- *  no_stream     : 1 = never the streaming kernel
+ *  no_stream     : 1 = never the streaming kernel (E4M3 weights: the FP8
+ *                  GEMM tiles at every token count)
  *  no_prefill    : 1 = never the 128 x 512 kernel
- *  fp8_tile      : FP8 GEMM tile by token rows: 32, 64, 128 or 256
+ *  fp8_tile      : FP8 GEMM tile by token rows: 32, 64, 128 or 256 (set:
+ *                  the FP8 GEMM tiles, never the streaming kernel)
  *  no_gemm16     : 1 = never the row pass + 256 x 256 GEMM
  *  gemm16_stages : 256 x 256 GEMM, LDS stages: 2 (K 64 per stage; taken
  *                  where hidden is a multiple of 128), 4 or 5 (K 32)

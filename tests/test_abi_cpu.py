@@ -248,7 +248,7 @@ def test_mxfp4_plans_and_rejections(plan_override):
 def test_fp8_plans(plan_override):
     plan_override()
     e = torch.float8_e4m3fn
-    # one family at every token count: per-token quantisation, then the FP8 GEMM
+    # one family at every token count: per-token quantisation, then a GEMM on the codes
     p = _plan(32, 4096, 28672, w=e, fn="swiglu")
     assert p["family"] == "fp8" and p["prep"] == "quant8_kernel<bf16>"
     assert p["kernel"] == "gemm8_kernel<bf16,32x256,swiglu>"
@@ -256,6 +256,35 @@ def test_fp8_plans(plan_override):
     assert _plan(64, 4096, 28672, w=e, fn="swiglu")["kernel"] == "gemm8_kernel<bf16,64x256,swiglu>"
     p = _plan(1, 4096, 6144, w=e)
     assert p["splits"] == 4 and p["grid"] == 24 * 4            # each split streams 256 KB of weights
+    assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 112 * 2 * 32 * 256 * 4
+    # the weight-streaming kernel on the codes when requested (up to 64
+    # tokens, hidden a multiple of the chunk), with the weight rows per
+    # workgroup and grid of int8 weights (one byte per weight as well)
+    try:
+        for M, N, sw in ((1, 6144, False), (32, 28672, True), (64, 6144, False), (64, 57344, True), (40, 768, False)):
+            fn = "swiglu" if sw else "none"
+            fra.tune_install([dict(m_lo=0, m_hi=64, hidden=K, n_cols=N, act_dtype=torch.bfloat16, w_dtype=e,
+                                   swiglu=sw, family="stream") for K in (768, 4096)])
+            a, b = _plan(M, 4096 if N != 768 else 768, N, w=e, fn=fn), _plan(M, 4096, N, w=torch.int8, fn=fn)
+            assert a["family"] == "fp8" and a["kernel"].startswith("stream_kernel<bf16-e4m3,"), a
+            if N != 768:
+                assert a["kernel"].split(",", 1)[1] == b["kernel"].split(",", 1)[1] and a["grid"] == b["grid"], (a, b)
+        fra.tune_install([dict(m_lo=0, m_hi=64, hidden=4096, n_cols=6144, act_dtype=torch.float16, w_dtype=e,
+                               swiglu=False, family="stream")])
+        assert _plan(16, 4096, 6144, act=torch.float16, w=e)["kernel"] == "stream_kernel<f16-e4m3,m16,n128,k256,linear>"
+        fra.tune_install([dict(m_lo=0, m_hi=64, hidden=K, n_cols=6144, act_dtype=torch.bfloat16, w_dtype=e,
+                               swiglu=False, family="stream") for K in (640, 4096)])
+        # the codes, row scales and the partial sums of tiles shared by workgroups
+        p = _plan(1, 4096, 6144, w=e)
+        assert p["slots"] > 1 and p["workspace"] >= 4096 + 4 + 48 * p["slots"] * 16 * 128 * 4
+        # hidden not a multiple of 256, or a tile requested: the FP8 GEMM tiles
+        assert _plan(8, 640, 6144, w=e)["kernel"] == "gemm8_kernel<bf16,32x256,linear>"
+        with fra.plan_override(fp8_tile=64):
+            assert _plan(1, 4096, 6144, w=e)["kernel"] == "gemm8_kernel<bf16,64x256,linear>"
+        with fra.plan_override(no_stream=1):
+            assert _plan(1, 4096, 6144, w=e)["kernel"] == "gemm8_kernel<bf16,32x256,linear>"
+    finally:
+        fra.tune_clear()
     p = _plan(200, 4096, 6144, w=e)
     assert p["kernel"] == "gemm8_kernel<bf16,128x128,linear>" and p["splits"] == 5 and p["grid"] == 2 * 48 * 5
     # enough 256 x 256 tiles for a round of CUs: the large tiles, unsplit
@@ -266,7 +295,6 @@ def test_fp8_plans(plan_override):
     assert p["kernel"] == "gemm8_kernel<f16,128x128,gelu>"
     # the workspace holds the codes and row scales (and the partials when split)
     assert fra.workspace_bytes(16384, 4096, 22016, torch.bfloat16, e) >= 16384 * 4096 + 16384 * 4
-    assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 112 * 2 * 32 * 256 * 4
     assert fra.workspace_bytes(8, 320, 512, torch.bfloat16, e) == 0      # hidden % 128
     with fra.plan_override(splits=3, fp8_tile=128):
         p = _plan(1, 4096, 6144, w=e)
@@ -542,7 +570,12 @@ def test_tuner_candidates_fp8_splits():
     from fusion_residual_add_amd import tune
     c = tune.candidates(32, 4096, 28672, torch.bfloat16, torch.float8_e4m3fn, True)
     assert {x["plan"]["family"] for x in c} == {"fp8"}
-    assert sorted(x["plan"]["splits"] for x in c) == [1, 2, 3, 4, 6, 8]
+    g8 = [x["plan"] for x in c if x["plan"]["kernel"].startswith("gemm8_kernel")]
+    st = [x["plan"] for x in c if x["plan"]["kernel"].startswith("stream_kernel<bf16-e4m3")]
+    assert len(g8) + len(st) == len(c)
+    assert sorted(p["splits"] for p in g8) == [1, 2, 3, 4, 6, 8]
+    # the streaming kernel at 128 and 256 rows per workgroup and several grids
+    assert {p["kernel"].split(",")[2] for p in st} == {"n128", "n256"} and len({p["grid"] for p in st}) > 3
     assert fra.tune_count() == 0
 
 
