@@ -89,9 +89,12 @@ def flops(wl, call: str) -> int:
 
 
 class Runner:
-    """Device copies of a workload with R rotating weight sets."""
+    """Device copies of a workload with R rotating weight sets.  layout
+    "packed": the fused calls read tile-packed copies of the weights (made
+    once here, as at model load; a weight whose shape the layout does not
+    take stays row-major), the torch reference the row-major ones."""
 
-    def __init__(self, wl, seed=0, min_sets=1, down=False):
+    def __init__(self, wl, seed=0, min_sets=1, down=False, layout="rows"):
         import torch
         from fusion_residual_add_amd import inputs
         self.wl = wl
@@ -111,6 +114,22 @@ class Runner:
             self.sets.append(s)
         import fusion_residual_add_amd as fra
         self.fra = fra
+        self.layout = layout
+        self.fsets = self.sets          # the weights the fused calls read
+        self.packed = []
+        if layout == "packed":
+            self.fsets = []
+            for st in self.sets:
+                f = dict(st)
+                for k in [k for k in st if k.startswith("w_")]:
+                    try:
+                        f[k] = fra.pack_weight(st[k], gate_up=(k == "w_gu" and wl.act_fn == "swiglu"))
+                        if k not in self.packed:
+                            self.packed.append(k)
+                    except fra.FusedProjError:
+                        pass
+                self.fsets.append(f)
+            torch.cuda.synchronize()
         M = wl.M
         self.q = torch.empty((M, wl.n_heads or 1, wl.head_dim or 1), dtype=self.base["x"].dtype, device=dev)
         self.k = torch.empty((M, wl.n_kv_heads or 1, wl.head_dim or 1), dtype=self.base["x"].dtype, device=dev)
@@ -122,30 +141,33 @@ class Runner:
         self.ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
         need = 0
         act_t = self.base["x"].dtype
+        lay = lambda k: (("packed_gate_up" if k == "w_gu" and wl.act_fn == "swiglu" else "packed")
+                         if k in self.packed else "rows")
         for call, N in (("qkv", wl.n_qkv), ("gu", wl.n_gu)):
             if N:
-                w = self.base["w_qkv" if call == "qkv" else "w_gu"]
-                need = max(need, fra.workspace_bytes(M, wl.hidden, N, act_t, w.dtype))
+                k = "w_qkv" if call == "qkv" else "w_gu"
+                need = max(need, fra.workspace_bytes(M, wl.hidden, N, act_t, self.base[k].dtype, lay(k)))
         if down:
-            need = max(need, fra.workspace_bytes(M, wl.ffn, wl.hidden, act_t, self.base["w_down"].dtype))
+            need = max(need, fra.workspace_bytes(M, wl.ffn, wl.hidden, act_t, self.base["w_down"].dtype,
+                                                 lay("w_down")))
         if need > self.ws.numel():
             self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def qkv(self, i):
-        s, wl = self.sets[i % self.R], self.wl
+        s, wl = self.fsets[i % self.R], self.wl
         self.fra.fused_add_norm_qkv(s["x"], s["r"], s["gamma"], s["w_qkv"], wl.n_heads, wl.n_kv_heads,
                                     wl.head_dim, beta=s.get("beta"), norm=wl.norm, eps=wl.eps,
                                     w_scale=s.get("s_qkv"), bias=s.get("b_qkv"), h_out=self.h,
                                     q=self.q, k=self.k, v=self.v, workspace=self.ws)
 
     def gu(self, i):
-        s, wl = self.sets[i % self.R], self.wl
+        s, wl = self.fsets[i % self.R], self.wl
         self.fra.fused_gateup_act(s["x"], s["r"], s["gamma"], s["w_gu"], wl.ffn, wl.act_fn,
                                   beta=s.get("beta"), norm=wl.norm, eps=wl.eps, w_scale=s.get("s_gu"),
                                   bias=s.get("b_gu"), out=self.out, workspace=self.ws)
 
     def down(self, i):
-        s = self.sets[i % self.R]
+        s = self.fsets[i % self.R]
         self.fra.fused_down_residual(s["a_down"], s["w_down"], self.h_down, w_scale=s.get("s_down"),
                                      out=self.h_down)
 
@@ -397,7 +419,7 @@ def library_kernel_name(cxx: str) -> str:
     return cxx
 
 
-def traffic_probe(wl_name: str) -> None:
+def traffic_probe(wl_name: str, layout: str = "rows") -> None:
     """Workload run under `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE): an
     elementwise pass over 1 GiB (reads 1 GiB, writes 1 GiB: the calibration of
     the counters) and six calls of each projection of the workload."""
@@ -412,7 +434,7 @@ def traffic_probe(wl_name: str) -> None:
     del src, dst
     torch.cuda.empty_cache()
     wl = inputs.workload(wl_name)
-    run = Runner(wl)
+    run = Runner(wl, layout=layout)
     for i in range(6):
         if wl.n_qkv:
             run.qkv(i)
@@ -608,7 +630,7 @@ def trace_summarize(tag: str, trace_dir: str, cmd: str) -> None:
     print("\n".join(md))
 
 
-def all_configs(steps: int) -> None:
+def all_configs(steps: int, layout: str = "rows") -> None:
     """One JSON line per workload: per-call kernel times and the roofline
     fraction of each call (HBM GB/s when the call is bandwidth-bound, MFMA
     TFLOP/s otherwise)."""
@@ -616,7 +638,7 @@ def all_configs(steps: int) -> None:
     from fusion_residual_add_amd import inputs
     for name in inputs.WORKLOADS:
         wl = inputs.workload(name)
-        run = Runner(wl, down=True)
+        run = Runner(wl, down=True, layout=layout)
         ms = time_steps(run.step, steps, 3)
         calls = {}
         for call in (["qkv"] if wl.n_qkv else []) + ["gu", "down"]:
@@ -633,7 +655,7 @@ def all_configs(steps: int) -> None:
                            "rate": round(rate, 1), "unit": "GB/s" if mem_bound else "TFLOP/s",
                            "frac": round(rate / peak, 4)}
         print(json.dumps({"workload": name, "M": wl.M, "hidden": wl.hidden, "act": wl.act, "weights": wl.wdt,
-                          "ms_per_step": round(ms, 5), "calls": calls}), flush=True)
+                          "weights_packed": run.packed, "ms_per_step": round(ms, 5), "calls": calls}), flush=True)
         del run
         torch.cuda.empty_cache()
 
@@ -658,7 +680,7 @@ def all_configs_summarize(path: str, cmd: str) -> None:
     print("\n".join(md))
 
 
-def fusion_gain(steps: int, repeats: int) -> None:
+def fusion_gain(steps: int, repeats: int, layout: str = "rows") -> None:
     """Fused calls against the same step as torch ops on the same GPU, per
     16-bit workload (the pages' fusion-gain comparison), with hipBLASLt's
     plain GEMMs of the same shapes (torch.nn.functional.linear on an
@@ -683,7 +705,7 @@ def fusion_gain(steps: int, repeats: int) -> None:
     torch.cuda.empty_cache()
     for name in ("llama3-8b-decode", "llama2-7b-prefill", "gpt-fp16-gelu"):
         wl = inputs.workload(name)
-        run = Runner(wl)
+        run = Runner(wl, layout=layout)
         n = steps if wl.M <= 64 else max(20, steps // 10)
         with ClockSampler() as clk:
             fused = med(run.step, n)
@@ -800,6 +822,8 @@ def main():
     ap.add_argument("--workload", default="llama3-8b-decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--layout", choices=("rows", "packed"), default="rows",
+                    help="weight layout the fused calls read: row-major, or tile-packed once at load")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra timed runs of --steps steps each, for the median / p10 / p90 spread")
@@ -858,19 +882,19 @@ def main():
         from fusion_residual_add_amd import tune
         fra.tune_install(tune.load(args.tune_file))
     if args.traffic_probe:
-        traffic_probe(args.workload)
+        traffic_probe(args.workload, args.layout)
         return
     if args.blas_probe:
         blas_probe(args.workload)
         return
     if args.all_configs:
-        all_configs(min(args.steps, 20))
+        all_configs(min(args.steps, 20), args.layout)
         return
     if args.fusion_gain:
-        fusion_gain(args.steps, args.repeats)
+        fusion_gain(args.steps, args.repeats, args.layout)
         return
     wl = inputs.workload(args.workload)
-    run = Runner(wl)
+    run = Runner(wl, layout=args.layout)
     ms = time_steps(run.step, args.steps, args.warmup)
     with ClockSampler() as clk:
         reps = repeat_stats(run.step, args.steps, args.repeats)
@@ -917,7 +941,8 @@ def main():
                    "act_fn": wl.act_fn, "norm": wl.norm, "weights": wl.wdt,
                    "calls": (["fused_add_norm_qkv"] if wl.n_qkv else []) + [f"fused_gateup_act({wl.act_fn})"],
                    "step_algo_bytes": step_bytes, "step_flops": step_flops,
-                   "weight_sets_rotated": run.R},
+                   "weight_sets_rotated": run.R, "weights_layout": args.layout,
+                   "weights_packed": run.packed},
         "roofline": roof,
         "repeats": reps,
         "clocks": clk.report(),
@@ -932,7 +957,7 @@ def main():
         sec = {}
         for name in ("llama2-7b-prefill", "llama2-7b-prefill-fp8", "llama3-8b-decode-fp8"):
             pwl = inputs.workload(name)
-            pr = Runner(pwl)
+            pr = Runner(pwl, layout=args.layout)
             nsteps = args.prefill_steps if pwl.M > 64 else 100
             pms = time_steps(pr.step, nsteps, 3)
             with ClockSampler() as pclk:
@@ -946,7 +971,7 @@ def main():
                 pval, punit = pfl / (pms * 1e-3) / 1e12, "TFLOP/s"
             else:               # decode: HBM bound (algorithmic bytes)
                 ppeak, pval, punit = HBM_PEAK_GBS, pby / (pms * 1e-3) / 1e9, "GB/s"
-            ent = {"value": round(pval, 2), "unit": punit, "steps": nsteps,
+            ent = {"value": round(pval, 2), "unit": punit, "steps": nsteps, "weights_packed": pr.packed,
                    "ms_per_step": round(pms, 4), "repeats": preps, "clocks": pclk.report(),
                    "dtype": "e4m3" if pwl.wdt == "e4m3" else pwl.act, "peak": ppeak,
                    "frac_of_peak": round(pval / ppeak, 4),

@@ -20,7 +20,7 @@ __all__ = ["fused_add_norm_qkv", "fused_add_norm_qkv_noalloc", "fused_gateup_act
            "fused_dequant_i4_bf16", "fused_dequant_mxfp4_bf16",
            "workspace_bytes", "describe_plan", "FusedProjError", "profile_start", "profile_stop",
            "library_path", "tune_install", "tune_clear", "tune_count", "plan_override",
-           "set_plan_override", "get_plan_override"]
+           "set_plan_override", "get_plan_override", "PackedWeight", "pack_weight", "unpack_weight"]
 
 # torch.uint8 weights are int4 pairs (two values per byte, even k in the low nibble)
 # torch.float4_e2m1fn_x2 weights are MXFP4 element pairs (two per byte, even
@@ -29,6 +29,81 @@ _DT = {torch.float32: _lib.FP_F32, torch.float16: _lib.FP_F16,
        torch.bfloat16: _lib.FP_BF16, torch.int8: _lib.FP_I8, torch.uint8: _lib.FP_I4,
        torch.float8_e4m3fn: _lib.FP_E4M3, torch.float4_e2m1fn_x2: _lib.FP_MXFP4}
 _PACKED4 = (torch.uint8, torch.float4_e2m1fn_x2)
+_LAYOUT = {"rows": 0, "packed": _lib.FP_LAYOUT_PACKED, "packed_gate_up": _lib.FP_LAYOUT_PACKED_GATE_UP}
+
+
+class PackedWeight:
+    """A weight tile-packed by fused_pack_weight (see ``pack_weight``).
+
+    ``data`` has the dtype and shape of the row-major weight and holds the same
+    bytes in the packed order; ``gate_up`` is the gate/up pairing, for the
+    SwiGLU gate/up call.  The projection calls take it wherever they take a
+    weight; their results do not depend on the layout."""
+    __slots__ = ("data", "gate_up")
+
+    def __init__(self, data: torch.Tensor, gate_up: bool):
+        self.data = data
+        self.gate_up = bool(gate_up)
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.data.dtype
+
+    @property
+    def shape(self):
+        return self.data.shape
+
+    @property
+    def device(self):
+        return self.data.device
+
+    @property
+    def layout(self) -> str:
+        return "packed_gate_up" if self.gate_up else "packed"
+
+
+def _wcode(w) -> Tuple[torch.Tensor, int]:
+    """The weight tensor and its w_dtype code (element type | layout bits)."""
+    if isinstance(w, PackedWeight):
+        return w.data, _DT[w.data.dtype] | _LAYOUT[w.layout]
+    return w, _DT[w.dtype]
+
+
+def _elems_per_row(w: torch.Tensor) -> int:
+    return w.shape[1] * 2 if w.dtype in _PACKED4 else w.shape[1]
+
+
+def pack_weight(w: torch.Tensor, gate_up: bool = False, out: Optional[torch.Tensor] = None) -> PackedWeight:
+    """fused_pack_weight: the tile-packed copy of a row-major weight [N, K]
+    (4-bit: [N, K / 2]) -- once, when a model is loaded.  ``gate_up``: the
+    weight of the SwiGLU gate/up call ([gate; up], N = 2 ffn)."""
+    lib = _lib.load()
+    _ptr(w, "w")
+    if w.dim() != 2:
+        raise ValueError(f"w must be 2-D, got shape {tuple(w.shape)}")
+    if out is None:
+        out = torch.empty_like(w)
+    if out.shape != w.shape or out.dtype != w.dtype:
+        raise ValueError("out must have the shape and dtype of w")
+    st = lib.fused_pack_weight(w.data_ptr(), _ptr(out, "out", w.device), w.shape[0], _elems_per_row(w),
+                               _DT[w.dtype], int(bool(gate_up)), _stream(w.device))
+    _check("fused_pack_weight", st)
+    return PackedWeight(out, gate_up)
+
+
+def unpack_weight(pw: PackedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fused_unpack_weight: the row-major weight back from a PackedWeight."""
+    lib = _lib.load()
+    w = pw.data
+    _ptr(w, "w")
+    if out is None:
+        out = torch.empty_like(w)
+    if out.shape != w.shape or out.dtype != w.dtype:
+        raise ValueError("out must have the shape and dtype of the packed weight")
+    st = lib.fused_unpack_weight(w.data_ptr(), _ptr(out, "out", w.device), w.shape[0], _elems_per_row(w),
+                                 _DT[w.dtype], int(pw.gate_up), _stream(w.device))
+    _check("fused_unpack_weight", st)
+    return out
 
 
 def _scale_dtype(w: torch.Tensor) -> torch.dtype:
@@ -83,22 +158,25 @@ _WS: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
 def workspace_bytes(M: int, hidden: int, n_cols: int, act_dtype: torch.dtype,
-                    w_dtype: torch.dtype) -> int:
-    return int(_lib.load().fp_workspace_bytes(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype]))
+                    w_dtype: torch.dtype, layout: str = "rows") -> int:
+    return int(_lib.load().fp_workspace_bytes(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype] | _LAYOUT[layout]))
 
 
-def down_workspace_bytes(M: int, ffn: int, hidden: int, act_dtype: torch.dtype, w_dtype: torch.dtype) -> int:
-    return int(_lib.load().fp_down_workspace_bytes(M, ffn, hidden, _DT[act_dtype], _DT[w_dtype]))
+def down_workspace_bytes(M: int, ffn: int, hidden: int, act_dtype: torch.dtype, w_dtype: torch.dtype,
+                         layout: str = "rows") -> int:
+    return int(_lib.load().fp_down_workspace_bytes(M, ffn, hidden, _DT[act_dtype], _DT[w_dtype] | _LAYOUT[layout]))
 
 
 def describe_plan(M: int, hidden: int, n_cols: int, act_dtype: torch.dtype, w_dtype: torch.dtype,
-                  act: str = "none") -> dict:
+                  act: str = "none", layout: str = "rows") -> dict:
     """The kernel and launch shape a call with these sizes would use (no device
-    work): {"family", "kernel", "grid", "splits", "slots", "workspace"}."""
+    work): {"family", "kernel", "grid", "splits", "slots", "workspace"}.
+    ``layout``: "rows", "packed" or "packed_gate_up" (see pack_weight)."""
     import ctypes
     lib = _lib.load()
     buf = ctypes.create_string_buffer(256)
-    st = lib.fp_describe_plan(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype], _lib.FP_ACT[act], buf, 256)
+    st = lib.fp_describe_plan(M, hidden, n_cols, _DT[act_dtype], _DT[w_dtype] | _LAYOUT[layout], _lib.FP_ACT[act],
+                              buf, 256)
     if st != 0:
         raise FusedProjError("fp_describe_plan", st, lib.fp_last_error().decode())
     out = dict(kv.split("=", 1) for kv in buf.value.decode().split(" "))
@@ -125,7 +203,7 @@ def _stream(device) -> int:
 
 
 def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: Optional[torch.Tensor],
-                       w_qkv: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int, *,
+                       w_qkv: torch.Tensor | PackedWeight, n_heads: int, n_kv_heads: int, head_dim: int, *,
                        beta: Optional[torch.Tensor] = None, norm: str = "rms", eps: float = 1e-5,
                        w_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                        write_h: bool = True, out_dtype: Optional[torch.dtype] = None,
@@ -143,7 +221,7 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
     M, K = x.shape
     act = x.dtype
     odt = out_dtype or act
-    wdt = w_qkv.dtype
+    w_qkv, wcode = _wcode(w_qkv)
     Nw = (n_heads + 2 * n_kv_heads) * head_dim
     _check_weight(w_qkv, w_scale, Nw, K, "w_qkv")
     qs = (n_heads, M, head_dim) if head_major else (M, n_heads, head_dim)
@@ -160,7 +238,7 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
     if h_out is None and write_h:
         h_out = torch.empty_like(x)
     stream = _stream(dev)
-    need = int(lib.fp_workspace_bytes(M, K, Nw, _DT[act], _DT[wdt]))
+    need = int(lib.fp_workspace_bytes(M, K, Nw, _DT[act], wcode))
     ws = workspace if workspace is not None else _workspace(dev, stream, need)
     fn = lib.fused_add_norm_qkv_hm if head_major else lib.fused_add_norm_qkv
     st = fn(
@@ -169,7 +247,7 @@ def fused_add_norm_qkv(x: torch.Tensor, residual: Optional[torch.Tensor], gamma:
         _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w_qkv)),
         _ptr(bias, "bias", dev, act), _ptr(q, "q", dev, odt), _ptr(k, "k", dev, odt),
         _ptr(v, "v", dev, odt), M, K, n_heads, n_kv_heads, head_dim,
-        _DT[act], _DT[wdt], _DT[odt],
+        _DT[act], wcode, _DT[odt],
         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
     _check("fused_add_norm_qkv", st)
     return q, k, v, h_out
@@ -179,7 +257,7 @@ NOALLOC_SCRATCH_BYTES = 16 << 20     # FP_NOALLOC_SCRATCH_BYTES of include/fused
 
 
 def fused_add_norm_qkv_noalloc(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: Optional[torch.Tensor],
-                               w_qkv: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int, *,
+                               w_qkv: torch.Tensor | PackedWeight, n_heads: int, n_kv_heads: int, head_dim: int, *,
                                q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                h_out: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
                                norm: str = "rms", eps: float = 1e-5, w_scale: Optional[torch.Tensor] = None,
@@ -193,6 +271,7 @@ def fused_add_norm_qkv_noalloc(x: torch.Tensor, residual: Optional[torch.Tensor]
     M, K = x.shape
     act = x.dtype
     odt = q.dtype
+    w_qkv, wcode = _wcode(w_qkv)
     Nw = (n_heads + 2 * n_kv_heads) * head_dim
     _check_weight(w_qkv, w_scale, Nw, K, "w_qkv")
     for t, shape, name in ((q, (M, n_heads, head_dim), "q"), (k, (M, n_kv_heads, head_dim), "k"),
@@ -205,13 +284,13 @@ def fused_add_norm_qkv_noalloc(x: torch.Tensor, residual: Optional[torch.Tensor]
         _ptr(w_qkv, "w_qkv", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w_qkv)),
         _ptr(bias, "bias", dev, act), _ptr(q, "q", dev, odt), _ptr(k, "k", dev, odt),
         _ptr(v, "v", dev, odt), M, K, n_heads, n_kv_heads, head_dim,
-        _DT[act], _DT[w_qkv.dtype], _DT[odt], _stream(dev))
+        _DT[act], wcode, _DT[odt], _stream(dev))
     _check("fused_add_norm_qkv_noalloc", st)
     return q, k, v, h_out
 
 
 def fused_gateup_act(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: Optional[torch.Tensor],
-                     w: torch.Tensor, ffn: int, act: str = "swiglu", *,
+                     w: torch.Tensor | PackedWeight, ffn: int, act: str = "swiglu", *,
                      beta: Optional[torch.Tensor] = None, norm: str = "rms", eps: float = 1e-5,
                      w_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
@@ -224,25 +303,25 @@ def fused_gateup_act(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: O
     M, K = x.shape
     adt = x.dtype
     odt = out_dtype or adt
-    wdt = w.dtype
+    w, wcode = _wcode(w)
     Nw = 2 * ffn if act == "swiglu" else ffn
     _check_weight(w, w_scale, Nw, K, "w")
     if out is None:
         out = torch.empty((M, ffn), dtype=odt, device=dev)
     stream = _stream(dev)
-    need = int(lib.fp_workspace_bytes(M, K, Nw, _DT[adt], _DT[wdt]))
+    need = int(lib.fp_workspace_bytes(M, K, Nw, _DT[adt], wcode))
     ws = workspace if workspace is not None else _workspace(dev, stream, need)
     st = lib.fused_gateup_act(
         _ptr(x, "x", dev, adt), _ptr(residual, "residual", dev, adt), _ptr(h_out, "h_out", dev, adt),
         _ptr(gamma, "gamma", dev, adt), _ptr(beta, "beta", dev, adt), FP_NORM[norm], float(eps),
         _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w)), _ptr(bias, "bias", dev, adt),
-        _ptr(out, "out", dev, odt), M, K, ffn, FP_ACT[act], _DT[adt], _DT[wdt], _DT[odt],
+        _ptr(out, "out", dev, odt), M, K, ffn, FP_ACT[act], _DT[adt], wcode, _DT[odt],
         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
     _check("fused_gateup_act", st)
     return out
 
 
-def fused_down_residual(a: torch.Tensor, w: torch.Tensor, residual: Optional[torch.Tensor] = None, *,
+def fused_down_residual(a: torch.Tensor, w: torch.Tensor | PackedWeight, residual: Optional[torch.Tensor] = None, *,
                         w_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                         out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -254,17 +333,18 @@ def fused_down_residual(a: torch.Tensor, w: torch.Tensor, residual: Optional[tor
     M, F = a.shape
     adt = a.dtype
     odt = out_dtype or adt
+    w, wcode = _wcode(w)
     Nw = w.shape[0]
     _check_weight(w, w_scale, Nw, F, "w")
     if out is None:
         out = torch.empty((M, Nw), dtype=odt, device=dev)
     stream = _stream(dev)
-    need = int(lib.fp_down_workspace_bytes(M, F, Nw, _DT[adt], _DT[w.dtype]))
+    need = int(lib.fp_down_workspace_bytes(M, F, Nw, _DT[adt], wcode))
     ws = workspace if workspace is not None else _workspace(dev, stream, need)
     st = lib.fused_down_residual(
         _ptr(a, "a", dev, adt), _ptr(w, "w", dev), _ptr(w_scale, "w_scale", dev, _scale_dtype(w)),
         _ptr(bias, "bias", dev, adt), _ptr(residual, "residual", dev, adt), _ptr(out, "out", dev, odt),
-        M, F, Nw, _DT[adt], _DT[w.dtype], _DT[odt],
+        M, F, Nw, _DT[adt], wcode, _DT[odt],
         None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), stream)
     _check("fused_down_residual", st)
     return out

@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FUSEDPROJ_LIBRARY") or os.path.join(PKG, "libfusedproj.so")
 
 FP_F32, FP_F16, FP_BF16, FP_I8, FP_I4, FP_E4M3, FP_MXFP4 = 0, 1, 2, 3, 4, 5, 6
+FP_LAYOUT_PACKED, FP_LAYOUT_PACKED_GATE_UP = 0x100, 0x200     # weight layout bits of w_dtype
 FP_NORM = {"none": 0, "rms": 1, "layer": 2}
 FP_ACT = {"none": 0, "swiglu": 1, "gelu_tanh": 2}
 STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_ALIAS",
@@ -21,7 +22,8 @@ STATUS = ["FP_OK", "FP_E_NULL", "FP_E_SHAPE", "FP_E_DTYPE", "FP_E_ALIGN", "FP_E_
 
 # every symbol include/fusedproj.h declares
 EXPORTS = ["fp_workspace_bytes", "fp_down_workspace_bytes", "fused_add_norm_qkv", "fused_add_norm_qkv_hm", "fused_add_norm_qkv_noalloc", "fused_gateup_act", "fused_down_residual",
-           "fused_dequant_i8_bf16", "fused_dequant_i4_bf16", "fused_dequant_mxfp4_bf16", "fp_describe_plan", "fp_status_str", "fp_last_error",
+           "fused_dequant_i8_bf16", "fused_dequant_i4_bf16", "fused_dequant_mxfp4_bf16", "fused_pack_weight",
+           "fused_unpack_weight", "fp_describe_plan", "fp_status_str", "fp_last_error",
            "fp_profile_start", "fp_profile_stop", "fp_tune_install", "fp_tune_count",
            "fp_plan_override_set", "fp_plan_override_get"]
 
@@ -84,6 +86,9 @@ def load(path: str = None):
     lib.fused_dequant_i4_bf16.restype = ci
     lib.fused_dequant_mxfp4_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.fused_dequant_mxfp4_bf16.restype = ci
+    for fn in (lib.fused_pack_weight, lib.fused_unpack_weight):
+        fn.argtypes = [vp, vp, i64, i64, ci, ctypes.c_int32, vp]
+        fn.restype = ci
     lib.fp_describe_plan.argtypes = [i64, i64, i64, ci, ci, ci, ctypes.c_char_p, sz]
     lib.fp_describe_plan.restype = ci
     lib.fp_status_str.argtypes = [ci]

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["fp_rows.hip", "fp_tiled.hip", "fp_stream.hip", "fp_stream_bf16.hip", "fp_stream_f16.hip",
-           "fp_stream_i8.hip", "fp_stream_i4.hip", "fp_stream_mx.hip", "fp_stream_f8.hip", "fp_prefill_bf16.hip", "fp_prefill_f16.hip", "fp_prefill_i8.hip", "fp_prefill_i4.hip", "fp_prefill_mx.hip", "fp_gemm8.hip", "fp_gemm16.hip",
+           "fp_stream_i8.hip", "fp_stream_i4.hip", "fp_stream_mx.hip", "fp_stream_f8.hip", "fp_pack.hip", "fp_prefill_bf16.hip", "fp_prefill_f16.hip", "fp_prefill_i8.hip", "fp_prefill_i4.hip", "fp_prefill_mx.hip", "fp_gemm8.hip", "fp_gemm16.hip",
            "fp_noalloc.hip", "fp_api.cpp"]
 LIB = os.path.join(PKG, "libfusedproj.so")
 OBJDIR = os.path.join(PKG, "_build")

@@ -56,6 +56,8 @@ struct Plan {
     int nst = 4;                    // gemm16: LDS stages
     bool rows = false;              // gemm16: the row pass forms A (else A is the call's input)
     size_t rows_off = 0;            // gemm16: normalised rows [M, K]
+    bool unpack = false;            // tile-packed weights unpacked into the workspace first (tiled family)
+    size_t unpack_off = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -250,7 +252,7 @@ void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool q
 // allocation-free entry point's static scratch) the 128 x 512 kernel takes
 // the call instead.
 Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bool swiglu, bool form_rows = true,
-               size_t ws_cap = SIZE_MAX) {
+               size_t ws_cap = SIZE_MAX, int wl = fp::WL_ROWS) {
     Plan p;
     const Knobs kb = knobs_for(M, K, Nw, act, wdt, swiglu);
     if (wdt == FP_E4M3) {
@@ -269,14 +271,17 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         // workgroups run (same limits).  The fp8_tile override (32, 64,
         // 128 or 256) forces a tile.
         p.family = 3;
-        // Requested (family 1), up to 64 tokens with K a multiple of the
-        // chunk and no tile requested: the weight-streaming kernel on the
-        // codes, E4M3 weights decoded in registers, shaped like a call with
-        // int8 weights (the same bytes per weight).  Not the default on
-        // row-major weights: measured on MI355X, Llama-3-8B decode, the FP8
-        // tiles below are faster (step 53.3 against 56.0 us; QKV 15.5
-        // against 18.3 us, gate/up 31.0 against 29.8 us)
-        if (M <= 64 && K % stream_chunk(M) == 0 && kb.fp8_tile == 0 && !kb.no_stream && kb.family == 1) {
+        // Up to 64 tokens with K a multiple of the chunk and no tile
+        // requested, on tile-packed weights (or when requested, family 1):
+        // the weight-streaming kernel on the codes, E4M3 weights decoded in
+        // registers, shaped like a call with int8 weights (the same bytes per
+        // weight).  Measured on MI355X, Llama-3-8B decode step (both calls):
+        // packed weights 50.4 us streaming against 65.2 us in the FP8 tiles
+        // (whose 8-row LDS loads lose on the packed order); row-major
+        // weights 57.1 us streaming against 55.1 us in the tiles, which stay
+        // the default there
+        if (M <= 64 && K % stream_chunk(M) == 0 && kb.fp8_tile == 0 && !kb.no_stream &&
+            (kb.family == 1 || (kb.family == -1 && wl != fp::WL_ROWS))) {
             p.stream8 = true;
             plan_stream(p, M, K, Nw, wdt, true, swiglu, kb);
             const int64_t tiles = p.tiles_n;
@@ -427,6 +432,13 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     p.part_off = off;
     if (p.slots > 1) off = align256(off + (size_t)tiles * p.slots * p.tile_elems * 4);
     (void)wdt_stored;
+    // the tiled kernel reads row-major weights only: tile-packed ones are
+    // unpacked into the workspace first (before any dequantisation)
+    if (wl != fp::WL_ROWS && p.family == 0) {
+        p.unpack = true;
+        p.unpack_off = off;
+        off = align256(off + (size_t)Nw * (size_t)(w4 ? K / 2 : K * act_size(wdt_stored)));
+    }
     if (w4 && p.family == 0) {
         p.deq = true;
         p.deq_off = off;
@@ -434,6 +446,36 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     }
     p.total = off;
     return p;
+}
+
+// A call's w_dtype: the element type in the low byte, the storage layout in
+// the layout bits (FP_LAYOUT_*)
+void split_wdt(fp_dtype w_dtype, fp_dtype &base, int &layout) {
+    base = (fp_dtype)((int)w_dtype & 0xFF);
+    const int bits = (int)w_dtype & ~0xFF;
+    layout = bits == 0 ? fp::WL_ROWS : bits == FP_LAYOUT_PACKED ? fp::WL_PACKED
+           : bits == FP_LAYOUT_PACKED_GATE_UP ? fp::WL_PACKED_GATE_UP : -1;
+}
+
+// bytes of one weight row of K elements
+int64_t row_bytes(fp_dtype wdt, int64_t K) {
+    return (wdt == FP_I4 || wdt == FP_MXFP4) ? K / 2 : K * act_size(wdt);
+}
+
+// The shape rules of the tile-packed layouts (fused_pack_weight): whole
+// 128-row groups (gate/up pairs: whole 64-row halves) of whole 64-byte slices
+fp_status check_layout(int layout, fp_dtype wdt, int64_t n_rows, int64_t K, int64_t gate_rows) {
+    if (layout < 0) return fail(FP_E_DTYPE, "w_dtype carries unknown layout bits");
+    if (layout == fp::WL_ROWS) return FP_OK;
+    if (wdt == FP_F32) return fail(FP_E_DTYPE, "tile-packed weights are 16-bit, int8, int4, E4M3 or MXFP4");
+    if (row_bytes(wdt, K) % 64 != 0)
+        return fail(FP_E_SHAPE, "tile-packed weights need rows of a multiple of 64 bytes (K = %lld)", (long long)K);
+    if (layout == fp::WL_PACKED && n_rows % 128 != 0)
+        return fail(FP_E_SHAPE, "tile-packed weights need a multiple of 128 rows (%lld)", (long long)n_rows);
+    if (layout == fp::WL_PACKED_GATE_UP && (gate_rows <= 0 || gate_rows % 64 != 0 || n_rows != 2 * gate_rows))
+        return fail(FP_E_SHAPE, "gate/up-packed weights are for the SwiGLU call, with ffn a multiple of 64 "
+                    "(ffn = %lld)", (long long)gate_rows);
+    return FP_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -527,6 +569,8 @@ struct Common {
     void *ws;
     size_t ws_bytes;
     hipStream_t stream;
+    int wl = fp::WL_ROWS;     // storage layout of w (fp::WLayout; -1: unknown bits)
+    int64_t gate_rows = 0;    // the SwiGLU call: ffn (the gate/up pairing of a packed w)
 };
 
 fp_status validate_common(const Common &c, const char *wname) {
@@ -536,6 +580,8 @@ fp_status validate_common(const Common &c, const char *wname) {
     if (c.norm != FP_NORM_NONE && c.norm != FP_NORM_RMS && c.norm != FP_NORM_LAYER)
         return fail(FP_E_ARG, "norm = %d is not a fp_norm value", (int)c.norm);
     fp_status st = check_dtypes(c.act, c.wdt, c.odt);
+    if (st != FP_OK) return st;
+    st = check_layout(c.wl, c.wdt, c.Nw, c.K, c.gate_rows);
     if (st != FP_OK) return st;
     if (!c.x && c.M > 0) return fail(FP_E_NULL, "x is NULL");
     if (!c.w) return fail(FP_E_NULL, "%s is NULL", wname);
@@ -595,6 +641,7 @@ fp_status run_fp8(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.x = codes;
     pa.a_scale = qscale;
     pa.w = c.w;
+    pa.w_layout = c.wl;
     pa.w_scale = (const float *)c.w_scale;
     pa.bias = c.bias;
     pa.out_f32 = c.odt == FP_F32;
@@ -649,6 +696,7 @@ fp_status run_gemm16(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.stats = nullptr;
     pa.norm = 0;
     pa.w = c.w;
+    pa.w_layout = c.wl;
     pa.bias = c.bias;
     pa.out_f32 = c.odt == FP_F32;
     pa.M = c.M;
@@ -697,19 +745,29 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
     pa.norm = (int)c.norm;
     pa.w = c.w;
+    pa.w_layout = c.wl;
     pa.w_scale = (const float *)c.w_scale;
     const bool wi8 = c.wdt == FP_I8;
     const int wq = c.wdt == FP_I8 ? 1 : plan.deq ? 0 : c.wdt == FP_I4 ? 2 : c.wdt == FP_MXFP4 ? 3 : 0;
+    const void *wsrc = c.w;   // row-major weights for the dequantisation
+    if (plan.unpack) {
+        void *wu = ws + plan.unpack_off;
+        ProfScope ps(fp::pack_kernel_name(true), c.stream);
+        hipError_t e = fp::launch_pack(c.w, wu, c.Nw, row_bytes(c.wdt, c.K), c.gate_rows, c.wl, true, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "unpack_kernel launch");
+        pa.w = wsrc = wu;
+        pa.w_layout = fp::WL_ROWS;
+    }
     if (plan.deq) {
         void *wb = ws + plan.deq_off;
         if (c.wdt == FP_MXFP4) {
             ProfScope ps(fp::dequant_mxfp4_kernel_name(), c.stream);
-            hipError_t e = fp::launch_dequant_mxfp4((const uint8_t *)c.w, (const uint8_t *)c.w_scale, wb, c.Nw, c.K,
+            hipError_t e = fp::launch_dequant_mxfp4((const uint8_t *)wsrc, (const uint8_t *)c.w_scale, wb, c.Nw, c.K,
                                                     c.stream);
             if (e != hipSuccess) return hip_fail(e, "dequant_mxfp4_kernel launch");
         } else {
             ProfScope ps(fp::dequant_i4_kernel_name(), c.stream);
-            hipError_t e = fp::launch_dequant_i4((const uint8_t *)c.w, (const float *)c.w_scale, wb, c.Nw, c.K,
+            hipError_t e = fp::launch_dequant_i4((const uint8_t *)wsrc, (const float *)c.w_scale, wb, c.Nw, c.K,
                                                  c.stream);
             if (e != hipSuccess) return hip_fail(e, "dequant_i4_kernel launch");
         }
@@ -760,20 +818,28 @@ extern "C" {
 
 size_t fp_workspace_bytes(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
                           fp_dtype w_dtype) {
-    if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0) return 0;
-    if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
-    if ((w_dtype == FP_I4 || w_dtype == FP_E4M3) && hidden % 128 != 0) return 0;
+    fp_dtype wdt;
+    int wl;
+    split_wdt(w_dtype, wdt, wl);
+    if (M < 0 || hidden <= 0 || hidden % 64 != 0 || n_cols <= 0 || wl < 0) return 0;
+    if (check_dtypes(act_dtype, wdt, act_dtype) != FP_OK) return 0;
+    if ((wdt == FP_I4 || wdt == FP_E4M3) && hidden % 128 != 0) return 0;
     if (M == 0) return 0;
-    const size_t a = make_plan(M, hidden, n_cols, act_dtype, w_dtype, false).total;
-    const size_t b = make_plan(M, hidden, n_cols, act_dtype, w_dtype, true).total;
+    // gate/up-packed weights only go to the SwiGLU call
+    const size_t a = wl == fp::WL_PACKED_GATE_UP ? 0 : make_plan(M, hidden, n_cols, act_dtype, wdt, false, true,
+                                                                 SIZE_MAX, wl).total;
+    const size_t b = make_plan(M, hidden, n_cols, act_dtype, wdt, true, true, SIZE_MAX, wl).total;
     return a > b ? a : b;
 }
 
 size_t fp_down_workspace_bytes(int64_t M, int64_t ffn, int64_t hidden, fp_dtype act_dtype, fp_dtype w_dtype) {
-    if (M <= 0 || ffn <= 0 || ffn % 64 != 0 || hidden <= 0) return 0;
-    if (check_dtypes(act_dtype, w_dtype, act_dtype) != FP_OK) return 0;
-    if ((w_dtype == FP_I4 || w_dtype == FP_E4M3) && ffn % 128 != 0) return 0;
-    return make_plan(M, ffn, hidden, act_dtype, w_dtype, false, false).total;
+    fp_dtype wdt;
+    int wl;
+    split_wdt(w_dtype, wdt, wl);
+    if (M <= 0 || ffn <= 0 || ffn % 64 != 0 || hidden <= 0 || wl < 0) return 0;
+    if (check_dtypes(act_dtype, wdt, act_dtype) != FP_OK) return 0;
+    if ((wdt == FP_I4 || wdt == FP_E4M3) && ffn % 128 != 0) return 0;
+    return make_plan(M, ffn, hidden, act_dtype, wdt, false, false, SIZE_MAX, wl).total;
 }
 
 }  // extern "C"
@@ -792,9 +858,13 @@ fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const v
                     (long long)n_heads, (long long)n_kv_heads);
     if (head_dim <= 0 || head_dim % 16 != 0)
         return fail(FP_E_SHAPE, "head_dim = %lld must be a positive multiple of 16", (long long)head_dim);
+    fp_dtype wdt;
+    int wl;
+    split_wdt(w_dtype, wdt, wl);
     Common c{x, residual, h_out, gamma, beta, norm, eps, w_qkv, w_scale, bias,
-             M, hidden, (n_heads + 2 * n_kv_heads) * head_dim, act_dtype, w_dtype, out_dtype,
+             M, hidden, (n_heads + 2 * n_kv_heads) * head_dim, act_dtype, wdt, out_dtype,
              workspace, workspace_bytes, (hipStream_t)hip_stream};
+    c.wl = wl;
     fp_status st = validate_common(c, "w_qkv");
     if (st != FP_OK) return st;
     if ((!q || !k || !v) && M > 0) return fail(FP_E_NULL, "q, k and v must all be non-NULL");
@@ -808,8 +878,8 @@ fp_status add_norm_qkv(const void *x, const void *residual, void *h_out, const v
     outs.push_back(rng("q", q, M * nq * eo));
     outs.push_back(rng("k", k, M * nkv * eo));
     outs.push_back(rng("v", v, M * nkv * eo));
-    const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, w_dtype, false, true,
-                                source ? (size_t)FP_NOALLOC_SCRATCH_BYTES : SIZE_MAX);
+    const Plan plan = make_plan(M, hidden, c.Nw, act_dtype, wdt, false, true,
+                                source ? (size_t)FP_NOALLOC_SCRATCH_BYTES : SIZE_MAX, wl);
     // the workspace of a call that brings none: from the source, once every
     // argument has been checked (it may touch the device)
     if (source) {
@@ -891,9 +961,14 @@ fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, con
     if (ffn <= 0 || ffn % 16 != 0)
         return fail(FP_E_SHAPE, "ffn = %lld must be a positive multiple of 16", (long long)ffn);
     const int64_t Nw = act == FP_ACT_SWIGLU ? 2 * ffn : ffn;
+    fp_dtype wdt;
+    int wl;
+    split_wdt(w_dtype, wdt, wl);
     Common c{x, residual, h_out, gamma, beta, norm, eps, w, w_scale, bias,
-             M, hidden, Nw, act_dtype, w_dtype, out_dtype, workspace, workspace_bytes,
+             M, hidden, Nw, act_dtype, wdt, out_dtype, workspace, workspace_bytes,
              (hipStream_t)hip_stream};
+    c.wl = wl;
+    c.gate_rows = act == FP_ACT_SWIGLU ? ffn : 0;
     fp_status st = validate_common(c, "w");
     if (st != FP_OK) return st;
     if (!out && M > 0) return fail(FP_E_NULL, "out is NULL");
@@ -903,7 +978,7 @@ fp_status fused_gateup_act(const void *x, const void *residual, void *h_out, con
     add_inputs(c, ins, "w");
     if (h_out) outs.push_back(rng("h_out", h_out, M * hidden * ea));
     outs.push_back(rng("out", out, M * ffn * eo));
-    const Plan plan = make_plan(M, hidden, Nw, act_dtype, w_dtype, act == FP_ACT_SWIGLU);
+    const Plan plan = make_plan(M, hidden, Nw, act_dtype, wdt, act == FP_ACT_SWIGLU, true, SIZE_MAX, wl);
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);
@@ -923,9 +998,13 @@ fp_status fused_down_residual(const void *a, const void *w, const void *w_scale,
     if (hidden <= 0 || hidden % 16 != 0)
         return fail(FP_E_SHAPE, "hidden = %lld must be a positive multiple of 16", (long long)hidden);
     // the projection of a (K = ffn) onto hidden output columns, no norm prologue
+    fp_dtype wdt;
+    int wl;
+    split_wdt(w_dtype, wdt, wl);
     Common c{a, nullptr, nullptr, nullptr, nullptr, FP_NORM_NONE, 0.0f, w, w_scale, bias,
-             M, ffn, hidden, act_dtype, w_dtype, out_dtype, workspace, workspace_bytes,
+             M, ffn, hidden, act_dtype, wdt, out_dtype, workspace, workspace_bytes,
              (hipStream_t)hip_stream};
+    c.wl = wl;
     if (ffn <= 0 || ffn % 64 != 0)
         return fail(FP_E_SHAPE, "ffn = %lld must be a positive multiple of 64", (long long)ffn);
     fp_status st = validate_common(c, "w");
@@ -941,7 +1020,7 @@ fp_status fused_down_residual(const void *a, const void *w, const void *w_scale,
     ins[0].name = "a";
     if (residual && !in_place) ins.push_back(rng("residual", residual, M * hidden * ea));
     outs.push_back(rng("out", out, M * hidden * eo));
-    const Plan plan = make_plan(M, ffn, hidden, act_dtype, w_dtype, false, false);
+    const Plan plan = make_plan(M, ffn, hidden, act_dtype, wdt, false, false, SIZE_MAX, wl);
     st = check_workspace(c, plan, outs);
     if (st != FP_OK) return st;
     st = check_alias(ins, outs);
@@ -1011,6 +1090,49 @@ fp_status fused_dequant_mxfp4_bf16(const void *q, const void *scale, void *out_b
     return FP_OK;
 }
 
+}  // extern "C"
+
+namespace {
+fp_status pack_common(const char *fn, const void *src, void *dst, int64_t n_rows, int64_t K, fp_dtype w_dtype,
+                      int32_t gate_up, void *hip_stream, bool unpack) {
+    if (w_dtype != FP_F16 && w_dtype != FP_BF16 && w_dtype != FP_I8 && w_dtype != FP_I4 && w_dtype != FP_E4M3 &&
+        w_dtype != FP_MXFP4)
+        return fail(FP_E_DTYPE, "%s: w_dtype %d is not F16, BF16, I8, I4, E4M3 or MXFP4", fn, (int)w_dtype);
+    if (gate_up != 0 && gate_up != 1) return fail(FP_E_ARG, "%s: gate_up = %d (0 or 1)", fn, (int)gate_up);
+    if (n_rows < 0 || K <= 0) return fail(FP_E_SHAPE, "%s: n_rows = %lld, K = %lld", fn, (long long)n_rows,
+                                          (long long)K);
+    if ((w_dtype == FP_I4 || w_dtype == FP_MXFP4) && K % 2 != 0)
+        return fail(FP_E_SHAPE, "%s: K = %lld must be even for 4-bit weights", fn, (long long)K);
+    const int layout = gate_up ? fp::WL_PACKED_GATE_UP : fp::WL_PACKED;
+    fp_status st = check_layout(layout, w_dtype, n_rows, K, gate_up ? n_rows / 2 : 0);
+    if (st != FP_OK) return st;
+    if (!src || !dst) return fail(FP_E_NULL, "%s: both weight pointers must be non-NULL", fn);
+    if (!aligned16(src) || !aligned16(dst)) return fail(FP_E_ALIGN, "%s: both weights must be 16-byte aligned", fn);
+    const int64_t bytes = n_rows * row_bytes(w_dtype, K);
+    std::vector<Range> ins{rng("source weight", src, bytes)}, outs{rng("destination weight", dst, bytes)};
+    st = check_alias(ins, outs);
+    if (st != FP_OK) return st;
+    if (n_rows == 0) return FP_OK;
+    hipStream_t s = (hipStream_t)hip_stream;
+    ProfScope ps(fp::pack_kernel_name(unpack), s);
+    hipError_t e = fp::launch_pack(src, dst, n_rows, row_bytes(w_dtype, K), n_rows / 2, layout, unpack, s);
+    if (e != hipSuccess) return hip_fail(e, unpack ? "unpack_kernel launch" : "pack_kernel launch");
+    return FP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+fp_status fused_pack_weight(const void *w, void *w_packed, int64_t n_rows, int64_t K, fp_dtype w_dtype,
+                            int32_t gate_up, void *hip_stream) {
+    return pack_common("fused_pack_weight", w, w_packed, n_rows, K, w_dtype, gate_up, hip_stream, false);
+}
+
+fp_status fused_unpack_weight(const void *w_packed, void *w, int64_t n_rows, int64_t K, fp_dtype w_dtype,
+                              int32_t gate_up, void *hip_stream) {
+    return pack_common("fused_unpack_weight", w_packed, w, n_rows, K, w_dtype, gate_up, hip_stream, true);
+}
+
 fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype act_dtype,
                            fp_dtype w_dtype, fp_act act, char *buf, size_t cap) {
     if (!buf || cap == 0) return fail(FP_E_NULL, "buf must be non-NULL with cap > 0");
@@ -1018,11 +1140,16 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
         return fail(FP_E_SHAPE, "M = %lld, hidden = %lld (a positive multiple of 64), n_cols = %lld",
                     (long long)M, (long long)hidden, (long long)n_cols);
     if ((int)act < 0 || (int)act > 2) return fail(FP_E_ARG, "act = %d", (int)act);
-    const fp_status st = check_dtypes(act_dtype, w_dtype, act_dtype);
+    const fp_dtype w_dtype_arg = w_dtype;
+    int wl;
+    split_wdt(w_dtype_arg, w_dtype, wl);
+    fp_status st = check_dtypes(act_dtype, w_dtype, act_dtype);
+    if (st != FP_OK) return st;
+    st = check_layout(wl, w_dtype, n_cols, hidden, act == FP_ACT_SWIGLU ? n_cols / 2 : 0);
     if (st != FP_OK) return st;
     if ((w_dtype == FP_I4 || w_dtype == FP_E4M3) && hidden % 128 != 0)
         return fail(FP_E_SHAPE, "hidden = %lld must be a multiple of 128 for int4 / E4M3 weights", (long long)hidden);
-    const Plan p = make_plan(M, hidden, n_cols, act_dtype, w_dtype, act == FP_ACT_SWIGLU);
+    const Plan p = make_plan(M, hidden, n_cols, act_dtype, w_dtype, act == FP_ACT_SWIGLU, true, SIZE_MAX, wl);
     if (p.family == 3) {
         const int a8 = act_code(act_dtype);
         const int e8 = act == FP_ACT_SWIGLU ? fp::EPI_SWIGLU : act == FP_ACT_GELU_TANH ? fp::EPI_GELU : fp::EPI_LINEAR;
@@ -1051,9 +1178,10 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
                      : p.family == 2 ? fp::prefill_kernel_name(a, wq, epi)
                                      : fp::proj_kernel_name(a, wi8, p.tile, epi);
     const int64_t grid = p.family == 1 ? p.grid : (int64_t)p.tiles_m * p.tiles_n * p.splits;
-    snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s", fam, name,
+    const char *deq = !p.deq ? "" : w_dtype == FP_MXFP4 ? "dequant_mxfp4_kernel" : "dequant_i4_kernel";
+    snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s%s%s%s", fam, name,
              (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total,
-             !p.deq ? "" : w_dtype == FP_MXFP4 ? " prep=dequant_mxfp4_kernel" : " prep=dequant_i4_kernel");
+             p.unpack || p.deq ? " prep=" : "", p.unpack ? "unpack_kernel" : "", p.unpack && p.deq ? "+" : "", deq);
     return FP_OK;
 }
 

@@ -128,14 +128,18 @@ void gemm16_kernel(ProjArgs p) {
         if constexpr (SW) wr = r < BN / 2 ? (int64_t)tn * (BN / 2) + r : p.F + (int64_t)tn * (BN / 2) + (r - BN / 2);
         else wr = (int64_t)tn * BN + r;
         wr = wr < p.Nw ? wr : p.Nw - 1;
-        b_off[i] = (uint32_t)(wr * p.K * 2) + gc * 16;
+        b_off[i] = (uint32_t)weight_off(p.w_layout, wr, gc * 16, p.F, p.K * 2);
     }
+    // stage kt: row bytes kt * ROWB of both operands, added as the scalar
+    // offset (tile-packed weights: that byte's offset in the packed layout,
+    // additive since ROWB is a multiple of 64)
     auto issue = [&](int kt, unsigned char *st) __attribute__((always_inline)) {
         const uint32_t soff = (uint32_t)kt * ROWB;
+        const uint32_t wsoff = p.w_layout ? (uint32_t)packed_col_off(soff) : soff;
 #pragma unroll
         for (int i = 0; i < NI; ++i) load_lds16(ra, st + (NI * wave + i) * 1024, a_off[i], soff);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) load_lds16(rw, st + TILE + (NI * wave + i) * 1024, b_off[i], soff);
+        for (int i = 0; i < NI; ++i) load_lds16(rw, st + TILE + (NI * wave + i) * 1024, b_off[i], wsoff);
     };
 
     // ---- fragments: A rows 128 wm + 32 f + l % 32; B tile rows: SwiGLU the

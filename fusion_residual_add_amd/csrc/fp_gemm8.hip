@@ -111,14 +111,17 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
         if constexpr (SW) wr = r < BN / 2 ? (int64_t)tn * (BN / 2) + r : p.F + (int64_t)tn * (BN / 2) + (r - BN / 2);
         else wr = (int64_t)tn * BN + r;
         wr = wr < p.Nw ? wr : p.Nw - 1;
-        b_off[i] = (uint32_t)(wr * p.K) + c * 16;
+        b_off[i] = (uint32_t)weight_off(p.w_layout, wr, c * 16, p.F, p.K);
     }
+    // stage kt: row bytes kt * BK, the scalar offset (tile-packed weights:
+    // that byte's packed offset, additive since BK is a multiple of 64)
     auto issue = [&](int kt, unsigned char *la, unsigned char *lb) {
         const uint32_t soff = (uint32_t)kt * BK;
+        const uint32_t wsoff = p.w_layout ? (uint32_t)packed_col_off(soff) : soff;
 #pragma unroll
         for (int i = 0; i < IA; ++i) load_lds16(ra, la + (IA * wave + i) * 1024, a_off[i], soff);
 #pragma unroll
-        for (int i = 0; i < IB; ++i) load_lds16(rw, lb + (IB * wave + i) * 1024, b_off[i], soff);
+        for (int i = 0; i < IB; ++i) load_lds16(rw, lb + (IB * wave + i) * 1024, b_off[i], wsoff);
     };
 
     // ---- fragments: A rows 32 (FM wm + f) + l % 32; B tile rows: SwiGLU the

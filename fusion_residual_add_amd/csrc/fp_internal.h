@@ -25,6 +25,41 @@ enum TileCfg {
 struct TileShape { int bm, bn, bk; };
 TileShape tile_shape(int cfg);
 
+// Weight storage layouts (the layout bits of a call's w_dtype).
+enum WLayout { WL_ROWS = 0, WL_PACKED = 1, WL_PACKED_GATE_UP = 2 };
+
+// Tile-packed weights (fused_pack_weight).  The rows are taken in groups of
+// 128 -- with the gate/up pairing, the gate rows 64 t .. 64 t + 63 followed
+// by the matching up rows F + 64 t .. F + 64 t + 63 -- and a group is stored
+// K slice by K slice: for each 64-byte slice s of the row bytes, its eight
+// 16-row blocks, 1 KB each; inside a block, byte 256 g + 16 i + j holds byte
+// 64 s + 16 g + j of the block's row i.  A workgroup that streams a group
+// K slice by K slice then reads one contiguous run per step.
+// Byte offset of logical row r's first byte:
+__host__ __device__ inline int64_t packed_row_off(int64_t r, int64_t F, int64_t row_bytes, int layout) {
+    int64_t t, i;
+    if (layout == WL_PACKED_GATE_UP) {
+        const bool up = r >= F;
+        const int64_t j = up ? r - F : r;
+        t = j >> 6;
+        i = ((j >> 4) & 3) + (up ? 4 : 0);
+    } else {
+        t = r >> 7;
+        i = (r >> 4) & 7;
+    }
+    return t * 128 * row_bytes + i * 1024 + (r & 15) * 16;
+}
+// ... to which row byte c adds (additively over a 64-byte-aligned base and a
+// part inside its slice: packed_col_off(a + b) = packed_col_off(a) +
+// packed_col_off(b) for a % 64 == 0, and for b < 64 - a % 64 with a % 16 == 0)
+__host__ __device__ inline int64_t packed_col_off(int64_t c) {
+    return (c >> 6) * 8192 + ((c >> 4) & 3) * 256 + (c & 15);
+}
+// byte offset of row byte c of weight row r in either layout
+__host__ __device__ inline int64_t weight_off(int layout, int64_t r, int64_t c, int64_t F, int64_t row_bytes) {
+    return layout == WL_ROWS ? r * row_bytes + c : packed_row_off(r, F, row_bytes, layout) + packed_col_off(c);
+}
+
 // Everything one projection launch needs.
 struct ProjArgs {
     // prologue inputs
@@ -36,6 +71,7 @@ struct ProjArgs {
     int norm;               // 0 none, 1 rms, 2 layer
     // weights
     const void *w;          // [Nw, K] act or int8
+    int w_layout;           // WLayout (packed: gate/up pairs against F, the SwiGLU width)
     const float *w_scale;   // int8 / E4M3: [Nw] fp32; int4: [Nw, K/128] fp32; MXFP4: [Nw, K/32] E8M0 bytes
     const void *bias;       // [Nw] act or null
     const void *res_epi;    // EPI_LINEAR: [M, F] act added to the output (residual stream), or null
@@ -118,6 +154,11 @@ const char *dequant_mxfp4_kernel_name();
 // E4M3 (W8A8) path: per-token quantisation of the normalised rows, then the
 // FP8 GEMM on the codes (x = codes, a_scale, w = E4M3 weights, w_scale [Nw])
 hipError_t launch_quant8(int act, const StatsArgs &a, hipStream_t s);
+// tile-packed weights: pack (unpack = false) a row-major weight of n_rows rows
+// of row_bytes bytes, or unpack it back (F: gate rows of the gate/up pairing)
+hipError_t launch_pack(const void *src, void *dst, int64_t n_rows, int64_t row_bytes, int64_t F, int layout,
+                       bool unpack, hipStream_t s);
+const char *pack_kernel_name(bool unpack);
 const char *quant8_kernel_name(int act);
 // 256 x 256 prefill path: the row pass writes the normalised rows (h_out as
 // stats_kernel, the rows into StatsArgs::rows), then the 16-bit GEMM reads

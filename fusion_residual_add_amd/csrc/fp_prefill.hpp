@@ -169,15 +169,15 @@ void prefill_kernel(ProjArgs p) {
             wrow = wrow < p.Nw ? wrow : p.Nw - 1;
         }
         if constexpr (WI8) {
-            b_off[i] = (uint32_t)(wrow * p.K) + (tid & 3) * 16;
+            b_off[i] = (uint32_t)weight_off(p.w_layout, wrow, (tid & 3) * 16, p.F, p.K);
             b_sc[i] = p.w_scale[wrow];
         } else if constexpr (WI4) {
-            b_off[i] = (uint32_t)(wrow * (p.K / 2)) + (tid & 1) * 16;
+            b_off[i] = (uint32_t)weight_off(p.w_layout, wrow, (tid & 1) * 16, p.F, p.K / 2);
             // MXFP4: the thread's 32 values of a stage are block 2 kt + (tid & 1) of the row
             b_soff[i] = WMX ? (uint32_t)(wrow * (p.K / 32)) + (tid & 1) : (uint32_t)(wrow * (p.K / 128) * 4);
         } else {
             const int c = (lane & 7) ^ ((br >> 1) & 7);
-            b_off[i] = (uint32_t)((wrow * p.K + c * 8) * 2);
+            b_off[i] = (uint32_t)weight_off(p.w_layout, wrow, c * 16, p.F, p.K * 2);
         }
     }
 
@@ -234,9 +234,12 @@ void prefill_kernel(ProjArgs p) {
     auto a_store = [&](unsigned char *la, int i, const float (&n)[8]) {
         *(u32x4 *)(la + swz(a_r0 + 32 * i, a_c)) = T::pack(n);
     };
-    // ---- weight side
+    // ---- weight side.  A stage's weight bytes start at row byte kt times the
+    // stage's bytes per row; its offset in the weight's layout is added as the
+    // scalar offset to the lanes' offsets of stage 0 (additive in both layouts)
+    auto wsoff = [&](uint32_t rb) -> uint32_t { return p.w_layout ? (uint32_t)packed_col_off(rb) : rb; };
     auto bload_lds = [&](int kt, unsigned char *lb) {   // 16-bit weights, straight to LDS
-        const uint32_t kb = (uint32_t)kt * (BK * 2);
+        const uint32_t kb = wsoff((uint32_t)kt * (BK * 2));
 #pragma unroll
         for (int i = 0; i < 16; ++i) load_lds16(rw, lb + (128 * wave + 8 * i) * ROWB, b_off[i], kb);
     };
@@ -244,14 +247,14 @@ void prefill_kernel(ProjArgs p) {
     // the LDS tile of its stage (16 values -> two 16-byte bf16 chunks)
     auto bload_one = [&](int kt, int i) {
         if constexpr (WMX) {
-            B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * (BK / 2));
+            B.q[i] = ld16(rw, b_off[i], wsoff((uint32_t)kt * (BK / 2)));
             B.sm[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, b_soff[i], (uint32_t)kt * 2, 0);
         } else if constexpr (WI4) {
-            B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * (BK / 2));
+            B.q[i] = ld16(rw, b_off[i], wsoff((uint32_t)kt * (BK / 2)));
             B.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, b_soff[i],
                                                                                     (uint32_t)(kt / 2) * 4, 0));
         } else {
-            B.q[i] = ld16(rw, b_off[i], (uint32_t)kt * BK);
+            B.q[i] = ld16(rw, b_off[i], wsoff((uint32_t)kt * BK));
         }
     };
     auto bstore_one = [&](unsigned char *lb, int i) {

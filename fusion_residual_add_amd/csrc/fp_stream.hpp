@@ -79,7 +79,12 @@ void stream_kernel(ProjArgs p) {
         // accumulator column, which the epilogue never stores.  Keeping every load
         // unconditional keeps the main loop free of branches, so the compiler can
         // count outstanding loads exactly instead of draining them.
-        const char *wrow[NR];
+        // row bytes; a chunk's bytes per row; the address step per chunk and per
+        // 64-byte load slice (row-major rows, or tile-packed 1 KB block slices)
+        constexpr int64_t CKB = WI4 ? CK / 2 : WI8 ? CK : CK * 2;
+        const int64_t rbytes = WI4 ? p.K / 2 : WI8 ? p.K : p.K * 2;
+        const int64_t cstep = p.w_layout ? NL * 8192 : CKB, ustep = p.w_layout ? 8192 : 64;
+        const char *wrow[NR];   // this lane's first byte of its row (its 16-byte group of slice 0)
         float wsc[NR];
         const float *wsr[NR];   // int4: the row's group scales
         const unsigned char *wsm[NR];   // MXFP4: the row's block scales
@@ -95,7 +100,7 @@ void stream_kernel(ProjArgs p) {
                 r = (int64_t)tn * NB + wave * (NR * 16) + n * 16 + (lane & 15);
                 r = r < p.Nw ? r : p.Nw - 1;
             }
-            wrow[n] = (const char *)p.w + (WI4 ? r * (p.K / 2) : r * p.K * (WI8 ? 1 : 2));
+            wrow[n] = (const char *)p.w + weight_off(p.w_layout, r, (lane >> 4) * 16, p.F, rbytes);
             wsc[n] = 0.f;
             wsr[n] = nullptr;
             wsm[n] = nullptr;
@@ -103,13 +108,11 @@ void stream_kernel(ProjArgs p) {
             if constexpr (WQ == 2) wsr[n] = p.w_scale + r * (p.K / 128);
             if constexpr (WMX) wsm[n] = (const unsigned char *)p.w_scale + r * (p.K / 32);
         }
+        // load slice u of chunk c: row bytes c * CKB + 64 u + 16 (lane / 16) .. + 15
+        // (int8 / E4M3: 16 k; int4 / MXFP4: 32 k, one 128-k scale group per u
+        // with lane group g at k 32 g; 16-bit: 8 k)
         auto wload = [&](int c, int n, int u) -> u32x4 {
-            if constexpr (WI8)
-                return *(const u32x4 *)(wrow[n] + (int64_t)c * CK + u * 64 + (lane >> 4) * 16);
-            else if constexpr (WI4)   // 128 k (one scale group) per u; lane group g: k 32 g .. 32 g + 31
-                return *(const u32x4 *)(wrow[n] + (int64_t)c * (CK / 2) + u * 64 + (lane >> 4) * 16);
-            else
-                return *(const u32x4 *)(wrow[n] + ((int64_t)c * CK + u * 32 + (lane >> 4) * 8) * 2);
+            return *(const u32x4 *)(wrow[n] + (int64_t)c * cstep + u * ustep);
         };
 
         // ---- activation side: fixed k-vector, token rows a_r0 + i * AR (rows past

@@ -45,7 +45,7 @@ _NAMES = {v: k for k, v in _DTYPES.items()}
 
 
 def candidates(M: int, hidden: int, n_cols: int, act: torch.dtype, wdt: torch.dtype,
-               swiglu: bool) -> List[Dict]:
+               swiglu: bool, layout: str = "rows") -> List[Dict]:
     """Launch configurations for one call shape (plan overrides; {} is the
     planner's own choice), one per distinct plan."""
     fn = "swiglu" if swiglu else "none"
@@ -73,7 +73,7 @@ def candidates(M: int, hidden: int, n_cols: int, act: torch.dtype, wdt: torch.dt
     try:
         for c in raw:
             fra.tune_install([_entry(M, M, hidden, n_cols, act, wdt, swiglu, c)] if c else [])
-            p = fra.describe_plan(M, hidden, n_cols, act, wdt, fn)
+            p = fra.describe_plan(M, hidden, n_cols, act, wdt, fn, layout=layout)
             key = (p["kernel"], p["grid"], p["splits"])
             if key not in seen:
                 seen.add(key)
@@ -93,9 +93,10 @@ def _entry(m_lo, m_hi, hidden, n_cols, act, wdt, swiglu, cfg) -> Dict:
 
 
 class _Call:
-    """Device inputs of one call of a workload, with rotated weight copies."""
+    """Device inputs of one call of a workload, with rotated weight copies
+    (layout "packed": tile-packed copies, where the shape allows)."""
 
-    def __init__(self, wl, call: str, seed: int = 0):
+    def __init__(self, wl, call: str, seed: int = 0, layout: str = "rows"):
         dev = torch.device("cuda:0")
         host = inputs.generate(wl, seed=seed, parts=(call,))
         self.wl, self.call = wl, call
@@ -110,6 +111,13 @@ class _Call:
         self.wkey = wkey
         self.n_cols = w.shape[0]
         self.swiglu = call == "gu" and wl.act_fn == "swiglu"
+        self.layout = "rows"
+        if layout == "packed":
+            try:
+                self.ws = [fra.pack_weight(x, gate_up=self.swiglu) for x in self.ws]
+                self.layout = "packed_gate_up" if self.swiglu else "packed"
+            except fra.FusedProjError:
+                pass
 
     def run(self, i: int, out_dtype=None):
         wl, d = self.wl, self.d
@@ -125,13 +133,13 @@ class _Call:
                                     out_dtype=out_dtype)
 
 
-def tune_call(wl, call: str, reps: int = 20, rounds: int = 5, log=None) -> Dict:
+def tune_call(wl, call: str, reps: int = 20, rounds: int = 5, log=None, layout: str = "rows") -> Dict:
     """Time every candidate of one call of workload ``wl``; returns
     {"entry": table entry or None, "results": [(candidate, median us)], "default_us": ...}."""
-    c = _Call(wl, call)
+    c = _Call(wl, call, layout=layout)
     act, wdt = c.d["x"].dtype, c.ws[0].dtype
     M, K = wl.M, wl.hidden
-    cands = candidates(M, K, c.n_cols, act, wdt, c.swiglu)
+    cands = candidates(M, K, c.n_cols, act, wdt, c.swiglu, c.layout)
     times: List[List[float]] = [[] for _ in cands]
     ref = None
     try:
@@ -177,13 +185,13 @@ def tune_call(wl, call: str, reps: int = 20, rounds: int = 5, log=None) -> Dict:
                         for cnd, us in results]}
 
 
-def tune_workload(name: str, reps: int = 20, rounds: int = 5, log=print) -> List[Dict]:
+def tune_workload(name: str, reps: int = 20, rounds: int = 5, log=print, layout: str = "rows") -> List[Dict]:
     """Table entries for both calls of a named workload (only where a candidate
     beats the planner by more than 1 %)."""
     wl = inputs.workload(name)
     out = []
     for call in (("qkv", "gu") if wl.n_qkv else ("gu",)):
-        r = tune_call(wl, call, reps=reps, rounds=rounds, log=log)
+        r = tune_call(wl, call, reps=reps, rounds=rounds, log=log, layout=layout)
         if r["entry"]:
             out.append(r["entry"])
     return out
@@ -213,11 +221,13 @@ def main(argv: Optional[List[str]] = None) -> int:
     ap.add_argument("--out", help="write the table here (JSON)")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--rounds", type=int, default=5)
+    ap.add_argument("--layout", choices=("rows", "packed"), default="rows",
+                    help="time the calls on row-major or tile-packed weights")
     args = ap.parse_args(argv)
     entries = []
     for name in args.workload:
         entries += tune_workload(name, reps=args.reps, rounds=args.rounds,
-                                 log=lambda s: print(s, flush=True))
+                                 log=lambda s: print(s, flush=True), layout=args.layout)
     if args.out:
         save(entries, args.out)
     print(f"{len(entries)} table entries", flush=True)

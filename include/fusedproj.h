@@ -82,15 +82,23 @@
  *    zero codes); the product is then sum_k e4m3(a) e4m3(w) in fp32, times
  *    a_scale[m] * w_scale[c].  The codes and scales live in the workspace
  *    (M * hidden + 4 M bytes of it).  hidden must be a multiple of 128, and
- *    M * hidden and N * hidden must be below 2^32.  Up to 64 tokens with
- *    hidden a multiple of 256 the product runs in the weight-streaming
- *    kernel (both operands decoded exactly to bf16 in registers), otherwise
- *    in the FP8 GEMM tiles; the results are the same up to the order of the
- *    fp32 sums.
+ *    M * hidden and N * hidden must be below 2^32.  The product runs in the
+ *    FP8 GEMM tiles, or, where the tuning table asks for the streaming
+ *    family (up to 64 tokens, hidden a multiple of the streaming chunk), in
+ *    the weight-streaming kernel with both operands decoded exactly to bf16
+ *    in registers; the results are the same up to the order of the fp32
+ *    sums.
  *  - Dtypes: act_dtype in {F32, F16, BF16}; w_dtype == act_dtype, or FP_I8 /
  *    FP_I4 / FP_MXFP4 with act_dtype FP_BF16, or FP_E4M3 with act_dtype
  *    FP_BF16 / FP_F16; out_dtype == act_dtype or FP_F32.  gamma, beta and
  *    bias are act_dtype; w_scale is fp32, except E8M0 bytes for FP_MXFP4.
+ *  - Weight layout: w is row-major [N, hidden] (4-bit: [N, hidden / 2]
+ *    bytes), or tile-packed by fused_pack_weight, which the caller states by
+ *    OR-ing FP_LAYOUT_PACKED (QKV, down and non-SwiGLU gate/up calls) or
+ *    FP_LAYOUT_PACKED_GATE_UP (the SwiGLU gate/up call) into w_dtype.  The
+ *    results do not depend on the layout (the same kernels, the same order
+ *    of sums); the packed layout lets the kernels stream a weight as long
+ *    contiguous runs.  Scales (w_scale) stay row-major.
  *  - Every pointer must be 16-byte aligned.  No output range may overlap an
  *    input range, another output, or the workspace.
  *  - Execution is asynchronous on hip_stream (NULL = the default stream);
@@ -125,6 +133,13 @@ extern "C" {
 #endif
 
 typedef FP_ENUM(fp_dtype_e) { FP_F32 = 0, FP_F16 = 1, FP_BF16 = 2, FP_I8 = 3, FP_I4 = 4, FP_E4M3 = 5, FP_MXFP4 = 6 } fp_dtype;
+/* Weight layout bits, OR'd into a call's w_dtype (and into the w_dtype of
+ * fp_workspace_bytes, fp_down_workspace_bytes and fp_describe_plan): the
+ * weight was tile-packed by fused_pack_weight with gate_up = 0 / 1.  Any
+ * other bits above the low byte are FP_E_DTYPE.  The tuning table matches on
+ * the element type alone. */
+#define FP_LAYOUT_PACKED 0x100
+#define FP_LAYOUT_PACKED_GATE_UP 0x200
 typedef FP_ENUM(fp_norm_e) { FP_NORM_NONE = 0, FP_NORM_RMS = 1, FP_NORM_LAYER = 2 } fp_norm;
 typedef FP_ENUM(fp_act_e) { FP_ACT_NONE = 0, FP_ACT_SWIGLU = 1, FP_ACT_GELU_TANH = 2 } fp_act;
 /* Codes 0-6 keep the numbering of the boundary's first specification;
@@ -292,6 +307,32 @@ fp_status fused_dequant_i4_bf16(const void *q, const float *scale, void *out_bf1
  *  aligned. */
 fp_status fused_dequant_mxfp4_bf16(const void *q, const void *scale, void *out_bf16,
                                    int64_t N, int64_t K, void *hip_stream);
+
+/* Tile-packed weights: the weight re-laid-out once, when a model is loaded,
+ * so that the projections stream it as long contiguous runs (the pages'
+ * deployment flow converts the checkpoint and re-lays the weights out for
+ * the target GPU: "TensorRT-LLM 深度工程实践…", the build workflow, step 1,
+ * weight preparation and conversion).  Measured on MI355X, a read of a
+ * 117 MB weight by 224 workgroups of 128 rows each: 4.55 TB/s in row-major
+ * 64-byte row pieces, 5.75 TB/s as packed runs.
+ *
+ * fused_pack_weight reads w, row-major [n_rows, K] elements of w_dtype
+ * (F16, BF16, I8, E4M3: K elements per row; I4, MXFP4: K / 2 bytes), and
+ * writes the same bytes to w_packed in this order: rows in groups of 128 --
+ * with gate_up = 1 (weights of the SwiGLU call, n_rows = 2 * ffn: gate rows
+ * [0, ffn), up rows [ffn, 2 ffn)) group t is gate rows 64 t .. 64 t + 63
+ * followed by up rows ffn + 64 t .. ffn + 64 t + 63 -- and a group is stored
+ * as its 64-byte K slices in order, each as its eight 16-row blocks in
+ * order, 1 KB per block slice, in which byte 256 g + 16 i + j is byte
+ * 64 s + 16 g + j of the block's row i (s: the slice, g < 4, i < 16,
+ * j < 16).  Requires rows of a multiple of 64 bytes and n_rows a multiple of
+ * 128 (gate_up: ffn a multiple of 64), both pointers 16-byte aligned and not
+ * overlapping; FP_E_DTYPE for FP_F32.  fused_unpack_weight is the inverse.
+ * Asynchronous on hip_stream; the caller owns both buffers. */
+fp_status fused_pack_weight(const void *w, void *w_packed, int64_t n_rows, int64_t K, fp_dtype w_dtype,
+                            int32_t gate_up, void *hip_stream);
+fp_status fused_unpack_weight(const void *w_packed, void *w, int64_t n_rows, int64_t K, fp_dtype w_dtype,
+                              int32_t gate_up, void *hip_stream);
 
 /* Which kernel a call with these sizes would launch, and how: writes a
  * NUL-terminated line such as

@@ -257,9 +257,15 @@ def test_fp8_plans(plan_override):
     p = _plan(1, 4096, 6144, w=e)
     assert p["splits"] == 4 and p["grid"] == 24 * 4            # each split streams 256 KB of weights
     assert fra.workspace_bytes(32, 4096, 28672, torch.bfloat16, e) >= 112 * 2 * 32 * 256 * 4
-    # the weight-streaming kernel on the codes when requested (up to 64
-    # tokens, hidden a multiple of the chunk), with the weight rows per
-    # workgroup and grid of int8 weights (one byte per weight as well)
+    # the weight-streaming kernel on the codes for tile-packed weights or
+    # when requested (up to 64 tokens, hidden a multiple of the chunk), with
+    # the weight rows per workgroup and grid of int8 weights (one byte per
+    # weight as well)
+    p = fra.describe_plan(32, 4096, 28672, torch.bfloat16, e, "swiglu", layout="packed_gate_up")
+    assert p["kernel"] == "stream_kernel<bf16-e4m3,m32,n128,k256,swiglu>" and p["grid"] == 224, p
+    assert fra.describe_plan(200, 4096, 6144, torch.bfloat16, e, layout="packed")["kernel"].startswith("gemm8")
+    with fra.plan_override(fp8_tile=32):
+        assert fra.describe_plan(32, 4096, 6144, torch.bfloat16, e, layout="packed")["kernel"].startswith("gemm8")
     try:
         for M, N, sw in ((1, 6144, False), (32, 28672, True), (64, 6144, False), (64, 57344, True), (40, 768, False)):
             fn = "swiglu" if sw else "none"
@@ -301,6 +307,68 @@ def test_fp8_plans(plan_override):
         assert p["splits"] == 3 and p["kernel"] == "gemm8_kernel<bf16,128x128,linear>"
     with fra.plan_override(splits=3, fp8_tile=256):
         assert _plan(1, 4096, 6144, w=e)["splits"] == 1      # the 256 x 256 kernel does not split K
+
+
+PK, PKGU = 0x100, 0x200     # FP_LAYOUT_PACKED, FP_LAYOUT_PACKED_GATE_UP
+
+
+def test_packed_layout_rejects():
+    # QKV of Llama-3-8B: 6144 rows, packable
+    assert qkv(M=0, wdt=BF16 | PK)[0] == "FP_OK"
+    assert qkv(M=32, wdt=BF16 | PK, ws=FAKE + 0x7000000, ws_bytes=1 << 30)[0] != "FP_E_SHAPE"
+    assert qkv(wdt=BF16 | PKGU)[0] == "FP_E_SHAPE"           # the gate/up pairing is for the SwiGLU call
+    assert qkv(wdt=BF16 | 0x400)[0] == "FP_E_DTYPE"          # unknown layout bits
+    assert qkv(wdt=BF16 | PK | PKGU)[0] == "FP_E_DTYPE"
+    assert qkv(act=F32, odt=F32, wdt=F32 | PK)[0] == "FP_E_DTYPE"
+    assert qkv(H=5, Hkv=1, D=48, hidden=4096, wdt=BF16 | PK)[0] == "FP_E_SHAPE"   # 336 rows
+    assert qkv(hidden=4096, wdt=I4 | PK)[0] == "FP_E_NULL"   # (scales checked first) int4 packs
+    # SwiGLU: gate/up pairs of whole 64-row halves; plain packing also taken
+    assert gu(wdt=BF16 | PKGU)[0] == "FP_OK"
+    assert gu(wdt=BF16 | PK)[0] == "FP_OK"
+    assert gu(ffn=14336 + 32, wdt=BF16 | PKGU)[0] == "FP_E_SHAPE"
+    assert gu(act=2, ffn=1024, wdt=BF16 | PKGU)[0] == "FP_E_SHAPE"    # GELU: no pairing
+    assert gu(act=2, ffn=1024, wdt=BF16 | PK)[0] == "FP_OK"
+    assert gu(act=2, ffn=1040, wdt=BF16 | PK)[0] == "FP_E_SHAPE"      # 1040 rows
+    L = lib()
+    assert L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16 | 0x400) == 0
+    assert L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16 | PK) == L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16)
+
+
+def test_pack_weight_rejects():
+    L = lib()
+    f, g = L.fused_pack_weight, L.fused_unpack_weight
+    S = lambda st: _lib.STATUS[st]
+    for fn in (f, g):
+        assert S(fn(FAKE, FAKE + 0x1000000, 0, 64, BF16, 0, None)) == "FP_OK"           # nothing to do
+        assert S(fn(FAKE, FAKE + 0x1000000, 100, 64, BF16, 0, None)) == "FP_E_SHAPE"    # rows % 128
+        assert S(fn(FAKE, FAKE + 0x1000000, 128, 16, BF16, 0, None)) == "FP_E_SHAPE"    # 32-byte rows
+        assert S(fn(FAKE, FAKE + 0x1000000, 128, 64, I4, 0, None)) == "FP_E_SHAPE"      # 32-byte int4 rows
+        assert S(fn(FAKE, FAKE + 0x1000000, 192, 64, BF16, 1, None)) == "FP_E_SHAPE"    # ffn 96
+        assert S(fn(FAKE, FAKE + 0x1000000, 128, 64, F32, 0, None)) == "FP_E_DTYPE"
+        assert S(fn(FAKE, FAKE + 0x1000000, 128, 64, BF16, 2, None)) == "FP_E_ARG"
+        assert S(fn(None, FAKE + 0x1000000, 128, 64, BF16, 0, None)) == "FP_E_NULL"
+        assert S(fn(FAKE, FAKE + 0x1000008, 128, 64, BF16, 0, None)) == "FP_E_ALIGN"
+        assert S(fn(FAKE, FAKE + 0x100, 128, 64, BF16, 0, None)) == "FP_E_ALIAS"        # 16 KB each
+
+
+def test_packed_plans(plan_override):
+    plan_override()
+    b = torch.bfloat16
+    # the same kernel and grid as row-major weights; the tiled family unpacks first
+    for M, K, N, fn in ((32, 4096, 28672, "swiglu"), (32, 4096, 6144, "none"), (16384, 4096, 22016, "swiglu"),
+                        (300, 4096, 6144, "none")):
+        lay = "packed_gate_up" if fn == "swiglu" else "packed"
+        a, r = fra.describe_plan(M, K, N, b, b, fn, layout=lay), fra.describe_plan(M, K, N, b, b, fn)
+        assert a == r, (a, r)
+    p = fra.describe_plan(40, 320, 6144, b, b, layout="packed")
+    assert p["family"] == "tiled" and p["prep"] == "unpack_kernel"
+    assert p["workspace"] >= fra.describe_plan(40, 320, 6144, b, b)["workspace"] + 6144 * 320 * 2
+    p = fra.describe_plan(40, 512, 1024, b, torch.uint8, "swiglu", layout="packed_gate_up")
+    assert p["family"] == "stream" and "prep" not in p
+    with fra.plan_override(no_stream=1):
+        p = fra.describe_plan(40, 512, 1024, b, torch.uint8, "swiglu", layout="packed_gate_up")
+        assert p["family"] == "tiled" and p["prep"] == "unpack_kernel+dequant_i4_kernel", p
+        assert fra.workspace_bytes(40, 512, 1024, b, torch.uint8, "packed_gate_up") >= 1024 * 256 + 1024 * 512 * 2
 
 
 def test_binding_refuses_cpu_tensors():
