@@ -203,12 +203,15 @@ void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool q
     // 0.3 % of the decode step with them streamed from HBM; the gate/up of
     // Llama-2-70B's 8-way shard, 56 tiles, s = 4: 24.6 -> 23.4 us;
     // Llama-2-70B int8 gate/up, 224 tiles of 470 MB, 6 % slower so; an
-    // uneven 1/s of K, 32 chunks in 3, 1 us slower)
+    // uneven 1/s of K, 32 chunks in 3, 1 us slower; Llama-3-8B QKV on
+    // tile-packed weights, s = 2 of 64-row tiles (bf16) or s = 4 of 128-row
+    // tiles (E4M3) on 192 workgroups: 1.5 / 3.0 us faster than stream-K over
+    // 256, hence the three quarters)
     const int64_t wbytes = (wdt == FP_I4 || wdt == FP_MXFP4) ? Nw * K / 2
                            : Nw * K * ((wdt == FP_I8 || wdt == FP_E4M3) ? 1 : 2);
     if (wbytes <= (int64_t(256) << 20) && tiles > 0) {
         for (int64_t s = target / tiles < ksteps / minc ? target / tiles : ksteps / minc; s >= 1; --s) {
-            if (tiles * s * 100 < target * 85) break;
+            if (tiles * s * 100 < target * 75) break;
             if (ksteps % s == 0) {
                 G = tiles * s;
                 break;
@@ -336,10 +339,10 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     }
     const bool w4 = wdt == FP_I4 || wdt == FP_MXFP4;   // 4-bit weights, [N, K/2] bytes
     const fp_dtype wdt_stored = wdt;
-    const bool stream_elig = act != FP_F32 && M <= 64 && K % 256 == 0;
+    const size_t rows_bytes = form_rows ? align256((size_t)M * (size_t)K * 2) : 0;
+    const bool stream_elig = act != FP_F32 && M <= 64 && K % 256 == 0 && rows_bytes <= ws_cap;
     const bool prefill_elig = act != FP_F32 && M * K * 2 < (int64_t(1) << 32) && Nw * K * 2 < (int64_t(1) << 32);
     const int64_t tiles256 = ((M + 255) / 256) * (swiglu ? (Nw / 2 + 127) / 128 : (Nw + 255) / 256);
-    const size_t rows_bytes = form_rows ? align256((size_t)M * (size_t)K * 2) : 0;
     const bool g16_elig = prefill_elig && wdt == act && rows_bytes <= ws_cap;
     int fam;
     if (kb.family == 0 || (kb.family == 1 && stream_elig) || (kb.family == 2 && prefill_elig) ||
@@ -425,8 +428,16 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     }
 
     size_t off = 0;
-    p.stats_off = off;
-    off = align256(off + (size_t)M * 8);
+    if (p.family == 1 && form_rows) {
+        // the streaming kernel reads the rows the row pass forms (normalised,
+        // in the activation dtype) instead of normalising in every workgroup
+        p.rows = true;
+        p.rows_off = off;
+        off += rows_bytes;
+    } else {
+        p.stats_off = off;
+        off = align256(off + (size_t)M * 8);
+    }
     p.ctr_off = off;
     if (p.slots > 1) off = align256(off + (size_t)tiles * 4);
     p.part_off = off;
@@ -718,11 +729,30 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     if (plan.family == 4) return run_gemm16(c, plan, pa);
     char *ws = (char *)c.ws;
     const int act = act_code(c.act);
-    float2 *stats = c.norm != FP_NORM_NONE ? (float2 *)(ws + plan.stats_off) : nullptr;
+    float2 *stats = c.norm != FP_NORM_NONE && !plan.rows ? (float2 *)(ws + plan.stats_off) : nullptr;
     unsigned *ctr = plan.slots > 1 ? (unsigned *)(ws + plan.ctr_off) : nullptr;
     const int n_ctr = plan.slots > 1 ? plan.tiles_m * plan.tiles_n : 0;
 
-    if (stats || c.h_out || n_ctr) {
+    if (plan.rows) {
+        // the row pass: h_out, the normalised rows (the A operand), and the
+        // split-K counters cleared
+        fp::StatsArgs sa{};
+        sa.x = c.x;
+        sa.res = c.residual;
+        sa.h_out = c.h_out;
+        sa.norm = (int)c.norm;
+        sa.eps = c.eps;
+        sa.M = c.M;
+        sa.K = c.K;
+        sa.counters = ctr;
+        sa.n_counters = n_ctr;
+        sa.gamma = c.gamma;
+        sa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
+        sa.rows = ws + plan.rows_off;
+        ProfScope ps(fp::norm_kernel_name(act), c.stream);
+        hipError_t e = fp::launch_norm(act, sa, c.stream);
+        if (e != hipSuccess) return hip_fail(e, "norm_kernel launch");
+    } else if (stats || c.h_out || n_ctr) {
         fp::StatsArgs sa;
         sa.x = c.x;
         sa.res = c.residual;
@@ -738,12 +768,12 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
         hipError_t e = fp::launch_stats(act, sa, c.stream);
         if (e != hipSuccess) return hip_fail(e, "stats_kernel launch");
     }
-    pa.x = c.x;
-    pa.res = c.residual;
+    pa.x = plan.rows ? (const void *)(ws + plan.rows_off) : c.x;
+    pa.res = plan.rows ? nullptr : c.residual;
     pa.stats = stats;
     pa.gamma = c.gamma;
     pa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
-    pa.norm = (int)c.norm;
+    pa.norm = plan.rows ? 0 : (int)c.norm;
     pa.w = c.w;
     pa.w_layout = c.wl;
     pa.w_scale = (const float *)c.w_scale;
@@ -1179,9 +1209,12 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
                                      : fp::proj_kernel_name(a, wi8, p.tile, epi);
     const int64_t grid = p.family == 1 ? p.grid : (int64_t)p.tiles_m * p.tiles_n * p.splits;
     const char *deq = !p.deq ? "" : w_dtype == FP_MXFP4 ? "dequant_mxfp4_kernel" : "dequant_i4_kernel";
-    snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s%s%s%s", fam, name,
-             (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total,
-             p.unpack || p.deq ? " prep=" : "", p.unpack ? "unpack_kernel" : "", p.unpack && p.deq ? "+" : "", deq);
+    char prep[96] = "";
+    if (p.rows) snprintf(prep, sizeof prep, " prep=%s", fp::norm_kernel_name(a));
+    else if (p.unpack || p.deq)
+        snprintf(prep, sizeof prep, " prep=%s%s%s", p.unpack ? "unpack_kernel" : "", p.unpack && p.deq ? "+" : "", deq);
+    snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s", fam, name,
+             (long long)grid, p.splits, p.slots, M == 0 ? (size_t)0 : p.total, prep);
     return FP_OK;
 }
 

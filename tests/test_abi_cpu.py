@@ -202,9 +202,10 @@ def test_dequant_i4_rejects():
 def test_int4_plans(plan_override):
     plan_override()
     u8 = torch.uint8
-    # decode token counts, hidden a multiple of 256: streamed, dequantised in registers
+    # decode token counts, hidden a multiple of 256: streamed, dequantised in
+    # registers (the row pass forms the normalised rows)
     p = _plan(16, 8192, 57344, w=u8, fn="swiglu")
-    assert p["kernel"] == "stream_kernel<bf16-i4w,m16,n128,k256,swiglu>" and "prep" not in p
+    assert p["kernel"] == "stream_kernel<bf16-i4w,m16,n128,k256,swiglu>" and p["prep"] == "norm_kernel<bf16>"
     assert _plan(64, 8192, 57344, w=u8, fn="swiglu")["kernel"] == "stream_kernel<bf16-i4w,m64,n256,k128,swiglu>"
     # more than 64 tokens: the 128 x 512 kernel, dequantised in registers too
     p = _plan(256, 8192, 57344, w=u8, fn="swiglu")
@@ -222,7 +223,7 @@ def test_mxfp4_plans_and_rejections(plan_override):
     mx = torch.float4_e2m1fn_x2
     # decode token counts, hidden a multiple of 256: streamed, dequantised in registers
     p = _plan(16, 8192, 57344, w=mx, fn="swiglu")
-    assert p["kernel"] == "stream_kernel<bf16-mxfp4w,m16,n128,k256,swiglu>" and "prep" not in p
+    assert p["kernel"] == "stream_kernel<bf16-mxfp4w,m16,n128,k256,swiglu>" and p["prep"] == "norm_kernel<bf16>"
     assert _plan(64, 8192, 57344, w=mx, fn="swiglu")["kernel"] == "stream_kernel<bf16-mxfp4w,m64,n256,k128,swiglu>"
     # more than 64 tokens: the 128 x 512 kernel, any hidden that is a multiple of 64
     p = _plan(256, 8192, 10240, w=mx)
@@ -364,7 +365,7 @@ def test_packed_plans(plan_override):
     assert p["family"] == "tiled" and p["prep"] == "unpack_kernel"
     assert p["workspace"] >= fra.describe_plan(40, 320, 6144, b, b)["workspace"] + 6144 * 320 * 2
     p = fra.describe_plan(40, 512, 1024, b, torch.uint8, "swiglu", layout="packed_gate_up")
-    assert p["family"] == "stream" and "prep" not in p
+    assert p["family"] == "stream" and p["prep"] == "norm_kernel<bf16>"
     with fra.plan_override(no_stream=1):
         p = fra.describe_plan(40, 512, 1024, b, torch.uint8, "swiglu", layout="packed_gate_up")
         assert p["family"] == "tiled" and p["prep"] == "unpack_kernel+dequant_i4_kernel", p
@@ -397,10 +398,10 @@ def test_plan_routing_families(plan_override):
     # the same tile count on a 470 MB weight: stream-K over 256 workgroups
     p = _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")
     assert p["grid"] == 256 and p["slots"] >= 2
-    # 16-bit QKV weights at up to 32 tokens: 64-row tiles (96 of them), stream-K
-    # over 256 workgroups
+    # 16-bit QKV weights at up to 32 tokens: 64-row tiles (96 of them), two
+    # workgroups per tile (192: at least three quarters of the CUs)
     p = _plan(32, 4096, 6144)
-    assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear>" and p["grid"] == 256 and p["slots"] >= 2
+    assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear>" and p["grid"] == 192 and p["slots"] == 2
     # 33..64 tokens keep 128-row tiles
     assert _plan(64, 4096, 6144)["kernel"] == "stream_kernel<bf16,m64,n128,k128,linear>"
     # Llama-2-70B's 8-way shard: QKV (10 tiles x 32 chunks) on 160 workgroups of

@@ -59,7 +59,7 @@ def test_int4_small(cfg, native):
     print(f"int4 {wl.name} {plan['kernel']} {plan.get('prep', '')} native={native}", flush=True)
     stream = wl.M <= 64 and wl.hidden % 256 == 0
     assert (plan["family"] == "stream") == stream
-    assert ("prep" in plan) == (plan["family"] == "tiled")        # staged only for the tiled kernel
+    assert ("dequant" in plan.get("prep", "")) == (plan["family"] == "tiled")   # staged only for the tiled kernel
     q, k, v, h = run_qkv(wl, d, odt)
     out = run_gu(wl, d, odt)
     torch.cuda.synchronize()

@@ -19,7 +19,7 @@ import torch
 import oracle
 import fusion_residual_add_amd as fra
 from fusion_residual_add_amd import inputs
-from test_gpu_parity import DEV, TDT, check, small, to_dev
+from test_gpu_parity import DEV, TDT, check, small, to_dev, _sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -131,6 +131,10 @@ def test_packed_calls(case, table, plan_override):
         plan_override(stream_nr=4)
     if fam == "fp8-256":
         plan_override(fp8_tile=256)
+    if fam == "fp8":
+        # the FP8 tiles for both layouts (packed decode shapes default to the
+        # streaming kernel, checked against the oracle below)
+        plan_override(no_stream=1)
     inp = inputs.generate(wl, seed=21, parts=("qkv", "gu", "down"))
     d = to_dev(inp)
     a_dt, w_dt = TDT[act], WDT[wdt]
@@ -154,6 +158,15 @@ def test_packed_calls(case, table, plan_override):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name}: packed result differs"
     rg = oracle.workload_gateup(wl, inp)
     check("out", pk[3], rg["out"])
+    if fam == "fp8":
+        plan_override()
+        dflt = _run(wl, d, fra.pack_weight(d["w_qkv"]), fra.pack_weight(d["w_gu"], gate_up=sw),
+                    fra.pack_weight(d["w_down"]))
+        torch.cuda.synchronize()
+        rq = oracle.workload_qkv(wl, inp)
+        check("q", dflt[0], rq["q"])
+        check("v", dflt[2], rq["v"])
+        check("out", dflt[3], rg["out"])
 
 
 def test_packed_layout_mismatch():
@@ -170,11 +183,17 @@ def test_packed_layout_mismatch():
 
 
 @pytest.mark.parametrize("name", ["llama3-8b-decode", "llama3-8b-decode-fp8", "llama2-7b-prefill"])
-def test_packed_full_size(name):
-    """The workloads at full size: packed and row-major results bit for bit."""
+def test_packed_full_size(name, plan_override):
+    """The workloads at full size: packed and row-major results bit for bit
+    on the same kernels; FP8 decode, whose packed default is the streaming
+    kernel, then also against the oracle on sampled rows."""
     wl = inputs.workload(name)
-    d = to_dev(inputs.generate(wl, seed=5))
+    inp = inputs.generate(wl, seed=5)
+    d = to_dev(inp)
     sw = wl.act_fn == "swiglu"
+    fp8 = wl.wdt == "e4m3"
+    if fp8:
+        plan_override(no_stream=1)
 
     def both(w_qkv, w_gu):
         q, k, v, _ = fra.fused_add_norm_qkv(d["x"], d["r"], d["gamma"], w_qkv, wl.n_heads, wl.n_kv_heads,
@@ -185,7 +204,19 @@ def test_packed_full_size(name):
         return q.clone(), out.clone()
 
     a = both(d["w_qkv"], d["w_gu"])
-    b = both(fra.pack_weight(d["w_qkv"]), fra.pack_weight(d["w_gu"], gate_up=sw))
+    pq, pg = fra.pack_weight(d["w_qkv"]), fra.pack_weight(d["w_gu"], gate_up=sw)
+    b = both(pq, pg)
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+    if fp8:
+        plan_override()
+        assert fra.describe_plan(wl.M, wl.hidden, wl.n_gu, torch.bfloat16, torch.float8_e4m3fn, "swiglu",
+                                 layout="packed_gate_up")["kernel"].startswith("stream_kernel")
+        q, out = both(pq, pg)
+        torch.cuda.synchronize()
+        rows = _sample_rows(wl.M, 8)
+        rq = oracle.workload_qkv(wl, inp, row_idx=rows)
+        rg = oracle.workload_gateup(wl, inp, row_idx=rows)
+        check("q", q[rows], rq["q"])
+        check("out", out[rows], rg["out"])

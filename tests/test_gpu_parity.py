@@ -521,3 +521,33 @@ def test_qkv_head_major(cfg, native):
     for a, b in ((q, qt), (k, kt), (v, vt)):
         assert torch.equal(a.transpose(0, 1).contiguous().view(torch.int8), b.contiguous().view(torch.int8))
     assert np.array_equal(h.double().cpu().numpy(), rq["h_out"])
+
+
+# ---------------------------------------------------------------------------
+# the row pass of the decode path: the streaming kernel's A operand
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [dict(M=1, hidden=512), dict(M=32, hidden=768, norm="layer"),
+                                 dict(M=64, hidden=512, act="f16"), dict(M=17, hidden=1024, norm="none"),
+                                 dict(M=9, hidden=512, wdt="i8")],
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_stream_rows(cfg):
+    """The rows the row pass leaves at the start of the workspace of a
+    streaming call, bit for bit against the oracle's rows of the
+    single-precision reading (they are the kernel's A operand as they are)."""
+    wl = small(**cfg)
+    inp = inputs.generate(wl, seed=17)
+    d = to_dev(inp)
+    act = TDT[wl.act]
+    wdt = d["w_gu"].dtype
+    plan = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, act, wdt, wl.act_fn)
+    assert plan["family"] == "stream" and plan["prep"].startswith("norm_kernel"), plan
+    need = fra.workspace_bytes(wl.M, wl.hidden, wl.n_gu, act, wdt)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    out = fra.fused_gateup_act(d["x"], d["r"], d["gamma"], d["w_gu"], wl.ffn, wl.act_fn, beta=d.get("beta"),
+                               norm=wl.norm, eps=wl.eps, w_scale=d.get("s_gu"), out_dtype=torch.float32,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    rows = ws[:wl.M * wl.hidden * 2].view(act).reshape(wl.M, wl.hidden)
+    _, _, a_ref = oracle.add_norm(inp["x"], inp["r"], inp["gamma"], inp.get("beta"), wl.norm, wl.eps)
+    assert np.array_equal(rows.double().cpu().numpy(), a_ref), "normalised rows not bit-exact"
+    check("out", out, oracle.workload_gateup(wl, inp)["out"])
