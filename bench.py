@@ -360,16 +360,17 @@ def profile_call(runner, call: str, n: int):
     return {k: t / c for k, (c, t) in prof.items()}
 
 
-def load_traffic(kernel_key: str):
+def load_traffic(kernel_key: str, layout: str = "packed"):
     """HBM traffic per launch measured with rocprofv3 counters (profiles/traffic.json),
-    valid only while the kernel sources are unchanged since the counters were taken."""
+    valid only while the kernel sources are unchanged since the counters were taken
+    and for the weight layout they were taken on."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash() or d.get("layout", "rows") != layout:
         return None
     ent = d.get("kernels", {}).get(kernel_key)
     return None if ent is None else ent.get("bytes_per_launch")
@@ -409,7 +410,7 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::norm_kernel<(\d), \d+, \d+>", cxx)
     if m:
         return f"norm_kernel<{_ACT[m.group(1)]}>"
-    m = re.search(r"fp::gemm16_kernel<(\d), (\d), (\d)>", cxx)
+    m = re.search(r"fp::gemm16_kernel<(\d), (\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         return f"gemm16_kernel<{_ACT[m.group(1)]},256x256,{m.group(3)}st,{_EPI[m.group(2)]}>"
     m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), (\d), (\d)>", cxx)
@@ -481,7 +482,7 @@ def _counter_rows(d: str):
     return per
 
 
-def traffic_summarize(wl_name: str, fetch_dir: str, write_dir: str, cmds: str) -> None:
+def traffic_summarize(wl_name: str, fetch_dir: str, write_dir: str, cmds: str, layout: str = "packed") -> None:
     """profiles/traffic.json and a text summary from the two counter runs of --traffic-probe."""
     import statistics
     fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
@@ -501,13 +502,13 @@ def traffic_summarize(wl_name: str, fetch_dir: str, write_dir: str, cmds: str) -
         kernels[f"{wl_name}:{lib}"] = {"bytes_per_launch": round(f_b + w_b), "fetch_bytes": round(f_b),
                                        "write_bytes": round(w_b), "launches": len(fetch[name])}
         lines.append(f"| `{lib}` | {len(fetch[name])} | {f_b / 1e6:.2f} | {w_b / 1e6:.2f} | {(f_b + w_b) / 1e6:.2f} |")
-    out = {"source_hash": kernel_source_hash(), "workload": wl_name,
+    out = {"source_hash": kernel_source_hash(), "workload": wl_name, "layout": layout,
            "calibration": {"kernel": cal[0], "bytes_each_way": calib, "fetch_factor": round(kf, 4),
                            "write_factor": round(kw, 4)},
            "kernels": kernels}
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
-    md = [f"# HBM traffic per launch, {wl_name}", "",
+    md = [f"# HBM traffic per launch, {wl_name} ({layout} weights)", "",
           "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, L2 to memory), one rocprofv3 run each,",
           "scaled by what they read for an elementwise pass that reads and writes 1 GiB",
           f"(fetch factor {kf:.4f}, write factor {kw:.4f}).", "",
@@ -822,8 +823,9 @@ def main():
     ap.add_argument("--workload", default="llama3-8b-decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--layout", choices=("rows", "packed"), default="rows",
-                    help="weight layout the fused calls read: row-major, or tile-packed once at load")
+    ap.add_argument("--layout", choices=("rows", "packed"), default="packed",
+                    help="weight layout the fused calls read: tile-packed once at load (fused_pack_weight, as a "
+                         "deployment converts its checkpoint) or row-major")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra timed runs of --steps steps each, for the median / p10 / p90 spread")
@@ -851,7 +853,7 @@ def main():
                          "--out) before timing; the default is the built-in planner")
     args = ap.parse_args()
     if args.traffic_summarize:
-        traffic_summarize(args.workload, *args.traffic_summarize, args.cmd)
+        traffic_summarize(args.workload, *args.traffic_summarize, args.cmd, args.layout)
         return
     if args.trace_summarize:
         trace_summarize(*args.trace_summarize, args.cmd)
@@ -924,7 +926,7 @@ def main():
     roof["kernel"] = gu_kernel
     roof["kernel_avg_us"] = round(gu_ms * 1e3, 2)
     roof["algo_bytes_per_launch"] = algo_bytes(wl, "gu")
-    roof["traffic"] = load_traffic(f"{wl.name}:{gu_kernel}")
+    roof["traffic"] = load_traffic(f"{wl.name}:{gu_kernel}", args.layout)
     unfused = None
     if wl.wdt == wl.act:
         ums = time_steps(run.unfused, args.steps, args.warmup)

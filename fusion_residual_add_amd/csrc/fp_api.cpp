@@ -170,16 +170,18 @@ void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool q
     // normalises is then amortised over twice the weight rows; measured on
     // MI355X: Llama-2-70B gate/up at 64 tokens 232 -> 186 us, while fewer
     // rows per workgroup stay faster at 1 and 16 tokens and for QKV)
-    // 16-bit weights without the gate/up pairing at up to 32 tokens: 64
-    // rows, so that more workgroups share the (smaller) weight (measured on
-    // MI355X: Llama-3-8B QKV 1.1 us faster per call; with int8 weights, or
-    // at 33..64 tokens where the A tile is four times as large, 64-row
-    // tiles are slower)
+    // 16-bit and E4M3 weights without the gate/up pairing at up to 32
+    // tokens: 64 rows, so that more workgroups share the (smaller) weight
+    // (measured on MI355X: Llama-3-8B QKV 1.1 us faster per call, E4M3 on
+    // packed weights 2 us; with int8 weights, or at 33..64 tokens where the
+    // A tile is four times as large, 64-row tiles are slower)
     p.sc.nr = qw && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
-    if (!swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
-    // requested rows: only the instantiated forms (64 for 16-bit weights
-    // without the gate/up pairing at up to 32 tokens, 256 for quantised weights)
-    if (kb.rows == 64 && !swiglu && !qw && p.sc.mf <= 2) p.sc.nr = 1;
+    const bool nr1_ok = !swiglu && (!qw || wdt == FP_E4M3) && p.sc.mf <= 2;   // the instantiated 64-row forms
+    if (nr1_ok) p.sc.nr = 1;
+    // requested rows: only the instantiated forms (64 for 16-bit and E4M3
+    // weights without the gate/up pairing at up to 32 tokens, 256 for
+    // quantised weights)
+    if (kb.rows == 64 && nr1_ok) p.sc.nr = 1;
     if (kb.rows == 128 || (kb.rows == 256 && qw)) p.sc.nr = (int)(kb.rows / 64);
     p.sc.u = stream_chunk(M) / 32;   // K chunk 32 * u: must match the launcher
     const int nb = 64 * p.sc.nr;

@@ -29,6 +29,14 @@
 // For SwiGLU the weight rows of a tile are 128 gate rows and the 128
 // matching up rows, and each wave holds gate and up fragments of the same
 // columns, so SiLU(g) * u is formed in registers.
+// Tile-packed weights (PK): the B tile of a stage is the stage's 64-byte K
+// slices of the tile's 16-row blocks, 1 KB each and contiguous in the
+// weight, so one wave load copies one of them as it is and the B tile keeps
+// the packed order in LDS (block, slice, 16-byte group, row): the 16 lanes of
+// a fragment read (16 rows, one 16-byte group) then read 256 contiguous
+// bytes, no swizzle needed.  (Loading the packed weight into the row-major
+// tile instead makes each load gather 16-byte pieces: measured 37 % slower
+// on Llama-2-7B prefill, at the same L2 request count.)
 #include "fp_device.hpp"
 
 #include <cstdio>
@@ -67,13 +75,14 @@ template <int NST> struct Geo {
 };
 }  // namespace g16
 
-template <int ACT, int EPI, int NST>
+template <int ACT, int EPI, int NST, bool PK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm16_kernel(ProjArgs p) {
     using T = Act<ACT>;
     using namespace g16;
     using G = Geo<NST>;
     constexpr int ROWB = G::ROWB, TILE = G::TILE, STAGE = G::STAGE, NI = G::NI, RPI = G::RPI, KS = G::KS;
+    constexpr int SPS = ROWB / 64;   // packed B: 64-byte K slices per stage
     constexpr bool SW = EPI == EPI_SWIGLU;
     static_assert(ACT != ACT_F32, "16-bit operands");
     static_assert(NST == 2 || NST == 4 || NST == 5, "two stages of K 64 (an even number of them), or four / five of K 32");
@@ -125,17 +134,29 @@ void gemm16_kernel(ProjArgs p) {
         ma = ma < p.M ? ma : p.M - 1;
         a_off[i] = (uint32_t)(ma * p.K * 2) + gc * 16;
         int64_t wr;
-        if constexpr (SW) wr = r < BN / 2 ? (int64_t)tn * (BN / 2) + r : p.F + (int64_t)tn * (BN / 2) + (r - BN / 2);
-        else wr = (int64_t)tn * BN + r;
-        wr = wr < p.Nw ? wr : p.Nw - 1;
-        b_off[i] = (uint32_t)weight_off(p.w_layout, wr, gc * 16, p.F, p.K * 2);
+        if constexpr (PK) {
+            // instruction i of wave w: block slice q = NI w + i of the stage
+            // (16-row block q / SPS of the tile, slice q % SPS); a block past
+            // the weight reads its last block (packed weights have whole
+            // 128-row groups, so blocks are whole)
+            const int q = NI * wave + i, br = 16 * (q / SPS);
+            if constexpr (SW) wr = br < BN / 2 ? (int64_t)tn * (BN / 2) + br : p.F + (int64_t)tn * (BN / 2) + (br - BN / 2);
+            else wr = (int64_t)tn * BN + br;
+            wr = wr < p.Nw ? wr : p.Nw - 16;
+            b_off[i] = (uint32_t)(packed_row_off(wr, p.F, p.K * 2, p.w_layout) + (q % SPS) * 8192) + lane * 16;
+        } else {
+            if constexpr (SW) wr = r < BN / 2 ? (int64_t)tn * (BN / 2) + r : p.F + (int64_t)tn * (BN / 2) + (r - BN / 2);
+            else wr = (int64_t)tn * BN + r;
+            wr = wr < p.Nw ? wr : p.Nw - 1;
+            b_off[i] = (uint32_t)weight_off(p.w_layout, wr, gc * 16, p.F, p.K * 2);
+        }
     }
     // stage kt: row bytes kt * ROWB of both operands, added as the scalar
     // offset (tile-packed weights: that byte's offset in the packed layout,
     // additive since ROWB is a multiple of 64)
     auto issue = [&](int kt, unsigned char *st) __attribute__((always_inline)) {
         const uint32_t soff = (uint32_t)kt * ROWB;
-        const uint32_t wsoff = p.w_layout ? (uint32_t)packed_col_off(soff) : soff;
+        const uint32_t wsoff = PK || p.w_layout ? (uint32_t)packed_col_off(soff) : soff;
 #pragma unroll
         for (int i = 0; i < NI; ++i) load_lds16(ra, st + (NI * wave + i) * 1024, a_off[i], soff);
 #pragma unroll
@@ -156,14 +177,22 @@ void gemm16_kernel(ProjArgs p) {
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
         va[t] = 128 * wm * ROWB + fr * ROWB + (((2 * t + kh) ^ lsw) << 4);
-        vb[t] = TILE + wnb + fr * ROWB + (((2 * t + kh) ^ lsw) << 4);
+        if constexpr (PK) {
+            // packed B tile: tile row R, 16-byte chunk c at
+            // ((R / 16) SPS + c / 4) KB + 256 (c % 4) + 16 (R % 16)
+            const int c = 2 * t + kh, rw = (SW ? 64 : 128) * wn + fr;
+            vb[t] = TILE + (((rw >> 4) * SPS + (c >> 2)) << 10) + ((c & 3) << 8) + ((fr & 15) << 4);
+        } else {
+            vb[t] = TILE + wnb + fr * ROWB + (((2 * t + kh) ^ lsw) << 4);
+        }
     }
     auto frag_a = [&](const unsigned char *st, int f, int t) __attribute__((always_inline)) {
         return *(const u32x4 *)(st + va[t] + f * 32 * ROWB);
     };
     auto frag_b = [&](const unsigned char *st, int f, int t) __attribute__((always_inline)) {
         const int rb = SW ? (f < 2 ? 32 * f : BN / 2 + 32 * (f - 2)) : 32 * f;
-        return *(const u32x4 *)(st + vb[t] + rb * ROWB);
+        // rb is a multiple of 32: whole 16-row blocks either way
+        return *(const u32x4 *)(st + vb[t] + (PK ? (rb >> 4) * SPS * 1024 : rb * ROWB));
     };
 
     f32x16 acc[4][4];
@@ -388,14 +417,19 @@ void gemm16_kernel(ProjArgs p) {
     }
 }
 
+template <int ACT, int NST, bool PK>
+static hipError_t launch_gemm16_e(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    switch (a.epi) {
+    case EPI_QKV:    return launch_k(gemm16_kernel<ACT, EPI_QKV, NST, PK>, grid, s, a);
+    case EPI_SWIGLU: return launch_k(gemm16_kernel<ACT, EPI_SWIGLU, NST, PK>, grid, s, a);
+    case EPI_GELU:   return launch_k(gemm16_kernel<ACT, EPI_GELU, NST, PK>, grid, s, a);
+    default:         return launch_k(gemm16_kernel<ACT, EPI_LINEAR, NST, PK>, grid, s, a);
+    }
+}
+
 template <int ACT, int NST>
 static hipError_t launch_gemm16_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    switch (a.epi) {
-    case EPI_QKV:    return launch_k(gemm16_kernel<ACT, EPI_QKV, NST>, grid, s, a);
-    case EPI_SWIGLU: return launch_k(gemm16_kernel<ACT, EPI_SWIGLU, NST>, grid, s, a);
-    case EPI_GELU:   return launch_k(gemm16_kernel<ACT, EPI_GELU, NST>, grid, s, a);
-    default:         return launch_k(gemm16_kernel<ACT, EPI_LINEAR, NST>, grid, s, a);
-    }
+    return a.w_layout ? launch_gemm16_e<ACT, NST, true>(a, grid, s) : launch_gemm16_e<ACT, NST, false>(a, grid, s);
 }
 
 hipError_t launch_gemm16(int act, int nst, const ProjArgs &a, hipStream_t s) {

@@ -19,7 +19,8 @@ hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a,
     if (grid_wgs <= 0 || a.tiles_n <= 0) return hipSuccess;
     if (a.epi == EPI_SWIGLU && c.nr % 2 != 0) return hipErrorInvalidValue;
     // the instantiated row counts (see launch_stream_mf)
-    if (c.nr != 2 && !(c.nr == 1 && wq == 0 && c.mf <= 2) && !(c.nr == 4 && wq != 0)) return hipErrorInvalidValue;
+    if (c.nr != 2 && !(c.nr == 1 && (wq == 0 || wq == 4) && c.mf <= 2) && !(c.nr == 4 && wq != 0))
+        return hipErrorInvalidValue;
     const unsigned grid = (unsigned)grid_wgs;
     if (wq == 1) return launch_stream_i8(c, a, grid, s);
     if (wq == 2) return launch_stream_i4(c, a, grid, s);

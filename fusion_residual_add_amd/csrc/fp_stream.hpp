@@ -430,15 +430,15 @@ inline hipError_t launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, h
 
 // 64 token rows: 128-wide K chunks (two activation / weight register sets of
 // 256-wide chunks do not fit in the register file next to the accumulators)
-// Weight rows per workgroup: 64 (NR = 1) only for 16-bit weights at up to 32
-// tokens, 256 (NR = 4) only for int8 / int4 weights; only those combinations
-// are instantiated.
+// Weight rows per workgroup: 64 (NR = 1) only for 16-bit and E4M3 weights at
+// up to 32 tokens, 256 (NR = 4) only for quantised weights; only those
+// combinations are instantiated.
 template <int ACT, int WQ, int MF>
 inline hipError_t launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
     constexpr int U = MF >= 4 ? 4 : 8;
     if (c.nr == 2) return launch_stream_cfg<ACT, WQ, MF, 2, U>(a.epi, a, grid, s);
     if (c.nr == 1) {
-        if constexpr (WQ == 0 && MF <= 2) return launch_stream_cfg<ACT, WQ, MF, 1, U>(a.epi, a, grid, s);
+        if constexpr ((WQ == 0 || WQ == 4) && MF <= 2) return launch_stream_cfg<ACT, WQ, MF, 1, U>(a.epi, a, grid, s);
         return hipErrorInvalidValue;
     }
     if constexpr (WQ != 0) return launch_stream_cfg<ACT, WQ, MF, 4, U>(a.epi, a, grid, s);   // 256 rows share one A tile

@@ -264,6 +264,8 @@ def test_fp8_plans(plan_override):
     # weight as well)
     p = fra.describe_plan(32, 4096, 28672, torch.bfloat16, e, "swiglu", layout="packed_gate_up")
     assert p["kernel"] == "stream_kernel<bf16-e4m3,m32,n128,k256,swiglu>" and p["grid"] == 224, p
+    p = fra.describe_plan(32, 4096, 6144, torch.bfloat16, e, layout="packed")
+    assert p["kernel"] == "stream_kernel<bf16-e4m3,m32,n64,k256,linear>" and p["grid"] == 192, p
     assert fra.describe_plan(200, 4096, 6144, torch.bfloat16, e, layout="packed")["kernel"].startswith("gemm8")
     with fra.plan_override(fp8_tile=32):
         assert fra.describe_plan(32, 4096, 6144, torch.bfloat16, e, layout="packed")["kernel"].startswith("gemm8")
@@ -274,16 +276,20 @@ def test_fp8_plans(plan_override):
                                    swiglu=sw, family="stream") for K in (768, 4096)])
             a, b = _plan(M, 4096 if N != 768 else 768, N, w=e, fn=fn), _plan(M, 4096, N, w=torch.int8, fn=fn)
             assert a["family"] == "fp8" and a["kernel"].startswith("stream_kernel<bf16-e4m3,"), a
-            if N != 768:
+            # 64 weight rows per workgroup without the gate/up pairing at up
+            # to 32 tokens (as 16-bit weights), else int8's shapes
+            if M <= 32 and not sw:
+                assert ",n64," in a["kernel"], a
+            elif N != 768:
                 assert a["kernel"].split(",", 1)[1] == b["kernel"].split(",", 1)[1] and a["grid"] == b["grid"], (a, b)
         fra.tune_install([dict(m_lo=0, m_hi=64, hidden=4096, n_cols=6144, act_dtype=torch.float16, w_dtype=e,
                                swiglu=False, family="stream")])
-        assert _plan(16, 4096, 6144, act=torch.float16, w=e)["kernel"] == "stream_kernel<f16-e4m3,m16,n128,k256,linear>"
+        assert _plan(16, 4096, 6144, act=torch.float16, w=e)["kernel"] == "stream_kernel<f16-e4m3,m16,n64,k256,linear>"
         fra.tune_install([dict(m_lo=0, m_hi=64, hidden=K, n_cols=6144, act_dtype=torch.bfloat16, w_dtype=e,
                                swiglu=False, family="stream") for K in (640, 4096)])
         # the codes, row scales and the partial sums of tiles shared by workgroups
         p = _plan(1, 4096, 6144, w=e)
-        assert p["slots"] > 1 and p["workspace"] >= 4096 + 4 + 48 * p["slots"] * 16 * 128 * 4
+        assert p["slots"] > 1 and p["workspace"] >= 4096 + 4 + 96 * p["slots"] * 16 * 64 * 4
         # hidden not a multiple of 256, or a tile requested: the FP8 GEMM tiles
         assert _plan(8, 640, 6144, w=e)["kernel"] == "gemm8_kernel<bf16,32x256,linear>"
         with fra.plan_override(fp8_tile=64):

@@ -49,7 +49,8 @@ def test_algo_bytes_down():
     ("void fp::stats_kernel<2, 256>(fp::StatsArgs)", "stats_kernel<bf16>"),
     ("void fp::stats_kernel<1, 64, 8>(fp::StatsArgs)", "stats_kernel<f16>"),
     ("void fp::norm_kernel<2, 64, 8>(fp::StatsArgs)", "norm_kernel<bf16>"),
-    ("void fp::gemm16_kernel<2, 1, 2>(fp::ProjArgs)", "gemm16_kernel<bf16,256x256,2st,swiglu>"),
+    ("void fp::gemm16_kernel<2, 1, 2, false>(fp::ProjArgs)", "gemm16_kernel<bf16,256x256,2st,swiglu>"),
+    ("void fp::gemm16_kernel<1, 0, 4, true>(fp::ProjArgs)", "gemm16_kernel<f16,256x256,4st,qkv>"),
     ("void fp::quant8_kernel<1, 64, 8>(fp::StatsArgs)", "quant8_kernel<f16>"),
     ("void fp::gemm8_kernel<2, 1, 4, 4, 2>(fp::ProjArgs)", "gemm8_kernel<bf16,256x256,swiglu>"),
     ("void fp::gemm8_kernel<2, 0, 1, 2, 1>(fp::ProjArgs)", "gemm8_kernel<bf16,32x256,qkv>"),
