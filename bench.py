@@ -413,7 +413,7 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::gemm16_kernel<(\d), (\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         return f"gemm16_kernel<{_ACT[m.group(1)]},256x256,{m.group(3)}st,{_EPI[m.group(2)]}>"
-    m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), (\d), (\d)>", cxx)
+    m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), (\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         fm, fn, wgm = int(m.group(3)), int(m.group(4)), int(m.group(5))
         return f"gemm8_kernel<{_ACT[m.group(1)]},{32 * fm * wgm}x{32 * fn * (4 // wgm)},{_EPI[m.group(2)]}>"

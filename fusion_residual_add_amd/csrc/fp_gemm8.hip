@@ -46,7 +46,12 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned ch
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 }  // namespace g8
 
-template <int ACT, int EPI, int FM, int FN, int WGM>
+// PK: tile-packed weights.  The B tile of a stage is its 16-row blocks'
+// two 64-byte K slices, 1 KB each and contiguous in the weight: one wave
+// load copies one as it is, and the tile keeps the packed order in LDS
+// (block, slice, 16-byte group, row), where a fragment read of 16 rows of
+// one 16-byte group covers 256 contiguous bytes.
+template <int ACT, int EPI, int FM, int FN, int WGM, bool PK>
 __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjArgs p) {
     using T = Act<ACT>;
     using namespace g8;
@@ -105,19 +110,29 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
     }
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
-        const int r = (BN / 4) * wave + 8 * i + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
         int64_t wr;
-        if constexpr (SW) wr = r < BN / 2 ? (int64_t)tn * (BN / 2) + r : p.F + (int64_t)tn * (BN / 2) + (r - BN / 2);
-        else wr = (int64_t)tn * BN + r;
-        wr = wr < p.Nw ? wr : p.Nw - 1;
-        b_off[i] = (uint32_t)weight_off(p.w_layout, wr, c * 16, p.F, p.K);
+        if constexpr (PK) {
+            // block slice q = IB w + i of the stage: block q / 2 of the tile,
+            // slice q % 2 (a block past the weight reads its last block)
+            const int q = IB * wave + i, br = 16 * (q >> 1);
+            if constexpr (SW) wr = br < BN / 2 ? (int64_t)tn * (BN / 2) + br : p.F + (int64_t)tn * (BN / 2) + (br - BN / 2);
+            else wr = (int64_t)tn * BN + br;
+            wr = wr < p.Nw ? wr : p.Nw - 16;
+            b_off[i] = (uint32_t)(packed_row_off(wr, p.F, p.K, p.w_layout) + (q & 1) * 8192) + lane * 16;
+        } else {
+            const int r = (BN / 4) * wave + 8 * i + (lane >> 3);
+            const int c = (lane & 7) ^ (r & 7);
+            if constexpr (SW) wr = r < BN / 2 ? (int64_t)tn * (BN / 2) + r : p.F + (int64_t)tn * (BN / 2) + (r - BN / 2);
+            else wr = (int64_t)tn * BN + r;
+            wr = wr < p.Nw ? wr : p.Nw - 1;
+            b_off[i] = (uint32_t)weight_off(p.w_layout, wr, c * 16, p.F, p.K);
+        }
     }
     // stage kt: row bytes kt * BK, the scalar offset (tile-packed weights:
     // that byte's packed offset, additive since BK is a multiple of 64)
     auto issue = [&](int kt, unsigned char *la, unsigned char *lb) {
         const uint32_t soff = (uint32_t)kt * BK;
-        const uint32_t wsoff = p.w_layout ? (uint32_t)packed_col_off(soff) : soff;
+        const uint32_t wsoff = PK || p.w_layout ? (uint32_t)packed_col_off(soff) : soff;
 #pragma unroll
         for (int i = 0; i < IA; ++i) load_lds16(ra, la + (IA * wave + i) * 1024, a_off[i], soff);
 #pragma unroll
@@ -144,6 +159,15 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
         const u32x4 hi = *(const u32x4 *)(l + swz(row, c + 1));
         return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
+    // packed B tile: chunks c (even) and c + 1 of tile row `row` sit in slice
+    // c / 4 of its block, 16-byte groups c % 4 and c % 4 + 1
+    auto frag_pk = [&](const unsigned char *l, int row, int kb) -> i32x8 {
+        const int c = 4 * kb + 2 * kh;
+        const unsigned char *b = l + ((((row >> 4) * 2 + (c >> 2)) << 10) + ((c & 3) << 8) + ((row & 15) << 4));
+        const u32x4 lo = *(const u32x4 *)b;
+        const u32x4 hi = *(const u32x4 *)(b + 256);
+        return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -160,7 +184,7 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
 #pragma unroll
             for (int f = 0; f < FM; ++f) af[f] = frag(la, arow[f], kb);
 #pragma unroll
-            for (int f = 0; f < FN; ++f) bf[f] = frag(lb, brow[f], kb);
+            for (int f = 0; f < FN; ++f) bf[f] = PK ? frag_pk(lb, brow[f], kb) : frag(lb, brow[f], kb);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -310,14 +334,20 @@ __global__ __launch_bounds__(256, FM * FN >= 16 ? 1 : 2) void gemm8_kernel(ProjA
     }
 }
 
+template <int ACT, int FM, int FN, int WGM, bool PK>
+static hipError_t launch_gemm8_e(const ProjArgs &a, unsigned grid, hipStream_t s) {
+    switch (a.epi) {
+    case EPI_QKV:    return launch_k(gemm8_kernel<ACT, EPI_QKV, FM, FN, WGM, PK>, grid, s, a);
+    case EPI_SWIGLU: return launch_k(gemm8_kernel<ACT, EPI_SWIGLU, FM, FN, WGM, PK>, grid, s, a);
+    case EPI_GELU:   return launch_k(gemm8_kernel<ACT, EPI_GELU, FM, FN, WGM, PK>, grid, s, a);
+    default:         return launch_k(gemm8_kernel<ACT, EPI_LINEAR, FM, FN, WGM, PK>, grid, s, a);
+    }
+}
+
 template <int ACT, int FM, int FN, int WGM>
 static hipError_t launch_gemm8_t(const ProjArgs &a, unsigned grid, hipStream_t s) {
-    switch (a.epi) {
-    case EPI_QKV:    return launch_k(gemm8_kernel<ACT, EPI_QKV, FM, FN, WGM>, grid, s, a);
-    case EPI_SWIGLU: return launch_k(gemm8_kernel<ACT, EPI_SWIGLU, FM, FN, WGM>, grid, s, a);
-    case EPI_GELU:   return launch_k(gemm8_kernel<ACT, EPI_GELU, FM, FN, WGM>, grid, s, a);
-    default:         return launch_k(gemm8_kernel<ACT, EPI_LINEAR, FM, FN, WGM>, grid, s, a);
-    }
+    return a.w_layout ? launch_gemm8_e<ACT, FM, FN, WGM, true>(a, grid, s)
+                      : launch_gemm8_e<ACT, FM, FN, WGM, false>(a, grid, s);
 }
 
 template <int ACT>
