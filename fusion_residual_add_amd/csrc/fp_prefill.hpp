@@ -53,16 +53,22 @@ __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ ((r >
 // LN: LayerNorm (mean, beta); otherwise RMSNorm or no norm, whose
 // normalisation is two multiplies (h * rstd * gamma) and has no beta to load.
 // WQ: weight storage -- 0 the activation dtype (straight into LDS), 1 int8,
-// 2 int4, 3 MXFP4 (all three through registers, dequantised into LDS).
+// 2 int4, 3 MXFP4 (all three through registers, dequantised into LDS), 5 the
+// activation dtype tile-packed: a wave load copies one contiguous 1 KB
+// block slice (16 rows x 64 bytes) and the B tile keeps the packed order in
+// LDS (block, slice, 16-byte group, row), where the 16 lanes of a fragment
+// read cover 256 contiguous bytes.  (Quantised weights go through registers,
+// so either layout only changes their load addresses.)
 template <int ACT, int WQ, int EPI, bool LN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(ProjArgs p) {
     using T = Act<ACT>;
     using namespace pf;
     // WI4: 4-bit weights of either kind ([N, K/2] bytes, 32 values per 16-byte vector)
-    constexpr bool WI8 = WQ == 1, WMX = WQ == 3, WI4 = WQ == 2 || WMX, WREG = WQ != 0;
+    constexpr bool PK = WQ == 5;
+    constexpr bool WI8 = WQ == 1, WMX = WQ == 3, WI4 = WQ == 2 || WMX, WREG = WQ != 0 && !PK;
     static_assert(ACT != ACT_F32, "16-bit activations");
-    static_assert(WQ == 0 || ACT == ACT_BF16, "int8 / int4 / MXFP4 weights feed bf16 MFMA");
+    static_assert(WQ == 0 || PK || ACT == ACT_BF16, "int8 / int4 / MXFP4 weights feed bf16 MFMA");
     // A and B tiles of the two stages as four distinct LDS objects, so that
     // the compiler can tell the direct-to-LDS weight loads into one stage from
     // the fragment reads of the other (and waits for them only at the end of
@@ -155,6 +161,7 @@ void prefill_kernel(ProjArgs p) {
         int br;
         if constexpr (WI8) br = (tid >> 2) + 64 * i;
         else if constexpr (WI4) br = (tid >> 1) + 128 * i;
+        else if constexpr (PK) br = 128 * wave + 16 * (i >> 1);   // block slice 16 wave + i: block row, slice i % 2
         else br = 128 * wave + 8 * i + (lane >> 3);
         int64_t wrow;
         if constexpr (EPI == EPI_SWIGLU) {
@@ -162,11 +169,11 @@ void prefill_kernel(ProjArgs p) {
             // of a wave hold the gate and up values of the same outputs
             const int blk = br >> 5;
             int64_t j = (int64_t)tn * (BN / 2) + (blk >> 1) * 32 + (br & 31);
-            j = j < p.F ? j : p.F - 1;
+            j = j < p.F ? j : PK ? p.F - 16 : p.F - 1;   // (packed: whole blocks of 16 rows)
             wrow = (blk & 1) ? p.F + j : j;
         } else {
             wrow = (int64_t)tn * BN + br;
-            wrow = wrow < p.Nw ? wrow : p.Nw - 1;
+            wrow = wrow < p.Nw ? wrow : PK ? p.Nw - 16 : p.Nw - 1;
         }
         if constexpr (WI8) {
             b_off[i] = (uint32_t)weight_off(p.w_layout, wrow, (tid & 3) * 16, p.F, p.K);
@@ -175,6 +182,8 @@ void prefill_kernel(ProjArgs p) {
             b_off[i] = (uint32_t)weight_off(p.w_layout, wrow, (tid & 1) * 16, p.F, p.K / 2);
             // MXFP4: the thread's 32 values of a stage are block 2 kt + (tid & 1) of the row
             b_soff[i] = WMX ? (uint32_t)(wrow * (p.K / 32)) + (tid & 1) : (uint32_t)(wrow * (p.K / 128) * 4);
+        } else if constexpr (PK) {
+            b_off[i] = (uint32_t)(packed_row_off(wrow, p.F, p.K * 2, p.w_layout) + (i & 1) * 8192) + lane * 16;
         } else {
             const int c = (lane & 7) ^ ((br >> 1) & 7);
             b_off[i] = (uint32_t)weight_off(p.w_layout, wrow, c * 16, p.F, p.K * 2);
@@ -237,7 +246,7 @@ void prefill_kernel(ProjArgs p) {
     // ---- weight side.  A stage's weight bytes start at row byte kt times the
     // stage's bytes per row; its offset in the weight's layout is added as the
     // scalar offset to the lanes' offsets of stage 0 (additive in both layouts)
-    auto wsoff = [&](uint32_t rb) -> uint32_t { return p.w_layout ? (uint32_t)packed_col_off(rb) : rb; };
+    auto wsoff = [&](uint32_t rb) -> uint32_t { return PK || p.w_layout ? (uint32_t)packed_col_off(rb) : rb; };
     auto bload_lds = [&](int kt, unsigned char *lb) {   // 16-bit weights, straight to LDS
         const uint32_t kb = wsoff((uint32_t)kt * (BK * 2));
 #pragma unroll
@@ -301,6 +310,10 @@ void prefill_kernel(ProjArgs p) {
         return *(const u32x4 *)(la + swz(i * 32 + (lane & 31), 2 * t + (lane >> 5)));
     };
     auto frag_b = [&](const unsigned char *lb, int t, int j) {
+        if constexpr (PK) {   // packed B tile: row R, chunk c at ((R / 16) 2 + c / 4) KB + 256 (c % 4) + 16 (R % 16)
+            const int r = wave * 128 + j * 32 + (lane & 31), c = 2 * t + (lane >> 5);
+            return *(const u32x4 *)(lb + ((((r >> 4) * 2 + (c >> 2)) << 10) + ((c & 3) << 8) + ((r & 15) << 4)));
+        }
         return *(const u32x4 *)(lb + swz(wave * 128 + j * 32 + (lane & 31), 2 * t + (lane >> 5)));
     };
     auto mma = [&](const unsigned char *la, const unsigned char *lb, unsigned char *na, unsigned char *nb, int kn) {
