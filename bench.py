@@ -413,6 +413,8 @@ def library_kernel_name(cxx: str) -> str:
     m = re.search(r"fp::gemm16_kernel<(\d), (\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         return f"gemm16_kernel<{_ACT[m.group(1)]},256x256,{m.group(3)}st,{_EPI[m.group(2)]}>"
+    if "fp::pack_kernel(" in cxx:
+        return "pack_kernel"
     m = re.search(r"fp::gemm8_kernel<(\d), (\d), (\d), (\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         fm, fn, wgm = int(m.group(3)), int(m.group(4)), int(m.group(5))

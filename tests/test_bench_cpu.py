@@ -54,6 +54,8 @@ def test_algo_bytes_down():
     ("void fp::quant8_kernel<1, 64, 8>(fp::StatsArgs)", "quant8_kernel<f16>"),
     ("void fp::gemm8_kernel<2, 1, 4, 4, 2>(fp::ProjArgs)", "gemm8_kernel<bf16,256x256,swiglu>"),
     ("void fp::gemm8_kernel<2, 0, 1, 2, 1, true>(fp::ProjArgs)", "gemm8_kernel<bf16,32x256,qkv>"),
+    ("fp::pack_kernel(unsigned int __vector(4) const*, unsigned int __vector(4)*, long, long, long, int, int)",
+     "pack_kernel"),
     ("void fp::gemm8_kernel<2, 0, 1, 2, 1>(fp::ProjArgs)", "gemm8_kernel<bf16,32x256,qkv>"),
     ("void fp::gemm8_kernel<1, 3, 2, 2, 2>(fp::ProjArgs)", "gemm8_kernel<f16,128x128,linear>"),
     ("void fp::gemm8_kernel<2, 2, 2, 2, 1>(fp::ProjArgs)", "gemm8_kernel<bf16,64x256,gelu>"),
