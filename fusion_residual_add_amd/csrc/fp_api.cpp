@@ -183,11 +183,33 @@ void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool q
     // quantised weights)
     if (kb.rows == 64 && nr1_ok) p.sc.nr = 1;
     if (kb.rows == 128 || (kb.rows == 256 && qw)) p.sc.nr = (int)(kb.rows / 64);
-    p.sc.u = stream_chunk(M) / 32;   // K chunk 32 * u: must match the launcher
-    const int nb = 64 * p.sc.nr;
+    // 32 rows (K halves: two waves per 16 rows, each streaming half of every
+    // chunk) where the 32-row tiles fill three quarters of the workgroups or
+    // more without outnumbering them, so that each workgroup streams one whole
+    // tile where 64-row tiles would be split between two (measured on MI355X
+    // with rocprofv3, Llama-3-8B QKV on tile-packed weights, 192 tiles, at 1 /
+    // 16 / 32 tokens: bf16 14.1 / 14.4 / 15.8 -> 11.3 / 12.2 / 15.2 us, E4M3
+    // 9.2 / 10.2 / 11.6 -> 7.6 / 8.5 / 11.3 us; where the 32-row tiles
+    // outnumber the workgroups they are slower, Llama-2-7B QKV, 384 tiles:
+    // 1.07 - 1.26x the 64-row time by HIP events)
+    const int64_t t32 = (Nw + 31) / 32;
+    const bool kh_ok = nr1_ok && K % (2 * stream_chunk(M)) == 0;
+    p.sc.kh = 1;
+    if (kb.rows == 0 && kh_ok && t32 <= kb.target && t32 * 100 >= kb.target * 75) {
+        p.sc.nr = 1;
+        p.sc.kh = 2;
+    }
+    if (kb.rows == 32 && kh_ok) {
+        p.sc.nr = 1;
+        p.sc.kh = 2;
+    }
+    p.sc.u = p.sc.kh * stream_chunk(M) / 32;   // K chunk 32 * u: must match the launcher
+    const int nb = 64 * p.sc.nr / p.sc.kh;
     p.tiles_m = 1;
     p.tiles_n = (int)((Nw + nb - 1) / nb);
-    p.tile_elems = (int64_t)16 * p.sc.mf * nb;
+    // partial sums: 256 threads x the accumulators of 64 * nr rows (with K
+    // halves, the second half's waves hold zeros)
+    p.tile_elems = (int64_t)16 * p.sc.mf * 64 * p.sc.nr;
     const int64_t tiles = p.tiles_n, ksteps = K / (32 * p.sc.u), target = kb.target;
     // stream-K: `grid` workgroups take equal contiguous unit ranges of at
     // least 512 of K each (2 chunks of 256, 4 of 128; measured on MI355X:
@@ -1227,7 +1249,7 @@ fp_status fp_tune_install(const fp_tune_entry *entries, int64_t n) {
         const fp_tune_entry &e = entries[i];
         const bool ok = e.m_lo >= 0 && e.m_hi >= e.m_lo && e.hidden > 0 && e.n_cols > 0 &&
                         e.family >= -1 && e.family <= 4 && e.family != 3 &&
-                        (e.rows == 0 || e.rows == 64 || e.rows == 128 || e.rows == 256) &&
+                        (e.rows == 0 || e.rows == 32 || e.rows == 64 || e.rows == 128 || e.rows == 256) &&
                         e.grid >= 0 && e.grid <= 65535 && e.splits >= 0 && e.splits <= 64 &&
                         (e.swiglu == 0 || e.swiglu == 1) && check_dtypes(e.act_dtype, e.w_dtype, e.act_dtype) == FP_OK;
         if (!ok) return fail(FP_E_ARG, "tuning entry %lld is out of range", (long long)i);

@@ -131,7 +131,7 @@ hipError_t launch_tiled(int act, bool w_i8, int tile, const ProjArgs &a, hipStre
 //  wave (1 or 2; 2 for SwiGLU) -> 64 * nr weight rows per workgroup;
 //  u: 32-wide k slices per chunk (8) -> K must be a multiple of 32 * u.
 //  tiles_m must be 1.
-struct StreamCfg { int mf, nr, u; };
+struct StreamCfg { int mf, nr, u, kh = 1; };   // kh: K parts per chunk (2: 32-row workgroups)
 // grid_wgs workgroups share the (weight tile, K chunk) units evenly
 hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s);
 hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,

@@ -21,6 +21,7 @@ hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a,
     // the instantiated row counts (see launch_stream_mf)
     if (c.nr != 2 && !(c.nr == 1 && (wq == 0 || wq == 4) && c.mf <= 2) && !(c.nr == 4 && wq != 0))
         return hipErrorInvalidValue;
+    if (c.kh != 1 && !(c.kh == 2 && c.nr == 1 && a.epi != EPI_SWIGLU)) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)grid_wgs;
     if (wq == 1) return launch_stream_i8(c, a, grid, s);
     if (wq == 2) return launch_stream_i4(c, a, grid, s);
@@ -62,7 +63,7 @@ const char *stream_kernel_name(int act, int wq, const StreamCfg &c, int epi) {
     thread_local char buf[64];
     const char *an = wq == 4 ? (act == ACT_F16 ? "f16-e4m3" : "bf16-e4m3") : acts[wq ? 2 + wq : act];
     snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", an, 16 * c.mf,
-             64 * c.nr, 32 * c.u, epis[epi]);
+             64 * c.nr / c.kh, 32 * c.u, epis[epi]);
     return buf;
 }
 

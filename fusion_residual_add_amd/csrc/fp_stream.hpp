@@ -45,7 +45,13 @@ namespace fp {
 //   a_scale [M]) instead of x + residual and the norm, both operands are
 //   decoded exactly to bf16 in registers (the products are those of the FP8
 //   matrix cores), and the epilogue scales by a_scale[m] * w_scale[c].
-template <int ACT, int WQ, int MF, int NR, int U, int EPI>
+// KH: K parts per chunk.  KH = 2 (16-bit and E4M3 weights, no gate/up
+// pairing): the four waves are two row groups x two halves of each chunk's
+// K, so a workgroup covers 32 weight rows (NR = 1) with the bytes per chunk
+// of a 64-row tile; the two halves' sums meet in LDS at the end.  The host
+// gives every such workgroup one whole tile (no partial sums between
+// workgroups), so a 6144-row QKV weight is 192 tiles on 192 workgroups.
+template <int ACT, int WQ, int MF, int NR, int U, int EPI, int KH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(ProjArgs p) {
     constexpr bool WF8 = WQ == 4;
@@ -58,10 +64,14 @@ void stream_kernel(ProjArgs p) {
     static_assert(!WI8 || U % 2 == 0, "one int8 load covers two k slices");
     static_assert(!WI4 || U % 4 == 0, "one int4 load covers four k slices (one scale group)");
     constexpr int BMP = 16 * MF;                 // padded token rows
-    constexpr int NB = 64 * NR;                  // weight rows per workgroup
+    static_assert(KH == 1 || (KH == 2 && NR == 1 && EPI != EPI_SWIGLU && (WQ == 0 || WF8)), "K halves");
+    constexpr int NWR = 4 / KH;                  // row groups of waves
+    constexpr int NB = 16 * NR * NWR;            // weight rows per workgroup
     constexpr int CK = 32 * U;                   // k per chunk
     constexpr int LDA = CK + 8;                  // LDS row stride (elements), +16 B pad
     constexpr int NL = WI8 ? U / 2 : WI4 ? U / 4 : U;   // weight loads per fragment per chunk
+    constexpr int NLW = NL / KH;                 // ... of them by one wave
+    static_assert(NL % KH == 0, "whole loads per K part");
     constexpr int KVR = CK / 8;                  // 16-byte activation vectors per row per chunk
     constexpr int AV = (BMP * KVR + 255) / 256;  // activation vectors per thread per chunk
     constexpr int AR = 256 / KVR;                // row step between a thread's vectors
@@ -69,6 +79,8 @@ void stream_kernel(ProjArgs p) {
     __shared__ __attribute__((aligned(16))) unsigned short lds_a[2][BMP * LDA];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave % NWR, kh = wave / NWR;   // the wave's row group and K part
+    const int ub = kh * NLW;                      // its first load slice of a chunk
     const int G = (int)gridDim.x;
     const int g = xcd_remap(blockIdx.x, G);
     const int nchunks = (int)(p.K / CK);
@@ -97,11 +109,11 @@ void stream_kernel(ProjArgs p) {
             int64_t r;
             if constexpr (EPI == EPI_SWIGLU) {
                 // fragment pairs (gate, up) of the same 16 output columns
-                int64_t j = (int64_t)tn * (NB / 2) + wave * (NR * 8) + (n / 2) * 16 + (lane & 15);
+                int64_t j = (int64_t)tn * (NB / 2) + wr * (NR * 8) + (n / 2) * 16 + (lane & 15);
                 j = j < p.F ? j : p.F - 1;
                 r = (n & 1) ? p.F + j : j;
             } else {
-                r = (int64_t)tn * NB + wave * (NR * 16) + n * 16 + (lane & 15);
+                r = (int64_t)tn * NB + wr * (NR * 16) + n * 16 + (lane & 15);
                 r = r < p.Nw ? r : p.Nw - 1;
             }
             wrow[n] = (const char *)p.w + weight_off(p.w_layout, r, (lane >> 4) * 16, p.F, rbytes);
@@ -116,7 +128,7 @@ void stream_kernel(ProjArgs p) {
         // (int8 / E4M3: 16 k; int4 / MXFP4: 32 k, one 128-k scale group per u
         // with lane group g at k 32 g; 16-bit: 8 k)
         auto wload = [&](int c, int n, int u) -> u32x4 {
-            return *(const u32x4 *)(wrow[n] + (int64_t)c * cstep + u * ustep);
+            return *(const u32x4 *)(wrow[n] + (int64_t)c * cstep + (ub + u) * ustep);
         };
 
         // ---- activation side: fixed k-vector, token rows a_r0 + i * AR (rows past
@@ -185,13 +197,13 @@ void stream_kernel(ProjArgs p) {
         // weight registers of one chunk (int4: with the group scales of the
         // chunk; MXFP4: with the block scale code of each lane's load)
         struct WRegs {
-            u32x4 w[NR][NL];
+            u32x4 w[NR][NLW];
             float s[NR][WI4 ? NL : 1];
             unsigned sm[NR][WMX ? NL : 1];
         };
         auto wload_all = [&](int c, WRegs &W) {
     #pragma unroll
-            for (int u = 0; u < NL; ++u)
+            for (int u = 0; u < NLW; ++u)
     #pragma unroll
                 for (int n = 0; n < NR; ++n) W.w[n][u] = wload(c, n, u);
             if constexpr (WMX) {
@@ -221,7 +233,8 @@ void stream_kernel(ProjArgs p) {
             constexpr bool PF = decltype(pf)::value;
             const unsigned short *la = lds_a[buf];
     #pragma unroll
-            for (int u = 0; u < NL; ++u) {
+            for (int u = 0; u < NLW; ++u) {
+                const int ug = ub + u;   // the load's slice of the chunk
                 if constexpr (WI4) {
                     u32x4 b[NR][4];
     #pragma unroll
@@ -232,7 +245,7 @@ void stream_kernel(ProjArgs p) {
                     // a lane's 32 int4 are k = 128u + 32 (lane / 16) + [0, 32): four MFMA k slices
     #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) {
-                        const int koff = u * 128 + (lane >> 4) * 32 + qq * 8;
+                        const int koff = ug * 128 + (lane >> 4) * 32 + qq * 8;
     #pragma unroll
                         for (int m = 0; m < MF; ++m) {
                             const u32x4 a = *(const u32x4 *)&la[(m * 16 + (lane & 15)) * LDA + koff];
@@ -254,7 +267,7 @@ void stream_kernel(ProjArgs p) {
                     // a lane's 16 int8 are k = 64u + 16 (lane / 16) + [0, 16): two MFMA k slices
     #pragma unroll
                     for (int half = 0; half < 2; ++half) {
-                        const int koff = u * 64 + (lane >> 4) * 16 + half * 8;
+                        const int koff = ug * 64 + (lane >> 4) * 16 + half * 8;
     #pragma unroll
                         for (int m = 0; m < MF; ++m) {
                             const u32x4 a = *(const u32x4 *)&la[(m * 16 + (lane & 15)) * LDA + koff];
@@ -263,7 +276,7 @@ void stream_kernel(ProjArgs p) {
                         }
                     }
                 } else {
-                    const int koff = u * 32 + (lane >> 4) * 8;
+                    const int koff = ug * 32 + (lane >> 4) * 8;
     #pragma unroll
                     for (int m = 0; m < MF; ++m) {
                         const u32x4 a = *(const u32x4 *)&la[(m * 16 + (lane & 15)) * LDA + koff];
@@ -343,6 +356,24 @@ void stream_kernel(ProjArgs p) {
             }
         }
 
+        // ---- K halves: the second half's waves hand their sums to the first
+        // half's waves of the same row group through LDS (then hold zeros, so
+        // that a shared tile's partial sums below stay whole-workgroup)
+        if constexpr (KH == 2) {
+            __shared__ float red[NWR][MF * 4][64];
+            if (kh) {
+    #pragma unroll
+                for (int m = 0; m < MF; ++m)
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) red[wr][m * 4 + e][lane] = acc[m][0][e];
+            }
+            __syncthreads();
+    #pragma unroll
+            for (int m = 0; m < MF; ++m)
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) acc[m][0][e] = kh ? 0.f : acc[m][0][e] + red[wr][m * 4 + e][lane];
+        }
+
         // ---- a tile shared with other workgroups: partial sums, and the last
         // contributor to arrive adds them in contributor order
         const int first = owner((int64_t)tn * nchunks), last = owner((int64_t)tn * nchunks + nchunks - 1);
@@ -364,6 +395,7 @@ void stream_kernel(ProjArgs p) {
         }
 
         // ---- epilogue: lane holds token rows 16 m + 4 (lane / 16) + e of weight row lane % 16
+        if (kh) return;
     #pragma unroll
         for (int m = 0; m < MF; ++m) {
     #pragma unroll
@@ -376,13 +408,13 @@ void stream_kernel(ProjArgs p) {
                 if constexpr (EPI == EPI_SWIGLU) {
     #pragma unroll
                     for (int n = 0; n < NR; n += 2) {
-                        const int64_t j = (int64_t)tn * (NB / 2) + wave * (NR * 8) + (n / 2) * 16 + (lane & 15);
+                        const int64_t j = (int64_t)tn * (NB / 2) + wr * (NR * 8) + (n / 2) * 16 + (lane & 15);
                         if (j < p.F) store_swiglu<ACT>(p, row, j, scaled(n), scaled(n + 1));
                     }
                 } else {
     #pragma unroll
                     for (int n = 0; n < NR; ++n) {
-                        const int64_t c = (int64_t)tn * NB + wave * (NR * 16) + n * 16 + (lane & 15);
+                        const int64_t c = (int64_t)tn * NB + wr * (NR * 16) + n * 16 + (lane & 15);
                         if (c >= p.Nw) continue;
                         float y = scaled(n);
                         if (p.bias) y += T::ld(p.bias, c);
@@ -413,29 +445,37 @@ void stream_kernel(ProjArgs p) {
 // ---------------------------------------------------------------------------
 // launch helpers (instantiated per activation / weight dtype in fp_stream_*.hip)
 // ---------------------------------------------------------------------------
-template <int ACT, int WQ, int MF, int NR, int U>
+template <int ACT, int WQ, int MF, int NR, int U, int KH = 1>
 inline hipError_t launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (epi) {
     case EPI_QKV:
-        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_QKV>, grid, s, a);
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_QKV, KH>, grid, s, a);
     case EPI_SWIGLU:
-        if constexpr (NR % 2 == 0) return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_SWIGLU>, grid, s, a);
+        if constexpr (NR % 2 == 0 && KH == 1)
+            return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_SWIGLU, KH>, grid, s, a);
         return hipErrorInvalidValue;
     case EPI_GELU:
-        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_GELU>, grid, s, a);
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_GELU, KH>, grid, s, a);
     default:
-        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_LINEAR>, grid, s, a);
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_LINEAR, KH>, grid, s, a);
     }
 }
 
 // 64 token rows: 128-wide K chunks (two activation / weight register sets of
 // 256-wide chunks do not fit in the register file next to the accumulators)
 // Weight rows per workgroup: 64 (NR = 1) only for 16-bit and E4M3 weights at
-// up to 32 tokens, 256 (NR = 4) only for quantised weights; only those
+// up to 32 tokens, 256 (NR = 4) only for quantised weights; 32 (NR = 1 with
+// K halves, chunks twice as wide so that a wave's loads per chunk stay the
+// same) for 16-bit and E4M3 weights at up to 32 tokens; only those
 // combinations are instantiated.
 template <int ACT, int WQ, int MF>
 inline hipError_t launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
     constexpr int U = MF >= 4 ? 4 : 8;
+    if (c.kh == 2) {
+        if constexpr ((WQ == 0 || WQ == 4) && MF <= 2)
+            if (c.nr == 1) return launch_stream_cfg<ACT, WQ, MF, 1, 2 * U, 2>(a.epi, a, grid, s);
+        return hipErrorInvalidValue;
+    }
     if (c.nr == 2) return launch_stream_cfg<ACT, WQ, MF, 2, U>(a.epi, a, grid, s);
     if (c.nr == 1) {
         if constexpr ((WQ == 0 || WQ == 4) && MF <= 2) return launch_stream_cfg<ACT, WQ, MF, 1, U>(a.epi, a, grid, s);

@@ -371,8 +371,10 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
  *           weight-streaming kernel on the codes, any other value the FP8
  *           GEMM tiles;
  *  rows   : streaming kernel, weight rows per workgroup: 128, 64 (16-bit
- *           weights, no gate/up pairing, M <= 32) or 256 (int8, int4, MXFP4
- *           and E4M3 weights); other values are ignored;
+ *           and E4M3 weights, no gate/up pairing, M <= 32), 32 (as 64, with
+ *           hidden a multiple of 512: each K chunk split between two waves
+ *           per 16 rows) or 256 (int8, int4, MXFP4 and E4M3 weights); other
+ *           values are ignored;
  *  grid   : streaming kernel, workgroups (at most one per unit of work);
  *  splits : tiled, 128 x 512 and FP8 GEMM kernels, ways K is split.
  * Results stay within the parity bounds for any entry (only the order of the

@@ -265,7 +265,8 @@ def test_fp8_plans(plan_override):
     p = fra.describe_plan(32, 4096, 28672, torch.bfloat16, e, "swiglu", layout="packed_gate_up")
     assert p["kernel"] == "stream_kernel<bf16-e4m3,m32,n128,k256,swiglu>" and p["grid"] == 224, p
     p = fra.describe_plan(32, 4096, 6144, torch.bfloat16, e, layout="packed")
-    assert p["kernel"] == "stream_kernel<bf16-e4m3,m32,n64,k256,linear>" and p["grid"] == 192, p
+    assert p["kernel"] == "stream_kernel<bf16-e4m3,m32,n32,k512,linear>" and p["grid"] == 192, p
+    assert p["slots"] == 1
     assert fra.describe_plan(200, 4096, 6144, torch.bfloat16, e, layout="packed")["kernel"].startswith("gemm8")
     with fra.plan_override(fp8_tile=32):
         assert fra.describe_plan(32, 4096, 6144, torch.bfloat16, e, layout="packed")["kernel"].startswith("gemm8")
@@ -276,17 +277,18 @@ def test_fp8_plans(plan_override):
                                    swiglu=sw, family="stream") for K in (768, 4096)])
             a, b = _plan(M, 4096 if N != 768 else 768, N, w=e, fn=fn), _plan(M, 4096, N, w=torch.int8, fn=fn)
             assert a["family"] == "fp8" and a["kernel"].startswith("stream_kernel<bf16-e4m3,"), a
-            # 64 weight rows per workgroup without the gate/up pairing at up
-            # to 32 tokens (as 16-bit weights), else int8's shapes
+            # 32 (192 tiles of 6144 rows) or 64 weight rows per workgroup
+            # without the gate/up pairing at up to 32 tokens (as 16-bit
+            # weights), else int8's shapes
             if M <= 32 and not sw:
-                assert ",n64," in a["kernel"], a
+                assert (",n32,k512," if N == 6144 else ",n64,") in a["kernel"], a
             elif N != 768:
                 assert a["kernel"].split(",", 1)[1] == b["kernel"].split(",", 1)[1] and a["grid"] == b["grid"], (a, b)
         fra.tune_install([dict(m_lo=0, m_hi=64, hidden=4096, n_cols=6144, act_dtype=torch.float16, w_dtype=e,
                                swiglu=False, family="stream")])
-        assert _plan(16, 4096, 6144, act=torch.float16, w=e)["kernel"] == "stream_kernel<f16-e4m3,m16,n64,k256,linear>"
+        assert _plan(16, 4096, 6144, act=torch.float16, w=e)["kernel"] == "stream_kernel<f16-e4m3,m16,n32,k512,linear>"
         fra.tune_install([dict(m_lo=0, m_hi=64, hidden=K, n_cols=6144, act_dtype=torch.bfloat16, w_dtype=e,
-                               swiglu=False, family="stream") for K in (640, 4096)])
+                               swiglu=False, family="stream", rows=64) for K in (640, 4096)])
         # the codes, row scales and the partial sums of tiles shared by workgroups
         p = _plan(1, 4096, 6144, w=e)
         assert p["slots"] > 1 and p["workspace"] >= 4096 + 4 + 96 * p["slots"] * 16 * 64 * 4
@@ -404,10 +406,32 @@ def test_plan_routing_families(plan_override):
     # the same tile count on a 470 MB weight: stream-K over 256 workgroups
     p = _plan(64, 8192, 57344, w=torch.int8, fn="swiglu")
     assert p["grid"] == 256 and p["slots"] >= 2
-    # 16-bit QKV weights at up to 32 tokens: 64-row tiles (96 of them), two
-    # workgroups per tile (192: at least three quarters of the CUs)
+    # 16-bit QKV weights at up to 32 tokens: 32-row tiles with K halves (192
+    # of them: at least three quarters of the CUs), one whole tile per workgroup
     p = _plan(32, 4096, 6144)
-    assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear>" and p["grid"] == 192 and p["slots"] == 2
+    assert p["kernel"] == "stream_kernel<bf16,m32,n32,k512,linear>" and p["grid"] == 192 and p["slots"] == 1
+    # more 32-row tiles than workgroups (Llama-2-7B QKV): 64-row tiles, one each
+    p = _plan(16, 4096, 12288)
+    assert p["kernel"] == "stream_kernel<bf16,m16,n64,k256,linear>" and p["grid"] == 192 and p["slots"] == 1
+    # requested: 64 rows, two workgroups per tile; or 32 rows where 64 would be chosen
+    with fra.plan_override(stream_nr=1):
+        p = _plan(32, 4096, 6144)
+        assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear>" and p["grid"] == 192 and p["slots"] == 2
+    try:
+        fra.tune_install([dict(m_lo=0, m_hi=64, hidden=4096, n_cols=12288, act_dtype=torch.bfloat16,
+                               w_dtype=torch.bfloat16, swiglu=False, family="stream", rows=32)])
+        assert _plan(16, 4096, 12288)["kernel"] == "stream_kernel<bf16,m16,n32,k512,linear>"
+        # not for gate/up pairs, 4-bit or int8 weights, 33..64 tokens or hidden not a multiple of 512
+        fra.tune_install([dict(m_lo=0, m_hi=64, hidden=K, n_cols=N, act_dtype=torch.bfloat16, w_dtype=w,
+                               swiglu=sw, family="stream", rows=32)
+                          for K in (768, 4096) for N in (6144, 28672) for w in (torch.bfloat16, torch.int8)
+                          for sw in (False, True)])
+        assert ",n128," in _plan(16, 4096, 28672, fn="swiglu")["kernel"]
+        assert ",n128," in _plan(16, 4096, 6144, w=torch.int8)["kernel"]
+        assert ",n128," in _plan(48, 4096, 6144)["kernel"]
+        assert ",n64," in _plan(16, 768, 6144)["kernel"]
+    finally:
+        fra.tune_clear()
     # 33..64 tokens keep 128-row tiles
     assert _plan(64, 4096, 6144)["kernel"] == "stream_kernel<bf16,m64,n128,k128,linear>"
     # Llama-2-70B's 8-way shard: QKV (10 tiles x 32 chunks) on 160 workgroups of
@@ -466,8 +490,12 @@ def test_plan_grid_slots_consistent(plan_override):
         plan_override(splits=int(splits))
         for M, K, N in ((1, 2048, 640), (32, 4096, 6144), (20, 1024, 928)):
             p = _plan(M, K, N)
-            tiles = -(-N // 64)               # 64-row tiles: 16-bit weights, no pairing, <= 32 tokens
-            chunks = K // 256
+            # 64-row tiles of 256-wide chunks, or 32-row tiles of 512-wide
+            # chunks (16-bit weights, no pairing, <= 32 tokens)
+            nb, ck = (int(f[1:]) for f in p["kernel"].split(",")[2:4])
+            assert (nb, ck) in ((64, 256), (32, 512)), p
+            tiles = -(-N // nb)
+            chunks = K // ck
             units = tiles * chunks
             G = min(tiles * int(splits), units)
             assert p["grid"] == G

@@ -3,8 +3,11 @@ scratch) against the workspace call it varies (fused_add_norm_qkv) and the
 oracle: two calls in a row on one device, the second with a smaller input,
 each checked bit for bit against the workspace call's outputs and to the
 parity bounds against the oracle.  The first shape splits its 96 weight
-tiles between workgroups, so the partial sums and arrival counters in the
-scratch are exercised; the second reuses the scratch the first left behind.
+tiles of 64 rows between workgroups (64 rows requested: the planner's own
+choice for it, 32-row tiles with K halves, gives every workgroup a whole
+tile), so the partial sums and arrival counters in the scratch are
+exercised; the second reuses the scratch the first left behind.  The
+planner's 32-row form is checked against the workspace call as well.
 """
 import numpy as np
 import pytest
@@ -43,12 +46,20 @@ def _noalloc_vs_workspace(wl, seed, out_dtype):
     assert np.array_equal(h.double().cpu().numpy(), ref["h_out"])
 
 
-def test_noalloc_two_calls_second_smaller():
+def test_noalloc_two_calls_second_smaller(plan_override):
+    plan_override(stream_nr=1)
     big = inputs.workload("llama3-8b-decode")                     # 32 tokens, 96 shared tiles
     assert fra.describe_plan(big.M, big.hidden, big.n_qkv, torch.bfloat16, torch.bfloat16)["slots"] > 1
     _noalloc_vs_workspace(big, seed=0, out_dtype=torch.float32)
     smaller = small(M=5, hidden=1024, H=8, Hkv=2, D=64)             # fewer tokens, narrower rows
     _noalloc_vs_workspace(smaller, seed=1, out_dtype=torch.bfloat16)
+
+
+def test_noalloc_khalves():
+    big = inputs.workload("llama3-8b-decode")
+    p = fra.describe_plan(big.M, big.hidden, big.n_qkv, torch.bfloat16, torch.bfloat16)
+    assert ",n32," in p["kernel"] and p["slots"] == 1, p
+    _noalloc_vs_workspace(big, seed=2, out_dtype=torch.bfloat16)
 
 
 def test_noalloc_rejects_beyond_the_scratch():
