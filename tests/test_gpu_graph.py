@@ -6,7 +6,8 @@ give exactly the bits of eager calls on the same inputs, with eager work and
 synchronisations between replays.  Calls on two streams, each with its own
 workspace, may overlap: each must give the bits of the same call made alone.
 Each case covers one kernel family (weight streaming with shared tiles, its
-int8 form, the 128 x 512 kernel with split K, the fp32 tiled kernel).
+32-row form with K halves, its int8 form, the 128 x 512 kernel with split K,
+the fp32 tiled kernel).
 """
 import pytest
 import torch
@@ -21,6 +22,7 @@ TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 CASES = [
     dict(act="bf16", M=32, hidden=2048, H=8, Hkv=2, D=64, ffn=512),   # weight streaming, two per tile
+    dict(act="bf16", M=16, hidden=1024, H=64, Hkv=16, D=64, ffn=256),  # QKV: 32-row tiles with K halves
     dict(act="bf16", wdt="i8", M=16, hidden=2048, H=4, Hkv=2, D=32, ffn=400),
     dict(act="bf16", M=200, hidden=512, H=4, Hkv=2, D=64, ffn=384),   # 128 x 512 tiles, K split
     dict(act="f32", M=40, hidden=256, H=4, Hkv=2, D=32, ffn=96),      # tiled kernel
