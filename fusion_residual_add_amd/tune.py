@@ -8,7 +8,8 @@ call shape at a time:
 
 * candidates: every configuration the library can run for the shape -- the
   kernel family, and for the weight-streaming kernel the weight rows per
-  workgroup and the workgroup count, for the tiled and 128 x 512 kernels the
+  workgroup (32, 64, 128 or 256, as the weight dtype allows) and the
+  workgroup count, for the tiled and 128 x 512 kernels the
   K split -- deduplicated by the plan each one produces (fp_describe_plan);
 * each candidate is installed as a one-entry table (fp_tune_install), run
   once with fp32 outputs and checked against the planner's own result (the
@@ -53,10 +54,15 @@ def candidates(M: int, hidden: int, n_cols: int, act: torch.dtype, wdt: torch.dt
     stream_ok = act != torch.float32 and M <= 64 and hidden % 256 == 0
     big = M * hidden * 2 >= (1 << 32) or n_cols * hidden * 2 >= (1 << 32)
     if stream_ok:
-        quant = wdt in (torch.int8, torch.uint8, torch.float8_e4m3fn)      # int8 / int4 / E4M3 weights
+        # the instantiated rows per workgroup: 128 always; 64 and 32 (K halves,
+        # hidden a multiple of 512) for 16-bit and E4M3 weights without the
+        # gate/up pairing at up to 32 tokens; 256 for one-byte and 4-bit weights
+        quant = wdt in (torch.int8, torch.uint8, torch.float8_e4m3fn, torch.float4_e2m1fn_x2)
         rows = [128]
-        if not swiglu and not quant and M <= 32:
+        if not swiglu and M <= 32 and wdt not in (torch.int8, torch.uint8, torch.float4_e2m1fn_x2):
             rows.append(64)
+            if hidden % 512 == 0:
+                rows.append(32)
         if quant:
             rows.append(256)
         for r in rows:

@@ -690,4 +690,10 @@ def test_tuner_candidates_cover_every_family():
         kernels = {c["plan"]["kernel"] for c in tune.candidates(16, 1024, 1024, torch.bfloat16, w, False)}
         if w != torch.bfloat16:
             assert any(",n256," in k for k in kernels), kernels   # 256 rows per workgroup for int8 / int4
+        else:   # 16-bit weights without gate/up pairing: 32, 64 and 128 rows
+            assert {k.split(",")[2] for k in kernels if k.startswith("stream")} == {"n32", "n64", "n128"}, kernels
+    # E4M3 QKV at decode counts: every instantiated row count of the streaming kernel
+    c = tune.candidates(16, 4096, 6144, torch.bfloat16, torch.float8_e4m3fn, False)
+    st = {x["plan"]["kernel"].split(",")[2] for x in c if x["plan"]["kernel"].startswith("stream")}
+    assert st == {"n32", "n64", "n128", "n256"}, st
     assert fra.tune_count() == 0
