@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,13 +35,25 @@ MFMA_FP8_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 MFMA
 MALL_BYTES = 256 << 20
 
 
-def kernel_source_hash() -> str:
+_COMMENT_OR_STRING = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """C++ / HIP source with its comments removed (string literals kept) and
+    every run of white space made one space."""
+    return " ".join(_COMMENT_OR_STRING.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", src).split())
+
+
+def kernel_source_hash(csrc: str = "") -> str:
+    """Hash of the library sources' code (comments excluded: they change no
+    kernel), which keys the stored traffic counters to the code they were
+    taken on."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "fusion_residual_add_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "fusion_residual_add_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode())
-            h.update(fh.read())
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

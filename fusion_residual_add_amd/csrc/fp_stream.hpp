@@ -5,18 +5,19 @@
 //
 // Design:
 //  * Work is split stream-K style: the (weight tile of NB = 64 * NR rows,
-//    K chunk of 32 * U) units are laid out tile by tile and every workgroup
-//    takes an equal contiguous range of them, so all CUs stream the same
-//    number of bytes whatever the tile count.  A range covers one or more
-//    tile segments; a tile covered by several workgroups is finished by the
-//    last of them to arrive, which adds the partial sums in a fixed order.
+//    or 32 with K halves, K chunk of 32 * U) units are laid out tile by tile
+//    and every workgroup takes an equal contiguous range of them, so all CUs
+//    stream the same number of bytes whatever the tile count.  A range
+//    covers one or more tile segments; a tile covered by several workgroups
+//    is finished by the last of them to arrive, which adds the partial sums
+//    in a fixed order.
 //  * Weights go straight from HBM into registers in the MFMA B-operand layout
 //    (lane l: row l % 16, eight consecutive k at group l / 16), a whole chunk
-//    per wave in flight (NR * U 16-byte loads per lane), reloaded slice by
-//    slice as the MFMAs consume them.  int8 weights are dequantised in
-//    registers; one 16-byte load then feeds two MFMAs.  int4 weights likewise,
-//    one 16-byte load (32 values of one 128-wide scale group) feeding four
-//    MFMAs, the group scales loaded with the chunk.
+//    per wave in flight (16-bit weights: NR * U / KH 16-byte loads per
+//    lane), reloaded slice by slice as the MFMAs consume them.  int8 weights
+//    are dequantised in registers; one 16-byte load then feeds two MFMAs.
+//    int4 weights likewise, one 16-byte load (32 values of one 128-wide scale
+//    group) feeding four MFMAs, the group scales loaded with the chunk.
 //  * The activation side of each chunk -- the rows of all M tokens, as the
 //    row pass formed them once per call (h = x + r, normalised, rounded to
 //    the activation dtype), or the per-token E4M3 codes -- is read (an L2

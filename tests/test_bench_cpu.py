@@ -72,3 +72,20 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+def test_source_hash_ignores_comments(tmp_path):
+    """The stored traffic counters are keyed by the sources' code: a comment
+    or a reflowed line changes no kernel, any code change does."""
+    src = 'int f(int a) { // add one\n  return a + 1; /* "x" */ }\nconst char *s = "// kept";\n'
+    assert bench.code_text(src) == 'int f(int a) { return a + 1; } const char *s = "// kept";'
+    d = tmp_path / "csrc"
+    d.mkdir()
+    (d / "k.hip").write_text(src)
+    h0 = bench.kernel_source_hash(str(d))
+    (d / "k.hip").write_text("// header\n" + src.replace("// add one", "// adds\n// one"))
+    assert bench.kernel_source_hash(str(d)) == h0
+    (d / "k.hip").write_text(src.replace("a + 1", "a + 2"))
+    assert bench.kernel_source_hash(str(d)) != h0
+    (d / "k.hip").write_text(src.replace('"// kept"', '"// changed"'))
+    assert bench.kernel_source_hash(str(d)) != h0
