@@ -163,7 +163,8 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
 // 33.8 us: a longer pipeline ramp for the few chunks per workgroup.)
 int stream_chunk(int64_t M) { return M > 32 ? 128 : 256; }
 
-void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool qw, bool swiglu, const Knobs &kb) {
+void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool qw, bool swiglu, const Knobs &kb,
+                 bool packed) {
     p.sc.mf = M <= 16 ? 1 : M <= 32 ? 2 : 4;
     // weight rows per workgroup 64 * nr: int8 weights at 33..64 tokens take
     // 256 when that still leaves >= 128 tiles (the A tile every workgroup
@@ -176,6 +177,16 @@ void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool q
     // packed weights 2 us; with int8 weights, or at 33..64 tokens where the
     // A tile is four times as large, 64-row tiles are slower)
     p.sc.nr = qw && p.sc.mf >= 4 && Nw / 256 >= 128 ? 4 : 2;
+    // On tile-packed weights at up to 32 tokens, int8 and MXFP4 gate/up
+    // weights take 256 rows where the 256-row tiles fill 75-100 % of the
+    // workgroups, one whole tile each (measured on MI355X by the tuner's HIP
+    // events, Llama-2-70B gate/up, 224 tiles: int8 100.5 -> 90.2 us at 1
+    // token, 97.6 -> 90.7 us at 16; MXFP4 87.2 -> 83.7 us at 16; int4 stays
+    // faster at 128 rows)
+    const int64_t t256 = (Nw + 255) / 256;
+    if (packed && swiglu && (wdt == FP_I8 || wdt == FP_MXFP4) && p.sc.mf <= 2 && t256 <= kb.target &&
+        t256 * 100 >= kb.target * 75)
+        p.sc.nr = 4;
     const bool nr1_ok = !swiglu && (!qw || wdt == FP_E4M3) && p.sc.mf <= 2;   // the instantiated 64-row forms
     if (nr1_ok) p.sc.nr = 1;
     // requested rows: only the instantiated forms (64 for 16-bit and E4M3
@@ -226,17 +237,26 @@ void plan_stream(Plan &p, int64_t M, int64_t K, int64_t Nw, fp_dtype wdt, bool q
     // MB, s = 1: 51.3 -> 49.3 us with the weights in the last-level cache,
     // 0.3 % of the decode step with them streamed from HBM; the gate/up of
     // Llama-2-70B's 8-way shard, 56 tiles, s = 4: 24.6 -> 23.4 us;
-    // Llama-2-70B int8 gate/up, 224 tiles of 470 MB, 6 % slower so; an
-    // uneven 1/s of K, 32 chunks in 3, 1 us slower; Llama-3-8B QKV on
-    // tile-packed weights, s = 2 of 64-row tiles (bf16) or s = 4 of 128-row
-    // tiles (E4M3) on 192 workgroups: 1.5 / 3.0 us faster than stream-K over
-    // 256, hence the three quarters)
+    // Llama-2-70B int8 gate/up on row-major weights, 224 tiles of 470 MB, 6 %
+    // slower so; there, an uneven 1/s of K, 32 chunks in 3, 1 us slower;
+    // Llama-3-8B QKV on tile-packed weights, s = 2 of 64-row tiles (bf16) or
+    // s = 4 of 128-row tiles (E4M3) on 192 workgroups: 1.5 / 3.0 us faster
+    // than stream-K over 256, hence the three quarters).  On tile-packed
+    // weights whole tiles also pay for weights over 256 MB at up to 32 tokens
+    // (the int8 gate/up above) and an uneven 1/s of K is taken (Llama-2-70B
+    // QKV, 80 tiles, s = 3 on 240 workgroups against stream-K over 256, by
+    // the tuner's HIP events: int8 31.3 -> 28.5 us at 1 token, 32.1 -> 29.8
+    // at 16, 48.1 -> 45.8 at 64; int4 28.4 -> 26.7 and MXFP4 30.3 -> 29.8 us
+    // at 1 / 16 tokens); at 33..64 tokens a weight over 256 MB stays on
+    // stream-K (int8 gate/up at 64 tokens: 127.3 us over 256 workgroups,
+    // 129.3 us in whole tiles)
     const int64_t wbytes = (wdt == FP_I4 || wdt == FP_MXFP4) ? Nw * K / 2
                            : Nw * K * ((wdt == FP_I8 || wdt == FP_E4M3) ? 1 : 2);
-    if (wbytes <= (int64_t(256) << 20) && tiles > 0) {
+    const bool small_w = wbytes <= (int64_t(256) << 20);
+    if ((small_w || (packed && p.sc.mf <= 2)) && tiles > 0) {
         for (int64_t s = target / tiles < ksteps / minc ? target / tiles : ksteps / minc; s >= 1; --s) {
             if (tiles * s * 100 < target * 75) break;
-            if (ksteps % s == 0) {
+            if (packed || ksteps % s == 0) {
                 G = tiles * s;
                 break;
             }
@@ -310,7 +330,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         if (M <= 64 && K % stream_chunk(M) == 0 && kb.fp8_tile == 0 && !kb.no_stream &&
             (kb.family == 1 || (kb.family == -1 && wl != fp::WL_ROWS))) {
             p.stream8 = true;
-            plan_stream(p, M, K, Nw, wdt, true, swiglu, kb);
+            plan_stream(p, M, K, Nw, wdt, true, swiglu, kb, wl != fp::WL_ROWS);
             const int64_t tiles = p.tiles_n;
             size_t off = 0;
             p.ctr_off = off;
@@ -402,7 +422,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     int64_t tiles, ksteps, target;
     if (fam == 1) {
         p.family = 1;
-        plan_stream(p, M, K, Nw, wdt, qw, swiglu, kb);
+        plan_stream(p, M, K, Nw, wdt, qw, swiglu, kb, wl != fp::WL_ROWS);
         tiles = p.tiles_n;
     } else if (fam == 2) {
         p.family = 2;

@@ -340,7 +340,11 @@ def test_packed_layout_rejects():
     assert gu(act=2, ffn=1040, wdt=BF16 | PK)[0] == "FP_E_SHAPE"      # 1040 rows
     L = lib()
     assert L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16 | 0x400) == 0
-    assert L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16 | PK) == L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16)
+    # the query covers both calls on that layout (plans may differ by layout)
+    need = {lay: max(fra.describe_plan(32, 4096, 6144, torch.bfloat16, torch.bfloat16, fn, layout=lay)["workspace"]
+                     for fn in ("none", "swiglu")) for lay in ("rows", "packed")}
+    assert L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16 | PK) == need["packed"]
+    assert L.fp_workspace_bytes(32, 4096, 6144, BF16, BF16) == need["rows"]
 
 
 def test_pack_weight_rejects():
