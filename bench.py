@@ -401,16 +401,18 @@ def library_kernel_name(cxx: str) -> str:
     import re
     # the second template argument: the weight storage (false / 0: the
     # activation dtype, true / 1: int8, 2: int4, 3: MXFP4, 4: E4M3 with E4M3 activation codes)
-    # the last one: K parts per chunk (2: 32 weight rows per workgroup of one 16-row fragment)
-    m = re.search(r"fp::stream_kernel<(\d), (true|false|\d), (\d+), (\d+), (\d+), (\d)(?:, (\d))?>", cxx)
+    # the seventh: K parts per chunk (2: 32 weight rows per workgroup of one 16-row fragment);
+    # the eighth: nonzero when the kernel forms the normalised rows itself
+    m = re.search(r"fp::stream_kernel<(\d), (true|false|\d), (\d+), (\d+), (\d+), (\d)(?:, (\d))?(?:, (\d))?>", cxx)
     if m:
         wq = {"true": "1", "false": "0"}.get(m.group(2), m.group(2))
         act = {"1": "bf16-i8w", "2": "bf16-i4w", "3": "bf16-mxfp4w"}.get(wq) or _ACT[m.group(1)]
         if wq == "4":
             act = _ACT[m.group(1)] + "-e4m3"
         kh = int(m.group(7) or 1)
+        rows = ",rows" if int(m.group(8) or 0) else ""
         return (f"stream_kernel<{act},m{16 * int(m.group(3))},n{64 * int(m.group(4)) // kh},"
-                f"k{32 * int(m.group(5))},{_EPI[m.group(6)]}>")
+                f"k{32 * int(m.group(5))},{_EPI[m.group(6)]}{rows}>")
     m = re.search(r"fp::prefill_kernel<(\d), (true|false|\d), (\d)(?:, (?:true|false))?>", cxx)
     if m:
         wq = {"true": "1", "false": "0"}.get(m.group(2), m.group(2))

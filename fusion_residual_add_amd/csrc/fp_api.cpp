@@ -9,7 +9,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
+#include <random>
 #include <string>
 #include <vector>
 
@@ -58,6 +60,7 @@ struct Plan {
     size_t rows_off = 0;            // gemm16: normalised rows [M, K]
     bool unpack = false;            // tile-packed weights unpacked into the workspace first (tiled family)
     size_t unpack_off = 0;
+    size_t flags_off = 0;           // stream with sc.rp: the rows' ready flags [M] (8 bytes each)
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -82,6 +85,7 @@ struct Knobs {
     int fp8_tile = 0;         // FP8 GEMM tile by token rows (overrides only)
     int gemm16_stages = 0;    // gemm16: LDS stages, 2, 4 or 5 (overrides only)
     bool no_stream = false, no_prefill = false, no_gemm16 = false;
+    bool no_stream_rows = false;   // stream: never the kernel's own row pass (overrides only)
 };
 
 std::mutex g_tune_mu;
@@ -99,6 +103,7 @@ const fp_plan_override &env_overrides() {
         o.fp8_tile = (int32_t)env_long("FUSEDPROJ_FP8_TILE", 0);
         o.no_gemm16 = env_long("FUSEDPROJ_NO_GEMM16", 0) != 0;
         o.gemm16_stages = (int32_t)env_long("FUSEDPROJ_GEMM16_STAGES", 0);
+        o.no_stream_rows = env_long("FUSEDPROJ_NO_STREAM_ROWS", 0) != 0;
         return o;
     }();
     return v;
@@ -143,6 +148,7 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
         if (kb.family == 4) kb.family = -1;
     }
     kb.gemm16_stages = o.gemm16_stages;
+    kb.no_stream_rows = o.no_stream_rows != 0;
     if (o.stream_nr > 0) kb.rows = 64 * o.stream_nr;
     if (o.splits > 0) {
         kb.splits = o.splits;
@@ -474,10 +480,19 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
     size_t off = 0;
     if (p.family == 1 && form_rows) {
         // the streaming kernel reads the rows the row pass forms (normalised,
-        // in the activation dtype) instead of normalising in every workgroup
+        // in the activation dtype) instead of normalising in every workgroup;
+        // the row pass runs inside the streaming kernel (sc.rp: M extra
+        // workgroups, one per token, while the others' first weights are in
+        // flight) for rows of up to 8192 values where the extra workgroups
+        // fit in the workgroup budget next to the streaming grid (on CUs it
+        // leaves idle), else as a launch of its own (also under graph
+        // capture: see run)
         p.rows = true;
         p.rows_off = off;
         off += rows_bytes;
+        p.flags_off = off;
+        off = align256(off + (size_t)M * 8);
+        p.sc.rp = K <= 8192 && p.grid + M <= kb.target && wdt != FP_E4M3 && !kb.no_stream_rows ? 1 : 0;
     } else {
         p.stats_off = off;
         off = align256(off + (size_t)M * 8);
@@ -767,6 +782,26 @@ fp_status run_gemm16(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     return FP_OK;
 }
 
+// true while work on s is being captured into a HIP graph (or when that
+// cannot be told: the separate row pass is right in either case)
+bool stream_capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) return true;
+    return st != hipStreamCaptureStatusNone;
+}
+
+// A tag for one launch of the streaming kernel's own row pass: distinct for
+// every launch in the process (a counter), and with its top bit set and a
+// random start, so that neither a tag of an earlier launch nor other data
+// left in a reused workspace equals it
+unsigned long long next_rp_tag() {
+    static std::atomic<unsigned long long> next{[] {
+        std::random_device rd;
+        return ((unsigned long long)rd() << 32 | rd()) | (1ull << 63);
+    }()};
+    return next.fetch_add(1, std::memory_order_relaxed);
+}
+
 fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     if (c.M == 0) return FP_OK;
     if (plan.family == 3) return run_fp8(c, plan, pa);
@@ -776,10 +811,16 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     float2 *stats = c.norm != FP_NORM_NONE && !plan.rows ? (float2 *)(ws + plan.stats_off) : nullptr;
     unsigned *ctr = plan.slots > 1 ? (unsigned *)(ws + plan.ctr_off) : nullptr;
     const int n_ctr = plan.slots > 1 ? plan.tiles_m * plan.tiles_n : 0;
+    // the streaming kernel forms the rows itself only outside graph capture:
+    // a replay repeats the launch's tag, so the flags the previous replay
+    // left would read as ready
+    fp::StreamCfg sc = plan.sc;
+    if (plan.family != 1 || !plan.rows || stream_capturing(c.stream)) sc.rp = 0;
 
     if (plan.rows) {
         // the row pass: h_out, the normalised rows (the A operand), and the
-        // split-K counters cleared
+        // split-K counters cleared -- a launch of its own, or the streaming
+        // kernel's first workgroups (sc.rp)
         fp::StatsArgs sa{};
         sa.x = c.x;
         sa.res = c.residual;
@@ -793,9 +834,15 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
         sa.gamma = c.gamma;
         sa.beta = c.norm == FP_NORM_LAYER ? c.beta : nullptr;
         sa.rows = ws + plan.rows_off;
-        ProfScope ps(fp::norm_kernel_name(act), c.stream);
-        hipError_t e = fp::launch_norm(act, sa, c.stream);
-        if (e != hipSuccess) return hip_fail(e, "norm_kernel launch");
+        if (sc.rp) {
+            pa.rp = sa;
+            pa.rp_flags = (unsigned long long *)(ws + plan.flags_off);
+            pa.rp_tag = next_rp_tag();
+        } else {
+            ProfScope ps(fp::norm_kernel_name(act), c.stream);
+            hipError_t e = fp::launch_norm(act, sa, c.stream);
+            if (e != hipSuccess) return hip_fail(e, "norm_kernel launch");
+        }
     } else if (stats || c.h_out || n_ctr) {
         fp::StatsArgs sa;
         sa.x = c.x;
@@ -860,8 +907,8 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
     pa.partials = plan.slots > 1 ? (float *)(ws + plan.part_off) : nullptr;
     pa.counters = ctr;
     if (plan.family == 1) {
-        ProfScope ps(fp::stream_kernel_name(act, wq, plan.sc, pa.epi), c.stream);
-        hipError_t e = fp::launch_stream(act, wq, plan.sc, pa, plan.grid, c.stream);
+        ProfScope ps(fp::stream_kernel_name(act, wq, sc, pa.epi), c.stream);
+        hipError_t e = fp::launch_stream(act, wq, sc, pa, plan.grid, c.stream);
         if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
     } else if (plan.family == 2) {
         ProfScope ps(fp::prefill_kernel_name(act, wq, pa.epi), c.stream);
@@ -1254,7 +1301,7 @@ fp_status fp_describe_plan(int64_t M, int64_t hidden, int64_t n_cols, fp_dtype a
     const int64_t grid = p.family == 1 ? p.grid : (int64_t)p.tiles_m * p.tiles_n * p.splits;
     const char *deq = !p.deq ? "" : w_dtype == FP_MXFP4 ? "dequant_mxfp4_kernel" : "dequant_i4_kernel";
     char prep[96] = "";
-    if (p.rows) snprintf(prep, sizeof prep, " prep=%s", fp::norm_kernel_name(a));
+    if (p.rows && !(p.family == 1 && p.sc.rp)) snprintf(prep, sizeof prep, " prep=%s", fp::norm_kernel_name(a));
     else if (p.unpack || p.deq)
         snprintf(prep, sizeof prep, " prep=%s%s%s", p.unpack ? "unpack_kernel" : "", p.unpack && p.deq ? "+" : "", deq);
     snprintf(buf, cap, "family=%s kernel=%s grid=%lld splits=%d slots=%d workspace=%zu%s", fam, name,
@@ -1292,7 +1339,8 @@ fp_status fp_plan_override_set(const fp_plan_override *o) {
                     (v.no_prefill == 0 || v.no_prefill == 1) &&
                     (v.fp8_tile == 0 || v.fp8_tile == 32 || v.fp8_tile == 64 || v.fp8_tile == 128 || v.fp8_tile == 256) &&
                     (v.no_gemm16 == 0 || v.no_gemm16 == 1) &&
-                    (v.gemm16_stages == 0 || v.gemm16_stages == 2 || v.gemm16_stages == 4 || v.gemm16_stages == 5);
+                    (v.gemm16_stages == 0 || v.gemm16_stages == 2 || v.gemm16_stages == 4 || v.gemm16_stages == 5) &&
+                    (v.no_stream_rows == 0 || v.no_stream_rows == 1);
     if (!ok) return fail(FP_E_ARG, "a plan override is out of range");
     std::lock_guard<std::mutex> lk(g_tune_mu);
     g_ov = v;

@@ -60,6 +60,23 @@ __host__ __device__ inline int64_t weight_off(int layout, int64_t r, int64_t c, 
     return layout == WL_ROWS ? r * row_bytes + c : packed_row_off(r, F, row_bytes, layout) + packed_col_off(c);
 }
 
+struct StatsArgs {
+    const void *x, *res;
+    void *h_out;
+    float2 *stats;
+    int norm;
+    float eps;
+    int64_t M, K;
+    unsigned *counters;
+    int n_counters;
+    // per-token E4M3 quantisation (quant8_kernel only)
+    const void *gamma, *beta;   // [K] act; beta LayerNorm only, may be null
+    unsigned char *codes;       // [M, K] E4M3 codes of the normalised rows
+    float *qscale;              // [M] dequantisation scale of each row
+    // normalised rows in the activation dtype (norm_kernel only)
+    void *rows;                 // [M, K] act
+};
+
 // Everything one projection launch needs.
 struct ProjArgs {
     // prologue inputs
@@ -94,24 +111,16 @@ struct ProjArgs {
                             // workgroups sharing one tile in the stream kernel)
     float *partials;        // [tile][slot][tile elements] partial sums
     unsigned *counters;     // per-tile arrival counters (splits > 1)
+    // the stream kernel's own row pass (its RP form): workgroups 0 .. M - 1
+    // each form one token row as norm_kernel does (rp: x, residual, gamma,
+    // beta, h_out, rows, the split-K counters to clear) and publish it by
+    // writing rp_tag to rp_flags[m]; every workgroup waits for all M flags
+    // before it reads the rows (x above is then rp.rows)
+    StatsArgs rp;
+    unsigned long long *rp_flags;   // [M]
+    unsigned long long rp_tag;      // this launch's tag (unique per launch in the process)
 };
 
-struct StatsArgs {
-    const void *x, *res;
-    void *h_out;
-    float2 *stats;
-    int norm;
-    float eps;
-    int64_t M, K;
-    unsigned *counters;
-    int n_counters;
-    // per-token E4M3 quantisation (quant8_kernel only)
-    const void *gamma, *beta;   // [K] act; beta LayerNorm only, may be null
-    unsigned char *codes;       // [M, K] E4M3 codes of the normalised rows
-    float *qscale;              // [M] dequantisation scale of each row
-    // normalised rows in the activation dtype (norm_kernel only)
-    void *rows;                 // [M, K] act
-};
 
 // Launch a kernel of 256-thread workgroups and return the status of this
 // launch itself (hipLaunchKernel's return value), never an error that an
@@ -131,7 +140,11 @@ hipError_t launch_tiled(int act, bool w_i8, int tile, const ProjArgs &a, hipStre
 //  wave (1 or 2; 2 for SwiGLU) -> 64 * nr weight rows per workgroup;
 //  u: 32-wide k slices per chunk (8) -> K must be a multiple of 32 * u.
 //  tiles_m must be 1.
-struct StreamCfg { int mf, nr, u, kh = 1; };   // kh: K parts per chunk (2: 32-row workgroups)
+struct StreamCfg {
+    int mf, nr, u, kh = 1;   // kh: K parts per chunk (2: 32-row workgroups)
+    int rp = 0;              // 1: the kernel's own row pass (ProjArgs::rp; 16-bit, int8, int4 and
+                             // MXFP4 weights; hidden <= 8192, M <= the grid)
+};
 // grid_wgs workgroups share the (weight tile, K chunk) units evenly
 hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a, int grid_wgs, hipStream_t s);
 hipError_t launch_dequant(const int8_t *q, const float *scale, void *out, int64_t N, int64_t K,

@@ -22,7 +22,10 @@ hipError_t launch_stream(int act, int wq, const StreamCfg &c, const ProjArgs &a,
     if (c.nr != 2 && !(c.nr == 1 && (wq == 0 || wq == 4) && c.mf <= 2) && !(c.nr == 4 && wq != 0))
         return hipErrorInvalidValue;
     if (c.kh != 1 && !(c.kh == 2 && c.nr == 1 && a.epi != EPI_SWIGLU)) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)grid_wgs;
+    // the kernel's own row pass: M more workgroups (one per token), rows of
+    // up to 8192 values
+    if (c.rp && (wq == 4 || a.M > 64 || a.rp.K > 8192 || !a.rp_flags)) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)(grid_wgs + (c.rp ? a.M : 0));
     if (wq == 1) return launch_stream_i8(c, a, grid, s);
     if (wq == 2) return launch_stream_i4(c, a, grid, s);
     if (wq == 3) return launch_stream_mx(c, a, grid, s);
@@ -62,8 +65,8 @@ const char *stream_kernel_name(int act, int wq, const StreamCfg &c, int epi) {
     static const char *epis[4] = {"qkv", "swiglu", "gelu", "linear"};
     thread_local char buf[64];
     const char *an = wq == 4 ? (act == ACT_F16 ? "f16-e4m3" : "bf16-e4m3") : acts[wq ? 2 + wq : act];
-    snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s>", an, 16 * c.mf,
-             64 * c.nr / c.kh, 32 * c.u, epis[epi]);
+    snprintf(buf, sizeof buf, "stream_kernel<%s,m%d,n%d,k%d,%s%s>", an, 16 * c.mf,
+             64 * c.nr / c.kh, 32 * c.u, epis[epi], c.rp ? ",rows" : "");
     return buf;
 }
 

@@ -31,7 +31,7 @@
 //  * Epilogue: bias, then the GQA split / SwiGLU / tanh-GELU / nothing.
 #pragma once
 
-#include "fp_device.hpp"
+#include "fp_rows.hpp"
 
 #include <cstdio>
 #include <type_traits>
@@ -52,7 +52,13 @@ namespace fp {
 // of a 64-row tile; the two halves' sums meet in LDS at the end.  The host
 // gives every such workgroup one whole tile (no partial sums between
 // workgroups), so a 6144-row QKV weight is 192 tiles on 192 workgroups.
-template <int ACT, int WQ, int MF, int NR, int U, int EPI, int KH>
+// RP: 0 -- the A rows come formed (p.x); RP > 0 -- the kernel forms them
+// itself (p.rp, hidden up to 2048 * RP): M extra workgroups, the first of the
+// launch, each run the row pass for one token and publish the row; every
+// other workgroup waits for all M rows after it has requested its first two
+// chunks of weights (see rp_wait).  The host takes this form where the extra
+// workgroups fit on CUs that the streaming grid leaves idle.
+template <int ACT, int WQ, int MF, int NR, int U, int EPI, int KH, int RP = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void stream_kernel(ProjArgs p) {
     constexpr bool WF8 = WQ == 4;
@@ -82,15 +88,78 @@ void stream_kernel(ProjArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave % NWR, kh = wave / NWR;   // the wave's row group and K part
     const int ub = kh * NLW;                      // its first load slice of a chunk
-    const int G = (int)gridDim.x;
-    const int g = xcd_remap(blockIdx.x, G);
+    const int G = (int)gridDim.x - (RP > 0 ? (int)p.M : 0);   // workgroups that stream
+    const int g = xcd_remap((int)blockIdx.x - (RP > 0 ? (int)p.M : 0), G);
     const int nchunks = (int)(p.K / CK);
     const int64_t units = (int64_t)p.tiles_n * nchunks;
     // workgroup holding unit v: the largest h with floor(h * units / G) <= v
     auto owner = [&](int64_t v) { return (int)(((v + 1) * G - 1) / units); };
 
+    // ---- the kernel's own row pass (RP > 0).  The launch has M extra
+    // workgroups, the first M (dispatched before any that waits for them):
+    // workgroup b forms token row b (h_out, the normalised row into
+    // p.rp.rows, the split-K counters cleared), waits for its stores to
+    // complete and publishes the row by storing this launch's tag into the
+    // row's flag.  Rows, counters and flags are written with device-coherent
+    // stores (complete at the device-wide coherence point, not in the XCD's
+    // L2), so a flag is visible only after the row it publishes is in
+    // memory; a waiting workgroup (rp_wait) reads the flags with
+    // device-coherent loads and only then issues its first load of the rows,
+    // which fills its XCD's L2 from memory: no L2 held the rows' lines when
+    // the launch started (the launch boundary writes back and invalidates the
+    // XCDs' L2s), and nothing in this launch reads them before their flags.
+    // (Fences at device scope instead write back and invalidate a whole L2 at
+    // every publication and wait: measured on MI355X, Llama-3-8B decode,
+    // 26.6 us against 23.6 us for the separate row pass + kernel on QKV.)
+    // Measured on MI355X, decode steps on tile-packed weights (median of 3 x
+    // 100 steps, both calls): Llama-3-8B 64.3 -> 63.6 us, Llama-2-70B int8 at
+    // 1 token 110.1 -> 108.1 us, at 16 tokens 113.1 -> 112.6 us, MXFP4 at 16
+    // 102.7 -> 97.2 us.  The gain is small because the hand-over is itself a
+    // chain of memory round trips (the rows' loads, the acknowledged stores,
+    // the flag, the poll, the rows' first load); waiting for the rows before
+    // requesting any weights measured slower (66.8 us for Llama-3-8B), and
+    // delaying the weight requests to let the rows' loads ahead gained nothing.
+    const int nprod = RP > 0 ? (int)p.M : 0;
+    if constexpr (RP > 0) {
+        if ((int)blockIdx.x < nprod) {
+            rows_fast<ACT, 256, RP, OUT_ROWS, true>(p.rp, (int)blockIdx.x, nprod);
+            __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have completed
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(&p.rp_flags[blockIdx.x], p.rp_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+    }
+    // Wait until all M flags hold this launch's tag (lane m of wave 0 polls
+    // row m's flag); the workgroup barrier then releases the other waves.
+    // The tag is unique per launch within the process, so a flag left by an
+    // earlier launch never reads as ready.  The wait is bounded (about a
+    // second): if it runs out the workgroup carries on and stores NaN, so a
+    // fault in the dispatch order shows in the outputs instead of hanging
+    // the device.  Returns false when it ran out.
+    auto rp_wait = [&]() -> bool {
+        bool ok = true;
+        if (wave == 0) {
+            ok = false;
+            for (int spin = 0; spin < (1 << 20); ++spin) {
+                const unsigned long long v =
+                    lane < p.M ? __hip_atomic_load(&p.rp_flags[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : p.rp_tag;
+                if (__ballot(v != p.rp_tag) == 0) {
+                    ok = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        return __syncthreads_or(ok ? 0 : 1) == 0;
+    };
+    bool rp_ok = true;
+
     // one tile segment: tile tn, chunks [c0, c1)
-    auto segment = [&](const int tn, const int c0, const int c1) {
+    // RPF (std::true_type): the launch's first segment of an RP kernel
+    auto segment = [&](const int tn, const int c0, const int c1, auto rpf) {
+        constexpr bool RPF = decltype(rpf)::value;
         // ---- this lane's weight rows of tile tn (one per fragment).  Rows past the end are
         // clamped to a valid row: the garbage they produce stays in their own
         // accumulator column, which the epilogue never stores.  Keeping every load
@@ -323,18 +392,30 @@ void stream_kernel(ProjArgs p) {
         const std::false_type N{};
         const int nc = c1 - c0;
         if (nc > 0) {
-            // prologue, in issue order: the activations of chunk c0 (needed
-            // first), then the weights of c0, the activations and weights of
-            // c0 + 1; the fences keep the scheduler from moving a weight burst
-            // in front of the loads that the first LDS copy waits for
-            aload(c0, A0);
-            __builtin_amdgcn_sched_barrier(0);
-            wload_all(c0, W0);
             // unconditional (a branch here would make the compiler drain every load
             // at the join); a one-chunk range just reads its chunk twice
             const int c0n = nc > 1 ? c0 + 1 : c0;
-            aload(c0n, A1);
-            wload_all(c0n, W1);
+            if constexpr (RPF) {
+                // the weights of c0 and c0 + 1 first, then the wait for the
+                // rows, then their activations
+                wload_all(c0, W0);
+                wload_all(c0n, W1);
+                __builtin_amdgcn_sched_barrier(0);
+                rp_ok = rp_wait();
+                __builtin_amdgcn_sched_barrier(0);
+                aload(c0, A0);
+                aload(c0n, A1);
+            } else {
+                // prologue, in issue order: the activations of chunk c0 (needed
+                // first), then the weights of c0, the activations and weights of
+                // c0 + 1; the fences keep the scheduler from moving a weight burst
+                // in front of the loads that the first LDS copy waits for
+                aload(c0, A0);
+                __builtin_amdgcn_sched_barrier(0);
+                wload_all(c0, W0);
+                aload(c0n, A1);
+                wload_all(c0n, W1);
+            }
             __builtin_amdgcn_sched_barrier(0);
             astore(0, A0);
             __syncthreads();
@@ -397,6 +478,14 @@ void stream_kernel(ProjArgs p) {
 
         // ---- epilogue: lane holds token rows 16 m + 4 (lane / 16) + e of weight row lane % 16
         if (kh) return;
+        if constexpr (RP > 0) {
+            if (!rp_ok) {
+    #pragma unroll
+                for (int m = 0; m < MF; ++m)
+    #pragma unroll
+                    for (int n = 0; n < NR; ++n) acc[m][n] = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            }
+        }
     #pragma unroll
         for (int m = 0; m < MF; ++m) {
     #pragma unroll
@@ -437,8 +526,13 @@ void stream_kernel(ProjArgs p) {
         // last chunk possibly read from LDS buffer 0: every wave must be done
         // with it before the next segment's prologue normalises into buffer 0
         if (!first_segment) __syncthreads();
+        if constexpr (RP > 0) {
+            if (first_segment) segment(tn, c0, c1, std::true_type{});
+            else segment(tn, c0, c1, std::false_type{});
+        } else {
+            segment(tn, c0, c1, std::false_type{});
+        }
         first_segment = false;
-        segment(tn, c0, c1);
         u += c1 - c0;
     }
 }
@@ -446,20 +540,32 @@ void stream_kernel(ProjArgs p) {
 // ---------------------------------------------------------------------------
 // launch helpers (instantiated per activation / weight dtype in fp_stream_*.hip)
 // ---------------------------------------------------------------------------
-template <int ACT, int WQ, int MF, int NR, int U, int KH = 1>
-inline hipError_t launch_stream_cfg(int epi, const ProjArgs &a, unsigned grid, hipStream_t s) {
+template <int ACT, int WQ, int MF, int NR, int U, int KH, int RP>
+inline hipError_t launch_stream_epi(int epi, const ProjArgs &a, unsigned grid, hipStream_t s) {
     switch (epi) {
     case EPI_QKV:
-        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_QKV, KH>, grid, s, a);
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_QKV, KH, RP>, grid, s, a);
     case EPI_SWIGLU:
         if constexpr (NR % 2 == 0 && KH == 1)
-            return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_SWIGLU, KH>, grid, s, a);
+            return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_SWIGLU, KH, RP>, grid, s, a);
         return hipErrorInvalidValue;
     case EPI_GELU:
-        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_GELU, KH>, grid, s, a);
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_GELU, KH, RP>, grid, s, a);
     default:
-        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_LINEAR, KH>, grid, s, a);
+        return launch_k(stream_kernel<ACT, WQ, MF, NR, U, EPI_LINEAR, KH, RP>, grid, s, a);
     }
+}
+
+// c.rp: the kernel's own row pass, for rows of up to 8192 values (four
+// 16-byte vectors per thread); not for the E4M3 path, whose A side is the
+// quantisation pass's codes
+template <int ACT, int WQ, int MF, int NR, int U, int KH = 1>
+inline hipError_t launch_stream_cfg(const StreamCfg &c, const ProjArgs &a, unsigned grid, hipStream_t s) {
+    if (c.rp) {
+        if constexpr (WQ != 4) return launch_stream_epi<ACT, WQ, MF, NR, U, KH, 4>(a.epi, a, grid, s);
+        return hipErrorInvalidValue;
+    }
+    return launch_stream_epi<ACT, WQ, MF, NR, U, KH, 0>(a.epi, a, grid, s);
 }
 
 // 64 token rows: 128-wide K chunks (two activation / weight register sets of
@@ -474,15 +580,15 @@ inline hipError_t launch_stream_mf(const StreamCfg &c, const ProjArgs &a, unsign
     constexpr int U = MF >= 4 ? 4 : 8;
     if (c.kh == 2) {
         if constexpr ((WQ == 0 || WQ == 4) && MF <= 2)
-            if (c.nr == 1) return launch_stream_cfg<ACT, WQ, MF, 1, 2 * U, 2>(a.epi, a, grid, s);
+            if (c.nr == 1) return launch_stream_cfg<ACT, WQ, MF, 1, 2 * U, 2>(c, a, grid, s);
         return hipErrorInvalidValue;
     }
-    if (c.nr == 2) return launch_stream_cfg<ACT, WQ, MF, 2, U>(a.epi, a, grid, s);
+    if (c.nr == 2) return launch_stream_cfg<ACT, WQ, MF, 2, U>(c, a, grid, s);
     if (c.nr == 1) {
-        if constexpr ((WQ == 0 || WQ == 4) && MF <= 2) return launch_stream_cfg<ACT, WQ, MF, 1, U>(a.epi, a, grid, s);
+        if constexpr ((WQ == 0 || WQ == 4) && MF <= 2) return launch_stream_cfg<ACT, WQ, MF, 1, U>(c, a, grid, s);
         return hipErrorInvalidValue;
     }
-    if constexpr (WQ != 0) return launch_stream_cfg<ACT, WQ, MF, 4, U>(a.epi, a, grid, s);   // 256 rows share one A tile
+    if constexpr (WQ != 0) return launch_stream_cfg<ACT, WQ, MF, 4, U>(c, a, grid, s);   // 256 rows share one A tile
     return hipErrorInvalidValue;
 }
 

@@ -40,8 +40,14 @@
  *    and enough tokens to fill the GPU with 256 x 256 tiles: prefill; see
  *    fp_describe_plan, prep=norm_kernel) have a row pass write the rounded
  *    rows once into the workspace (M * hidden * 2 bytes of it), which the
- *    projection reads: the same values.  In the other calls n never goes to
- *    memory.
+ *    projection reads: the same values.  In streaming calls with hidden up
+ *    to 8192 whose grid leaves a CU per token idle (kernel name ending in
+ *    ",rows"), M extra workgroups of the streaming launch itself form the rows
+ *    (one per token) and publish them through per-row flags in the workspace,
+ *    tagged per launch, while the other workgroups request their first
+ *    weights; under HIP graph capture (a replay would repeat the tag) and
+ *    with the no_stream_rows override the row pass stays a launch of its own.
+ *    In the other calls n never goes to memory.
  *  - Product: fp32 accumulation of n * W^T.
  *  - Int8 weights (w_dtype FP_I8, act_dtype FP_BF16 only): each element is
  *    dequantised as bf16_rne(f32_rne(q * w_scale[row])), bit-exactly the
@@ -109,8 +115,9 @@
  *  - Errors: every argument is validated before any HIP call; on any status
  *    other than FP_OK nothing has been enqueued and no memory was touched,
  *    except FP_E_HIP (a launch failed; fp_last_error() has the HIP text).
- *  - The workspace holds per-row statistics, normalised rows, split-K
- *    partial sums and arrival counters.  Its contents on entry do not matter.  Two calls that
+ *  - The workspace holds per-row statistics, normalised rows, the rows'
+ *    ready flags, split-K partial sums and arrival counters.  Its contents
+ *    on entry do not matter.  Two calls that
  *    run concurrently must not share a workspace.
  *  - Results are deterministic: the same inputs give the same bits.
  */
@@ -420,10 +427,13 @@ int64_t fp_tune_count(void);
  *  no_gemm16     : 1 = never the row pass + 256 x 256 GEMM
  *  gemm16_stages : 256 x 256 GEMM, LDS stages: 2 (K 64 per stage; taken
  *                  where hidden is a multiple of 128), 4 or 5 (K 32)
+ *  no_stream_rows: 1 = the streaming kernel never forms the normalised rows
+ *                  itself (a separate row-pass launch forms them first, as
+ *                  under HIP graph capture)
  * The initial values come from the environment variables FUSEDPROJ_SPLITS,
  * FUSEDPROJ_STREAM_NR, FUSEDPROJ_STREAM_TARGET, FUSEDPROJ_NO_STREAM,
- * FUSEDPROJ_NO_PREFILL, FUSEDPROJ_FP8_TILE, FUSEDPROJ_NO_GEMM16 and
- * FUSEDPROJ_GEMM16_STAGES, read once, at the first call that plans a
+ * FUSEDPROJ_NO_PREFILL, FUSEDPROJ_FP8_TILE, FUSEDPROJ_NO_GEMM16,
+ * FUSEDPROJ_GEMM16_STAGES and FUSEDPROJ_NO_STREAM_ROWS, read once, at the first call that plans a
  * launch; no call reads the environment after that.
  * fp_plan_override_set replaces the overrides (NULL restores the values read
  * from the environment); FP_E_ARG if a field is out of range.  Process-wide,
@@ -438,6 +448,7 @@ typedef struct {
     int32_t fp8_tile;
     int32_t no_gemm16;
     int32_t gemm16_stages;
+    int32_t no_stream_rows;
 } fp_plan_override;
 
 fp_status fp_plan_override_set(const fp_plan_override *o);

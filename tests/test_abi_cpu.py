@@ -283,7 +283,10 @@ def test_fp8_plans(plan_override):
             if M <= 32 and not sw:
                 assert (",n32,k512," if N == 6144 else ",n64,") in a["kernel"], a
             elif N != 768:
-                assert a["kernel"].split(",", 1)[1] == b["kernel"].split(",", 1)[1] and a["grid"] == b["grid"], (a, b)
+                # (the int8 call's kernel forms the rows itself; the E4M3
+                # call's quantisation pass stays a launch of its own)
+                assert a["kernel"].split(",", 1)[1] == b["kernel"].split(",", 1)[1].replace(",rows>", ">") and \
+                    a["grid"] == b["grid"], (a, b)
         fra.tune_install([dict(m_lo=0, m_hi=64, hidden=4096, n_cols=6144, act_dtype=torch.float16, w_dtype=e,
                                swiglu=False, family="stream")])
         assert _plan(16, 4096, 6144, act=torch.float16, w=e)["kernel"] == "stream_kernel<f16-e4m3,m16,n32,k512,linear>"
@@ -377,7 +380,8 @@ def test_packed_plans(plan_override):
     assert p["family"] == "tiled" and p["prep"] == "unpack_kernel"
     assert p["workspace"] >= fra.describe_plan(40, 320, 6144, b, b)["workspace"] + 6144 * 320 * 2
     p = fra.describe_plan(40, 512, 1024, b, torch.uint8, "swiglu", layout="packed_gate_up")
-    assert p["family"] == "stream" and p["prep"] == "norm_kernel<bf16>"
+    # the streaming grid leaves CUs for one workgroup per token: the kernel forms the rows
+    assert p["family"] == "stream" and p["kernel"].endswith(",rows>") and "prep" not in p, p
     with fra.plan_override(no_stream=1):
         p = fra.describe_plan(40, 512, 1024, b, torch.uint8, "swiglu", layout="packed_gate_up")
         assert p["family"] == "tiled" and p["prep"] == "unpack_kernel+dequant_i4_kernel", p
@@ -404,7 +408,7 @@ def test_plan_routing_families(plan_override):
     plan_override()
     # decode token counts with K a multiple of 256: the weight-streaming kernel
     p = _plan(32, 4096, 2 * 14336, fn="swiglu")
-    assert p["family"] == "stream" and p["kernel"] == "stream_kernel<bf16,m32,n128,k256,swiglu>"
+    assert p["family"] == "stream" and p["kernel"] == "stream_kernel<bf16,m32,n128,k256,swiglu,rows>"
     # 224 tiles of a 235 MB weight: one whole tile per workgroup, nothing shared
     assert p["grid"] == 224 and p["slots"] == 1
     # the same tile count on a 470 MB weight: stream-K over 256 workgroups
@@ -413,14 +417,14 @@ def test_plan_routing_families(plan_override):
     # 16-bit QKV weights at up to 32 tokens: 32-row tiles with K halves (192
     # of them: at least three quarters of the CUs), one whole tile per workgroup
     p = _plan(32, 4096, 6144)
-    assert p["kernel"] == "stream_kernel<bf16,m32,n32,k512,linear>" and p["grid"] == 192 and p["slots"] == 1
+    assert p["kernel"] == "stream_kernel<bf16,m32,n32,k512,linear,rows>" and p["grid"] == 192 and p["slots"] == 1
     # more 32-row tiles than workgroups (Llama-2-7B QKV): 64-row tiles, one each
     p = _plan(16, 4096, 12288)
-    assert p["kernel"] == "stream_kernel<bf16,m16,n64,k256,linear>" and p["grid"] == 192 and p["slots"] == 1
+    assert p["kernel"] == "stream_kernel<bf16,m16,n64,k256,linear,rows>" and p["grid"] == 192 and p["slots"] == 1
     # requested: 64 rows, two workgroups per tile; or 32 rows where 64 would be chosen
     with fra.plan_override(stream_nr=1):
         p = _plan(32, 4096, 6144)
-        assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear>" and p["grid"] == 192 and p["slots"] == 2
+        assert p["kernel"] == "stream_kernel<bf16,m32,n64,k256,linear,rows>" and p["grid"] == 192 and p["slots"] == 2
     try:
         fra.tune_install([dict(m_lo=0, m_hi=64, hidden=4096, n_cols=12288, act_dtype=torch.bfloat16,
                                w_dtype=torch.bfloat16, swiglu=False, family="stream", rows=32)])
@@ -437,7 +441,7 @@ def test_plan_routing_families(plan_override):
     finally:
         fra.tune_clear()
     # 33..64 tokens keep 128-row tiles
-    assert _plan(64, 4096, 6144)["kernel"] == "stream_kernel<bf16,m64,n128,k128,linear>"
+    assert _plan(64, 4096, 6144)["kernel"] == "stream_kernel<bf16,m64,n128,k128,linear,rows>"
     # Llama-2-70B's 8-way shard: QKV (10 tiles x 32 chunks) on 160 workgroups of
     # 2 chunks; gate/up (56 tiles x 32 chunks) 4 workgroups per tile, 8 chunks each
     p = _plan(1, 8192, 1280, w=torch.int8)
@@ -515,7 +519,7 @@ def test_plan_overrides(plan_override):
     assert _plan(300, 4096, 6144)["family"] == "tiled"
     assert _plan(32, 4096, 6144)["family"] == "stream"
     plan_override(stream_nr=2)
-    assert _plan(8, 4096, 6144)["kernel"] == "stream_kernel<bf16,m16,n128,k256,linear>"
+    assert _plan(8, 4096, 6144)["kernel"] == "stream_kernel<bf16,m16,n128,k256,linear,rows>"
     plan_override(stream_target=64)
     assert _plan(8, 4096, 28672, fn="swiglu")["grid"] == 64
     plan_override(no_gemm16=1)
@@ -529,13 +533,16 @@ def test_plan_overrides(plan_override):
     assert _plan(16384, 4160, 12288)["kernel"] == "gemm16_kernel<bf16,256x256,4st,linear>"
     plan_override(no_gemm16=1, no_prefill=1)
     assert _plan(16384, 4096, 12288)["family"] == "tiled"
+    plan_override(no_stream_rows=1)
+    p = _plan(32, 4096, 6144)
+    assert p["kernel"] == "stream_kernel<bf16,m32,n32,k512,linear>" and p["prep"] == "norm_kernel<bf16>"
     plan_override()
     assert fra.get_plan_override() == dict(splits=0, stream_nr=0, stream_target=0, no_stream=0, no_prefill=0,
-                                           fp8_tile=0, no_gemm16=0, gemm16_stages=0)
+                                           fp8_tile=0, no_gemm16=0, gemm16_stages=0, no_stream_rows=0)
     # out-of-range values are rejected and leave the overrides as they were
     plan_override(splits=2)
     for bad in (dict(splits=65), dict(splits=-1), dict(stream_nr=3), dict(no_stream=2), dict(fp8_tile=100),
-                dict(stream_target=70000), dict(no_gemm16=2), dict(gemm16_stages=3)):
+                dict(stream_target=70000), dict(no_gemm16=2), dict(gemm16_stages=3), dict(no_stream_rows=2)):
         with pytest.raises(fra.FusedProjError) as ei:
             fra.set_plan_override(bad)
         assert ei.value.status == 8                     # FP_E_ARG
@@ -597,7 +604,7 @@ def test_tuning_table_overrides_matching_calls(plan_override):
         fra.tune_install([_entry(family="stream", rows=128, grid=192)])
         assert fra.tune_count() == 1
         p = _plan(32, 4096, 6144)
-        assert p["kernel"] == "stream_kernel<bf16,m32,n128,k256,linear>" and p["grid"] == 192
+        assert p["kernel"] == "stream_kernel<bf16,m32,n128,k256,linear,rows>" and p["grid"] == 192
         assert _plan(17, 4096, 6144)["grid"] == 192
         # other token counts, the gate/up pairing and other sizes keep the planner's choice
         assert _plan(33, 4096, 6144) == base_33
@@ -619,7 +626,7 @@ def test_tuning_table_overrides_matching_calls(plan_override):
         fra.tune_install([_entry(rows=64, swiglu=True)])
         assert _plan(32, 4096, 6144, fn="swiglu") == base_gu
         fra.tune_install([_entry(rows=128)])
-        assert _plan(32, 4096, 6144)["kernel"] == "stream_kernel<bf16,m32,n128,k256,linear>"
+        assert _plan(32, 4096, 6144)["kernel"] == "stream_kernel<bf16,m32,n128,k256,linear,rows>"
         # the first matching entry wins; the plan overrides win over the table
         fra.tune_install([_entry(grid=128), _entry(grid=64)])
         assert _plan(32, 4096, 6144)["grid"] == 128

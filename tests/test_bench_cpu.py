@@ -47,6 +47,9 @@ def test_algo_bytes_down():
     ("void fp::stream_kernel<2, 0, 2, 2, 8, 1, 1>(fp::ProjArgs)", "stream_kernel<bf16,m32,n128,k256,swiglu>"),
     ("void fp::stream_kernel<2, 0, 2, 1, 16, 0, 2>(fp::ProjArgs)", "stream_kernel<bf16,m32,n32,k512,qkv>"),
     ("void fp::stream_kernel<2, 4, 1, 1, 16, 3, 2>(fp::ProjArgs)", "stream_kernel<bf16-e4m3,m16,n32,k512,linear>"),
+    ("void fp::stream_kernel<2, 0, 2, 1, 16, 0, 2, 0>(fp::ProjArgs)", "stream_kernel<bf16,m32,n32,k512,qkv>"),
+    ("void fp::stream_kernel<2, 0, 2, 1, 16, 0, 2, 4>(fp::ProjArgs)", "stream_kernel<bf16,m32,n32,k512,qkv,rows>"),
+    ("void fp::stream_kernel<2, 1, 1, 4, 8, 1, 1, 4>(fp::ProjArgs)", "stream_kernel<bf16-i8w,m16,n256,k256,swiglu,rows>"),
     ("void fp::prefill_kernel<1, 0, 2, true>(fp::ProjArgs)", "prefill_kernel<f16,128x512,gelu>"),
     ("void fp::prefill_kernel<2, 1, 1, false>(fp::ProjArgs)", "prefill_kernel<bf16-i8w,128x512,swiglu>"),
     ("void fp::stats_kernel<2, 256>(fp::StatsArgs)", "stats_kernel<bf16>"),

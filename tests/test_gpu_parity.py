@@ -526,21 +526,29 @@ def test_qkv_head_major(cfg, native):
 # ---------------------------------------------------------------------------
 # the row pass of the decode path: the streaming kernel's A operand
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("own", [False, True], ids=["rowpass", "inkernel"])
 @pytest.mark.parametrize("cfg", [dict(M=1, hidden=512), dict(M=32, hidden=768, norm="layer"),
                                  dict(M=64, hidden=512, act="f16"), dict(M=17, hidden=1024, norm="none"),
                                  dict(M=9, hidden=512, wdt="i8")],
                          ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
-def test_stream_rows(cfg):
+def test_stream_rows(cfg, own, plan_override):
     """The rows the row pass leaves at the start of the workspace of a
     streaming call, bit for bit against the oracle's rows of the
-    single-precision reading (they are the kernel's A operand as they are)."""
+    single-precision reading (they are the kernel's A operand as they are):
+    from the row-pass launch, and from the streaming kernel's own row pass
+    (its first M workgroups)."""
+    plan_override(no_stream_rows=0 if own else 1)
     wl = small(**cfg)
     inp = inputs.generate(wl, seed=17)
     d = to_dev(inp)
     act = TDT[wl.act]
     wdt = d["w_gu"].dtype
     plan = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, act, wdt, wl.act_fn)
-    assert plan["family"] == "stream" and plan["prep"].startswith("norm_kernel"), plan
+    assert plan["family"] == "stream", plan
+    if own and plan["grid"] + wl.M <= 256:
+        assert plan["kernel"].endswith(",rows>") and "prep" not in plan, plan
+    else:
+        assert plan["prep"].startswith("norm_kernel"), plan
     need = fra.workspace_bytes(wl.M, wl.hidden, wl.n_gu, act, wdt)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
     out = fra.fused_gateup_act(d["x"], d["r"], d["gamma"], d["w_gu"], wl.ffn, wl.act_fn, beta=d.get("beta"),
