@@ -438,6 +438,17 @@ void stream_kernel(ProjArgs p) {
             }
         }
 
+        // a workgroup whose wait for the rows ran out stores NaN (its partial
+        // sums, if it shares the tile, carry them to the tile's last arriver)
+        if constexpr (RP > 0) {
+            if (!rp_ok) {
+    #pragma unroll
+                for (int m = 0; m < MF; ++m)
+    #pragma unroll
+                    for (int n = 0; n < NR; ++n) acc[m][n] = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            }
+        }
+
         // ---- K halves: the second half's waves hand their sums to the first
         // half's waves of the same row group through LDS (then hold zeros, so
         // that a shared tile's partial sums below stay whole-workgroup)
@@ -478,14 +489,6 @@ void stream_kernel(ProjArgs p) {
 
         // ---- epilogue: lane holds token rows 16 m + 4 (lane / 16) + e of weight row lane % 16
         if (kh) return;
-        if constexpr (RP > 0) {
-            if (!rp_ok) {
-    #pragma unroll
-                for (int m = 0; m < MF; ++m)
-    #pragma unroll
-                    for (int n = 0; n < NR; ++n) acc[m][n] = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-            }
-        }
     #pragma unroll
         for (int m = 0; m < MF; ++m) {
     #pragma unroll
