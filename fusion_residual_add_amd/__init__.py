@@ -441,7 +441,7 @@ def tune_count() -> int:
 
 
 _OVERRIDE_FIELDS = ("splits", "stream_nr", "stream_target", "no_stream", "no_prefill", "fp8_tile", "no_gemm16",
-                    "gemm16_stages", "no_stream_rows")
+                    "gemm16_stages", "no_stream_rows", "stream_rows_expire")
 
 
 def get_plan_override() -> dict:
@@ -454,7 +454,7 @@ def get_plan_override() -> dict:
 def set_plan_override(values: Optional[dict]) -> None:
     """Replace the plan overrides (fp_plan_override_set): a dict with any of
     splits, stream_nr, stream_target, no_stream, no_prefill, fp8_tile, no_gemm16, gemm16_stages,
-    no_stream_rows (missing
+    no_stream_rows, stream_rows_expire (missing
     fields 0 = the planner's choice); None restores the values the FUSEDPROJ_*
     environment variables held when the library first planned a call."""
     import ctypes

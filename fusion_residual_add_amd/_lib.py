@@ -45,7 +45,8 @@ class PlanOverride(ctypes.Structure):
     """fp_plan_override of include/fusedproj.h."""
     _fields_ = [("splits", ctypes.c_int32), ("stream_nr", ctypes.c_int32), ("stream_target", ctypes.c_int32),
                 ("no_stream", ctypes.c_int32), ("no_prefill", ctypes.c_int32), ("fp8_tile", ctypes.c_int32),
-                ("no_gemm16", ctypes.c_int32), ("gemm16_stages", ctypes.c_int32), ("no_stream_rows", ctypes.c_int32)]
+                ("no_gemm16", ctypes.c_int32), ("gemm16_stages", ctypes.c_int32), ("no_stream_rows", ctypes.c_int32),
+                ("stream_rows_expire", ctypes.c_int32)]
 
 
 _lib = None

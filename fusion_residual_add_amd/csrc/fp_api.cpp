@@ -61,6 +61,7 @@ struct Plan {
     bool unpack = false;            // tile-packed weights unpacked into the workspace first (tiled family)
     size_t unpack_off = 0;
     size_t flags_off = 0;           // stream with sc.rp: the rows' ready flags [M] (8 bytes each)
+    bool rows_expire = false;       // sc.rp: the waits expect an unpublished tag (tests of the bounded wait)
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -86,6 +87,7 @@ struct Knobs {
     int gemm16_stages = 0;    // gemm16: LDS stages, 2, 4 or 5 (overrides only)
     bool no_stream = false, no_prefill = false, no_gemm16 = false;
     bool no_stream_rows = false;   // stream: never the kernel's own row pass (overrides only)
+    bool stream_rows_expire = false;   // stream: its waits expect an unpublished tag (tests only)
 };
 
 std::mutex g_tune_mu;
@@ -149,6 +151,7 @@ Knobs knobs_for(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, bo
     }
     kb.gemm16_stages = o.gemm16_stages;
     kb.no_stream_rows = o.no_stream_rows != 0;
+    kb.stream_rows_expire = o.stream_rows_expire != 0;
     if (o.stream_nr > 0) kb.rows = 64 * o.stream_nr;
     if (o.splits > 0) {
         kb.splits = o.splits;
@@ -493,6 +496,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t Nw, fp_dtype act, fp_dtype wdt, boo
         p.flags_off = off;
         off = align256(off + (size_t)M * 8);
         p.sc.rp = K <= 8192 && p.grid + M <= kb.target && wdt != FP_E4M3 && !kb.no_stream_rows ? 1 : 0;
+        p.rows_expire = kb.stream_rows_expire;
     } else {
         p.stats_off = off;
         off = align256(off + (size_t)M * 8);
@@ -838,6 +842,12 @@ fp_status run(const Common &c, const Plan &plan, fp::ProjArgs &pa) {
             pa.rp = sa;
             pa.rp_flags = (unsigned long long *)(ws + plan.flags_off);
             pa.rp_tag = next_rp_tag();
+            pa.rp_wait_tag = pa.rp_tag;
+            pa.rp_spin = 1 << 20;
+            if (plan.rows_expire) {   // tests of the bounded wait: a tag no launch publishes
+                pa.rp_wait_tag = pa.rp_tag ^ (1ull << 62);
+                pa.rp_spin = 64;
+            }
         } else {
             ProfScope ps(fp::norm_kernel_name(act), c.stream);
             hipError_t e = fp::launch_norm(act, sa, c.stream);
@@ -1340,7 +1350,8 @@ fp_status fp_plan_override_set(const fp_plan_override *o) {
                     (v.fp8_tile == 0 || v.fp8_tile == 32 || v.fp8_tile == 64 || v.fp8_tile == 128 || v.fp8_tile == 256) &&
                     (v.no_gemm16 == 0 || v.no_gemm16 == 1) &&
                     (v.gemm16_stages == 0 || v.gemm16_stages == 2 || v.gemm16_stages == 4 || v.gemm16_stages == 5) &&
-                    (v.no_stream_rows == 0 || v.no_stream_rows == 1);
+                    (v.no_stream_rows == 0 || v.no_stream_rows == 1) &&
+                    (v.stream_rows_expire == 0 || v.stream_rows_expire == 1);
     if (!ok) return fail(FP_E_ARG, "a plan override is out of range");
     std::lock_guard<std::mutex> lk(g_tune_mu);
     g_ov = v;

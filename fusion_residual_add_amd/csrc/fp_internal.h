@@ -119,6 +119,8 @@ struct ProjArgs {
     StatsArgs rp;
     unsigned long long *rp_flags;   // [M]
     unsigned long long rp_tag;      // this launch's tag (unique per launch in the process)
+    unsigned long long rp_wait_tag; // the tag the waiting workgroups expect (rp_tag)
+    int rp_spin;                    // polls before a waiting workgroup gives up
 };
 
 

@@ -133,19 +133,19 @@ void stream_kernel(ProjArgs p) {
     // Wait until all M flags hold this launch's tag (lane m of wave 0 polls
     // row m's flag); the workgroup barrier then releases the other waves.
     // The tag is unique per launch within the process, so a flag left by an
-    // earlier launch never reads as ready.  The wait is bounded (about a
-    // second): if it runs out the workgroup carries on and stores NaN, so a
-    // fault in the dispatch order shows in the outputs instead of hanging
-    // the device.  Returns false when it ran out.
+    // earlier launch never reads as ready.  The wait is bounded (p.rp_spin
+    // polls, about a second): if it runs out the workgroup carries on and
+    // stores NaN, so a fault in the dispatch order shows in the outputs
+    // instead of hanging the device.  Returns false when it ran out.
     auto rp_wait = [&]() -> bool {
         bool ok = true;
         if (wave == 0) {
             ok = false;
-            for (int spin = 0; spin < (1 << 20); ++spin) {
+            for (int spin = 0; spin < p.rp_spin; ++spin) {
                 const unsigned long long v =
                     lane < p.M ? __hip_atomic_load(&p.rp_flags[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : p.rp_tag;
-                if (__ballot(v != p.rp_tag) == 0) {
+                               : p.rp_wait_tag;
+                if (__ballot(v != p.rp_wait_tag) == 0) {
                     ok = true;
                     break;
                 }

@@ -430,10 +430,16 @@ int64_t fp_tune_count(void);
  *  no_stream_rows: 1 = the streaming kernel never forms the normalised rows
  *                  itself (a separate row-pass launch forms them first, as
  *                  under HIP graph capture)
+ *  stream_rows_expire: 1 = for tests of the bounded wait only: when the
+ *                  streaming kernel forms the rows itself, its waiting
+ *                  workgroups expect a tag that no workgroup publishes and
+ *                  give up after a short wait, so every output of the call
+ *                  is NaN (h_out is still written)
  * The initial values come from the environment variables FUSEDPROJ_SPLITS,
  * FUSEDPROJ_STREAM_NR, FUSEDPROJ_STREAM_TARGET, FUSEDPROJ_NO_STREAM,
  * FUSEDPROJ_NO_PREFILL, FUSEDPROJ_FP8_TILE, FUSEDPROJ_NO_GEMM16,
- * FUSEDPROJ_GEMM16_STAGES and FUSEDPROJ_NO_STREAM_ROWS, read once, at the first call that plans a
+ * FUSEDPROJ_GEMM16_STAGES and FUSEDPROJ_NO_STREAM_ROWS (stream_rows_expire
+ * only through fp_plan_override_set), read once, at the first call that plans a
  * launch; no call reads the environment after that.
  * fp_plan_override_set replaces the overrides (NULL restores the values read
  * from the environment); FP_E_ARG if a field is out of range.  Process-wide,
@@ -449,6 +455,7 @@ typedef struct {
     int32_t no_gemm16;
     int32_t gemm16_stages;
     int32_t no_stream_rows;
+    int32_t stream_rows_expire;
 } fp_plan_override;
 
 fp_status fp_plan_override_set(const fp_plan_override *o);

@@ -538,11 +538,13 @@ def test_plan_overrides(plan_override):
     assert p["kernel"] == "stream_kernel<bf16,m32,n32,k512,linear>" and p["prep"] == "norm_kernel<bf16>"
     plan_override()
     assert fra.get_plan_override() == dict(splits=0, stream_nr=0, stream_target=0, no_stream=0, no_prefill=0,
-                                           fp8_tile=0, no_gemm16=0, gemm16_stages=0, no_stream_rows=0)
+                                           fp8_tile=0, no_gemm16=0, gemm16_stages=0, no_stream_rows=0,
+                                           stream_rows_expire=0)
     # out-of-range values are rejected and leave the overrides as they were
     plan_override(splits=2)
     for bad in (dict(splits=65), dict(splits=-1), dict(stream_nr=3), dict(no_stream=2), dict(fp8_tile=100),
-                dict(stream_target=70000), dict(no_gemm16=2), dict(gemm16_stages=3), dict(no_stream_rows=2)):
+                dict(stream_target=70000), dict(no_gemm16=2), dict(gemm16_stages=3), dict(no_stream_rows=2),
+                dict(stream_rows_expire=2)):
         with pytest.raises(fra.FusedProjError) as ei:
             fra.set_plan_override(bad)
         assert ei.value.status == 8                     # FP_E_ARG

@@ -14,7 +14,8 @@ Cases: bf16 / fp16 / int8 / int4 / MXFP4 weights; QKV (with h_out), SwiGLU,
 tanh-GELU and plain epilogues; RMSNorm, LayerNorm with and without beta, no
 norm with a residual; 1 .. 64 tokens; hidden up to 8192; row-major and
 tile-packed weights; consecutive calls on one workspace (flags of earlier
-launches left in it) without synchronising between them.
+launches left in it) without synchronising between them; the bounded wait,
+forced from the host (every wait expires: NaN outputs, the launch ends).
 """
 import numpy as np
 import pytest
@@ -162,3 +163,42 @@ def test_rows_in_kernel_full_size(name, plan_override):
     sep, own = _both(wl, d, plan_override, out_dtype=None)
     for nm, a, b in zip(("q", "k", "v", "h_out", "out"), sep, own):
         assert torch.equal(a, b), f"{name}: {nm}"
+
+
+def test_rows_in_kernel_wait_is_bounded(plan_override):
+    """The bounded wait, forced from the host (the stream_rows_expire
+    override): the waiting workgroups expect a tag that no workgroup
+    publishes, so every wait runs out after a short bound.  The launch ends,
+    every output is NaN (QKV here on tiles that several workgroups share, so
+    the NaN also travels through the partial sums), h_out is still exact, and
+    the next call on the same workspace is right again."""
+    wl = _wl(dict(M=16, hidden=2048, H=6, Hkv=2, D=64, ffn=512))
+    inp = inputs.generate(wl, seed=53)
+    d = to_dev(inp)
+    pq = fra.describe_plan(wl.M, wl.hidden, wl.n_qkv, torch.bfloat16, torch.bfloat16)
+    pg = fra.describe_plan(wl.M, wl.hidden, wl.n_gu, torch.bfloat16, torch.bfloat16, wl.act_fn)
+    print(f"bounded wait: qkv {pq['kernel']} grid={pq['grid']} slots={pq['slots']}; gu {pg['kernel']}", flush=True)
+    assert pq["kernel"].endswith(",rows>") and pq["slots"] > 1, pq
+    assert pg["kernel"].endswith(",rows>"), pg
+    need = max(fra.workspace_bytes(wl.M, wl.hidden, n, torch.bfloat16, torch.bfloat16) for n in (wl.n_qkv, wl.n_gu))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+
+    def calls():
+        q, k, v, h = fra.fused_add_norm_qkv(d["x"], d["r"], d["gamma"], d["w_qkv"], wl.n_heads, wl.n_kv_heads,
+                                            wl.head_dim, eps=wl.eps, workspace=ws, out_dtype=torch.float32)
+        out = fra.fused_gateup_act(d["x"], d["r"], d["gamma"], d["w_gu"], wl.ffn, wl.act_fn, eps=wl.eps,
+                                   workspace=ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return q, k, v, h, out
+
+    rq, rg = oracle.workload_qkv(wl, inp), oracle.workload_gateup(wl, inp)
+    plan_override(stream_rows_expire=1)
+    q, k, v, h, out = calls()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        assert torch.isnan(t).all(), f"{name}: an expired wait must leave NaN"
+    assert np.array_equal(h.double().cpu().numpy(), rq["h_out"]), "h_out not bit-exact"
+    plan_override(stream_rows_expire=0)
+    q, k, v, h, out = calls()
+    for name, got in (("q", q), ("k", k), ("v", v)):
+        check(name, got, rq[name])
+    check("out", out, rg["out"])
