@@ -122,11 +122,17 @@ def test_rows_in_kernel_packed(cfg, plan_override):
         assert torch.equal(a, b), name
 
 
-def test_rows_in_kernel_consecutive_calls_one_workspace(plan_override):
+@pytest.mark.parametrize("cfg", [dict(M=32, hidden=4096, H=32, Hkv=8, D=128, ffn=512),
+                                 dict(M=32, hidden=512, H=4, Hkv=2, D=64, ffn=256)],
+                         ids=["large", "l2-resident"])
+def test_rows_in_kernel_consecutive_calls_one_workspace(cfg, plan_override):
     """Four calls on one workspace, back to back without synchronising: each
     launch waits for its own rows (a new tag), never for the flags an
-    earlier launch left, so every result equals the separate row pass's."""
-    wl = _wl(dict(M=32, hidden=4096, H=32, Hkv=8, D=128, ffn=512))
+    earlier launch left, so every result equals the separate row pass's.
+    The second shape's weights, rows and flags (under 1 MB) all stay in the
+    XCDs' L2s from one call to the next, so a row line that an earlier launch
+    left in an L2 would be read stale by a later one."""
+    wl = _wl(cfg)
     ins = [to_dev(inputs.generate(wl, seed=s)) for s in (51, 52, 53, 54)]
     plan_override(no_stream_rows=1)
     ref = [(*run_qkv(wl, d, None), run_gu(wl, d, None)) for d in ins]
